@@ -1,0 +1,270 @@
+"""CPU oracle for the TokenGate pruned-prefill path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, the package's smoke check and the benchmark's CPU-baseline
+leg may import this module.  The product path (the HIP library and its Python
+binding) never calls it and shares no code with it.
+
+Every function is the plain definition of one step, in float64 on the CPU,
+with library primitives (matmul, erf, exp, a stable lexicographic sort) as the
+only building blocks and no blocking, fusion or reordering.  The steps follow
+the three-phase forward pass and the token-gated attention described on the
+MarkTechPost article as rendered in French on spke.com ("Comment TokenGate
+a-t-il appris le fonctionnement de la réduction des tokens ?" and "Qu'est-ce que
+l'attention gérée par des tokens ?"):
+
+* a small MLP scores every token from its post-attention residual at the gate
+  layer L                                               -> ``gate_score``
+* a top-K selector keeps the best-scoring tokens; only the document part of
+  the prompt may be dropped, the question is always kept -> ``topk_select``
+* layers above L process only the K kept tokens and create no KV for the
+  dropped ones                                           -> ``gather_compact``
+* each kept token's score becomes a bias on the attention logits, with a
+  learnable per-head gain and a per-head temperature     -> ``gated_attention``
+
+The pages only sketch the bias.  The exact logit used here is
+``tau_h * (q_i . k_j) / sqrt(d_head) + g_h * s_j`` over causal ``j <= i``.
+
+Pins (tests/test_oracle_pins.py): the gate against torch's own Linear+GELU and
+textbook values of the normal CDF; the selector against brute force (Python
+``sorted`` and an O(N^2) rank count) and its invariants; the attention against
+torch's scaled_dot_product_attention (plain causal when gains are 0 and
+temperatures 1, with an explicit additive mask otherwise) and closed forms (row
+0, shift invariance, a dominant key); the layer stack against an independent
+float64 composition.  Nothing here is "parity unpinned" except what the pages
+themselves leave open: fidelity to the authors' unpublished kernels.
+"""
+from __future__ import annotations
+
+import bisect
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+__all__ = [
+    "gelu_erf",
+    "gate_score",
+    "plan",
+    "topk_select",
+    "gather_compact",
+    "gated_attention",
+    "gated_attention_rows",
+    "linear",
+    "stack_forward",
+]
+
+
+# --------------------------------------------------------------------------
+# Gate MLP (spke.com page, three-phase list, second bullet: an MLP scores each
+# token from its post-attention residual at layer L).
+# The activation is GELU in its exact (erf) form; the score is the raw MLP
+# output, with no squashing: the selector only needs an order, and the bias
+# uses the score itself.
+# --------------------------------------------------------------------------
+def gelu_erf(z: torch.Tensor) -> torch.Tensor:
+    """GELU(z) = z * Phi(z) = z/2 * (1 + erf(z / sqrt 2)), float64."""
+    z = z.double()
+    return 0.5 * z * (1.0 + torch.erf(z / math.sqrt(2.0)))
+
+
+def gate_score(hidden: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor],
+               w2: torch.Tensor, b2: Optional[torch.Tensor]) -> torch.Tensor:
+    """s_t = w2 . GELU(W1 x_t + b1) + b2 for every token t, returned as fp32.
+
+    hidden[T][d], w1[d_gate][d] (Linear layout), b1[d_gate] or None,
+    w2[d_gate], b2[1] or None.  Computed in float64 from the stored values,
+    rounded once to fp32 (round to nearest even).
+    """
+    x = hidden.double()
+    z = x @ w1.double().t()
+    if b1 is not None:
+        z = z + b1.double()
+    h = gelu_erf(z)
+    s = h @ w2.double()
+    if b2 is not None:
+        s = s + b2.double().reshape(())
+    return s.float()
+
+
+# --------------------------------------------------------------------------
+# Top-K selection (spke.com page: the top-K selector keeps the best-scoring
+# tokens; only the document may be pruned, the question never is; `generate`
+# takes a max_kept_prefill_tokens budget, "Comment déployer TokenGate ?").
+# Readings: the budget counts the question tail; the question is the tail of
+# each request; ties go to the lower token index; -0 equals +0; NaN ranks below
+# -inf; the kept ids come out ascending.
+# --------------------------------------------------------------------------
+def plan(seq_len: Sequence[int], q_len: Sequence[int], budget: Sequence[int]
+         ) -> Tuple[List[int], List[int]]:
+    """Validate a batch and return (cu_seqlens, cu_kept), each of length B+1.
+
+    Kept per request is min(budget_b, N_b).  Raises ValueError when N_b < 1,
+    q_b outside [0, N_b], budget_b < 1 or q_b > min(budget_b, N_b).
+    """
+    if not (len(seq_len) == len(q_len) == len(budget)) or len(seq_len) < 1:
+        raise ValueError("batch arrays must have one equal, non-zero length")
+    cu_s, cu_k = [0], [0]
+    for n, q, k in zip(seq_len, q_len, budget):
+        n, q, k = int(n), int(q), int(k)
+        if n < 1 or q < 0 or q > n or k < 1 or q > min(k, n):
+            raise ValueError(f"bad request: seq_len={n} q_len={q} budget={k}")
+        cu_s.append(cu_s[-1] + n)
+        cu_k.append(cu_k[-1] + min(k, n))
+    return cu_s, cu_k
+
+
+def topk_select(scores: torch.Tensor, seq_len: Sequence[int], q_len: Sequence[int],
+                budget: Sequence[int]) -> Tuple[torch.Tensor, List[int]]:
+    """Kept global token ids (int32, ascending within each request) and cu_kept.
+
+    Per request: if the budget covers the request, keep it all; otherwise keep
+    the K_b - q_b best document tokens under (score descending, index
+    ascending) plus the whole question tail.
+    """
+    cu_s, cu_k = plan(seq_len, q_len, budget)
+    s_all = scores.detach().cpu().double().numpy()
+    kept = []
+    for b in range(len(seq_len)):
+        lo, n, q = cu_s[b], int(seq_len[b]), int(q_len[b])
+        keep = min(int(budget[b]), n)
+        if keep >= n:
+            ids = np.arange(n)
+        else:
+            ndoc = n - q
+            sd = s_all[lo: lo + ndoc]
+            nan = np.isnan(sd)
+            val = np.where(nan, 0.0, sd) + 0.0          # -0 -> +0
+            cls = np.where(nan, 0, 1)                   # NaN below every number
+            idx = np.arange(ndoc)
+            order = np.lexsort((idx, -val, -cls))       # cls desc, val desc, idx asc
+            ids = np.sort(np.concatenate([order[: keep - q], np.arange(ndoc, n)]))
+        kept.append(ids + lo)
+    out = np.concatenate(kept).astype(np.int32) if kept else np.zeros(0, np.int32)
+    return torch.from_numpy(out), cu_k
+
+
+# --------------------------------------------------------------------------
+# Gather / compaction (spke.com page, third bullet: layers above L process only
+# the K kept tokens and never create KV entries for the pruned ones).
+# --------------------------------------------------------------------------
+def gather_compact(hidden: torch.Tensor, scores: Optional[torch.Tensor],
+                   kept_idx: torch.Tensor):
+    """hidden_kept[r] = hidden[kept_idx[r]] (bit for bit), s_kept[r] = s[kept_idx[r]]."""
+    idx = kept_idx.long()
+    hk = hidden[idx].clone()
+    sk = scores[idx].clone() if scores is not None else None
+    return hk, sk
+
+
+# --------------------------------------------------------------------------
+# Token-gated attention (spke.com page, "Qu'est-ce que l'attention gérée par des
+# tokens ?": the score of each kept token becomes a bias on the attention
+# logits above L; a learnable per-head gain and a per-head temperature, the
+# latter correcting for each query seeing fewer keys).
+# Exact form: l_ij = tau_h (q_i . k_j) / sqrt(d_head) + g_h s_j, j <= i,
+# softmax over j, GQA head h reads KV head h // (Hq / Hkv).
+# --------------------------------------------------------------------------
+def _head_logits(Q, Kb, s, gain_h, temp_h, dh):
+    return temp_h * (Q @ Kb.t()) / math.sqrt(dh) + gain_h * s[None, :]
+
+
+def gated_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    s_kept: torch.Tensor, gain: torch.Tensor, temp: torch.Tensor,
+                    cu_kept: Sequence[int]) -> Tuple[torch.Tensor, torch.Tensor]:
+    """out[Kt][Hq][dh] (float64) and lse[Hq][Kt] (float64, natural log).
+
+    q[Kt][Hq][dh], k,v[Kt][Hkv][dh]; requests are the row ranges of cu_kept and
+    never attend to each other.
+    """
+    Kt, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    out = torch.zeros(Kt, Hq, dh, dtype=torch.float64)
+    lse = torch.zeros(Hq, Kt, dtype=torch.float64)
+    s64 = s_kept.double()
+    g64, t64 = gain.double(), temp.double()
+    for b in range(len(cu_kept) - 1):
+        lo, hi = int(cu_kept[b]), int(cu_kept[b + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        future = torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1)
+        for h in range(Hq):
+            kv = h // group
+            Q = q[lo:hi, h].double()
+            Kb = k[lo:hi, kv].double()
+            V = v[lo:hi, kv].double()
+            logits = _head_logits(Q, Kb, s64[lo:hi], g64[h], t64[h], dh)
+            logits = logits.masked_fill(future, -math.inf)
+            m = logits.max(dim=1).values
+            p = torch.exp(logits - m[:, None])
+            denom = p.sum(dim=1)
+            out[lo:hi, h] = (p @ V) / denom[:, None]
+            lse[h, lo:hi] = m + torch.log(denom)
+    return out, lse
+
+
+def gated_attention_rows(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int],
+                         rows: Sequence[int]) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The same definition evaluated only at the given global query rows.
+
+    Returns out[len(rows)][Hq][dh] and lse[Hq][len(rows)], float64.
+    """
+    Kt, Hq, dh = q.shape
+    group = Hq // k.shape[1]
+    cu = list(int(c) for c in cu_kept)
+    out = torch.zeros(len(rows), Hq, dh, dtype=torch.float64)
+    lse = torch.zeros(Hq, len(rows), dtype=torch.float64)
+    s64 = s_kept.double()
+    for r_i, r in enumerate(rows):
+        if not 0 <= r < cu[-1]:
+            raise IndexError(r)
+        lo = cu[bisect.bisect_right(cu, r) - 1]
+        for h in range(Hq):
+            kv = h // group
+            Qr = q[r:r + 1, h].double()
+            Kb = k[lo:r + 1, kv].double()
+            V = v[lo:r + 1, kv].double()
+            logits = _head_logits(Qr, Kb, s64[lo:r + 1], float(gain[h]), float(temp[h]), dh)[0]
+            m = logits.max()
+            p = torch.exp(logits - m)
+            denom = p.sum()
+            out[r_i, h] = (p @ V) / denom
+            lse[h, r_i] = m + torch.log(denom)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# Layers above the gate on the kept tokens only (spke.com page, third bullet).
+# The pages give no layer detail; this stack is the attention sub-layer alone:
+# q|k|v = x W^T, then x <- x + attn W_o^T, with the gated attention above.
+# Each stored tensor is rounded to the storage dtype where a GPU pipeline
+# stores it (q, k, v, attention output, updated residual).
+# --------------------------------------------------------------------------
+def linear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    """y = x W^T in float64 (W in Linear layout [out][in])."""
+    return x.double() @ w.double().t()
+
+
+def stack_forward(x_kept: torch.Tensor, s_kept: torch.Tensor, layers: List[Dict[str, torch.Tensor]],
+                  cu_kept: Sequence[int], n_q_heads: int, n_kv_heads: int, d_head: int,
+                  store_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    """Run the attention stack over the compacted rows; returns the residual.
+
+    store_dtype=None keeps everything in float64 (for pinning); otherwise each
+    stored tensor is rounded to that dtype.
+    """
+    def store(t):
+        return t if store_dtype is None else t.to(store_dtype)
+
+    Kt = x_kept.shape[0]
+    x = x_kept.double() if store_dtype is None else x_kept.to(store_dtype)
+    for L in layers:
+        q = store(linear(x, L["wq"])).reshape(Kt, n_q_heads, d_head)
+        k = store(linear(x, L["wk"])).reshape(Kt, n_kv_heads, d_head)
+        v = store(linear(x, L["wv"])).reshape(Kt, n_kv_heads, d_head)
+        a, _ = gated_attention(q, k, v, s_kept, L["gain"], L["temp"], cu_kept)
+        a = store(a).reshape(Kt, n_q_heads * d_head)
+        x = store(x.double() + linear(a, L["wo"]))
+    return x

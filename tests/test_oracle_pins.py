@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test checks one oracle function against a library routine it does not
+use, brute force, a closed form, a textbook value or an invariant the
+TokenGate pages state, chosen so that a plausible slip (dropped bias, wrong
+sign, transposed weight, wrong GQA mapping, bias on the query instead of the
+key, anti-causal mask, wrong softmax scale, wrong tie-break) fails at least
+one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- gate ----
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gate_matches_torch_linear_gelu(with_bias):
+    g = torch.Generator().manual_seed(1)
+    T, d, dg = 37, 48, 16                   # non-square W1 catches a transpose
+    x = torch.randn(T, d, generator=g)
+    w1 = torch.randn(dg, d, generator=g) / math.sqrt(d)
+    w2 = torch.randn(dg, generator=g) / math.sqrt(dg)
+    b1 = torch.randn(dg, generator=g) if with_bias else None
+    b2 = torch.randn(1, generator=g) if with_bias else None
+    got = oracle.gate_score(x, w1, b1, w2, b2)
+    h = F.gelu(F.linear(x.double(), w1.double(), None if b1 is None else b1.double()),
+               approximate="none")
+    want = F.linear(h, w2.double()[None, :], None if b2 is None else b2.double())[:, 0]
+    assert got.dtype == torch.float32 and got.shape == (T,)
+    torch.testing.assert_close(got.double(), want.float().double(), rtol=2e-7, atol=1e-9)
+
+
+def _normal_cdf_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "normal_cdf.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                x, p = line.split()
+                rows.append((float(x), float(p)))
+    return rows
+
+
+def test_gate_gelu_textbook_points():
+    """W1 = 0 makes every score w2 . GELU(b1) + b2, and GELU(x) = x Phi(x)."""
+    rows = _normal_cdf_table()
+    pts = [x for x, _ in rows] + [-x for x, _ in rows if x > 0]
+    phi = {x: p for x, p in rows}
+    phi.update({-x: 1.0 - p for x, p in rows if x > 0})
+    dg, d, T = len(pts), 8, 3
+    b1 = torch.tensor(pts, dtype=torch.float64)
+    w1 = torch.zeros(dg, d, dtype=torch.float64)
+    x = torch.randn(T, d, dtype=torch.float64)
+    for u, xv in enumerate(pts):
+        w2 = torch.zeros(dg, dtype=torch.float64)
+        w2[u] = 1.0
+        s = oracle.gate_score(x, w1, b1, w2, torch.tensor([0.25], dtype=torch.float64))
+        want = xv * phi[xv] + 0.25
+        assert torch.allclose(s.double(), torch.full((T,), want, dtype=torch.float64),
+                              rtol=1e-7, atol=2e-10), (xv, s, want)
+
+
+def test_gate_constant_when_w1_zero_all_ties():
+    """All-equal scores are a degenerate case the selector must handle."""
+    w1 = torch.zeros(4, 6)
+    b1 = torch.tensor([0.3, -0.2, 1.0, 0.0])
+    w2 = torch.tensor([0.5, -1.0, 0.25, 2.0])
+    s = oracle.gate_score(torch.randn(9, 6), w1, b1, w2, torch.tensor([0.1]))
+    assert torch.all(s == s[0])
+
+
+# --------------------------------------------------------------- select ----
+def _brute_sorted(scores, seq_len, q_len, budget):
+    """Kept ids by a full Python sort with an explicit comparison key."""
+    out, lo = [], 0
+    for n, q, k in zip(seq_len, q_len, budget):
+        keep = min(k, n)
+        if keep >= n:
+            ids = list(range(n))
+        else:
+            def key(i):
+                v = float(scores[lo + i])
+                if math.isnan(v):
+                    return (1, 0.0, i)
+                return (0, -(v + 0.0), i)
+            doc = sorted(range(n - q), key=key)[: keep - q]
+            ids = sorted(doc + list(range(n - q, n)))
+        out += [lo + i for i in ids]
+        lo += n
+    return out
+
+
+def _brute_rank(scores, seq_len, q_len, budget):
+    """Kept ids by counting, for every document token, how many beat it."""
+    def beats(a, ia, b, ib):            # does (a, ia) come before (b, ib)?
+        na, nb = math.isnan(a), math.isnan(b)
+        if na != nb:
+            return nb
+        if not na and a != b:
+            return a > b
+        return ia < ib
+
+    out, lo = [], 0
+    for n, q, k in zip(seq_len, q_len, budget):
+        keep = min(k, n)
+        for i in range(n):
+            if keep >= n or i >= n - q:
+                out.append(lo + i)
+                continue
+            vi = float(scores[lo + i])
+            rank = sum(beats(float(scores[lo + j]), j, vi, i) for j in range(n - q) if j != i)
+            if rank < keep - q:
+                out.append(lo + i)
+        lo += n
+    return out
+
+
+SPECIALS = [0.0, -0.0, float("inf"), float("-inf"), float("nan"), 1.0, -1.0, 1e-30, -1e-30]
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_select_matches_brute_force(case):
+    g = torch.Generator().manual_seed(100 + case)
+    B = 1 + case % 3
+    seq_len = torch.randint(1, 60, (B,), generator=g).tolist()
+    q_len = [int(torch.randint(0, n + 1, (1,), generator=g)) for n in seq_len]
+    budget = [max(1, q + int(torch.randint(0, n + 3, (1,), generator=g))) for q, n in zip(q_len, seq_len)]
+    budget = [max(b, 1) for b in budget]
+    T = sum(seq_len)
+    if case % 2:
+        s = (torch.randint(0, 5, (T,), generator=g).float() - 2.0) / 2.0   # heavy ties
+    else:
+        s = torch.randn(T, generator=g)
+    if case % 4 == 3:
+        pos = torch.randint(0, T, (min(T, 8),), generator=g)
+        for j, p in enumerate(pos.tolist()):
+            s[p] = SPECIALS[(j + case) % len(SPECIALS)]
+    kept, cu = oracle.topk_select(s, seq_len, q_len, budget)
+    assert kept.tolist() == _brute_sorted(s, seq_len, q_len, budget)
+    assert kept.tolist() == _brute_rank(s, seq_len, q_len, budget)
+    assert cu[-1] == len(kept)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.sampled_from(SPECIALS + [0.5, 0.25, -2.0]), min_size=1, max_size=40),
+       st.integers(0, 40), st.integers(1, 45))
+def test_select_invariants(vals, q, budget):
+    n = len(vals)
+    q = min(q, n)
+    budget = max(budget, q) if q > 0 else budget
+    s = torch.tensor(vals, dtype=torch.float32)
+    kept, cu = oracle.topk_select(s, [n], [q], [budget])
+    k = kept.tolist()
+    assert len(k) == min(budget, n) == cu[1]
+    assert k == sorted(set(k))                          # ascending, unique
+    assert set(range(n - q, n)) <= set(k)               # question tail always kept
+    doc = [i for i in range(n - q)]
+    kept_doc = [i for i in doc if i in set(k)]
+    drop_doc = [i for i in doc if i not in set(k)]
+
+    def key(i):
+        v = float(s[i])
+        return (-math.inf, 0) if math.isnan(v) else (v + 0.0, 1)
+
+    for i in kept_doc:                                  # threshold property
+        for j in drop_doc:
+            ki, kj = key(i), key(j)
+            assert ki[0] > kj[0] or (ki[0] == kj[0] and (ki[1] > kj[1] or (ki[1] == kj[1] and i < j)))
+
+
+def test_select_special_budgets():
+    s = torch.randn(50)
+    kept, _ = oracle.topk_select(s, [50], [10], [10])          # budget == tail
+    assert kept.tolist() == list(range(40, 50))
+    kept, _ = oracle.topk_select(s, [50], [10], [500])         # budget >= N
+    assert kept.tolist() == list(range(50))
+    kept, _ = oracle.topk_select(torch.full((50,), 0.75), [50], [5], [12])   # all ties
+    assert kept.tolist() == list(range(7)) + list(range(45, 50))
+    with pytest.raises(ValueError):
+        oracle.topk_select(s, [50], [10], [9])                 # budget below tail
+    with pytest.raises(ValueError):
+        oracle.topk_select(s, [50], [51], [60])
+
+
+def test_select_nan_zero_inf_order():
+    s = torch.tensor([float("nan"), -0.0, 0.0, float("-inf"), float("inf"), 1.0, float("nan"), -1.0])
+    kept, _ = oracle.topk_select(s, [8], [0], [4])
+    assert kept.tolist() == [1, 2, 4, 5]                       # inf, 1, then -0/+0 tie by index
+    kept, _ = oracle.topk_select(s, [8], [0], [7])
+    assert kept.tolist() == [0, 1, 2, 3, 4, 5, 7]              # first NaN beats the second by index
+
+
+# --------------------------------------------------------------- gather ----
+def test_gather_bitwise():
+    h = torch.randn(20, 7).to(torch.bfloat16)
+    s = torch.randn(20)
+    idx = torch.tensor([0, 3, 4, 19], dtype=torch.int32)
+    hk, sk = oracle.gather_compact(h, s, idx)
+    for r, i in enumerate(idx.tolist()):
+        assert torch.equal(hk[r].view(torch.int16), h[i].view(torch.int16))
+        assert sk[r].item() == s[i].item()
+
+
+# ------------------------------------------------------------ attention ----
+def _attn_case(seed, lens=(5, 17, 33), Hq=4, Hkv=2, dh=16):
+    g = torch.Generator().manual_seed(seed)
+    Kt = sum(lens)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    q = torch.randn(Kt, Hq, dh, generator=g, dtype=torch.float64)
+    k = torch.randn(Kt, Hkv, dh, generator=g, dtype=torch.float64)
+    v = torch.randn(Kt, Hkv, dh, generator=g, dtype=torch.float64)
+    s = torch.randn(Kt, generator=g, dtype=torch.float64)
+    gain = torch.rand(Hq, generator=g, dtype=torch.float64) + 0.5
+    temp = torch.rand(Hq, generator=g, dtype=torch.float64) * 0.4 + 0.8
+    return q, k, v, s, gain, temp, cu
+
+
+def _sdpa_reference(q, k, v, s, gain, temp, cu):
+    """torch SDPA (float64): queries scaled by tau_h, float mask g_h s_j plus causal."""
+    Kt, Hq, dh = q.shape
+    rep = Hq // k.shape[1]
+    out = torch.zeros_like(q)
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        n = hi - lo
+        Q = (q[lo:hi].permute(1, 0, 2) * temp[:, None, None])          # [Hq][n][dh]
+        K = k[lo:hi].permute(1, 0, 2).repeat_interleave(rep, dim=0).contiguous()
+        V = v[lo:hi].permute(1, 0, 2).repeat_interleave(rep, dim=0).contiguous()
+        mask = gain[:, None, None] * s[lo:hi][None, None, :].expand(Hq, n, n)
+        mask = mask.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), -math.inf)
+        o = F.scaled_dot_product_attention(Q[None], K[None], V[None], attn_mask=mask[None])
+        out[lo:hi] = o[0].permute(1, 0, 2)
+    return out
+
+
+def test_attention_plain_causal_when_gain0_temp1():
+    q, k, v, s, _, _, cu = _attn_case(3)
+    Hq = q.shape[1]
+    out, _ = oracle.gated_attention(q, k, v, s, torch.zeros(Hq), torch.ones(Hq), cu)
+    rep = Hq // k.shape[1]
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        Q = q[lo:hi].permute(1, 0, 2)[None]
+        K = k[lo:hi].permute(1, 0, 2).repeat_interleave(rep, dim=0)[None].contiguous()
+        V = v[lo:hi].permute(1, 0, 2).repeat_interleave(rep, dim=0)[None].contiguous()
+        want = F.scaled_dot_product_attention(Q, K, V, is_causal=True)[0].permute(1, 0, 2)
+        torch.testing.assert_close(out[lo:hi], want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_attention_general_matches_sdpa_with_mask(seed):
+    q, k, v, s, gain, temp, cu = _attn_case(seed)
+    out, _ = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    torch.testing.assert_close(out, _sdpa_reference(q, k, v, s, gain, temp, cu), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_lse_from_sdpa_probabilities():
+    """With V = identity, SDPA returns the probability matrix; p_i0 = exp(l_i0 - lse_i)."""
+    n, Hq, dh = 9, 2, 9
+    g = torch.Generator().manual_seed(8)
+    q = torch.randn(n, Hq, dh, generator=g, dtype=torch.float64)
+    k = torch.randn(n, 1, dh, generator=g, dtype=torch.float64)
+    v = torch.eye(n, dtype=torch.float64)[:, None, :]
+    s = torch.randn(n, generator=g, dtype=torch.float64)
+    gain = torch.tensor([0.7, 1.3], dtype=torch.float64)
+    temp = torch.tensor([0.9, 1.1], dtype=torch.float64)
+    out, lse = oracle.gated_attention(q, k, v, s, gain, temp, [0, n])
+    P = _sdpa_reference(q, k, v, s, gain, temp, [0, n])        # [n][Hq][n] = probabilities
+    torch.testing.assert_close(out, P, rtol=1e-12, atol=1e-12)
+    for h in range(Hq):
+        l0 = temp[h] * (q[:, h] @ k[0, 0]) / math.sqrt(dh) + gain[h] * s[0]
+        torch.testing.assert_close(lse[h], l0 - torch.log(P[:, h, 0]), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    q, k, v, s, gain, temp, cu = _attn_case(6, lens=(12,))
+    out, lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    Hq = q.shape[1]
+    rep = Hq // k.shape[1]
+    for h in range(Hq):      # row 0 sees only key 0
+        assert torch.equal(out[0, h], v[0, h // rep])
+        want = temp[h] * (q[0, h] @ k[0, h // rep]) / math.sqrt(q.shape[2]) + gain[h] * s[0]
+        assert abs(float(lse[h, 0] - want)) < 1e-12
+    # constant scores: output does not depend on the gain
+    c = torch.full_like(s, 0.37)
+    o1, _ = oracle.gated_attention(q, k, v, c, gain, temp, cu)
+    o2, _ = oracle.gated_attention(q, k, v, c, gain * 3.0, temp, cu)
+    torch.testing.assert_close(o1, o2, rtol=1e-12, atol=1e-12)
+    # shifting every score leaves the output unchanged and moves lse by g_h * c
+    o3, l3 = oracle.gated_attention(q, k, v, s + 2.5, gain, temp, cu)
+    torch.testing.assert_close(o3, out, rtol=1e-10, atol=1e-12)
+    torch.testing.assert_close(l3, lse + 2.5 * gain[:, None], rtol=1e-12, atol=1e-10)
+    # one dominant KEY: every later query row collapses onto its value
+    big = s.clone()
+    big[4] = 1e4
+    o4, _ = oracle.gated_attention(q, k, v, big, gain, temp, cu)
+    for h in range(Hq):
+        torch.testing.assert_close(o4[4:, h], v[4, h // rep].expand(8, -1), rtol=0, atol=1e-12)
+        torch.testing.assert_close(o4[:4, h], out[:4, h], rtol=0, atol=0)
+
+
+def test_attention_rows_agree_with_full():
+    q, k, v, s, gain, temp, cu = _attn_case(7)
+    out, lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    rows = [0, 4, 5, 6, 21, 22, 54]
+    o_r, l_r = oracle.gated_attention_rows(q, k, v, s, gain, temp, cu, rows)
+    torch.testing.assert_close(o_r, out[rows], rtol=1e-12, atol=1e-12)
+    torch.testing.assert_close(l_r, lse[:, rows], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- stack ----
+def test_stack_matches_independent_composition():
+    g = torch.Generator().manual_seed(9)
+    Kt, d, Hq, Hkv, dh = 23, 32, 4, 2, 8
+    cu = [0, 10, 23]
+    x = torch.randn(Kt, d, generator=g, dtype=torch.float64)
+    s = torch.randn(Kt, generator=g, dtype=torch.float64)
+    layers = []
+    for _ in range(2):
+        layers.append(dict(
+            wq=torch.randn(Hq * dh, d, generator=g, dtype=torch.float64) / math.sqrt(d),
+            wk=torch.randn(Hkv * dh, d, generator=g, dtype=torch.float64) / math.sqrt(d),
+            wv=torch.randn(Hkv * dh, d, generator=g, dtype=torch.float64) / math.sqrt(d),
+            wo=torch.randn(d, Hq * dh, generator=g, dtype=torch.float64) / math.sqrt(Hq * dh),
+            gain=torch.rand(Hq, generator=g, dtype=torch.float64) + 0.5,
+            temp=torch.rand(Hq, generator=g, dtype=torch.float64) * 0.4 + 0.8))
+    got = oracle.stack_forward(x, s, layers, cu, Hq, Hkv, dh)
+    want = x.clone()
+    for L in layers:
+        q = F.linear(want, L["wq"]).view(Kt, Hq, dh)
+        k = F.linear(want, L["wk"]).view(Kt, Hkv, dh)
+        v = F.linear(want, L["wv"]).view(Kt, Hkv, dh)
+        a = _sdpa_reference(q, k, v, s, L["gain"], L["temp"], cu).reshape(Kt, Hq * dh)
+        want = want + F.linear(a, L["wo"])
+    torch.testing.assert_close(got, want, rtol=1e-10, atol=1e-10)
+
+
+# ---------------------------------------------------------------- e2e ------
+def test_needles_survive_reduced_haystack():
+    """Planted needles (the 128k workload's construction) survive the oracle's
+    gate + top-K on a shorter haystack of the same layer shape."""
+    w = workloads.Workload("needles_16k", workloads.WORKLOADS["qwen3_1p7b_128k_niah"].shape,
+                           [16384], [128], [1024], n_needles=64)
+    inp = workloads.gate_inputs(w, seed=0)
+    s = oracle.gate_score(inp["hidden"], inp["w1"], inp["b1"], inp["w2"], inp["b2"])
+    kept, _ = oracle.topk_select(s, w.seq_len, w.q_len, w.budget)
+    needles = set(workloads.needle_positions(w, 0).tolist())
+    assert needles <= set(kept.tolist())
