@@ -1,0 +1,241 @@
+"""Benchmark of the TokenGate pruned-prefill hot path on one MI355X.
+
+One step is one gated layer over one batch of synthetic, HBM-resident input:
+    gate MLP score (all tokens) -> top-K select (+ question tail)
+    -> gather/compact -> causal GQA token-gated attention over the kept rows
+(plus the four QKV/attention/O layers above the gate for the stack workload).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line: whole-step throughput in tokens of context per second
+(N / step time), the per-kernel split, the roofline of the dominant kernel and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+F32_PEAK_TFLOPS = 157.3      # MI355X fp32 vector, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="qwen3_1p7b_128k_niah")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--detail", default="", help="also write per-kernel detail JSON to this path")
+    return p.parse_args()
+
+
+def algorithmic(w, Kt_per_req):
+    """Algorithmic bytes / FLOPs per launch of each kernel for workload w."""
+    sh = w.shape
+    eb = 2 if sh.dtype.is_floating_point and sh.dtype.itemsize == 2 else 4
+    T, d, dg = w.total_tokens, sh.d_model, sh.d_gate
+    Kt = sum(Kt_per_req)
+    pairs = sum(k * (k + 1) // 2 for k in Kt_per_req)
+    return {
+        "gate": {"bytes": T * (d * eb + 4) + dg * d * eb + 2 * dg * eb,
+                 "flops": 2 * T * (d * dg + dg)},
+        "select": {"bytes": T * 4 + Kt * 4, "flops": 0},
+        "gather": {"bytes": Kt * (2 * d * eb + 12), "flops": 0},
+        "attention": {"bytes": Kt * (sh.n_q_heads * 2 + sh.n_kv_heads * 2) * sh.d_head * eb + Kt * 4,
+                      "flops": 4 * sh.d_head * sh.n_q_heads * pairs},
+    }
+
+
+def cpu_baseline(w, gi, ai, s_gpu, kept, cu):
+    """The oracle as it stands, on a bounded sample of the workload, scaled to
+    the whole layer: the gate on the first 8192 tokens, the selector and the
+    gather on the whole layer, attention for 2 of the query heads (one KV head)
+    on all kept rows."""
+    import torch
+
+    import oracle
+
+    sh = w.shape
+    T = w.total_tokens
+    t_s = min(T, 8192)
+    t0 = time.perf_counter()
+    oracle.gate_score(gi["hidden"][:t_s], gi["w1"], gi["b1"], gi["w2"], gi["b2"])
+    t_gate = (time.perf_counter() - t0) * T / t_s
+    t0 = time.perf_counter()
+    oracle.topk_select(s_gpu, w.seq_len, w.q_len, w.budget)
+    t_sel = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.gather_compact(gi["hidden"], s_gpu, kept)
+    t_gath = time.perf_counter() - t0
+    hs = min(2, sh.n_q_heads)
+    group = sh.n_q_heads // sh.n_kv_heads
+    kv_need = (hs + group - 1) // group
+    s_kept = s_gpu[kept.long()]
+    t0 = time.perf_counter()
+    oracle.gated_attention(ai["q"][:, :hs].contiguous(), ai["k"][:, :kv_need].contiguous(),
+                           ai["v"][:, :kv_need].contiguous(), s_kept, ai["gain"][:hs],
+                           ai["temp"][:hs], cu)
+    t_attn = (time.perf_counter() - t0) * sh.n_q_heads / hs
+    total = t_gate + t_sel + t_gath + t_attn
+    return {
+        "value": T / total,
+        "unit": "tokens/s",
+        "cores": torch.get_num_threads(),
+        "kind": "oracle",
+        "sample": (f"oracle gate on {t_s} of {T} tokens, selector and gather on the whole layer, "
+                   f"attention for {hs} of {sh.n_q_heads} query heads on all {len(kept)} kept rows; "
+                   "each part scaled to the whole layer"),
+        "seconds_scaled": {"gate": t_gate, "select": t_sel, "gather": t_gath, "attention": t_attn},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import learned_token_pruning_02_amd as tg
+    import workloads
+    from learned_token_pruning_02_amd.path import AttentionStack, GatedLayer
+
+    tg.lib()  # fail loudly when the library is missing
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    w = workloads.get(args.workload, args.seed)
+    sh = w.shape
+    dev = torch.device("cuda:0")
+
+    gi = workloads.gate_inputs(w, seed=args.seed)
+    ai = workloads.attn_inputs(w, seed=args.seed)
+    g = {k: v.to(dev) for k, v in gi.items()}
+    a = {k: v.to(dev) for k, v in ai.items()}
+    layer = GatedLayer(w.total_tokens, sh.d_model, sh.n_q_heads, sh.d_head, w.seq_len, w.q_len,
+                       w.budget, sh.dtype, device=dev)
+    stack = None
+    if w.stack_layers:
+        stack = AttentionStack(layer.Kt, sh.d_model, sh.n_q_heads, sh.n_kv_heads, sh.d_head,
+                               sh.dtype, device=dev)
+        sw = [{k: v.to(dev) for k, v in L.items()} for L in workloads.stack_weights(w, args.seed)]
+        x_stack = torch.empty_like(layer.hidden_kept)
+
+    names = ["gate", "select", "gather", "attention"] + (["stack"] if stack else [])
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        layer.gate(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"])
+        if ev is not None:
+            ev[1].record()
+        layer.select()
+        if ev is not None:
+            ev[2].record()
+        layer.gather(g["hidden"])
+        if ev is not None:
+            ev[3].record()
+        layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"])
+        if ev is not None:
+            ev[4].record()
+        if stack is not None:
+            x_stack.copy_(layer.hidden_kept)
+            stack(x_stack, layer.s_kept, layer.cu_kept, sw)
+            if ev is not None:
+                ev[5].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per = {n: 0.0 for n in names}
+    for e in evs:
+        for j, n in enumerate(names):
+            per[n] += e[j].elapsed_time(e[j + 1])
+    per = {n: v / args.steps for n, v in per.items()}      # ms per launch
+    gpu_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    kept_per_req = [layer.cu_kept[i + 1] - layer.cu_kept[i] for i in range(w.batch)]
+    alg = algorithmic(w, kept_per_req)
+    kernels = {}
+    for n in ["gate", "select", "gather", "attention"]:
+        t = per[n] * 1e-3
+        kernels[n] = {"ms": per[n], "GB/s": alg[n]["bytes"] / t / 1e9,
+                      "hbm_frac": alg[n]["bytes"] / t / 1e9 / HBM_PEAK_GBS,
+                      "TFLOP/s": alg[n]["flops"] / t / 1e12}
+    bf16 = sh.dtype == torch.bfloat16
+    mfma_peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
+    kernels["attention"]["mfma_frac"] = kernels["attention"]["TFLOP/s"] / mfma_peak
+    kernels["gate"]["mfma_frac"] = kernels["gate"]["TFLOP/s"] / mfma_peak
+    if stack is not None:
+        kernels["stack"] = {"ms": per["stack"]}
+
+    dominant = max(["gate", "select", "gather", "attention"], key=lambda n: per[n])
+    if dominant == "attention":
+        roof = {"bound": "mfma" if bf16 else "alu", "achieved": kernels["attention"]["TFLOP/s"],
+                "peak": mfma_peak, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dominant
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        s_cpu = layer.scores.cpu()
+        kept_cpu = layer.kept.cpu()
+        cpu = cpu_baseline(w, gi, ai, s_cpu, kept_cpu, layer.cu_kept)
+
+    line = {
+        "metric": "gated-prefill tokens/s per layer",
+        "value": w.total_tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded; random-init gate and projection weights)",
+        "config": {"workload": w.name, "tokens": w.total_tokens, "kept": layer.Kt,
+                   "requests": w.batch, "d_model": sh.d_model, "heads_q": sh.n_q_heads,
+                   "heads_kv": sh.n_kv_heads, "d_head": sh.d_head, "d_gate": sh.d_gate,
+                   "stack_layers": w.stack_layers},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "gpu_ms_per_step": gpu_ms,
+    }
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump(line, f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

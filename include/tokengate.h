@@ -1,0 +1,198 @@
+/*
+ * tokengate.h -- C ABI of the TokenGate pruned-prefill hot path on MI355X (gfx950).
+ *
+ * TokenGate (MarkTechPost article, French rendering on spke.com, section
+ * "Comment TokenGate a-t-il appris le fonctionnement de la réduction des
+ * tokens ?") splits prefill in three phases: layers up to the gate layer L see
+ * all N tokens; at L a small MLP scores every token from its post-attention
+ * residual and a top-K selector keeps the best ones; layers above L see only
+ * the K kept tokens and never create KV for the pruned ones.  Only the
+ * document part of the prompt may be pruned, the question never is.  In the
+ * layers above L the score of each kept token is a bias on the attention
+ * logits, with a learnable per-head gain and temperature (same page, "Qu'est-ce
+ * que l'attention gérée par des tokens ?").  `generate` takes a
+ * max_kept_prefill_tokens budget (same page, "Comment déployer TokenGate ?").
+ *
+ * The four calls below are those steps.  The pages sketch the bias only; the
+ * attention here computes, for query row i and key j <= i of one request,
+ *     l_ij = tau_h * (q_i . k_j) / sqrt(d_head) + g_h * s_j
+ * and softmax over j.
+ *
+ * Conventions shared by every call
+ *  - Tensors are DEVICE pointers owned by the caller, row-major, contiguous and
+ *    16-byte aligned.  Batch metadata (tg_batch, cu_kept_host) is HOST memory,
+ *    read during the call only.
+ *  - The library never allocates, frees or synchronises.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the default stream).  Pointers must stay
+ *    valid until that work completes.
+ *  - Output buffers must not overlap input buffers (TG_ERR_ALIAS where the
+ *    extents are known on the host).
+ *  - Every argument is validated on the host before anything is launched; on
+ *    an error status nothing is launched and no output is written.
+ *    TG_ERR_LAUNCH reports a launch failure returned by the HIP runtime.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - No exceptions cross the ABI.  The library keeps no mutable global state:
+ *    calls on different streams are independent.
+ *  - Scores, gains and temperatures are always fp32.  Hidden states and
+ *    q/k/v/out are fp32 (TG_F32) or bf16 (TG_BF16); bf16 results are rounded
+ *    to nearest even from fp32 accumulators.
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_ABI_VERSION 1
+
+/* Largest number of requests in one packed batch. */
+#define TG_MAX_BATCH 64
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_NULL_PTR = 1,     /* a required pointer is NULL                         */
+    TG_ERR_BAD_SHAPE = 2,    /* a size is negative, zero where it may not be, or
+                                sizes disagree with each other                      */
+    TG_ERR_BAD_BUDGET = 3,   /* a request violates N_b >= 1, 0 <= q_b <= N_b,
+                                budget_b >= 1 or q_b <= min(budget_b, N_b)          */
+    TG_ERR_BAD_DTYPE = 4,    /* dtype is not TG_F32 / TG_BF16                       */
+    TG_ERR_UNSUPPORTED = 5,  /* valid but outside what the kernels implement        */
+    TG_ERR_ALIGNMENT = 6,    /* a tensor pointer is not 16-byte aligned             */
+    TG_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than tg_plan reported     */
+    TG_ERR_LAUNCH = 8,       /* the HIP runtime rejected a launch                   */
+    TG_ERR_ALIAS = 9         /* an output buffer overlaps an input buffer           */
+} tg_status;
+
+typedef enum { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
+
+/* A packed batch of B requests laid out back to back in the token dimension.
+ * Request b owns global tokens [cu_seqlens[b], cu_seqlens[b+1]); its last
+ * q_len[b] tokens are the question (never pruned), the rest is the document.
+ * budget[b] is max_kept_prefill_tokens for that request and COUNTS the
+ * question: min(budget[b], seq_len[b]) tokens are kept.  All three arrays are
+ * host memory of length `batch` (1 <= batch <= TG_MAX_BATCH). */
+typedef struct {
+    int32_t batch;
+    const int32_t *seq_len;
+    const int32_t *q_len;
+    const int32_t *budget;
+} tg_batch;
+
+/* Human-readable name of a status code (never NULL). */
+const char *tg_status_str(int status);
+
+/* TG_ABI_VERSION of the loaded library. */
+int tg_abi_version(void);
+
+/*
+ * tg_plan -- host only, launches nothing.
+ * Validates `b` and writes cu_seqlens[B+1] and cu_kept[B+1] (exclusive prefix
+ * sums of seq_len and of K_b = min(budget_b, seq_len_b)) and the workspace
+ * size tg_topk_select needs.  Any output pointer may be NULL to skip it.
+ * Errors: TG_ERR_NULL_PTR (b or its arrays), TG_ERR_BAD_SHAPE (batch outside
+ * [1, TG_MAX_BATCH], total tokens >= 2^31), TG_ERR_BAD_BUDGET.
+ */
+tg_status tg_plan(const tg_batch *b, int32_t *cu_seqlens, int32_t *cu_kept,
+                  size_t *topk_ws_bytes);
+
+/*
+ * tg_gate_score -- the gate MLP (spke.com page, three-phase list, second
+ * bullet: an MLP scores every token from its post-attention residual at L).
+ *     s_t = w2 . GELU(W1 x_t + b1) + b2,   GELU(z) = z * Phi(z) (erf form)
+ * hidden : [T][d_model] in dt            (the layer-L post-attention residual)
+ * w1     : [d_gate][d_model] in dt       (torch Linear layout)
+ * b1     : [d_gate] in dt, or NULL for no bias
+ * w2     : [d_gate] in dt
+ * b2     : [1] in dt (device scalar), or NULL for no bias
+ * scores : [T] fp32 output, one score per token, question tokens included.
+ * Supported: TG_F32 with d_model % 4 == 0 and d_gate <= 1024;
+ *            TG_BF16 with d_model % 64 == 0 and d_gate in {64, 128, 256}.
+ * T == 0 is a no-op.  Errors: TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE,
+ * TG_ERR_BAD_DTYPE, TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT, TG_ERR_LAUNCH.
+ */
+tg_status tg_gate_score(tg_dtype dt, const void *hidden, int64_t T, int32_t d_model,
+                        const void *w1, const void *b1, const void *w2, const void *b2,
+                        int32_t d_gate, float *scores, hipStream_t stream);
+
+/*
+ * tg_topk_select -- the top-K selector (spke.com page, second bullet; the
+ * question is never pruned; the budget is max_kept_prefill_tokens).
+ * For each request: if budget_b >= N_b every token is kept; otherwise the
+ * K_b - q_b best DOCUMENT tokens under the total order
+ *     (score descending, token index ascending)
+ * are kept together with the whole question tail.  For ordering, -0 equals +0
+ * and NaN ranks below -inf.
+ * scores      : [T] fp32 (T = sum of seq_len), device
+ * kept_idx    : [sum K_b] int32 output: global token ids, ascending within each
+ *               request, requests in batch order (request b fills
+ *               [cu_kept[b], cu_kept[b+1]))
+ * cu_kept_dev : [B+1] int32 output copy of cu_kept, or NULL
+ * ws/ws_bytes : device workspace of at least tg_plan's topk_ws_bytes (may be
+ *               NULL when that size is 0)
+ * Errors: those of tg_plan, TG_ERR_NULL_PTR, TG_ERR_WORKSPACE, TG_ERR_LAUNCH.
+ */
+tg_status tg_topk_select(const float *scores, const tg_batch *b, int32_t *kept_idx,
+                         int32_t *cu_kept_dev, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * tg_gather_compact -- compaction (spke.com page, third bullet: layers above L
+ * process only the kept tokens).
+ *     hidden_kept[r] = hidden[kept_idx[r]]   (bit for bit)
+ *     scores_kept[r] = scores[kept_idx[r]]   (when both pointers are given)
+ * hidden      : [T][d_model] in dt;  kept_idx : [Kt] int32 in [0, T)
+ * hidden_kept : [Kt][d_model] in dt output
+ * scores, scores_kept : [T] / [Kt] fp32, both NULL or both non-NULL
+ * An index outside [0, T) is not dereferenced: its output row is left as is
+ * and its score is set to NaN.
+ * Supported: d_model * sizeof(dt) % 16 == 0.  Kt == 0 is a no-op.
+ */
+tg_status tg_gather_compact(tg_dtype dt, const void *hidden, int64_t T, int32_t d_model,
+                            const float *scores, const int32_t *kept_idx, int64_t Kt,
+                            void *hidden_kept, float *scores_kept, hipStream_t stream);
+
+/*
+ * tg_gated_attn_prefill -- causal GQA token-gated attention over the kept
+ * tokens (spke.com page, "Qu'est-ce que l'attention gérée par des tokens ?").
+ * For request b (rows [cu_kept_host[b], cu_kept_host[b+1])), query head h,
+ * KV head h / (Hq / Hkv), local query row i and local key j <= i:
+ *     l_ij = temp[h] * (q_i . k_j) / sqrt(d_head) + gain[h] * s_kept[j]
+ *     out_i = sum_j softmax_j(l_ij) v_j,   lse_i = ln sum_j exp(l_ij)
+ * Requests never attend to each other.
+ * q   : [Kt][Hq][d_head] in dt       k, v : [Kt][Hkv][d_head] in dt
+ * s_kept : [Kt] fp32                 gain, temp : [Hq] fp32
+ * cu_kept_host : [batch+1] HOST int32, cu_kept_host[0] == 0, non-decreasing
+ * out : [Kt][Hq][d_head] in dt output
+ * lse : [Hq][Kt] fp32 output, or NULL
+ * Supported: d_head in {64, 128}, Hq % Hkv == 0, 1 <= batch <= TG_MAX_BATCH.
+ * Only K/V rows of kept tokens exist: nothing of size N is read or written.
+ */
+tg_status tg_gated_attn_prefill(tg_dtype dt, const void *q, const void *k, const void *v,
+                                const float *s_kept, const float *gain, const float *temp,
+                                const int32_t *cu_kept_host, int32_t batch, int32_t Hq,
+                                int32_t Hkv, int32_t d_head, void *out, float *lse,
+                                hipStream_t stream);
+
+/*
+ * tg_linear -- auxiliary projection for layers above the gate, run on the
+ * kept rows only (spke.com page, third bullet).
+ *     y[M][N] = x[M][K] . w[N][K]^T            (accumulate == 0)
+ *     y[M][N] = y[M][N] + x[M][K] . w[N][K]^T  (accumulate != 0; residual add)
+ * fp32 accumulation, one rounding to dt at the store.
+ * Supported: TG_BF16 with N % 64 == 0 and K % 64 == 0; TG_F32 any N, K with
+ * K % 4 == 0.  M == 0 is a no-op.
+ */
+tg_status tg_linear(tg_dtype dt, const void *x, const void *w, void *y, int64_t M,
+                    int32_t N, int32_t K, int accumulate, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

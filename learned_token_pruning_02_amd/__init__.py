@@ -1,0 +1,259 @@
+"""TokenGate pruned-prefill hot path on MI355X: Python binding of libtokengate.so.
+
+The binding only marshals arguments: it checks that tensors live on the GPU
+with the right dtype and layout, allocates outputs with ``torch.empty`` when
+the caller gives none, and calls the C ABI (``include/tokengate.h``) on the
+current HIP stream.  Every step runs in the library's gfx950 kernels; there is
+no fallback of any kind.  If the library is not built, every call raises.
+
+Steps (MarkTechPost article on TokenGate, French rendering on spke.com):
+  tg_gate_score          gate MLP score per token          (three-phase list, 2nd bullet)
+  tg_topk_select         top-K of the document + question  (same bullet; question never pruned)
+  tg_gather_compact      kept rows compacted               (3rd bullet)
+  tg_gated_attn_prefill  causal GQA attention with a per-key score bias, per-head gain and
+                         temperature                       ("attention gérée par des tokens")
+  tg_linear              projection on the kept rows (layers above the gate)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple
+
+__all__ = [
+    "TokenGateError",
+    "lib",
+    "library_path",
+    "TG_F32",
+    "TG_BF16",
+    "TG_MAX_BATCH",
+    "tg_plan",
+    "tg_gate_score",
+    "tg_topk_select",
+    "tg_gather_compact",
+    "tg_gated_attn_prefill",
+    "tg_linear",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libtokengate.so")
+
+TG_F32 = 0
+TG_BF16 = 1
+TG_MAX_BATCH = 64
+
+STATUS = {
+    0: "TG_OK", 1: "TG_ERR_NULL_PTR", 2: "TG_ERR_BAD_SHAPE", 3: "TG_ERR_BAD_BUDGET",
+    4: "TG_ERR_BAD_DTYPE", 5: "TG_ERR_UNSUPPORTED", 6: "TG_ERR_ALIGNMENT",
+    7: "TG_ERR_WORKSPACE", 8: "TG_ERR_LAUNCH", 9: "TG_ERR_ALIAS",
+}
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+class _Batch(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seq_len", ctypes.POINTER(ctypes.c_int32)),
+        ("q_len", ctypes.POINTER(ctypes.c_int32)),
+        ("budget", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtokengate.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m learned_token_pruning_02_amd.build` "
+            "(there is no fallback implementation)")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    p_i32 = ctypes.POINTER(ctypes.c_int32)
+    L.tg_status_str.restype = ctypes.c_char_p
+    L.tg_status_str.argtypes = [ctypes.c_int]
+    L.tg_abi_version.restype = ctypes.c_int
+    L.tg_abi_version.argtypes = []
+    L.tg_plan.restype = ctypes.c_int
+    L.tg_plan.argtypes = [ctypes.POINTER(_Batch), p_i32, p_i32, ctypes.POINTER(sz)]
+    L.tg_gate_score.restype = ctypes.c_int
+    L.tg_gate_score.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp, vp, vp, i32, vp, vp]
+    L.tg_topk_select.restype = ctypes.c_int
+    L.tg_topk_select.argtypes = [vp, ctypes.POINTER(_Batch), vp, vp, vp, sz, vp]
+    L.tg_gather_compact.restype = ctypes.c_int
+    L.tg_gather_compact.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp, i64, vp, vp, vp]
+    L.tg_gated_attn_prefill.restype = ctypes.c_int
+    L.tg_gated_attn_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, p_i32, i32, i32,
+                                        i32, i32, vp, vp, vp]
+    L.tg_linear.restype = ctypes.c_int
+    L.tg_linear.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
+    _lib = L
+    return L
+
+
+# ------------------------------------------------------------- helpers ----
+def _torch():
+    import torch
+    return torch
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise TokenGateError(fn, status)
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return TG_F32
+    if t.dtype == torch.bfloat16:
+        return TG_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _dev(t, name: str, dtype=None):
+    """Device pointer of a contiguous GPU tensor (None passes through)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32_array(vals: Sequence[int]):
+    arr = (ctypes.c_int32 * max(1, len(vals)))(*[int(v) for v in vals])
+    return arr
+
+
+def _batch(seq_len, q_len, budget):
+    n = len(seq_len)
+    if not (len(q_len) == len(budget) == n):
+        raise ValueError("seq_len, q_len and budget must have the same length")
+    s, q, b = _i32_array(seq_len), _i32_array(q_len), _i32_array(budget)
+    bt = _Batch(n, ctypes.cast(s, ctypes.POINTER(ctypes.c_int32)),
+                ctypes.cast(q, ctypes.POINTER(ctypes.c_int32)),
+                ctypes.cast(b, ctypes.POINTER(ctypes.c_int32)))
+    return bt, (s, q, b)
+
+
+# ----------------------------------------------------------------- API ----
+def tg_plan(seq_len: Sequence[int], q_len: Sequence[int], budget: Sequence[int]
+            ) -> Tuple[List[int], List[int], int]:
+    """Host-only plan: (cu_seqlens, cu_kept, select workspace bytes)."""
+    L = lib()
+    bt, keep = _batch(seq_len, q_len, budget)
+    n = len(seq_len)
+    cu_s = (ctypes.c_int32 * (n + 1))()
+    cu_k = (ctypes.c_int32 * (n + 1))()
+    ws = ctypes.c_size_t(0)
+    _check("tg_plan", L.tg_plan(ctypes.byref(bt), cu_s, cu_k, ctypes.byref(ws)))
+    return list(cu_s), list(cu_k), int(ws.value)
+
+
+def tg_gate_score(hidden, w1, b1, w2, b2, scores=None, stream=None):
+    """scores[T] (fp32) = w2 . GELU(W1 x_t + b1) + b2 for every row x_t of hidden."""
+    torch = _torch()
+    T, d = hidden.shape
+    dg = w1.shape[0]
+    dt = _dt(hidden)
+    if scores is None:
+        scores = torch.empty(T, dtype=torch.float32, device=hidden.device)
+    _check("tg_gate_score", lib().tg_gate_score(
+        dt, _dev(hidden, "hidden"), T, d, _dev(w1, "w1", hidden.dtype),
+        _dev(b1, "b1", hidden.dtype), _dev(w2, "w2", hidden.dtype), _dev(b2, "b2", hidden.dtype),
+        dg, _dev(scores, "scores", torch.float32), _stream(stream)))
+    return scores
+
+
+def tg_topk_select(scores, seq_len: Sequence[int], q_len: Sequence[int], budget: Sequence[int],
+                   kept_idx=None, cu_kept_dev=None, workspace=None, stream=None):
+    """Kept global token ids (int32, ascending per request) and the host cu_kept list."""
+    torch = _torch()
+    cu_s, cu_k, ws_bytes = tg_plan(seq_len, q_len, budget)
+    if kept_idx is None:
+        kept_idx = torch.empty(cu_k[-1], dtype=torch.int32, device=scores.device)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
+    bt, keep = _batch(seq_len, q_len, budget)
+    _check("tg_topk_select", lib().tg_topk_select(
+        _dev(scores, "scores", torch.float32), ctypes.byref(bt),
+        _dev(kept_idx, "kept_idx", torch.int32), _dev(cu_kept_dev, "cu_kept_dev", torch.int32),
+        _dev(workspace, "workspace"), ws_bytes if workspace is None else workspace.numel(),
+        _stream(stream)))
+    return kept_idx, cu_k
+
+
+def tg_gather_compact(hidden, kept_idx, scores=None, hidden_kept=None, scores_kept=None,
+                      stream=None):
+    """hidden_kept[r] = hidden[kept_idx[r]]; scores_kept[r] = scores[kept_idx[r]]."""
+    torch = _torch()
+    T, d = hidden.shape
+    Kt = kept_idx.numel()
+    if hidden_kept is None:
+        hidden_kept = torch.empty(Kt, d, dtype=hidden.dtype, device=hidden.device)
+    if scores is not None and scores_kept is None:
+        scores_kept = torch.empty(Kt, dtype=torch.float32, device=hidden.device)
+    _check("tg_gather_compact", lib().tg_gather_compact(
+        _dt(hidden), _dev(hidden, "hidden"), T, d, _dev(scores, "scores", torch.float32),
+        _dev(kept_idx, "kept_idx", torch.int32), Kt, _dev(hidden_kept, "hidden_kept", hidden.dtype),
+        _dev(scores_kept, "scores_kept", torch.float32), _stream(stream)))
+    return hidden_kept, scores_kept
+
+
+def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], out=None,
+                          lse=None, want_lse: bool = False, stream=None):
+    """Causal GQA token-gated attention over packed kept rows; returns (out, lse or None)."""
+    torch = _torch()
+    Kt, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(Hq, Kt, dtype=torch.float32, device=q.device)
+    cu = _i32_array(cu_kept)
+    _check("tg_gated_attn_prefill", lib().tg_gated_attn_prefill(
+        _dt(q), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(s_kept, "s_kept", torch.float32), _dev(gain, "gain", torch.float32),
+        _dev(temp, "temp", torch.float32), ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
+        len(cu_kept) - 1, Hq, Hkv, dh, _dev(out, "out", q.dtype),
+        _dev(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse
+
+
+def tg_linear(x, w, y=None, accumulate: bool = False, stream=None):
+    """y = x w^T, or y += x w^T with accumulate=True (w in Linear layout [N][K])."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs y")
+        y = torch.empty(M, N, dtype=x.dtype, device=x.device)
+    _check("tg_linear", lib().tg_linear(
+        _dt(x), _dev(x, "x"), _dev(w, "w", x.dtype), _dev(y, "y", x.dtype), M, N, K,
+        1 if accumulate else 0, _stream(stream)))
+    return y

@@ -1,0 +1,400 @@
+// Token-gated causal GQA attention over the kept tokens (spke.com page,
+// "Qu'est-ce que l'attention gérée par des tokens ?": each kept token's gate
+// score is a bias on the attention logits, with a per-head gain and a
+// per-head temperature).  For query row i, key j <= i of one request:
+//     l_ij = temp[h] * (q_i . k_j) / sqrt(d_head) + gain[h] * s_j
+//
+// bf16 path, flash style (exact softmax computed online, never materialising
+// the score matrix): a workgroup of 4 waves owns one KV head, HPB query heads
+// that share it and BQ = 128/HPB query rows of one request.  Each wave owns
+// 32 query rows of one head.  Per 64-key tile:
+//   S^T[key][query] = K . Q^T with the 32x32x16 bf16 MFMA: K fragments from
+//     LDS (A operand), Q fragments resident in registers (B operand), so each
+//     lane holds all scores of ONE query row and the row max / row sum need
+//     only one exchange with the partner lane half;
+//   scale and bias are one FMA in the exp2 domain: x = c1*S + g2*s_j with
+//     c1 = temp*log2(e)/sqrt(d), g2 = gain*log2(e);
+//   O^T[dh][query] += V^T . P^T: V is stored transposed in LDS (A operand) and
+//     the probabilities, converted to bf16, are fed straight from the S
+//     registers as the B operand, again one query per lane, so the online
+//     rescale of O needs no data exchange.
+// Only the tiles on the diagonal (or past the end of the request) are masked.
+// K/V tiles are double buffered: the next tile is fetched into registers
+// while the current one is consumed.  Heavy query tiles (many keys) are
+// dispatched first and consecutive workgroup ids cycle over the KV heads, so
+// the 8 XCDs each keep one head's K/V in their own L2.
+#include "tg_device.h"
+#include "tg_kernels.h"
+
+namespace tg {
+
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- fp32 ----
+template <int DH>
+__global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__ q,
+                                                       const float* __restrict__ k,
+                                                       const float* __restrict__ v,
+                                                       const float* __restrict__ s,
+                                                       const float* __restrict__ gain,
+                                                       const float* __restrict__ temp,
+                                                       AttnShape sh, float* __restrict__ out,
+                                                       float* __restrict__ lse) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= sh.Kt * sh.Hq) return;
+    const int64_t r = gid / sh.Hq;
+    const int h = (int)(gid % sh.Hq);
+    int b = 0;
+    while (b + 1 < sh.batch && sh.cu[b + 1] <= r) ++b;
+    const int64_t lo = sh.cu[b];
+    const int kvh = h / (sh.Hq / sh.Hkv);
+    const float c1 = temp[h] / sqrtf((float)DH);
+    const float g = gain[h];
+    const float* qr = q + (r * sh.Hq + h) * DH;
+    float qv[DH], acc[DH];
+#pragma unroll
+    for (int e = 0; e < DH; ++e) {
+        qv[e] = qr[e];
+        acc[e] = 0.f;
+    }
+    float m = -INFINITY, l = 0.f;
+    for (int64_t j = lo; j <= r; ++j) {
+        const float* kr = k + (j * sh.Hkv + kvh) * DH;
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < DH; ++e) dot = fmaf(qv[e], kr[e], dot);
+        const float x = c1 * dot + g * s[j];
+        const float mn = fmaxf(m, x);
+        const float sc = expf(m - mn);
+        const float p = expf(x - mn);
+        l = l * sc + p;
+        const float* vr = v + (j * sh.Hkv + kvh) * DH;
+#pragma unroll
+        for (int e = 0; e < DH; ++e) acc[e] = fmaf(acc[e], sc, p * vr[e]);
+        m = mn;
+    }
+    float* orow = out + (r * sh.Hq + h) * DH;
+#pragma unroll
+    for (int e = 0; e < DH; ++e) orow[e] = acc[e] / l;
+    if (lse != nullptr) lse[(int64_t)h * sh.Kt + r] = m + logf(l);
+}
+
+// ---------------------------------------------------------------- bf16 ----
+struct AttnArgs {
+    const bf16* q;
+    const bf16* k;
+    const bf16* v;
+    const float* s;
+    const float* gain;
+    const float* temp;
+    bf16* out;
+    float* lse;
+    int64_t Kt;
+    int32_t Hq, Hkv, n_hg, batch, max_tiles;
+    int32_t cu[TG_MAX_BATCH + 1];
+    int32_t ntiles[TG_MAX_BATCH];
+};
+
+constexpr int KVT = 64;          // keys per tile
+constexpr int VT_STRIDE = KVT + 8;  // LDS row stride of V^T (bf16 elements)
+
+// Number of query tiles whose local index is >= t.
+__device__ __forceinline__ int tiles_at_or_above(const AttnArgs& a, int t) {
+    int c = 0;
+    for (int b = 0; b < a.batch; ++b) c += max(0, a.ntiles[b] - t);
+    return c;
+}
+
+template <int DH, int HPB>
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
+    constexpr int WPH = 4 / HPB;       // waves per head
+    constexpr int BQ = 32 * WPH;       // query rows per head per workgroup
+    constexpr int KS = DH + 8;         // LDS row stride of K (bf16 elements)
+    constexpr int KU = KVT * DH / 8 / 256;  // 16-byte K units per thread per tile
+    constexpr int VU = (KVT / 4) * (DH / 8);  // V units (4 keys x 8 dh) per tile
+    constexpr int NKK = DH / 16;       // k steps of the QK^T product
+    constexpr int NMD = DH / 32;       // 32-row dh tiles of O^T
+
+    __shared__ __attribute__((aligned(16))) bf16 Ks[2][KVT * KS];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * VT_STRIDE];
+    __shared__ __attribute__((aligned(16))) float Ss[2][KVT];
+
+    const int tid = threadIdx.x;
+    const int lane = lane_id();
+    const int w = tid / WAVE;
+    const int hh = lane / 32;
+    const int l32 = lane % 32;
+
+    // ---- which (request, query tile, head group) this workgroup owns ------
+    const int hg = blockIdx.x % a.n_hg;
+    const int u = blockIdx.x / a.n_hg;
+    int b, t;
+    if (a.batch == 1) {
+        b = 0;
+        t = a.ntiles[0] - 1 - u;
+    } else {
+        int lo = 0, hi = a.max_tiles - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (tiles_at_or_above(a, mid) > u) lo = mid;
+            else hi = mid - 1;
+        }
+        t = lo;
+        int j = u - tiles_at_or_above(a, t + 1);
+        for (b = 0; b < a.batch; ++b) {
+            if (a.ntiles[b] > t) {
+                if (j == 0) break;
+                --j;
+            }
+        }
+        if (b >= a.batch) return;  // unreachable for a consistent tile count
+    }
+    const int64_t rbase = a.cu[b];
+    const int n = a.cu[b + 1] - a.cu[b];
+    const int q0 = t * BQ;
+    const int kend = min(q0 + BQ, n);
+    const int nkv = (kend + KVT - 1) / KVT;
+    const int group = a.Hq / a.Hkv;
+    const int kvh = (hg * HPB) / group;
+    const int h = hg * HPB + w / WPH;
+    const int qmin = q0 + 32 * (w % WPH);  // first query row of this wave
+    const int qi = qmin + l32;               // this lane's query row
+    const bool qvalid = qi < n;
+
+    // ---- resident Q fragments (B operand of S^T = K Q^T) ----------------
+    bf16x8 qf[NKK];
+    {
+        const bf16* qp = a.q + ((rbase + (qvalid ? qi : 0)) * a.Hq + h) * DH + (DH / 2) * hh;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            uint4 val = qvalid ? *reinterpret_cast<const uint4*>(qp + 8 * kk) : make_uint4(0, 0, 0, 0);
+            qf[kk] = as_bf16x8(val);
+        }
+    }
+    const float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
+    const float g2 = a.gain[h] * LOG2E;
+
+    // ---- K/V/s tile staging ------------------------------------------------
+    uint4 kreg[KU];
+    uint4 vreg[4];
+    float sreg = 0.f;
+    auto load_tile = [&](int jt) {
+        const int j0 = jt * KVT;
+#pragma unroll
+        for (int i = 0; i < KU; ++i) {
+            const int uu = tid + i * 256;
+            const int row = uu / (DH / 8), c = uu % (DH / 8);
+            const int key = min(j0 + row, n - 1);
+            kreg[i] = *reinterpret_cast<const uint4*>(a.k + ((rbase + key) * a.Hkv + kvh) * DH + 8 * c);
+        }
+        if (tid < VU) {
+            const int kg = tid % (KVT / 4), dg = tid / (KVT / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = min(j0 + 4 * kg + i, n - 1);
+                vreg[i] = *reinterpret_cast<const uint4*>(a.v + ((rbase + key) * a.Hkv + kvh) * DH + 8 * dg);
+            }
+        }
+        if (tid < KVT) sreg = a.s[rbase + min(j0 + tid, n - 1)];
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KU; ++i) {
+            const int uu = tid + i * 256;
+            const int row = uu / (DH / 8), c = uu % (DH / 8);
+            *reinterpret_cast<uint4*>(&Ks[buf][row * KS + 8 * c]) = kreg[i];
+        }
+        if (tid < VU) {
+            const int kg = tid % (KVT / 4), dg = tid / (KVT / 4);
+            const uint16_t* r0 = reinterpret_cast<const uint16_t*>(&vreg[0]);
+            const uint16_t* r1 = reinterpret_cast<const uint16_t*>(&vreg[1]);
+            const uint16_t* r2 = reinterpret_cast<const uint16_t*>(&vreg[2]);
+            const uint16_t* r3 = reinterpret_cast<const uint16_t*>(&vreg[3]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                uint2 pk;
+                pk.x = (uint32_t)r0[e] | ((uint32_t)r1[e] << 16);
+                pk.y = (uint32_t)r2[e] | ((uint32_t)r3[e] << 16);
+                *reinterpret_cast<uint2*>(&Vt[buf][(8 * dg + e) * VT_STRIDE + 4 * kg]) = pk;
+            }
+        }
+        if (tid < KVT) Ss[buf][tid] = sreg;
+    };
+
+    f32x16 o[NMD];
+#pragma unroll
+    for (int md = 0; md < NMD; ++md)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[md][r] = 0.f;
+    float m = -INFINITY, lpart = 0.f;
+
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int jt = 0; jt < nkv; ++jt) {
+        const int buf = jt & 1;
+        const bool more = jt + 1 < nkv;
+        if (more) load_tile(jt + 1);
+
+        // S^T = K Q^T for 64 keys x 32 queries.
+        f32x16 sacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(
+                    &Ks[buf][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));
+                sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);
+            }
+        }
+
+        // Scale, bias, causal mask; lane holds keys 32mt + 8(r/4) + 4hh + r%4.
+        const int j0 = jt * KVT;
+        const bool need_mask = j0 + KVT - 1 > qmin;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int kl = 32 * mt + 8 * rq + 4 * hh;
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(&Ss[buf][kl]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x = fmaf(c1, sacc[mt][4 * rq + e], g2 * sv[e]);
+                    if (need_mask && j0 + kl + e > qi) x = -INFINITY;
+                    sacc[mt][4 * rq + e] = x;
+                    mx = fmaxf(mx, x);
+                }
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        const float m_new = fmaxf(m, mx);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        float psum = 0.f;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - m_use);
+                psum += p;
+                pf[kk][e] = to_bf16(p);
+            }
+        }
+        lpart = fmaf(lpart, alpha, psum);
+        m = m_new;
+#pragma unroll
+        for (int md = 0; md < NMD; ++md)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
+
+        // O^T += V^T P^T; the key order of the P fragment (registers
+        // 8(kk%2)..+7 of tile kk/2) is keys 16kk + 4hh + {0..3, 8..11}.
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const bf16* vrow = &Vt[buf][(32 * md + l32) * VT_STRIDE + 16 * kk + 4 * hh];
+                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+                const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                o[md] = mfma32(vf, pf[kk], o[md]);
+            }
+        }
+
+        if (more) store_tile(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- normalise and store ------------------------------------------------
+    const float l = lpart + __shfl_xor(lpart, 32, WAVE);
+    const float inv = 1.0f / l;
+    if (qvalid) {
+        bf16* op = a.out + ((rbase + qi) * a.Hq + h) * DH + 4 * hh;
+#pragma unroll
+        for (int md = 0; md < NMD; ++md) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                bf16x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ov[e] = to_bf16(o[md][4 * rq + e] * inv);
+                *reinterpret_cast<bf16x4*>(op + 32 * md + 8 * rq) = ov;
+            }
+        }
+        if (a.lse != nullptr && hh == 0) a.lse[(int64_t)h * a.Kt + rbase + qi] = (m + log2f(l)) * LN2;
+    }
+}
+
+template <int DH, int HPB>
+hipError_t launch_bf16(const AttnArgs& a, int total_tiles, hipStream_t st) {
+    const int blocks = total_tiles * a.n_hg;
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB>), dim3(blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const float* s,
+                           const float* gain, const float* temp, const AttnShape& sh, float* out,
+                           float* lse, hipStream_t st) {
+    const int64_t n = sh.Kt * sh.Hq;
+    const int blocks = (int)((n + 127) / 128);
+    if (sh.d_head == 64)
+        hipLaunchKernelGGL(attn_f32_kernel<64>, dim3(blocks), dim3(128), 0, st, q, k, v, s, gain,
+                           temp, sh, out, lse);
+    else
+        hipLaunchKernelGGL(attn_f32_kernel<128>, dim3(blocks), dim3(128), 0, st, q, k, v, s, gain,
+                           temp, sh, out, lse);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const float* s,
+                            const float* gain, const float* temp, const AttnShape& sh, void* out,
+                            float* lse, hipStream_t st) {
+    const int group = sh.Hq / sh.Hkv;
+    const int hpb = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+    const int bq = 128 / hpb;
+    AttnArgs a;
+    a.q = (const bf16*)q;
+    a.k = (const bf16*)k;
+    a.v = (const bf16*)v;
+    a.s = s;
+    a.gain = gain;
+    a.temp = temp;
+    a.out = (bf16*)out;
+    a.lse = lse;
+    a.Kt = sh.Kt;
+    a.Hq = sh.Hq;
+    a.Hkv = sh.Hkv;
+    a.n_hg = sh.Hq / hpb;
+    a.batch = sh.batch;
+    int total = 0, mx = 0;
+    for (int b = 0; b <= sh.batch; ++b) a.cu[b] = sh.cu[b];
+    for (int b = 0; b < sh.batch; ++b) {
+        const int nt = (sh.cu[b + 1] - sh.cu[b] + bq - 1) / bq;
+        a.ntiles[b] = nt;
+        total += nt;
+        mx = nt > mx ? nt : mx;
+    }
+    a.max_tiles = mx;
+    if (total == 0) return hipSuccess;
+    if (sh.d_head == 64) {
+        if (hpb == 4) return launch_bf16<64, 4>(a, total, st);
+        if (hpb == 2) return launch_bf16<64, 2>(a, total, st);
+        return launch_bf16<64, 1>(a, total, st);
+    }
+    if (hpb == 4) return launch_bf16<128, 4>(a, total, st);
+    if (hpb == 2) return launch_bf16<128, 2>(a, total, st);
+    return launch_bf16<128, 1>(a, total, st);
+}
+
+}  // namespace tg

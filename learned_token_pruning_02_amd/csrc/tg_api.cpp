@@ -1,0 +1,212 @@
+// C ABI of the TokenGate pruned-prefill library: argument validation on the
+// host, then one launch per call on the caller's stream.  Nothing here
+// allocates, frees or synchronises, and every check runs before any launch,
+// so an error status means nothing was enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "tg_kernels.h"
+#include "tokengate.h"
+
+namespace {
+
+constexpr int64_t I32_LIMIT = (int64_t)1 << 31;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (a == nullptr || b == nullptr || abytes <= 0 || bbytes <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+int64_t elt_bytes(tg_dtype dt) { return dt == TG_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == TG_F32 || dt == TG_BF16; }
+
+tg_status launched(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH; }
+
+// Shared by tg_plan and tg_topk_select.
+tg_status plan_batch(const tg_batch* b, tg::BatchArgs* out) {
+    if (b == nullptr) return TG_ERR_NULL_PTR;
+    if (b->batch < 1 || b->batch > TG_MAX_BATCH) return TG_ERR_BAD_SHAPE;
+    if (b->seq_len == nullptr || b->q_len == nullptr || b->budget == nullptr)
+        return TG_ERR_NULL_PTR;
+    int64_t tok = 0, kept = 0;
+    out->batch = b->batch;
+    out->cu_seq[0] = 0;
+    out->cu_kept[0] = 0;
+    for (int i = 0; i < b->batch; ++i) {
+        const int64_t n = b->seq_len[i], q = b->q_len[i], k = b->budget[i];
+        if (n < 1 || q < 0 || q > n || k < 1 || q > (k < n ? k : n)) return TG_ERR_BAD_BUDGET;
+        tok += n;
+        kept += k < n ? k : n;
+        if (tok >= I32_LIMIT) return TG_ERR_BAD_SHAPE;
+        out->cu_seq[i + 1] = (int32_t)tok;
+        out->cu_kept[i + 1] = (int32_t)kept;
+        out->q_len[i] = (int32_t)q;
+    }
+    return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tg_status_str(int status) {
+    switch (status) {
+        case TG_OK: return "TG_OK";
+        case TG_ERR_NULL_PTR: return "TG_ERR_NULL_PTR";
+        case TG_ERR_BAD_SHAPE: return "TG_ERR_BAD_SHAPE";
+        case TG_ERR_BAD_BUDGET: return "TG_ERR_BAD_BUDGET";
+        case TG_ERR_BAD_DTYPE: return "TG_ERR_BAD_DTYPE";
+        case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED";
+        case TG_ERR_ALIGNMENT: return "TG_ERR_ALIGNMENT";
+        case TG_ERR_WORKSPACE: return "TG_ERR_WORKSPACE";
+        case TG_ERR_LAUNCH: return "TG_ERR_LAUNCH";
+        case TG_ERR_ALIAS: return "TG_ERR_ALIAS";
+        default: return "TG_ERR_UNKNOWN";
+    }
+}
+
+int tg_abi_version(void) { return TG_ABI_VERSION; }
+
+tg_status tg_plan(const tg_batch* b, int32_t* cu_seqlens, int32_t* cu_kept,
+                  size_t* topk_ws_bytes) {
+    tg::BatchArgs a;
+    const tg_status st = plan_batch(b, &a);
+    if (st != TG_OK) return st;
+    if (cu_seqlens != nullptr) std::memcpy(cu_seqlens, a.cu_seq, sizeof(int32_t) * (a.batch + 1));
+    if (cu_kept != nullptr) std::memcpy(cu_kept, a.cu_kept, sizeof(int32_t) * (a.batch + 1));
+    if (topk_ws_bytes != nullptr) *topk_ws_bytes = 0;
+    return TG_OK;
+}
+
+tg_status tg_gate_score(tg_dtype dt, const void* hidden, int64_t T, int32_t d_model,
+                        const void* w1, const void* b1, const void* w2, const void* b2,
+                        int32_t d_gate, float* scores, hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (T < 0 || T >= I32_LIMIT || d_model < 1 || d_gate < 1) return TG_ERR_BAD_SHAPE;
+    if (hidden == nullptr || w1 == nullptr || w2 == nullptr || scores == nullptr)
+        return TG_ERR_NULL_PTR;
+    if (dt == TG_F32) {
+        if (d_model % 4 != 0 || d_gate > 1024 || d_model > 16384) return TG_ERR_UNSUPPORTED;
+    } else {
+        if (d_model % 64 != 0 || (d_gate != 64 && d_gate != 128 && d_gate != 256))
+            return TG_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(hidden) || !aligned16(w1) || !aligned4(scores)) return TG_ERR_ALIGNMENT;
+    const int64_t eb = elt_bytes(dt);
+    if (overlap(scores, T * 4, hidden, T * d_model * eb) ||
+        overlap(scores, T * 4, w1, (int64_t)d_gate * d_model * eb))
+        return TG_ERR_ALIAS;
+    if (T == 0) return TG_OK;
+    if (dt == TG_F32)
+        return launched(tg::launch_gate_f32((const float*)hidden, T, d_model, (const float*)w1,
+                                            (const float*)b1, (const float*)w2, (const float*)b2,
+                                            d_gate, scores, stream));
+    return launched(
+        tg::launch_gate_bf16(hidden, T, d_model, w1, b1, w2, b2, d_gate, scores, stream));
+}
+
+tg_status tg_topk_select(const float* scores, const tg_batch* b, int32_t* kept_idx,
+                         int32_t* cu_kept_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+    tg::BatchArgs a;
+    const tg_status st = plan_batch(b, &a);
+    if (st != TG_OK) return st;
+    if (scores == nullptr || kept_idx == nullptr) return TG_ERR_NULL_PTR;
+    (void)ws;
+    (void)ws_bytes;  // the current selector needs no workspace
+    if (!aligned4(scores) || !aligned4(kept_idx)) return TG_ERR_ALIGNMENT;
+    const int64_t T = a.cu_seq[a.batch], Kt = a.cu_kept[a.batch];
+    if (overlap(kept_idx, Kt * 4, scores, T * 4) ||
+        overlap(cu_kept_dev, (a.batch + 1) * 4, scores, T * 4) ||
+        overlap(cu_kept_dev, (a.batch + 1) * 4, kept_idx, Kt * 4))
+        return TG_ERR_ALIAS;
+    return launched(tg::launch_select(scores, a, kept_idx, cu_kept_dev, stream));
+}
+
+tg_status tg_gather_compact(tg_dtype dt, const void* hidden, int64_t T, int32_t d_model,
+                            const float* scores, const int32_t* kept_idx, int64_t Kt,
+                            void* hidden_kept, float* scores_kept, hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (T < 0 || Kt < 0 || d_model < 1 || T >= I32_LIMIT || Kt >= I32_LIMIT)
+        return TG_ERR_BAD_SHAPE;
+    if (hidden == nullptr || kept_idx == nullptr || hidden_kept == nullptr)
+        return TG_ERR_NULL_PTR;
+    if ((scores == nullptr) != (scores_kept == nullptr)) return TG_ERR_NULL_PTR;
+    const int64_t row_bytes = (int64_t)d_model * elt_bytes(dt);
+    if (row_bytes % 16 != 0) return TG_ERR_UNSUPPORTED;
+    if (!aligned16(hidden) || !aligned16(hidden_kept) || !aligned4(kept_idx)) return TG_ERR_ALIGNMENT;
+    if (scores != nullptr && (!aligned4(scores) || !aligned4(scores_kept))) return TG_ERR_ALIGNMENT;
+    if (overlap(hidden_kept, Kt * row_bytes, hidden, T * row_bytes) ||
+        overlap(hidden_kept, Kt * row_bytes, kept_idx, Kt * 4) ||
+        overlap(scores_kept, Kt * 4, scores, T * 4) ||
+        overlap(scores_kept, Kt * 4, hidden_kept, Kt * row_bytes))
+        return TG_ERR_ALIAS;
+    if (Kt == 0) return TG_OK;
+    return launched(tg::launch_gather(hidden, T, (int)row_bytes, scores, kept_idx, Kt, hidden_kept,
+                                      scores_kept, stream));
+}
+
+tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const void* v,
+                                const float* s_kept, const float* gain, const float* temp,
+                                const int32_t* cu_kept_host, int32_t batch, int32_t Hq,
+                                int32_t Hkv, int32_t d_head, void* out, float* lse,
+                                hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (q == nullptr || k == nullptr || v == nullptr || s_kept == nullptr || gain == nullptr ||
+        temp == nullptr || cu_kept_host == nullptr || out == nullptr)
+        return TG_ERR_NULL_PTR;
+    if (batch < 1 || batch > TG_MAX_BATCH || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return TG_ERR_BAD_SHAPE;
+    if (d_head != 64 && d_head != 128) return TG_ERR_UNSUPPORTED;
+    tg::AttnShape sh;
+    sh.batch = batch;
+    sh.Hq = Hq;
+    sh.Hkv = Hkv;
+    sh.d_head = d_head;
+    if (cu_kept_host[0] != 0) return TG_ERR_BAD_SHAPE;
+    for (int i = 0; i <= batch; ++i) {
+        if (i > 0 && cu_kept_host[i] < cu_kept_host[i - 1]) return TG_ERR_BAD_SHAPE;
+        sh.cu[i] = cu_kept_host[i];
+    }
+    sh.Kt = cu_kept_host[batch];
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(s_kept) ||
+        !aligned4(gain) || !aligned4(temp) || (lse != nullptr && !aligned4(lse)))
+        return TG_ERR_ALIGNMENT;
+    const int64_t eb = elt_bytes(dt);
+    const int64_t qb = sh.Kt * Hq * d_head * eb, kb = sh.Kt * Hkv * d_head * eb;
+    if (overlap(out, qb, q, qb) || overlap(out, qb, k, kb) || overlap(out, qb, v, kb) ||
+        overlap(out, qb, s_kept, sh.Kt * 4) || overlap(lse, (int64_t)Hq * sh.Kt * 4, out, qb) ||
+        overlap(lse, (int64_t)Hq * sh.Kt * 4, q, qb) || overlap(lse, (int64_t)Hq * sh.Kt * 4, k, kb) ||
+        overlap(lse, (int64_t)Hq * sh.Kt * 4, v, kb))
+        return TG_ERR_ALIAS;
+    if (sh.Kt == 0) return TG_OK;
+    if (dt == TG_F32)
+        return launched(tg::launch_attn_f32((const float*)q, (const float*)k, (const float*)v,
+                                            s_kept, gain, temp, sh, (float*)out, lse, stream));
+    return launched(tg::launch_attn_bf16(q, k, v, s_kept, gain, temp, sh, out, lse, stream));
+}
+
+tg_status tg_linear(tg_dtype dt, const void* x, const void* w, void* y, int64_t M, int32_t N,
+                    int32_t K, int accumulate, hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (M < 0 || N < 1 || K < 1 || M >= I32_LIMIT) return TG_ERR_BAD_SHAPE;
+    if (x == nullptr || w == nullptr || y == nullptr) return TG_ERR_NULL_PTR;
+    if (dt == TG_BF16 && (N % 64 != 0 || K % 64 != 0)) return TG_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TG_ERR_ALIGNMENT;
+    const int64_t eb = elt_bytes(dt);
+    if (overlap(y, M * N * eb, x, M * K * eb) || overlap(y, M * N * eb, w, (int64_t)N * K * eb))
+        return TG_ERR_ALIAS;
+    if (M == 0) return TG_OK;
+    if (dt == TG_F32)
+        return launched(tg::launch_linear_f32((const float*)x, (const float*)w, (float*)y, M, N, K,
+                                              accumulate, stream));
+    return launched(tg::launch_linear_bf16(x, w, y, M, N, K, accumulate, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal launcher interface between the C ABI (tg_api.cpp) and the kernels.
+// Arguments reaching these functions are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tokengate.h"
+
+namespace tg {
+
+// Per-request layout of a packed batch, passed to kernels by value.
+struct BatchArgs {
+    int32_t batch;
+    int32_t cu_seq[TG_MAX_BATCH + 1];   // token offsets of each request
+    int32_t cu_kept[TG_MAX_BATCH + 1];  // kept-row offsets of each request
+    int32_t q_len[TG_MAX_BATCH];        // question tail length of each request
+};
+
+hipError_t launch_gate_f32(const float* hidden, int64_t T, int d, const float* w1, const float* b1,
+                           const float* w2, const float* b2, int dg, float* scores, hipStream_t st);
+hipError_t launch_gate_bf16(const void* hidden, int64_t T, int d, const void* w1, const void* b1,
+                            const void* w2, const void* b2, int dg, float* scores, hipStream_t st);
+
+hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept, int32_t* cu_dev,
+                         hipStream_t st);
+
+hipError_t launch_gather(const void* hidden, int64_t T, int row_bytes, const float* scores,
+                         const int32_t* kept, int64_t Kt, void* hidden_kept, float* scores_kept,
+                         hipStream_t st);
+
+struct AttnShape {
+    int32_t batch;
+    int32_t Hq, Hkv, d_head;
+    int64_t Kt;
+    int32_t cu[TG_MAX_BATCH + 1];
+};
+
+hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const float* s,
+                           const float* gain, const float* temp, const AttnShape& sh, float* out,
+                           float* lse, hipStream_t st);
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const float* s,
+                            const float* gain, const float* temp, const AttnShape& sh, void* out,
+                            float* lse, hipStream_t st);
+
+hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M, int N, int K,
+                             int accumulate, hipStream_t st);
+hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
+                              int accumulate, hipStream_t st);
+
+}  // namespace tg

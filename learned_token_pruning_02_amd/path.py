@@ -1,0 +1,87 @@
+"""The pruned-prefill hot path composed from the C-ABI calls.
+
+One gated layer (MarkTechPost article on TokenGate, French rendering on
+spke.com, three-phase list): score every token with the gate MLP, keep the
+top-K document tokens plus the question, compact the kept rows, run token-gated
+attention over the kept tokens only.  ``GatedLayer`` owns its output buffers so
+repeated calls allocate nothing; every step is one library call on the current
+stream.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+from . import (tg_gate_score, tg_gated_attn_prefill, tg_gather_compact, tg_linear, tg_plan,
+               tg_topk_select)
+
+
+class GatedLayer:
+    """Buffers and calls of one gated layer for a fixed batch layout."""
+
+    def __init__(self, T: int, d_model: int, n_q_heads: int, d_head: int, seq_len: Sequence[int],
+                 q_len: Sequence[int], budget: Sequence[int], dtype: torch.dtype,
+                 device="cuda", want_lse: bool = False):
+        self.seq_len, self.q_len, self.budget = list(seq_len), list(q_len), list(budget)
+        self.cu_seq, self.cu_kept, ws = tg_plan(self.seq_len, self.q_len, self.budget)
+        if self.cu_seq[-1] != T:
+            raise ValueError("sum(seq_len) must equal the number of hidden rows")
+        Kt = self.cu_kept[-1]
+        self.Kt = Kt
+        self.scores = torch.empty(T, dtype=torch.float32, device=device)
+        self.kept = torch.empty(Kt, dtype=torch.int32, device=device)
+        self.cu_kept_dev = torch.empty(len(self.cu_kept), dtype=torch.int32, device=device)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device) if ws else None
+        self.hidden_kept = torch.empty(Kt, d_model, dtype=dtype, device=device)
+        self.s_kept = torch.empty(Kt, dtype=torch.float32, device=device)
+        self.out = torch.empty(Kt, n_q_heads, d_head, dtype=dtype, device=device)
+        self.lse = torch.empty(n_q_heads, Kt, dtype=torch.float32, device=device) if want_lse else None
+
+    def gate(self, hidden, w1, b1, w2, b2):
+        return tg_gate_score(hidden, w1, b1, w2, b2, scores=self.scores)
+
+    def select(self):
+        return tg_topk_select(self.scores, self.seq_len, self.q_len, self.budget,
+                              kept_idx=self.kept, cu_kept_dev=self.cu_kept_dev,
+                              workspace=self.workspace)[0]
+
+    def gather(self, hidden):
+        return tg_gather_compact(hidden, self.kept, self.scores, hidden_kept=self.hidden_kept,
+                                 scores_kept=self.s_kept)
+
+    def attend(self, q, k, v, gain, temp):
+        return tg_gated_attn_prefill(q, k, v, self.s_kept, gain, temp, self.cu_kept, out=self.out,
+                                     lse=self.lse)[0]
+
+    def __call__(self, hidden, w1, b1, w2, b2, q, k, v, gain, temp):
+        """gate -> select -> gather -> gated attention; returns the attention output."""
+        self.gate(hidden, w1, b1, w2, b2)
+        self.select()
+        self.gather(hidden)
+        return self.attend(q, k, v, gain, temp)
+
+
+class AttentionStack:
+    """Layers above the gate on the kept rows only: per layer q|k|v = x W^T,
+    token-gated attention, x += attn W_o^T (the residual updated in place)."""
+
+    def __init__(self, Kt: int, d_model: int, n_q_heads: int, n_kv_heads: int, d_head: int,
+                 dtype: torch.dtype, device="cuda"):
+        self.Hq, self.Hkv, self.dh = n_q_heads, n_kv_heads, d_head
+        self.q = torch.empty(Kt, n_q_heads * d_head, dtype=dtype, device=device)
+        self.k = torch.empty(Kt, n_kv_heads * d_head, dtype=dtype, device=device)
+        self.v = torch.empty(Kt, n_kv_heads * d_head, dtype=dtype, device=device)
+        self.attn = torch.empty(Kt, n_q_heads, d_head, dtype=dtype, device=device)
+
+    def __call__(self, x, s_kept, cu_kept: Sequence[int], layers: List[Dict[str, torch.Tensor]]):
+        Kt = x.shape[0]
+        for L in layers:
+            tg_linear(x, L["wq"], y=self.q)
+            tg_linear(x, L["wk"], y=self.k)
+            tg_linear(x, L["wv"], y=self.v)
+            tg_gated_attn_prefill(self.q.view(Kt, self.Hq, self.dh), self.k.view(Kt, self.Hkv, self.dh),
+                                  self.v.view(Kt, self.Hkv, self.dh), s_kept, L["gain"], L["temp"],
+                                  cu_kept, out=self.attn)
+            tg_linear(self.attn.view(Kt, self.Hq * self.dh), L["wo"], y=x, accumulate=True)
+        return x

@@ -1,0 +1,136 @@
+"""GPU parity of token-gated attention (and the projection GEMM) against the oracle.
+
+Attention outputs and log-sum-exps: within 1e-5 (fp32) or 2e-2 relative /
+1e-2 absolute (bf16) of the oracle's float64 result on the same stored
+inputs.  Full-size layers are checked on sampled rows.
+"""
+import zlib
+
+import pytest
+import torch
+
+import learned_token_pruning_02_amd as tg
+import oracle
+import workloads
+from parity_util import announce, assert_within, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(lens, Hq, Hkv, dh, dtype, seed, s_scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    Kt = sum(lens)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    q = torch.randn(Kt, Hq, dh, generator=g).to(dtype)
+    k = torch.randn(Kt, Hkv, dh, generator=g).to(dtype)
+    v = torch.randn(Kt, Hkv, dh, generator=g).to(dtype)
+    s = torch.randn(Kt, generator=g) * s_scale
+    gain = torch.rand(Hq, generator=g) + 0.5
+    temp = torch.rand(Hq, generator=g) * 0.4 + 0.8
+    return q, k, v, s, gain, temp, cu
+
+
+def _run(q, k, v, s, gain, temp, cu):
+    out, lse = tg.tg_gated_attn_prefill(q.cuda(), k.cuda(), v.cuda(), s.cuda(), gain.cuda(),
+                                        temp.cuda(), cu, want_lse=True)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+CASES = [
+    ("fp32_tiny", [128], 4, 2, 64, torch.float32),
+    ("fp32_varlen", [1, 5, 64, 130], 2, 1, 128, torch.float32),
+    ("bf16_qwen_heads_varlen", [1, 37, 200, 700], 16, 8, 128, torch.bfloat16),
+    ("bf16_dh64_pairs", [129, 64, 63], 4, 2, 64, torch.bfloat16),
+    ("bf16_group4", [300], 8, 2, 128, torch.bfloat16),
+    ("bf16_mha", [150, 90], 3, 3, 64, torch.bfloat16),
+    ("bf16_16k_layer_kept", [2048], 16, 8, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("name,lens,Hq,Hkv,dh,dtype", CASES, ids=[c[0] for c in CASES])
+def test_attention_parity(name, lens, Hq, Hkv, dh, dtype):
+    announce(f"attn {name} lens={lens} Hq={Hq} Hkv={Hkv} dh={dh}")
+    q, k, v, s, gain, temp, cu = _inputs(lens, Hq, Hkv, dh, dtype, seed=zlib.crc32(name.encode()) % 1000)
+    out, lse = _run(q, k, v, s, gain, temp, cu)
+    ref, ref_lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    rtol, atol = tol(dtype)
+    assert_within(out, ref, rtol, atol, f"{name} out")
+    assert_within(lse, ref_lse, rtol, atol, f"{name} lse")
+
+
+def test_attention_gain0_temp1_is_plain_causal():
+    q, k, v, s, _, _, cu = _inputs([333, 77], 16, 8, 128, torch.bfloat16, seed=21)
+    Hq = q.shape[1]
+    gain, temp = torch.zeros(Hq), torch.ones(Hq)
+    out, _ = _run(q, k, v, s, gain, temp, cu)
+    ref, _ = oracle.gated_attention(q, k, v, torch.zeros_like(s), gain, temp, cu)
+    assert_within(out, ref, 2e-2, 1e-2, "gain0/temp1")
+
+
+def test_attention_large_bias_range():
+    """Scores spread over +-40: the bias dominates the logits."""
+    q, k, v, s, gain, temp, cu = _inputs([513], 16, 8, 128, torch.bfloat16, seed=22, s_scale=20.0)
+    out, lse = _run(q, k, v, s, gain, temp, cu)
+    ref, ref_lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    assert_within(out, ref, 2e-2, 1e-2, "large bias out")
+    assert_within(lse, ref_lse, 2e-2, 1e-2, "large bias lse")
+
+
+def test_attention_deterministic():
+    q, k, v, s, gain, temp, cu = _inputs([1000, 24], 16, 8, 128, torch.bfloat16, seed=23)
+    a, _ = _run(q, k, v, s, gain, temp, cu)
+    b, _ = _run(q, k, v, s, gain, temp, cu)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _sampled_rows(cu, per_req, seed):
+    g = torch.Generator().manual_seed(seed)
+    rows = []
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        n = hi - lo
+        fixed = [0, 1, 63, 64, 65, 127, 128, n - 2, n - 1]
+        rows += [lo + r for r in fixed if 0 <= r < n]
+        rows += (lo + torch.randint(0, n, (per_req,), generator=g)).tolist()
+    return sorted(set(rows))
+
+
+@pytest.mark.parametrize("wname", ["qwen3_1p7b_128k_niah", "qwen3_1p7b_varlen4", "qwen3_1p7b_32k_stack4"])
+def test_attention_full_size_sampled(wname):
+    """Workload-size attention (kept rows only) in the benchmark's launch
+    configuration; the oracle evaluates sampled query rows, all heads."""
+    w = workloads.WORKLOADS[wname]
+    announce(f"attn full-size {wname} Kt={w.total_kept}")
+    a = workloads.attn_inputs(w, seed=1)
+    s = workloads.random_scores(w.total_kept, seed=2)
+    cu = oracle.plan(w.seq_len, w.q_len, w.budget)[1]
+    out, lse = _run(a["q"], a["k"], a["v"], s, a["gain"], a["temp"], cu)
+    rows = _sampled_rows(cu, 24, seed=3)
+    ref, ref_lse = oracle.gated_attention_rows(a["q"], a["k"], a["v"], s, a["gain"], a["temp"], cu, rows)
+    assert_within(out[rows], ref, 2e-2, 1e-2, f"{wname} out")
+    assert_within(lse[:, rows], ref_lse, 2e-2, 1e-2, f"{wname} lse")
+
+
+# ---------------------------------------------------------------- linear ----
+@pytest.mark.parametrize("M,N,K,dtype,acc", [
+    (300, 192, 256, torch.bfloat16, False),
+    (300, 192, 256, torch.bfloat16, True),
+    (1, 64, 64, torch.bfloat16, True),
+    (4096, 1024, 2048, torch.bfloat16, False),
+    (37, 50, 20, torch.float32, False),
+    (37, 50, 20, torch.float32, True),
+])
+def test_linear_parity(M, N, K, dtype, acc):
+    announce(f"linear M={M} N={N} K={K} {dtype} acc={acc}")
+    g = torch.Generator().manual_seed(M + N + K)
+    x = torch.randn(M, K, generator=g).to(dtype)
+    w = (torch.randn(N, K, generator=g) / K ** 0.5).to(dtype)
+    y0 = torch.randn(M, N, generator=g).to(dtype)
+    y = y0.cuda().clone()
+    tg.tg_linear(x.cuda(), w.cuda(), y=y, accumulate=acc)
+    ref = oracle.linear(x, w) + (y0.double() if acc else 0.0)
+    rtol, atol = tol(dtype)
+    assert_within(y.cpu(), ref, rtol, atol, "linear")

@@ -1,0 +1,178 @@
+"""GPU parity of the gate, the top-K selector and the gather against the oracle.
+
+Gate scores: within the fp32 (1e-5) or bf16 (2e-2 relative / 1e-2 absolute)
+tolerance.  Selection, run on the oracle's fp32 scores: bit-exact kept ids.
+Gather: bitwise.
+"""
+import math
+
+import pytest
+import torch
+
+import learned_token_pruning_02_amd as tg
+import oracle
+import workloads
+from parity_util import announce, assert_within, tol
+
+pytestmark = pytest.mark.gpu
+
+
+def _shape(d, dg, dtype, hq=4, hkv=2, dh=64):
+    return workloads.LayerShape(d, hq, hkv, dh, dg, dtype)
+
+
+def _wl(name, shape, seq, q, bud, needles=0):
+    return workloads.Workload(name, shape, list(seq), list(q), list(bud), n_needles=needles)
+
+
+# ------------------------------------------------------------------ gate ----
+GATE_CASES = [
+    ("tiny_fp32", None, True),
+    ("tiny_fp32", None, False),
+    ("fp32_T77_d64_dg200", (77, 64, 200, torch.float32), True),
+    ("bf16_T3000_d2048_dg256", (3000, 2048, 256, torch.bfloat16), True),
+    ("bf16_T3000_d2048_dg256_nobias", (3000, 2048, 256, torch.bfloat16), False),
+    ("bf16_T700_d128_dg64", (700, 128, 64, torch.bfloat16), False),
+    ("bf16_T1000_d256_dg128", (1000, 256, 128, torch.bfloat16), True),
+    ("bf16_T1_d64_dg64", (1, 64, 64, torch.bfloat16), True),
+    ("bf16_T70001_d128_dg256", (70001, 128, 256, torch.bfloat16), True),     # 128-token tiles
+    ("bf16_T131109_d128_dg256", (131109, 128, 256, torch.bfloat16), True),   # 256-token tiles
+    ("qwen3_1p7b_16k", None, True),
+]
+
+
+@pytest.mark.parametrize("name,spec,bias", GATE_CASES, ids=[c[0] + ("" if c[2] else "-nobias") for c in GATE_CASES])
+def test_gate_parity(name, spec, bias):
+    if spec is None:
+        w = workloads.WORKLOADS[name]
+    else:
+        T, d, dg, dt = spec
+        w = _wl(name, _shape(d, dg, dt), [T], [0], [T])
+    announce(f"gate {name} bias={bias} T={w.total_tokens} d={w.shape.d_model} dg={w.shape.d_gate}")
+    inp = workloads.gate_inputs(w, seed=3, with_bias=bias)
+    ref = oracle.gate_score(inp["hidden"], inp["w1"], inp["b1"], inp["w2"], inp["b2"])
+    g = {k: (v.cuda() if v is not None else None) for k, v in inp.items()}
+    got = tg.tg_gate_score(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"])
+    torch.cuda.synchronize()
+    rtol, atol = tol(w.shape.dtype)
+    assert_within(got, ref, rtol, atol, f"gate {name}")
+
+
+def test_gate_full_128k_sampled_rows():
+    """The 128k-token layer in the launch configuration the benchmark times,
+    checked on sampled rows (all needles, the ends, random rows)."""
+    w = workloads.WORKLOADS["qwen3_1p7b_128k_niah"]
+    announce("gate 128k sampled")
+    inp = workloads.gate_inputs(w, seed=0)
+    g = {k: v.cuda() for k, v in inp.items()}
+    got = tg.tg_gate_score(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"]).cpu()
+    gen = torch.Generator().manual_seed(5)
+    rows = torch.cat([torch.tensor([0, 1, 255, 256, w.total_tokens - 1]),
+                      workloads.needle_positions(w, 0),
+                      torch.randint(0, w.total_tokens, (3000,), generator=gen)]).unique()
+    ref = oracle.gate_score(inp["hidden"][rows], inp["w1"], inp["b1"], inp["w2"], inp["b2"])
+    assert_within(got[rows], ref, 2e-2, 1e-2, "gate 128k sampled")
+
+
+def test_gate_deterministic():
+    w = _wl("det", _shape(512, 256, torch.bfloat16), [4099], [0], [4099])
+    inp = {k: v.cuda() for k, v in workloads.gate_inputs(w, seed=9).items()}
+    a = tg.tg_gate_score(inp["hidden"], inp["w1"], inp["b1"], inp["w2"], inp["b2"]).clone()
+    b = tg.tg_gate_score(inp["hidden"], inp["w1"], inp["b1"], inp["w2"], inp["b2"])
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+# ---------------------------------------------------------------- select ----
+def _select_case(seq, q, bud, scores):
+    announce(f"select B={len(seq)} T={sum(seq)} seq={seq[:4]} q={q[:4]} budget={bud[:4]}")
+    ref, cu_ref = oracle.topk_select(scores, seq, q, bud)
+    got, cu = tg.tg_topk_select(scores.cuda(), seq, q, bud,
+                                cu_kept_dev=torch.empty(len(seq) + 1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert cu == cu_ref
+    assert torch.equal(got.cpu(), ref), "kept ids differ"
+
+
+@pytest.mark.parametrize("wname", list(workloads.WORKLOADS))
+def test_select_workload_shapes_random_scores(wname):
+    w = workloads.WORKLOADS[wname]
+    _select_case(w.seq_len, w.q_len, w.budget, workloads.random_scores(w.total_tokens, seed=4))
+
+
+def test_select_on_oracle_gate_scores_16k():
+    w = workloads.WORKLOADS["qwen3_1p7b_16k"]
+    inp = workloads.gate_inputs(w, seed=0)
+    s = oracle.gate_score(inp["hidden"], inp["w1"], inp["b1"], inp["w2"], inp["b2"])
+    _select_case(w.seq_len, w.q_len, w.budget, s)
+
+
+@pytest.mark.parametrize("levels", [3, 50, 1000])
+def test_select_heavy_ties(levels):
+    T = 40000
+    _select_case([T], [100], [5000], workloads.random_scores(T, seed=6, ties=levels))
+
+
+def test_select_all_equal():
+    T = 50000
+    _select_case([T], [64], [7000], torch.full((T,), 0.3125))
+
+
+def test_select_specials():
+    g = torch.Generator().manual_seed(7)
+    T = 20000
+    s = torch.randn(T, generator=g)
+    specials = torch.tensor([float("nan"), -0.0, 0.0, float("inf"), float("-inf")])
+    pos = torch.randint(0, T - 50, (4000,), generator=g)
+    s[pos] = specials[torch.randint(0, 5, (4000,), generator=g)]
+    for bud in (60, 2000, 9000, 16000, 19999):
+        _select_case([T], [50], [bud], s)
+
+
+def test_select_budget_edges():
+    g = torch.Generator().manual_seed(8)
+    seq = [1, 1, 2, 5, 300, 300, 300, 4096, 17000, 9]
+    q = [0, 1, 0, 5, 0, 100, 299, 128, 0, 3]
+    bud = [1, 1, 1, 5, 1, 100, 400, 4096, 16999, 4]
+    s = torch.randn(sum(seq), generator=g)
+    _select_case(seq, q, bud, s)
+
+
+def test_select_max_batch_and_large_request():
+    g = torch.Generator().manual_seed(9)
+    seq = [int(x) for x in torch.randint(1, 3000, (tg.TG_MAX_BATCH,), generator=g)]
+    q = [min(n, int(x)) for n, x in zip(seq, torch.randint(0, 300, (len(seq),), generator=g))]
+    bud = [max(qq, 1) + int(x) for qq, x in zip(q, torch.randint(0, 1500, (len(seq),), generator=g))]
+    _select_case(seq, q, bud, torch.randn(sum(seq), generator=g))
+    T = 1 << 20
+    _select_case([T], [128], [T // 16], workloads.random_scores(T, seed=10))
+
+
+# ---------------------------------------------------------------- gather ----
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 2048), (torch.float32, 256), (torch.bfloat16, 8)])
+def test_gather_bitwise(dtype, d):
+    announce(f"gather {dtype} d={d}")
+    g = torch.Generator().manual_seed(11)
+    T = 5000
+    hidden = torch.randn(T, d, generator=g).to(dtype)
+    s = torch.randn(T, generator=g)
+    kept = torch.sort(torch.randperm(T, generator=g)[:777]).values.to(torch.int32)
+    hk, sk = tg.tg_gather_compact(hidden.cuda(), kept.cuda(), s.cuda())
+    rh, rs = oracle.gather_compact(hidden, s, kept)
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(hk.cpu().view(bits), rh.view(bits))
+    assert torch.equal(sk.cpu().view(torch.int32), rs.view(torch.int32))
+
+
+def test_gather_out_of_range_rows_untouched():
+    T, d = 100, 64
+    hidden = torch.randn(T, d).to(torch.bfloat16).cuda()
+    s = torch.randn(T).cuda()
+    kept = torch.tensor([3, -1, 99, 100, 7], dtype=torch.int32).cuda()
+    out = torch.full((5, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    sk = torch.zeros(5, device="cuda")
+    tg.tg_gather_compact(hidden, kept, s, hidden_kept=out, scores_kept=sk)
+    out, sk = out.cpu(), sk.cpu()
+    assert torch.equal(out[0], hidden[3].cpu()) and torch.equal(out[2], hidden[99].cpu())
+    assert torch.equal(out[4], hidden[7].cpu())
+    assert (out[1] == 7.0).all() and (out[3] == 7.0).all()
+    assert math.isnan(sk[1]) and math.isnan(sk[3]) and sk[0] == s[3].cpu()
