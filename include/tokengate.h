@@ -133,8 +133,10 @@ tg_status tg_gate_score(tg_dtype dt, const void *hidden, int64_t T, int32_t d_mo
  *               request, requests in batch order (request b fills
  *               [cu_kept[b], cu_kept[b+1]))
  * cu_kept_dev : [B+1] int32 output copy of cu_kept, or NULL
- * ws/ws_bytes : device workspace of at least tg_plan's topk_ws_bytes (may be
- *               NULL when that size is 0)
+ * ws/ws_bytes : device workspace of at least tg_plan's topk_ws_bytes bytes,
+ *               16-byte aligned (may be NULL when that size is 0).  Its
+ *               contents on entry do not matter; calls that share one
+ *               workspace must not run concurrently.
  * Errors: those of tg_plan, TG_ERR_NULL_PTR, TG_ERR_WORKSPACE, TG_ERR_LAUNCH.
  */
 tg_status tg_topk_select(const float *scores, const tg_batch *b, int32_t *kept_idx,

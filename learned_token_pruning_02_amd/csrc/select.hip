@@ -3,21 +3,30 @@
 // question; "Comment déployer TokenGate ?" for the max_kept_prefill_tokens
 // budget).
 //
-// Per request b (one 1024-thread workgroup each, all requests in one launch):
+// Per request b:
 //   * budget >= N_b: keep every token;
 //   * otherwise keep the K_b - q_b best document tokens under the total order
 //     (score descending, index ascending) plus the q_b question tokens.
+// Kept ids come out ascending.
 //
 // Scores become order-preserving u32 keys (larger key = better score; -0 and
-// +0 share a key; NaN maps to 0, below -inf).  An LDS radix select over the
-// key digits (11, 11 and 10 bits, most significant first) narrows the
-// threshold: after each pass the digit holding the K_doc-th best key is fixed,
-// and the passes stop as soon as every key sharing the fixed prefix is needed.
-// The result is a prefix P (under mask M) and a count `rem` of keys with
-// (key & M) == P to take.  A last pass over the document in index order keeps
-// key & M > P, and the first `rem` keys equal to P in index order; wave
-// ballots and a per-chunk (item, wave) count table give each kept token its
-// output slot, so kept ids come out ascending without any sort.
+// +0 share a key; NaN maps to 0, below -inf).  The document of every request
+// is cut into chunks of 2048 keys, one 256-thread workgroup per chunk, and
+// the whole batch goes through four launches:
+//   1. clear the per-request histograms and counters;
+//   2. histogram of the top 11 key bits per chunk (LDS), summed into the
+//      request's histogram with global atomics; the chunk that finishes last
+//      (atomic ticket, no waiting) finds the bucket d1 holding the K_doc-th
+//      best key;
+//   3. per chunk, count the keys above d1 and append the keys in d1 with their
+//      index; the last chunk ranks those candidates exactly by an LDS radix
+//      select over the 52-bit composite (low 21 key bits, then reversed index),
+//      which turns (key desc, index asc) into a single descending order, then
+//      counts the kept tokens of every chunk and scans them into output offsets;
+//   4. per chunk, re-derive each key's keep flag from (d1, composite prefix)
+//      and write the kept ids in index order (wave ballots + a small count
+//      table per workgroup), and the question tail after them.
+// Results do not depend on which workgroup finishes last.
 #include "tg_device.h"
 #include "tg_kernels.h"
 
@@ -25,11 +34,13 @@ namespace tg {
 
 namespace {
 
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_WAVES = SEL_THREADS / WAVE;
-constexpr int SEL_ITEMS = 16;                       // keys per thread per chunk
-constexpr int SEL_CHUNK = SEL_THREADS * SEL_ITEMS;  // 16384 keys per chunk
-constexpr int TAB = SEL_ITEMS * SEL_WAVES;          // 256 table entries
+constexpr int SB = 256;                 // threads per workgroup
+constexpr int SWAVES = SB / WAVE;
+constexpr int SITEMS = 8;               // keys per thread
+constexpr int SCHUNK = SB * SITEMS;     // 2048 keys per chunk
+constexpr int NBIN = 2048;
+constexpr int META = 8;                 // u32 words of per-request metadata
+constexpr int CTR = 4;                  // u32 counters per request
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -38,179 +49,412 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of TAB counters in place by wave 0 (4 per lane); returns the
-// total to every lane of wave 0 and stores it in *total.
-__device__ __forceinline__ void wave0_scan_table(uint32_t* tab, uint32_t* total) {
-    const int lane = lane_id();
-    uint32_t v[4];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[i] = tab[lane * 4 + i];
-        sum += v[i];
-    }
-    uint32_t incl = sum;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        const uint32_t n = __shfl_up(incl, o, WAVE);
-        if (lane >= o) incl += n;
-    }
-    uint32_t run = incl - sum;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        tab[lane * 4 + i] = run;
-        run += v[i];
-    }
-    if (lane == WAVE - 1) *total = incl;
+// Composite rank key of a candidate inside the threshold bucket: the low 21
+// key bits, then 0x7fffffff - index, so that larger = better and unique.
+__device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
+    return ((uint64_t)(key & 0x1fffffu) << 31) | (uint64_t)(0x7fffffffu - idx);
 }
 
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __restrict__ scores,
-                                                             BatchArgs a,
-                                                             int32_t* __restrict__ kept,
-                                                             int32_t* __restrict__ cu_dev) {
-    const int b = blockIdx.x;
+__device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint2 coherent_load2(const uint2* p) {
+    const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+
+struct SelArgs {
+    int32_t batch;
+    int32_t off[TG_MAX_BATCH + 1];        // token offset of each request
+    int32_t out[TG_MAX_BATCH + 1];        // kept-row offset of each request
+    int32_t q[TG_MAX_BATCH];              // question tail
+    int32_t doc_chunk0[TG_MAX_BATCH + 1]; // first document chunk (selecting requests only)
+    int32_t all_chunk0[TG_MAX_BATCH + 1]; // first chunk over the whole request
+    const float* scores;
+    int32_t* kept;
+    int32_t* cu_dev;
+    uint32_t* hist;       // [B][NBIN]
+    uint32_t* meta;       // [B][META]: d1, rem1, cnt1, cprefix lo/hi, cmask lo/hi
+    uint32_t* ctr;        // [B][CTR]: hist ticket, candidate ticket, candidate count
+    uint32_t* chunk_def;  // [doc chunks]: keys above d1
+    uint32_t* chunk_off;  // [doc chunks]: output offset of the chunk's first kept token
+    uint2* cand;          // [T]: (key, local index), request b at off[b]
+};
+
+__device__ __forceinline__ int find_request(const int32_t* base, int batch, int blk) {
+    int b = 0;
+    while (b + 1 < batch && base[b + 1] <= blk) ++b;
+    return b;
+}
+
+// Inclusive block scan (256 threads) of v; *total gets the sum.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wtot, uint32_t* total) {
+    const int lane = lane_id(), w = threadIdx.x / WAVE;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t n = __shfl_up(v, o, WAVE);
+        if (lane >= o) v += n;
+    }
+    if (lane == WAVE - 1) wtot[w] = v;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < SWAVES; ++i) {
+        if (i < w) before += wtot[i];
+        all += wtot[i];
+    }
+    __syncthreads();
+    if (total != nullptr) *total = all;
+    return v + before;
+}
+
+// Over `nb` bins (multiple of SB) of hist (LDS or global via loader), find the
+// bin d with count(bins > d) < rem <= count(bins >= d).  Results go to *out_d,
+// *out_gt, *out_cnt (shared) from the owning thread.
+template <class Get>
+__device__ __forceinline__ void find_bin(Get get, int nb, uint32_t rem, uint32_t* wtot,
+                                         uint32_t* out_d, uint32_t* out_gt, uint32_t* out_cnt) {
+    const int per = nb / SB;
+    const int g = SB - 1 - (int)threadIdx.x;  // descending bin groups in thread order
+    uint32_t vals[NBIN / SB];
+    uint32_t gs = 0;
+    for (int j = 0; j < per; ++j) {
+        vals[j] = get(g * per + j);
+        gs += vals[j];
+    }
+    uint32_t incl = block_incl_scan(gs, wtot, nullptr);
+    uint32_t ge = incl - gs;
+    for (int j = per - 1; j >= 0; --j) {
+        const uint32_t gt = ge;
+        ge += vals[j];
+        if (gt < rem && rem <= ge) {
+            *out_d = (uint32_t)(g * per + j);
+            *out_gt = gt;
+            *out_cnt = vals[j];
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------------------------------------- launch 1 ----
+__global__ __launch_bounds__(SB) void sel_clear_kernel(uint32_t* hist, uint32_t* ctr, int n_hist,
+                                                       int n_ctr) {
+    const int i = blockIdx.x * SB + threadIdx.x;
+    if (i < n_hist) hist[i] = 0u;
+    if (i < n_ctr) ctr[i] = 0u;
+}
+
+// ------------------------------------------------------------- launch 2 ----
+__global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
+    __shared__ uint32_t h[NBIN];
+    __shared__ uint32_t wtot[SWAVES];
+    __shared__ uint32_t sh_last, sh_d, sh_gt, sh_cnt;
     const int tid = threadIdx.x;
-    const int lane = lane_id();
-    const int w = tid / WAVE;
+    const int b = find_request(a.doc_chunk0, a.batch, blockIdx.x);
+    const int c = blockIdx.x - a.doc_chunk0[b];
+    const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
+    const int N = a.off[b + 1] - a.off[b];
+    const int ndoc = N - a.q[b];
+    const int kdoc = a.out[b + 1] - a.out[b] - a.q[b];
+    const float* s = a.scores + a.off[b];
 
-    if (b == 0 && cu_dev != nullptr)
-        for (int i = tid; i <= a.batch; i += SEL_THREADS) cu_dev[i] = a.cu_kept[i];
+    for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
+    __syncthreads();
+    uint32_t kv[SITEMS];
+#pragma unroll
+    for (int it = 0; it < SITEMS; ++it) {
+        const int i = c * SCHUNK + it * SB + tid;
+        kv[it] = i < ndoc ? order_key(s[i]) : 0u;
+    }
+#pragma unroll
+    for (int it = 0; it < SITEMS; ++it) {
+        const int i = c * SCHUNK + it * SB + tid;
+        if (i < ndoc) atomicAdd(&h[kv[it] >> 21], 1u);
+    }
+    __syncthreads();
+    uint32_t* gh = a.hist + (size_t)b * NBIN;
+    for (int i = tid; i < NBIN; i += SB)
+        if (h[i] != 0u) atomicAdd(&gh[i], h[i]);
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 0], 1u) == (uint32_t)(nck - 1);
+    __syncthreads();
+    if (!sh_last) return;
+    __threadfence();
+    find_bin([&](int i) { return coherent_load(&gh[i]); }, NBIN, (uint32_t)kdoc, wtot, &sh_d,
+             &sh_gt, &sh_cnt);
+    if (tid == 0) {
+        uint32_t* m = a.meta + b * META;
+        m[0] = sh_d;
+        m[1] = (uint32_t)kdoc - sh_gt;
+        m[2] = sh_cnt;
+    }
+}
 
-    const int off = a.cu_seq[b];
-    const int N = a.cu_seq[b + 1] - off;
-    const int q = a.q_len[b];
-    const int out = a.cu_kept[b];
-    const int keep = a.cu_kept[b + 1] - out;
+// ------------------------------------------------------------- launch 3 ----
+__global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
+    __shared__ uint32_t wtot[SWAVES];
+    __shared__ uint32_t sh_base, sh_last, sh_d, sh_gt, sh_cnt, sh_total;
+    __shared__ uint32_t h[NBIN];
+    const int tid = threadIdx.x;
+    const int b = find_request(a.doc_chunk0, a.batch, blockIdx.x);
+    const int c = blockIdx.x - a.doc_chunk0[b];
+    const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
+    const int N = a.off[b + 1] - a.off[b];
+    const int ndoc = N - a.q[b];
+    const float* s = a.scores + a.off[b];
+    uint32_t* m = a.meta + b * META;
+    const uint32_t d1 = m[0];
+    uint2* cand = a.cand + a.off[b];
 
+    uint32_t kv[SITEMS];
+    uint32_t above = 0, ncand = 0;
+#pragma unroll
+    for (int it = 0; it < SITEMS; ++it) {
+        const int i = c * SCHUNK + it * SB + tid;
+        kv[it] = i < ndoc ? order_key(s[i]) : 0u;
+        if (i < ndoc) {
+            above += (kv[it] >> 21) > d1;
+            ncand += (kv[it] >> 21) == d1;
+        }
+    }
+    uint32_t tot_above;
+    block_incl_scan(above, wtot, &tot_above);
+    uint32_t tot_cand;
+    const uint32_t incl = block_incl_scan(ncand, wtot, &tot_cand);
+    if (tid == 0) {
+        a.chunk_def[a.doc_chunk0[b] + c] = tot_above;
+        sh_base = tot_cand ? atomicAdd(&a.ctr[b * CTR + 2], tot_cand) : 0u;
+    }
+    __syncthreads();
+    uint32_t pos = sh_base + incl - ncand;
+#pragma unroll
+    for (int it = 0; it < SITEMS; ++it) {
+        const int i = c * SCHUNK + it * SB + tid;
+        if (i < ndoc && (kv[it] >> 21) == d1) cand[pos++] = make_uint2(kv[it], (uint32_t)i);
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 1], 1u) == (uint32_t)(nck - 1);
+    __syncthreads();
+    if (!sh_last) return;
+    __threadfence();
+
+    // ---- the last chunk: exact rank inside bucket d1 ----------------------
+    const uint32_t cnt1 = m[2];
+    uint32_t rem = m[1];
+    uint64_t cprefix = 0, cmask = 0;
+    const int shifts[5] = {41, 31, 20, 9, 0};
+    const int widths[5] = {11, 10, 11, 11, 9};
+    for (int p = 0; p < 5; ++p) {
+        const int sh = shifts[p];
+        const int nb = 1 << widths[p];
+        for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
+        __syncthreads();
+        for (uint32_t j = tid; j < cnt1; j += SB) {
+            const uint2 e = coherent_load2(&cand[j]);
+            const uint64_t cp = composite(e.x, e.y);
+            if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        find_bin([&](int i) { return h[i]; }, nb < SB ? SB : nb, rem, wtot, &sh_d, &sh_gt, &sh_cnt);
+        rem -= sh_gt;
+        cprefix |= (uint64_t)sh_d << sh;
+        cmask |= (uint64_t)(nb - 1) << sh;
+        const uint32_t cnt = sh_cnt;
+        __syncthreads();
+        if (cnt == rem) break;  // every composite with this prefix is kept
+    }
+
+    // Kept candidates per chunk, then exclusive offsets of all chunks.
+    uint32_t* ccnt = h;  // reuse: up to NBIN chunks handled per round
+    const uint32_t* def = a.chunk_def + a.doc_chunk0[b];
+    uint32_t* coff = a.chunk_off + a.doc_chunk0[b];
+    uint32_t carry = 0;
+    for (int c0 = 0; c0 < nck; c0 += NBIN) {
+        for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
+        __syncthreads();
+        for (uint32_t j = tid; j < cnt1; j += SB) {
+            const uint2 e = coherent_load2(&cand[j]);
+            const int ch = (int)(e.y / SCHUNK) - c0;
+            if (ch >= 0 && ch < NBIN && (composite(e.x, e.y) & cmask) >= cprefix)
+                atomicAdd(&ccnt[ch], 1u);
+        }
+        __syncthreads();
+        // each thread owns NBIN/SB consecutive chunks
+        const int per = NBIN / SB;
+        uint32_t v[NBIN / SB];
+        uint32_t sum = 0;
+        for (int j = 0; j < per; ++j) {
+            const int ch = c0 + tid * per + j;
+            v[j] = ch < nck ? ccnt[tid * per + j] + coherent_load(&def[ch]) : 0u;
+            sum += v[j];
+        }
+        const uint32_t incl2 = block_incl_scan(sum, wtot, &sh_total);
+        uint32_t run = carry + incl2 - sum;
+        for (int j = 0; j < per; ++j) {
+            const int ch = c0 + tid * per + j;
+            if (ch < nck) coff[ch] = run;
+            run += v[j];
+        }
+        carry += sh_total;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        m[3] = (uint32_t)cprefix;
+        m[4] = (uint32_t)(cprefix >> 32);
+        m[5] = (uint32_t)cmask;
+        m[6] = (uint32_t)(cmask >> 32);
+    }
+}
+
+// ------------------------------------------------------------- launch 4 ----
+__global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
+    __shared__ uint32_t tab[SITEMS * SWAVES];
+    const int tid = threadIdx.x, lane = lane_id(), w = tid / WAVE;
+    const int b = find_request(a.all_chunk0, a.batch, blockIdx.x);
+    const int c = blockIdx.x - a.all_chunk0[b];
+    if (blockIdx.x == 0 && a.cu_dev != nullptr)
+        for (int i = tid; i <= a.batch; i += SB) a.cu_dev[i] = a.out[i];
+    const int off = a.off[b];
+    const int N = a.off[b + 1] - off;
+    const int q = a.q[b];
+    const int out = a.out[b];
+    const int keep = a.out[b + 1] - out;
+    const int lo = c * SCHUNK;
+    const int hi = min(lo + SCHUNK, N);
     if (keep >= N) {
-        for (int i = tid; i < N; i += SEL_THREADS) kept[out + i] = off + i;
+        for (int i = lo + tid; i < hi; i += SB) a.kept[out + i] = off + i;
         return;
     }
     const int ndoc = N - q;
     const int kdoc = keep - q;
-    for (int i = tid; i < q; i += SEL_THREADS) kept[out + kdoc + i] = off + ndoc + i;
-    if (kdoc <= 0) return;
+    for (int i = max(lo, ndoc) + tid; i < hi; i += SB) a.kept[out + kdoc + (i - ndoc)] = off + i;
+    if (kdoc <= 0 || lo >= ndoc) return;
 
-    const float* s = scores + off;
+    const uint32_t* m = a.meta + b * META;
+    const uint32_t d1 = m[0];
+    const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
+    const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
+    const uint32_t base = a.chunk_off[a.doc_chunk0[b] + c];
+    const float* s = a.scores + off;
 
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wsum[SEL_WAVES];
-    __shared__ uint32_t sh_prefix, sh_rem, sh_cnt;
-    __shared__ uint32_t tabE[TAB], tabK[TAB];
-    __shared__ uint32_t totE, totK;
-
-    // ---- radix select of the threshold ----------------------------------
-    uint32_t prefix = 0, mask = 0, rem = (uint32_t)kdoc;
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-        const int nbins = pass == 2 ? 1024 : 2048;
-        for (int i = tid; i < 2048; i += SEL_THREADS) hist[i] = 0;
-        __syncthreads();
-        for (int base = 0; base < ndoc; base += SEL_CHUNK) {
-            uint32_t kv[SEL_ITEMS];
+    uint64_t km[SITEMS];
 #pragma unroll
-            for (int it = 0; it < SEL_ITEMS; ++it) {
-                const int i = base + it * SEL_THREADS + tid;
-                kv[it] = i < ndoc ? order_key(s[i]) : 0u;
-            }
-#pragma unroll
-            for (int it = 0; it < SEL_ITEMS; ++it) {
-                const int i = base + it * SEL_THREADS + tid;
-                if (i < ndoc && (kv[it] & mask) == prefix)
-                    atomicAdd(&hist[(kv[it] >> shift) & (uint32_t)(nbins - 1)], 1u);
-            }
+    for (int it = 0; it < SITEMS; ++it) {
+        const int i = lo + it * SB + tid;
+        bool k = false;
+        if (i < ndoc) {
+            const uint32_t key = order_key(s[i]);
+            const uint32_t dg = key >> 21;
+            k = dg > d1 || (dg == d1 && (composite(key, (uint32_t)i) & cmask) >= cprefix);
         }
-        __syncthreads();
-
-        // Suffix counts: thread tid owns bin group g = SEL_THREADS-1-tid, so
-        // an inclusive scan in thread order runs from the highest bins down.
-        const int per = nbins / SEL_THREADS;
-        const int g = SEL_THREADS - 1 - tid;
-        uint32_t gs = 0;
-        for (int j = 0; j < per; ++j) gs += hist[g * per + j];
-        uint32_t incl = gs;
+        km[it] = __ballot(k);
+        if (lane == 0) tab[it * SWAVES + w] = (uint32_t)__popcll(km[it]);
+    }
+    __syncthreads();
+    if (w == 0) {  // exclusive scan of the SITEMS*SWAVES = 32 counts
+        uint32_t v = lane < SITEMS * SWAVES ? tab[lane] : 0u;
+        uint32_t incl = v;
 #pragma unroll
         for (int o = 1; o < WAVE; o <<= 1) {
             const uint32_t n = __shfl_up(incl, o, WAVE);
             if (lane >= o) incl += n;
         }
-        if (lane == WAVE - 1) wsum[w] = incl;
-        __syncthreads();
-        uint32_t before = 0;
-        for (int i = 0; i < w; ++i) before += wsum[i];
-        uint32_t ge = before + incl - gs;  // keys whose digit is above this group
-        for (int j = per - 1; j >= 0; --j) {
-            const int bin = g * per + j;
-            const uint32_t gt = ge;
-            ge += hist[bin];
-            if (gt < rem && rem <= ge) {
-                sh_prefix = prefix | ((uint32_t)bin << shift);
-                sh_rem = rem - gt;
-                sh_cnt = hist[bin];
-            }
-        }
-        __syncthreads();
-        prefix = sh_prefix;
-        mask |= (uint32_t)(nbins - 1) << shift;
-        rem = sh_rem;
-        const uint32_t cnt = sh_cnt;
-        __syncthreads();
-        if (cnt == rem) break;  // every key with this prefix is kept
+        if (lane < SITEMS * SWAVES) tab[lane] = incl - v;
     }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < SITEMS; ++it) {
+        if ((km[it] >> lane) & 1ull) {
+            const int i = lo + it * SB + tid;
+            const uint32_t pos = base + tab[it * SWAVES + w] + lanes_below(km[it]);
+            if (pos < (uint32_t)kdoc) a.kept[out + pos] = off + i;
+        }
+    }
+}
 
-    // ---- ordered compaction of the document ------------------------------
-    uint32_t eq_carry = 0, keep_carry = 0;
-    for (int base = 0; base < ndoc && keep_carry < (uint32_t)kdoc; base += SEL_CHUNK) {
-        uint32_t kv[SEL_ITEMS];
-        uint64_t em[SEL_ITEMS];
-#pragma unroll
-        for (int it = 0; it < SEL_ITEMS; ++it) {
-            const int i = base + it * SEL_THREADS + tid;
-            kv[it] = i < ndoc ? order_key(s[i]) : 0u;
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+    size_t hist, meta, ctr, def, off, cand, total;
+};
+
+WsLayout ws_layout(int batch, int doc_chunks, int64_t T) {
+    WsLayout L;
+    size_t p = 0;
+    L.hist = p; p = align256(p + (size_t)batch * NBIN * 4);
+    L.meta = p; p = align256(p + (size_t)batch * META * 4);
+    L.ctr = p;  p = align256(p + (size_t)batch * CTR * 4);
+    L.def = p;  p = align256(p + (size_t)doc_chunks * 4);
+    L.off = p;  p = align256(p + (size_t)doc_chunks * 4);
+    L.cand = p; p = align256(p + (size_t)T * 8);
+    L.total = p;
+    return L;
+}
+
+void chunk_plan(const BatchArgs& a, SelArgs* s, int* doc_chunks, int* all_chunks) {
+    int dc = 0, ac = 0;
+    for (int b = 0; b < a.batch; ++b) {
+        const int N = a.cu_seq[b + 1] - a.cu_seq[b];
+        const int keep = a.cu_kept[b + 1] - a.cu_kept[b];
+        const int ndoc = N - a.q_len[b];
+        const bool selecting = keep < N && keep - a.q_len[b] > 0;
+        if (s != nullptr) {
+            s->doc_chunk0[b] = dc;
+            s->all_chunk0[b] = ac;
         }
-#pragma unroll
-        for (int it = 0; it < SEL_ITEMS; ++it) {
-            const int i = base + it * SEL_THREADS + tid;
-            const bool e = i < ndoc && (kv[it] & mask) == prefix;
-            em[it] = __ballot(e);
-            if (lane == 0) tabE[it * SEL_WAVES + w] = (uint32_t)__popcll(em[it]);
-        }
-        __syncthreads();
-        if (w == 0) wave0_scan_table(tabE, &totE);
-        __syncthreads();
-        uint64_t km[SEL_ITEMS];
-#pragma unroll
-        for (int it = 0; it < SEL_ITEMS; ++it) {
-            const int i = base + it * SEL_THREADS + tid;
-            const bool e = (em[it] >> lane) & 1ull;
-            const uint32_t rank = eq_carry + tabE[it * SEL_WAVES + w] + lanes_below(em[it]);
-            const bool k = i < ndoc && ((kv[it] & mask) > prefix || (e && rank < rem));
-            km[it] = __ballot(k);
-            if (lane == 0) tabK[it * SEL_WAVES + w] = (uint32_t)__popcll(km[it]);
-        }
-        __syncthreads();
-        if (w == 0) wave0_scan_table(tabK, &totK);
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < SEL_ITEMS; ++it) {
-            if ((km[it] >> lane) & 1ull) {
-                const int i = base + it * SEL_THREADS + tid;
-                const uint32_t pos = keep_carry + tabK[it * SEL_WAVES + w] + lanes_below(km[it]);
-                if (pos < (uint32_t)kdoc) kept[out + pos] = off + i;
-            }
-        }
-        eq_carry += totE;
-        keep_carry += totK;
-        __syncthreads();
+        if (selecting) dc += (ndoc + SCHUNK - 1) / SCHUNK;
+        ac += (N + SCHUNK - 1) / SCHUNK;
     }
+    if (s != nullptr) {
+        s->doc_chunk0[a.batch] = dc;
+        s->all_chunk0[a.batch] = ac;
+    }
+    *doc_chunks = dc;
+    *all_chunks = ac;
 }
 
 }  // namespace
 
+size_t select_workspace_bytes(const BatchArgs& a) {
+    int dc, ac;
+    chunk_plan(a, nullptr, &dc, &ac);
+    return ws_layout(a.batch, dc, a.cu_seq[a.batch]).total;
+}
+
 hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept, int32_t* cu_dev,
-                         hipStream_t st) {
-    hipLaunchKernelGGL(select_kernel, dim3(a.batch), dim3(SEL_THREADS), 0, st, scores, a, kept,
-                       cu_dev);
+                         void* ws, hipStream_t st) {
+    SelArgs s;
+    s.batch = a.batch;
+    for (int b = 0; b <= a.batch; ++b) {
+        s.off[b] = a.cu_seq[b];
+        s.out[b] = a.cu_kept[b];
+    }
+    for (int b = 0; b < a.batch; ++b) s.q[b] = a.q_len[b];
+    int dc, ac;
+    chunk_plan(a, &s, &dc, &ac);
+    const WsLayout L = ws_layout(a.batch, dc, a.cu_seq[a.batch]);
+    char* base = (char*)ws;
+    s.scores = scores;
+    s.kept = kept;
+    s.cu_dev = cu_dev;
+    s.hist = (uint32_t*)(base + L.hist);
+    s.meta = (uint32_t*)(base + L.meta);
+    s.ctr = (uint32_t*)(base + L.ctr);
+    s.chunk_def = (uint32_t*)(base + L.def);
+    s.chunk_off = (uint32_t*)(base + L.off);
+    s.cand = (uint2*)(base + L.cand);
+    if (dc > 0) {
+        const int n_hist = a.batch * NBIN, n_ctr = a.batch * CTR;
+        hipLaunchKernelGGL(sel_clear_kernel, dim3((n_hist + SB - 1) / SB), dim3(SB), 0, st, s.hist,
+                           s.ctr, n_hist, n_ctr);
+        hipLaunchKernelGGL(sel_hist_kernel, dim3(dc), dim3(SB), 0, st, s);
+        hipLaunchKernelGGL(sel_cand_kernel, dim3(dc), dim3(SB), 0, st, s);
+    }
+    hipLaunchKernelGGL(sel_compact_kernel, dim3(ac), dim3(SB), 0, st, s);
     return hipGetLastError();
 }
 

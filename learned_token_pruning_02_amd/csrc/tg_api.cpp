@@ -81,7 +81,7 @@ tg_status tg_plan(const tg_batch* b, int32_t* cu_seqlens, int32_t* cu_kept,
     if (st != TG_OK) return st;
     if (cu_seqlens != nullptr) std::memcpy(cu_seqlens, a.cu_seq, sizeof(int32_t) * (a.batch + 1));
     if (cu_kept != nullptr) std::memcpy(cu_kept, a.cu_kept, sizeof(int32_t) * (a.batch + 1));
-    if (topk_ws_bytes != nullptr) *topk_ws_bytes = 0;
+    if (topk_ws_bytes != nullptr) *topk_ws_bytes = tg::select_workspace_bytes(a);
     return TG_OK;
 }
 
@@ -118,15 +118,18 @@ tg_status tg_topk_select(const float* scores, const tg_batch* b, int32_t* kept_i
     const tg_status st = plan_batch(b, &a);
     if (st != TG_OK) return st;
     if (scores == nullptr || kept_idx == nullptr) return TG_ERR_NULL_PTR;
-    (void)ws;
-    (void)ws_bytes;  // the current selector needs no workspace
-    if (!aligned4(scores) || !aligned4(kept_idx)) return TG_ERR_ALIGNMENT;
+    const size_t need = tg::select_workspace_bytes(a);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return TG_ERR_WORKSPACE;
+    if (!aligned4(scores) || !aligned4(kept_idx) || !aligned16(ws)) return TG_ERR_ALIGNMENT;
     const int64_t T = a.cu_seq[a.batch], Kt = a.cu_kept[a.batch];
+    const int64_t wb = (int64_t)need;
     if (overlap(kept_idx, Kt * 4, scores, T * 4) ||
         overlap(cu_kept_dev, (a.batch + 1) * 4, scores, T * 4) ||
-        overlap(cu_kept_dev, (a.batch + 1) * 4, kept_idx, Kt * 4))
+        overlap(cu_kept_dev, (a.batch + 1) * 4, kept_idx, Kt * 4) ||
+        overlap(ws, wb, scores, T * 4) || overlap(ws, wb, kept_idx, Kt * 4) ||
+        overlap(ws, wb, cu_kept_dev, (a.batch + 1) * 4))
         return TG_ERR_ALIAS;
-    return launched(tg::launch_select(scores, a, kept_idx, cu_kept_dev, stream));
+    return launched(tg::launch_select(scores, a, kept_idx, cu_kept_dev, ws, stream));
 }
 
 tg_status tg_gather_compact(tg_dtype dt, const void* hidden, int64_t T, int32_t d_model,

@@ -22,8 +22,9 @@ hipError_t launch_gate_f32(const float* hidden, int64_t T, int d, const float* w
 hipError_t launch_gate_bf16(const void* hidden, int64_t T, int d, const void* w1, const void* b1,
                             const void* w2, const void* b2, int dg, float* scores, hipStream_t st);
 
+size_t select_workspace_bytes(const BatchArgs& a);
 hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept, int32_t* cu_dev,
-                         hipStream_t st);
+                         void* ws, hipStream_t st);
 
 hipError_t launch_gather(const void* hidden, int64_t T, int row_bytes, const float* scores,
                          const int32_t* kept, int64_t Kt, void* hidden_kept, float* scores_kept,

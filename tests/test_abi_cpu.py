@@ -53,7 +53,7 @@ def test_library_exports_every_declared_symbol():
 def test_plan_matches_oracle(case):
     cu_s, cu_k, ws = tg.tg_plan(*case)
     o_s, o_k = oracle.plan(*case)
-    assert cu_s == o_s and cu_k == o_k and ws == 0
+    assert cu_s == o_s and cu_k == o_k and ws > 0
 
 
 @pytest.mark.parametrize("seq,q,bud", [
@@ -110,13 +110,28 @@ def test_gate_validation():
 def test_select_validation():
     L = tg.lib()
     bt, keep = _batch([100], [10], [20])
-    assert L.tg_topk_select(None, ctypes.byref(bt), B, None, None, 0, None) == 1
-    assert L.tg_topk_select(A, ctypes.byref(bt), None, None, None, 0, None) == 1
-    assert L.tg_topk_select(A, None, B, None, None, 0, None) == 1
-    assert L.tg_topk_select(A + 2, ctypes.byref(bt), B, None, None, 0, None) == 6
-    assert L.tg_topk_select(A, ctypes.byref(bt), A + 40, None, None, 0, None) == 9
+    ws = tg.tg_plan([100], [10], [20])[2]
+    assert ws > 0
+    f = L.tg_topk_select
+    assert f(None, ctypes.byref(bt), B, None, C, ws, None) == 1
+    assert f(A, ctypes.byref(bt), None, None, C, ws, None) == 1
+    assert f(A, None, B, None, C, ws, None) == 1
+    assert f(A, ctypes.byref(bt), B, None, None, ws, None) == 7          # no workspace
+    assert f(A, ctypes.byref(bt), B, None, C, ws - 1, None) == 7         # too small
+    assert f(A + 2, ctypes.byref(bt), B, None, C, ws, None) == 6
+    assert f(A, ctypes.byref(bt), B, None, C + 8, ws, None) == 6         # workspace alignment
+    assert f(A, ctypes.byref(bt), A + 40, None, C, ws, None) == 9
+    assert f(A, ctypes.byref(bt), B, None, A, ws, None) == 9             # workspace over scores
     bad, keep2 = _batch([100], [10], [5])
-    assert L.tg_topk_select(A, ctypes.byref(bad), B, None, None, 0, None) == 3
+    assert f(A, ctypes.byref(bad), B, None, C, ws, None) == 3
+
+
+def test_select_workspace_grows_with_tokens_and_requests():
+    w1 = tg.tg_plan([1000], [10], [100])[2]
+    w2 = tg.tg_plan([100000], [10], [100])[2]
+    w3 = tg.tg_plan([1000] * 8, [10] * 8, [100] * 8)[2]
+    assert w2 > w1 and w3 > w1
+    assert w2 >= 100000 * 8                                               # candidate buffer
 
 
 def test_gather_validation():
