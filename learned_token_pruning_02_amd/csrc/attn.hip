@@ -170,16 +170,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         const bf16* qp = a.q + ((rbase + (qvalid ? qi : 0)) * a.Hq + h) * DH + (DH / 2) * hh;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-            uint4 val = qvalid ? *reinterpret_cast<const uint4*>(qp + 8 * kk) : make_uint4(0, 0, 0, 0);
-            qf[kk] = as_bf16x8(val);
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            qf[kk] = as_bf16x8(qvalid ? ld16(qp + 8 * kk) : zero);
         }
     }
     const float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
     const float g2 = a.gain[h] * LOG2E;
 
     // ---- K/V/s tile staging ------------------------------------------------
-    uint4 kreg[KU];
-    uint4 vreg[4];
+    u32x4 kreg[KU];
+    u32x4 vreg[4];
     float sreg = 0.f;
     auto load_tile = [&](int jt) {
         const int j0 = jt * KVT;
@@ -188,14 +188,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             const int uu = tid + i * 256;
             const int row = uu / (DH / 8), c = uu % (DH / 8);
             const int key = min(j0 + row, n - 1);
-            kreg[i] = *reinterpret_cast<const uint4*>(a.k + ((rbase + key) * a.Hkv + kvh) * DH + 8 * c);
+            kreg[i] = ld16(a.k + ((rbase + key) * a.Hkv + kvh) * DH + 8 * c);
         }
         if (tid < VU) {
             const int kg = tid % (KVT / 4), dg = tid / (KVT / 4);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int key = min(j0 + 4 * kg + i, n - 1);
-                vreg[i] = *reinterpret_cast<const uint4*>(a.v + ((rbase + key) * a.Hkv + kvh) * DH + 8 * dg);
+                vreg[i] = ld16(a.v + ((rbase + key) * a.Hkv + kvh) * DH + 8 * dg);
             }
         }
         if (tid < KVT) sreg = a.s[rbase + min(j0 + tid, n - 1)];
@@ -205,20 +205,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int i = 0; i < KU; ++i) {
             const int uu = tid + i * 256;
             const int row = uu / (DH / 8), c = uu % (DH / 8);
-            *reinterpret_cast<uint4*>(&Ks[buf][row * KS + 8 * c]) = kreg[i];
+            st16(&Ks[buf][row * KS + 8 * c], kreg[i]);
         }
         if (tid < VU) {
             const int kg = tid % (KVT / 4), dg = tid / (KVT / 4);
-            const uint16_t* r0 = reinterpret_cast<const uint16_t*>(&vreg[0]);
-            const uint16_t* r1 = reinterpret_cast<const uint16_t*>(&vreg[1]);
-            const uint16_t* r2 = reinterpret_cast<const uint16_t*>(&vreg[2]);
-            const uint16_t* r3 = reinterpret_cast<const uint16_t*>(&vreg[3]);
+            // Transpose 4 keys x 8 dh: element e of a row is half e%2 of word e/2.
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                uint2 pk;
-                pk.x = (uint32_t)r0[e] | ((uint32_t)r1[e] << 16);
-                pk.y = (uint32_t)r2[e] | ((uint32_t)r3[e] << 16);
-                *reinterpret_cast<uint2*>(&Vt[buf][(8 * dg + e) * VT_STRIDE + 4 * kg]) = pk;
+                const int wd = e / 2, sh = 16 * (e % 2);
+                u32x2 pk;
+                pk[0] = ((vreg[0][wd] >> sh) & 0xffffu) | (((vreg[1][wd] >> sh) & 0xffffu) << 16);
+                pk[1] = ((vreg[2][wd] >> sh) & 0xffffu) | (((vreg[3][wd] >> sh) & 0xffffu) << 16);
+                st8(&Vt[buf][(8 * dg + e) * VT_STRIDE + 4 * kg], pk);
             }
         }
         if (tid < KVT) Ss[buf][tid] = sreg;
@@ -250,8 +248,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
-                const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    &Ks[buf][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));
+                const bf16x8 kf =
+                    as_bf16x8(ld16(&Ks[buf][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));
                 sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);
             }
         }
@@ -304,9 +302,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 const bf16* vrow = &Vt[buf][(32 * md + l32) * VT_STRIDE + 16 * kk + 4 * hh];
-                const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-                const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-                const bf16x8 vf = as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+                const u32x2 lo = ld8(vrow);
+                const u32x2 hi = ld8(vrow + 8);
+                const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
+                const bf16x8 vf = as_bf16x8(both);
                 o[md] = mfma32(vf, pf[kk], o[md]);
             }
         }

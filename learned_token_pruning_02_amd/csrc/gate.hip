@@ -2,16 +2,21 @@
 // scores every token from its post-attention residual at the gate layer).
 //     s_t = w2 . GELU(W1 x_t + b1) + b2,  GELU in its exact erf form.
 //
-// bf16 path: one workgroup of 2*WM waves scores BM = 64*WM tokens against all
-// d_gate gate units.  Wave (wm, wn) owns 64 tokens x d_gate/2 units, i.e.
-// 2 x (d_gate/64) tiles of the 32x32x16 bf16 MFMA with fp32 accumulators.
-// The residual streams from HBM straight into registers (each lane reads
-// 64 contiguous bytes of one token row per 64-wide k chunk, one chunk ahead);
-// W1 chunks [d_gate][64] are staged through double-buffered LDS and shared by
-// all waves.  Inside a 64-wide k chunk, lane half h covers k in [32h, 32h+32)
-// for both operands, so every operand fetch is a contiguous 16-byte access.
-// The epilogue adds b1, applies GELU, weights by w2, reduces over the units
-// (lane butterfly, then the two unit halves through LDS) and adds b2.
+// bf16 path: a workgroup of WAVES waves scores 64*WAVES tokens; each wave owns
+// 64 tokens against ALL d_gate gate units (2 x d_gate/32 tiles of the
+// 32x32x16 bf16 MFMA, fp32 accumulators held in the accumulation registers,
+// one wave per SIMD).  The residual streams from HBM straight into registers:
+// each lane reads 64 contiguous bytes of one token row per 64-wide k chunk,
+// through a ring of three register sets issued two chunks ahead, so about
+// 64 KB per CU is in flight.  W1 chunks [d_gate][64] are read coalesced into
+// registers and stored into double-buffered LDS in a fragment-major layout,
+// so each MFMA B fragment is one conflict-free 16-byte LDS read; they are
+// requested before the residual so that waiting for them (in-order load
+// counter) never waits for the residual prefetch.  Inside a 64-wide k chunk, lane half h covers k in
+// [32h, 32h+32) for both operands, so every operand fetch is one contiguous
+// 16-byte access.  The epilogue adds b1, applies GELU (branch-free erf of
+// Abramowitz & Stegun 7.1.26), weights by w2, reduces over the units with a
+// lane butterfly and adds b2.
 #include "tg_device.h"
 #include "tg_kernels.h"
 
@@ -54,43 +59,59 @@ __global__ __launch_bounds__(GF_THREADS) void gate_f32_kernel(
 }
 
 // --------------------------------------------------------------- bf16 ----
-constexpr int GK = 64;            // k chunk
-constexpr int W_STRIDE = GK + 8;  // LDS row stride of a W1 chunk (bf16 elements)
+constexpr int GK = 64;   // k chunk
+constexpr int RING = 3;  // residual fragment sets per wave (two chunks in flight)
 
-template <int DG, int WM>
-__global__ __launch_bounds__(128 * WM) void gate_bf16_kernel(
+template <int DG, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     const bf16* __restrict__ hidden, int64_t T, int d, const bf16* __restrict__ w1,
     const bf16* __restrict__ b1, const bf16* __restrict__ w2, const bf16* __restrict__ b2,
     float* __restrict__ scores) {
-    constexpr int THREADS = 128 * WM;
-    constexpr int BM = 64 * WM;
-    constexpr int NT = DG / 64;                   // 32-unit tiles per wave
-    constexpr int WUNITS = (DG * GK / 8) / THREADS;  // 16-byte W1 units per thread per chunk
-    static_assert(WUNITS >= 1 && (DG * GK / 8) % THREADS == 0, "W1 chunk split");
+    constexpr int BM = 64 * WAVES;
+    constexpr int NT = DG / 32;            // 32-unit tiles
+    constexpr int NFRAG = NT * 4;          // W1 fragments (1 KB each) per k chunk
 
-    __shared__ __attribute__((aligned(16))) bf16 wl[2][DG * W_STRIDE];
-    __shared__ float red[2][BM];
+    // W1 chunks in fragment layout: [buf][nt*4 + kk][lane] 16-byte units.
+    __shared__ __attribute__((aligned(16))) u32x4 wl[2][NFRAG * WAVE];
 
-    const int tid = threadIdx.x;
     const int lane = lane_id();
-    const int w = tid / WAVE;
-    const int wm = w % WM;
-    const int wn = w / WM;
+    const int w = threadIdx.x / WAVE;
     const int hh = lane / 32;
     const int l32 = lane % 32;
     const int64_t tok0 = (int64_t)blockIdx.x * BM;
 
-    // Token rows this lane feeds to the MFMA A operand (clamped in range).
     const bf16* arow[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-        int64_t r = tok0 + 64 * wm + 32 * mt + l32;
+        int64_t r = tok0 + 64 * w + 32 * mt + l32;
         if (r > T - 1) r = T - 1;
         arow[mt] = hidden + r * d + 32 * hh;
     }
+    // W1 chunk staging: 16-byte unit u = tid + i*THREADS of a chunk is row
+    // u/8, column 8*(u%8) (coalesced rows).  It lands in the fragment-major LDS
+    // layout (fragment f = nt*4 + kk, 64 lanes of 16 bytes) at position
+    // lane ^ swz(kk, half) with swz = 2*kk + 8*half: a bijection on the low
+    // four position bits, so the fragment reads stay conflict-free, while the
+    // 16 lanes of every write group (two rows x four kk x two halves) land on
+    // 16 distinct bank quads.
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int WUNITS = NFRAG * WAVE / THREADS;
+    constexpr int R = THREADS / 8;
+    static_assert(32 % R == 0, "rows per staging round");
+    const int r0 = threadIdx.x / 8, c0 = threadIdx.x % 8;
+    const bf16* wbase = w1 + (int64_t)r0 * d + 8 * c0;
+    const int wkk = c0 % 4, whq = c0 / 4;
+    auto wpos = [&](int i) {
+        const int row = r0 + R * i;
+        const int ln = (row % 32) + 32 * whq;
+        return ((row / 32) * 4 + wkk) * WAVE + (ln ^ (2 * wkk + 8 * whq));
+    };
+    int rd_pos[4];  // this lane's read position inside a fragment, per kk
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) rd_pos[kk] = lane ^ (2 * kk + 8 * hh);
+    u32x4 wreg[WUNITS];
 
-    uint4 acur[2][4], anext[2][4];
-    uint4 wreg[WUNITS];
+    u32x4 a0[2][4], a1[2][4], a2[2][4];
     f32x16 acc[2][NT];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -99,90 +120,120 @@ __global__ __launch_bounds__(128 * WM) void gate_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
-    auto load_a = [&](uint4 (&dst)[2][4], int k0) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                dst[mt][kk] = *reinterpret_cast<const uint4*>(arow[mt] + k0 + 8 * kk);
-    };
-    auto load_w = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < WUNITS; ++i) {
-            const int u = tid + i * THREADS;
-            const int row = u / (GK / 8), c = u % (GK / 8);
-            wreg[i] = *reinterpret_cast<const uint4*>(w1 + (int64_t)row * d + k0 + 8 * c);
-        }
-    };
-    auto store_w = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < WUNITS; ++i) {
-            const int u = tid + i * THREADS;
-            const int row = u / (GK / 8), c = u % (GK / 8);
-            *reinterpret_cast<uint4*>(&wl[buf][row * W_STRIDE + 8 * c]) = wreg[i];
-        }
-    };
-
     const int nsteps = d / GK;
-    load_a(acur, 0);
-    load_w(0);
-    store_w(0);
+    // Each workgroup walks the k chunks starting at its own offset, so that
+    // concurrent workgroups read different column slices of their rows (and
+    // different memory channels); the contraction order does not matter.
+    const int rot = (int)(blockIdx.x % (unsigned)nsteps);
+
+    auto rot_k = [&](int step) {
+        const int r = step + rot;
+        return (r >= nsteps ? r - nsteps : r) * GK;
+    };
+#define TG_LOAD_A(dst, step)                                                                 \
+    do {                                                                                     \
+        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
+            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk)                                 \
+                dst[mt][kk] = ld16(arow[mt] + rot_k(step) + 8 * kk);                           \
+    } while (0)
+#define TG_LOAD_W(step)                                                                      \
+    do {                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < WUNITS; ++i)                                   \
+            wreg[i] = ld16(wbase + (int64_t)(R * i) * d + rot_k(step));                   \
+    } while (0)
+#define TG_STORE_W(buf)                                                                      \
+    do {                                                                                     \
+        _Pragma("unroll") for (int i = 0; i < WUNITS; ++i)                                   \
+            wl[buf][wpos(i)] = wreg[i];                                                       \
+    } while (0)
+#define TG_READ_B(dst, buf, kk)                                                              \
+    do {                                                                                     \
+        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                    \
+            dst[nt] = as_bf16x8(wl[buf][(nt * 4 + (kk)) * WAVE + rd_pos[kk]]);                \
+    } while (0)
+#define TG_MMA(cur, b, kk)                                                                   \
+    do {                                                                                     \
+        _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                    \
+            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                 \
+                acc[mt][nt] = mfma32(as_bf16x8(cur[mt][kk]), b[nt], acc[mt][nt]);            \
+    } while (0)
+    bf16x8 bA[NT], bB[NT];
+
+    // One k chunk: W1 of the next chunk and then the residual two chunks ahead
+    // are requested, this chunk's MFMAs run, and the W1 registers go to LDS
+    // (the in-order load counter lets that wait skip the residual loads).
+    // Prefetch addresses are clamped to the last chunk instead of branching,
+    // so the three-step body is straight-line code and the register ring
+    // rotates without copies; the clamped extra loads are never used.
+#define TG_STEP(s, cur, ahead)                                                               \
+    do {                                                                                     \
+        const int buf_ = (s) & 1;                                                            \
+        TG_LOAD_W(min((s) + 1, nsteps - 1));                                                 \
+        TG_LOAD_A(ahead, min((s) + 2, nsteps - 1));                                          \
+        __builtin_amdgcn_sched_barrier(0); /* keep the prefetch at the top */                \
+        /* B fragments double buffered across k slices: slice kk+1 is read */               \
+        /* from LDS while slice kk's MFMAs run.                              */               \
+        TG_READ_B(bA, buf_, 0);                                                              \
+        TG_READ_B(bB, buf_, 1);                                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        TG_MMA(cur, bA, 0);                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        TG_READ_B(bA, buf_, 2);                                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        TG_MMA(cur, bB, 1);                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        TG_READ_B(bB, buf_, 3);                                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        TG_MMA(cur, bA, 2);                                                                  \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        TG_MMA(cur, bB, 3);                                                                  \
+        TG_STORE_W(buf_ ^ 1);                                                                \
+        __syncthreads();                                                                     \
+    } while (0)
+
+    TG_LOAD_W(0);
+    TG_LOAD_A(a0, 0);
+    TG_LOAD_A(a1, min(1, nsteps - 1));
+    TG_STORE_W(0);
     __syncthreads();
-
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        const bool more = s + 1 < nsteps;
-        if (more) {
-            load_a(anext, (s + 1) * GK);
-            load_w((s + 1) * GK);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                const int row = wn * (DG / 2) + 32 * nt + l32;
-                const bf16x8 bv = as_bf16x8(
-                    *reinterpret_cast<const uint4*>(&wl[buf][row * W_STRIDE + 32 * hh + 8 * kk]));
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-                    acc[mt][nt] = mfma32(as_bf16x8(acur[mt][kk]), bv, acc[mt][nt]);
-            }
-        }
-        if (more) store_w(buf ^ 1);
-        __syncthreads();
-        if (more) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acur[mt][kk] = anext[mt][kk];
-        }
+    const int groups = nsteps / RING;
+    for (int g = 0; g < groups; ++g) {
+        const int s = g * RING;
+        TG_STEP(s, a0, a2);
+        TG_STEP(s + 1, a1, a0);
+        TG_STEP(s + 2, a2, a1);
     }
+    const int rest = nsteps - groups * RING;
+    if (rest > 0) TG_STEP(groups * RING, a0, a2);
+    if (rest > 1) TG_STEP(groups * RING + 1, a1, a0);
+#undef TG_STEP
+#undef TG_MMA
+#undef TG_READ_B
+#undef TG_STORE_W
+#undef TG_LOAD_W
+#undef TG_LOAD_A
 
-    // Epilogue: lane holds unit wn*DG/2 + 32nt + l32, tokens 8(r/4)+4hh+r%4 (+32mt).
+    // Epilogue: lane holds unit 32nt + l32 and tokens 8(r/4)+4hh+r%4 (+32mt).
     float bias[NT], wout[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int u = wn * (DG / 2) + 32 * nt + l32;
+        const int u = 32 * nt + l32;
         bias[nt] = b1 != nullptr ? to_f32(b1[u]) : 0.f;
         wout[nt] = to_f32(w2[u]);
     }
+    const float bout = b2 != nullptr ? to_f32(b2[0]) : 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float p = 0.f;
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) p = fmaf(wout[nt], gelu_erf(acc[mt][nt][r] + bias[nt]), p);
+            for (int nt = 0; nt < NT; ++nt) p = fmaf(wout[nt], gelu_fast(acc[mt][nt][r] + bias[nt]), p);
 #pragma unroll
             for (int o = 16; o > 0; o >>= 1) p += __shfl_xor(p, o, WAVE);
-            if (l32 == 0) red[wn][64 * wm + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4)] = p;
+            const int64_t t = tok0 + 64 * w + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
+            if (l32 == 0 && t < T) scores[t] = p + bout;
         }
-    }
-    __syncthreads();
-    if (tid < BM && tok0 + tid < T) {
-        float sum = red[0][tid] + red[1][tid];
-        if (b2 != nullptr) sum += to_f32(b2[0]);
-        scores[tok0 + tid] = sum;
     }
 }
 
@@ -190,19 +241,17 @@ template <int DG>
 hipError_t launch_gate_bf16_dg(const bf16* hidden, int64_t T, int d, const bf16* w1,
                                const bf16* b1, const bf16* w2, const bf16* b2, float* scores,
                                hipStream_t st) {
-    // Largest token tile that still gives at least two workgroups per CU.
+    // Largest token tile that still gives about two workgroups per CU (one
+    // wave with d_gate 256 would need 128 registers of W1 staging: not used).
     if (T >= 256 * 512) {
-        const int64_t blocks = (T + 255) / 256;
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4>), dim3(blocks), dim3(512), 0, st, hidden, T,
-                           d, w1, b1, w2, b2, scores);
-    } else if (T >= 128 * 512) {
-        const int64_t blocks = (T + 127) / 128;
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 2>), dim3(blocks), dim3(256), 0, st, hidden, T,
-                           d, w1, b1, w2, b2, scores);
-    } else {
-        const int64_t blocks = (T + 63) / 64;
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 1>), dim3(blocks), dim3(128), 0, st, hidden, T,
-                           d, w1, b1, w2, b2, scores);
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4>), dim3((T + 255) / 256), dim3(256), 0, st,
+                           hidden, T, d, w1, b1, w2, b2, scores);
+    } else if (DG == 256 || T >= 128 * 512) {
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 2>), dim3((T + 127) / 128), dim3(128), 0, st,
+                           hidden, T, d, w1, b1, w2, b2, scores);
+    } else if constexpr (DG != 256) {
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 1>), dim3((T + 63) / 64), dim3(64), 0, st,
+                           hidden, T, d, w1, b1, w2, b2, scores);
     }
     return hipGetLastError();
 }

@@ -16,8 +16,8 @@ constexpr int ROWS_PER_BLOCK = GATHER_THREADS / WAVE;
 constexpr int UNROLL = 4;
 
 __global__ __launch_bounds__(GATHER_THREADS) void gather_rows_kernel(
-    const uint4* __restrict__ hidden, int64_t T, int row_vecs, const float* __restrict__ scores,
-    const int32_t* __restrict__ kept, int64_t Kt, uint4* __restrict__ out,
+    const u32x4* __restrict__ hidden, int64_t T, int row_vecs, const float* __restrict__ scores,
+    const int32_t* __restrict__ kept, int64_t Kt, u32x4* __restrict__ out,
     float* __restrict__ s_out) {
     const int lane = lane_id();
     const int64_t stride = (int64_t)gridDim.x * ROWS_PER_BLOCK;
@@ -27,11 +27,11 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_rows_kernel(
         const bool ok = src >= 0 && (int64_t)src < T;
         if (s_out != nullptr && lane == 0) s_out[row] = ok ? scores[src] : __builtin_nanf("");
         if (!ok) continue;
-        const uint4* s = hidden + (int64_t)src * row_vecs;
-        uint4* d = out + row * row_vecs;
+        const u32x4* s = hidden + (int64_t)src * row_vecs;
+        u32x4* d = out + row * row_vecs;
         int c = lane;
         for (; c + (UNROLL - 1) * WAVE < row_vecs; c += UNROLL * WAVE) {
-            uint4 t[UNROLL];
+            u32x4 t[UNROLL];
 #pragma unroll
             for (int u = 0; u < UNROLL; ++u) t[u] = s[c + u * WAVE];
 #pragma unroll
@@ -49,8 +49,8 @@ hipError_t launch_gather(const void* hidden, int64_t T, int row_bytes, const flo
     const int64_t want = (Kt + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
     const int blocks = (int)(want < 65536 ? want : 65536);
     hipLaunchKernelGGL(gather_rows_kernel, dim3(blocks), dim3(GATHER_THREADS), 0, st,
-                       (const uint4*)hidden, T, row_bytes / 16, scores, kept, Kt,
-                       (uint4*)hidden_kept, scores_kept);
+                       (const u32x4*)hidden, T, row_bytes / 16, scores, kept, Kt,
+                       (u32x4*)hidden_kept, scores_kept);
     return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(const bf16* __restr
     const int n0 = blockIdx.y * LB;
 
     // 16-byte units of one 128x64 chunk: 1024, four per thread.
-    uint4 xr[4], wr[4];
+    u32x4 xr[4], wr[4];
     auto load = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -62,8 +62,8 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(const bf16* __restr
             if (mr > M - 1) mr = M - 1;
             int nr = n0 + row;
             if (nr > N - 1) nr = N - 1;
-            xr[i] = *reinterpret_cast<const uint4*>(x + mr * K + k0 + 8 * c);
-            wr[i] = *reinterpret_cast<const uint4*>(w + (int64_t)nr * K + k0 + 8 * c);
+            xr[i] = ld16(x + mr * K + k0 + 8 * c);
+            wr[i] = ld16(w + (int64_t)nr * K + k0 + 8 * c);
         }
     };
     auto store = [&](int buf) {
@@ -71,8 +71,8 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(const bf16* __restr
         for (int i = 0; i < 4; ++i) {
             const int uu = tid + i * 256;
             const int row = uu / (LK / 8), c = uu % (LK / 8);
-            *reinterpret_cast<uint4*>(&Xs[buf][row * LS + 8 * c]) = xr[i];
-            *reinterpret_cast<uint4*>(&Ws[buf][row * LS + 8 * c]) = wr[i];
+            st16(&Xs[buf][row * LS + 8 * c], xr[i]);
+            st16(&Ws[buf][row * LS + 8 * c], wr[i]);
         }
     };
 
@@ -97,10 +97,8 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(const bf16* __restr
             bf16x8 af[2], bfv[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                af[t] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    &Ws[buf][(64 * wn + 32 * t + l32) * LS + 32 * hh + 8 * kk]));
-                bfv[t] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                    &Xs[buf][(64 * wm + 32 * t + l32) * LS + 32 * hh + 8 * kk]));
+                af[t] = as_bf16x8(ld16(&Ws[buf][(64 * wn + 32 * t + l32) * LS + 32 * hh + 8 * kk]));
+                bfv[t] = as_bf16x8(ld16(&Xs[buf][(64 * wm + 32 * t + l32) * LS + 32 * hh + 8 * kk]));
             }
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)

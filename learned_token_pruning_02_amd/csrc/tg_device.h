@@ -22,6 +22,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+// Raw 16- and 8-byte payloads.  Native vector types (not HIP's uint4 struct)
+// so that arrays of them stay in registers instead of private memory.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 
@@ -29,13 +33,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
-    return __builtin_bit_cast(bf16x8, u);
-}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-__device__ __forceinline__ uint4 as_uint4(bf16x8 v) {
-    return __builtin_bit_cast(uint4, v);
-}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
 // Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
@@ -50,6 +53,25 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf
 // Exact GELU, z * Phi(z) = z/2 * (1 + erf(z / sqrt 2)), with the device erff.
 __device__ __forceinline__ float gelu_erf(float z) {
     return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+
+// GELU with erf from Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (Hastings' approximation): for x >= 0
+//     erf(x) ~= 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//     t = 1 / (1 + p x),
+// with |error| <= 1.5e-7, and erf(-x) = -erf(x).  Branch-free; used where
+// the result feeds a bf16 pipeline.
+__device__ __forceinline__ float gelu_fast(float z) {
+    constexpr float p = 0.3275911f;
+    constexpr float a1 = 0.254829592f, a2 = -0.284496736f, a3 = 1.421413741f;
+    constexpr float a4 = -1.453152027f, a5 = 1.061405429f;
+    const float x = fabsf(z) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(p, x, 1.0f));
+    const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+    const float e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);
+    const float erf_abs = fmaf(-poly, e, 1.0f);
+    const float erf_z = copysignf(erf_abs, z);
+    return 0.5f * z * (1.0f + erf_z);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
