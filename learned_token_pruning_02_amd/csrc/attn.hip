@@ -7,7 +7,8 @@
 // bf16 path, flash style (exact softmax computed online, never materialising
 // the score matrix): a workgroup of 4 waves owns one KV head, HPB query heads
 // that share it and BQ = 128/HPB query rows of one request.  Each wave owns
-// 32 query rows of one head.  Per 64-key tile:
+// 32 query rows of one head; two workgroups share a CU so one wave's softmax
+// overlaps the other's MFMAs.  Per 64-key tile:
 //   S^T[key][query] = K . Q^T with the 32x32x16 bf16 MFMA: K fragments from
 //     LDS (A operand), Q fragments resident in registers (B operand), so each
 //     lane holds all scores of ONE query row and the row max / row sum need
@@ -18,7 +19,10 @@
 //     the probabilities, converted to bf16, are fed straight from the S
 //     registers as the B operand, again one query per lane, so the online
 //     rescale of O needs no data exchange.
-// Only the tiles on the diagonal (or past the end of the request) are masked.
+// Only the tiles on the diagonal (or past the end of the request) are masked,
+// and a wave skips tiles whose keys all lie after its rows.  The exponent base
+// of each row only moves when the row max exceeds it by more than 2^8, so the
+// rescale of O is rare; the final O / l and lse are exact either way.
 // K/V tiles are double buffered: the next tile is fetched into registers
 // while the current one is consumed.  Heavy query tiles (many keys) are
 // dispatched first and consecutive workgroup ids cycle over the KV heads, so
@@ -117,6 +121,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     constexpr int VU = (KVT / 4) * (DH / 8);  // V units (4 keys x 8 dh) per tile
     constexpr int NKK = DH / 16;       // k steps of the QK^T product
     constexpr int NMD = DH / 32;       // 32-row dh tiles of O^T
+    constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before O is rescaled
 
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][KVT * KS];
     __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * VT_STRIDE];
@@ -168,11 +173,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     bf16x8 qf[NKK];
     {
         const bf16* qp = a.q + ((rbase + (qvalid ? qi : 0)) * a.Hq + h) * DH + (DH / 2) * hh;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            qf[kk] = as_bf16x8(qvalid ? ld16(qp + 8 * kk) : zero);
-        }
+        for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(qvalid ? ld16(qp + 8 * kk) : zero);
     }
     const float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
     const float g2 = a.gain[h] * LOG2E;
@@ -227,92 +230,86 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int md = 0; md < NMD; ++md)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[md][r] = 0.f;
-    float m = -INFINITY, lpart = 0.f;
+    float m = -INFINITY, lpart = 0.f;  // exponent base (log2 units) and this lane's row-sum half
 
     load_tile(0);
     store_tile(0);
     __syncthreads();
 
+    // One 64-key tile.  MASKED adds the causal mask (diagonal tile only); the
+    // exponent base m of a row moves only when the row max exceeds it by more
+    // than RESCALE_SLACK (log2 units), so the O rescale is rare.
+#define TG_TILE(MASKED)                                                                      \
+    do {                                                                                     \
+        f32x16 sacc[2];                                                                      \
+        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;                \
+        _Pragma("unroll") for (int kk = 0; kk < NKK; ++kk) {                                 \
+            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                               \
+                const bf16x8 kf = as_bf16x8(                                                 \
+                    ld16(&Ks[buf][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));          \
+                sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);                                     \
+            }                                                                                \
+        }                                                                                    \
+        float mx = -INFINITY;                                                                \
+        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                                   \
+            _Pragma("unroll") for (int rq = 0; rq < 4; ++rq) {                               \
+                const int kl = 32 * mt + 8 * rq + 4 * hh;                                    \
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(&Ss[buf][kl]);              \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e) {                              \
+                    float x = fmaf(c1, sacc[mt][4 * rq + e], g2 * sv[e]);                    \
+                    if (MASKED && j0 + kl + e > qi) x = -INFINITY;                           \
+                    sacc[mt][4 * rq + e] = x;                                                \
+                    mx = fmaxf(mx, x);                                                       \
+                }                                                                            \
+            }                                                                                \
+        }                                                                                    \
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                            \
+        if (__any(mx > m + RESCALE_SLACK)) {                                                 \
+            const float m_new = mx > m + RESCALE_SLACK ? mx : m;                             \
+            const float alpha = m_new == m ? 1.f : __builtin_amdgcn_exp2f(m - m_new);         \
+            lpart *= alpha;                                                                  \
+            _Pragma("unroll") for (int md = 0; md < NMD; ++md)                               \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r) o[md][r] *= alpha;            \
+            m = m_new;                                                                       \
+        }                                                                                    \
+        const float mb = m == -INFINITY ? 0.f : m;                                           \
+        float psum = 0.f;                                                                    \
+        bf16x8 pf[4];                                                                        \
+        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                   \
+            _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                  \
+                const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - mb);  \
+                psum += p;                                                                   \
+                pf[kk][e] = to_bf16(p);                                                      \
+            }                                                                                \
+        }                                                                                    \
+        lpart += psum;                                                                       \
+        _Pragma("unroll") for (int md = 0; md < NMD; ++md) {                                 \
+            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                               \
+                const bf16* vrow = &Vt[buf][(32 * md + l32) * VT_STRIDE + 16 * kk + 4 * hh]; \
+                const u32x2 lo = ld8(vrow);                                                  \
+                const u32x2 hi = ld8(vrow + 8);                                              \
+                const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};                             \
+                o[md] = mfma32(as_bf16x8(both), pf[kk], o[md]);                              \
+            }                                                                                \
+        }                                                                                    \
+    } while (0)
+
+    // Tiles strictly before this wave's rows need no mask; the tile holding
+    // the wave's first row is the diagonal one; later tiles are all masked
+    // out for this wave and skipped (the workgroup still stages them).
+    const int jt_diag = qmin / KVT;
     for (int jt = 0; jt < nkv; ++jt) {
         const int buf = jt & 1;
         const bool more = jt + 1 < nkv;
         if (more) load_tile(jt + 1);
-
-        // S^T = K Q^T for 64 keys x 32 queries.
-        f32x16 sacc[2];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const bf16x8 kf =
-                    as_bf16x8(ld16(&Ks[buf][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));
-                sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);
-            }
-        }
-
-        // Scale, bias, causal mask; lane holds keys 32mt + 8(r/4) + 4hh + r%4.
         const int j0 = jt * KVT;
-        const bool need_mask = j0 + KVT - 1 > qmin;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {
-                const int kl = 32 * mt + 8 * rq + 4 * hh;
-                const f32x4 sv = *reinterpret_cast<const f32x4*>(&Ss[buf][kl]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float x = fmaf(c1, sacc[mt][4 * rq + e], g2 * sv[e]);
-                    if (need_mask && j0 + kl + e > qi) x = -INFINITY;
-                    sacc[mt][4 * rq + e] = x;
-                    mx = fmaxf(mx, x);
-                }
-            }
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
-        const float m_new = fmaxf(m, mx);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-        float psum = 0.f;
-        bf16x8 pf[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - m_use);
-                psum += p;
-                pf[kk][e] = to_bf16(p);
-            }
-        }
-        lpart = fmaf(lpart, alpha, psum);
-        m = m_new;
-#pragma unroll
-        for (int md = 0; md < NMD; ++md)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[md][r] *= alpha;
-
-        // O^T += V^T P^T; the key order of the P fragment (registers
-        // 8(kk%2)..+7 of tile kk/2) is keys 16kk + 4hh + {0..3, 8..11}.
-#pragma unroll
-        for (int md = 0; md < NMD; ++md) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const bf16* vrow = &Vt[buf][(32 * md + l32) * VT_STRIDE + 16 * kk + 4 * hh];
-                const u32x2 lo = ld8(vrow);
-                const u32x2 hi = ld8(vrow + 8);
-                const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
-                const bf16x8 vf = as_bf16x8(both);
-                o[md] = mfma32(vf, pf[kk], o[md]);
-            }
-        }
-
+        if (jt < jt_diag) TG_TILE(false);
+        else if (jt == jt_diag) TG_TILE(true);
         if (more) store_tile(buf ^ 1);
         __syncthreads();
     }
+#undef TG_TILE
 
     // ---- normalise and store ------------------------------------------------
     const float l = lpart + __shfl_xor(lpart, 32, WAVE);
