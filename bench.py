@@ -37,7 +37,30 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--detail", default="", help="also write per-kernel detail JSON to this path")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain device copy of 512 MiB (reference for HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of exactly 512 MiB, timed; run under a
+    counter collector, its FETCH_SIZE / WRITE_SIZE readings give the factor
+    that turns those counters into bytes."""
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "ms": ms,
+                      "GB/s_read_plus_write": 2 * n / ms / 1e6}), flush=True)
 
 
 def algorithmic(w, Kt_per_req):
@@ -55,6 +78,28 @@ def algorithmic(w, Kt_per_req):
         "attention": {"bytes": Kt * (sh.n_q_heads * 2 + sh.n_kv_heads * 2) * sh.d_head * eb + Kt * 4,
                       "flops": 4 * sh.d_head * sh.n_q_heads * pairs},
     }
+
+
+KERNEL_FRAG = {"gate": "gate_bf16_kernel", "select": "sel_cand_kernel",
+               "gather": "gather_rows_kernel", "attention": "attn_bf16_kernel"}
+
+
+def recorded_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from a committed counter record of this
+    workload, or None when there is none or the kernel source changed since."""
+    import glob
+    import hashlib
+    frag = KERNEL_FRAG[kernel]
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.json"))):
+        rec = json.load(open(f))
+        if not rec.get("workload", "").startswith(workload) or frag not in rec.get("kernels", {}):
+            continue
+        k = rec["kernels"][frag]
+        with open(os.path.join(ROOT, k["source"]), "rb") as src:
+            if hashlib.sha256(src.read()).hexdigest() != k["source_sha256"]:
+                return None
+        return k["read_bytes"] + k["written_bytes"]
+    return None
 
 
 def cpu_baseline(w, gi, ai, s_gpu, kept, cu):
@@ -102,6 +147,9 @@ def cpu_baseline(w, gi, ai, s_gpu, kept, cu):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path is single-GPU; sharding is a design note, not built)", file=sys.stderr)
@@ -200,7 +248,7 @@ def main():
         roof = {"bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(w.name, dominant)
     roof["kernel"] = dominant
 
     cpu = None
