@@ -125,7 +125,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][KVT * KS];
     __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * VT_STRIDE];
-    __shared__ __attribute__((aligned(16))) float Ss[2][KVT];
+    // Per key of the tile and per head of the workgroup: g_h log2(e) s_j.
+    __shared__ __attribute__((aligned(16))) float Bs[2][HPB][KVT];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -164,7 +165,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     const int nkv = (kend + KVT - 1) / KVT;
     const int group = a.Hq / a.Hkv;
     const int kvh = (hg * HPB) / group;
-    const int h = hg * HPB + w / WPH;
+    const int hp = w / WPH;  // head of this wave within the workgroup
+    const int h = hg * HPB + hp;
     const int qmin = q0 + 32 * (w % WPH);  // first query row of this wave
     const int qi = qmin + l32;               // this lane's query row
     const bool qvalid = qi < n;
@@ -178,7 +180,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(qvalid ? ld16(qp + 8 * kk) : zero);
     }
     const float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
-    const float g2 = a.gain[h] * LOG2E;
+    float gbias[HPB];
+#pragma unroll
+    for (int j = 0; j < HPB; ++j) gbias[j] = a.gain[hg * HPB + j] * LOG2E;
 
     // ---- K/V/s tile staging ------------------------------------------------
     u32x4 kreg[KU];
@@ -212,6 +216,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         }
         if (tid < VU) {
             const int kg = tid % (KVT / 4), dg = tid / (KVT / 4);
+            // Keys 16G + 4h + {0..3} and 16G + 8 + 4h + {0..3} (one PV operand
+            // of lane half h) are stored next to each other at 16G + 8h.
+            const int vpos = 16 * (kg / 4) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
             // Transpose 4 keys x 8 dh: element e of a row is half e%2 of word e/2.
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -219,10 +226,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 u32x2 pk;
                 pk[0] = ((vreg[0][wd] >> sh) & 0xffffu) | (((vreg[1][wd] >> sh) & 0xffffu) << 16);
                 pk[1] = ((vreg[2][wd] >> sh) & 0xffffu) | (((vreg[3][wd] >> sh) & 0xffffu) << 16);
-                st8(&Vt[buf][(8 * dg + e) * VT_STRIDE + 4 * kg], pk);
+                st8(&Vt[buf][(8 * dg + e) * VT_STRIDE + vpos], pk);
             }
         }
-        if (tid < KVT) Ss[buf][tid] = sreg;
+        if (tid < KVT) {
+#pragma unroll
+            for (int j = 0; j < HPB; ++j) Bs[buf][j][tid] = gbias[j] * sreg;
+        }
     };
 
     f32x16 o[NMD];
@@ -255,9 +265,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                                   \
             _Pragma("unroll") for (int rq = 0; rq < 4; ++rq) {                               \
                 const int kl = 32 * mt + 8 * rq + 4 * hh;                                    \
-                const f32x4 sv = *reinterpret_cast<const f32x4*>(&Ss[buf][kl]);              \
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(&Bs[buf][hp][kl]);          \
                 _Pragma("unroll") for (int e = 0; e < 4; ++e) {                              \
-                    float x = fmaf(c1, sacc[mt][4 * rq + e], g2 * sv[e]);                    \
+                    float x = fmaf(c1, sacc[mt][4 * rq + e], sv[e]);                         \
                     if (MASKED && j0 + kl + e > qi) x = -INFINITY;                           \
                     sacc[mt][4 * rq + e] = x;                                                \
                     mx = fmaxf(mx, x);                                                       \
@@ -286,11 +296,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         lpart += psum;                                                                       \
         _Pragma("unroll") for (int md = 0; md < NMD; ++md) {                                 \
             _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                               \
-                const bf16* vrow = &Vt[buf][(32 * md + l32) * VT_STRIDE + 16 * kk + 4 * hh]; \
-                const u32x2 lo = ld8(vrow);                                                  \
-                const u32x2 hi = ld8(vrow + 8);                                              \
-                const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};                             \
-                o[md] = mfma32(as_bf16x8(both), pf[kk], o[md]);                              \
+                const bf16x8 vf = as_bf16x8(                                                 \
+                    ld16(&Vt[buf][(32 * md + l32) * VT_STRIDE + 16 * kk + 8 * hh]));          \
+                o[md] = mfma32(vf, pf[kk], o[md]);                                           \
             }                                                                                \
         }                                                                                    \
     } while (0)
