@@ -41,6 +41,7 @@ constexpr int SCHUNK = SB * SITEMS;     // 2048 keys per chunk
 constexpr int NBIN = 2048;
 constexpr int META = 8;                 // u32 words of per-request metadata
 constexpr int CTR = 4;                  // u32 counters per request
+constexpr uint32_t CAND_LDS = 8192;     // threshold-bucket candidates staged in LDS
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -198,6 +199,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     __shared__ uint32_t wtot[SWAVES];
     __shared__ uint32_t sh_base, sh_last, sh_d, sh_gt, sh_cnt, sh_total;
     __shared__ uint32_t h[NBIN];
+    __shared__ uint2 cl[CAND_LDS];
     const int tid = threadIdx.x;
     const int b = find_request(a.doc_chunk0, a.batch, blockIdx.x);
     const int c = blockIdx.x - a.doc_chunk0[b];
@@ -243,23 +245,31 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     __threadfence();
 
     // ---- the last chunk: exact rank inside bucket d1 ----------------------
+    // Candidates are staged once into LDS when they fit (the usual case: a
+    // bucket holds a few thousand keys); a degenerate bucket (heavy ties) is
+    // read from global memory on every pass instead.
     const uint32_t cnt1 = m[2];
+    const bool in_lds = cnt1 <= CAND_LDS;
+    if (in_lds)
+        for (uint32_t j = tid; j < cnt1; j += SB) cl[j] = coherent_load2(&cand[j]);
+    __syncthreads();
+    auto cand_at = [&](uint32_t j) { return in_lds ? cl[j] : coherent_load2(&cand[j]); };
     uint32_t rem = m[1];
     uint64_t cprefix = 0, cmask = 0;
-    const int shifts[5] = {41, 31, 20, 9, 0};
-    const int widths[5] = {11, 10, 11, 11, 9};
+#pragma unroll 1
     for (int p = 0; p < 5; ++p) {
-        const int sh = shifts[p];
-        const int nb = 1 << widths[p];
+        const int sh = p == 0 ? 41 : (p == 1 ? 31 : (p == 2 ? 20 : (p == 3 ? 9 : 0)));
+        const int wd = p == 1 ? 10 : (p == 4 ? 9 : 11);
+        const int nb = 1 << wd;
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
         __syncthreads();
         for (uint32_t j = tid; j < cnt1; j += SB) {
-            const uint2 e = coherent_load2(&cand[j]);
+            const uint2 e = cand_at(j);
             const uint64_t cp = composite(e.x, e.y);
             if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        find_bin([&](int i) { return h[i]; }, nb < SB ? SB : nb, rem, wtot, &sh_d, &sh_gt, &sh_cnt);
+        find_bin([&](int i) { return h[i]; }, nb, rem, wtot, &sh_d, &sh_gt, &sh_cnt);
         rem -= sh_gt;
         cprefix |= (uint64_t)sh_d << sh;
         cmask |= (uint64_t)(nb - 1) << sh;
@@ -277,7 +287,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
         __syncthreads();
         for (uint32_t j = tid; j < cnt1; j += SB) {
-            const uint2 e = coherent_load2(&cand[j]);
+            const uint2 e = cand_at(j);
             const int ch = (int)(e.y / SCHUNK) - c0;
             if (ch >= 0 && ch < NBIN && (composite(e.x, e.y) & cmask) >= cprefix)
                 atomicAdd(&ccnt[ch], 1u);
