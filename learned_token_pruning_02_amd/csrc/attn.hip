@@ -5,10 +5,11 @@
 //     l_ij = temp[h] * (q_i . k_j) / sqrt(d_head) + gain[h] * s_j
 //
 // bf16 path, flash style (exact softmax computed online, never materialising
-// the score matrix): a workgroup of 4 waves owns one KV head, HPB query heads
-// that share it and BQ = 128/HPB query rows of one request.  Each wave owns
-// 32 query rows of one head; two workgroups share a CU so one wave's softmax
-// overlaps the other's MFMAs.  Per 64-key tile:
+// the score matrix): a workgroup of 8 waves (two per SIMD, so one wave's
+// softmax overlaps the other's MFMAs) owns one KV head, HPB query heads that
+// share it and BQ = 256/HPB query rows of one request; each wave owns 32 query
+// rows of one head, and every K/V tile staged in LDS feeds all eight waves.
+// Per 64-key tile:
 //   S^T[key][query] = K . Q^T with the 32x32x16 bf16 MFMA: K fragments from
 //     LDS (A operand), Q fragments resident in registers (B operand), so each
 //     lane holds all scores of ONE query row and the row max / row sum need
@@ -112,12 +113,13 @@ __device__ __forceinline__ int tiles_at_or_above(const AttnArgs& a, int t) {
     return c;
 }
 
-template <int DH, int HPB>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-    constexpr int WPH = 4 / HPB;       // waves per head
+template <int DH, int HPB, int NWAVE>
+__global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnArgs a) {
+    // NWAVE = 8: two waves per SIMD from one workgroup; 4: two workgroups per CU.
+    constexpr int WPH = NWAVE / HPB;   // waves per head
     constexpr int BQ = 32 * WPH;       // query rows per head per workgroup
     constexpr int KS = DH + 8;         // LDS row stride of K (bf16 elements)
-    constexpr int KU = KVT * DH / 8 / 256;  // 16-byte K units per thread per tile
+    constexpr int KU = KVT * DH / 8 / 256;  // 16-byte K units per staging thread per tile
     constexpr int VU = (KVT / 4) * (DH / 8);  // V units (4 keys x 8 dh) per tile
     constexpr int NKK = DH / 16;       // k steps of the QK^T product
     constexpr int NMD = DH / 32;       // 32-row dh tiles of O^T
@@ -188,50 +190,63 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     u32x4 kreg[KU];
     u32x4 vreg[4];
     float sreg = 0.f;
+    // With 8 waves, threads [0, 256) stage V (transposed) and the bias and
+    // threads [256, 512) stage K; with 4 waves every thread stages both.
+    const bool kstager = NWAVE == 8 ? tid >= 256 : true;
+    const bool vstager = NWAVE == 8 ? tid < 256 : true;
+    const int st = tid & 255;
     auto load_tile = [&](int jt) {
         const int j0 = jt * KVT;
+        if (kstager) {
 #pragma unroll
-        for (int i = 0; i < KU; ++i) {
-            const int uu = tid + i * 256;
-            const int row = uu / (DH / 8), c = uu % (DH / 8);
-            const int key = min(j0 + row, n - 1);
-            kreg[i] = ld16(a.k + ((rbase + key) * a.Hkv + kvh) * DH + 8 * c);
-        }
-        if (tid < VU) {
-            const int kg = tid % (KVT / 4), dg = tid / (KVT / 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = min(j0 + 4 * kg + i, n - 1);
-                vreg[i] = ld16(a.v + ((rbase + key) * a.Hkv + kvh) * DH + 8 * dg);
+            for (int i = 0; i < KU; ++i) {
+                const int uu = st + i * 256;
+                const int row = uu / (DH / 8), c = uu % (DH / 8);
+                const int key = min(j0 + row, n - 1);
+                kreg[i] = ld16(a.k + ((rbase + key) * a.Hkv + kvh) * DH + 8 * c);
             }
         }
-        if (tid < KVT) sreg = a.s[rbase + min(j0 + tid, n - 1)];
+        if (vstager) {
+            if (st < VU) {
+                const int kg = st % (KVT / 4), dg = st / (KVT / 4);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = min(j0 + 4 * kg + i, n - 1);
+                    vreg[i] = ld16(a.v + ((rbase + key) * a.Hkv + kvh) * DH + 8 * dg);
+                }
+            }
+            if (st < KVT) sreg = a.s[rbase + min(j0 + st, n - 1)];
+        }
     };
     auto store_tile = [&](int buf) {
+        if (kstager) {
 #pragma unroll
-        for (int i = 0; i < KU; ++i) {
-            const int uu = tid + i * 256;
-            const int row = uu / (DH / 8), c = uu % (DH / 8);
-            st16(&Ks[buf][row * KS + 8 * c], kreg[i]);
-        }
-        if (tid < VU) {
-            const int kg = tid % (KVT / 4), dg = tid / (KVT / 4);
-            // Keys 16G + 4h + {0..3} and 16G + 8 + 4h + {0..3} (one PV operand
-            // of lane half h) are stored next to each other at 16G + 8h.
-            const int vpos = 16 * (kg / 4) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
-            // Transpose 4 keys x 8 dh: element e of a row is half e%2 of word e/2.
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int wd = e / 2, sh = 16 * (e % 2);
-                u32x2 pk;
-                pk[0] = ((vreg[0][wd] >> sh) & 0xffffu) | (((vreg[1][wd] >> sh) & 0xffffu) << 16);
-                pk[1] = ((vreg[2][wd] >> sh) & 0xffffu) | (((vreg[3][wd] >> sh) & 0xffffu) << 16);
-                st8(&Vt[buf][(8 * dg + e) * VT_STRIDE + vpos], pk);
+            for (int i = 0; i < KU; ++i) {
+                const int uu = st + i * 256;
+                const int row = uu / (DH / 8), c = uu % (DH / 8);
+                st16(&Ks[buf][row * KS + 8 * c], kreg[i]);
             }
         }
-        if (tid < KVT) {
+        if (vstager) {
+            if (st < VU) {
+                const int kg = st % (KVT / 4), dg = st / (KVT / 4);
+                // Keys 16G + 4h + {0..3} and 16G + 8 + 4h + {0..3} (one PV operand
+                // of lane half h) are stored next to each other at 16G + 8h.
+                const int vpos = 16 * (kg / 4) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+                // Transpose 4 keys x 8 dh: element e of a row is half e%2 of word e/2.
 #pragma unroll
-            for (int j = 0; j < HPB; ++j) Bs[buf][j][tid] = gbias[j] * sreg;
+                for (int e = 0; e < 8; ++e) {
+                    const int wd = e / 2, sh = 16 * (e % 2);
+                    u32x2 pk;
+                    pk[0] = ((vreg[0][wd] >> sh) & 0xffffu) | (((vreg[1][wd] >> sh) & 0xffffu) << 16);
+                    pk[1] = ((vreg[2][wd] >> sh) & 0xffffu) | (((vreg[3][wd] >> sh) & 0xffffu) << 16);
+                    st8(&Vt[buf][(8 * dg + e) * VT_STRIDE + vpos], pk);
+                }
+            }
+            if (st < KVT) {
+#pragma unroll
+                for (int j = 0; j < HPB; ++j) Bs[buf][j][st] = gbias[j] * sreg;
+            }
         }
     };
 
@@ -338,11 +353,33 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
 }
 
-template <int DH, int HPB>
+template <int DH, int HPB, int NWAVE>
 hipError_t launch_bf16(const AttnArgs& a, int total_tiles, hipStream_t st) {
     const int blocks = total_tiles * a.n_hg;
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB>), dim3(blocks), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB, NWAVE>), dim3(blocks), dim3(64 * NWAVE), 0, st, a);
     return hipGetLastError();
+}
+
+template <int DH, int HPB>
+hipError_t launch_bf16_w(AttnArgs& a, const AttnShape& sh, hipStream_t st) {
+    // Eight-wave workgroups (K/V staged once for 256 query rows) unless that
+    // leaves fewer than two workgroups per CU; then four-wave workgroups.
+    auto tiles = [&](int bq) {
+        int total = 0, mx = 0;
+        for (int b = 0; b < sh.batch; ++b) {
+            const int nt = (sh.cu[b + 1] - sh.cu[b] + bq - 1) / bq;
+            a.ntiles[b] = nt;
+            total += nt;
+            mx = nt > mx ? nt : mx;
+        }
+        a.max_tiles = mx;
+        return total;
+    };
+    const int t8 = tiles(256 / HPB);
+    if (t8 * a.n_hg >= 512) return launch_bf16<DH, HPB, 8>(a, t8, st);
+    const int t4 = tiles(128 / HPB);
+    if (t4 == 0) return hipSuccess;
+    return launch_bf16<DH, HPB, 4>(a, t4, st);
 }
 
 }  // namespace
@@ -366,7 +403,6 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const f
                             float* lse, hipStream_t st) {
     const int group = sh.Hq / sh.Hkv;
     const int hpb = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-    const int bq = 128 / hpb;
     AttnArgs a;
     a.q = (const bf16*)q;
     a.k = (const bf16*)k;
@@ -381,24 +417,16 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const f
     a.Hkv = sh.Hkv;
     a.n_hg = sh.Hq / hpb;
     a.batch = sh.batch;
-    int total = 0, mx = 0;
     for (int b = 0; b <= sh.batch; ++b) a.cu[b] = sh.cu[b];
-    for (int b = 0; b < sh.batch; ++b) {
-        const int nt = (sh.cu[b + 1] - sh.cu[b] + bq - 1) / bq;
-        a.ntiles[b] = nt;
-        total += nt;
-        mx = nt > mx ? nt : mx;
-    }
-    a.max_tiles = mx;
-    if (total == 0) return hipSuccess;
+    if (sh.Kt == 0) return hipSuccess;
     if (sh.d_head == 64) {
-        if (hpb == 4) return launch_bf16<64, 4>(a, total, st);
-        if (hpb == 2) return launch_bf16<64, 2>(a, total, st);
-        return launch_bf16<64, 1>(a, total, st);
+        if (hpb == 4) return launch_bf16_w<64, 4>(a, sh, st);
+        if (hpb == 2) return launch_bf16_w<64, 2>(a, sh, st);
+        return launch_bf16_w<64, 1>(a, sh, st);
     }
-    if (hpb == 4) return launch_bf16<128, 4>(a, total, st);
-    if (hpb == 2) return launch_bf16<128, 2>(a, total, st);
-    return launch_bf16<128, 1>(a, total, st);
+    if (hpb == 4) return launch_bf16_w<128, 4>(a, sh, st);
+    if (hpb == 2) return launch_bf16_w<128, 2>(a, sh, st);
+    return launch_bf16_w<128, 1>(a, sh, st);
 }
 
 }  // namespace tg
