@@ -172,8 +172,14 @@ tg_status tg_gather_compact(tg_dtype dt, const void *hidden, int64_t T, int32_t 
  * cu_kept_host : [batch+1] HOST int32, cu_kept_host[0] == 0, non-decreasing
  * out : [Kt][Hq][d_head] in dt output
  * lse : [Hq][Kt] fp32 output, or NULL
- * Supported: d_head in {64, 128}, Hq % Hkv == 0, 1 <= batch <= TG_MAX_BATCH.
+ * Supported: d_head in {64, 128}, Hq % Hkv == 0, 1 <= batch <= TG_MAX_BATCH;
+ * for TG_BF16 the K (and V) rows of one request span less than 2 GiB,
+ * (cu_kept_host[b+1] - cu_kept_host[b]) * Hkv * d_head * 2 < 2^31, else
+ * TG_ERR_UNSUPPORTED.
  * Only K/V rows of kept tokens exist: nothing of size N is read or written.
+ * Errors: TG_ERR_BAD_DTYPE, TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE (batch, heads,
+ * cu_kept_host), TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT, TG_ERR_ALIAS,
+ * TG_ERR_LAUNCH.
  */
 tg_status tg_gated_attn_prefill(tg_dtype dt, const void *q, const void *k, const void *v,
                                 const float *s_kept, const float *gain, const float *temp,

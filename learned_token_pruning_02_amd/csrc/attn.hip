@@ -104,6 +104,8 @@ struct AttnArgs {
 };
 
 constexpr int KVT = 64;          // keys per tile
+// Fourth word of a raw buffer resource (32-bit data format, no swizzle).
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 constexpr int VT_STRIDE = KVT + 8;  // LDS row stride of V^T (bf16 elements)
 
 // Number of query tiles whose local index is >= t.
@@ -124,6 +126,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     constexpr int NKK = DH / 16;       // k steps of the QK^T product
     constexpr int NMD = DH / 32;       // 32-row dh tiles of O^T
     constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before O is rescaled
+    constexpr int SM_VALU = 256 / (4 * NMD);  // softmax VALU slots next to each PV MFMA
 
     __shared__ __attribute__((aligned(16))) bf16 Ks[2][KVT * KS];
     __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * VT_STRIDE];
@@ -132,7 +135,9 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
-    const int w = tid / WAVE;
+    // Wave index, read through a scalar register so that the compiler treats
+    // everything derived from it (rows, loop bounds, buffer bases) as uniform.
+    const int w = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int hh = lane / 32;
     const int l32 = lane % 32;
 
@@ -187,38 +192,60 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     for (int j = 0; j < HPB; ++j) gbias[j] = a.gain[hg * HPB + j] * LOG2E;
 
     // ---- K/V/s tile staging ------------------------------------------------
-    u32x4 kreg[KU];
-    u32x4 vreg[4];
+    // K (with the score bias) is staged for tile jt+1 while V is staged one
+    // tile behind, for tile jt: iteration jt computes QK and the softmax of
+    // tile jt next to the PV product of tile jt-1, so each wave overlaps its
+    // own VALU work with MFMAs.  With 8 waves, threads [0, 256) stage V and
+    // threads [256, 512) stage K and the bias; with 4 waves every thread does both.
+    // With 8 waves a thread stages either K or V, so both share one register array.
+    constexpr int NSTG = NWAVE == 8 ? (KU > 4 ? KU : 4) : KU + 4;
+    u32x4 stg[NSTG];
+    u32x4* const kreg = stg;
+    u32x4* const vreg = NWAVE == 8 ? stg : stg + KU;
     float sreg = 0.f;
-    // With 8 waves, threads [0, 256) stage V (transposed) and the bias and
-    // threads [256, 512) stage K; with 4 waves every thread stages both.
-    const bool kstager = NWAVE == 8 ? tid >= 256 : true;
-    const bool vstager = NWAVE == 8 ? tid < 256 : true;
+    const bool kstager = NWAVE == 8 ? w >= 4 : true;
+    const bool vstager = NWAVE == 8 ? w < 4 : true;
     const int st = tid & 255;
-    auto load_tile = [&](int jt) {
+    // Tiles are read through buffer resources whose base is the tile's first
+    // key and whose size ends at the request's last key: the per-lane offsets
+    // stay fixed from tile to tile, and keys past the request read as zero
+    // (those keys are masked, and 0 * V = 0 keeps the PV product finite).
+    const int64_t row_elems = (int64_t)a.Hkv * DH;
+    auto tile_rsrc = [&](const bf16* base, int j0) {
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base + (rbase + j0) * row_elems + kvh * DH), (short)0,
+            (int)((n - j0) * row_elems * 2), BUFFER_RSRC_WORD3);
+    };
+    auto load_k = [&](int jt) {
         const int j0 = jt * KVT;
         if (kstager) {
+            const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k, j0);
 #pragma unroll
             for (int i = 0; i < KU; ++i) {
                 const int uu = st + i * 256;
                 const int row = uu / (DH / 8), c = uu % (DH / 8);
-                const int key = min(j0 + row, n - 1);
-                kreg[i] = ld16(a.k + ((rbase + key) * a.Hkv + kvh) * DH + 8 * c);
+                kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rk, (int)(row * row_elems * 2) + 16 * c, 0, 0);
             }
-        }
-        if (vstager) {
-            if (st < VU) {
-                const int kg = st % (KVT / 4), dg = st / (KVT / 4);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = min(j0 + 4 * kg + i, n - 1);
-                    vreg[i] = ld16(a.v + ((rbase + key) * a.Hkv + kvh) * DH + 8 * dg);
-                }
+            if (st < KVT) {
+                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)(a.s + rbase + j0), (short)0, (n - j0) * 4, BUFFER_RSRC_WORD3);
+                sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * st, 0, 0));
             }
-            if (st < KVT) sreg = a.s[rbase + min(j0 + st, n - 1)];
         }
     };
-    auto store_tile = [&](int buf) {
+    auto load_v = [&](int jt) {
+        const int j0 = jt * KVT;
+        if (vstager && st < VU) {
+            const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v, j0);
+            const int kg = st % (KVT / 4), dg = st / (KVT / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rv, (int)((4 * kg + i) * row_elems * 2) + 16 * dg, 0, 0);
+        }
+    };
+    auto store_k = [&](int buf) {
         if (kstager) {
 #pragma unroll
             for (int i = 0; i < KU; ++i) {
@@ -226,26 +253,28 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
                 const int row = uu / (DH / 8), c = uu % (DH / 8);
                 st16(&Ks[buf][row * KS + 8 * c], kreg[i]);
             }
-        }
-        if (vstager) {
-            if (st < VU) {
-                const int kg = st % (KVT / 4), dg = st / (KVT / 4);
-                // Keys 16G + 4h + {0..3} and 16G + 8 + 4h + {0..3} (one PV operand
-                // of lane half h) are stored next to each other at 16G + 8h.
-                const int vpos = 16 * (kg / 4) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
-                // Transpose 4 keys x 8 dh: element e of a row is half e%2 of word e/2.
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int wd = e / 2, sh = 16 * (e % 2);
-                    u32x2 pk;
-                    pk[0] = ((vreg[0][wd] >> sh) & 0xffffu) | (((vreg[1][wd] >> sh) & 0xffffu) << 16);
-                    pk[1] = ((vreg[2][wd] >> sh) & 0xffffu) | (((vreg[3][wd] >> sh) & 0xffffu) << 16);
-                    st8(&Vt[buf][(8 * dg + e) * VT_STRIDE + vpos], pk);
-                }
-            }
             if (st < KVT) {
 #pragma unroll
                 for (int j = 0; j < HPB; ++j) Bs[buf][j][st] = gbias[j] * sreg;
+            }
+        }
+    };
+    auto store_v = [&](int buf) {
+        if (vstager && st < VU) {
+            const int kg = st % (KVT / 4), dg = st / (KVT / 4);
+            // Keys 16G + 4h + {0..3} and 16G + 8 + 4h + {0..3} (one PV operand
+            // of lane half h) are stored next to each other at 16G + 8h.
+            const int vpos = 16 * (kg / 4) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
+            // Transpose 4 keys x 8 dh: element e of a row is half e%2 of word e/2.
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int wd = e / 2;
+                // Byte select: low (e even) or high (e odd) halves of two words.
+                const unsigned sel = e % 2 ? 0x07060302u : 0x05040100u;
+                u32x2 pk;
+                pk[0] = __builtin_amdgcn_perm(vreg[1][wd], vreg[0][wd], sel);
+                pk[1] = __builtin_amdgcn_perm(vreg[3][wd], vreg[2][wd], sel);
+                st8(&Vt[buf][(8 * dg + e) * VT_STRIDE + vpos], pk);
             }
         }
     };
@@ -256,83 +285,129 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[md][r] = 0.f;
     float m = -INFINITY, lpart = 0.f;  // exponent base (log2 units) and this lane's row-sum half
+    bf16x8 pold[4];                    // probabilities of the previous tile (PV operand)
+    float alpha_prev = 1.f;            // rescale of O owed before the next PV product
+    bool pend = false;                 // some row of the wave owes a rescale
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-
-    // One 64-key tile.  MASKED adds the causal mask (diagonal tile only); the
-    // exponent base m of a row moves only when the row max exceeds it by more
-    // than RESCALE_SLACK (log2 units), so the O rescale is rare.
-#define TG_TILE(MASKED)                                                                      \
+    // One iteration.  DO_S: QK and softmax of tile jt (MASKED on the diagonal
+    // tile); DO_PV: O += V(jt-1) P(jt-1).  The exponent base of a row moves
+    // only when its max exceeds it by more than RESCALE_SLACK; the rescale of
+    // O this causes is owed until just before the next PV product, so that
+    // the softmax and the PV product of one iteration form one straight run
+    // of independent VALU and MFMA work.
+#define TG_ITER(MASKED, DO_S, DO_PV)                                                         \
     do {                                                                                     \
-        f32x16 sacc[2];                                                                      \
-        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
-            _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;                \
-        _Pragma("unroll") for (int kk = 0; kk < NKK; ++kk) {                                 \
-            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                               \
-                const bf16x8 kf = as_bf16x8(                                                 \
-                    ld16(&Ks[buf][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));          \
-                sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);                                     \
-            }                                                                                \
+        if (DO_PV && pend) {                                                                 \
+            _Pragma("unroll") for (int md = 0; md < NMD; ++md)                               \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r) o[md][r] *= alpha_prev;       \
         }                                                                                    \
-        float mx = -INFINITY;                                                                \
-        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                                   \
-            _Pragma("unroll") for (int rq = 0; rq < 4; ++rq) {                               \
-                const int kl = 32 * mt + 8 * rq + 4 * hh;                                    \
-                const f32x4 sv = *reinterpret_cast<const f32x4*>(&Bs[buf][hp][kl]);          \
-                _Pragma("unroll") for (int e = 0; e < 4; ++e) {                              \
-                    float x = fmaf(c1, sacc[mt][4 * rq + e], sv[e]);                         \
-                    if (MASKED && j0 + kl + e > qi) x = -INFINITY;                           \
-                    sacc[mt][4 * rq + e] = x;                                                \
-                    mx = fmaxf(mx, x);                                                       \
+        f32x16 sacc[2];                                                                      \
+        bf16x8 pnew[4];                                                                      \
+        if (DO_S) {                                                                          \
+            const int kb = jt & 1;                                                           \
+            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                 \
+                _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;            \
+            _Pragma("unroll") for (int kk = 0; kk < NKK; ++kk) {                             \
+                _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                           \
+                    const bf16x8 kf = as_bf16x8(                                             \
+                        ld16(&Ks[kb][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));       \
+                    sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);                                 \
                 }                                                                            \
             }                                                                                \
         }                                                                                    \
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                            \
-        if (__any(mx > m + RESCALE_SLACK)) {                                                 \
-            const float m_new = mx > m + RESCALE_SLACK ? mx : m;                             \
-            const float alpha = m_new == m ? 1.f : __builtin_amdgcn_exp2f(m - m_new);         \
-            lpart *= alpha;                                                                  \
-            _Pragma("unroll") for (int md = 0; md < NMD; ++md)                               \
-                _Pragma("unroll") for (int r = 0; r < 16; ++r) o[md][r] *= alpha;            \
+        if (DO_PV) {                                                                         \
+            const int vb = (jt - 1) & 1;                                                     \
+            bf16x8 v0[4];                                                                    \
+            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) v0[kk] = as_bf16x8(             \
+                ld16(&Vt[vb][l32 * VT_STRIDE + 16 * kk + 8 * hh]));                          \
+            /* QK above, then PV interleaved with the softmax below. */                      \
+            if (DO_S) __builtin_amdgcn_sched_barrier(0);                                     \
+            _Pragma("unroll") for (int md = 0; md < NMD; ++md) {                             \
+                _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                           \
+                    const bf16x8 vf = md == 0 ? v0[kk] : as_bf16x8(                          \
+                        ld16(&Vt[vb][(32 * md + l32) * VT_STRIDE + 16 * kk + 8 * hh]));      \
+                    o[md] = mfma32(vf, pold[kk], o[md]);                                     \
+                }                                                                            \
+            }                                                                                \
+        }                                                                                    \
+        if (DO_S) {                                                                          \
+            const int kb = jt & 1;                                                           \
+            const int j0 = jt * KVT;                                                         \
+            float mx = -INFINITY;                                                            \
+            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                               \
+                _Pragma("unroll") for (int rq = 0; rq < 4; ++rq) {                           \
+                    const int kl = 32 * mt + 8 * rq + 4 * hh;                                \
+                    const f32x4 sv = *reinterpret_cast<const f32x4*>(&Bs[kb][hp][kl]);       \
+                    _Pragma("unroll") for (int e = 0; e < 4; ++e) {                          \
+                        float x = fmaf(c1, sacc[mt][4 * rq + e], sv[e]);                     \
+                        if (MASKED && j0 + kl + e > qi) x = -INFINITY;                       \
+                        sacc[mt][4 * rq + e] = x;                                            \
+                        mx = fmaxf(mx, x);                                                   \
+                    }                                                                        \
+                }                                                                            \
+            }                                                                                \
+            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                        \
+            const bool grow = mx > m + RESCALE_SLACK;                                        \
+            const float m_new = grow ? mx : m;                                               \
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;              \
             m = m_new;                                                                       \
-        }                                                                                    \
-        const float mb = m == -INFINITY ? 0.f : m;                                           \
-        float psum = 0.f;                                                                    \
-        bf16x8 pf[4];                                                                        \
-        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                                   \
-            _Pragma("unroll") for (int e = 0; e < 8; ++e) {                                  \
-                const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - mb);  \
-                psum += p;                                                                   \
-                pf[kk][e] = to_bf16(p);                                                      \
-            }                                                                                \
-        }                                                                                    \
-        lpart += psum;                                                                       \
-        _Pragma("unroll") for (int md = 0; md < NMD; ++md) {                                 \
+            const float mb = m == -INFINITY ? 0.f : m;                                       \
+            float psum = 0.f;                                                                \
             _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                               \
-                const bf16x8 vf = as_bf16x8(                                                 \
-                    ld16(&Vt[buf][(32 * md + l32) * VT_STRIDE + 16 * kk + 8 * hh]));          \
-                o[md] = mfma32(vf, pf[kk], o[md]);                                           \
+                _Pragma("unroll") for (int e = 0; e < 8; ++e) {                              \
+                    const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - mb); \
+                    psum += p;                                                               \
+                    pnew[kk][e] = to_bf16(p);                                                \
+                }                                                                            \
             }                                                                                \
+            /* Pin the probabilities here: left alone, the compiler sinks the   */         \
+            /* exponentials below the staging stores, away from the PV MFMAs.   */         \
+            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(pnew[kk])); \
+            if (DO_PV) {                                                                     \
+                _Pragma("unroll") for (int i = 0; i < 4 * NMD; ++i) {                        \
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       \
+                    __builtin_amdgcn_sched_group_barrier(0x002, SM_VALU, 0);                 \
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                       \
+                }                                                                            \
+            }                                                                                \
+            lpart = fmaf(lpart, alpha, psum);                                                \
+            alpha_prev = alpha;                                                              \
+            pend = __any(grow);                                                              \
+            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) pold[kk] = pnew[kk];            \
         }                                                                                    \
     } while (0)
 
+    // One step of the workgroup: stage K(jt+1) and V(jt) around BODY.  Every
+    // wave takes nkv + 1 steps, each ending in one barrier.
+    int jt = 0;
+#define TG_STEP(BODY)                                     \
+    do {                                                  \
+        const bool knext = jt + 1 < nkv;                  \
+        const bool vnow = jt < nkv;                       \
+        if (knext) load_k(jt + 1);                        \
+        if (vnow) load_v(jt);                             \
+        BODY;                                             \
+        if (knext) store_k((jt + 1) & 1);                 \
+        if (vnow) store_v(jt & 1);                        \
+        __syncthreads();                                  \
+        ++jt;                                             \
+    } while (0)
+
     // Tiles strictly before this wave's rows need no mask; the tile holding
-    // the wave's first row is the diagonal one; later tiles are all masked
-    // out for this wave and skipped (the workgroup still stages them).
-    const int jt_diag = qmin / KVT;
-    for (int jt = 0; jt < nkv; ++jt) {
-        const int buf = jt & 1;
-        const bool more = jt + 1 < nkv;
-        if (more) load_tile(jt + 1);
-        const int j0 = jt * KVT;
-        if (jt < jt_diag) TG_TILE(false);
-        else if (jt == jt_diag) TG_TILE(true);
-        if (more) store_tile(buf ^ 1);
-        __syncthreads();
-    }
-#undef TG_TILE
+    // the wave's first row is the diagonal one; later tiles are skipped by
+    // this wave (the workgroup still stages them).
+    const int jt_diag = qmin / KVT;  // <= nkv - 1
+    load_k(0);
+    store_k(0);
+    __syncthreads();
+    if (jt_diag == 0) TG_STEP(TG_ITER(true, true, false));
+    else TG_STEP(TG_ITER(false, true, false));
+    while (jt < jt_diag) TG_STEP(TG_ITER(false, true, true));
+    if (jt == jt_diag) TG_STEP(TG_ITER(true, true, true));
+    TG_STEP(TG_ITER(false, false, true));
+    while (jt <= nkv) TG_STEP((void)0);
+#undef TG_STEP
+#undef TG_ITER
 
     // ---- normalise and store ------------------------------------------------
     const float l = lpart + __shfl_xor(lpart, 32, WAVE);

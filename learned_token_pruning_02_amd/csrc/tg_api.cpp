@@ -178,6 +178,12 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const
         sh.cu[i] = cu_kept_host[i];
     }
     sh.Kt = cu_kept_host[batch];
+    if (dt == TG_BF16) {
+        // The bf16 kernel addresses one request's K/V rows with 32-bit offsets.
+        for (int i = 0; i < batch; ++i)
+            if ((int64_t)(cu_kept_host[i + 1] - cu_kept_host[i]) * Hkv * d_head * 2 >= I32_LIMIT)
+                return TG_ERR_UNSUPPORTED;
+    }
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(s_kept) ||
         !aligned4(gain) || !aligned4(temp) || (lse != nullptr && !aligned4(lse)))
         return TG_ERR_ALIGNMENT;

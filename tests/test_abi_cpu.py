@@ -180,6 +180,9 @@ def test_attention_validation():
     assert call(lse=B + 4) == 9          # lse overlaps k
     zero = tg._i32_array([0, 0])
     assert call(cu=ctypes.cast(zero, ctypes.POINTER(ctypes.c_int32))) == 0    # no rows: no-op
+    # bf16 K/V rows of one request must span < 2 GiB: 2^20 rows x 8 x 128 x 2 B = 2^31
+    big = tg._i32_array([0, 1 << 20])
+    assert call(cu=ctypes.cast(big, ctypes.POINTER(ctypes.c_int32))) == 5
 
 
 def test_linear_validation():
