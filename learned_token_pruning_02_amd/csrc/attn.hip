@@ -126,12 +126,16 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     constexpr int NKK = DH / 16;       // k steps of the QK^T product
     constexpr int NMD = DH / 32;       // 32-row dh tiles of O^T
     constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before O is rescaled
-    constexpr int SM_VALU = 256 / (4 * NMD);  // softmax VALU slots next to each PV MFMA
+    // Four waves (two workgroups per CU) interleave the softmax with the PV
+    // MFMAs by hand, slice by slice; eight waves (one workgroup per CU) leave
+    // the interleave to scheduling groups, which measures faster there.
+    constexpr bool FUSED = NWAVE == 4;
+    constexpr int NKB = 2;  // K / bias buffers
 
-    __shared__ __attribute__((aligned(16))) bf16 Ks[2][KVT * KS];
+    __shared__ __attribute__((aligned(16))) bf16 Ks[NKB][KVT * KS];
     __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * VT_STRIDE];
     // Per key of the tile and per head of the workgroup: g_h log2(e) s_j.
-    __shared__ __attribute__((aligned(16))) float Bs[2][HPB][KVT];
+    __shared__ __attribute__((aligned(16))) float Bs[NKB][HPB][KVT];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -289,32 +293,38 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     float alpha_prev = 1.f;            // rescale of O owed before the next PV product
     bool pend = false;                 // some row of the wave owes a rescale
 
-    // One iteration.  DO_S: QK and softmax of tile jt (MASKED on the diagonal
-    // tile); DO_PV: O += V(jt-1) P(jt-1).  The exponent base of a row moves
-    // only when its max exceeds it by more than RESCALE_SLACK; the rescale of
-    // O this causes is owed until just before the next PV product, so that
-    // the softmax and the PV product of one iteration form one straight run
-    // of independent VALU and MFMA work.
-#define TG_ITER(MASKED, DO_S, DO_PV)                                                         \
+    f32x16 sacc[2];  // S^T of one tile
+
+    // S^T of tile T from its staged K.
+#define TG_QK(T)                                                                             \
     do {                                                                                     \
-        if (DO_PV && pend) {                                                                 \
+        const int kb = (T) % NKB;                                                            \
+        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
+            _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;                \
+        _Pragma("unroll") for (int kk = 0; kk < NKK; ++kk) {                                 \
+            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                               \
+                const bf16x8 kf = as_bf16x8(                                                 \
+                    ld16(&Ks[kb][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));           \
+                sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);                                     \
+            }                                                                                \
+        }                                                                                    \
+    } while (0)
+
+    // DO_S: softmax of tile jt from sacc (MASKED on the diagonal tile);
+    // DO_PV: O += V(jt-1) P(jt-1).  The exponent base of a row moves only when
+    // its max exceeds it by more than RESCALE_SLACK; the rescale of O this
+    // causes is owed until the start of the next step (TG_RESCALE), before
+    // the next PV product, so that the QK product, the PV product and the
+    // softmax form one straight run of independent MFMA and VALU work.
+#define TG_RESCALE()                                                                         \
+    do {                                                                                     \
+        if (pend) {                                                                          \
             _Pragma("unroll") for (int md = 0; md < NMD; ++md)                               \
                 _Pragma("unroll") for (int r = 0; r < 16; ++r) o[md][r] *= alpha_prev;       \
         }                                                                                    \
-        f32x16 sacc[2];                                                                      \
-        bf16x8 pnew[4];                                                                      \
-        if (DO_S) {                                                                          \
-            const int kb = jt & 1;                                                           \
-            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                 \
-                _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;            \
-            _Pragma("unroll") for (int kk = 0; kk < NKK; ++kk) {                             \
-                _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                           \
-                    const bf16x8 kf = as_bf16x8(                                             \
-                        ld16(&Ks[kb][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));       \
-                    sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);                                 \
-                }                                                                            \
-            }                                                                                \
-        }                                                                                    \
+    } while (0)
+#define TG_PVSM(MASKED, DO_S, DO_PV)                                                         \
+    do {                                                                                     \
         if (DO_PV) {                                                                         \
             const int vb = (jt - 1) & 1;                                                     \
             bf16x8 v0[4];                                                                    \
@@ -331,13 +341,13 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
             }                                                                                \
         }                                                                                    \
         if (DO_S) {                                                                          \
-            const int kb = jt & 1;                                                           \
+            const int bb = jt % NKB;                                                         \
             const int j0 = jt * KVT;                                                         \
             float mx = -INFINITY;                                                            \
             _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                               \
                 _Pragma("unroll") for (int rq = 0; rq < 4; ++rq) {                           \
                     const int kl = 32 * mt + 8 * rq + 4 * hh;                                \
-                    const f32x4 sv = *reinterpret_cast<const f32x4*>(&Bs[kb][hp][kl]);       \
+                    const f32x4 sv = *reinterpret_cast<const f32x4*>(&Bs[bb][hp][kl]);       \
                     _Pragma("unroll") for (int e = 0; e < 4; ++e) {                          \
                         float x = fmaf(c1, sacc[mt][4 * rq + e], sv[e]);                     \
                         if (MASKED && j0 + kl + e > qi) x = -INFINITY;                       \
@@ -353,6 +363,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
             m = m_new;                                                                       \
             const float mb = m == -INFINITY ? 0.f : m;                                       \
             float psum = 0.f;                                                                \
+            bf16x8 pnew[4];                                                                  \
             _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                               \
                 _Pragma("unroll") for (int e = 0; e < 8; ++e) {                              \
                     const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - mb); \
@@ -366,7 +377,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
             if (DO_PV) {                                                                     \
                 _Pragma("unroll") for (int i = 0; i < 4 * NMD; ++i) {                        \
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       \
-                    __builtin_amdgcn_sched_group_barrier(0x002, SM_VALU, 0);                 \
+                    __builtin_amdgcn_sched_group_barrier(0x002, 256 / (4 * NMD), 0);         \
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                       \
                 }                                                                            \
             }                                                                                \
@@ -377,8 +388,74 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         }                                                                                    \
     } while (0)
 
-    // One step of the workgroup: stage K(jt+1) and V(jt) around BODY.  Every
-    // wave takes nkv + 1 steps, each ending in one barrier.
+    // Softmax of tile jt and PV(jt-1) together, interleaved by hand: the
+    // first half of the PV MFMAs each go with a slice of the logits and their
+    // max, the second half each with a slice of the exponentials.  Scheduling
+    // fences keep every slice next to its MFMA; V operands are read four
+    // MFMAs ahead and bias vectors one slice ahead.
+    constexpr int NPV = 4 * NMD;            // PV MFMAs per tile
+    constexpr int NA = NPV / 2;             // MFMAs next to the logits
+    constexpr int CA = 8 / NA;              // logit slices (4 keys each) per MFMA
+    constexpr int EB = 32 / (NPV - NA);     // exponentials per MFMA
+#define TG_VFRAG(I)                                                                          \
+    as_bf16x8(ld16(&Vt[vb][(32 * ((I) / 4) + l32) * VT_STRIDE + 16 * ((I) % 4) + 8 * hh]))
+#define TG_BIAS(C)                                                                           \
+    (*reinterpret_cast<const f32x4*>(&Bs[bb][hp][32 * ((C) / 4) + 8 * ((C) % 4) + 4 * hh]))
+#define TG_PVSM_FUSED(MASKED)                                                                \
+    do {                                                                                     \
+        const int vb = (jt - 1) & 1;                                                         \
+        const int bb = jt % NKB;                                                             \
+        const int j0 = jt * KVT;                                                             \
+        bf16x8 vq[4];                                                                        \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) vq[i] = TG_VFRAG(i);                   \
+        f32x4 sv = TG_BIAS(0);                                                               \
+        float mx = -INFINITY;                                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        _Pragma("unroll") for (int i = 0; i < NA; ++i) {                                     \
+            o[i / 4] = mfma32(vq[i % 4], pold[i % 4], o[i / 4]);                             \
+            if (i + 4 < NPV) vq[i % 4] = TG_VFRAG(i + 4);                                    \
+            _Pragma("unroll") for (int c = i * CA; c < (i + 1) * CA; ++c) {                  \
+                const f32x4 cur = sv;                                                        \
+                if (c + 1 < 8) sv = TG_BIAS(c + 1);                                          \
+                const int mt = c / 4, rq = c % 4;                                            \
+                const int kl = 32 * mt + 8 * rq + 4 * hh;                                    \
+                _Pragma("unroll") for (int e = 0; e < 4; ++e) {                              \
+                    float x = fmaf(c1, sacc[mt][4 * rq + e], cur[e]);                        \
+                    if (MASKED && j0 + kl + e > qi) x = -INFINITY;                           \
+                    sacc[mt][4 * rq + e] = x;                                                \
+                    mx = fmaxf(mx, x);                                                       \
+                }                                                                            \
+            }                                                                                \
+            __builtin_amdgcn_sched_barrier(0);                                               \
+        }                                                                                    \
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                            \
+        const bool grow = mx > m + RESCALE_SLACK;                                            \
+        const float m_new = grow ? mx : m;                                                   \
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;                  \
+        m = m_new;                                                                           \
+        const float mb = m == -INFINITY ? 0.f : m;                                           \
+        float psum = 0.f;                                                                    \
+        bf16x8 pnew[4];                                                                      \
+        _Pragma("unroll") for (int i = NA; i < NPV; ++i) {                                   \
+            o[i / 4] = mfma32(vq[i % 4], pold[i % 4], o[i / 4]);                             \
+            if (i + 4 < NPV) vq[i % 4] = TG_VFRAG(i + 4);                                    \
+            _Pragma("unroll") for (int x = (i - NA) * EB; x < (i - NA + 1) * EB; ++x) {      \
+                const int kk = x / 8, e = x % 8;                                             \
+                const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - mb); \
+                psum += p;                                                                   \
+                pnew[kk][e] = to_bf16(p);                                                    \
+            }                                                                                \
+            __builtin_amdgcn_sched_barrier(0);                                               \
+        }                                                                                    \
+        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(pnew[kk])); \
+        lpart = fmaf(lpart, alpha, psum);                                                    \
+        alpha_prev = alpha;                                                                  \
+        pend = __any(grow);                                                                  \
+        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) pold[kk] = pnew[kk];                \
+    } while (0)
+
+    // One step of the workgroup: stage K(jt+1) and V(jt) around BODY.
+    // Every wave takes nkv + 1 steps, each ending in one barrier.
     int jt = 0;
 #define TG_STEP(BODY)                                     \
     do {                                                  \
@@ -387,7 +464,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         if (knext) load_k(jt + 1);                        \
         if (vnow) load_v(jt);                             \
         BODY;                                             \
-        if (knext) store_k((jt + 1) & 1);                 \
+        if (knext) store_k((jt + 1) % NKB);               \
         if (vnow) store_v(jt & 1);                        \
         __syncthreads();                                  \
         ++jt;                                             \
@@ -400,14 +477,27 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     load_k(0);
     store_k(0);
     __syncthreads();
-    if (jt_diag == 0) TG_STEP(TG_ITER(true, true, false));
-    else TG_STEP(TG_ITER(false, true, false));
-    while (jt < jt_diag) TG_STEP(TG_ITER(false, true, true));
-    if (jt == jt_diag) TG_STEP(TG_ITER(true, true, true));
-    TG_STEP(TG_ITER(false, false, true));
+    if (jt_diag == 0) {
+        TG_STEP({ TG_QK(jt); TG_PVSM(true, true, false); });
+    } else {
+        TG_STEP({ TG_QK(jt); TG_PVSM(false, true, false); });
+        if (FUSED) {
+            while (jt < jt_diag) TG_STEP({ TG_RESCALE(); TG_QK(jt); TG_PVSM_FUSED(false); });
+            TG_STEP({ TG_RESCALE(); TG_QK(jt); TG_PVSM_FUSED(true); });
+        } else {
+            while (jt < jt_diag) TG_STEP({ TG_RESCALE(); TG_QK(jt); TG_PVSM(false, true, true); });
+            TG_STEP({ TG_RESCALE(); TG_QK(jt); TG_PVSM(true, true, true); });
+        }
+    }
+    TG_STEP({ TG_RESCALE(); TG_PVSM(false, false, true); });
     while (jt <= nkv) TG_STEP((void)0);
 #undef TG_STEP
-#undef TG_ITER
+#undef TG_PVSM
+#undef TG_RESCALE
+#undef TG_PVSM_FUSED
+#undef TG_VFRAG
+#undef TG_BIAS
+#undef TG_QK
 
     // ---- normalise and store ------------------------------------------------
     const float l = lpart + __shfl_xor(lpart, 32, WAVE);
