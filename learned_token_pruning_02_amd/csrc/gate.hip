@@ -130,16 +130,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
         const int r = step + rot;
         return (r >= nsteps ? r - nsteps : r) * GK;
     };
+#define TG_LOAD_A1(dst, step, li) dst[(li) / 4][(li) % 4] = ld16(arow[(li) / 4] + rot_k(step) + 8 * ((li) % 4))
+#define TG_LOAD_W1(step, li) wreg[li] = ld16(wbase + (int64_t)(R * (li)) * d + rot_k(step))
 #define TG_LOAD_A(dst, step)                                                                 \
     do {                                                                                     \
-        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
-            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk)                                 \
-                dst[mt][kk] = ld16(arow[mt] + rot_k(step) + 8 * kk);                           \
+        _Pragma("unroll") for (int li = 0; li < 8; ++li) TG_LOAD_A1(dst, step, li);          \
     } while (0)
 #define TG_LOAD_W(step)                                                                      \
     do {                                                                                     \
-        _Pragma("unroll") for (int i = 0; i < WUNITS; ++i)                                   \
-            wreg[i] = ld16(wbase + (int64_t)(R * i) * d + rot_k(step));                   \
+        _Pragma("unroll") for (int li = 0; li < WUNITS; ++li) TG_LOAD_W1(step, li);          \
     } while (0)
 #define TG_STORE_W(buf)                                                                      \
     do {                                                                                     \
@@ -151,6 +150,18 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
         _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                    \
             dst[nt] = as_bf16x8(wl[buf][(nt * 4 + (kk)) * WAVE + rd_pos[kk]]);                \
     } while (0)
+    // The 2*NT MFMAs of one k slice, with NL loads (LOAD1(li)) spread evenly
+    // between them, so that the vector-memory pipe fills while MFMAs run
+    // instead of stalling the wave at the top of the chunk.
+#define TG_MMA_LOADS(cur, b, kk, NL, LOAD1)                                                  \
+    do {                                                                                     \
+        _Pragma("unroll") for (int j = 0; j < 2 * NT; ++j) {                                 \
+            acc[j % 2][j / 2] = mfma32(as_bf16x8(cur[j % 2][kk]), b[j / 2], acc[j % 2][j / 2]); \
+            _Pragma("unroll") for (int li = j * (NL) / (2 * NT); li < (j + 1) * (NL) / (2 * NT); ++li) \
+                LOAD1(li);                                                                   \
+            __builtin_amdgcn_sched_barrier(0);                                               \
+        }                                                                                    \
+    } while (0)
 #define TG_MMA(cur, b, kk)                                                                   \
     do {                                                                                     \
         _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                    \
@@ -159,29 +170,28 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     } while (0)
     bf16x8 bA[NT], bB[NT];
 
-    // One k chunk: W1 of the next chunk and then the residual two chunks ahead
-    // are requested, this chunk's MFMAs run, and the W1 registers go to LDS
-    // (the in-order load counter lets that wait skip the residual loads).
-    // Prefetch addresses are clamped to the last chunk instead of branching,
-    // so the three-step body is straight-line code and the register ring
-    // rotates without copies; the clamped extra loads are never used.
+    // One k chunk: the B fragments of slices 0 and 1 are read from LDS; W1 of
+    // the next chunk is requested between slice 0's MFMAs and the residual
+    // two chunks ahead between slice 1's; then slices 2 and 3 run and the W1
+    // registers go to LDS (the in-order load counter lets that wait skip the
+    // residual loads).  Prefetch addresses are clamped to the last chunk
+    // instead of branching, so the three-step body is straight-line code and
+    // the register ring rotates without copies; the clamped extra loads are
+    // never used.
+#define TG_LW(li) TG_LOAD_W1(min(s_ + 1, nsteps - 1), li)
+#define TG_LA(li) TG_LOAD_A1(ahead_, min(s_ + 2, nsteps - 1), li)
 #define TG_STEP(s, cur, ahead)                                                               \
     do {                                                                                     \
-        const int buf_ = (s) & 1;                                                            \
-        TG_LOAD_W(min((s) + 1, nsteps - 1));                                                 \
-        TG_LOAD_A(ahead, min((s) + 2, nsteps - 1));                                          \
-        __builtin_amdgcn_sched_barrier(0); /* keep the prefetch at the top */                \
-        /* B fragments double buffered across k slices: slice kk+1 is read */               \
-        /* from LDS while slice kk's MFMAs run.                              */               \
+        const int s_ = (s);                                                                  \
+        auto& ahead_ = ahead;                                                                \
+        const int buf_ = s_ & 1;                                                             \
         TG_READ_B(bA, buf_, 0);                                                              \
         TG_READ_B(bB, buf_, 1);                                                              \
         __builtin_amdgcn_sched_barrier(0);                                                   \
-        TG_MMA(cur, bA, 0);                                                                  \
-        __builtin_amdgcn_sched_barrier(0);                                                   \
+        TG_MMA_LOADS(cur, bA, 0, WUNITS, TG_LW);                                             \
         TG_READ_B(bA, buf_, 2);                                                              \
         __builtin_amdgcn_sched_barrier(0);                                                   \
-        TG_MMA(cur, bB, 1);                                                                  \
-        __builtin_amdgcn_sched_barrier(0);                                                   \
+        TG_MMA_LOADS(cur, bB, 1, 8, TG_LA);                                                  \
         TG_READ_B(bB, buf_, 3);                                                              \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         TG_MMA(cur, bA, 2);                                                                  \
@@ -207,7 +217,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     if (rest > 0) TG_STEP(groups * RING, a0, a2);
     if (rest > 1) TG_STEP(groups * RING + 1, a1, a0);
 #undef TG_STEP
+#undef TG_LW
+#undef TG_LA
 #undef TG_MMA
+#undef TG_MMA_LOADS
+#undef TG_LOAD_A1
+#undef TG_LOAD_W1
 #undef TG_READ_B
 #undef TG_STORE_W
 #undef TG_LOAD_W
