@@ -61,6 +61,7 @@ __global__ __launch_bounds__(GF_THREADS) void gate_f32_kernel(
 // --------------------------------------------------------------- bf16 ----
 constexpr int GK = 64;   // k chunk
 constexpr int RING = 3;  // residual fragment sets per wave (two chunks in flight)
+constexpr int RED_STRIDE = 36;  // floats per row of the unit-sum tile (16-byte aligned, skewed banks)
 
 template <int DG, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
@@ -73,6 +74,13 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
 
     // W1 chunks in fragment layout: [buf][nt*4 + kk][lane] 16-byte units.
     __shared__ __attribute__((aligned(16))) u32x4 wl[2][NFRAG * WAVE];
+    // Per-wave tile for the final unit sum: 64 rows (token slot, half) of 32
+    // unit-lane partials, rows padded to RED_STRIDE floats.  It lives in the
+    // W1 buffers (dead after the last barrier) whenever they are big enough,
+    // so that it costs no extra LDS.
+    constexpr int RED_FLOATS = 64 * RED_STRIDE;
+    constexpr bool RED_IN_WL = WAVES * RED_FLOATS * 4 <= 2 * NFRAG * WAVE * 16;
+    __shared__ __attribute__((aligned(16))) float red_own[RED_IN_WL ? 4 : WAVES * RED_FLOATS];
 
     const int lane = lane_id();
     const int w = threadIdx.x / WAVE;
@@ -229,6 +237,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
 #undef TG_LOAD_A
 
     // Epilogue: lane holds unit 32nt + l32 and tokens 8(r/4)+4hh+r%4 (+32mt).
+    // Each lane folds its NT units per token, then the 32 unit-lanes of every
+    // token are summed through a per-wave LDS tile: lane (l32, hh) writes its
+    // partial of token slot j = 16mt + r into row 2j + hh, and lane i then adds
+    // up row i (token slot i/2, half i%2), a transpose instead of 32
+    // five-level shuffle butterflies.
     float bias[NT], wout[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -236,7 +249,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
         bias[nt] = b1 != nullptr ? to_f32(b1[u]) : 0.f;
         wout[nt] = to_f32(w2[u]);
     }
-    const float bout = b2 != nullptr ? to_f32(b2[0]) : 0.f;
+    float* rt = (RED_IN_WL ? reinterpret_cast<float*>(&wl[0][0]) : red_own) + w * RED_FLOATS;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -244,11 +257,20 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
             float p = 0.f;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) p = fmaf(wout[nt], gelu_fast(acc[mt][nt][r] + bias[nt]), p);
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) p += __shfl_xor(p, o, WAVE);
-            const int64_t t = tok0 + 64 * w + 32 * mt + 8 * (r / 4) + 4 * hh + (r % 4);
-            if (l32 == 0 && t < T) scores[t] = p + bout;
+            rt[(2 * (16 * mt + r) + hh) * RED_STRIDE + l32] = p;
         }
+    }
+    __builtin_amdgcn_wave_barrier();
+    float sum = b2 != nullptr ? to_f32(b2[0]) : 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&rt[lane * RED_STRIDE + 4 * c]);
+        sum += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+    {
+        const int j = lane / 2, half = lane % 2, mt = j / 16, r = j % 16;
+        const int64_t t = tok0 + 64 * w + 32 * mt + 8 * (r / 4) + 4 * half + (r % 4);
+        if (t < T) scores[t] = sum;
     }
 }
 
