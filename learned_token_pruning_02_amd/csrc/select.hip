@@ -60,6 +60,24 @@ __device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ void coherent_store(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void coherent_store2(uint2* p, uint2 v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)v.x | ((uint64_t)v.y << 32),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publishing to the last workgroup of a launch.  Everything one workgroup
+// hands to another inside a launch is written with device-coherent atomic
+// stores or atomic adds and read with device-coherent atomic loads, so no
+// cache needs flushing; each wave only has to wait until its own writes are
+// performed before the workgroup takes its ticket.  (A device-wide fence
+// here would also write back and invalidate whole caches, which costs
+// microseconds per workgroup.)
+__device__ __forceinline__ void wait_own_writes() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ uint2 coherent_load2(const uint2* p) {
     const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
@@ -178,12 +196,11 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
     uint32_t* gh = a.hist + (size_t)b * NBIN;
     for (int i = tid; i < NBIN; i += SB)
         if (h[i] != 0u) atomicAdd(&gh[i], h[i]);
-    __threadfence();
+    wait_own_writes();
     __syncthreads();
     if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 0], 1u) == (uint32_t)(nck - 1);
     __syncthreads();
     if (!sh_last) return;
-    __threadfence();
     find_bin([&](int i) { return coherent_load(&gh[i]); }, NBIN, (uint32_t)kdoc, wtot, &sh_d,
              &sh_gt, &sh_cnt);
     if (tid == 0) {
@@ -227,7 +244,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     uint32_t tot_cand;
     const uint32_t incl = block_incl_scan(ncand, wtot, &tot_cand);
     if (tid == 0) {
-        a.chunk_def[a.doc_chunk0[b] + c] = tot_above;
+        coherent_store(&a.chunk_def[a.doc_chunk0[b] + c], tot_above);
         sh_base = tot_cand ? atomicAdd(&a.ctr[b * CTR + 2], tot_cand) : 0u;
     }
     __syncthreads();
@@ -235,14 +252,13 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
 #pragma unroll
     for (int it = 0; it < SITEMS; ++it) {
         const int i = c * SCHUNK + it * SB + tid;
-        if (i < ndoc && (kv[it] >> 21) == d1) cand[pos++] = make_uint2(kv[it], (uint32_t)i);
+        if (i < ndoc && (kv[it] >> 21) == d1) coherent_store2(&cand[pos++], make_uint2(kv[it], (uint32_t)i));
     }
-    __threadfence();
+    wait_own_writes();
     __syncthreads();
     if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 1], 1u) == (uint32_t)(nck - 1);
     __syncthreads();
     if (!sh_last) return;
-    __threadfence();
 
     // ---- the last chunk: exact rank inside bucket d1 ----------------------
     // Candidates are staged once into LDS when they fit (the usual case: a
