@@ -114,6 +114,29 @@ def test_attention_full_size_sampled(wname):
     assert_within(lse[:, rows], ref_lse, 2e-2, 1e-2, f"{wname} lse")
 
 
+EIGHT_WAVE = [
+    # (name, lens, Hq, Hkv, d_head): sized so that the eight-wave kernel runs
+    # (at least 512 workgroups of 256/HPB query rows per head group).
+    ("dh64_mha", [8192], 16, 16, 64),
+    ("dh128_group4", [8192], 16, 4, 128),
+    ("dh64_group2_varlen", [3000, 9000, 5000], 16, 8, 64),
+]
+
+
+@pytest.mark.parametrize("name,lens,Hq,Hkv,dh", EIGHT_WAVE, ids=[c[0] for c in EIGHT_WAVE])
+def test_attention_eight_wave_sampled(name, lens, Hq, Hkv, dh):
+    """The eight-wave kernel's other instantiations (one and four query heads
+    per KV head, d_head 64), checked on sampled rows, all heads."""
+    announce(f"attn eight-wave {name} lens={lens} Hq={Hq} Hkv={Hkv} dh={dh}")
+    q, k, v, s, gain, temp, cu = _inputs(lens, Hq, Hkv, dh, torch.bfloat16,
+                                         seed=zlib.crc32(name.encode()) % 1000)
+    out, lse = _run(q, k, v, s, gain, temp, cu)
+    rows = _sampled_rows(cu, 16, seed=5)
+    ref, ref_lse = oracle.gated_attention_rows(q, k, v, s, gain, temp, cu, rows)
+    assert_within(out[rows], ref, 2e-2, 1e-2, f"{name} out")
+    assert_within(lse[:, rows], ref_lse, 2e-2, 1e-2, f"{name} lse")
+
+
 # ---------------------------------------------------------------- linear ----
 @pytest.mark.parametrize("M,N,K,dtype,acc", [
     (300, 192, 256, torch.bfloat16, False),
