@@ -6,10 +6,15 @@ One step is one gated layer over one batch of synthetic, HBM-resident input:
 (plus the four QKV/attention/O layers above the gate for the stack workload).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py --select-sweep      # selector alone, T = 2^20 .. 2^26, K = T/16
 
 Prints ONE JSON line: whole-step throughput in tokens of context per second
-(N / step time), the per-kernel split, the roofline of the dominant kernel and
-the CPU oracle timed on a bounded sample of the same workload.
+(N / step time), the per-kernel split (mean, median, minimum), the roofline of
+the dominant kernel, derived rates (attention-only and kept-token rates, the
+bias overhead against the bias-free build of the same attention kernel, K/V
+bytes kept vs full) and the CPU oracle timed on a bounded sample of the same
+workload.  With --detail, each kernel is also timed cold, right after 512 MiB
+are written to evict the 256 MiB Infinity Cache.
 """
 from __future__ import annotations
 
@@ -39,7 +44,40 @@ def parse():
     p.add_argument("--detail", default="", help="also write per-kernel detail JSON to this path")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of 512 MiB (reference for HBM byte counters)")
+    p.add_argument("--select-sweep", action="store_true",
+                   help="only time the selector on T = 2^20 .. 2^26 random scores, K = T/16")
     return p.parse_args()
+
+
+def select_sweep(reps: int = 20):
+    """Selector throughput beyond the layer sizes: one request of T random
+    fp32 scores, keep K = T/16 (no question tail); one JSON line per T."""
+    import torch
+
+    import learned_token_pruning_02_amd as tg
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for e in range(20, 27):
+        T = 1 << e
+        K = T // 16
+        scores = torch.randn(T, generator=g, device="cuda")
+        cu_s, cu_k, ws = tg.tg_plan([T], [0], [K])
+        kept = torch.empty(K, dtype=torch.int32, device="cuda")
+        wsb = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            tg.tg_topk_select(scores, [T], [0], [K], kept_idx=kept, workspace=wsb)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            tg.tg_topk_select(scores, [T], [0], [K], kept_idx=kept, workspace=wsb)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+        med = ms[reps // 2]
+        print(json.dumps({"metric": "select GB/s (T*4 read + K*4 written)", "T": T, "K": K,
+                          "us_median": med * 1e3, "us_min": ms[0] * 1e3,
+                          "GB/s": (T * 4 + K * 4) / (med * 1e-3) / 1e9}), flush=True)
+        del scores, kept, wsb
 
 
 def copy_calibration():
@@ -150,6 +188,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.select_sweep:
+        select_sweep()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the path is single-GPU; sharding is a design note, not built)", file=sys.stderr)
@@ -217,11 +258,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per = {n: 0.0 for n in names}
-    for e in evs:
-        for j, n in enumerate(names):
-            per[n] += e[j].elapsed_time(e[j + 1])
-    per = {n: v / args.steps for n, v in per.items()}      # ms per launch
+    samples = {n: sorted(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    per = {n: sum(v) / len(v) for n, v in samples.items()}  # ms per launch (mean)
     gpu_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
@@ -230,7 +268,8 @@ def main():
     kernels = {}
     for n in ["gate", "select", "gather", "attention"]:
         t = per[n] * 1e-3
-        kernels[n] = {"ms": per[n], "GB/s": alg[n]["bytes"] / t / 1e9,
+        kernels[n] = {"ms": per[n], "ms_median": samples[n][len(samples[n]) // 2],
+                      "ms_min": samples[n][0], "GB/s": alg[n]["bytes"] / t / 1e9,
                       "hbm_frac": alg[n]["bytes"] / t / 1e9 / HBM_PEAK_GBS,
                       "TFLOP/s": alg[n]["flops"] / t / 1e12}
     bf16 = sh.dtype == torch.bfloat16
@@ -250,6 +289,59 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = recorded_traffic(w.name, dominant)
     roof["kernel"] = dominant
+
+    # Derived rates and the bias overhead: the same attention kernel built
+    # without the bias stage (s_kept = gain = NULL), same inputs, same stream.
+    def timed(fn, reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for _ in range(2):
+            fn()
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+
+    nobias_out = torch.empty_like(layer.out)
+    t_bias = timed(lambda: layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"]), 10)
+    t_nobias = timed(lambda: tg.tg_gated_attn_prefill(a["q"], a["k"], a["v"], None, None, a["temp"],
+                                                     layer.cu_kept, out=nobias_out), 10)
+    eb = 2 if bf16 else 4
+    kv_row = 2 * sh.n_kv_heads * sh.d_head * eb
+    derived = {
+        "attn_layer_tok_s": w.total_tokens / (per["attention"] * 1e-3),
+        "kept_tok_s": layer.Kt / (per["attention"] * 1e-3),
+        "bias_overhead": t_bias[len(t_bias) // 2] / t_nobias[len(t_nobias) // 2],
+        "attn_ms_median_bias": t_bias[len(t_bias) // 2],
+        "attn_ms_median_nobias": t_nobias[len(t_nobias) // 2],
+        "kv_bytes_kept": layer.Kt * kv_row,
+        "kv_bytes_full": w.total_tokens * kv_row,
+    }
+
+    cold = None
+    if args.detail:
+        # Each kernel again, right after 512 MiB are written (evicting the
+        # 256 MiB Infinity Cache), on the outputs of the last timed step.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        calls = {"gate": lambda: layer.gate(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"]),
+                 "select": layer.select,
+                 "gather": lambda: layer.gather(g["hidden"]),
+                 "attention": lambda: layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"])}
+        cold = {}
+        for n, fn in calls.items():
+            ms = []
+            for _ in range(5):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            ms.sort()
+            cold[n] = {"ms_median": ms[len(ms) // 2], "ms_min": ms[0]}
+        del flush
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -277,8 +369,11 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "derived": derived,
         "gpu_ms_per_step": gpu_ms,
     }
+    if cold is not None:
+        line["cold_after_cache_flush"] = cold
     if args.detail:
         with open(args.detail, "w") as f:
             json.dump(line, f, indent=1)

@@ -169,6 +169,9 @@ tg_status tg_gather_compact(tg_dtype dt, const void *hidden, int64_t T, int32_t 
  * Requests never attend to each other.
  * q   : [Kt][Hq][d_head] in dt       k, v : [Kt][Hkv][d_head] in dt
  * s_kept : [Kt] fp32                 gain, temp : [Hq] fp32
+ * s_kept and gain may both be NULL: the bias term is then zero (plain causal
+ * GQA attention with the per-head temperature; the kernel is built without
+ * the bias stage).  Exactly one of them NULL is TG_ERR_NULL_PTR.
  * cu_kept_host : [batch+1] HOST int32, cu_kept_host[0] == 0, non-decreasing
  * out : [Kt][Hq][d_head] in dt output
  * lse : [Hq][Kt] fp32 output, or NULL

@@ -226,7 +226,10 @@ def tg_gather_compact(hidden, kept_idx, scores=None, hidden_kept=None, scores_ke
 
 def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], out=None,
                           lse=None, want_lse: bool = False, stream=None):
-    """Causal GQA token-gated attention over packed kept rows; returns (out, lse or None)."""
+    """Causal GQA token-gated attention over packed kept rows; returns (out, lse or None).
+
+    s_kept=None and gain=None drop the bias term (plain causal attention with
+    the per-head temperature)."""
     torch = _torch()
     Kt, Hq, dh = q.shape
     Hkv = k.shape[1]

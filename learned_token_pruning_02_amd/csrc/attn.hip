@@ -57,7 +57,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__
     const int64_t lo = sh.cu[b];
     const int kvh = h / (sh.Hq / sh.Hkv);
     const float c1 = temp[h] / sqrtf((float)DH);
-    const float g = gain[h];
+    const float g = s != nullptr ? gain[h] : 0.f;
     const float* qr = q + (r * sh.Hq + h) * DH;
     float qv[DH], acc[DH];
 #pragma unroll
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const float* __restrict__
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < DH; ++e) dot = fmaf(qv[e], kr[e], dot);
-        const float x = c1 * dot + g * s[j];
+        const float x = s != nullptr ? c1 * dot + g * s[j] : c1 * dot;
         const float mn = fmaxf(m, x);
         const float sc = expf(m - mn);
         const float p = expf(x - mn);
@@ -115,7 +115,7 @@ __device__ __forceinline__ int tiles_at_or_above(const AttnArgs& a, int t) {
     return c;
 }
 
-template <int DH, int HPB, int NWAVE>
+template <int DH, int HPB, int NWAVE, bool BIAS>
 __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnArgs a) {
     // NWAVE = 8: two waves per SIMD from one workgroup; 4: two workgroups per CU.
     constexpr int WPH = NWAVE / HPB;   // waves per head
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     const float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
     float gbias[HPB];
 #pragma unroll
-    for (int j = 0; j < HPB; ++j) gbias[j] = a.gain[hg * HPB + j] * LOG2E;
+    for (int j = 0; j < HPB; ++j) gbias[j] = BIAS ? a.gain[hg * HPB + j] * LOG2E : 0.f;
 
     // ---- K/V/s tile staging ------------------------------------------------
     // K (with the score bias) is staged for tile jt+1 while V is staged one
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
                 kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
                     rk, (int)(row * row_elems * 2) + 16 * c, 0, 0);
             }
-            if (st < KVT) {
+            if (BIAS && st < KVT) {
                 const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
                     (void*)(a.s + rbase + j0), (short)0, (n - j0) * 4, BUFFER_RSRC_WORD3);
                 sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * st, 0, 0));
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
                 const int row = uu / (DH / 8), c = uu % (DH / 8);
                 st16(&Ks[buf][row * KS + 8 * c], kreg[i]);
             }
-            if (st < KVT) {
+            if (BIAS && st < KVT) {
 #pragma unroll
                 for (int j = 0; j < HPB; ++j) Bs[buf][j][st] = gbias[j] * sreg;
             }
@@ -347,7 +347,8 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
             _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                               \
                 _Pragma("unroll") for (int rq = 0; rq < 4; ++rq) {                           \
                     const int kl = 32 * mt + 8 * rq + 4 * hh;                                \
-                    const f32x4 sv = *reinterpret_cast<const f32x4*>(&Bs[bb][hp][kl]);       \
+                    const f32x4 sv = BIAS ? *reinterpret_cast<const f32x4*>(&Bs[bb][hp][kl]) \
+                                          : f32x4{0.f, 0.f, 0.f, 0.f};                       \
                     _Pragma("unroll") for (int e = 0; e < 4; ++e) {                          \
                         float x = fmaf(c1, sacc[mt][4 * rq + e], sv[e]);                     \
                         if (MASKED && j0 + kl + e > qi) x = -INFINITY;                       \
@@ -400,7 +401,8 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 #define TG_VFRAG(I)                                                                          \
     as_bf16x8(ld16(&Vt[vb][(32 * ((I) / 4) + l32) * VT_STRIDE + 16 * ((I) % 4) + 8 * hh]))
 #define TG_BIAS(C)                                                                           \
-    (*reinterpret_cast<const f32x4*>(&Bs[bb][hp][32 * ((C) / 4) + 8 * ((C) % 4) + 4 * hh]))
+    (BIAS ? *reinterpret_cast<const f32x4*>(&Bs[bb][hp][32 * ((C) / 4) + 8 * ((C) % 4) + 4 * hh]) \
+          : f32x4{0.f, 0.f, 0.f, 0.f})
 #define TG_PVSM_FUSED(MASKED)                                                                \
     do {                                                                                     \
         const int vb = (jt - 1) & 1;                                                         \
@@ -521,7 +523,10 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 template <int DH, int HPB, int NWAVE>
 hipError_t launch_bf16(const AttnArgs& a, int total_tiles, hipStream_t st) {
     const int blocks = total_tiles * a.n_hg;
-    hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB, NWAVE>), dim3(blocks), dim3(64 * NWAVE), 0, st, a);
+    if (a.s != nullptr)
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB, NWAVE, true>), dim3(blocks), dim3(64 * NWAVE), 0, st, a);
+    else
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB, NWAVE, false>), dim3(blocks), dim3(64 * NWAVE), 0, st, a);
     return hipGetLastError();
 }
 

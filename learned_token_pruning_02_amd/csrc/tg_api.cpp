@@ -161,8 +161,8 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const
                                 int32_t Hkv, int32_t d_head, void* out, float* lse,
                                 hipStream_t stream) {
     if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
-    if (q == nullptr || k == nullptr || v == nullptr || s_kept == nullptr || gain == nullptr ||
-        temp == nullptr || cu_kept_host == nullptr || out == nullptr)
+    if (q == nullptr || k == nullptr || v == nullptr || temp == nullptr || cu_kept_host == nullptr ||
+        out == nullptr || (s_kept == nullptr) != (gain == nullptr))
         return TG_ERR_NULL_PTR;
     if (batch < 1 || batch > TG_MAX_BATCH || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
         return TG_ERR_BAD_SHAPE;
@@ -184,8 +184,9 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const
             if ((int64_t)(cu_kept_host[i + 1] - cu_kept_host[i]) * Hkv * d_head * 2 >= I32_LIMIT)
                 return TG_ERR_UNSUPPORTED;
     }
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(s_kept) ||
-        !aligned4(gain) || !aligned4(temp) || (lse != nullptr && !aligned4(lse)))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (s_kept != nullptr && (!aligned4(s_kept) || !aligned4(gain))) || !aligned4(temp) ||
+        (lse != nullptr && !aligned4(lse)))
         return TG_ERR_ALIGNMENT;
     const int64_t eb = elt_bytes(dt);
     const int64_t qb = sh.Kt * Hq * d_head * eb, kb = sh.Kt * Hkv * d_head * eb;

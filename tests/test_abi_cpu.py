@@ -166,6 +166,8 @@ def test_attention_validation():
     assert call(dt=5) == 4
     assert call(q=None) == 1
     assert call(temp=None) == 1
+    assert call(s=None) == 1             # s_kept and gain are NULL together or not at all
+    assert call(gain=None) == 1
     assert call(cu=None) == 1
     assert call(batch=0) == 2
     assert call(batch=tg.TG_MAX_BATCH + 1) == 2

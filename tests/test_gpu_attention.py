@@ -70,6 +70,35 @@ def test_attention_gain0_temp1_is_plain_causal():
     assert_within(out, ref, 2e-2, 1e-2, "gain0/temp1")
 
 
+@pytest.mark.parametrize("lens,Hq,Hkv,dh", [([333, 77], 16, 8, 128), ([8192], 16, 8, 128), ([200, 129], 4, 2, 64)])
+def test_attention_without_bias(lens, Hq, Hkv, dh):
+    """s_kept = gain = NULL: the bias-free build equals the definition with a
+    zero bias (checked on sampled rows for the larger case)."""
+    announce(f"attn no-bias lens={lens} Hq={Hq} Hkv={Hkv} dh={dh}")
+    q, k, v, s, gain, temp, cu = _inputs(lens, Hq, Hkv, dh, torch.bfloat16, seed=31)
+    out, lse = tg.tg_gated_attn_prefill(q.cuda(), k.cuda(), v.cuda(), None, None, temp.cuda(), cu,
+                                        want_lse=True)
+    out, lse = out.cpu(), lse.cpu()
+    zero = torch.zeros_like(s)
+    if sum(lens) > 4096:
+        rows = _sampled_rows(cu, 16, seed=7)
+        ref, ref_lse = oracle.gated_attention_rows(q, k, v, zero, gain, temp, cu, rows)
+        out, lse = out[rows], lse[:, rows]
+    else:
+        ref, ref_lse = oracle.gated_attention(q, k, v, zero, gain, temp, cu)
+    assert_within(out, ref, 2e-2, 1e-2, "no-bias out")
+    assert_within(lse, ref_lse, 2e-2, 1e-2, "no-bias lse")
+
+
+def test_attention_fp32_without_bias():
+    q, k, v, s, gain, temp, cu = _inputs([100, 30], 4, 2, 64, torch.float32, seed=32)
+    out, lse = tg.tg_gated_attn_prefill(q.cuda(), k.cuda(), v.cuda(), None, None, temp.cuda(), cu,
+                                        want_lse=True)
+    ref, ref_lse = oracle.gated_attention(q, k, v, torch.zeros_like(s), gain, temp, cu)
+    assert_within(out.cpu(), ref, 1e-5, 1e-5, "fp32 no-bias out")
+    assert_within(lse.cpu(), ref_lse, 1e-5, 1e-5, "fp32 no-bias lse")
+
+
 def test_attention_large_bias_range():
     """Scores spread over +-40: the bias dominates the logits."""
     q, k, v, s, gain, temp, cu = _inputs([513], 16, 8, 128, torch.bfloat16, seed=22, s_scale=20.0)

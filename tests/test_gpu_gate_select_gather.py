@@ -147,6 +147,13 @@ def test_select_max_batch_and_large_request():
     _select_case([T], [128], [T // 16], workloads.random_scores(T, seed=10))
 
 
+def test_select_sweep_scale():
+    """The selector at the throughput sweep's scale (one request, no tail,
+    K = T/16), bit-exact against the oracle."""
+    T = 1 << 24
+    _select_case([T], [0], [T // 16], workloads.random_scores(T, seed=11))
+
+
 # ---------------------------------------------------------------- gather ----
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 2048), (torch.float32, 256), (torch.bfloat16, 8)])
 def test_gather_bitwise(dtype, d):
