@@ -27,6 +27,8 @@
 //      and write the kept ids in index order (wave ballots + a small count
 //      table per workgroup), and the question tail after them.
 // Results do not depend on which workgroup finishes last.
+#include <algorithm>
+
 #include "tg_device.h"
 #include "tg_kernels.h"
 
@@ -40,7 +42,10 @@ constexpr int SITEMS = 8;               // keys per thread
 constexpr int SCHUNK = SB * SITEMS;     // 2048 keys per chunk
 constexpr int NBIN = 2048;
 constexpr int META = 8;                 // u32 words of per-request metadata
-constexpr int CTR = 4;                  // u32 counters per request
+constexpr int CTR = 16;                 // u32 counters per request (tickets, candidate count)
+constexpr int NPASS = 5;                // radix passes over the 52-bit candidate composite
+constexpr int BIG_DOC = 1 << 20;        // documents above this rank their candidates with every workgroup
+constexpr int RANK_WG = 512;            // workgroups of the many-workgroup candidate passes
 constexpr uint32_t CAND_LDS = 8192;     // threshold-bucket candidates staged in LDS
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -55,6 +60,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
     return ((uint64_t)(key & 0x1fffffu) << 31) | (uint64_t)(0x7fffffffu - idx);
 }
+
+// Digit p of the composite: bit offset and width (11 + 10 + 11 + 11 + 9 = 52).
+__device__ __forceinline__ int pass_shift(int p) {
+    return p == 0 ? 41 : (p == 1 ? 31 : (p == 2 ? 20 : (p == 3 ? 9 : 0)));
+}
+__device__ __forceinline__ int pass_width(int p) { return p == 1 ? 10 : (p == 4 ? 9 : 11); }
 
 __device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -95,8 +106,12 @@ struct SelArgs {
     int32_t* kept;
     int32_t* cu_dev;
     uint32_t* hist;       // [B][NBIN]
-    uint32_t* meta;       // [B][META]: d1, rem1, cnt1, cprefix lo/hi, cmask lo/hi
-    uint32_t* ctr;        // [B][CTR]: hist ticket, candidate ticket, candidate count
+    uint32_t* meta;       // [B][META]: d1, rem1, cnt1, cprefix lo/hi, cmask lo/hi, done
+    uint32_t* ctr;        // [B][CTR]: hist ticket, candidate ticket, candidate count,
+                          //           rank-pass tickets [4, 4+NPASS), count ticket 4+NPASS
+    uint32_t* rank_hist;  // [B][NPASS][NBIN] (many-workgroup ranking only)
+    uint32_t* chunk_kept; // [doc chunks]: kept candidates per chunk (many-workgroup ranking only)
+    int32_t big;          // rank candidates with every workgroup (some document > BIG_DOC)
     uint32_t* chunk_def;  // [doc chunks]: keys above d1
     uint32_t* chunk_off;  // [doc chunks]: output offset of the chunk's first kept token
     uint2* cand;          // [T]: (key, local index), request b at off[b]
@@ -159,10 +174,13 @@ __device__ __forceinline__ void find_bin(Get get, int nb, uint32_t rem, uint32_t
 
 // ------------------------------------------------------------- launch 1 ----
 __global__ __launch_bounds__(SB) void sel_clear_kernel(uint32_t* hist, uint32_t* ctr, int n_hist,
-                                                       int n_ctr) {
+                                                       int n_ctr, uint32_t* rank_hist, int n_rank,
+                                                       uint32_t* chunk_kept, int n_kept) {
     const int i = blockIdx.x * SB + threadIdx.x;
     if (i < n_hist) hist[i] = 0u;
     if (i < n_ctr) ctr[i] = 0u;
+    if (i < n_rank) rank_hist[i] = 0u;
+    if (i < n_kept) chunk_kept[i] = 0u;
 }
 
 // ------------------------------------------------------------- launch 2 ----
@@ -260,6 +278,15 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     __syncthreads();
     if (!sh_last) return;
 
+    if (a.big) {
+        // Ranking is left to the many-workgroup passes (sel_rank_kernel).
+        if (tid == 0) {
+            m[3] = m[4] = m[5] = m[6] = 0u;
+            m[7] = 0u;
+        }
+        return;
+    }
+
     // ---- the last chunk: exact rank inside bucket d1 ----------------------
     // Candidates are staged once into LDS when they fit (the usual case: a
     // bucket holds a few thousand keys); a degenerate bucket (heavy ties) is
@@ -273,9 +300,9 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     uint32_t rem = m[1];
     uint64_t cprefix = 0, cmask = 0;
 #pragma unroll 1
-    for (int p = 0; p < 5; ++p) {
-        const int sh = p == 0 ? 41 : (p == 1 ? 31 : (p == 2 ? 20 : (p == 3 ? 9 : 0)));
-        const int wd = p == 1 ? 10 : (p == 4 ? 9 : 11);
+    for (int p = 0; p < NPASS; ++p) {
+        const int sh = pass_shift(p);
+        const int wd = pass_width(p);
         const int nb = 1 << wd;
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
         __syncthreads();
@@ -333,6 +360,112 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         m[4] = (uint32_t)(cprefix >> 32);
         m[5] = (uint32_t)cmask;
         m[6] = (uint32_t)(cmask >> 32);
+    }
+}
+
+// ------------------------------------ large documents: ranking by all ----
+// The same radix passes over the candidate composite as the last chunk runs
+// above, with the candidate list of every selecting request spread over
+// RANK_WG workgroups: each histograms its share of the candidates that match
+// the prefix fixed so far (LDS, then global atomics), and the workgroup that
+// finishes last picks the digit and updates the request's prefix.  Launched
+// once per pass; a request whose rank is already fixed is skipped.
+__global__ __launch_bounds__(SB) void sel_rank_kernel(SelArgs a, int p) {
+    __shared__ uint32_t h[NBIN];
+    __shared__ uint32_t wtot[SWAVES];
+    __shared__ uint32_t sh_last, sh_d, sh_gt, sh_cnt;
+    const int tid = threadIdx.x;
+    const int sh = pass_shift(p), nb = 1 << pass_width(p);
+    for (int b = 0; b < a.batch; ++b) {
+        if (a.doc_chunk0[b + 1] == a.doc_chunk0[b]) continue;  // not selecting
+        uint32_t* m = a.meta + b * META;
+        if (m[7] != 0u) continue;  // rank already fixed by an earlier pass
+        const uint32_t cnt1 = m[2];
+        const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
+        const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
+        const uint2* cand = a.cand + a.off[b];
+        for (int i = tid; i < nb; i += SB) h[i] = 0u;
+        __syncthreads();
+        for (uint32_t j = blockIdx.x * SB + tid; j < cnt1; j += RANK_WG * SB) {
+            const uint2 e = cand[j];
+            const uint64_t cp = composite(e.x, e.y);
+            if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
+        }
+        __syncthreads();
+        uint32_t* gh = a.rank_hist + ((size_t)b * NPASS + p) * NBIN;
+        for (int i = tid; i < nb; i += SB)
+            if (h[i] != 0u) atomicAdd(&gh[i], h[i]);
+        wait_own_writes();
+        __syncthreads();
+        if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 4 + p], 1u) == (uint32_t)(RANK_WG - 1);
+        __syncthreads();
+        if (sh_last) {
+            const uint32_t rem = m[1];
+            find_bin([&](int i) { return coherent_load(&gh[i]); }, nb, rem, wtot, &sh_d, &sh_gt,
+                     &sh_cnt);
+            if (tid == 0) {
+                const uint32_t rem2 = rem - sh_gt;
+                const uint64_t np = cprefix | ((uint64_t)sh_d << sh);
+                const uint64_t nm = cmask | ((uint64_t)(nb - 1) << sh);
+                m[1] = rem2;
+                m[3] = (uint32_t)np;
+                m[4] = (uint32_t)(np >> 32);
+                m[5] = (uint32_t)nm;
+                m[6] = (uint32_t)(nm >> 32);
+                if (sh_cnt == rem2) m[7] = 1u;  // every composite with this prefix is kept
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Kept candidates per chunk (global atomics over all workgroups), then the
+// workgroup finishing last scans every chunk's kept count into its output
+// offset, as the last chunk of sel_cand does for small documents.
+__global__ __launch_bounds__(SB) void sel_rankcount_kernel(SelArgs a) {
+    __shared__ uint32_t wtot[SWAVES];
+    __shared__ uint32_t sh_last, sh_total;
+    const int tid = threadIdx.x;
+    for (int b = 0; b < a.batch; ++b) {
+        if (a.doc_chunk0[b + 1] == a.doc_chunk0[b]) continue;
+        const uint32_t* m = a.meta + b * META;
+        const uint32_t cnt1 = m[2];
+        const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
+        const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
+        const uint2* cand = a.cand + a.off[b];
+        uint32_t* kc = a.chunk_kept + a.doc_chunk0[b];
+        for (uint32_t j = blockIdx.x * SB + tid; j < cnt1; j += RANK_WG * SB) {
+            const uint2 e = cand[j];
+            if ((composite(e.x, e.y) & cmask) >= cprefix) atomicAdd(&kc[e.y / SCHUNK], 1u);
+        }
+        wait_own_writes();
+        __syncthreads();
+        if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 4 + NPASS], 1u) == (uint32_t)(RANK_WG - 1);
+        __syncthreads();
+        if (!sh_last) continue;
+        const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
+        const uint32_t* def = a.chunk_def + a.doc_chunk0[b];
+        uint32_t* coff = a.chunk_off + a.doc_chunk0[b];
+        uint32_t carry = 0;
+        constexpr int per = NBIN / SB;
+        for (int c0 = 0; c0 < nck; c0 += NBIN) {
+            uint32_t v[per];
+            uint32_t sum = 0;
+            for (int j = 0; j < per; ++j) {
+                const int ch = c0 + tid * per + j;
+                v[j] = ch < nck ? coherent_load(&kc[ch]) + coherent_load(&def[ch]) : 0u;
+                sum += v[j];
+            }
+            const uint32_t incl = block_incl_scan(sum, wtot, &sh_total);
+            uint32_t run = carry + incl - sum;
+            for (int j = 0; j < per; ++j) {
+                const int ch = c0 + tid * per + j;
+                if (ch < nck) coff[ch] = run;
+                run += v[j];
+            }
+            carry += sh_total;
+            __syncthreads();
+        }
     }
 }
 
@@ -405,7 +538,7 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-    size_t hist, meta, ctr, def, off, cand, total;
+    size_t hist, meta, ctr, def, off, cand, rank, kept, total;
 };
 
 WsLayout ws_layout(int batch, int doc_chunks, int64_t T) {
@@ -417,6 +550,8 @@ WsLayout ws_layout(int batch, int doc_chunks, int64_t T) {
     L.def = p;  p = align256(p + (size_t)doc_chunks * 4);
     L.off = p;  p = align256(p + (size_t)doc_chunks * 4);
     L.cand = p; p = align256(p + (size_t)T * 8);
+    L.rank = p; p = align256(p + (size_t)batch * NPASS * NBIN * 4);
+    L.kept = p; p = align256(p + (size_t)doc_chunks * 4);
     L.total = p;
     return L;
 }
@@ -473,12 +608,26 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
     s.chunk_def = (uint32_t*)(base + L.def);
     s.chunk_off = (uint32_t*)(base + L.off);
     s.cand = (uint2*)(base + L.cand);
+    s.rank_hist = (uint32_t*)(base + L.rank);
+    s.chunk_kept = (uint32_t*)(base + L.kept);
+    s.big = 0;
+    for (int b = 0; b < a.batch; ++b)
+        if (s.doc_chunk0[b + 1] > s.doc_chunk0[b] &&
+            a.cu_seq[b + 1] - a.cu_seq[b] - a.q_len[b] > BIG_DOC)
+            s.big = 1;
     if (dc > 0) {
         const int n_hist = a.batch * NBIN, n_ctr = a.batch * CTR;
-        hipLaunchKernelGGL(sel_clear_kernel, dim3((n_hist + SB - 1) / SB), dim3(SB), 0, st, s.hist,
-                           s.ctr, n_hist, n_ctr);
+        const int n_rank = s.big ? a.batch * NPASS * NBIN : 0, n_kept = s.big ? dc : 0;
+        const int n_clear = std::max(std::max(n_hist, n_ctr), std::max(n_rank, n_kept));
+        hipLaunchKernelGGL(sel_clear_kernel, dim3((n_clear + SB - 1) / SB), dim3(SB), 0, st, s.hist,
+                           s.ctr, n_hist, n_ctr, s.rank_hist, n_rank, s.chunk_kept, n_kept);
         hipLaunchKernelGGL(sel_hist_kernel, dim3(dc), dim3(SB), 0, st, s);
         hipLaunchKernelGGL(sel_cand_kernel, dim3(dc), dim3(SB), 0, st, s);
+        if (s.big) {
+            for (int p = 0; p < NPASS; ++p)
+                hipLaunchKernelGGL(sel_rank_kernel, dim3(RANK_WG), dim3(SB), 0, st, s, p);
+            hipLaunchKernelGGL(sel_rankcount_kernel, dim3(RANK_WG), dim3(SB), 0, st, s);
+        }
     }
     hipLaunchKernelGGL(sel_compact_kernel, dim3(ac), dim3(SB), 0, st, s);
     return hipGetLastError();

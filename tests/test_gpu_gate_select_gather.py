@@ -154,6 +154,27 @@ def test_select_sweep_scale():
     _select_case([T], [0], [T // 16], workloads.random_scores(T, seed=11))
 
 
+@pytest.mark.parametrize("levels", [0, 40, 5000])
+def test_select_large_document_path(levels):
+    """Documents above 2^20 tokens rank their threshold candidates with every
+    workgroup; with heavy ties the passes run down to the index digits."""
+    T = (1 << 21) + 5
+    s = workloads.random_scores(T, seed=12, ties=levels) if levels else workloads.random_scores(T, seed=12)
+    _select_case([T], [77], [T // 10], s)
+
+
+def test_select_large_document_in_a_batch():
+    """One large document switches the whole batch to the many-workgroup
+    ranking; the small requests must come out the same."""
+    seq = [(1 << 20) + 3000, 5000, 70000, 9]
+    q = [100, 10, 0, 3]
+    bud = [300000, 4000, 6000, 4]
+    g = torch.Generator().manual_seed(13)
+    s = torch.randn(sum(seq), generator=g)
+    s[(1 << 20):(1 << 20) + 2000] = 0.5  # a run of equal scores near the first threshold
+    _select_case(seq, q, bud, s)
+
+
 # ---------------------------------------------------------------- gather ----
 @pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 2048), (torch.float32, 256), (torch.bfloat16, 8)])
 def test_gather_bitwise(dtype, d):
