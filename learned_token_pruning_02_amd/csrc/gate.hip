@@ -278,9 +278,10 @@ template <int DG>
 hipError_t launch_gate_bf16_dg(const bf16* hidden, int64_t T, int d, const bf16* w1,
                                const bf16* b1, const bf16* w2, const bf16* b2, float* scores,
                                hipStream_t st) {
-    // Largest token tile that still gives about two workgroups per CU (one
+    // Largest token tile that still gives at least one workgroup per CU (one
     // wave with d_gate 256 would need 128 registers of W1 staging: not used).
-    if (T >= 256 * 512) {
+    // Fewer, larger workgroups read each W1 chunk for more tokens.
+    if (T >= 256 * 256) {
         hipLaunchKernelGGL((gate_bf16_kernel<DG, 4>), dim3((T + 255) / 256), dim3(256), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
     } else if (DG == 256 || T >= 128 * 512) {
