@@ -63,12 +63,12 @@ constexpr int GK = 64;   // k chunk
 constexpr int RING = 3;  // residual fragment sets per wave (two chunks in flight)
 constexpr int RED_STRIDE = 36;  // floats per row of the unit-sum tile (16-byte aligned, skewed banks)
 
-template <int DG, int WAVES>
+template <int DG, int WAVES, int MT>
 __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     const bf16* __restrict__ hidden, int64_t T, int d, const bf16* __restrict__ w1,
     const bf16* __restrict__ b1, const bf16* __restrict__ w2, const bf16* __restrict__ b2,
     float* __restrict__ scores) {
-    constexpr int BM = 64 * WAVES;
+    constexpr int BM = 32 * MT * WAVES;   // tokens per workgroup (MT 32-token blocks per wave)
     constexpr int NT = DG / 32;            // 32-unit tiles
     constexpr int NFRAG = NT * 4;          // W1 fragments (1 KB each) per k chunk
 
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     // unit-lane partials, rows padded to RED_STRIDE floats.  It lives in the
     // W1 buffers (dead after the last barrier) whenever they are big enough,
     // so that it costs no extra LDS.
-    constexpr int RED_FLOATS = 64 * RED_STRIDE;
+    constexpr int RED_FLOATS = 32 * MT * RED_STRIDE;
     constexpr bool RED_IN_WL = WAVES * RED_FLOATS * 4 <= 2 * NFRAG * WAVE * 16;
     __shared__ __attribute__((aligned(16))) float red_own[RED_IN_WL ? 4 : WAVES * RED_FLOATS];
 
@@ -88,10 +88,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     const int l32 = lane % 32;
     const int64_t tok0 = (int64_t)blockIdx.x * BM;
 
-    const bf16* arow[2];
+    const bf16* arow[MT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        int64_t r = tok0 + 64 * w + 32 * mt + l32;
+    for (int mt = 0; mt < MT; ++mt) {
+        int64_t r = tok0 + 32 * MT * w + 32 * mt + l32;
         if (r > T - 1) r = T - 1;
         arow[mt] = hidden + r * d + 32 * hh;
     }
@@ -119,10 +119,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     for (int kk = 0; kk < 4; ++kk) rd_pos[kk] = lane ^ (2 * kk + 8 * hh);
     u32x4 wreg[WUNITS];
 
-    u32x4 a0[2][4], a1[2][4], a2[2][4];
-    f32x16 acc[2][NT];
+    u32x4 a0[MT][4], a1[MT][4], a2[MT][4];
+    f32x16 acc[MT][NT];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
 #define TG_LOAD_W1(step, li) wreg[li] = ld16(wbase + (int64_t)(R * (li)) * d + rot_k(step))
 #define TG_LOAD_A(dst, step)                                                                 \
     do {                                                                                     \
-        _Pragma("unroll") for (int li = 0; li < 8; ++li) TG_LOAD_A1(dst, step, li);          \
+        _Pragma("unroll") for (int li = 0; li < 4 * MT; ++li) TG_LOAD_A1(dst, step, li);     \
     } while (0)
 #define TG_LOAD_W(step)                                                                      \
     do {                                                                                     \
@@ -163,9 +163,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     // instead of stalling the wave at the top of the chunk.
 #define TG_MMA_LOADS(cur, b, kk, NL, LOAD1)                                                  \
     do {                                                                                     \
-        _Pragma("unroll") for (int j = 0; j < 2 * NT; ++j) {                                 \
-            acc[j % 2][j / 2] = mfma32(as_bf16x8(cur[j % 2][kk]), b[j / 2], acc[j % 2][j / 2]); \
-            _Pragma("unroll") for (int li = j * (NL) / (2 * NT); li < (j + 1) * (NL) / (2 * NT); ++li) \
+        _Pragma("unroll") for (int j = 0; j < MT * NT; ++j) {                                \
+            acc[j % MT][j / MT] = mfma32(as_bf16x8(cur[j % MT][kk]), b[j / MT], acc[j % MT][j / MT]); \
+            _Pragma("unroll") for (int li = j * (NL) / (MT * NT); li < (j + 1) * (NL) / (MT * NT); ++li) \
                 LOAD1(li);                                                                   \
             __builtin_amdgcn_sched_barrier(0);                                               \
         }                                                                                    \
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
 #define TG_MMA(cur, b, kk)                                                                   \
     do {                                                                                     \
         _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                    \
-            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                 \
+            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                \
                 acc[mt][nt] = mfma32(as_bf16x8(cur[mt][kk]), b[nt], acc[mt][nt]);            \
     } while (0)
     bf16x8 bA[NT], bB[NT];
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
         TG_MMA_LOADS(cur, bA, 0, WUNITS, TG_LW);                                             \
         TG_READ_B(bA, buf_, 2);                                                              \
         __builtin_amdgcn_sched_barrier(0);                                                   \
-        TG_MMA_LOADS(cur, bB, 1, 8, TG_LA);                                                  \
+        TG_MMA_LOADS(cur, bB, 1, 4 * MT, TG_LA);                                             \
         TG_READ_B(bB, buf_, 3);                                                              \
         __builtin_amdgcn_sched_barrier(0);                                                   \
         TG_MMA(cur, bA, 2);                                                                  \
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     }
     float* rt = (RED_IN_WL ? reinterpret_cast<float*>(&wl[0][0]) : red_own) + w * RED_FLOATS;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             float p = 0.f;
@@ -261,15 +261,15 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
         }
     }
     __builtin_amdgcn_wave_barrier();
-    float sum = b2 != nullptr ? to_f32(b2[0]) : 0.f;
+    if (lane < 32 * MT) {
+        float sum = b2 != nullptr ? to_f32(b2[0]) : 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&rt[lane * RED_STRIDE + 4 * c]);
-        sum += (v[0] + v[1]) + (v[2] + v[3]);
-    }
-    {
+        for (int c = 0; c < 8; ++c) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(&rt[lane * RED_STRIDE + 4 * c]);
+            sum += (v[0] + v[1]) + (v[2] + v[3]);
+        }
         const int j = lane / 2, half = lane % 2, mt = j / 16, r = j % 16;
-        const int64_t t = tok0 + 64 * w + 32 * mt + 8 * (r / 4) + 4 * half + (r % 4);
+        const int64_t t = tok0 + 32 * MT * w + 32 * mt + 8 * (r / 4) + 4 * half + (r % 4);
         if (t < T) scores[t] = sum;
     }
 }
@@ -278,17 +278,21 @@ template <int DG>
 hipError_t launch_gate_bf16_dg(const bf16* hidden, int64_t T, int d, const bf16* w1,
                                const bf16* b1, const bf16* w2, const bf16* b2, float* scores,
                                hipStream_t st) {
-    // Largest token tile that still gives at least one workgroup per CU (one
-    // wave with d_gate 256 would need 128 registers of W1 staging: not used).
-    // Fewer, larger workgroups read each W1 chunk for more tokens.
+    // Largest token tile that still gives at least one workgroup per CU:
+    // fewer, larger workgroups read each W1 chunk for more tokens.  Below
+    // that, 32-token waves (MT = 1) double the waves for the same tile.  (One
+    // wave with d_gate 256 would need 128 registers of W1 staging: not used.)
     if (T >= 256 * 256) {
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4>), dim3((T + 255) / 256), dim3(256), 0, st,
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 2>), dim3((T + 255) / 256), dim3(256), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
-    } else if (DG == 256 || T >= 128 * 512) {
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 2>), dim3((T + 127) / 128), dim3(128), 0, st,
+    } else if (DG == 256) {
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 1>), dim3((T + 127) / 128), dim3(256), 0, st,
+                           hidden, T, d, w1, b1, w2, b2, scores);
+    } else if (T >= 128 * 512) {
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 2, 2>), dim3((T + 127) / 128), dim3(128), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
     } else if constexpr (DG != 256) {
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 1>), dim3((T + 63) / 64), dim3(64), 0, st,
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 1, 2>), dim3((T + 63) / 64), dim3(64), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
     }
     return hipGetLastError();
