@@ -14,18 +14,24 @@
 //     LDS (A operand), Q fragments resident in registers (B operand), so each
 //     lane holds all scores of ONE query row and the row max / row sum need
 //     only one exchange with the partner lane half;
-//   scale and bias are one FMA in the exp2 domain: x = c1*S + g2*s_j with
-//     c1 = temp*log2(e)/sqrt(d), g2 = gain*log2(e);
+//   the product lands directly in the exp2 domain with the bias added and the
+//     row's exponent base subtracted: Q is pre-scaled by temp*log2(e)/sqrt(d),
+//     and one extra k step multiplies a per-key column [s split into two bf16
+//     halves, 1] with a per-query one [gain*log2(e) split likewise, -base], so
+//     the softmax needs no per-element scale, bias or subtraction;
 //   O^T[dh][query] += V^T . P^T: V is stored transposed in LDS (A operand) and
 //     the probabilities, converted to bf16, are fed straight from the S
 //     registers as the B operand, again one query per lane, so the online
 //     rescale of O needs no data exchange.
 // Only the tiles on the diagonal (or past the end of the request) are masked,
 // and a wave skips tiles whose keys all lie after its rows.  The exponent base
-// of each row only moves when the row max exceeds it by more than 2^8, so the
-// rescale of O is rare; the final O / l and lse are exact either way.
-// K/V tiles are double buffered: the next tile is fetched into registers
-// while the current one is consumed.  Heavy query tiles (many keys) are
+// of each row only moves when the row max exceeds it by more than 2^8 (and
+// then from the next tile on), so the rescale of O is rare; the final O / l
+// and lse are exact either way.  Row sums are taken from the bf16
+// probabilities that feed the PV product, two per dot instruction.
+// K/V tiles are double buffered: the next tile is fetched into registers,
+// in four loads spread between the QK MFMAs, while the current one is
+// consumed.  Heavy query tiles (many keys) are
 // dispatched first and consecutive workgroup ids cycle over the KV heads, so
 // the 8 XCDs each keep one head's K/V in their own L2.
 #include "tg_device.h"
@@ -37,6 +43,7 @@ namespace {
 
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
+constexpr bf16x2 ONES = {(bf16)1.0f, (bf16)1.0f};
 
 // ---------------------------------------------------------------- fp32 ----
 template <int DH>
@@ -120,22 +127,21 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     // NWAVE = 8: two waves per SIMD from one workgroup; 4: two workgroups per CU.
     constexpr int WPH = NWAVE / HPB;   // waves per head
     constexpr int BQ = 32 * WPH;       // query rows per head per workgroup
-    constexpr int KS = DH + 8;         // LDS row stride of K (bf16 elements)
+    constexpr int KS = DH + 8;         // LDS row stride of K: DH values, then the 8-value bias column
     constexpr int KU = KVT * DH / 8 / 256;  // 16-byte K units per staging thread per tile
     constexpr int VU = (KVT / 4) * (DH / 8);  // V units (4 keys x 8 dh) per tile
-    constexpr int NKK = DH / 16;       // k steps of the QK^T product
+    constexpr int NKK = DH / 16;       // k steps of the QK^T product (plus one for the bias column)
     constexpr int NMD = DH / 32;       // 32-row dh tiles of O^T
-    constexpr float RESCALE_SLACK = 8.0f;  // log2 headroom before O is rescaled
+    constexpr float RESCALE_SLACK = 8.0f;   // log2 headroom before a row's base moves
+    constexpr float REBASE_LIMIT = 64.0f;   // beyond it, exponentials are redone against the new base
     // Four waves (two workgroups per CU) interleave the softmax with the PV
     // MFMAs by hand, slice by slice; eight waves (one workgroup per CU) leave
     // the interleave to scheduling groups, which measures faster there.
     constexpr bool FUSED = NWAVE == 4;
-    constexpr int NKB = 2;  // K / bias buffers
+    constexpr int NKB = 2;  // K buffers
 
     __shared__ __attribute__((aligned(16))) bf16 Ks[NKB][KVT * KS];
     __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * VT_STRIDE];
-    // Per key of the tile and per head of the workgroup: g_h log2(e) s_j.
-    __shared__ __attribute__((aligned(16))) float Bs[NKB][HPB][KVT];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -183,20 +189,48 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     const bool qvalid = qi < n;
 
     // ---- resident Q fragments (B operand of S^T = K Q^T) ----------------
+    // Q is scaled by c1 = temp * log2(e) / sqrt(d) on the way in, so that the
+    // MFMA yields the exp2-domain logit directly.
+    const float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
     bf16x8 qf[NKK];
     {
         const bf16* qp = a.q + ((rbase + (qvalid ? qi : 0)) * a.Hq + h) * DH + (DH / 2) * hh;
         const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(qvalid ? ld16(qp + 8 * kk) : zero);
-    }
-    const float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
-    float gbias[HPB];
+        for (int kk = 0; kk < NKK; ++kk) {
+            bf16x8 v = as_bf16x8(qvalid ? ld16(qp + 8 * kk) : zero);
 #pragma unroll
-    for (int j = 0; j < HPB; ++j) gbias[j] = BIAS ? a.gain[hg * HPB + j] * LOG2E : 0.f;
+            for (int e = 0; e < 8; ++e) v[e] = to_bf16((float)v[e] * c1);
+            qf[kk] = v;
+        }
+    }
+    // ---- the bias column --------------------------------------------------
+    // One more k step of the same product adds the gate bias and subtracts
+    // the row's exponent base: per key, the K side holds
+    //     [s_hi, s_hi, s_lo, s_lo, 1, 1, 0, 0]      (s = s_hi + s_lo in bf16)
+    // and lane half 0 of each query holds
+    //     [g_hi, g_lo, g_hi, g_lo, -m_hi, -m_lo, 0, 0]  (g = gain * log2(e))
+    // (lane half 1: zeros), so the step contributes (g_hi + g_lo)(s_hi + s_lo)
+    // - m with bf16 products that are exact in the fp32 accumulator.  The base
+    // m is kept as the value its two bf16 halves represent.
+    uint32_t qx_g = 0u;
+    if (BIAS && hh == 0) {
+        const float g = a.gain[h] * LOG2E;
+        const bf16 g_hi = to_bf16(g);
+        const bf16 g_lo = to_bf16(g - (float)g_hi);
+        qx_g = __builtin_bit_cast(uint32_t, bf16x2{g_hi, g_lo});
+    }
+    u32x4 qx = {qx_g, qx_g, 0u, 0u};
+    float mcur = 0.f;  // base subtracted by the bias column in the next QK product
+    auto set_base = [&](float m_new) {
+        const bf16 b_hi = to_bf16(-m_new);
+        const bf16 b_lo = to_bf16(-m_new - (float)b_hi);
+        mcur = -((float)b_hi + (float)b_lo);
+        qx[2] = hh == 0 ? __builtin_bit_cast(uint32_t, bf16x2{b_hi, b_lo}) : 0u;
+    };
 
     // ---- K/V/s tile staging ------------------------------------------------
-    // K (with the score bias) is staged for tile jt+1 while V is staged one
+    // K (with its bias column) is staged for tile jt+1 while V is staged one
     // tile behind, for tile jt: iteration jt computes QK and the softmax of
     // tile jt next to the PV product of tile jt-1, so each wave overlaps its
     // own VALU work with MFMAs.  With 8 waves, threads [0, 256) stage V and
@@ -220,33 +254,64 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
             (void*)(base + (rbase + j0) * row_elems + kvh * DH), (short)0,
             (int)((n - j0) * row_elems * 2), BUFFER_RSRC_WORD3);
     };
-    auto load_k = [&](int jt) {
+    // Load i (0..3) of this thread's share of K tile jt (with the bias of
+    // its keys at i = 0) and of V tile jv.  The four loads are issued at
+    // separate points of a step, between MFMAs, so that the vector memory
+    // pipe works through them in the background instead of holding up every
+    // wave at the top of the step.
+    // The loads are branch-free: a tile that is not needed gets a buffer of
+    // size zero, and lanes without a unit get an offset past the buffer, so
+    // both read zeros without touching memory.
+    constexpr int OFF_NONE = 0x7ffffff0;
+    auto k_rsrc = [&](bool kdo, int jt) {
         const int j0 = jt * KVT;
-        if (kstager) {
-            const __amdgpu_buffer_rsrc_t rk = tile_rsrc(a.k, j0);
-#pragma unroll
-            for (int i = 0; i < KU; ++i) {
-                const int uu = st + i * 256;
-                const int row = uu / (DH / 8), c = uu % (DH / 8);
-                kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rk, (int)(row * row_elems * 2) + 16 * c, 0, 0);
-            }
-            if (BIAS && st < KVT) {
-                const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                    (void*)(a.s + rbase + j0), (short)0, (n - j0) * 4, BUFFER_RSRC_WORD3);
-                sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * st, 0, 0));
-            }
-        }
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.k + (rbase + j0) * row_elems + kvh * DH), (short)0,
+            kdo ? (int)((n - j0) * row_elems * 2) : 0, BUFFER_RSRC_WORD3);
     };
-    auto load_v = [&](int jt) {
-        const int j0 = jt * KVT;
-        if (vstager && st < VU) {
-            const __amdgpu_buffer_rsrc_t rv = tile_rsrc(a.v, j0);
-            const int kg = st % (KVT / 4), dg = st / (KVT / 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rv, (int)((4 * kg + i) * row_elems * 2) + 16 * dg, 0, 0);
+    auto v_rsrc = [&](bool vdo, int jv) {
+        const int j0 = jv * KVT;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(a.v + (rbase + j0) * row_elems + kvh * DH), (short)0,
+            vdo ? (int)((n - j0) * row_elems * 2) : 0, BUFFER_RSRC_WORD3);
+    };
+    auto k_off = [&](int i) {
+        const int uu = st + i * 256;
+        const int row = uu / (DH / 8), c = uu % (DH / 8);
+        return (int)(row * row_elems * 2) + 16 * c;
+    };
+    auto v_off = [&](int i) {
+        const int kg = st % (KVT / 4), dg = st / (KVT / 4);
+        return st < VU ? (int)((4 * kg + i) * row_elems * 2) + 16 * dg : OFF_NONE;
+    };
+    // With eight waves a thread stages either K or V (one shared register
+    // array); the tile base and size are chosen arithmetically so that the
+    // wave-uniform choice needs no branch.
+    const uint64_t kmask = kstager ? ~0ull : 0ull;
+    auto load_part = [&](int i, bool kdo, int jt, bool vdo, int jv) {
+        if (NWAVE == 8) {
+            if (i < KU || !kstager) {
+                const int jk0 = jt * KVT, jv0 = jv * KVT;
+                const uint64_t kb = (uint64_t)(a.k + (rbase + jk0) * row_elems + kvh * DH);
+                const uint64_t vb = (uint64_t)(a.v + (rbase + jv0) * row_elems + kvh * DH);
+                const uint32_t ksz = kdo ? (uint32_t)((n - jk0) * row_elems * 2) : 0u;
+                const uint32_t vsz = vdo ? (uint32_t)((n - jv0) * row_elems * 2) : 0u;
+                const uint64_t base = vb + ((kb - vb) & kmask);
+                const uint32_t size = vsz + ((ksz - vsz) & (uint32_t)kmask);
+                const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                    (void*)base, (short)0, (int)size, BUFFER_RSRC_WORD3);
+                stg[i] = __builtin_amdgcn_raw_buffer_load_b128(r, kstager ? k_off(i) : v_off(i), 0, 0);
+            }
+        } else {
+            if (i < KU) kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(k_rsrc(kdo, jt), k_off(i), 0, 0);
+            vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(v_rsrc(vdo, jv), v_off(i), 0, 0);
+        }
+        if (BIAS && i == 0) {
+            const int j0 = jt * KVT;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(a.s + rbase + j0), (short)0, kdo && kstager ? (n - j0) * 4 : 0, BUFFER_RSRC_WORD3);
+            sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                rs, st < KVT ? 4 * st : OFF_NONE, 0, 0));
         }
     };
     auto store_k = [&](int buf) {
@@ -257,9 +322,16 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
                 const int row = uu / (DH / 8), c = uu % (DH / 8);
                 st16(&Ks[buf][row * KS + 8 * c], kreg[i]);
             }
-            if (BIAS && st < KVT) {
-#pragma unroll
-                for (int j = 0; j < HPB; ++j) Bs[buf][j][st] = gbias[j] * sreg;
+            if (st < KVT) {
+                uint32_t w_hi = 0u, w_lo = 0u;
+                if (BIAS) {
+                    const bf16 s_hi = to_bf16(sreg);
+                    const bf16 s_lo = to_bf16(sreg - (float)s_hi);
+                    w_hi = __builtin_bit_cast(uint32_t, bf16x2{s_hi, s_hi});
+                    w_lo = __builtin_bit_cast(uint32_t, bf16x2{s_lo, s_lo});
+                }
+                const u32x4 col = {w_hi, w_lo, 0x3F803F80u /* bf16 1, 1 */, 0u};
+                st16(&Ks[buf][st * KS + DH], col);
             }
         }
     };
@@ -288,34 +360,118 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     for (int md = 0; md < NMD; ++md)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[md][r] = 0.f;
-    float m = -INFINITY, lpart = 0.f;  // exponent base (log2 units) and this lane's row-sum half
+    // Online softmax state.  The exponentials of a tile are taken against the
+    // base its QK product subtracted (mcur at the time), whatever the tile's
+    // max turns out to be: pf is the base of the latest probabilities, O and
+    // lpart are kept against pf, and a change of pf rescales them by
+    // alpha = 2^(pf_old - pf_new).  The base only moves when a row's max
+    // exceeds it by more than RESCALE_SLACK, and then for the next tile, so
+    // the probabilities of a tile are at most 2^REBASE_LIMIT; a row past that
+    // redoes its exponentials against its new base (a rare, separate path).
+    float pf = 0.f, lpart = 0.f;       // base of O / lpart, and this lane's row-sum half
     bf16x8 pold[4];                    // probabilities of the previous tile (PV operand)
     float alpha_prev = 1.f;            // rescale of O owed before the next PV product
     bool pend = false;                 // some row of the wave owes a rescale
 
-    f32x16 sacc[2];  // S^T of one tile
+    f32x16 sacc[2];  // S^T of one tile, less the base: log2-domain logits - mcur
 
-    // S^T of tile T from its staged K.
-#define TG_QK(T)                                                                             \
+    // S^T of tile T from its staged K: the bias column first, then d_head;
+    // LD(i) issues staging load i after the MFMAs of k step i.
+#define TG_KFRAG(KK, MT)                                                                     \
+    as_bf16x8(ld16(&Ks[kb][(32 * (MT) + l32) * KS + ((KK) < 0 ? DH : (DH / 2) * hh + 8 * (KK))]))
+#define TG_QK(T, LD)                                                                         \
     do {                                                                                     \
         const int kb = (T) % NKB;                                                            \
-        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                     \
+        bf16x8 kc[2], kn[2];                                                                 \
+        _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                                   \
             _Pragma("unroll") for (int r = 0; r < 16; ++r) sacc[mt][r] = 0.f;                \
-        _Pragma("unroll") for (int kk = 0; kk < NKK; ++kk) {                                 \
-            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                               \
-                const bf16x8 kf = as_bf16x8(                                                 \
-                    ld16(&Ks[kb][(32 * mt + l32) * KS + (DH / 2) * hh + 8 * kk]));           \
-                sacc[mt] = mfma32(kf, qf[kk], sacc[mt]);                                     \
-            }                                                                                \
+            kc[mt] = TG_KFRAG(-1, mt);                                                       \
+        }                                                                                    \
+        /* K fragments are read one k step ahead; the fences keep the two */                 \
+        /* accumulators alternating. */                                                      \
+        _Pragma("unroll") for (int kk = -1; kk < NKK; ++kk) {                                \
+            if (kk + 1 < NKK) { kn[0] = TG_KFRAG(kk + 1, 0); kn[1] = TG_KFRAG(kk + 1, 1); }  \
+            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt)                                 \
+                sacc[mt] = mfma32(kc[mt], kk < 0 ? as_bf16x8(qx) : qf[kk < 0 ? 0 : kk], sacc[mt]); \
+            if (kk >= 0 && kk < 4) LD(kk);                                                   \
+            __builtin_amdgcn_sched_barrier(0);                                               \
+            kc[0] = kn[0];                                                                   \
+            kc[1] = kn[1];                                                                   \
         }                                                                                    \
     } while (0)
 
+    // Logit element c (0..31) of this lane: S^T register 4rq + e of tile mt
+    // holds key 32mt + 8rq + 4hh + e.  Probability element (kk, e) of the PV
+    // operand is S^T register 8(kk%2) + e of tile kk/2.
+#define TG_MASK_MAX(MASKED, C)                                                               \
+    do {                                                                                     \
+        const int mt_ = (C) / 16, r_ = (C) % 16;                                             \
+        float y_ = sacc[mt_][r_];                                                            \
+        if (MASKED && j0 + 32 * mt_ + 8 * (r_ / 4) + 4 * hh + (r_ % 4) > qi) y_ = -INFINITY; \
+        sacc[mt_][r_] = y_;                                                                  \
+        mx = fmaxf(mx, y_);                                                                  \
+    } while (0)
+#define TG_EXP_PAIR(X, SUB)                                                                  \
+    do {                                                                                     \
+        const int kk_ = (X) / 8, e_ = (X) % 8;                                               \
+        const float p0_ = __builtin_amdgcn_exp2f(sacc[kk_ / 2][8 * (kk_ % 2) + e_] - (SUB)); \
+        const float p1_ = __builtin_amdgcn_exp2f(sacc[kk_ / 2][8 * (kk_ % 2) + e_ + 1] - (SUB)); \
+        const bf16x2 pp_ = {to_bf16(p0_), to_bf16(p1_)};                                     \
+        pnew[kk_][e_] = pp_[0];                                                              \
+        pnew[kk_][e_ + 1] = pp_[1];                                                          \
+        psum[kk_ % 2] = __builtin_amdgcn_fdot2_f32_bf16(pp_, ONES, psum[kk_ % 2], false);    \
+    } while (0)
+
+    // After the exponentials of tile jt (against mcur): rows whose max grew
+    // past the slack move their base for the next tile; rows past the limit
+    // also redo this tile's exponentials against the new base.  Then the
+    // rescale owed by a change of base is recorded and the row sum updated.
+#define TG_SOFTMAX_TAIL()                                                                    \
+    do {                                                                                     \
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                            \
+        float pf_new = mcur;                                                                 \
+        const bool grow = mx > RESCALE_SLACK;                                                \
+        if (__any(grow)) {                                                                   \
+            const float m_old = mcur;                                                        \
+            if (grow) set_base(m_old + mx);                                                  \
+            const bool redo = mx > REBASE_LIMIT;                                             \
+            if (__any(redo)) {                                                               \
+                const float sub = redo ? mcur - m_old : 0.f;                                 \
+                psum[0] = psum[1] = 0.f;                                                     \
+                _Pragma("unroll") for (int x = 0; x < 32; x += 2) TG_EXP_PAIR(x, sub);       \
+                if (redo) pf_new = mcur;                                                     \
+            }                                                                                \
+        }                                                                                    \
+        const float alpha = __builtin_amdgcn_exp2f(pf - pf_new);                             \
+        pf = pf_new;                                                                         \
+        lpart = fmaf(lpart, alpha, psum[0] + psum[1]);                                       \
+        alpha_prev = alpha;                                                                  \
+        pend = __any(alpha != 1.f);                                                          \
+        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) pold[kk] = pnew[kk];                \
+    } while (0)
+
+    // The first tile of a wave: its row max becomes the base, and the
+    // exponentials are taken against it (nothing accumulated yet).
+#define TG_SOFTMAX_FIRST(MASKED)                                                             \
+    do {                                                                                     \
+        const int j0 = jt * KVT;                                                             \
+        float mx = -INFINITY;                                                                \
+        _Pragma("unroll") for (int c = 0; c < 32; ++c) TG_MASK_MAX(MASKED, c);               \
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                            \
+        set_base(mx);                                                                        \
+        pf = mcur;                                                                           \
+        float psum[2] = {0.f, 0.f};                                                          \
+        bf16x8 pnew[4];                                                                      \
+        _Pragma("unroll") for (int x = 0; x < 32; x += 2) TG_EXP_PAIR(x, mcur);              \
+        lpart = psum[0] + psum[1];                                                           \
+        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) pold[kk] = pnew[kk];                \
+    } while (0)
+
     // DO_S: softmax of tile jt from sacc (MASKED on the diagonal tile);
-    // DO_PV: O += V(jt-1) P(jt-1).  The exponent base of a row moves only when
-    // its max exceeds it by more than RESCALE_SLACK; the rescale of O this
-    // causes is owed until the start of the next step (TG_RESCALE), before
-    // the next PV product, so that the QK product, the PV product and the
-    // softmax form one straight run of independent MFMA and VALU work.
+    // DO_PV: O += V(jt-1) P(jt-1).  The rescale of O owed by a change of base
+    // is applied at the start of the next step (TG_RESCALE), before the next
+    // PV product, so that the QK product, the PV product and the softmax form
+    // one straight run of independent MFMA and VALU work.
 #define TG_RESCALE()                                                                         \
     do {                                                                                     \
         if (pend) {                                                                          \
@@ -323,137 +479,64 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
                 _Pragma("unroll") for (int r = 0; r < 16; ++r) o[md][r] *= alpha_prev;       \
         }                                                                                    \
     } while (0)
-#define TG_PVSM(MASKED, DO_S, DO_PV)                                                         \
+#define TG_PVSM(MASKED)                                                                      \
     do {                                                                                     \
-        if (DO_PV) {                                                                         \
-            const int vb = (jt - 1) & 1;                                                     \
-            bf16x8 v0[4];                                                                    \
-            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) v0[kk] = as_bf16x8(             \
-                ld16(&Vt[vb][l32 * VT_STRIDE + 16 * kk + 8 * hh]));                          \
-            /* QK above, then PV interleaved with the softmax below. */                      \
-            if (DO_S) __builtin_amdgcn_sched_barrier(0);                                     \
-            _Pragma("unroll") for (int md = 0; md < NMD; ++md) {                             \
-                _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                           \
-                    const bf16x8 vf = md == 0 ? v0[kk] : as_bf16x8(                          \
-                        ld16(&Vt[vb][(32 * md + l32) * VT_STRIDE + 16 * kk + 8 * hh]));      \
-                    o[md] = mfma32(vf, pold[kk], o[md]);                                     \
-                }                                                                            \
-            }                                                                                \
+        const int vb = (jt - 1) & 1;                                                         \
+        const int j0 = jt * KVT;                                                             \
+        bf16x8 v0[NMD];                                                                      \
+        _Pragma("unroll") for (int md = 0; md < NMD; ++md) v0[md] = TG_VFRAG(md);            \
+        /* QK above, then PV interleaved with the softmax below. */                          \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        _Pragma("unroll") for (int i = 0; i < NPV; ++i)                                      \
+            o[i % NMD] = mfma32(i < NMD ? v0[i] : TG_VFRAG(i), pold[i / NMD], o[i % NMD]);   \
+        float mx = -INFINITY;                                                                \
+        _Pragma("unroll") for (int c = 0; c < 32; ++c) TG_MASK_MAX(MASKED, c);               \
+        float psum[2] = {0.f, 0.f};                                                          \
+        bf16x8 pnew[4];                                                                      \
+        _Pragma("unroll") for (int x = 0; x < 32; x += 2) TG_EXP_PAIR(x, 0.f);               \
+        /* Pin the probabilities here: left alone, the compiler sinks the   */               \
+        /* exponentials below the staging stores, away from the PV MFMAs.   */               \
+        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(pnew[kk])); \
+        _Pragma("unroll") for (int i = 0; i < 4 * NMD; ++i) {                                \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                               \
+            __builtin_amdgcn_sched_group_barrier(0x002, SG_VALU, 0);                         \
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                               \
         }                                                                                    \
-        if (DO_S) {                                                                          \
-            const int bb = jt % NKB;                                                         \
-            const int j0 = jt * KVT;                                                         \
-            float mx = -INFINITY;                                                            \
-            _Pragma("unroll") for (int mt = 0; mt < 2; ++mt) {                               \
-                _Pragma("unroll") for (int rq = 0; rq < 4; ++rq) {                           \
-                    const int kl = 32 * mt + 8 * rq + 4 * hh;                                \
-                    const f32x4 sv = BIAS ? *reinterpret_cast<const f32x4*>(&Bs[bb][hp][kl]) \
-                                          : f32x4{0.f, 0.f, 0.f, 0.f};                       \
-                    _Pragma("unroll") for (int e = 0; e < 4; ++e) {                          \
-                        float x = fmaf(c1, sacc[mt][4 * rq + e], sv[e]);                     \
-                        if (MASKED && j0 + kl + e > qi) x = -INFINITY;                       \
-                        sacc[mt][4 * rq + e] = x;                                            \
-                        mx = fmaxf(mx, x);                                                   \
-                    }                                                                        \
-                }                                                                            \
-            }                                                                                \
-            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                        \
-            const bool grow = mx > m + RESCALE_SLACK;                                        \
-            const float m_new = grow ? mx : m;                                               \
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;              \
-            m = m_new;                                                                       \
-            const float mb = m == -INFINITY ? 0.f : m;                                       \
-            float psum = 0.f;                                                                \
-            bf16x8 pnew[4];                                                                  \
-            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                               \
-                _Pragma("unroll") for (int e = 0; e < 8; ++e) {                              \
-                    const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - mb); \
-                    psum += p;                                                               \
-                    pnew[kk][e] = to_bf16(p);                                                \
-                }                                                                            \
-            }                                                                                \
-            /* Pin the probabilities here: left alone, the compiler sinks the   */         \
-            /* exponentials below the staging stores, away from the PV MFMAs.   */         \
-            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(pnew[kk])); \
-            if (DO_PV) {                                                                     \
-                _Pragma("unroll") for (int i = 0; i < 4 * NMD; ++i) {                        \
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       \
-                    __builtin_amdgcn_sched_group_barrier(0x002, 256 / (4 * NMD), 0);         \
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                       \
-                }                                                                            \
-            }                                                                                \
-            lpart = fmaf(lpart, alpha, psum);                                                \
-            alpha_prev = alpha;                                                              \
-            pend = __any(grow);                                                              \
-            _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) pold[kk] = pnew[kk];            \
-        }                                                                                    \
+        TG_SOFTMAX_TAIL();                                                                   \
     } while (0)
 
-    // Softmax of tile jt and PV(jt-1) together, interleaved by hand: the
-    // first half of the PV MFMAs each go with a slice of the logits and their
-    // max, the second half each with a slice of the exponentials.  Scheduling
-    // fences keep every slice next to its MFMA; V operands are read four
-    // MFMAs ahead and bias vectors one slice ahead.
+    // Softmax of tile jt and PV(jt-1) together, interleaved by hand: each PV
+    // MFMA goes with a slice of the logits (mask and max) and of the
+    // exponentials.  Scheduling fences keep every slice next to its MFMA; V
+    // operands are read four MFMAs ahead.
     constexpr int NPV = 4 * NMD;            // PV MFMAs per tile
-    constexpr int NA = NPV / 2;             // MFMAs next to the logits
-    constexpr int CA = 8 / NA;              // logit slices (4 keys each) per MFMA
-    constexpr int EB = 32 / (NPV - NA);     // exponentials per MFMA
+    constexpr int CPM = 32 / NPV;           // logits per MFMA (even)
+    constexpr int SG_VALU = (5 * 32 / 2 + NPV - 1) / NPV;  // VALU per MFMA in the scheduling groups
 #define TG_VFRAG(I)                                                                          \
-    as_bf16x8(ld16(&Vt[vb][(32 * ((I) / 4) + l32) * VT_STRIDE + 16 * ((I) % 4) + 8 * hh]))
-#define TG_BIAS(C)                                                                           \
-    (BIAS ? *reinterpret_cast<const f32x4*>(&Bs[bb][hp][32 * ((C) / 4) + 8 * ((C) % 4) + 4 * hh]) \
-          : f32x4{0.f, 0.f, 0.f, 0.f})
+    as_bf16x8(ld16(&Vt[vb][(32 * ((I) % NMD) + l32) * VT_STRIDE + 16 * ((I) / NMD) + 8 * hh]))
 #define TG_PVSM_FUSED(MASKED)                                                                \
     do {                                                                                     \
         const int vb = (jt - 1) & 1;                                                         \
-        const int bb = jt % NKB;                                                             \
         const int j0 = jt * KVT;                                                             \
         bf16x8 vq[4];                                                                        \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) vq[i] = TG_VFRAG(i);                   \
-        f32x4 sv = TG_BIAS(0);                                                               \
         float mx = -INFINITY;                                                                \
-        __builtin_amdgcn_sched_barrier(0);                                                   \
-        _Pragma("unroll") for (int i = 0; i < NA; ++i) {                                     \
-            o[i / 4] = mfma32(vq[i % 4], pold[i % 4], o[i / 4]);                             \
-            if (i + 4 < NPV) vq[i % 4] = TG_VFRAG(i + 4);                                    \
-            _Pragma("unroll") for (int c = i * CA; c < (i + 1) * CA; ++c) {                  \
-                const f32x4 cur = sv;                                                        \
-                if (c + 1 < 8) sv = TG_BIAS(c + 1);                                          \
-                const int mt = c / 4, rq = c % 4;                                            \
-                const int kl = 32 * mt + 8 * rq + 4 * hh;                                    \
-                _Pragma("unroll") for (int e = 0; e < 4; ++e) {                              \
-                    float x = fmaf(c1, sacc[mt][4 * rq + e], cur[e]);                        \
-                    if (MASKED && j0 + kl + e > qi) x = -INFINITY;                           \
-                    sacc[mt][4 * rq + e] = x;                                                \
-                    mx = fmaxf(mx, x);                                                       \
-                }                                                                            \
-            }                                                                                \
-            __builtin_amdgcn_sched_barrier(0);                                               \
-        }                                                                                    \
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                            \
-        const bool grow = mx > m + RESCALE_SLACK;                                            \
-        const float m_new = grow ? mx : m;                                                   \
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;                  \
-        m = m_new;                                                                           \
-        const float mb = m == -INFINITY ? 0.f : m;                                           \
-        float psum = 0.f;                                                                    \
+        float psum[2] = {0.f, 0.f};                                                          \
         bf16x8 pnew[4];                                                                      \
-        _Pragma("unroll") for (int i = NA; i < NPV; ++i) {                                   \
-            o[i / 4] = mfma32(vq[i % 4], pold[i % 4], o[i / 4]);                             \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        _Pragma("unroll") for (int i = 0; i < NPV; ++i) {                                    \
+            o[i % NMD] = mfma32(vq[i % 4], pold[i / NMD], o[i % NMD]);                       \
             if (i + 4 < NPV) vq[i % 4] = TG_VFRAG(i + 4);                                    \
-            _Pragma("unroll") for (int x = (i - NA) * EB; x < (i - NA + 1) * EB; ++x) {      \
+            _Pragma("unroll") for (int x = i * CPM; x < (i + 1) * CPM; x += 2) {             \
                 const int kk = x / 8, e = x % 8;                                             \
-                const float p = __builtin_amdgcn_exp2f(sacc[kk / 2][8 * (kk % 2) + e] - mb); \
-                psum += p;                                                                   \
-                pnew[kk][e] = to_bf16(p);                                                    \
+                TG_MASK_MAX(MASKED, 16 * (kk / 2) + 8 * (kk % 2) + e);                       \
+                TG_MASK_MAX(MASKED, 16 * (kk / 2) + 8 * (kk % 2) + e + 1);                   \
+                TG_EXP_PAIR(x, 0.f);                                                         \
             }                                                                                \
             __builtin_amdgcn_sched_barrier(0);                                               \
         }                                                                                    \
         _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(pnew[kk])); \
-        lpart = fmaf(lpart, alpha, psum);                                                    \
-        alpha_prev = alpha;                                                                  \
-        pend = __any(grow);                                                                  \
-        _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) pold[kk] = pnew[kk];                \
+        TG_SOFTMAX_TAIL();                                                                   \
     } while (0)
 
     // One step of the workgroup: stage K(jt+1) and V(jt) around BODY.
@@ -463,43 +546,58 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     do {                                                  \
         const bool knext = jt + 1 < nkv;                  \
         const bool vnow = jt < nkv;                       \
-        if (knext) load_k(jt + 1);                        \
-        if (vnow) load_v(jt);                             \
         BODY;                                             \
         if (knext) store_k((jt + 1) % NKB);               \
         if (vnow) store_v(jt & 1);                        \
         __syncthreads();                                  \
         ++jt;                                             \
     } while (0)
+#define TG_LD(i) load_part((i), knext, jt + 1, vnow, jt)
+#define TG_LD_ALL() do { TG_LD(0); TG_LD(1); TG_LD(2); TG_LD(3); } while (0)
 
     // Tiles strictly before this wave's rows need no mask; the tile holding
     // the wave's first row is the diagonal one; later tiles are skipped by
     // this wave (the workgroup still stages them).
     const int jt_diag = qmin / KVT;  // <= nkv - 1
-    load_k(0);
+    load_part(0, true, 0, false, 0);
+    load_part(1, true, 0, false, 0);
+    load_part(2, true, 0, false, 0);
+    load_part(3, true, 0, false, 0);
     store_k(0);
     __syncthreads();
     if (jt_diag == 0) {
-        TG_STEP({ TG_QK(jt); TG_PVSM(true, true, false); });
+        TG_STEP({ TG_QK(jt, TG_LD); TG_SOFTMAX_FIRST(true); });
     } else {
-        TG_STEP({ TG_QK(jt); TG_PVSM(false, true, false); });
+        TG_STEP({ TG_QK(jt, TG_LD); TG_SOFTMAX_FIRST(false); });
         if (FUSED) {
-            while (jt < jt_diag) TG_STEP({ TG_RESCALE(); TG_QK(jt); TG_PVSM_FUSED(false); });
-            TG_STEP({ TG_RESCALE(); TG_QK(jt); TG_PVSM_FUSED(true); });
+            while (jt < jt_diag) TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM_FUSED(false); });
+            TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM_FUSED(true); });
         } else {
-            while (jt < jt_diag) TG_STEP({ TG_RESCALE(); TG_QK(jt); TG_PVSM(false, true, true); });
-            TG_STEP({ TG_RESCALE(); TG_QK(jt); TG_PVSM(true, true, true); });
+            while (jt < jt_diag) TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM(false); });
+            TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM(true); });
         }
     }
-    TG_STEP({ TG_RESCALE(); TG_PVSM(false, false, true); });
-    while (jt <= nkv) TG_STEP((void)0);
+    // The PV product of the last tile.
+    TG_STEP({
+        TG_LD_ALL();
+        TG_RESCALE();
+        const int vb = (jt - 1) & 1;
+        _Pragma("unroll") for (int i = 0; i < NPV; ++i) o[i % NMD] = mfma32(TG_VFRAG(i), pold[i / NMD], o[i % NMD]);
+    });
+    while (jt <= nkv) TG_STEP(TG_LD_ALL());
+#undef TG_LD_ALL
+#undef TG_LD
 #undef TG_STEP
 #undef TG_PVSM
-#undef TG_RESCALE
 #undef TG_PVSM_FUSED
+#undef TG_RESCALE
+#undef TG_SOFTMAX_FIRST
+#undef TG_SOFTMAX_TAIL
+#undef TG_EXP_PAIR
+#undef TG_MASK_MAX
 #undef TG_VFRAG
-#undef TG_BIAS
 #undef TG_QK
+#undef TG_KFRAG
 
     // ---- normalise and store ------------------------------------------------
     const float l = lpart + __shfl_xor(lpart, 32, WAVE);
@@ -516,7 +614,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
                 *reinterpret_cast<bf16x4*>(op + 32 * md + 8 * rq) = ov;
             }
         }
-        if (a.lse != nullptr && hh == 0) a.lse[(int64_t)h * a.Kt + rbase + qi] = (m + log2f(l)) * LN2;
+        if (a.lse != nullptr && hh == 0) a.lse[(int64_t)h * a.Kt + rbase + qi] = (pf + log2f(l)) * LN2;
     }
 }
 
