@@ -14,11 +14,11 @@
 //     LDS (A operand), Q fragments resident in registers (B operand), so each
 //     lane holds all scores of ONE query row and the row max / row sum need
 //     only one exchange with the partner lane half;
-//   the product lands directly in the exp2 domain with the bias added and the
-//     row's exponent base subtracted: Q is pre-scaled by temp*log2(e)/sqrt(d),
-//     and one extra k step multiplies a per-key column [s split into two bf16
-//     halves, 1] with a per-query one [gain*log2(e) split likewise, -base], so
-//     the softmax needs no per-element scale, bias or subtraction;
+//   one extra k step of the product multiplies a per-key column [s split into
+//     two bf16 halves, 1] with a per-query one [gain*log2(e)/c1 and -base/c1,
+//     each split likewise], where c1 = temp*log2(e)/sqrt(d), so that one
+//     multiply by c1 per element gives the exp2-domain logit with the bias
+//     added and the row's exponent base subtracted;
 //   O^T[dh][query] += V^T . P^T: V is stored transposed in LDS (A operand) and
 //     the probabilities, converted to bf16, are fed straight from the S
 //     registers as the B operand, again one query per lane, so the online
@@ -189,33 +189,34 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     const bool qvalid = qi < n;
 
     // ---- resident Q fragments (B operand of S^T = K Q^T) ----------------
-    // Q is scaled by c1 = temp * log2(e) / sqrt(d) on the way in, so that the
-    // MFMA yields the exp2-domain logit directly.
-    const float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
     bf16x8 qf[NKK];
     {
         const bf16* qp = a.q + ((rbase + (qvalid ? qi : 0)) * a.Hq + h) * DH + (DH / 2) * hh;
         const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            bf16x8 v = as_bf16x8(qvalid ? ld16(qp + 8 * kk) : zero);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = to_bf16((float)v[e] * c1);
-            qf[kk] = v;
-        }
+        for (int kk = 0; kk < NKK; ++kk) qf[kk] = as_bf16x8(qvalid ? ld16(qp + 8 * kk) : zero);
     }
+    // Scale of the exp2-domain logit: c1 = temp * log2(e) / sqrt(d), kept at
+    // least 2^-60 in magnitude so that it can divide (a zero temperature then
+    // contributes q.k * 2^-60, far below fp32 resolution of the bias).
+    float c1 = a.temp[h] * LOG2E / sqrtf((float)DH);
+    if (fabsf(c1) < 0x1p-60f) c1 = c1 < 0.f ? -0x1p-60f : 0x1p-60f;
+    const float inv_c1 = 1.0f / c1;
     // ---- the bias column --------------------------------------------------
     // One more k step of the same product adds the gate bias and subtracts
-    // the row's exponent base: per key, the K side holds
+    // the row's exponent base, both divided by c1, so that a single multiply
+    // by c1 turns the MFMA result into the exp2-domain logit less the base.
+    // Per key, the K side holds
     //     [s_hi, s_hi, s_lo, s_lo, 1, 1, 0, 0]      (s = s_hi + s_lo in bf16)
     // and lane half 0 of each query holds
-    //     [g_hi, g_lo, g_hi, g_lo, -m_hi, -m_lo, 0, 0]  (g = gain * log2(e))
-    // (lane half 1: zeros), so the step contributes (g_hi + g_lo)(s_hi + s_lo)
-    // - m with bf16 products that are exact in the fp32 accumulator.  The base
-    // m is kept as the value its two bf16 halves represent.
+    //     [g_hi, g_lo, g_hi, g_lo, -b_hi, -b_lo, 0, 0]
+    // with g = gain * log2(e) / c1 and b = base / c1 split likewise (lane
+    // half 1: zeros), so the step contributes (g_hi + g_lo)(s_hi + s_lo) - b
+    // with bf16 products that are exact in the fp32 accumulator.  The base is
+    // kept as c1 times the value its two bf16 halves represent.
     uint32_t qx_g = 0u;
     if (BIAS && hh == 0) {
-        const float g = a.gain[h] * LOG2E;
+        const float g = a.gain[h] * LOG2E * inv_c1;
         const bf16 g_hi = to_bf16(g);
         const bf16 g_lo = to_bf16(g - (float)g_hi);
         qx_g = __builtin_bit_cast(uint32_t, bf16x2{g_hi, g_lo});
@@ -223,9 +224,10 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     u32x4 qx = {qx_g, qx_g, 0u, 0u};
     float mcur = 0.f;  // base subtracted by the bias column in the next QK product
     auto set_base = [&](float m_new) {
-        const bf16 b_hi = to_bf16(-m_new);
-        const bf16 b_lo = to_bf16(-m_new - (float)b_hi);
-        mcur = -((float)b_hi + (float)b_lo);
+        const float nb = -m_new * inv_c1;
+        const bf16 b_hi = to_bf16(nb);
+        const bf16 b_lo = to_bf16(nb - (float)b_hi);
+        mcur = -((float)b_hi + (float)b_lo) * c1;
         qx[2] = hh == 0 ? __builtin_bit_cast(uint32_t, bf16x2{b_hi, b_lo}) : 0u;
     };
 
@@ -373,7 +375,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     float alpha_prev = 1.f;            // rescale of O owed before the next PV product
     bool pend = false;                 // some row of the wave owes a rescale
 
-    f32x16 sacc[2];  // S^T of one tile, less the base: log2-domain logits - mcur
+    f32x16 sacc[2];  // S^T of one tile: (log2-domain logits - mcur) / c1, then times c1
 
     // S^T of tile T from its staged K: the bias column first, then d_head;
     // LD(i) issues staging load i after the MFMAs of k step i.
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 #define TG_MASK_MAX(MASKED, C)                                                               \
     do {                                                                                     \
         const int mt_ = (C) / 16, r_ = (C) % 16;                                             \
-        float y_ = sacc[mt_][r_];                                                            \
+        float y_ = sacc[mt_][r_] * c1;                                                       \
         if (MASKED && j0 + 32 * mt_ + 8 * (r_ / 4) + 4 * hh + (r_ % 4) > qi) y_ = -INFINITY; \
         sacc[mt_][r_] = y_;                                                                  \
         mx = fmaxf(mx, y_);                                                                  \

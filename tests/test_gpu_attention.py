@@ -108,6 +108,58 @@ def test_attention_large_bias_range():
     assert_within(lse, ref_lse, 2e-2, 1e-2, "large bias lse")
 
 
+def _score_pattern(kind, Kt, g):
+    """Gate scores that move a row's exponent base: a step far above the
+    base (past the limit of the optimistic exponentials), a steady climb
+    (the base moves on most tiles), a first tile far below the rest, and a
+    descent (the base never moves)."""
+    j = torch.arange(Kt, dtype=torch.float32)
+    if kind == "step_up":
+        return torch.where(j % 700 >= 200, 100.0, 0.0) + torch.randn(Kt, generator=g)
+    if kind == "climb":
+        return 0.4 * (j % 700) + torch.randn(Kt, generator=g)
+    if kind == "low_first_tile":
+        return torch.where(j % 700 < 64, -400.0, 0.0) + torch.randn(Kt, generator=g)
+    if kind == "descent":
+        return -0.4 * (j % 700) + torch.randn(Kt, generator=g)
+    raise ValueError(kind)
+
+
+BASE_KINDS = ["step_up", "climb", "low_first_tile", "descent"]
+
+
+@pytest.mark.parametrize("kind", BASE_KINDS)
+def test_attention_base_moves(kind):
+    """Rows whose logits jump, climb or start far below the rest, in the
+    four-wave kernel (all rows) and the eight-wave kernel (sampled rows)."""
+    announce(f"attn base moves {kind}")
+    q, k, v, _, gain, temp, cu = _inputs([700, 130], 16, 8, 128, torch.bfloat16, seed=31)
+    s = _score_pattern(kind, cu[-1], torch.Generator().manual_seed(32))
+    out, lse = _run(q, k, v, s, gain, temp, cu)
+    ref, ref_lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    assert_within(out, ref, 2e-2, 1e-2, f"{kind} out")
+    assert_within(lse, ref_lse, 2e-2, 1e-2, f"{kind} lse")
+
+    q, k, v, _, gain, temp, cu = _inputs([8192], 16, 8, 128, torch.bfloat16, seed=33)
+    s = _score_pattern(kind, cu[-1], torch.Generator().manual_seed(34))
+    out, lse = _run(q, k, v, s, gain, temp, cu)
+    rows = _sampled_rows(cu, 24, seed=35) + [190, 200, 201, 260, 700, 900, 4000]
+    rows = sorted(set(rows))
+    ref, ref_lse = oracle.gated_attention_rows(q, k, v, s, gain, temp, cu, rows)
+    assert_within(out[rows], ref, 2e-2, 1e-2, f"{kind} eight-wave out")
+    assert_within(lse[:, rows], ref_lse, 2e-2, 1e-2, f"{kind} eight-wave lse")
+
+
+def test_attention_high_temperature():
+    """Temperatures of 6-10: the QK part alone spans tens of log2 units."""
+    q, k, v, s, gain, temp, cu = _inputs([600], 16, 8, 128, torch.bfloat16, seed=36)
+    temp = temp * 8.0
+    out, lse = _run(q, k, v, s, gain, temp, cu)
+    ref, ref_lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    assert_within(out, ref, 2e-2, 1e-2, "high temperature out")
+    assert_within(lse, ref_lse, 2e-2, 1e-2, "high temperature lse")
+
+
 def test_attention_deterministic():
     q, k, v, s, gain, temp, cu = _inputs([1000, 24], 16, 8, 128, torch.bfloat16, seed=23)
     a, _ = _run(q, k, v, s, gain, temp, cu)
