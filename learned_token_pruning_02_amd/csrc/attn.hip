@@ -122,6 +122,31 @@ __device__ __forceinline__ int tiles_at_or_above(const AttnArgs& a, int t) {
     return c;
 }
 
+// Request b and query tile t of the u-th workgroup (per head group): tiles
+// with more keys first, so that the heaviest work starts earliest.
+__device__ __forceinline__ bool locate_tile(const AttnArgs& a, int u, int& b, int& t) {
+    if (a.batch == 1) {
+        b = 0;
+        t = a.ntiles[0] - 1 - u;
+        return true;
+    }
+    int lo = 0, hi = a.max_tiles - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) / 2;
+        if (tiles_at_or_above(a, mid) > u) lo = mid;
+        else hi = mid - 1;
+    }
+    t = lo;
+    int j = u - tiles_at_or_above(a, t + 1);
+    for (b = 0; b < a.batch; ++b) {
+        if (a.ntiles[b] > t) {
+            if (j == 0) break;
+            --j;
+        }
+    }
+    return b < a.batch;  // false only for an inconsistent tile count
+}
+
 template <int DH, int HPB, int NWAVE, bool BIAS>
 __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnArgs a) {
     // NWAVE = 8: two waves per SIMD from one workgroup; 4: two workgroups per CU.
@@ -153,28 +178,8 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 
     // ---- which (request, query tile, head group) this workgroup owns ------
     const int hg = blockIdx.x % a.n_hg;
-    const int u = blockIdx.x / a.n_hg;
     int b, t;
-    if (a.batch == 1) {
-        b = 0;
-        t = a.ntiles[0] - 1 - u;
-    } else {
-        int lo = 0, hi = a.max_tiles - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            if (tiles_at_or_above(a, mid) > u) lo = mid;
-            else hi = mid - 1;
-        }
-        t = lo;
-        int j = u - tiles_at_or_above(a, t + 1);
-        for (b = 0; b < a.batch; ++b) {
-            if (a.ntiles[b] > t) {
-                if (j == 0) break;
-                --j;
-            }
-        }
-        if (b >= a.batch) return;  // unreachable for a consistent tile count
-    }
+    if (!locate_tile(a, (int)(blockIdx.x / a.n_hg), b, t)) return;
     const int64_t rbase = a.cu[b];
     const int n = a.cu[b + 1] - a.cu[b];
     const int q0 = t * BQ;
