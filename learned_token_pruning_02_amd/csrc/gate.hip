@@ -63,8 +63,8 @@ constexpr int GK = 64;   // k chunk
 constexpr int RING = 3;  // residual fragment sets per wave (two chunks in flight)
 constexpr int RED_STRIDE = 36;  // floats per row of the unit-sum tile (16-byte aligned, skewed banks)
 
-template <int DG, int WAVES, int MT>
-__global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
+template <int DG, int WAVES, int MT, int OCC>
+__global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
     const bf16* __restrict__ hidden, int64_t T, int d, const bf16* __restrict__ w1,
     const bf16* __restrict__ b1, const bf16* __restrict__ w2, const bf16* __restrict__ b2,
     float* __restrict__ scores) {
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     constexpr int THREADS = 64 * WAVES;
     constexpr int WUNITS = NFRAG * WAVE / THREADS;
     constexpr int R = THREADS / 8;
-    static_assert(32 % R == 0, "rows per staging round");
+    static_assert(32 % R == 0 || R % 32 == 0, "rows per staging round");
     const int r0 = threadIdx.x / 8, c0 = threadIdx.x % 8;
     const bf16* wbase = w1 + (int64_t)r0 * d + 8 * c0;
     const int wkk = c0 % 4, whq = c0 / 4;
@@ -176,7 +176,10 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
             _Pragma("unroll") for (int mt = 0; mt < MT; ++mt)                                \
                 acc[mt][nt] = mfma32(as_bf16x8(cur[mt][kk]), b[nt], acc[mt][nt]);            \
     } while (0)
-    bf16x8 bA[NT], bB[NT];
+    // Two waves per SIMD (two workgroups, or eight waves) leave no room for
+    // a whole slice of B fragments.
+    constexpr bool STREAM = WAVES * OCC >= 8;
+    bf16x8 bA[STREAM ? 1 : NT], bB[STREAM ? 1 : NT];
 
     // One k chunk: the B fragments of slices 0 and 1 are read from LDS; W1 of
     // the next chunk is requested between slice 0's MFMAs and the residual
@@ -188,6 +191,35 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     // never used.
 #define TG_LW(li) TG_LOAD_W1(min(s_ + 1, nsteps - 1), li)
 #define TG_LA(li) TG_LOAD_A1(ahead_, min(s_ + 2, nsteps - 1), li)
+    // Two workgroups per CU (OCC = 2) leave no room for a whole slice of B
+    // fragments: they are read PD MFMAs ahead, one at a time, with W1 loads
+    // spread over slice 0 and residual loads over slice 1.
+    constexpr int PD = 4;
+#define TG_BFRAG(buf, i) as_bf16x8(wl[buf][(((i) % NT) * 4 + (i) / NT) * WAVE + rd_pos[(i) / NT]])
+#define TG_STEP_STREAM(s, cur, ahead)                                                        \
+    do {                                                                                     \
+        const int s_ = (s);                                                                  \
+        auto& ahead_ = ahead;                                                                \
+        const int buf_ = s_ & 1;                                                             \
+        bf16x8 bq[PD];                                                                       \
+        _Pragma("unroll") for (int i = 0; i < PD; ++i) bq[i] = TG_BFRAG(buf_, i);            \
+        __builtin_amdgcn_sched_barrier(0);                                                   \
+        _Pragma("unroll") for (int i = 0; i < 4 * NT; ++i) {                                 \
+            const int kk = i / NT, nt = i % NT;                                              \
+            acc[0][nt] = mfma32(as_bf16x8(cur[0][kk]), bq[i % PD], acc[0][nt]);              \
+            if (i + PD < 4 * NT) bq[i % PD] = TG_BFRAG(buf_, i + PD);                        \
+            if (kk == 0) {                                                                   \
+                _Pragma("unroll") for (int li = nt * WUNITS / NT; li < (nt + 1) * WUNITS / NT; ++li) \
+                    TG_LW(li);                                                               \
+            } else if (kk == 1) {                                                            \
+                _Pragma("unroll") for (int li = nt * 4 / NT; li < (nt + 1) * 4 / NT; ++li)   \
+                    TG_LA(li);                                                               \
+            }                                                                                \
+            __builtin_amdgcn_sched_barrier(0);                                               \
+        }                                                                                    \
+        TG_STORE_W(buf_ ^ 1);                                                                \
+        __syncthreads();                                                                     \
+    } while (0)
 #define TG_STEP(s, cur, ahead)                                                               \
     do {                                                                                     \
         const int s_ = (s);                                                                  \
@@ -215,16 +247,31 @@ __global__ __launch_bounds__(64 * WAVES, 1) void gate_bf16_kernel(
     TG_STORE_W(0);
     __syncthreads();
     const int groups = nsteps / RING;
-    for (int g = 0; g < groups; ++g) {
-        const int s = g * RING;
-        TG_STEP(s, a0, a2);
-        TG_STEP(s + 1, a1, a0);
-        TG_STEP(s + 2, a2, a1);
+    if constexpr (STREAM) {
+        static_assert(MT == 1, "two waves per SIMD use 32-token waves");
+        for (int g = 0; g < groups; ++g) {
+            const int s = g * RING;
+            TG_STEP_STREAM(s, a0, a2);
+            TG_STEP_STREAM(s + 1, a1, a0);
+            TG_STEP_STREAM(s + 2, a2, a1);
+        }
+        const int rest = nsteps - groups * RING;
+        if (rest > 0) TG_STEP_STREAM(groups * RING, a0, a2);
+        if (rest > 1) TG_STEP_STREAM(groups * RING + 1, a1, a0);
+    } else {
+        for (int g = 0; g < groups; ++g) {
+            const int s = g * RING;
+            TG_STEP(s, a0, a2);
+            TG_STEP(s + 1, a1, a0);
+            TG_STEP(s + 2, a2, a1);
+        }
+        const int rest = nsteps - groups * RING;
+        if (rest > 0) TG_STEP(groups * RING, a0, a2);
+        if (rest > 1) TG_STEP(groups * RING + 1, a1, a0);
     }
-    const int rest = nsteps - groups * RING;
-    if (rest > 0) TG_STEP(groups * RING, a0, a2);
-    if (rest > 1) TG_STEP(groups * RING + 1, a1, a0);
 #undef TG_STEP
+#undef TG_STEP_STREAM
+#undef TG_BFRAG
 #undef TG_LW
 #undef TG_LA
 #undef TG_MMA
@@ -278,21 +325,22 @@ template <int DG>
 hipError_t launch_gate_bf16_dg(const bf16* hidden, int64_t T, int d, const bf16* w1,
                                const bf16* b1, const bf16* w2, const bf16* b2, float* scores,
                                hipStream_t st) {
-    // Largest token tile that still gives at least one workgroup per CU:
-    // fewer, larger workgroups read each W1 chunk for more tokens.  Below
-    // that, 32-token waves (MT = 1) double the waves for the same tile.  (One
-    // wave with d_gate 256 would need 128 registers of W1 staging: not used.)
     if (T >= 256 * 256) {
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 2>), dim3((T + 255) / 256), dim3(256), 0, st,
+        // Largest token tile that still gives at least one workgroup per CU:
+        // fewer, larger workgroups read each W1 chunk for more tokens.
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 2, 1>), dim3((T + 255) / 256), dim3(256), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
-    } else if (DG == 256) {
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 1>), dim3((T + 127) / 128), dim3(256), 0, st,
+    } else if constexpr (DG == 256) {
+        // Below that, 128-token workgroups of 32-token waves, two per CU:
+        // more waves, and one workgroup's GELU epilogue overlaps the other's
+        // MFMAs and loads.
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 1, 2>), dim3((T + 127) / 128), dim3(256), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
     } else if (T >= 128 * 512) {
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 2, 2>), dim3((T + 127) / 128), dim3(128), 0, st,
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 2, 2, 1>), dim3((T + 127) / 128), dim3(128), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
-    } else if constexpr (DG != 256) {
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 1, 2>), dim3((T + 63) / 64), dim3(64), 0, st,
+    } else {
+        hipLaunchKernelGGL((gate_bf16_kernel<DG, 1, 2, 1>), dim3((T + 63) / 64), dim3(64), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
     }
     return hipGetLastError();
