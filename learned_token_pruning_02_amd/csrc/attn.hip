@@ -566,6 +566,10 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     // the wave's first row is the diagonal one; later tiles are skipped by
     // this wave (the workgroup still stages them).
     const int jt_diag = qmin / KVT;  // <= nkv - 1
+    // Waves 4-7 share each SIMD with one of waves 0-3, which the hardware
+    // favours when both can issue; raising their priority evens out the
+    // two waves' step times, so neither idles long at the barrier.
+    if (NWAVE == 8 && w >= 4) __builtin_amdgcn_s_setprio(2);
     load_part(0, true, 0, false, 0);
     load_part(1, true, 0, false, 0);
     load_part(2, true, 0, false, 0);
