@@ -18,11 +18,13 @@
 //      request's histogram with global atomics; the chunk that finishes last
 //      (atomic ticket, no waiting) finds the bucket d1 holding the K_doc-th
 //      best key;
-//   3. per chunk, count the keys above d1 and append the keys in d1 with their
-//      index; the last chunk ranks those candidates exactly by an LDS radix
-//      select over the 52-bit composite (low 21 key bits, then reversed index),
-//      which turns (key desc, index asc) into a single descending order, then
-//      counts the kept tokens of every chunk and scans them into output offsets;
+//   3. per chunk, count the keys above d1, append the keys in d1 with their
+//      index and histogram their next 11 key bits; the last chunk picks the
+//      first digit from that histogram and ranks the candidates sharing it
+//      exactly by an LDS radix select over the 52-bit composite (low 21 key
+//      bits, then reversed index), which turns (key desc, index asc) into a
+//      single descending order, then counts the kept tokens of every chunk and
+//      scans them into output offsets;
 //   4. per chunk, re-derive each key's keep flag from (d1, composite prefix)
 //      and write the kept ids in index order (wave ballots + a small count
 //      table per workgroup), and the question tail after them.
@@ -109,7 +111,7 @@ struct SelArgs {
     uint32_t* meta;       // [B][META]: d1, rem1, cnt1, cprefix lo/hi, cmask lo/hi, done
     uint32_t* ctr;        // [B][CTR]: hist ticket, candidate ticket, candidate count,
                           //           rank-pass tickets [4, 4+NPASS), count ticket 4+NPASS
-    uint32_t* rank_hist;  // [B][NPASS][NBIN] (many-workgroup ranking only)
+    uint32_t* rank_hist;  // [B][NPASS][NBIN]: first-digit histogram ([b][0]), and every pass of the many-workgroup ranking
     uint32_t* chunk_kept; // [doc chunks]: kept candidates per chunk (many-workgroup ranking only)
     int32_t big;          // rank candidates with every workgroup (some document > BIG_DOC)
     uint32_t* chunk_def;  // [doc chunks]: keys above d1
@@ -272,6 +274,22 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         const int i = c * SCHUNK + it * SB + tid;
         if (i < ndoc && (kv[it] >> 21) == d1) coherent_store2(&cand[pos++], make_uint2(kv[it], (uint32_t)i));
     }
+    if (!a.big && tot_cand != 0u) {
+        // The first ranking digit of the candidates (key bits 10-20) is
+        // histogrammed here by every chunk, so that the last chunk starts
+        // from the request's histogram instead of a pass over all of them.
+        for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) {
+            const int i = c * SCHUNK + it * SB + tid;
+            if (i < ndoc && (kv[it] >> 21) == d1) atomicAdd(&h[(kv[it] >> 10) & (NBIN - 1)], 1u);
+        }
+        __syncthreads();
+        uint32_t* gh0 = a.rank_hist + (size_t)b * NPASS * NBIN;
+        for (int i = tid; i < NBIN; i += SB)
+            if (h[i] != 0u) atomicAdd(&gh0[i], h[i]);
+    }
     wait_own_writes();
     __syncthreads();
     if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 1], 1u) == (uint32_t)(nck - 1);
@@ -288,25 +306,42 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     }
 
     // ---- the last chunk: exact rank inside bucket d1 ----------------------
-    // Candidates are staged once into LDS when they fit (the usual case: a
-    // bucket holds a few thousand keys); a degenerate bucket (heavy ties) is
-    // read from global memory on every pass instead.
+    // The first digit comes from the histogram the chunks built; only the
+    // candidates sharing it (usually a handful) go on, staged in LDS when
+    // they fit (a degenerate bucket of heavy ties is read from global memory
+    // on every pass instead), through the remaining radix passes.
     const uint32_t cnt1 = m[2];
-    const bool in_lds = cnt1 <= CAND_LDS;
-    if (in_lds)
-        for (uint32_t j = tid; j < cnt1; j += SB) cl[j] = coherent_load2(&cand[j]);
-    __syncthreads();
-    auto cand_at = [&](uint32_t j) { return in_lds ? cl[j] : coherent_load2(&cand[j]); };
     uint32_t rem = m[1];
     uint64_t cprefix = 0, cmask = 0;
+    {
+        const uint32_t* gh0 = a.rank_hist + (size_t)b * NPASS * NBIN;
+        find_bin([&](int i) { return coherent_load(&gh0[i]); }, NBIN, rem, wtot, &sh_d, &sh_gt,
+                 &sh_cnt);
+        rem -= sh_gt;
+        cprefix = (uint64_t)sh_d << pass_shift(0);
+        cmask = (uint64_t)(NBIN - 1) << pass_shift(0);
+    }
+    const uint32_t cnt0 = sh_cnt;  // candidates sharing the first digit
+    const bool in_lds = cnt0 <= CAND_LDS;
+    if (tid == 0) sh_total = 0u;
+    __syncthreads();
+    if (cnt0 != rem && in_lds) {
+        for (uint32_t j = tid; j < cnt1; j += SB) {
+            const uint2 e = coherent_load2(&cand[j]);
+            if ((composite(e.x, e.y) & cmask) == cprefix) cl[atomicAdd(&sh_total, 1u)] = e;
+        }
+    }
+    __syncthreads();
+    const uint32_t nlist = in_lds ? cnt0 : cnt1;
+    auto cand_at = [&](uint32_t j) { return in_lds ? cl[j] : coherent_load2(&cand[j]); };
 #pragma unroll 1
-    for (int p = 0; p < NPASS; ++p) {
+    for (int p = 1; p < NPASS && cnt0 != rem; ++p) {
         const int sh = pass_shift(p);
         const int wd = pass_width(p);
         const int nb = 1 << wd;
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
         __syncthreads();
-        for (uint32_t j = tid; j < cnt1; j += SB) {
+        for (uint32_t j = tid; j < nlist; j += SB) {
             const uint2 e = cand_at(j);
             const uint64_t cp = composite(e.x, e.y);
             if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
@@ -330,7 +365,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
         __syncthreads();
         for (uint32_t j = tid; j < cnt1; j += SB) {
-            const uint2 e = cand_at(j);
+            const uint2 e = coherent_load2(&cand[j]);
             const int ch = (int)(e.y / SCHUNK) - c0;
             if (ch >= 0 && ch < NBIN && (composite(e.x, e.y) & cmask) >= cprefix)
                 atomicAdd(&ccnt[ch], 1u);
@@ -617,7 +652,7 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
             s.big = 1;
     if (dc > 0) {
         const int n_hist = a.batch * NBIN, n_ctr = a.batch * CTR;
-        const int n_rank = s.big ? a.batch * NPASS * NBIN : 0, n_kept = s.big ? dc : 0;
+        const int n_rank = a.batch * NPASS * NBIN, n_kept = s.big ? dc : 0;
         const int n_clear = std::max(std::max(n_hist, n_ctr), std::max(n_rank, n_kept));
         hipLaunchKernelGGL(sel_clear_kernel, dim3((n_clear + SB - 1) / SB), dim3(SB), 0, st, s.hist,
                            s.ctr, n_hist, n_ctr, s.rank_hist, n_rank, s.chunk_kept, n_kept);
