@@ -80,10 +80,11 @@ def test_gate_constant_when_w1_zero_all_ties():
 
 
 # --------------------------------------------------------------- select ----
-def _brute_sorted(scores, seq_len, q_len, budget):
+def _brute_sorted(scores, seq_len, q_len, budget, prefix_len=None):
     """Kept ids by a full Python sort with an explicit comparison key."""
     out, lo = [], 0
-    for n, q, k in zip(seq_len, q_len, budget):
+    prefix_len = prefix_len or [0] * len(seq_len)
+    for n, q, k, p in zip(seq_len, q_len, budget, prefix_len):
         keep = min(k, n)
         if keep >= n:
             ids = list(range(n))
@@ -93,14 +94,14 @@ def _brute_sorted(scores, seq_len, q_len, budget):
                 if math.isnan(v):
                     return (1, 0.0, i)
                 return (0, -(v + 0.0), i)
-            doc = sorted(range(n - q), key=key)[: keep - q]
-            ids = sorted(doc + list(range(n - q, n)))
+            doc = sorted(range(p, n - q), key=key)[: keep - q - p]
+            ids = sorted(list(range(p)) + doc + list(range(n - q, n)))
         out += [lo + i for i in ids]
         lo += n
     return out
 
 
-def _brute_rank(scores, seq_len, q_len, budget):
+def _brute_rank(scores, seq_len, q_len, budget, prefix_len=None):
     """Kept ids by counting, for every document token, how many beat it."""
     def beats(a, ia, b, ib):            # does (a, ia) come before (b, ib)?
         na, nb = math.isnan(a), math.isnan(b)
@@ -111,15 +112,16 @@ def _brute_rank(scores, seq_len, q_len, budget):
         return ia < ib
 
     out, lo = [], 0
-    for n, q, k in zip(seq_len, q_len, budget):
+    prefix_len = prefix_len or [0] * len(seq_len)
+    for n, q, k, p in zip(seq_len, q_len, budget, prefix_len):
         keep = min(k, n)
         for i in range(n):
-            if keep >= n or i >= n - q:
+            if keep >= n or i >= n - q or i < p:
                 out.append(lo + i)
                 continue
             vi = float(scores[lo + i])
-            rank = sum(beats(float(scores[lo + j]), j, vi, i) for j in range(n - q) if j != i)
-            if rank < keep - q:
+            rank = sum(beats(float(scores[lo + j]), j, vi, i) for j in range(p, n - q) if j != i)
+            if rank < keep - q - p:
                 out.append(lo + i)
         lo += n
     return out
@@ -176,6 +178,48 @@ def test_select_invariants(vals, q, budget):
         for j in drop_doc:
             ki, kj = key(i), key(j)
             assert ki[0] > kj[0] or (ki[0] == kj[0] and (ki[1] > kj[1] or (ki[1] == kj[1] and i < j)))
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_select_with_template_prefix_matches_brute_force(case):
+    """Always-kept template prefix in front of the document span."""
+    g = torch.Generator().manual_seed(300 + case)
+    B = 1 + case % 3
+    seq_len = torch.randint(1, 60, (B,), generator=g).tolist()
+    q_len, p_len, budget = [], [], []
+    for n in seq_len:
+        q = int(torch.randint(0, n + 1, (1,), generator=g))
+        p = int(torch.randint(0, n - q + 1, (1,), generator=g))
+        q_len.append(q)
+        p_len.append(p)
+        budget.append(max(1, p + q + int(torch.randint(0, n + 3, (1,), generator=g))))
+    T = sum(seq_len)
+    if case % 2:
+        s = (torch.randint(0, 5, (T,), generator=g).float() - 2.0) / 2.0   # heavy ties
+    else:
+        s = torch.randn(T, generator=g)
+    if case % 4 == 3:
+        pos = torch.randint(0, T, (min(T, 8),), generator=g)
+        for j, p in enumerate(pos.tolist()):
+            s[p] = SPECIALS[(j + case) % len(SPECIALS)]
+    kept, cu = oracle.topk_select(s, seq_len, q_len, budget, p_len)
+    assert kept.tolist() == _brute_sorted(s, seq_len, q_len, budget, p_len)
+    assert kept.tolist() == _brute_rank(s, seq_len, q_len, budget, p_len)
+    assert cu[-1] == len(kept)
+
+
+def test_select_prefix_special_cases():
+    s = torch.randn(50)
+    kept, _ = oracle.topk_select(s, [50], [10], [25], [15])    # budget == prefix + tail
+    assert kept.tolist() == list(range(15)) + list(range(40, 50))
+    kept, _ = oracle.topk_select(s, [50], [10], [20], [0])     # prefix 0: the plain selector
+    assert kept.tolist() == oracle.topk_select(s, [50], [10], [20])[0].tolist()
+    kept, _ = oracle.topk_select(torch.full((50,), 0.75), [50], [5], [12], [3])   # all ties
+    assert kept.tolist() == list(range(7)) + list(range(45, 50))
+    with pytest.raises(ValueError):
+        oracle.topk_select(s, [50], [10], [24], [15])          # budget below prefix + tail
+    with pytest.raises(ValueError):
+        oracle.topk_select(s, [50], [10], [30], [-1])
 
 
 def test_select_special_budgets():
