@@ -143,6 +143,47 @@ tg_status tg_topk_select(const float *scores, const tg_batch *b, int32_t *kept_i
                          int32_t *cu_kept_dev, void *ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/* A packed batch whose requests also start with a template prefix that is
+ * never pruned (spke.com page, "Comment déployer TokenGate ?": a placeholder
+ * in the prompt template marks the document that may be pruned; the template
+ * text around it stays).  Request b is [prefix | document | question]:
+ * prefix_len[b] leading tokens and q_len[b] trailing tokens are always kept,
+ * the document is the span between them.  prefix_len is host memory of length
+ * `batch`, or NULL for no prefix (then this is tg_batch). */
+typedef struct {
+    int32_t batch;
+    const int32_t *seq_len;
+    const int32_t *q_len;
+    const int32_t *budget;
+    const int32_t *prefix_len;
+} tg_batch_prefix;
+
+/*
+ * tg_plan_prefix -- tg_plan for a tg_batch_prefix.  A request must also have
+ * prefix_len[b] >= 0 and prefix_len[b] + q_len[b] <= min(budget[b],
+ * seq_len[b]), else TG_ERR_BAD_BUDGET.
+ */
+tg_status tg_plan_prefix(const tg_batch_prefix *b, int32_t *cu_seqlens, int32_t *cu_kept,
+                         size_t *topk_ws_bytes);
+
+/*
+ * tg_topk_select_prefix -- tg_topk_select for a tg_batch_prefix: when the
+ * budget does not cover the request, the K_b - p_b - q_b best document tokens
+ * (same order as tg_topk_select, document span [p_b, N_b - q_b)) are kept with
+ * the whole prefix and the whole question; kept ids ascend within a request.
+ * The workspace size comes from tg_plan_prefix.  Errors: those of
+ * tg_plan_prefix and of tg_topk_select.
+ *
+ * Random-K selection (same page, benchmarks: even a random choice of K
+ * tokens scores well on the co-adapted backbone) is this selector, or
+ * tg_topk_select, run on random keys in place of the gate scores: the caller
+ * draws them (the library draws no random numbers) and passes them as
+ * `scores`; ties go to the lower index as always.
+ */
+tg_status tg_topk_select_prefix(const float *scores, const tg_batch_prefix *b, int32_t *kept_idx,
+                                int32_t *cu_kept_dev, void *ws, size_t ws_bytes,
+                                hipStream_t stream);
+
 /*
  * tg_gather_compact -- compaction (spke.com page, third bullet: layers above L
  * process only the kept tokens).

@@ -64,6 +64,16 @@ class _Batch(ctypes.Structure):
     ]
 
 
+class _BatchPrefix(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seq_len", ctypes.POINTER(ctypes.c_int32)),
+        ("q_len", ctypes.POINTER(ctypes.c_int32)),
+        ("budget", ctypes.POINTER(ctypes.c_int32)),
+        ("prefix_len", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
 _lib = None
 
 
@@ -93,6 +103,10 @@ def lib() -> ctypes.CDLL:
     L.tg_gate_score.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp, vp, vp, i32, vp, vp]
     L.tg_topk_select.restype = ctypes.c_int
     L.tg_topk_select.argtypes = [vp, ctypes.POINTER(_Batch), vp, vp, vp, sz, vp]
+    L.tg_plan_prefix.restype = ctypes.c_int
+    L.tg_plan_prefix.argtypes = [ctypes.POINTER(_BatchPrefix), p_i32, p_i32, ctypes.POINTER(sz)]
+    L.tg_topk_select_prefix.restype = ctypes.c_int
+    L.tg_topk_select_prefix.argtypes = [vp, ctypes.POINTER(_BatchPrefix), vp, vp, vp, sz, vp]
     L.tg_gather_compact.restype = ctypes.c_int
     L.tg_gather_compact.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp, i64, vp, vp, vp]
     L.tg_gated_attn_prefill.restype = ctypes.c_int
@@ -149,28 +163,33 @@ def _i32_array(vals: Sequence[int]):
     return arr
 
 
-def _batch(seq_len, q_len, budget):
+def _batch(seq_len, q_len, budget, prefix_len=None):
+    """tg_batch (prefix_len None) or tg_batch_prefix, and the arrays it points to."""
     n = len(seq_len)
-    if not (len(q_len) == len(budget) == n):
-        raise ValueError("seq_len, q_len and budget must have the same length")
+    if not (len(q_len) == len(budget) == n) or (prefix_len is not None and len(prefix_len) != n):
+        raise ValueError("seq_len, q_len, budget (and prefix_len) must have the same length")
     s, q, b = _i32_array(seq_len), _i32_array(q_len), _i32_array(budget)
-    bt = _Batch(n, ctypes.cast(s, ctypes.POINTER(ctypes.c_int32)),
-                ctypes.cast(q, ctypes.POINTER(ctypes.c_int32)),
-                ctypes.cast(b, ctypes.POINTER(ctypes.c_int32)))
-    return bt, (s, q, b)
+    ptr = lambda a: ctypes.cast(a, ctypes.POINTER(ctypes.c_int32))
+    if prefix_len is None:
+        return _Batch(n, ptr(s), ptr(q), ptr(b)), (s, q, b)
+    p = _i32_array(prefix_len)
+    return _BatchPrefix(n, ptr(s), ptr(q), ptr(b), ptr(p)), (s, q, b, p)
 
 
 # ----------------------------------------------------------------- API ----
-def tg_plan(seq_len: Sequence[int], q_len: Sequence[int], budget: Sequence[int]
-            ) -> Tuple[List[int], List[int], int]:
-    """Host-only plan: (cu_seqlens, cu_kept, select workspace bytes)."""
+def tg_plan(seq_len: Sequence[int], q_len: Sequence[int], budget: Sequence[int],
+            prefix_len: Optional[Sequence[int]] = None) -> Tuple[List[int], List[int], int]:
+    """Host-only plan: (cu_seqlens, cu_kept, select workspace bytes).  With
+    prefix_len, each request also keeps that many leading template tokens
+    (tg_plan_prefix)."""
     L = lib()
-    bt, keep = _batch(seq_len, q_len, budget)
+    bt, keep = _batch(seq_len, q_len, budget, prefix_len)
     n = len(seq_len)
     cu_s = (ctypes.c_int32 * (n + 1))()
     cu_k = (ctypes.c_int32 * (n + 1))()
     ws = ctypes.c_size_t(0)
-    _check("tg_plan", L.tg_plan(ctypes.byref(bt), cu_s, cu_k, ctypes.byref(ws)))
+    fn, name = (L.tg_plan, "tg_plan") if prefix_len is None else (L.tg_plan_prefix, "tg_plan_prefix")
+    _check(name, fn(ctypes.byref(bt), cu_s, cu_k, ctypes.byref(ws)))
     return list(cu_s), list(cu_k), int(ws.value)
 
 
@@ -190,16 +209,21 @@ def tg_gate_score(hidden, w1, b1, w2, b2, scores=None, stream=None):
 
 
 def tg_topk_select(scores, seq_len: Sequence[int], q_len: Sequence[int], budget: Sequence[int],
-                   kept_idx=None, cu_kept_dev=None, workspace=None, stream=None):
-    """Kept global token ids (int32, ascending per request) and the host cu_kept list."""
+                   kept_idx=None, cu_kept_dev=None, workspace=None, stream=None, prefix_len=None):
+    """Kept global token ids (int32, ascending per request) and the host cu_kept list.
+    With prefix_len, each request also keeps that many leading template tokens
+    and selects from the span between them and the question
+    (tg_topk_select_prefix).  Random-K selection is this call on random keys
+    drawn by the caller in place of the scores."""
     torch = _torch()
-    cu_s, cu_k, ws_bytes = tg_plan(seq_len, q_len, budget)
+    cu_s, cu_k, ws_bytes = tg_plan(seq_len, q_len, budget, prefix_len)
     if kept_idx is None:
         kept_idx = torch.empty(cu_k[-1], dtype=torch.int32, device=scores.device)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
-    bt, keep = _batch(seq_len, q_len, budget)
-    _check("tg_topk_select", lib().tg_topk_select(
+    bt, keep = _batch(seq_len, q_len, budget, prefix_len)
+    fn = lib().tg_topk_select if prefix_len is None else lib().tg_topk_select_prefix
+    _check("tg_topk_select" if prefix_len is None else "tg_topk_select_prefix", fn(
         _dev(scores, "scores", torch.float32), ctypes.byref(bt),
         _dev(kept_idx, "kept_idx", torch.int32), _dev(cu_kept_dev, "cu_kept_dev", torch.int32),
         _dev(workspace, "workspace"), ws_bytes if workspace is None else workspace.numel(),

@@ -102,6 +102,7 @@ struct SelArgs {
     int32_t off[TG_MAX_BATCH + 1];        // token offset of each request
     int32_t out[TG_MAX_BATCH + 1];        // kept-row offset of each request
     int32_t q[TG_MAX_BATCH];              // question tail
+    int32_t p[TG_MAX_BATCH];              // template prefix (kept); the document is [p, N - q)
     int32_t doc_chunk0[TG_MAX_BATCH + 1]; // first document chunk (selecting requests only)
     int32_t all_chunk0[TG_MAX_BATCH + 1]; // first chunk over the whole request
     const float* scores;
@@ -195,9 +196,9 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
     const int c = blockIdx.x - a.doc_chunk0[b];
     const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
     const int N = a.off[b + 1] - a.off[b];
-    const int ndoc = N - a.q[b];
-    const int kdoc = a.out[b + 1] - a.out[b] - a.q[b];
-    const float* s = a.scores + a.off[b];
+    const int ndoc = N - a.q[b] - a.p[b];
+    const int kdoc = a.out[b + 1] - a.out[b] - a.q[b] - a.p[b];
+    const float* s = a.scores + a.off[b] + a.p[b];  // document tokens, indexed from 0
 
     for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
     __syncthreads();
@@ -242,8 +243,8 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     const int c = blockIdx.x - a.doc_chunk0[b];
     const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
     const int N = a.off[b + 1] - a.off[b];
-    const int ndoc = N - a.q[b];
-    const float* s = a.scores + a.off[b];
+    const int ndoc = N - a.q[b] - a.p[b];
+    const float* s = a.scores + a.off[b] + a.p[b];  // document tokens, indexed from 0
     uint32_t* m = a.meta + b * META;
     const uint32_t d1 = m[0];
     uint2* cand = a.cand + a.off[b];
@@ -515,6 +516,7 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     const int off = a.off[b];
     const int N = a.off[b + 1] - off;
     const int q = a.q[b];
+    const int pf = a.p[b];
     const int out = a.out[b];
     const int keep = a.out[b + 1] - out;
     const int lo = c * SCHUNK;
@@ -523,9 +525,17 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
         for (int i = lo + tid; i < hi; i += SB) a.kept[out + i] = off + i;
         return;
     }
-    const int ndoc = N - q;
-    const int kdoc = keep - q;
-    for (int i = max(lo, ndoc) + tid; i < hi; i += SB) a.kept[out + kdoc + (i - ndoc)] = off + i;
+    const int ndoc = N - q - pf;
+    const int kdoc = keep - q - pf;
+    // The always-kept tokens, prefix then question, as one list of pf + q <= N
+    // entries shared out by chunk: prefix token f goes to output f, question
+    // token f - pf after the prefix and the kept document tokens.
+    for (int f = lo + tid; f < min(lo + SCHUNK, pf + q); f += SB) {
+        const int i = f < pf ? f : N - q + (f - pf);
+        a.kept[out + (f < pf ? f : pf + kdoc + (f - pf))] = off + i;
+    }
+    // Chunk c of the document: document tokens [lo, lo + SCHUNK), at request
+    // positions pf + i, written after the prefix.
     if (kdoc <= 0 || lo >= ndoc) return;
 
     const uint32_t* m = a.meta + b * META;
@@ -533,7 +543,7 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
     const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
     const uint32_t base = a.chunk_off[a.doc_chunk0[b] + c];
-    const float* s = a.scores + off;
+    const float* s = a.scores + off + pf;
 
     uint64_t km[SITEMS];
 #pragma unroll
@@ -565,7 +575,7 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
         if ((km[it] >> lane) & 1ull) {
             const int i = lo + it * SB + tid;
             const uint32_t pos = base + tab[it * SWAVES + w] + lanes_below(km[it]);
-            if (pos < (uint32_t)kdoc) a.kept[out + pos] = off + i;
+            if (pos < (uint32_t)kdoc) a.kept[out + pf + pos] = off + pf + i;
         }
     }
 }
@@ -596,8 +606,8 @@ void chunk_plan(const BatchArgs& a, SelArgs* s, int* doc_chunks, int* all_chunks
     for (int b = 0; b < a.batch; ++b) {
         const int N = a.cu_seq[b + 1] - a.cu_seq[b];
         const int keep = a.cu_kept[b + 1] - a.cu_kept[b];
-        const int ndoc = N - a.q_len[b];
-        const bool selecting = keep < N && keep - a.q_len[b] > 0;
+        const int ndoc = N - a.q_len[b] - a.p_len[b];
+        const bool selecting = keep < N && keep - a.q_len[b] - a.p_len[b] > 0;
         if (s != nullptr) {
             s->doc_chunk0[b] = dc;
             s->all_chunk0[b] = ac;
@@ -629,7 +639,10 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
         s.off[b] = a.cu_seq[b];
         s.out[b] = a.cu_kept[b];
     }
-    for (int b = 0; b < a.batch; ++b) s.q[b] = a.q_len[b];
+    for (int b = 0; b < a.batch; ++b) {
+        s.q[b] = a.q_len[b];
+        s.p[b] = a.p_len[b];
+    }
     int dc, ac;
     chunk_plan(a, &s, &dc, &ac);
     const WsLayout L = ws_layout(a.batch, dc, a.cu_seq[a.batch]);

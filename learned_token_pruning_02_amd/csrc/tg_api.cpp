@@ -29,27 +29,65 @@ bool valid_dtype(int dt) { return dt == TG_F32 || dt == TG_BF16; }
 
 tg_status launched(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ERR_LAUNCH; }
 
-// Shared by tg_plan and tg_topk_select.
-tg_status plan_batch(const tg_batch* b, tg::BatchArgs* out) {
-    if (b == nullptr) return TG_ERR_NULL_PTR;
-    if (b->batch < 1 || b->batch > TG_MAX_BATCH) return TG_ERR_BAD_SHAPE;
-    if (b->seq_len == nullptr || b->q_len == nullptr || b->budget == nullptr)
-        return TG_ERR_NULL_PTR;
+// Shared by the plan and select calls; prefix_len may be NULL (no prefix).
+tg_status plan_batch_arrays(int32_t batch, const int32_t* seq_len, const int32_t* q_len,
+                            const int32_t* budget, const int32_t* prefix_len,
+                            tg::BatchArgs* out) {
+    if (batch < 1 || batch > TG_MAX_BATCH) return TG_ERR_BAD_SHAPE;
+    if (seq_len == nullptr || q_len == nullptr || budget == nullptr) return TG_ERR_NULL_PTR;
     int64_t tok = 0, kept = 0;
-    out->batch = b->batch;
+    out->batch = batch;
     out->cu_seq[0] = 0;
     out->cu_kept[0] = 0;
-    for (int i = 0; i < b->batch; ++i) {
-        const int64_t n = b->seq_len[i], q = b->q_len[i], k = b->budget[i];
-        if (n < 1 || q < 0 || q > n || k < 1 || q > (k < n ? k : n)) return TG_ERR_BAD_BUDGET;
+    for (int i = 0; i < batch; ++i) {
+        const int64_t n = seq_len[i], q = q_len[i], k = budget[i];
+        const int64_t p = prefix_len != nullptr ? prefix_len[i] : 0;
+        const int64_t keep = k < n ? k : n;
+        if (n < 1 || q < 0 || q > n || k < 1 || p < 0 || p + q > keep) return TG_ERR_BAD_BUDGET;
         tok += n;
-        kept += k < n ? k : n;
+        kept += keep;
         if (tok >= I32_LIMIT) return TG_ERR_BAD_SHAPE;
         out->cu_seq[i + 1] = (int32_t)tok;
         out->cu_kept[i + 1] = (int32_t)kept;
         out->q_len[i] = (int32_t)q;
+        out->p_len[i] = (int32_t)p;
     }
     return TG_OK;
+}
+
+tg_status plan_batch(const tg_batch* b, tg::BatchArgs* out) {
+    if (b == nullptr) return TG_ERR_NULL_PTR;
+    return plan_batch_arrays(b->batch, b->seq_len, b->q_len, b->budget, nullptr, out);
+}
+
+tg_status plan_batch(const tg_batch_prefix* b, tg::BatchArgs* out) {
+    if (b == nullptr) return TG_ERR_NULL_PTR;
+    return plan_batch_arrays(b->batch, b->seq_len, b->q_len, b->budget, b->prefix_len, out);
+}
+
+tg_status plan_out(const tg::BatchArgs& a, int32_t* cu_seqlens, int32_t* cu_kept,
+                   size_t* topk_ws_bytes) {
+    if (cu_seqlens != nullptr) std::memcpy(cu_seqlens, a.cu_seq, sizeof(int32_t) * (a.batch + 1));
+    if (cu_kept != nullptr) std::memcpy(cu_kept, a.cu_kept, sizeof(int32_t) * (a.batch + 1));
+    if (topk_ws_bytes != nullptr) *topk_ws_bytes = tg::select_workspace_bytes(a);
+    return TG_OK;
+}
+
+tg_status select_checked(const float* scores, const tg::BatchArgs& a, int32_t* kept_idx,
+                         int32_t* cu_kept_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (scores == nullptr || kept_idx == nullptr) return TG_ERR_NULL_PTR;
+    const size_t need = tg::select_workspace_bytes(a);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return TG_ERR_WORKSPACE;
+    if (!aligned4(scores) || !aligned4(kept_idx) || !aligned16(ws)) return TG_ERR_ALIGNMENT;
+    const int64_t T = a.cu_seq[a.batch], Kt = a.cu_kept[a.batch];
+    const int64_t wb = (int64_t)need;
+    if (overlap(kept_idx, Kt * 4, scores, T * 4) ||
+        overlap(cu_kept_dev, (a.batch + 1) * 4, scores, T * 4) ||
+        overlap(cu_kept_dev, (a.batch + 1) * 4, kept_idx, Kt * 4) ||
+        overlap(ws, wb, scores, T * 4) || overlap(ws, wb, kept_idx, Kt * 4) ||
+        overlap(ws, wb, cu_kept_dev, (a.batch + 1) * 4))
+        return TG_ERR_ALIAS;
+    return launched(tg::launch_select(scores, a, kept_idx, cu_kept_dev, ws, stream));
 }
 
 }  // namespace
@@ -79,10 +117,15 @@ tg_status tg_plan(const tg_batch* b, int32_t* cu_seqlens, int32_t* cu_kept,
     tg::BatchArgs a;
     const tg_status st = plan_batch(b, &a);
     if (st != TG_OK) return st;
-    if (cu_seqlens != nullptr) std::memcpy(cu_seqlens, a.cu_seq, sizeof(int32_t) * (a.batch + 1));
-    if (cu_kept != nullptr) std::memcpy(cu_kept, a.cu_kept, sizeof(int32_t) * (a.batch + 1));
-    if (topk_ws_bytes != nullptr) *topk_ws_bytes = tg::select_workspace_bytes(a);
-    return TG_OK;
+    return plan_out(a, cu_seqlens, cu_kept, topk_ws_bytes);
+}
+
+tg_status tg_plan_prefix(const tg_batch_prefix* b, int32_t* cu_seqlens, int32_t* cu_kept,
+                         size_t* topk_ws_bytes) {
+    tg::BatchArgs a;
+    const tg_status st = plan_batch(b, &a);
+    if (st != TG_OK) return st;
+    return plan_out(a, cu_seqlens, cu_kept, topk_ws_bytes);
 }
 
 tg_status tg_gate_score(tg_dtype dt, const void* hidden, int64_t T, int32_t d_model,
@@ -117,19 +160,16 @@ tg_status tg_topk_select(const float* scores, const tg_batch* b, int32_t* kept_i
     tg::BatchArgs a;
     const tg_status st = plan_batch(b, &a);
     if (st != TG_OK) return st;
-    if (scores == nullptr || kept_idx == nullptr) return TG_ERR_NULL_PTR;
-    const size_t need = tg::select_workspace_bytes(a);
-    if (need > 0 && (ws == nullptr || ws_bytes < need)) return TG_ERR_WORKSPACE;
-    if (!aligned4(scores) || !aligned4(kept_idx) || !aligned16(ws)) return TG_ERR_ALIGNMENT;
-    const int64_t T = a.cu_seq[a.batch], Kt = a.cu_kept[a.batch];
-    const int64_t wb = (int64_t)need;
-    if (overlap(kept_idx, Kt * 4, scores, T * 4) ||
-        overlap(cu_kept_dev, (a.batch + 1) * 4, scores, T * 4) ||
-        overlap(cu_kept_dev, (a.batch + 1) * 4, kept_idx, Kt * 4) ||
-        overlap(ws, wb, scores, T * 4) || overlap(ws, wb, kept_idx, Kt * 4) ||
-        overlap(ws, wb, cu_kept_dev, (a.batch + 1) * 4))
-        return TG_ERR_ALIAS;
-    return launched(tg::launch_select(scores, a, kept_idx, cu_kept_dev, ws, stream));
+    return select_checked(scores, a, kept_idx, cu_kept_dev, ws, ws_bytes, stream);
+}
+
+tg_status tg_topk_select_prefix(const float* scores, const tg_batch_prefix* b, int32_t* kept_idx,
+                                int32_t* cu_kept_dev, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    tg::BatchArgs a;
+    const tg_status st = plan_batch(b, &a);
+    if (st != TG_OK) return st;
+    return select_checked(scores, a, kept_idx, cu_kept_dev, ws, ws_bytes, stream);
 }
 
 tg_status tg_gather_compact(tg_dtype dt, const void* hidden, int64_t T, int32_t d_model,

@@ -15,6 +15,7 @@ struct BatchArgs {
     int32_t cu_seq[TG_MAX_BATCH + 1];   // token offsets of each request
     int32_t cu_kept[TG_MAX_BATCH + 1];  // kept-row offsets of each request
     int32_t q_len[TG_MAX_BATCH];        // question tail length of each request
+    int32_t p_len[TG_MAX_BATCH];        // template prefix length of each request (kept)
 };
 
 hipError_t launch_gate_f32(const float* hidden, int64_t T, int d, const float* w1, const float* b1,

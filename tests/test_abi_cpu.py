@@ -84,8 +84,8 @@ def test_plan_rejects_bad_batch():
     assert L.tg_plan(None, None, None, None) == 1
 
 
-def _batch(seq, q, bud):
-    return tg._batch(seq, q, bud)
+def _batch(seq, q, bud, pre=None):
+    return tg._batch(seq, q, bud, pre)
 
 
 def test_gate_validation():
@@ -124,6 +124,36 @@ def test_select_validation():
     assert f(A, ctypes.byref(bt), B, None, A, ws, None) == 9             # workspace over scores
     bad, keep2 = _batch([100], [10], [5])
     assert f(A, ctypes.byref(bad), B, None, C, ws, None) == 3
+
+
+@pytest.mark.parametrize("case", [
+    ([512], [32], [128], [16]),
+    ([8192, 24576, 65536, 16384], [203, 203, 87, 235], [812, 3733, 19152, 4727], [40, 0, 300, 17]),
+    ([5, 1, 9], [0, 1, 0], [100, 1, 9], [2, 0, 9]),
+    ([50], [10], [25], [15]),
+])
+def test_plan_prefix_matches_oracle(case):
+    seq, q, bud, pre = case
+    cu_s, cu_k, ws = tg.tg_plan(seq, q, bud, pre)
+    o_s, o_k = oracle.plan(seq, q, bud, pre)
+    assert cu_s == o_s and cu_k == o_k and ws > 0
+
+
+def test_select_prefix_validation():
+    L = tg.lib()
+    ws = tg.tg_plan([100], [10], [40], [20])[2]
+    f = L.tg_topk_select_prefix
+    bt, keep = _batch([100], [10], [40], [20])
+    assert f(A, None, B, None, C, ws, None) == 1
+    assert f(None, ctypes.byref(bt), B, None, C, ws, None) == 1
+    assert f(A, ctypes.byref(bt), B, None, None, ws, None) == 7
+    for pre, bud in ((31, 40), (-1, 40), (0, 9), (95, 200)):           # p + q > kept, p < 0
+        bad, keep2 = _batch([100], [10], [bud], [pre])
+        assert L.tg_plan_prefix(ctypes.byref(bad), None, None, None) == 3, (pre, bud)
+        assert f(A, ctypes.byref(bad), B, None, C, ws, None) == 3, (pre, bud)
+    nul, keep3 = _batch([100], [10], [40], [0])
+    nul.prefix_len = ctypes.cast(None, ctypes.POINTER(ctypes.c_int32))  # NULL prefix: no prefix
+    assert L.tg_plan_prefix(ctypes.byref(nul), None, None, None) == 0
 
 
 def test_select_workspace_grows_with_tokens_and_requests():

@@ -83,11 +83,13 @@ def test_gate_deterministic():
 
 
 # ---------------------------------------------------------------- select ----
-def _select_case(seq, q, bud, scores):
-    announce(f"select B={len(seq)} T={sum(seq)} seq={seq[:4]} q={q[:4]} budget={bud[:4]}")
-    ref, cu_ref = oracle.topk_select(scores, seq, q, bud)
+def _select_case(seq, q, bud, scores, prefix=None):
+    announce(f"select B={len(seq)} T={sum(seq)} seq={seq[:4]} q={q[:4]} budget={bud[:4]}"
+             + ("" if prefix is None else f" prefix={prefix[:4]}"))
+    ref, cu_ref = oracle.topk_select(scores, seq, q, bud, prefix)
     got, cu = tg.tg_topk_select(scores.cuda(), seq, q, bud,
-                                cu_kept_dev=torch.empty(len(seq) + 1, dtype=torch.int32, device="cuda"))
+                                cu_kept_dev=torch.empty(len(seq) + 1, dtype=torch.int32, device="cuda"),
+                                prefix_len=prefix)
     torch.cuda.synchronize()
     assert cu == cu_ref
     assert torch.equal(got.cpu(), ref), "kept ids differ"
@@ -173,6 +175,63 @@ def test_select_large_document_in_a_batch():
     s = torch.randn(sum(seq), generator=g)
     s[(1 << 20):(1 << 20) + 2000] = 0.5  # a run of equal scores near the first threshold
     _select_case(seq, q, bud, s)
+
+
+# ----------------------------------------------- select: template prefix ----
+def _prefixes(seq, q, bud, g, cap=600):
+    return [int(torch.randint(0, max(1, min(cap, min(b, n) - qq) + 1), (1,), generator=g))
+            for n, qq, b in zip(seq, q, bud)]
+
+
+@pytest.mark.parametrize("wname", list(workloads.WORKLOADS))
+def test_select_prefix_workload_shapes(wname):
+    """An always-kept template prefix in front of every document."""
+    w = workloads.WORKLOADS[wname]
+    g = torch.Generator().manual_seed(21)
+    _select_case(w.seq_len, w.q_len, w.budget, workloads.random_scores(w.total_tokens, seed=22),
+                 _prefixes(w.seq_len, w.q_len, w.budget, g))
+
+
+def test_select_prefix_edges():
+    """Prefix only, prefix + question filling the budget, an empty document,
+    a budget covering the request, ties across the prefix boundary."""
+    g = torch.Generator().manual_seed(23)
+    seq = [1, 2, 300, 300, 300, 4096, 17000, 9, 5000, 777]
+    q = [0, 0, 0, 100, 50, 128, 0, 3, 64, 0]
+    bud = [1, 1, 120, 150, 400, 4096, 9000, 9, 700, 100]
+    pre = [1, 1, 120, 50, 250, 3968, 8999, 6, 33, 0]
+    s = torch.randn(sum(seq), generator=g)
+    s[1000:1300] = 0.75  # equal scores straddling a prefix boundary
+    _select_case(seq, q, bud, s, pre)
+
+
+def test_select_prefix_specials_and_ties():
+    g = torch.Generator().manual_seed(24)
+    T = 30000
+    s = workloads.random_scores(T, seed=25, ties=20)
+    specials = torch.tensor([float("nan"), -0.0, 0.0, float("inf"), float("-inf")])
+    pos = torch.randint(0, T, (3000,), generator=g)
+    s[pos] = specials[torch.randint(0, 5, (3000,), generator=g)]
+    for bud, pre in ((300, 200), (4000, 1), (12000, 5000), (29000, 28900)):
+        _select_case([T], [100], [bud], s, [pre])
+
+
+def test_select_prefix_max_batch_and_large_document():
+    g = torch.Generator().manual_seed(26)
+    seq = [int(x) for x in torch.randint(1, 3000, (tg.TG_MAX_BATCH,), generator=g)]
+    q = [min(n, int(x)) for n, x in zip(seq, torch.randint(0, 300, (len(seq),), generator=g))]
+    bud = [max(qq, 1) + int(x) for qq, x in zip(q, torch.randint(0, 1500, (len(seq),), generator=g))]
+    _select_case(seq, q, bud, torch.randn(sum(seq), generator=g), _prefixes(seq, q, bud, g))
+    T = (1 << 21) + 5   # the many-workgroup ranking of documents above 2^20 tokens
+    _select_case([T], [77], [T // 10], workloads.random_scores(T, seed=27, ties=40), [1500])
+
+
+def test_select_random_keys():
+    """Random-K selection: the selector run on caller-drawn uniform keys."""
+    w = workloads.WORKLOADS["qwen3_1p7b_16k"]
+    keys = torch.rand(w.total_tokens, generator=torch.Generator().manual_seed(28))
+    _select_case(w.seq_len, w.q_len, w.budget, keys)
+    _select_case(w.seq_len, w.q_len, w.budget, keys, [16] * len(w.seq_len))
 
 
 # ---------------------------------------------------------------- gather ----
