@@ -20,6 +20,9 @@ l'attention gérée par des tokens ?"):
   dropped ones                                           -> ``gather_compact``
 * each kept token's score becomes a bias on the attention logits, with a
   learnable per-head gain and a per-head temperature     -> ``gated_attention``
+* generation then reads a KV cache that holds the kept tokens only, each row
+  with its score; a new token attends to every cached row with the same bias
+                                                         -> ``gated_decode_attention``
 
 The pages only sketch the bias.  The exact logit used here is
 ``tau_h * (q_i . k_j) / sqrt(d_head) + g_h * s_j`` over causal ``j <= i``.
@@ -29,8 +32,10 @@ textbook values of the normal CDF; the selector against brute force (Python
 ``sorted`` and an O(N^2) rank count) and its invariants; the attention against
 torch's scaled_dot_product_attention (plain causal when gains are 0 and
 temperatures 1, with an explicit additive mask otherwise) and closed forms (row
-0, shift invariance, a dominant key); the layer stack against an independent
-float64 composition.  Nothing here is "parity unpinned" except what the pages
+0, shift invariance, a dominant key); the decode attention against SDPA with
+a float mask, against the last row of the prefill attention, and closed forms
+(one cached row, empty cache, layout independence); the layer stack against an
+independent float64 composition.  Nothing here is "parity unpinned" except what the pages
 themselves leave open: fidelity to the authors' unpublished kernels.
 """
 from __future__ import annotations
@@ -50,6 +55,7 @@ __all__ = [
     "gather_compact",
     "gated_attention",
     "gated_attention_rows",
+    "gated_decode_attention",
     "linear",
     "stack_forward",
 ]
@@ -242,6 +248,48 @@ def gated_attention_rows(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int],
             denom = p.sum()
             out[r_i, h] = (p @ V) / denom
             lse[h, r_i] = m + torch.log(denom)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# Decode over the kept-only KV cache (spke.com page, three-phase list, third
+# bullet: no KV record is created for a pruned token; "Comment déployer
+# TokenGate ?": generation runs on the pruned prompt).  The pages do not say
+# whether the score bias still applies when generating; it is read as yes,
+# with each cached row carrying its own gate score.
+# --------------------------------------------------------------------------
+def gated_decode_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           s: torch.Tensor, row_off: Sequence[int], cache_len: Sequence[int],
+                           gain: torch.Tensor, temp: torch.Tensor
+                           ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One new query per request against its cached rows.
+
+    q[B][Hq][dh]; k, v[R][Hkv][dh] and s[R] hold cache rows; request b owns
+    rows row_off[b] .. row_off[b] + cache_len[b] - 1 (the new token's own row
+    already appended).  Logit l_j = tau_h (q . k_j) / sqrt(dh) + g_h s_j over
+    every cached row (no causal mask: the query is the newest position).
+    Returns out[B][Hq][dh] and lse[B][Hq] (float64, natural log); an empty
+    cache gives a zero output and lse = -inf.
+    """
+    B, Hq, dh = q.shape
+    group = Hq // k.shape[1]
+    out = torch.zeros(B, Hq, dh, dtype=torch.float64)
+    lse = torch.full((B, Hq), -math.inf, dtype=torch.float64)
+    s64 = s.double()
+    for b in range(B):
+        lo, n = int(row_off[b]), int(cache_len[b])
+        if n == 0:
+            continue
+        for h in range(Hq):
+            kv = h // group
+            Qr = q[b:b + 1, h].double()
+            logits = _head_logits(Qr, k[lo:lo + n, kv].double(), s64[lo:lo + n],
+                                  float(gain[h]), float(temp[h]), dh)[0]
+            m = logits.max()
+            p = torch.exp(logits - m)
+            denom = p.sum()
+            out[b, h] = (p @ v[lo:lo + n, kv].double()) / denom
+            lse[b, h] = m + torch.log(denom)
     return out, lse
 
 

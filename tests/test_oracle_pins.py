@@ -364,6 +364,88 @@ def test_attention_rows_agree_with_full():
     torch.testing.assert_close(l_r, lse[:, rows], rtol=1e-12, atol=1e-12)
 
 
+# --------------------------------------------------------------- decode ----
+def _decode_case(seed, lens=(1, 7, 40, 0, 13), Hq=6, Hkv=2, dh=16, gap=5):
+    """Cache rows scattered through a pool: request b starts at row_off[b],
+    with `gap` unused rows (random junk) between requests."""
+    g = torch.Generator().manual_seed(seed)
+    row_off, r = [], gap
+    for n in lens:
+        row_off.append(r)
+        r += n + gap
+    R = r
+    q = torch.randn(len(lens), Hq, dh, generator=g, dtype=torch.float64)
+    k = torch.randn(R, Hkv, dh, generator=g, dtype=torch.float64)
+    v = torch.randn(R, Hkv, dh, generator=g, dtype=torch.float64)
+    s = torch.randn(R, generator=g, dtype=torch.float64)
+    gain = torch.rand(Hq, generator=g, dtype=torch.float64) + 0.5
+    temp = torch.rand(Hq, generator=g, dtype=torch.float64) * 0.4 + 0.8
+    return q, k, v, s, row_off, list(lens), gain, temp
+
+
+def test_decode_matches_sdpa_with_mask():
+    """Against torch SDPA: one query row, queries scaled by tau_h, float mask
+    g_h s_j over the cached rows, no causal mask."""
+    q, k, v, s, off, lens, gain, temp = _decode_case(31)
+    out, lse = oracle.gated_decode_attention(q, k, v, s, off, lens, gain, temp)
+    Hq, rep = q.shape[1], q.shape[1] // k.shape[1]
+    for b, (lo, n) in enumerate(zip(off, lens)):
+        if n == 0:
+            continue
+        Q = (q[b][:, None, :] * temp[:, None, None])[None]                       # [1][Hq][1][dh]
+        K = k[lo:lo + n].permute(1, 0, 2).repeat_interleave(rep, dim=0)[None].contiguous()
+        V = v[lo:lo + n].permute(1, 0, 2).repeat_interleave(rep, dim=0)[None].contiguous()
+        mask = (gain[:, None] * s[lo:lo + n][None, :])[None, :, None, :]
+        want = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask)[0, :, 0]
+        torch.testing.assert_close(out[b], want, rtol=1e-12, atol=1e-12)
+        # lse through the probabilities (V = identity over the cached rows)
+        P = F.scaled_dot_product_attention(Q, K, torch.eye(n, dtype=torch.float64).expand(1, Hq, n, n),
+                                           attn_mask=mask)[0, :, 0]                # [Hq][n]
+        l0 = temp * (q[b] @ k[lo].repeat_interleave(rep, dim=0).t()).diagonal() / math.sqrt(q.shape[2]) \
+            + gain * s[lo]
+        torch.testing.assert_close(lse[b], l0 - torch.log(P[:, 0]), rtol=1e-12, atol=1e-12)
+
+
+def test_decode_is_the_last_prefill_row():
+    """A cache holding a request's rows 0..r, queried with row r's q, gives
+    row r of the prefill attention (output and lse)."""
+    q, k, v, s, gain, temp, cu = _attn_case(32, lens=(29,))
+    out, lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    for r in (0, 1, 13, 28):
+        o_d, l_d = oracle.gated_decode_attention(q[r:r + 1], k, v, s, [0], [r + 1], gain, temp)
+        torch.testing.assert_close(o_d[0], out[r], rtol=1e-12, atol=1e-12)
+        torch.testing.assert_close(l_d[0], lse[:, r], rtol=1e-12, atol=1e-12)
+
+
+def test_decode_closed_forms_and_layout():
+    q, k, v, s, off, lens, gain, temp = _decode_case(33)
+    out, lse = oracle.gated_decode_attention(q, k, v, s, off, lens, gain, temp)
+    Hq, dh, rep = q.shape[1], q.shape[2], q.shape[1] // k.shape[1]
+    for h in range(Hq):      # a single cached row returns its value; lse is its logit
+        assert torch.equal(out[0, h], v[off[0], h // rep])
+        want = temp[h] * (q[0, h] @ k[off[0], h // rep]) / math.sqrt(dh) + gain[h] * s[off[0]]
+        assert abs(float(lse[0, h] - want)) < 1e-12
+    assert torch.equal(out[3], torch.zeros_like(out[3]))          # empty cache
+    assert torch.isneginf(lse[3]).all()
+    # the same rows packed back to back give the same result
+    idx = torch.cat([torch.arange(lo, lo + n) for lo, n in zip(off, lens)])
+    packed = [0]
+    for n in lens[:-1]:
+        packed.append(packed[-1] + n)
+    o2, l2 = oracle.gated_decode_attention(q, k[idx], v[idx], s[idx], packed, lens, gain, temp)
+    assert torch.equal(o2, out) and torch.equal(l2, lse)
+    # constant scores: no dependence on the gain; a dominant key takes over
+    c = torch.full_like(s, -0.8)
+    o3, _ = oracle.gated_decode_attention(q, k, v, c, off, lens, gain, temp)
+    o4, _ = oracle.gated_decode_attention(q, k, v, c, off, lens, gain * 4, temp)
+    torch.testing.assert_close(o3, o4, rtol=1e-12, atol=1e-12)
+    big = s.clone()
+    big[off[2] + 17] = 1e4
+    o5, _ = oracle.gated_decode_attention(q, k, v, big, off, lens, gain, temp)
+    for h in range(Hq):
+        torch.testing.assert_close(o5[2, h], v[off[2] + 17, h // rep], rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- stack ----
 def test_stack_matches_independent_composition():
     g = torch.Generator().manual_seed(9)
