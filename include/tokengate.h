@@ -231,6 +231,60 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void *q, const void *k, const
                                 int32_t Hkv, int32_t d_head, void *out, float *lse,
                                 hipStream_t stream);
 
+/* Cached rows per split of tg_gated_attn_decode; its workspace is sized in
+ * these. */
+#define TG_DECODE_CHUNK 128
+/* Largest batch of tg_gated_attn_decode (one grid dimension per request). */
+#define TG_DECODE_MAX_BATCH 65535
+
+/*
+ * tg_decode_plan -- workspace bytes for tg_gated_attn_decode with this batch,
+ * query-head count, head size and largest cache length (host only; 0 bytes
+ * when max_len == 0).  Errors: TG_ERR_NULL_PTR (ws_bytes), TG_ERR_BAD_SHAPE
+ * (batch outside [1, TG_DECODE_MAX_BATCH], Hq < 1, max_len < 0),
+ * TG_ERR_UNSUPPORTED (d_head not 64 or 128).
+ */
+tg_status tg_decode_plan(int32_t batch, int32_t Hq, int32_t d_head, int32_t max_len,
+                         size_t *ws_bytes);
+
+/*
+ * tg_gated_attn_decode -- one generation step of token-gated attention over
+ * the kept-only KV cache.  Pruned tokens never get a KV record (spke.com page,
+ * three-phase list, third bullet), so after a pruned prefill the cache holds
+ * the kept rows, each with its gate score, and generation runs on them (page
+ * "Comment déployer TokenGate ?").  The pages do not say whether the score
+ * bias applies while generating; here it does, with the prefill's logit.
+ * For request b, query head h and KV head h / (Hq / Hkv), over the
+ * n_b = min(cache_len[b], max_len) cached rows r_j = row_off[b] + j, j < n_b
+ * (the new token's own row already appended, so no causal mask):
+ *     l_j = temp[h] * (q_bh . k[r_j]) / sqrt(d_head) + gain[h] * s[r_j]
+ *     out_bh = sum_j softmax_j(l_j) v[r_j],   lse_bh = ln sum_j exp(l_j)
+ * q    : [batch][Hq][d_head] in dt      out : same shape, dt output
+ * k, v : [cache_rows][Hkv][d_head] in dt, the row pool of every request
+ *        (packed back to back, padded per request, or anything in between)
+ * s    : [cache_rows] fp32; s and gain may both be NULL (no bias term)
+ * gain, temp : [Hq] fp32           lse : [batch][Hq] fp32 output or NULL
+ * row_off   : [batch] DEVICE int64 first pool row of each request
+ * cache_len : [batch] DEVICE int32 cached rows of each request
+ *   Both are read on the device, so a decode loop needs no host round trip.
+ *   A row outside [0, cache_rows) counts as absent and is never read; a
+ *   request with no row present gets out = 0 and lse = -inf.
+ * ws   : tg_decode_plan bytes of device memory, caller-owned, 16-byte
+ *        aligned, no initialisation needed (NULL allowed when 0 bytes).
+ * Supported: d_head in {64, 128}, Hq % Hkv == 0 with Hq / Hkv <= 8, else
+ * TG_ERR_UNSUPPORTED.  Two kernels on `stream`: per (chunk of
+ * TG_DECODE_CHUNK rows, KV head, request) softmax partials, then their merge.
+ * Errors: TG_ERR_BAD_DTYPE, TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE,
+ * TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT, TG_ERR_WORKSPACE, TG_ERR_ALIAS,
+ * TG_ERR_LAUNCH.
+ */
+tg_status tg_gated_attn_decode(tg_dtype dt, const void *q, const void *k, const void *v,
+                               const float *s, int64_t cache_rows, const int64_t *row_off,
+                               const int32_t *cache_len, int32_t batch, int32_t max_len,
+                               const float *gain, const float *temp, int32_t Hq, int32_t Hkv,
+                               int32_t d_head, void *out, float *lse, void *ws,
+                               size_t ws_bytes, hipStream_t stream);
+
 /*
  * tg_linear -- auxiliary projection for layers above the gate, run on the
  * kept rows only (spke.com page, third bullet).

@@ -32,6 +32,8 @@ __all__ = [
     "tg_topk_select",
     "tg_gather_compact",
     "tg_gated_attn_prefill",
+    "tg_decode_plan",
+    "tg_gated_attn_decode",
     "tg_linear",
 ]
 
@@ -112,6 +114,11 @@ def lib() -> ctypes.CDLL:
     L.tg_gated_attn_prefill.restype = ctypes.c_int
     L.tg_gated_attn_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, p_i32, i32, i32,
                                         i32, i32, vp, vp, vp]
+    L.tg_decode_plan.restype = ctypes.c_int
+    L.tg_decode_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.tg_gated_attn_decode.restype = ctypes.c_int
+    L.tg_gated_attn_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp,
+                                       i32, i32, i32, vp, vp, vp, sz, vp]
     L.tg_linear.restype = ctypes.c_int
     L.tg_linear.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
     _lib = L
@@ -268,6 +275,40 @@ def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], o
         _dev(temp, "temp", torch.float32), ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
         len(cu_kept) - 1, Hq, Hkv, dh, _dev(out, "out", q.dtype),
         _dev(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse
+
+
+def tg_decode_plan(batch: int, Hq: int, d_head: int, max_len: int) -> int:
+    """Workspace bytes of tg_gated_attn_decode."""
+    ws = ctypes.c_size_t(0)
+    _check("tg_decode_plan", lib().tg_decode_plan(batch, Hq, d_head, max_len, ctypes.byref(ws)))
+    return ws.value
+
+
+def tg_gated_attn_decode(q, k, v, s, row_off, cache_len, gain, temp, max_len: int, out=None,
+                         lse=None, want_lse: bool = False, workspace=None, stream=None):
+    """One decode step over the kept-only KV cache; returns (out, lse or None).
+
+    q[B][Hq][dh]; k, v[R][Hkv][dh] and s[R] form the row pool; row_off (int64)
+    and cache_len (int32) are device tensors of length B.  s=None and
+    gain=None drop the bias term."""
+    torch = _torch()
+    B, Hq, dh = q.shape
+    R, Hkv = k.shape[0], k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    need = tg_decode_plan(B, Hq, dh, max_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check("tg_gated_attn_decode", lib().tg_gated_attn_decode(
+        _dt(q), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(s, "s", torch.float32), R, _dev(row_off, "row_off", torch.int64),
+        _dev(cache_len, "cache_len", torch.int32), B, max_len, _dev(gain, "gain", torch.float32),
+        _dev(temp, "temp", torch.float32), Hq, Hkv, dh, _dev(out, "out", q.dtype),
+        _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
 
 

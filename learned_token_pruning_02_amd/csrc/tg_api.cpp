@@ -242,6 +242,60 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const
     return launched(tg::launch_attn_bf16(q, k, v, s_kept, gain, temp, sh, out, lse, stream));
 }
 
+tg_status tg_decode_plan(int32_t batch, int32_t Hq, int32_t d_head, int32_t max_len,
+                         size_t* ws_bytes) {
+    if (ws_bytes == nullptr) return TG_ERR_NULL_PTR;
+    if (batch < 1 || batch > TG_DECODE_MAX_BATCH || Hq < 1 || max_len < 0) return TG_ERR_BAD_SHAPE;
+    if (d_head != 64 && d_head != 128) return TG_ERR_UNSUPPORTED;
+    *ws_bytes = tg::decode_workspace_bytes(batch, Hq, d_head, max_len);
+    return TG_OK;
+}
+
+tg_status tg_gated_attn_decode(tg_dtype dt, const void* q, const void* k, const void* v,
+                               const float* s, int64_t cache_rows, const int64_t* row_off,
+                               const int32_t* cache_len, int32_t batch, int32_t max_len,
+                               const float* gain, const float* temp, int32_t Hq, int32_t Hkv,
+                               int32_t d_head, void* out, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (q == nullptr || k == nullptr || v == nullptr || row_off == nullptr ||
+        cache_len == nullptr || temp == nullptr || out == nullptr || (s == nullptr) != (gain == nullptr))
+        return TG_ERR_NULL_PTR;
+    if (batch < 1 || batch > TG_DECODE_MAX_BATCH || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+        cache_rows < 0 || max_len < 0)
+        return TG_ERR_BAD_SHAPE;
+    if (d_head != 64 && d_head != 128) return TG_ERR_UNSUPPORTED;
+    if (Hq / Hkv > 8) return TG_ERR_UNSUPPORTED;
+    const size_t need = tg::decode_workspace_bytes(batch, Hq, d_head, max_len);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return TG_ERR_WORKSPACE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (need > 0 && !aligned16(ws)) || (s != nullptr && (!aligned4(s) || !aligned4(gain))) ||
+        !aligned4(temp) || (lse != nullptr && !aligned4(lse)) || ((uintptr_t)row_off & 7u) != 0 ||
+        !aligned4(cache_len))
+        return TG_ERR_ALIGNMENT;
+    const int64_t eb = elt_bytes(dt);
+    const int64_t qb = (int64_t)batch * Hq * d_head * eb, kb = cache_rows * Hkv * d_head * eb;
+    const int64_t sb = cache_rows * 4, lb = (int64_t)batch * Hq * 4, wb = (int64_t)need;
+    const void* ins[] = {q, k, v, s, row_off, cache_len, gain, temp};
+    const int64_t inb[] = {qb, kb, kb, sb, (int64_t)batch * 8, (int64_t)batch * 4, (int64_t)Hq * 4,
+                           (int64_t)Hq * 4};
+    for (int i = 0; i < 8; ++i)
+        if (overlap(out, qb, ins[i], inb[i]) || overlap(lse, lb, ins[i], inb[i]) ||
+            (need > 0 && overlap(ws, wb, ins[i], inb[i])))
+            return TG_ERR_ALIAS;
+    if (overlap(out, qb, lse, lb) || (need > 0 && (overlap(ws, wb, out, qb) || overlap(ws, wb, lse, lb))))
+        return TG_ERR_ALIAS;
+    tg::DecodeShape sh;
+    sh.batch = batch;
+    sh.Hq = Hq;
+    sh.Hkv = Hkv;
+    sh.d_head = d_head;
+    sh.max_len = max_len;
+    sh.rows = cache_rows;
+    return launched(tg::launch_decode(dt, sh, q, k, v, s, row_off, cache_len, gain, temp, out, lse,
+                                      ws, stream));
+}
+
 tg_status tg_linear(tg_dtype dt, const void* x, const void* w, void* y, int64_t M, int32_t N,
                     int32_t K, int accumulate, hipStream_t stream) {
     if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;

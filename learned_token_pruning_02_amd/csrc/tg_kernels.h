@@ -45,6 +45,19 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const f
                             const float* gain, const float* temp, const AttnShape& sh, void* out,
                             float* lse, hipStream_t st);
 
+struct DecodeShape {
+    int32_t batch;
+    int32_t Hq, Hkv, d_head;
+    int32_t max_len;
+    int64_t rows;  // rows in the K/V/score pool
+};
+
+size_t decode_workspace_bytes(int32_t batch, int32_t Hq, int32_t d_head, int32_t max_len);
+hipError_t launch_decode(tg_dtype dt, const DecodeShape& sh, const void* q, const void* k,
+                         const void* v, const float* s, const int64_t* row_off,
+                         const int32_t* cache_len, const float* gain, const float* temp, void* out,
+                         float* lse, void* ws, hipStream_t st);
+
 hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M, int N, int K,
                              int accumulate, hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,

@@ -217,6 +217,54 @@ def test_attention_validation():
     assert call(cu=ctypes.cast(big, ctypes.POINTER(ctypes.c_int32))) == 5
 
 
+def test_decode_plan():
+    L = tg.lib()
+    ws = ctypes.c_size_t(0)
+    assert L.tg_decode_plan(1, 16, 128, 8192, ctypes.byref(ws)) == 0
+    nch = 8192 // 128
+    assert ws.value >= 16 * nch * (128 + 2) * 4
+    assert L.tg_decode_plan(1, 16, 128, 0, ctypes.byref(ws)) == 0 and ws.value == 0
+    assert L.tg_decode_plan(0, 16, 128, 10, ctypes.byref(ws)) == 2
+    assert L.tg_decode_plan(65536, 16, 128, 10, ctypes.byref(ws)) == 2
+    assert L.tg_decode_plan(1, 16, 128, -1, ctypes.byref(ws)) == 2
+    assert L.tg_decode_plan(1, 16, 80, 10, ctypes.byref(ws)) == 5
+    assert L.tg_decode_plan(1, 16, 128, 10, None) == 1
+    assert tg.tg_decode_plan(4, 16, 64, 1000) > tg.tg_decode_plan(4, 16, 64, 100)
+
+
+def test_decode_validation():
+    L = tg.lib()
+    f = L.tg_gated_attn_decode
+    ws = tg.tg_decode_plan(1, 16, 128, 100)
+    W = H + 4096
+    ok = [1, A, B, C, D, 100, E, E + 64, 1, 100, F, F + 64, 16, 8, 128, G, H, W, ws, None]
+    names = ["dt", "q", "k", "v", "s", "rows", "off", "len", "batch", "max_len", "gain", "temp",
+             "Hq", "Hkv", "dh", "out", "lse", "ws", "ws_bytes", "stream"]
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(dt=3) == 4
+    for name in ("q", "k", "v", "off", "len", "temp", "out"):
+        assert call(**{name: None}) == 1, name
+    assert call(s=None) == 1 and call(gain=None) == 1      # NULL together or not at all
+    assert call(batch=0) == 2 and call(batch=65536) == 2
+    assert call(Hq=12) == 2 and call(rows=-1) == 2 and call(max_len=-1) == 2
+    assert call(dh=96) == 5
+    assert call(Hq=72, Hkv=8) == 5                          # group of 9 query heads
+    assert call(ws=None) == 7 and call(ws_bytes=ws - 1) == 7
+    assert call(q=A + 8) == 6 and call(out=G + 4) == 6 and call(ws=W + 8) == 6
+    assert call(off=E + 4) == 6 and call(s=D + 2) == 6
+    assert call(out=A + 512) == 9                           # out overlaps q
+    assert call(lse=B + 64) == 9                            # lse overlaps k
+    assert call(ws=C + 1024) == 9                           # workspace overlaps v
+    assert call(ws=G) == 9                                  # workspace overlaps out
+    assert call(lse=G + 1024) == 9                          # lse overlaps out
+
+
 def test_linear_validation():
     L = tg.lib()
     f = L.tg_linear

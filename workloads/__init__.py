@@ -37,6 +37,9 @@ __all__ = [
     "attn_inputs",
     "stack_weights",
     "random_scores",
+    "DecodeWorkload",
+    "DECODE_WORKLOADS",
+    "decode_inputs",
 ]
 
 
@@ -228,3 +231,53 @@ def random_scores(n: int, seed: int = 0, ties: int = 0) -> torch.Tensor:
     if ties > 0:
         return torch.randint(0, ties, (n,), generator=g).float() / ties - 0.5
     return torch.randn(n, generator=g, dtype=torch.float32)
+
+
+# ------------------------------------------------------------------ decode ----
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One generation step over kept-only KV caches: request b has cache_len[b]
+    cached rows (its kept prefill rows plus the new token's own row)."""
+    name: str
+    shape: LayerShape
+    cache_len: List[int]
+
+    @property
+    def batch(self) -> int:
+        return len(self.cache_len)
+
+
+# After a pruned 128k prefill each request caches its 8192 kept rows; the
+# generated token adds row 8193.  32 such requests decode together.
+DECODE_WORKLOADS: Dict[str, DecodeWorkload] = {
+    "qwen3_1p7b_128k_decode_b32": DecodeWorkload(
+        "qwen3_1p7b_128k_decode_b32",
+        LayerShape(dtype=torch.bfloat16, **QWEN3_1P7B), [8192 + 1] * 32),
+}
+
+
+def decode_inputs(shape: LayerShape, cache_len: List[int], seed: int = 0, gap: int = 0,
+                  with_bias: bool = True) -> Dict[str, torch.Tensor]:
+    """q[B][Hq][dh]; a row pool k, v[R][Hkv][dh] and s[R]; row_off[B] (int64),
+    cache_len[B] (int32); gain[Hq], temp[Hq].
+
+    Requests sit back to back in the pool with `gap` unused rows (random data)
+    in front of each.  Cached scores are N(0, 1) fp32 (they stand in for gate
+    scores), q/k/v N(0, 1) in the storage dtype."""
+    row_off, r = [], 0
+    for n in cache_len:
+        r += gap
+        row_off.append(r)
+        r += n
+    R = r
+    B, hq, hkv, dh = len(cache_len), shape.n_q_heads, shape.n_kv_heads, shape.d_head
+    return dict(
+        q=_normal((B, hq, dh), 1.0, seed, 30, shape.dtype),
+        k=_normal((R, hkv, dh), 1.0, seed, 31, shape.dtype),
+        v=_normal((R, hkv, dh), 1.0, seed, 32, shape.dtype),
+        s=torch.randn(R, generator=_gen(seed, 33), dtype=torch.float32) if with_bias else None,
+        row_off=torch.tensor(row_off, dtype=torch.int64),
+        cache_len=torch.tensor(cache_len, dtype=torch.int32),
+        gain=_uniform(hq, 0.5, 1.5, seed, 34) if with_bias else None,
+        temp=_uniform(hq, 0.8, 1.2, seed, 35),
+    )
