@@ -46,6 +46,8 @@ def parse():
                    help="only run a plain device copy of 512 MiB (reference for HBM byte counters)")
     p.add_argument("--select-sweep", action="store_true",
                    help="only time the selector on T = 2^20 .. 2^26 random scores, K = T/16")
+    p.add_argument("--decode", action="store_true",
+                   help="only time one decode step over kept-only KV caches (32 requests x 8193 rows)")
     return p.parse_args()
 
 
@@ -119,7 +121,8 @@ def algorithmic(w, Kt_per_req):
 
 
 KERNEL_FRAG = {"gate": "gate_bf16_kernel", "select": "sel_cand_kernel",
-               "gather": "gather_rows_kernel", "attention": "attn_bf16_kernel"}
+               "gather": "gather_rows_kernel", "attention": "attn_bf16_kernel",
+               "decode": "decode_chunk_kernel"}
 
 
 def recorded_traffic(workload: str, kernel: str):
@@ -183,10 +186,86 @@ def cpu_baseline(w, gi, ai, s_gpu, kept, cu):
     }
 
 
+def decode_bench(args):
+    """One decode step (both kernels of tg_gated_attn_decode) over the kept-only
+    caches of 32 requests, 8193 rows each; HBM-bound, so the roofline is the
+    cached K/V/score bytes plus q and out per call over the call's time."""
+    import torch
+
+    import learned_token_pruning_02_amd as tg
+    import workloads
+
+    w = workloads.DECODE_WORKLOADS["qwen3_1p7b_128k_decode_b32"]
+    sh = w.shape
+    inp = workloads.decode_inputs(sh, w.cache_len, seed=args.seed)
+    d = {k: v.cuda() for k, v in inp.items()}
+    B, max_len = w.batch, max(w.cache_len)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty(B, sh.n_q_heads, dtype=torch.float32, device="cuda")
+    ws = torch.empty(tg.tg_decode_plan(B, sh.n_q_heads, sh.d_head, max_len), dtype=torch.uint8,
+                     device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def call():
+        tg.tg_gated_attn_decode(d["q"], d["k"], d["v"], d["s"], d["row_off"], d["cache_len"],
+                                d["gain"], d["temp"], max_len, out=out, lse=lse, workspace=ws,
+                                stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        call()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    mean = sum(ms) / len(ms)
+    rows = sum(w.cache_len)
+    eb = 2
+    bytes_call = (rows * sh.n_kv_heads * sh.d_head * eb * 2 + rows * 4
+                  + 2 * B * sh.n_q_heads * sh.d_head * eb + B * sh.n_q_heads * 4)
+    gbs = bytes_call / (mean * 1e-3) / 1e9
+    rec = {
+        "metric": "gated decode tokens/s per layer", "value": B / (mean * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded)",
+        "config": {"workload": w.name, "requests": B, "cache_rows_per_request": max_len,
+                   "heads_q": sh.n_q_heads, "heads_kv": sh.n_kv_heads, "d_head": sh.d_head},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name, "decode"),
+                     "kernel": "decode (split-K chunk kernel + merge, one call)",
+                     "algorithmic_bytes_per_call": bytes_call},
+        "ms_call": {"mean": mean, "median": sorted(ms)[len(ms) // 2], "min": min(ms)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        nb = 4
+        off, lens = inp["row_off"].tolist()[:nb], w.cache_len[:nb]
+        t0 = time.perf_counter()
+        oracle.gated_decode_attention(inp["q"][:nb], inp["k"], inp["v"], inp["s"], off, lens,
+                                      inp["gain"], inp["temp"])
+        t = (time.perf_counter() - t0) * B / nb
+        rec["cpu_baseline"] = {"value": B / t, "unit": "tokens/s", "cores": torch.get_num_threads(),
+                               "kind": "oracle",
+                               "sample": f"oracle decode for {nb} of {B} requests, scaled to {B}"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.decode:
+        if args.gpus != 1:
+            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
+            sys.exit(2)
+        decode_bench(args)
         return
     if args.select_sweep:
         select_sweep()

@@ -109,23 +109,16 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_chunk_kernel(DecArgs a) {
     const int G = a.G;
     const int h0 = kvh * G;
 
-    // This lane's slice of every query head in the group, pre-scaled so that
-    // dot * 1 is tau_h q.k / sqrt(DH) in log2 units.
-    float qf[MAXG][EPL], gain2[MAXG];
+    // Raw query slices first; they are unpacked only after the K/V loads
+    // below are in flight, so their latency overlaps the stream.
+    u32x4 qr[MAXG];
+    float qsc[MAXG], gain2[MAXG];
 #pragma unroll
-    for (int g = 0; g < MAXG; ++g) {
-        gain2[g] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) qf[g][e] = 0.0f;
-        if (g < G) {
-            const int h = h0 + g;
-            const T* qp = (const T*)a.q + ((int64_t)b * a.Hq + h) * DH + col;
-            Elt<T>::unpack(ld16(qp), qf[g]);
-            const float sc = a.temp[h] * a.qscale;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) qf[g][e] *= sc;
-            if (a.gain != nullptr) gain2[g] = a.gain[h] * 1.4426950408889634f;
-        }
+    for (int g = 0; g < MAXG; ++g) {  // branch-free: padded heads reread the last one, scaled by 0
+        const int h = h0 + min(g, G - 1);
+        qr[g] = ld16((const T*)a.q + ((int64_t)b * a.Hq + h) * DH + col);
+        qsc[g] = g < G ? a.temp[h] * a.qscale : 0.0f;
+        gain2[g] = (g < G && a.gain != nullptr) ? a.gain[h] * 1.4426950408889634f : 0.0f;
     }
 
     // Issue every K, V and score load of this lane before using any.
@@ -146,6 +139,16 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_chunk_kernel(DecArgs a) {
             vr[it] = ld16((const T*)a.v + e0);
             if (a.s != nullptr) sj[it] = a.s[row];
         }
+    }
+
+    // Query slices pre-scaled so that the dot product is
+    // tau_h q.k / sqrt(DH) in log2 units.
+    float qf[MAXG][EPL];
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+        Elt<T>::unpack(qr[g], qf[g]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) qf[g][e] *= qsc[g];
     }
 
     // Logits (log2 units) and the chunk maximum of each head.
@@ -244,34 +247,80 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_chunk_kernel(DecArgs a) {
     }
 }
 
-// Merge the chunks of one (request, head): one workgroup of DH threads.
+// Merge the chunks of one (request, head): out = sum_c 2^(m_c - M) o_c / L
+// with M the largest chunk maximum and L = sum_c 2^(m_c - M) l_c.  The chunk
+// weights are computed once (kept in LDS for the first MERGE_LDS_CHUNKS
+// chunks); each thread then sums one column over every R-th chunk with
+// independent loads, and the R partial sums meet in LDS.
+constexpr int MERGE_THREADS = 256;
+constexpr int MERGE_LDS_CHUNKS = 2048;
+
 template <class T, int DH>
-__global__ __launch_bounds__(DH) void decode_merge_kernel(DecArgs a) {
+__global__ __launch_bounds__(MERGE_THREADS) void decode_merge_kernel(DecArgs a) {
+    constexpr int R = MERGE_THREADS / DH;
+    constexpr int NW = MERGE_THREADS / WAVE;
+    __shared__ float fac[MERGE_LDS_CHUNKS];
+    __shared__ float red_m[NW], red_l[NW];
+    __shared__ float red_o[R][DH];
+
     const int bh = blockIdx.x;
     const int b = bh / a.Hq;
-    const int d = threadIdx.x;
+    const int t = threadIdx.x, w = t / WAVE, lane = t % WAVE;
     const int len = min(max(a.cache_len[b], 0), a.max_len);
     const int nch = (len + TG_DECODE_CHUNK - 1) / TG_DECODE_CHUNK;
     const float* ml = a.part_ml + (int64_t)bh * a.nch * 2;
-    const float* po = a.part_o + (int64_t)bh * a.nch * DH + d;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c)
-        if (ml[2 * c + 1] > 0.0f) M = fmaxf(M, ml[2 * c]);
-    float L = 0.0f, o = 0.0f;
-    if (M != -INFINITY) {
-        for (int c = 0; c < nch; ++c) {
-            const float lc = ml[2 * c + 1];
-            if (lc > 0.0f) {
-                const float f = __builtin_amdgcn_exp2f(ml[2 * c] - M);
-                L = fmaf(lc, f, L);
-                o = fmaf(po[(int64_t)c * DH], f, o);
-            }
-        }
+    const float* po = a.part_o + (int64_t)bh * a.nch * DH;
+
+    float mx = -INFINITY;
+    for (int c = t; c < nch; c += MERGE_THREADS)
+        if (ml[2 * c + 1] > 0.0f) mx = fmaxf(mx, ml[2 * c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, WAVE));
+    if (lane == 0) red_m[w] = mx;
+    __syncthreads();
+    float M = red_m[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, red_m[i]);
+    const bool none = M == -INFINITY;  // no chunk holds a present row
+
+    float lp = 0.0f;
+    for (int c = t; c < nch; c += MERGE_THREADS) {
+        const float lc = ml[2 * c + 1];
+        const float f = (lc > 0.0f && !none) ? __builtin_amdgcn_exp2f(ml[2 * c] - M) : 0.0f;
+        if (c < MERGE_LDS_CHUNKS) fac[c] = f;
+        lp = fmaf(lc, f, lp);
     }
-    const bool any = L > 0.0f;
-    ((T*)a.out)[(int64_t)bh * DH + d] = from_f32<T>(any ? o / L : 0.0f);
-    if (a.lse != nullptr && d == 0)
-        a.lse[bh] = any ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
+    lp = wave_sum(lp);
+    if (lane == 0) red_l[w] = lp;
+    __syncthreads();
+    float L = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) L += red_l[i];
+
+    const int r = t / DH, d = t % DH;
+    float o = 0.0f;
+#pragma unroll 8
+    for (int c = r; c < nch; c += R) {
+        float f;
+        if (c < MERGE_LDS_CHUNKS) {
+            f = fac[c];
+        } else {
+            const float lc = ml[2 * c + 1];
+            f = (lc > 0.0f && !none) ? __builtin_amdgcn_exp2f(ml[2 * c] - M) : 0.0f;
+        }
+        o = fmaf(po[(int64_t)c * DH + d], f, o);
+    }
+    red_o[r][d] = o;
+    __syncthreads();
+    if (t < DH) {
+        float os = 0.0f;
+#pragma unroll
+        for (int i = 0; i < R; ++i) os += red_o[i][t];
+        const bool any = L > 0.0f;
+        ((T*)a.out)[(int64_t)bh * DH + t] = from_f32<T>(any ? os / L : 0.0f);
+        if (a.lse != nullptr && t == 0)
+            a.lse[bh] = any ? (M + __log2f(L)) * 0.6931471805599453f : -INFINITY;
+    }
 }
 
 template <class T, int DH>
@@ -289,7 +338,8 @@ hipError_t launch_dh(const DecArgs& a, int batch, hipStream_t st) {
         hipLaunchKernelGGL((decode_chunk_kernel<T, DH, 8>), grid, dim3(DEC_THREADS), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_merge_kernel<T, DH>), dim3(batch * a.Hq), dim3(DH), 0, st, a);
+    hipLaunchKernelGGL((decode_merge_kernel<T, DH>), dim3(batch * a.Hq), dim3(MERGE_THREADS), 0, st,
+                       a);
     return hipGetLastError();
 }
 

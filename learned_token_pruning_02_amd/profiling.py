@@ -38,6 +38,8 @@ KERNELS = [
     ("attn_bf16_kernel", "attention", "learned_token_pruning_02_amd/csrc/attn.hip"),
     ("attn_f32_kernel", "attention", "learned_token_pruning_02_amd/csrc/attn.hip"),
     ("linear_bf16_kernel", "linear", "learned_token_pruning_02_amd/csrc/linear.hip"),
+    ("decode_chunk_kernel", "decode", "learned_token_pruning_02_amd/csrc/decode.hip"),
+    ("decode_merge_kernel", "decode", "learned_token_pruning_02_amd/csrc/decode.hip"),
 ]
 COPY_BYTES = 512 << 20
 
