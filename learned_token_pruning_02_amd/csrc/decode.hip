@@ -135,8 +135,10 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_chunk_kernel(DecArgs a) {
         sj[it] = 0.0f;
         if (ok[it]) {
             const int64_t e0 = (row * a.Hkv + kvh) * DH + col;
-            kr[it] = ld16((const T*)a.k + e0);
-            vr[it] = ld16((const T*)a.v + e0);
+            // Each cached byte is read once per step: nontemporal loads keep
+            // the stream from evicting the partials and small operands.
+            kr[it] = __builtin_nontemporal_load((const u32x4*)((const T*)a.k + e0));
+            vr[it] = __builtin_nontemporal_load((const u32x4*)((const T*)a.v + e0));
             if (a.s != nullptr) sj[it] = a.s[row];
         }
     }

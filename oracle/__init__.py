@@ -35,7 +35,9 @@ temperatures 1, with an explicit additive mask otherwise) and closed forms (row
 0, shift invariance, a dominant key); the decode attention against SDPA with
 a float mask, against the last row of the prefill attention, and closed forms
 (one cached row, empty cache, layout independence); the layer stack against an
-independent float64 composition.  Nothing here is "parity unpinned" except what the pages
+independent float64 composition; the rest of the pruned layer against torch's
+rms_norm, rotary embedding written as complex multiplication, torch's silu,
+and an independent composition of the whole layer.  Nothing here is "parity unpinned" except what the pages
 themselves leave open: fidelity to the authors' unpublished kernels.
 """
 from __future__ import annotations
@@ -58,6 +60,12 @@ __all__ = [
     "gated_decode_attention",
     "linear",
     "stack_forward",
+    "rms_norm",
+    "rope",
+    "silu",
+    "swiglu",
+    "kept_positions",
+    "decoder_layer",
 ]
 
 
@@ -326,3 +334,92 @@ def stack_forward(x_kept: torch.Tensor, s_kept: torch.Tensor, layers: List[Dict[
         a = store(a).reshape(Kt, n_q_heads * d_head)
         x = store(x.double() + linear(a, L["wo"]))
     return x
+
+
+# --------------------------------------------------------------------------
+# The rest of a pruned decoder layer (spke.com page, three-phase list, third
+# bullet: the layers above L run on the kept tokens only).  The pages name the
+# backbone (Qwen3-1.7B) but not its layer; this is the published Qwen3 decoder
+# layer: RMSNorm before attention and before the FFN, a per-head RMSNorm of q
+# and k, rotary position embedding (RoFormer, Su et al.) with the half-split
+# pairing (element i turns with element i + d_head/2), a SwiGLU FFN, no
+# projection biases.  The attention in it is the token-gated attention above.
+# A kept token keeps its original position inside its request.
+# --------------------------------------------------------------------------
+def rms_norm(x: torch.Tensor, w: torch.Tensor, eps: float) -> torch.Tensor:
+    """x / sqrt(mean(x^2) + eps) * w over the last dimension, float64."""
+    x = x.double()
+    return x / torch.sqrt((x * x).mean(dim=-1, keepdim=True) + eps) * w.double()
+
+
+def rope(x: torch.Tensor, pos: torch.Tensor, theta: float) -> torch.Tensor:
+    """Rotate x[M][H][dh]: the pair (x_i, x_{i+dh/2}) turns by the angle
+    pos_m * theta^(-2i/dh), i < dh/2 (float64)."""
+    dh = x.shape[-1]
+    half = dh // 2
+    i = torch.arange(half, dtype=torch.float64)
+    inv_freq = float(theta) ** (-2.0 * i / dh)
+    ang = pos.double()[:, None] * inv_freq[None, :]
+    c = torch.cos(ang)[:, None, :]
+    s = torch.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half].double(), x[..., half:].double()
+    return torch.cat([x1 * c - x2 * s, x2 * c + x1 * s], dim=-1)
+
+
+def silu(z: torch.Tensor) -> torch.Tensor:
+    """z * sigmoid(z) = z / (1 + e^-z), float64."""
+    z = z.double()
+    return z / (1.0 + torch.exp(-z))
+
+
+def swiglu(x: torch.Tensor, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor) -> torch.Tensor:
+    """(silu(x Wg^T) * (x Wu^T)) Wd^T, float64."""
+    return linear(silu(linear(x, wg)) * linear(x, wu), wd)
+
+
+def kept_positions(kept_idx: torch.Tensor, cu_seqlens: Sequence[int],
+                   cu_kept: Sequence[int]) -> torch.Tensor:
+    """Original position of each kept row inside its request:
+    kept_idx[r] - cu_seqlens[b] for the request b that owns row r (int32)."""
+    pos = torch.empty(len(kept_idx), dtype=torch.int32)
+    for b in range(len(cu_kept) - 1):
+        lo, hi = int(cu_kept[b]), int(cu_kept[b + 1])
+        pos[lo:hi] = kept_idx[lo:hi] - int(cu_seqlens[b])
+    return pos
+
+
+def decoder_layer(x_kept: torch.Tensor, s_kept: torch.Tensor, pos: torch.Tensor,
+                  cu_kept: Sequence[int], L: Dict[str, torch.Tensor], n_q_heads: int,
+                  n_kv_heads: int, d_head: int, theta: float, eps: float,
+                  store_dtype: Optional[torch.dtype] = None) -> Dict[str, torch.Tensor]:
+    """One decoder layer over the kept rows; returns every stored tensor.
+
+    L holds in_norm[d], wq[Hq*dh][d], wk, wv[Hkv*dh][d], q_norm, k_norm[dh],
+    wo[d][Hq*dh], gain, temp[Hq], post_norm[d], wg, wu[F][d], wd[d][F].
+    store_dtype=None keeps float64 throughout; otherwise each tensor is rounded
+    where a GPU pipeline stores it: xn, q, k, v, q and k after norm + rotation,
+    the attention output, h, xn2, the gate/up products, their SwiGLU product,
+    and the layer output.
+    """
+    def store(t):
+        return t if store_dtype is None else t.to(store_dtype)
+
+    Kt = x_kept.shape[0]
+    x = x_kept.double() if store_dtype is None else x_kept.to(store_dtype)
+    r = {}
+    r["xn"] = store(rms_norm(x, L["in_norm"], eps))
+    q = store(linear(r["xn"], L["wq"])).reshape(Kt, n_q_heads, d_head)
+    k = store(linear(r["xn"], L["wk"])).reshape(Kt, n_kv_heads, d_head)
+    r["v"] = store(linear(r["xn"], L["wv"])).reshape(Kt, n_kv_heads, d_head)
+    r["q_proj"], r["k_proj"] = q, k
+    r["q"] = store(rope(rms_norm(q, L["q_norm"], eps), pos, theta))
+    r["k"] = store(rope(rms_norm(k, L["k_norm"], eps), pos, theta))
+    a, _ = gated_attention(r["q"], r["k"], r["v"], s_kept, L["gain"], L["temp"], cu_kept)
+    r["attn"] = store(a).reshape(Kt, n_q_heads * d_head)
+    r["h"] = store(x.double() + linear(r["attn"], L["wo"]))
+    r["xn2"] = store(rms_norm(r["h"], L["post_norm"], eps))
+    r["g"] = store(linear(r["xn2"], L["wg"]))
+    r["u"] = store(linear(r["xn2"], L["wu"]))
+    r["m"] = store(silu(r["g"]) * r["u"].double())
+    r["out"] = store(r["h"].double() + linear(r["m"], L["wd"]))
+    return r

@@ -484,3 +484,121 @@ def test_needles_survive_reduced_haystack():
     kept, _ = oracle.topk_select(s, w.seq_len, w.q_len, w.budget)
     needles = set(workloads.needle_positions(w, 0).tolist())
     assert needles <= set(kept.tolist())
+
+
+# ------------------------------------------------ rest of the pruned layer ----
+def test_rms_norm_matches_torch_and_closed_form():
+    g = torch.Generator().manual_seed(50)
+    x = torch.randn(7, 3, 48, generator=g, dtype=torch.float64) * 3
+    w = torch.randn(48, generator=g, dtype=torch.float64)
+    want = F.rms_norm(x, (48,), weight=w, eps=1e-6)
+    torch.testing.assert_close(oracle.rms_norm(x, w, 1e-6), want, rtol=1e-13, atol=1e-13)
+    c = torch.full((2, 16), -2.5, dtype=torch.float64)          # constant row: c / sqrt(c^2 + eps)
+    got = oracle.rms_norm(c, torch.ones(16, dtype=torch.float64), 0.25)
+    torch.testing.assert_close(got, torch.full_like(c, -2.5 / math.sqrt(6.25 + 0.25)), rtol=1e-15, atol=0)
+
+
+def test_rope_is_complex_rotation():
+    """The pair (x_i, x_{i+dh/2}) as the complex number x_i + j x_{i+dh/2},
+    multiplied by e^{j pos theta^(-2i/dh)}."""
+    g = torch.Generator().manual_seed(51)
+    M, H, dh, theta = 9, 3, 16, 10000.0
+    x = torch.randn(M, H, dh, generator=g, dtype=torch.float64)
+    pos = torch.tensor([0, 1, 2, 7, 100, 4095, 65536, 131071, 3], dtype=torch.int32)
+    half = dh // 2
+    inv = theta ** (-torch.arange(0, dh, 2, dtype=torch.float64) / dh)
+    ang = pos.double()[:, None] * inv[None, :]
+    z = torch.complex(x[..., :half], x[..., half:]) * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+    want = torch.cat([z.real, z.imag], dim=-1)
+    torch.testing.assert_close(oracle.rope(x, pos, theta), want, rtol=1e-12, atol=1e-12)
+
+
+def test_rope_invariants_and_hand_values():
+    g = torch.Generator().manual_seed(52)
+    x = torch.randn(6, 2, 32, generator=g, dtype=torch.float64)
+    zero = torch.zeros(6, dtype=torch.int32)
+    assert torch.equal(oracle.rope(x, zero, 1e6), x)                         # position 0: identity
+    pos = torch.tensor([3, 17, 900, 5, 131000, 2], dtype=torch.int32)
+    r = oracle.rope(x, pos, 1e6)
+    torch.testing.assert_close(r.norm(dim=-1), x.norm(dim=-1), rtol=1e-13, atol=0)
+    # only the offset between two positions matters for their dot product
+    qv, kv = x[0:1], x[1:2]
+    for m, n, t in ((5, 2, 11), (1000, 10, 12345), (7, 7, 3)):
+        a = (oracle.rope(qv, torch.tensor([m]), 1e6) * oracle.rope(kv, torch.tensor([n]), 1e6)).sum()
+        b = (oracle.rope(qv, torch.tensor([m + t]), 1e6) * oracle.rope(kv, torch.tensor([n + t]), 1e6)).sum()
+        assert abs(float(a - b)) < 1e-10
+    # dh = 4, theta = 100, position 1: angles 1 and 0.1 rad
+    e = torch.eye(4, dtype=torch.float64)[:, None, :]
+    out = oracle.rope(e, torch.ones(4, dtype=torch.int32), 100.0)[:, 0]
+    want = torch.tensor([[math.cos(1), 0, math.sin(1), 0], [0, math.cos(0.1), 0, math.sin(0.1)],
+                         [-math.sin(1), 0, math.cos(1), 0], [0, -math.sin(0.1), 0, math.cos(0.1)]],
+                        dtype=torch.float64)
+    torch.testing.assert_close(out, want, rtol=0, atol=1e-15)
+
+
+def test_silu_and_swiglu_match_torch():
+    g = torch.Generator().manual_seed(53)
+    z = torch.randn(1000, generator=g, dtype=torch.float64) * 6
+    torch.testing.assert_close(oracle.silu(z), F.silu(z), rtol=1e-14, atol=1e-15)
+    assert float(oracle.silu(torch.zeros(1))) == 0.0
+    x = torch.randn(5, 24, generator=g, dtype=torch.float64)
+    wg, wu = torch.randn(40, 24, generator=g, dtype=torch.float64), torch.randn(40, 24, generator=g, dtype=torch.float64)
+    wd = torch.randn(24, 40, generator=g, dtype=torch.float64)
+    want = F.linear(F.silu(F.linear(x, wg)) * F.linear(x, wu), wd)
+    torch.testing.assert_close(oracle.swiglu(x, wg, wu, wd), want, rtol=1e-12, atol=1e-12)
+
+
+def test_kept_positions():
+    seq, q, bud = [30, 1, 50], [5, 1, 10], [12, 1, 50]
+    s = torch.randn(sum(seq), generator=torch.Generator().manual_seed(54))
+    kept, cu_k = oracle.topk_select(s, seq, q, bud)
+    cu_s = oracle.plan(seq, q, bud)[0]
+    pos = oracle.kept_positions(kept, cu_s, cu_k)
+    for b in range(3):
+        p = pos[cu_k[b]:cu_k[b + 1]]
+        assert (p >= 0).all() and (p < seq[b]).all()
+        assert torch.equal(p + cu_s[b], kept[cu_k[b]:cu_k[b + 1]])
+    assert pos[cu_k[2]:].tolist() == list(range(50))                        # all kept: 0..N-1
+    assert pos[cu_k[0]:cu_k[1]][-5:].tolist() == list(range(25, 30))        # the question tail
+
+
+def _layer_weights(g, d, Hq, Hkv, dh, F_):
+    r = lambda *s: torch.randn(*s, generator=g, dtype=torch.float64)
+    return dict(in_norm=1 + 0.1 * r(d), wq=r(Hq * dh, d) / math.sqrt(d), wk=r(Hkv * dh, d) / math.sqrt(d),
+                wv=r(Hkv * dh, d) / math.sqrt(d), q_norm=1 + 0.1 * r(dh), k_norm=1 + 0.1 * r(dh),
+                wo=r(d, Hq * dh) / math.sqrt(Hq * dh), gain=torch.rand(Hq, generator=g, dtype=torch.float64) + 0.5,
+                temp=torch.rand(Hq, generator=g, dtype=torch.float64) * 0.4 + 0.8, post_norm=1 + 0.1 * r(d),
+                wg=r(F_, d) / math.sqrt(d), wu=r(F_, d) / math.sqrt(d), wd=r(d, F_) / math.sqrt(F_))
+
+
+def test_decoder_layer_matches_independent_composition():
+    """torch's rms_norm, rotary embedding as complex multiplication, SDPA with
+    tau-scaled queries and a float mask g_h s_j plus the causal mask, torch's
+    silu: the same layer composed independently, in float64."""
+    g = torch.Generator().manual_seed(55)
+    d, Hq, Hkv, dh, F_, theta, eps = 32, 4, 2, 8, 48, 1e6, 1e-6
+    cu = [0, 6, 19]
+    Kt = cu[-1]
+    L = _layer_weights(g, d, Hq, Hkv, dh, F_)
+    x = torch.randn(Kt, d, generator=g, dtype=torch.float64)
+    s = torch.randn(Kt, generator=g, dtype=torch.float64)
+    pos = torch.tensor([0, 3, 4, 9, 10, 11] + [2, 5, 8, 13, 21, 34, 55, 89, 144, 233, 377, 610, 987],
+                       dtype=torch.int32)
+    got = oracle.decoder_layer(x, s, pos, cu, L, Hq, Hkv, dh, theta, eps)["out"]
+
+    def rot(t):
+        half = dh // 2
+        inv = theta ** (-torch.arange(0, dh, 2, dtype=torch.float64) / dh)
+        ang = pos.double()[:, None] * inv[None, :]
+        z = torch.complex(t[..., :half], t[..., half:]) * torch.polar(torch.ones_like(ang), ang)[:, None, :]
+        return torch.cat([z.real, z.imag], dim=-1)
+
+    xn = F.rms_norm(x, (d,), weight=L["in_norm"], eps=eps)
+    q = rot(F.rms_norm(F.linear(xn, L["wq"]).view(Kt, Hq, dh), (dh,), weight=L["q_norm"], eps=eps))
+    k = rot(F.rms_norm(F.linear(xn, L["wk"]).view(Kt, Hkv, dh), (dh,), weight=L["k_norm"], eps=eps))
+    v = F.linear(xn, L["wv"]).view(Kt, Hkv, dh)
+    a = _sdpa_reference(q, k, v, s, L["gain"], L["temp"], cu).reshape(Kt, Hq * dh)
+    h = x + F.linear(a, L["wo"])
+    hn = F.rms_norm(h, (d,), weight=L["post_norm"], eps=eps)
+    want = h + F.linear(F.silu(F.linear(hn, L["wg"])) * F.linear(hn, L["wu"]), L["wd"])
+    torch.testing.assert_close(got, want, rtol=1e-11, atol=1e-11)
