@@ -285,6 +285,73 @@ tg_status tg_gated_attn_decode(tg_dtype dt, const void *q, const void *k, const 
                                int32_t d_head, void *out, float *lse, void *ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/* ---- The rest of a pruned decoder layer on the kept rows ----------------
+ * Layers above the gate run on the kept tokens only (spke.com page,
+ * three-phase list, third bullet).  The pages name the Qwen3-1.7B backbone
+ * but not its layer; these calls are the pieces of the published Qwen3
+ * decoder layer that are not projections (tg_linear) or attention:
+ *   x  -> tg_rmsnorm -> tg_linear (q, k, v) -> tg_qk_norm_rope
+ *      -> tg_gated_attn_prefill -> tg_linear (o, accumulate into x)
+ *      -> tg_rmsnorm -> tg_linear (gate|up) -> tg_silu_mul
+ *      -> tg_linear (down, accumulate into x)
+ * All run on the caller's stream, allocate nothing and compute in fp32 with
+ * one rounding at each store. */
+
+/*
+ * tg_rmsnorm -- y[m] = x[m] / sqrt(mean_j x[m][j]^2 + eps) * w, rows of d.
+ * x, y : [M][d] in dt (y == x allowed: in place; other overlaps are
+ * TG_ERR_ALIAS);  w : [d] in dt.  Supported: d * sizeof(dt) % 16 == 0.
+ * M == 0 is a no-op.  Errors: TG_ERR_BAD_DTYPE, TG_ERR_NULL_PTR,
+ * TG_ERR_BAD_SHAPE (M < 0, d < 1, eps < 0 or not finite), TG_ERR_UNSUPPORTED,
+ * TG_ERR_ALIGNMENT, TG_ERR_ALIAS, TG_ERR_LAUNCH.
+ */
+tg_status tg_rmsnorm(tg_dtype dt, const void *x, const void *w, float eps, int64_t M, int32_t d,
+                     void *y, hipStream_t stream);
+
+/*
+ * tg_kept_positions -- the original position of each kept row inside its
+ * request: pos[r] = kept_idx[r] - cu_seqlens_host[b] for the request b with
+ * cu_kept_host[b] <= r < cu_kept_host[b+1].  A kept token keeps the position
+ * it had in the full prompt (the rotary embedding of the layers above the
+ * gate uses it).  kept_idx, pos : [Kt] DEVICE int32, Kt = cu_kept_host[batch];
+ * cu_seqlens_host, cu_kept_host : [batch+1] HOST int32 as returned by tg_plan.
+ * Errors: TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE (batch, offsets not starting at 0
+ * or decreasing), TG_ERR_ALIGNMENT, TG_ERR_ALIAS, TG_ERR_LAUNCH.
+ */
+tg_status tg_kept_positions(const int32_t *kept_idx, const int32_t *cu_seqlens_host,
+                            const int32_t *cu_kept_host, int32_t batch, int32_t *pos,
+                            hipStream_t stream);
+
+/*
+ * tg_qk_norm_rope -- in place on q [M][Hq][d_head] and k [M][Hkv][d_head]
+ * (dt): each head vector is RMS-normalised over d_head with its weight
+ * (q_norm_w / k_norm_w, [d_head] in dt; NULL skips that normalisation), then
+ * rotated (rotary embedding, RoFormer, half-split pairing): for i < d_head/2
+ * and a = pos[m] * theta^(-2i/d_head),
+ *     x'_i = x_i cos a - x_{i+d/2} sin a,   x'_{i+d/2} = x_{i+d/2} cos a + x_i sin a.
+ * pos : [M] DEVICE int32 (tg_kept_positions).  The angle is formed and reduced
+ * modulo 2 pi in double precision; sin and cos in fp32.
+ * Supported: d_head in {64, 128}.  M == 0 is a no-op.  Errors:
+ * TG_ERR_BAD_DTYPE, TG_ERR_NULL_PTR (q, k, pos), TG_ERR_BAD_SHAPE (M < 0,
+ * heads < 1, theta <= 0, eps < 0), TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT,
+ * TG_ERR_ALIAS, TG_ERR_LAUNCH.
+ */
+tg_status tg_qk_norm_rope(tg_dtype dt, void *q, void *k, const void *q_norm_w,
+                          const void *k_norm_w, const int32_t *pos, int64_t M, int32_t Hq,
+                          int32_t Hkv, int32_t d_head, float theta, float eps,
+                          hipStream_t stream);
+
+/*
+ * tg_silu_mul -- the SwiGLU product: out[m][j] = silu(gu[m][j]) * gu[m][F+j]
+ * with silu(z) = z / (1 + e^-z); gu : [M][2F] in dt (the gate and up
+ * projections side by side, as one tg_linear with the two weights stacked),
+ * out : [M][F] in dt.  Supported: F * sizeof(dt) % 16 == 0.  M == 0 is a
+ * no-op.  Errors: TG_ERR_BAD_DTYPE, TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE,
+ * TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT, TG_ERR_ALIAS, TG_ERR_LAUNCH.
+ */
+tg_status tg_silu_mul(tg_dtype dt, const void *gu, int64_t M, int32_t F, void *out,
+                      hipStream_t stream);
+
 /*
  * tg_linear -- auxiliary projection for layers above the gate, run on the
  * kept rows only (spke.com page, third bullet).

@@ -34,6 +34,10 @@ __all__ = [
     "tg_gated_attn_prefill",
     "tg_decode_plan",
     "tg_gated_attn_decode",
+    "tg_rmsnorm",
+    "tg_kept_positions",
+    "tg_qk_norm_rope",
+    "tg_silu_mul",
     "tg_linear",
 ]
 
@@ -119,6 +123,15 @@ def lib() -> ctypes.CDLL:
     L.tg_gated_attn_decode.restype = ctypes.c_int
     L.tg_gated_attn_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp,
                                        i32, i32, i32, vp, vp, vp, sz, vp]
+    f32 = ctypes.c_float
+    L.tg_rmsnorm.restype = ctypes.c_int
+    L.tg_rmsnorm.argtypes = [ctypes.c_int, vp, vp, f32, i64, i32, vp, vp]
+    L.tg_kept_positions.restype = ctypes.c_int
+    L.tg_kept_positions.argtypes = [vp, p_i32, p_i32, i32, vp, vp]
+    L.tg_qk_norm_rope.restype = ctypes.c_int
+    L.tg_qk_norm_rope.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, i64, i32, i32, i32, f32, f32, vp]
+    L.tg_silu_mul.restype = ctypes.c_int
+    L.tg_silu_mul.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp]
     L.tg_linear.restype = ctypes.c_int
     L.tg_linear.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
     _lib = L
@@ -310,6 +323,56 @@ def tg_gated_attn_decode(q, k, v, s, row_off, cache_len, gain, temp, max_len: in
         _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
         0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
+
+
+def tg_rmsnorm(x, w, eps: float, y=None, stream=None):
+    """y = x / sqrt(mean(x^2) + eps) * w over the last dimension of x[M][d];
+    y=x runs in place."""
+    torch = _torch()
+    d = x.shape[-1]
+    M = x.numel() // d if d else 0
+    if y is None:
+        y = torch.empty_like(x)
+    _check("tg_rmsnorm", lib().tg_rmsnorm(_dt(x), _dev(x, "x"), _dev(w, "w", x.dtype), eps, M, d,
+                                          _dev(y, "y", x.dtype), _stream(stream)))
+    return y
+
+
+def tg_kept_positions(kept_idx, cu_seqlens: Sequence[int], cu_kept: Sequence[int], pos=None,
+                      stream=None):
+    """Original in-request position of every kept row (int32 device tensor)."""
+    torch = _torch()
+    if pos is None:
+        pos = torch.empty(int(cu_kept[-1]), dtype=torch.int32, device=kept_idx.device)
+    cs, ck = _i32_array(cu_seqlens), _i32_array(cu_kept)
+    P = ctypes.POINTER(ctypes.c_int32)
+    _check("tg_kept_positions", lib().tg_kept_positions(
+        _dev(kept_idx, "kept_idx", torch.int32), ctypes.cast(cs, P), ctypes.cast(ck, P),
+        len(cu_kept) - 1, _dev(pos, "pos", torch.int32), _stream(stream)))
+    return pos
+
+
+def tg_qk_norm_rope(q, k, q_norm_w, k_norm_w, pos, theta: float, eps: float, stream=None):
+    """In place: per-head RMSNorm of q[M][Hq][dh] and k[M][Hkv][dh] (weights may
+    be None), then the rotary embedding at positions pos[M]."""
+    torch = _torch()
+    M, Hq, dh = q.shape
+    _check("tg_qk_norm_rope", lib().tg_qk_norm_rope(
+        _dt(q), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(q_norm_w, "q_norm_w", q.dtype),
+        _dev(k_norm_w, "k_norm_w", q.dtype), _dev(pos, "pos", torch.int32), M, Hq, k.shape[1], dh,
+        theta, eps, _stream(stream)))
+    return q, k
+
+
+def tg_silu_mul(gu, out=None, stream=None):
+    """out[M][F] = silu(gu[:, :F]) * gu[:, F:] for gu[M][2F]."""
+    torch = _torch()
+    M, F2 = gu.shape
+    if out is None:
+        out = torch.empty(M, F2 // 2, dtype=gu.dtype, device=gu.device)
+    _check("tg_silu_mul", lib().tg_silu_mul(_dt(gu), _dev(gu, "gu"), M, F2 // 2,
+                                            _dev(out, "out", gu.dtype), _stream(stream)))
+    return out
 
 
 def tg_linear(x, w, y=None, accumulate: bool = False, stream=None):

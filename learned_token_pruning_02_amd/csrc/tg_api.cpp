@@ -4,6 +4,7 @@
 // so an error status means nothing was enqueued.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 
@@ -294,6 +295,79 @@ tg_status tg_gated_attn_decode(tg_dtype dt, const void* q, const void* k, const 
     sh.rows = cache_rows;
     return launched(tg::launch_decode(dt, sh, q, k, v, s, row_off, cache_len, gain, temp, out, lse,
                                       ws, stream));
+}
+
+tg_status tg_rmsnorm(tg_dtype dt, const void* x, const void* w, float eps, int64_t M, int32_t d,
+                     void* y, hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (x == nullptr || w == nullptr || y == nullptr) return TG_ERR_NULL_PTR;
+    if (M < 0 || d < 1 || !(eps >= 0.0f) || !std::isfinite(eps)) return TG_ERR_BAD_SHAPE;
+    const int64_t eb = elt_bytes(dt);
+    if ((int64_t)d * eb % 16 != 0) return TG_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TG_ERR_ALIGNMENT;
+    const int64_t xb = M * d * eb;
+    if ((y != x && overlap(y, xb, x, xb)) || overlap(y, xb, w, d * eb)) return TG_ERR_ALIAS;
+    if (M == 0) return TG_OK;
+    return launched(tg::launch_rmsnorm(dt, x, w, eps, M, d, y, stream));
+}
+
+tg_status tg_kept_positions(const int32_t* kept_idx, const int32_t* cu_seqlens_host,
+                            const int32_t* cu_kept_host, int32_t batch, int32_t* pos,
+                            hipStream_t stream) {
+    if (kept_idx == nullptr || cu_seqlens_host == nullptr || cu_kept_host == nullptr ||
+        pos == nullptr)
+        return TG_ERR_NULL_PTR;
+    if (batch < 1 || batch > TG_MAX_BATCH) return TG_ERR_BAD_SHAPE;
+    tg::BatchArgs a{};
+    a.batch = batch;
+    if (cu_seqlens_host[0] != 0 || cu_kept_host[0] != 0) return TG_ERR_BAD_SHAPE;
+    for (int i = 0; i <= batch; ++i) {
+        if (i > 0 && (cu_seqlens_host[i] < cu_seqlens_host[i - 1] || cu_kept_host[i] < cu_kept_host[i - 1]))
+            return TG_ERR_BAD_SHAPE;
+        a.cu_seq[i] = cu_seqlens_host[i];
+        a.cu_kept[i] = cu_kept_host[i];
+    }
+    const int64_t Kt = cu_kept_host[batch];
+    if (!aligned4(kept_idx) || !aligned4(pos)) return TG_ERR_ALIGNMENT;
+    if (overlap(pos, Kt * 4, kept_idx, Kt * 4)) return TG_ERR_ALIAS;
+    if (Kt == 0) return TG_OK;
+    return launched(tg::launch_kept_positions(kept_idx, Kt, a, pos, stream));
+}
+
+tg_status tg_qk_norm_rope(tg_dtype dt, void* q, void* k, const void* q_norm_w, const void* k_norm_w,
+                          const int32_t* pos, int64_t M, int32_t Hq, int32_t Hkv, int32_t d_head,
+                          float theta, float eps, hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (q == nullptr || k == nullptr || pos == nullptr) return TG_ERR_NULL_PTR;
+    if (M < 0 || Hq < 1 || Hkv < 1 || !(theta > 0.0f) || !std::isfinite(theta) || !(eps >= 0.0f) ||
+        !std::isfinite(eps))
+        return TG_ERR_BAD_SHAPE;
+    if (d_head != 64 && d_head != 128) return TG_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || (q_norm_w != nullptr && !aligned16(q_norm_w)) ||
+        (k_norm_w != nullptr && !aligned16(k_norm_w)) || !aligned4(pos))
+        return TG_ERR_ALIGNMENT;
+    const int64_t eb = elt_bytes(dt);
+    const int64_t qb = M * Hq * d_head * eb, kb = M * Hkv * d_head * eb, wb = d_head * eb;
+    if (overlap(q, qb, k, kb) || overlap(q, qb, pos, M * 4) || overlap(k, kb, pos, M * 4) ||
+        overlap(q, qb, q_norm_w, wb) || overlap(q, qb, k_norm_w, wb) || overlap(k, kb, q_norm_w, wb) ||
+        overlap(k, kb, k_norm_w, wb))
+        return TG_ERR_ALIAS;
+    if (M == 0) return TG_OK;
+    return launched(tg::launch_qk_norm_rope(dt, q, k, q_norm_w, k_norm_w, pos, M, Hq, Hkv, d_head,
+                                            theta, eps, stream));
+}
+
+tg_status tg_silu_mul(tg_dtype dt, const void* gu, int64_t M, int32_t F, void* out,
+                      hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (gu == nullptr || out == nullptr) return TG_ERR_NULL_PTR;
+    if (M < 0 || F < 1) return TG_ERR_BAD_SHAPE;
+    const int64_t eb = elt_bytes(dt);
+    if ((int64_t)F * eb % 16 != 0) return TG_ERR_UNSUPPORTED;
+    if (!aligned16(gu) || !aligned16(out)) return TG_ERR_ALIGNMENT;
+    if (overlap(out, M * F * eb, gu, M * 2 * F * eb)) return TG_ERR_ALIAS;
+    if (M == 0) return TG_OK;
+    return launched(tg::launch_silu_mul(dt, gu, M, F, out, stream));
 }
 
 tg_status tg_linear(tg_dtype dt, const void* x, const void* w, void* y, int64_t M, int32_t N,

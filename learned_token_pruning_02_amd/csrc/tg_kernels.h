@@ -58,6 +58,16 @@ hipError_t launch_decode(tg_dtype dt, const DecodeShape& sh, const void* q, cons
                          const int32_t* cache_len, const float* gain, const float* temp, void* out,
                          float* lse, void* ws, hipStream_t st);
 
+hipError_t launch_rmsnorm(tg_dtype dt, const void* x, const void* w, float eps, int64_t M, int d,
+                          void* y, hipStream_t st);
+hipError_t launch_qk_norm_rope(tg_dtype dt, void* q, void* k, const void* qw, const void* kw,
+                               const int32_t* pos, int64_t M, int Hq, int Hkv, int dh, float theta,
+                               float eps, hipStream_t st);
+hipError_t launch_silu_mul(tg_dtype dt, const void* gu, int64_t M, int F, void* out,
+                           hipStream_t st);
+hipError_t launch_kept_positions(const int32_t* kept, int64_t Kt, const BatchArgs& a, int32_t* pos,
+                                 hipStream_t st);
+
 hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M, int N, int K,
                              int accumulate, hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,

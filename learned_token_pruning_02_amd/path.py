@@ -13,8 +13,8 @@ from typing import Dict, List, Optional, Sequence
 
 import torch
 
-from . import (tg_gate_score, tg_gated_attn_prefill, tg_gather_compact, tg_linear, tg_plan,
-               tg_topk_select)
+from . import (tg_gate_score, tg_gated_attn_prefill, tg_gather_compact, tg_kept_positions,
+               tg_linear, tg_plan, tg_qk_norm_rope, tg_rmsnorm, tg_silu_mul, tg_topk_select)
 
 
 class GatedLayer:
@@ -84,4 +84,55 @@ class AttentionStack:
                                   self.v.view(Kt, self.Hkv, self.dh), s_kept, L["gain"], L["temp"],
                                   cu_kept, out=self.attn)
             tg_linear(self.attn.view(Kt, self.Hq * self.dh), L["wo"], y=x, accumulate=True)
+        return x
+
+
+class DecoderLayer:
+    """A whole decoder layer above the gate on the kept rows (the published
+    Qwen3 layer the pages' backbone uses), the residual updated in place:
+
+        xn = rmsnorm(x);  q, k, v = xn Wq^T, xn Wk^T, xn Wv^T
+        q, k <- rotary(rmsnorm_head(q)), rotary(rmsnorm_head(k))  at original positions
+        x += gated_attention(q, k, v; s_kept) Wo^T
+        xn = rmsnorm(x);  x += (silu(xn Wg^T) * (xn Wu^T)) Wd^T
+
+    Weights: in_norm[d], wq[Hq*dh][d], wk, wv[Hkv*dh][d], q_norm, k_norm[dh],
+    wo[d][Hq*dh], gain, temp[Hq], post_norm[d], wgu[2F][d] (gate rows then up
+    rows), wd[d][F].  Every step is one library call; buffers are owned here
+    so repeated calls allocate nothing.
+    """
+
+    def __init__(self, Kt: int, d_model: int, n_q_heads: int, n_kv_heads: int, d_head: int,
+                 d_ffn: int, dtype: torch.dtype, theta: float = 1e6, eps: float = 1e-6,
+                 device="cuda"):
+        self.Hq, self.Hkv, self.dh, self.F = n_q_heads, n_kv_heads, d_head, d_ffn
+        self.theta, self.eps = theta, eps
+        e = dict(dtype=dtype, device=device)
+        self.xn = torch.empty(Kt, d_model, **e)
+        self.q = torch.empty(Kt, n_q_heads, d_head, **e)
+        self.k = torch.empty(Kt, n_kv_heads, d_head, **e)
+        self.v = torch.empty(Kt, n_kv_heads, d_head, **e)
+        self.attn = torch.empty(Kt, n_q_heads, d_head, **e)
+        self.gu = torch.empty(Kt, 2 * d_ffn, **e)
+        self.m = torch.empty(Kt, d_ffn, **e)
+        self.pos = torch.empty(Kt, dtype=torch.int32, device=device)
+
+    def positions(self, kept_idx, cu_seqlens: Sequence[int], cu_kept: Sequence[int]):
+        return tg_kept_positions(kept_idx, cu_seqlens, cu_kept, pos=self.pos)
+
+    def __call__(self, x, s_kept, cu_kept: Sequence[int], L: Dict[str, torch.Tensor]):
+        """x[Kt][d] is updated in place; self.pos must hold the positions."""
+        Kt = x.shape[0]
+        tg_rmsnorm(x, L["in_norm"], self.eps, y=self.xn)
+        tg_linear(self.xn, L["wq"], y=self.q.view(Kt, -1))
+        tg_linear(self.xn, L["wk"], y=self.k.view(Kt, -1))
+        tg_linear(self.xn, L["wv"], y=self.v.view(Kt, -1))
+        tg_qk_norm_rope(self.q, self.k, L["q_norm"], L["k_norm"], self.pos, self.theta, self.eps)
+        tg_gated_attn_prefill(self.q, self.k, self.v, s_kept, L["gain"], L["temp"], cu_kept,
+                              out=self.attn)
+        tg_linear(self.attn.view(Kt, -1), L["wo"], y=x, accumulate=True)
+        tg_rmsnorm(x, L["post_norm"], self.eps, y=self.xn)
+        tg_linear(self.xn, L["wgu"], y=self.gu)
+        tg_silu_mul(self.gu, out=self.m)
+        tg_linear(self.m, L["wd"], y=x, accumulate=True)
         return x

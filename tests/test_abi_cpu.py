@@ -265,6 +265,49 @@ def test_decode_validation():
     assert call(lse=G + 1024) == 9                          # lse overlaps out
 
 
+def test_layer_piece_validation():
+    L = tg.lib()
+    rn = L.tg_rmsnorm
+    assert rn(3, A, B, 1e-6, 10, 2048, C, None) == 4
+    assert rn(1, None, B, 1e-6, 10, 2048, C, None) == 1 and rn(1, A, None, 1e-6, 10, 2048, C, None) == 1
+    assert rn(1, A, B, 1e-6, -1, 2048, C, None) == 2 and rn(1, A, B, -1.0, 10, 2048, C, None) == 2
+    assert rn(1, A, B, float("nan"), 10, 2048, C, None) == 2
+    assert rn(1, A, B, 1e-6, 10, 2044, C, None) == 5                    # bf16 rows of 16-byte multiples
+    assert rn(1, A + 2, B, 1e-6, 10, 2048, C, None) == 6
+    assert rn(1, A, B, 1e-6, 10, 2048, A + 4096, None) == 9             # partial overlap
+    assert rn(1, A, B, 1e-6, 10, 2048, B, None) == 9                    # y over w
+    assert rn(1, A, B, 1e-6, 0, 2048, A, None) == 0                     # in place, M == 0
+    qr = L.tg_qk_norm_rope
+    ok = [1, A, B, C, D, E, 100, 16, 8, 128, 1e6, 1e-6, None]
+
+    def q(**kw):
+        names = ["dt", "q", "k", "qw", "kw", "pos", "M", "Hq", "Hkv", "dh", "theta", "eps", "st"]
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return qr(*args)
+
+    assert q(dt=2) == 4 and q(q=None) == 1 and q(k=None) == 1 and q(pos=None) == 1
+    assert q(M=-1) == 2 and q(Hq=0) == 2 and q(theta=0.0) == 2 and q(eps=-1.0) == 2
+    assert q(dh=96) == 5 and q(q=A + 4) == 6 and q(pos=E + 2) == 6
+    assert q(k=A + 1024) == 9 and q(qw=A + 512) == 9 and q(pos=B + 64) == 9
+    assert q(M=0) == 0
+    sm = L.tg_silu_mul
+    assert sm(2, A, 10, 64, B, None) == 4 and sm(1, None, 10, 64, B, None) == 1
+    assert sm(1, A, -1, 64, B, None) == 2 and sm(1, A, 10, 0, B, None) == 2
+    assert sm(1, A, 10, 60, B, None) == 5 and sm(1, A, 10, 64, B + 8, None) == 6
+    assert sm(1, A, 10, 64, A + 1024, None) == 9 and sm(1, A, 0, 64, B, None) == 0
+    kp = L.tg_kept_positions
+    P = ctypes.POINTER(ctypes.c_int32)
+    cs, ck = tg._i32_array([0, 100, 150]), tg._i32_array([0, 30, 60])
+    cs_p, ck_p = ctypes.cast(cs, P), ctypes.cast(ck, P)
+    assert kp(None, cs_p, ck_p, 2, B, None) == 1 and kp(A, None, ck_p, 2, B, None) == 1
+    assert kp(A, cs_p, ck_p, 0, B, None) == 2 and kp(A, cs_p, ck_p, 65, B, None) == 2
+    bad = tg._i32_array([0, 40, 30])
+    assert kp(A, cs_p, ctypes.cast(bad, P), 2, B, None) == 2
+    assert kp(A + 2, cs_p, ck_p, 2, B, None) == 6 and kp(A, cs_p, ck_p, 2, A + 8, None) == 9
+
+
 def test_linear_validation():
     L = tg.lib()
     f = L.tg_linear

@@ -40,6 +40,9 @@ __all__ = [
     "DecodeWorkload",
     "DECODE_WORKLOADS",
     "decode_inputs",
+    "QWEN3_1P7B_FFN",
+    "layer_weights",
+    "kept_layout",
 ]
 
 
@@ -281,3 +284,50 @@ def decode_inputs(shape: LayerShape, cache_len: List[int], seed: int = 0, gap: i
         gain=_uniform(hq, 0.5, 1.5, seed, 34) if with_bias else None,
         temp=_uniform(hq, 0.8, 1.2, seed, 35),
     )
+
+
+# ------------------------------------------------- rest of the pruned layer ----
+QWEN3_1P7B_FFN = 6144      # Qwen3-1.7B intermediate size
+
+
+def layer_weights(shape: LayerShape, d_ffn: int, seed: int = 0, tid0: int = 200) -> Dict[str, torch.Tensor]:
+    """One decoder layer: projections N(0, 1/fan_in) in Linear layout, norm
+    weights 1 + N(0, 0.1^2) (so that they matter), gain U(0.5, 1.5), temp
+    U(0.8, 1.2).  wgu stacks the gate rows over the up rows ([2F][d])."""
+    d, hq, hkv, dh = shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.d_head
+    dt = shape.dtype
+
+    def norm_w(n, tid):
+        return (1.0 + 0.1 * torch.randn(n, generator=_gen(seed, tid), dtype=torch.float32)).to(dt)
+
+    wg = _normal((d_ffn, d), 1.0 / math.sqrt(d), seed, tid0 + 8, dt)
+    wu = _normal((d_ffn, d), 1.0 / math.sqrt(d), seed, tid0 + 9, dt)
+    return dict(
+        in_norm=norm_w(d, tid0 + 0),
+        wq=_normal((hq * dh, d), 1.0 / math.sqrt(d), seed, tid0 + 1, dt),
+        wk=_normal((hkv * dh, d), 1.0 / math.sqrt(d), seed, tid0 + 2, dt),
+        wv=_normal((hkv * dh, d), 1.0 / math.sqrt(d), seed, tid0 + 3, dt),
+        q_norm=norm_w(dh, tid0 + 4),
+        k_norm=norm_w(dh, tid0 + 5),
+        wo=_normal((d, hq * dh), 1.0 / math.sqrt(hq * dh), seed, tid0 + 6, dt),
+        post_norm=norm_w(d, tid0 + 7),
+        wg=wg, wu=wu, wgu=torch.cat([wg, wu], dim=0),
+        wd=_normal((d, d_ffn), 1.0 / math.sqrt(d_ffn), seed, tid0 + 10, dt),
+        gain=_uniform(hq, 0.5, 1.5, seed, tid0 + 11),
+        temp=_uniform(hq, 0.8, 1.2, seed, tid0 + 12),
+    )
+
+
+def kept_layout(seq_len: List[int], q_len: List[int], budget: List[int], seed: int = 0):
+    """A plausible kept-id layout without running a gate: per request, the
+    question tail plus a uniformly random sorted subset of the document.
+    Returns (kept ids int32, cu_seqlens, cu_kept)."""
+    g = _gen(seed, 40)
+    ids, cu_s, cu_k = [], [0], [0]
+    for n, q, k in zip(seq_len, q_len, budget):
+        k = min(k, n)
+        doc = torch.sort(torch.randperm(n - q, generator=g)[: k - q]).values
+        ids.append(torch.cat([doc, torch.arange(n - q, n)]) + cu_s[-1])
+        cu_s.append(cu_s[-1] + n)
+        cu_k.append(cu_k[-1] + k)
+    return torch.cat(ids).to(torch.int32), cu_s, cu_k
