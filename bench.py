@@ -46,6 +46,8 @@ def parse():
                    help="only run a plain device copy of 512 MiB (reference for HBM byte counters)")
     p.add_argument("--select-sweep", action="store_true",
                    help="only time the selector on T = 2^20 .. 2^26 random scores, K = T/16")
+    p.add_argument("--layer", action="store_true",
+                   help="only time one whole decoder layer on the 8192 kept rows of the 128k prompt")
     p.add_argument("--decode", action="store_true",
                    help="only time one decode step over kept-only KV caches (32 requests x 8193 rows)")
     return p.parse_args()
@@ -256,10 +258,125 @@ def decode_bench(args):
     print(json.dumps(rec), flush=True)
 
 
+def layer_bench(args):
+    """One whole decoder layer above the gate (RMSNorm, q/k/v projections, q/k
+    norm + rotary embedding, gated attention, output projection, RMSNorm,
+    SwiGLU FFN) on the 8192 kept rows of the pruned 128k prompt, Qwen3-1.7B
+    shape; per-call HIP events on the library's stream."""
+    import torch
+
+    import learned_token_pruning_02_amd as tg
+    import workloads
+    from learned_token_pruning_02_amd.path import DecoderLayer
+
+    w = workloads.WORKLOADS["qwen3_1p7b_128k_niah"]
+    sh = w.shape
+    F = workloads.QWEN3_1P7B_FFN
+    L = {k: v.cuda() for k, v in workloads.layer_weights(sh, F, seed=args.seed).items()}
+    kept, cu_s, cu_k = workloads.kept_layout(w.seq_len, w.q_len, w.budget, seed=args.seed)
+    Kt = cu_k[-1]
+    g = torch.Generator().manual_seed(args.seed * 7 + 1)
+    x0 = torch.randn(Kt, sh.d_model, generator=g).to(sh.dtype).cuda()
+    s = torch.randn(Kt, generator=g).cuda()
+    x = x0.clone()
+    layer = DecoderLayer(Kt, sh.d_model, sh.n_q_heads, sh.n_kv_heads, sh.d_head, F, sh.dtype)
+    layer.positions(kept.cuda(), cu_s, cu_k)
+    st = torch.cuda.current_stream()
+    theta, eps = layer.theta, layer.eps
+    names = ["in_norm", "q_proj", "k_proj", "v_proj", "qk_norm_rope", "attention", "o_proj",
+             "post_norm", "gate_up", "silu_mul", "down"]
+    calls = [
+        lambda: tg.tg_rmsnorm(x, L["in_norm"], eps, y=layer.xn, stream=st),
+        lambda: tg.tg_linear(layer.xn, L["wq"], y=layer.q.view(Kt, -1), stream=st),
+        lambda: tg.tg_linear(layer.xn, L["wk"], y=layer.k.view(Kt, -1), stream=st),
+        lambda: tg.tg_linear(layer.xn, L["wv"], y=layer.v.view(Kt, -1), stream=st),
+        lambda: tg.tg_qk_norm_rope(layer.q, layer.k, L["q_norm"], L["k_norm"], layer.pos, theta, eps,
+                                   stream=st),
+        lambda: tg.tg_gated_attn_prefill(layer.q, layer.k, layer.v, s, L["gain"], L["temp"], cu_k,
+                                         out=layer.attn, stream=st),
+        lambda: tg.tg_linear(layer.attn.view(Kt, -1), L["wo"], y=x, accumulate=True, stream=st),
+        lambda: tg.tg_rmsnorm(x, L["post_norm"], eps, y=layer.xn, stream=st),
+        lambda: tg.tg_linear(layer.xn, L["wgu"], y=layer.gu, stream=st),
+        lambda: tg.tg_silu_mul(layer.gu, out=layer.m, stream=st),
+        lambda: tg.tg_linear(layer.m, L["wd"], y=x, accumulate=True, stream=st),
+    ]
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(st)
+        for j, c in enumerate(calls):
+            c()
+            evs[i][j + 1].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
+    step_ms = sum(e[0].elapsed_time(e[-1]) for e in evs) / args.steps
+    d, hq, hkv, dh = sh.d_model, sh.n_q_heads, sh.n_kv_heads, sh.d_head
+    flops = {"q_proj": 2 * Kt * d * hq * dh, "k_proj": 2 * Kt * d * hkv * dh, "v_proj": 2 * Kt * d * hkv * dh,
+             "o_proj": 2 * Kt * hq * dh * d, "gate_up": 2 * Kt * d * 2 * F, "down": 2 * Kt * F * d,
+             "attention": 4 * dh * hq * Kt * (Kt + 1) // 2}
+    eb = 2
+    hbm = {"in_norm": 2 * Kt * d * eb, "post_norm": 2 * Kt * d * eb,
+           "qk_norm_rope": 2 * Kt * (hq + hkv) * dh * eb + Kt * 4, "silu_mul": 3 * Kt * F * eb}
+    kern = {n: {"ms": per[n]} for n in names}
+    for n, f in flops.items():
+        kern[n]["TFLOP/s"] = f / (per[n] * 1e-3) / 1e12
+        kern[n]["mfma_frac"] = kern[n]["TFLOP/s"] / BF16_PEAK_TFLOPS
+    for n, b in hbm.items():
+        kern[n]["GB/s"] = b / (per[n] * 1e-3) / 1e9
+        kern[n]["hbm_frac"] = kern[n]["GB/s"] / HBM_PEAK_GBS
+    gu = kern["gate_up"]["TFLOP/s"]
+    rec = {
+        "metric": "pruned decoder layer tokens/s (context tokens per layer)",
+        "value": w.total_tokens / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; random-init Qwen3-1.7B-shaped layer)",
+        "config": {"workload": "qwen3_1p7b_128k_layer", "tokens": w.total_tokens, "kept": Kt,
+                   "d_model": d, "heads_q": hq, "heads_kv": hkv, "d_head": dh, "d_ffn": F},
+        "roofline": {"bound": "mfma", "achieved": gu, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "gate_up (tg_linear)"},
+        "kept_rows_per_s": Kt / (step_ms * 1e-3), "gpu_ms_per_layer": step_ms,
+        "layer_TFLOP/s": sum(flops.values()) / (step_ms * 1e-3) / 1e12,
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 64
+        Lc = {k: v.cpu() for k, v in L.items()}
+        t0 = time.perf_counter()
+        xn = oracle.rms_norm(x0[:rows].cpu(), Lc["in_norm"], eps)
+        for nm in ("wq", "wk", "wv"):
+            oracle.linear(xn, Lc[nm])
+        h = oracle.linear(torch.zeros(rows, hq * dh, dtype=torch.float64), Lc["wo"])
+        oracle.swiglu(oracle.rms_norm(h, Lc["post_norm"], eps), Lc["wg"], Lc["wu"], Lc["wd"])
+        t_rows = (time.perf_counter() - t0) * Kt / rows
+        t0 = time.perf_counter()
+        q1 = layer.q[:, :2].cpu().contiguous()
+        oracle.gated_attention(q1, layer.k[:, :1].cpu().contiguous(), layer.v[:, :1].cpu().contiguous(),
+                               s.cpu(), Lc["gain"][:2], Lc["temp"][:2], cu_k)
+        t_attn = (time.perf_counter() - t0) * hq / 2
+        rec["cpu_baseline"] = {"value": w.total_tokens / (t_rows + t_attn), "unit": "tokens/s",
+                               "cores": torch.get_num_threads(), "kind": "oracle",
+                               "sample": (f"oracle row-wise steps on {rows} of {Kt} kept rows and "
+                                          f"attention for 2 of {hq} heads, each scaled to the layer")}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.layer:
+        if args.gpus != 1:
+            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
+            sys.exit(2)
+        layer_bench(args)
         return
     if args.decode:
         if args.gpus != 1:

@@ -38,6 +38,10 @@ KERNELS = [
     ("attn_bf16_kernel", "attention", "learned_token_pruning_02_amd/csrc/attn.hip"),
     ("attn_f32_kernel", "attention", "learned_token_pruning_02_amd/csrc/attn.hip"),
     ("linear_bf16_kernel", "linear", "learned_token_pruning_02_amd/csrc/linear.hip"),
+    ("rmsnorm_kernel", "layer", "learned_token_pruning_02_amd/csrc/layer.hip"),
+    ("qk_norm_rope_kernel", "layer", "learned_token_pruning_02_amd/csrc/layer.hip"),
+    ("silu_mul_kernel", "layer", "learned_token_pruning_02_amd/csrc/layer.hip"),
+    ("kept_positions_kernel", "layer", "learned_token_pruning_02_amd/csrc/layer.hip"),
     ("decode_chunk_kernel", "decode", "learned_token_pruning_02_amd/csrc/decode.hip"),
     ("decode_merge_kernel", "decode", "learned_token_pruning_02_amd/csrc/decode.hip"),
 ]
