@@ -66,6 +66,7 @@ __all__ = [
     "swiglu",
     "kept_positions",
     "decoder_layer",
+    "gated_attention_backward",
 ]
 
 
@@ -423,3 +424,57 @@ def decoder_layer(x_kept: torch.Tensor, s_kept: torch.Tensor, pos: torch.Tensor,
     r["m"] = store(silu(r["g"]) * r["u"].double())
     r["out"] = store(r["h"].double() + linear(r["m"], L["wd"]))
     return r
+
+
+# --------------------------------------------------------------------------
+# Backward of the token-gated attention (spke.com page, "Qu'est-ce que
+# l'attention gérée par des tokens ?": the score bias is what carries a
+# gradient back to the gate, since the top-K choice itself has none).  With
+# l_ij = tau_h r_ij + g_h s_j, r_ij = (q_i . k_j) / sqrt(dh), P = softmax_j l,
+# O_i = sum_j P_ij v_j and an upstream gradient dO:
+#   D_i = dO_i . O_i,  dP_ij = dO_i . v_j,  dL_ij = P_ij (dP_ij - D_i)
+#   dq_i = tau_h / sqrt(dh) sum_j dL_ij k_j,   dk_j = tau_h / sqrt(dh) sum_i dL_ij q_i
+#   dv_j = sum_i P_ij dO_i,   ds_j = sum_h g_h sum_i dL_ij
+#   dg_h = sum_ij dL_ij s_j,  dtau_h = sum_ij dL_ij r_ij
+# (GQA: a KV head collects dk, dv from every query head of its group.)
+# --------------------------------------------------------------------------
+def gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                             s_kept: torch.Tensor, gain: torch.Tensor, temp: torch.Tensor,
+                             cu_kept: Sequence[int], dout: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """Gradients of sum(dout * gated_attention(...).out) w.r.t. q, k, v,
+    s_kept, gain and temp, float64."""
+    Kt, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    out, lse = gated_attention(q, k, v, s_kept, gain, temp, cu_kept)
+    g = {"dq": torch.zeros(Kt, Hq, dh, dtype=torch.float64),
+         "dk": torch.zeros(Kt, Hkv, dh, dtype=torch.float64),
+         "dv": torch.zeros(Kt, Hkv, dh, dtype=torch.float64),
+         "ds": torch.zeros(Kt, dtype=torch.float64),
+         "dgain": torch.zeros(Hq, dtype=torch.float64),
+         "dtemp": torch.zeros(Hq, dtype=torch.float64)}
+    s64 = s_kept.double()
+    scale = 1.0 / math.sqrt(dh)
+    for b in range(len(cu_kept) - 1):
+        lo, hi = int(cu_kept[b]), int(cu_kept[b + 1])
+        n = hi - lo
+        if n == 0:
+            continue
+        future = torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1)
+        for h in range(Hq):
+            kv = h // group
+            Q, Kb, V = q[lo:hi, h].double(), k[lo:hi, kv].double(), v[lo:hi, kv].double()
+            dO, O = dout[lo:hi, h].double(), out[lo:hi, h]
+            r = (Q @ Kb.t()) * scale
+            P = torch.exp(float(temp[h]) * r + float(gain[h]) * s64[lo:hi][None, :] - lse[h, lo:hi][:, None])
+            P = P.masked_fill(future, 0.0)
+            D = (dO * O).sum(dim=1)
+            dL = P * (dO @ V.t() - D[:, None])
+            g["dq"][lo:hi, h] = float(temp[h]) * scale * (dL @ Kb)
+            g["dk"][lo:hi, kv] += float(temp[h]) * scale * (dL.t() @ Q)
+            g["dv"][lo:hi, kv] += P.t() @ dO
+            col = dL.sum(dim=0)
+            g["ds"][lo:hi] += float(gain[h]) * col
+            g["dgain"][h] += (col * s64[lo:hi]).sum()
+            g["dtemp"][h] += (dL * r).sum()
+    return g

@@ -602,3 +602,62 @@ def test_decoder_layer_matches_independent_composition():
     hn = F.rms_norm(h, (d,), weight=L["post_norm"], eps=eps)
     want = h + F.linear(F.silu(F.linear(hn, L["wg"])) * F.linear(hn, L["wu"]), L["wd"])
     torch.testing.assert_close(got, want, rtol=1e-11, atol=1e-11)
+
+
+# -------------------------------------------------------- attention backward ----
+def _autograd_grads(q, k, v, s, gain, temp, cu, dout):
+    leaves = [t.clone().requires_grad_(True) for t in (q, k, v, s, gain, temp)]
+    out, _ = oracle.gated_attention(*leaves, cu)
+    (out * dout).sum().backward()
+    return dict(zip(["dq", "dk", "dv", "ds", "dgain", "dtemp"], [t.grad for t in leaves]))
+
+
+@pytest.mark.parametrize("seed,lens,Hq,Hkv", [(70, (5, 17, 33), 4, 2), (71, (1, 40), 6, 2), (72, (24,), 3, 3)])
+def test_attention_backward_matches_autograd(seed, lens, Hq, Hkv):
+    """Autograd through the forward definition (gated_attention is built from
+    differentiable float64 torch ops) against the hand-derived backward."""
+    q, k, v, s, gain, temp, cu = _attn_case(seed, lens=lens, Hq=Hq, Hkv=Hkv)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(seed + 100), dtype=torch.float64)
+    got = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, dout)
+    want = _autograd_grads(q, k, v, s, gain, temp, cu, dout)
+    for name in want:
+        torch.testing.assert_close(got[name], want[name], rtol=1e-10, atol=1e-11, msg=name)
+
+
+def test_attention_backward_finite_differences():
+    """Central differences of L = sum(dout * out) for a few entries of every
+    input, independent of any autograd."""
+    q, k, v, s, gain, temp, cu = _attn_case(73, lens=(9, 14), Hq=4, Hkv=2, dh=8)
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(173), dtype=torch.float64)
+    got = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, dout)
+    args = dict(q=q, k=k, v=v, s=s, gain=gain, temp=temp)
+
+    def loss(**kw):
+        a = dict(args, **kw)
+        out, _ = oracle.gated_attention(a["q"], a["k"], a["v"], a["s"], a["gain"], a["temp"], cu)
+        return float((out * dout).sum())
+
+    eps = 1e-6
+    picks = {"q": [(3, 1, 2), (20, 3, 7)], "k": [(0, 0, 0), (12, 1, 5)], "v": [(8, 1, 3), (22, 0, 6)],
+             "s": [(0,), (4,), (15,)], "gain": [(0,), (3,)], "temp": [(1,), (2,)]}
+    for name, idxs in picks.items():
+        for idx in idxs:
+            plus, minus = args[name].clone(), args[name].clone()
+            plus[idx] += eps
+            minus[idx] -= eps
+            fd = (loss(**{name: plus}) - loss(**{name: minus})) / (2 * eps)
+            key = "d" + name
+            assert abs(fd - float(got[key][idx])) < 1e-6 * max(1.0, abs(fd)), (name, idx, fd, float(got[key][idx]))
+
+
+def test_attention_backward_special_cases():
+    q, k, v, s, gain, temp, cu = _attn_case(74, lens=(10,))
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(174), dtype=torch.float64)
+    g0 = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, dout)
+    # row 0 attends only to key 0: its softmax is constant, so it sends no gradient to q_0
+    assert float(g0["dq"][0].abs().max()) < 1e-14
+    # shifting every score leaves the output unchanged: the score gradients sum to zero
+    assert abs(float(g0["ds"].sum())) < 1e-12
+    # dout = 0 gives zero gradients everywhere
+    gz = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, torch.zeros_like(dout))
+    assert all(float(t.abs().max()) == 0.0 for t in gz.values())
