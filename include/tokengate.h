@@ -231,6 +231,48 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void *q, const void *k, const
                                 int32_t Hkv, int32_t d_head, void *out, float *lse,
                                 hipStream_t stream);
 
+/*
+ * tg_attn_backward_plan -- workspace bytes of tg_gated_attn_backward for this
+ * packed batch (cu_kept_host as for tg_gated_attn_prefill).  Errors:
+ * TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE (batch, heads, cu_kept_host).
+ */
+tg_status tg_attn_backward_plan(const int32_t *cu_kept_host, int32_t batch, int32_t Hq,
+                                int32_t Hkv, size_t *ws_bytes);
+
+/*
+ * tg_gated_attn_backward -- gradients of the token-gated attention.  The
+ * score bias is the path by which the gate receives a gradient (spke.com
+ * page, "Qu'est-ce que l'attention gérée par des tokens ?"; the top-K choice
+ * itself has none).  For the forward of tg_gated_attn_prefill on the same
+ * inputs, with out and lse as it returned them and an upstream gradient dout
+ * of the loss with respect to out, with l_ij = temp[h] r_ij + gain[h] s_j,
+ * r_ij = q_i.k_j / sqrt(d_head), P = softmax_j(l), D_i = dout_i . out_i,
+ * dL_ij = P_ij (dout_i . v_j - D_i):
+ *     dq_i = temp[h]/sqrt(d_head) sum_j dL_ij k_j
+ *     dk_j = sum_h temp[h]/sqrt(d_head) sum_i dL_ij q_i     (h over the group)
+ *     dv_j = sum_h sum_i P_ij dout_i
+ *     ds_j = sum_h gain[h] sum_i dL_ij,  dgain[h] = sum_ij dL_ij s_j,
+ *     dtemp[h] = sum_ij dL_ij r_ij
+ * Layouts as in tg_gated_attn_prefill: q, out, dout, dq [Kt][Hq][d_head];
+ * k, v, dk, dv [Kt][Hkv][d_head]; lse [Hq][Kt] fp32; s_kept, ds [Kt] fp32;
+ * gain, temp, dgain, dtemp [Hq] fp32.  s_kept, gain, ds and dgain are all
+ * NULL (no bias term) or all non-NULL.  Every gradient is overwritten.
+ * ws: tg_attn_backward_plan bytes, caller-owned, 16-byte aligned, no
+ * initialisation needed.  Deterministic: no floating-point atomics.
+ * Supported: TG_BF16 only, d_head in {64, 128}, Hq % Hkv == 0, per-request
+ * K/V spans below 2 GiB; else TG_ERR_UNSUPPORTED.
+ * Errors: TG_ERR_BAD_DTYPE, TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE,
+ * TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT, TG_ERR_WORKSPACE, TG_ERR_ALIAS,
+ * TG_ERR_LAUNCH.
+ */
+tg_status tg_gated_attn_backward(tg_dtype dt, const void *q, const void *k, const void *v,
+                                 const float *s_kept, const float *gain, const float *temp,
+                                 const void *out, const float *lse, const void *dout,
+                                 const int32_t *cu_kept_host, int32_t batch, int32_t Hq,
+                                 int32_t Hkv, int32_t d_head, void *dq, void *dk, void *dv,
+                                 float *ds, float *dgain, float *dtemp, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
 /* Cached rows per split of tg_gated_attn_decode; its workspace is sized in
  * these. */
 #define TG_DECODE_CHUNK 128

@@ -32,6 +32,8 @@ __all__ = [
     "tg_topk_select",
     "tg_gather_compact",
     "tg_gated_attn_prefill",
+    "tg_attn_backward_plan",
+    "tg_gated_attn_backward",
     "tg_decode_plan",
     "tg_gated_attn_decode",
     "tg_rmsnorm",
@@ -118,6 +120,11 @@ def lib() -> ctypes.CDLL:
     L.tg_gated_attn_prefill.restype = ctypes.c_int
     L.tg_gated_attn_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, p_i32, i32, i32,
                                         i32, i32, vp, vp, vp]
+    L.tg_attn_backward_plan.restype = ctypes.c_int
+    L.tg_attn_backward_plan.argtypes = [p_i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.tg_gated_attn_backward.restype = ctypes.c_int
+    L.tg_gated_attn_backward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, p_i32, i32,
+                                         i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.tg_decode_plan.restype = ctypes.c_int
     L.tg_decode_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
     L.tg_gated_attn_decode.restype = ctypes.c_int
@@ -289,6 +296,45 @@ def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], o
         len(cu_kept) - 1, Hq, Hkv, dh, _dev(out, "out", q.dtype),
         _dev(lse, "lse", torch.float32), _stream(stream)))
     return out, lse
+
+
+def tg_attn_backward_plan(cu_kept: Sequence[int], Hq: int, Hkv: int) -> int:
+    """Workspace bytes of tg_gated_attn_backward."""
+    ws = ctypes.c_size_t(0)
+    cu = _i32_array(cu_kept)
+    _check("tg_attn_backward_plan", lib().tg_attn_backward_plan(
+        ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)), len(cu_kept) - 1, Hq, Hkv, ctypes.byref(ws)))
+    return ws.value
+
+
+def tg_gated_attn_backward(q, k, v, s_kept, gain, temp, out, lse, dout, cu_kept: Sequence[int],
+                           grads=None, workspace=None, stream=None):
+    """Gradients of the token-gated attention; returns a dict with dq, dk, dv
+    (bf16) and ds, dgain (fp32; None without the bias) and dtemp (fp32)."""
+    torch = _torch()
+    Kt, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=q.device)
+        grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+                 "ds": torch.empty(Kt, **f32) if s_kept is not None else None,
+                 "dgain": torch.empty(Hq, **f32) if s_kept is not None else None,
+                 "dtemp": torch.empty(Hq, **f32)}
+    if workspace is None:
+        workspace = torch.empty(tg_attn_backward_plan(cu_kept, Hq, Hkv), dtype=torch.uint8,
+                                device=q.device)
+    cu = _i32_array(cu_kept)
+    f32t = torch.float32
+    _check("tg_gated_attn_backward", lib().tg_gated_attn_backward(
+        _dt(q), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+        _dev(s_kept, "s_kept", f32t), _dev(gain, "gain", f32t), _dev(temp, "temp", f32t),
+        _dev(out, "out", q.dtype), _dev(lse, "lse", f32t), _dev(dout, "dout", q.dtype),
+        ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)), len(cu_kept) - 1, Hq, Hkv, dh,
+        _dev(grads["dq"], "dq", q.dtype), _dev(grads["dk"], "dk", q.dtype),
+        _dev(grads["dv"], "dv", q.dtype), _dev(grads["ds"], "ds", f32t),
+        _dev(grads["dgain"], "dgain", f32t), _dev(grads["dtemp"], "dtemp", f32t),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return grads
 
 
 def tg_decode_plan(batch: int, Hq: int, d_head: int, max_len: int) -> int:

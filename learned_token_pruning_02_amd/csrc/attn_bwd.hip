@@ -1,0 +1,443 @@
+// Backward of the token-gated attention: gradients with respect to q, k, v,
+// the kept tokens' scores s_j, the per-head gains g_h and temperatures tau_h.
+//
+// The score bias is the only path by which the gate receives a gradient
+// (spke.com page, "Qu'est-ce que l'attention gérée par des tokens ?"; the
+// top-K choice has none).  With l_ij = tau_h r_ij + g_h s_j,
+// r_ij = q_i.k_j / sqrt(dh), P = softmax_j(l), the forward's lse and output O:
+//   D_i = dO_i . O_i,   dP_ij = dO_i . v_j,   dL_ij = P_ij (dP_ij - D_i)
+//   dq_i = tau/sqrt(dh) sum_j dL_ij k_j,  dk_j = sum_h tau_h/sqrt(dh) sum_i dL_ij q_i
+//   dv_j = sum_h sum_i P_ij dO_i,         ds_j = sum_h g_h sum_i dL_ij
+//   dg_h = sum_ij dL_ij s_j,              dtau_h = sum_ij dL_ij r_ij
+//
+// Two deterministic MFMA passes (no floating-point atomics):
+//   * KV-major: a wave owns 32 keys of one KV head and walks the query blocks
+//     of every query head in its group.  S = Q K^T and dP = dO V^T come out
+//     with lane = key; their fp32 registers, rounded to bf16, are used
+//     directly as the B operand of dK^T += Q^T dS and dV^T += dO^T P (the
+//     contraction over queries runs in the C-register order, and the A
+//     operand -- Q^T and dO^T staged transposed in LDS -- is read in that
+//     same order).  Column sums of dL give the score gradient per KV head;
+//     gain and temperature sums are left per wave.
+//   * Q-major: a wave owns 32 queries of one head and walks the key blocks;
+//     S^T = K Q^T and dP^T = V dO^T come out with lane = query and feed
+//     dQ^T += K^T dS^T the same way (K^T staged in LDS).
+// A small kernel then sums the per-KV-head score gradients and the per-wave
+// gain/temperature partials in a fixed order.  P and dL enter the matrix
+// cores rounded to bf16; everything else accumulates in fp32.
+
+#include <algorithm>
+
+#include "tg_device.h"
+#include "tg_kernels.h"
+
+namespace tg {
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int BW = 4;            // waves per workgroup
+constexpr int BT = BW * WAVE;
+constexpr int TB = 32;           // rows per wave (keys or queries) and per tile
+constexpr int TPAD = TB + 4;     // transposed tile row: 32 rows + pad, 8-byte aligned
+
+struct BwdArgs {
+    const bf16* q;      // [Kt][Hq][DH]
+    const bf16* k;      // [Kt][Hkv][DH]
+    const bf16* v;
+    const float* s;     // [Kt] or null
+    const float* gain;  // [Hq] or null
+    const float* temp;  // [Hq]
+    const bf16* out;    // [Kt][Hq][DH]
+    const float* lse;   // [Hq][Kt]
+    const bf16* dout;   // [Kt][Hq][DH]
+    bf16* dq;
+    bf16* dk;
+    bf16* dv;
+    float* ds;          // [Kt] or null
+    float* dgain;       // [Hq] or null
+    float* dtemp;       // [Hq]
+    float* D;           // ws: [Hq][Kt]
+    float* ds_part;     // ws: [Hkv][Kt]
+    float* gt_part;     // ws: [batch][nkb][Hkv][BW][G][2]
+    int64_t Kt;
+    int32_t Hq, Hkv, G;
+    int32_t nkb;        // key blocks of BW*TB per request (grid.x of the KV pass)
+    int32_t batch;
+    float inv_sqrt_dh;
+    int32_t cu[TG_MAX_BATCH + 1];
+};
+
+__device__ __forceinline__ bf16x8 pack8(const float* f) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (bf16)f[e];
+    return r;
+}
+
+// Row l%32 of a row-major tile as an MFMA operand: k-step t covers elements
+// [16t, 16t+16) of the row, this lane holds 8 of them.  Rows past `rows`
+// read as zero.
+template <int DH>
+__device__ __forceinline__ void load_rows(const bf16* base, int64_t row_stride, int row, int rows,
+                                          int lane, u32x4 (&r)[DH / 16]) {
+    const bool ok = row < rows;
+    const bf16* p = base + (int64_t)(ok ? row : 0) * row_stride + 8 * (lane / 32);
+#pragma unroll
+    for (int t = 0; t < DH / 16; ++t) r[t] = ok ? ld16(p + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// A operand read from a transposed LDS tile T[dh][TPAD] for the contraction
+// over its 32 columns in the C-register order of k-block c: slots 0..3 are
+// columns 16c + 4*(lane/32) + 0..3, slots 4..7 are 16c + 8 + 4*(lane/32) + 0..3.
+__device__ __forceinline__ bf16x8 lds_t_operand(const bf16* T, int dh_row, int c, int lane) {
+    const bf16* p = T + dh_row * TPAD + 16 * c + 4 * (lane / 32);
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
+    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Stage rows [r0, r0+32) of a [rows][stride] bf16 matrix (DH columns from
+// `col0`) transposed into T[DH][TPAD]; rows past `rows` become zero.
+template <int DH>
+__device__ __forceinline__ void stage_transposed(bf16* T, const bf16* base, int64_t stride, int r0,
+                                                 int rows, int tid) {
+    constexpr int SEGS = DH / 8;            // 16-byte segments per row
+    for (int i = tid; i < TB * SEGS; i += BT) {
+        const int r = i % TB, seg = i / TB;
+        const int row = r0 + r;
+        u32x4 u = u32x4{0u, 0u, 0u, 0u};
+        if (row < rows) u = ld16(base + (int64_t)row * stride + seg * 8);
+        const bf16x8 h = as_bf16x8(u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) T[(seg * 8 + e) * TPAD + r] = h[e];
+    }
+}
+
+// D[h][i] = dO_i . O_i over DH, one thread per (row, head).
+template <int DH>
+__global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= a.Kt * a.Hq) return;
+    const int64_t i = idx / a.Hq;
+    const int h = (int)(idx % a.Hq);
+    const bf16* o = a.out + (i * a.Hq + h) * DH;
+    const bf16* d = a.dout + (i * a.Hq + h) * DH;
+    float acc = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < DH; c += 8) {
+        const bf16x8 x = as_bf16x8(ld16(o + c)), y = as_bf16x8(ld16(d + c));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+    }
+    a.D[(int64_t)h * a.Kt + i] = acc;
+}
+
+// KV-major pass: dK, dV, score-gradient and gain/temperature partials.
+template <int DH>
+__global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
+    constexpr int KS = DH / 16;   // k-steps over the head dimension
+    constexpr int MT = DH / 32;   // 32-row output tiles over the head dimension
+    __shared__ __align__(16) bf16 QT[DH * TPAD];
+    __shared__ __align__(16) bf16 OT[DH * TPAD];
+    __shared__ float lse2[TB], Dq[TB];
+
+    const int kb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int lo = a.cu[b], n = a.cu[b + 1] - lo;
+    const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
+    const int col = lane % 32;
+    // This wave's own slot of gain/temperature partials: the G heads of its
+    // KV head, (dgain, dtemp) each.
+    float* gtp = a.gt_part + ((((int64_t)b * a.nkb + kb) * a.Hkv + kvh) * BW + w) * a.G * 2;
+    if (kb * BW * TB >= n) {  // uniform: no key of this block exists
+        for (int i = lane; i < a.G * 2; i += WAVE) gtp[i] = 0.0f;
+        return;
+    }
+    const int j0 = kb * BW * TB + w * TB;          // first key of this wave (request-local)
+    const bool wave_on = j0 < n;
+    const int key = j0 + col;
+    const bool key_ok = key < n;
+
+    u32x4 kr[KS], vr[KS];
+    load_rows<DH>(a.k + (int64_t)lo * a.Hkv * DH + kvh * DH, (int64_t)a.Hkv * DH, key, n, lane, kr);
+    load_rows<DH>(a.v + (int64_t)lo * a.Hkv * DH + kvh * DH, (int64_t)a.Hkv * DH, key, n, lane, vr);
+    const float s_key = (a.s != nullptr && key_ok) ? a.s[lo + key] : 0.0f;
+
+    f32x16 dkT[MT], dvT[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkT[m][r] = dvT[m][r] = 0.0f;
+    float ds_acc = 0.0f;
+
+    for (int g = 0; g < a.G; ++g) {
+        const int h = kvh * a.G + g;
+        const float tau = a.temp[h];
+        const float gn = a.gain != nullptr ? a.gain[h] : 0.0f;
+        const float c1 = tau * a.inv_sqrt_dh * LOG2E;
+        const float bias2 = gn * s_key * LOG2E;
+        const float kscale = tau * a.inv_sqrt_dh;
+        float dg_acc = 0.0f, dt_acc = 0.0f;
+        const bf16* qh = a.q + (int64_t)lo * a.Hq * DH + h * DH;
+        const bf16* oh = a.dout + (int64_t)lo * a.Hq * DH + h * DH;
+        for (int i0 = kb * BW * TB; i0 < n; i0 += TB) {
+            __syncthreads();  // previous tiles fully consumed
+            stage_transposed<DH>(QT, qh, (int64_t)a.Hq * DH, i0, n, tid);
+            stage_transposed<DH>(OT, oh, (int64_t)a.Hq * DH, i0, n, tid);
+            if (tid < TB) {
+                const bool ok = i0 + tid < n;
+                lse2[tid] = ok ? a.lse[(int64_t)h * a.Kt + lo + i0 + tid] * LOG2E : 0.0f;
+                Dq[tid] = ok ? a.D[(int64_t)h * a.Kt + lo + i0 + tid] : 0.0f;
+            }
+            __syncthreads();
+            if (!wave_on || i0 + TB - 1 < j0) continue;  // no query of this block sees these keys
+
+            u32x4 qa[KS], oa[KS];
+            load_rows<DH>(qh, (int64_t)a.Hq * DH, i0 + col, n, lane, qa);
+            load_rows<DH>(oh, (int64_t)a.Hq * DH, i0 + col, n, lane, oa);
+            f32x16 S, dP;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+                S = mfma32(as_bf16x8(qa[t]), as_bf16x8(kr[t]), S);
+                dP = mfma32(as_bf16x8(oa[t]), as_bf16x8(vr[t]), dP);
+            }
+            float P[16], dS[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qq = 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+                const int qi = i0 + qq;
+                const bool ok = key_ok && qi < n && qi >= key;
+                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[r], c1, bias2) - lse2[qq]) : 0.0f;
+                const float dl = p * (dP[r] - Dq[qq]);
+                P[r] = p;
+                dS[r] = dl * kscale;
+                ds_acc = fmaf(dl, gn, ds_acc);
+                dg_acc = fmaf(dl, s_key, dg_acc);
+                dt_acc = fmaf(dl, S[r] * a.inv_sqrt_dh, dt_acc);
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bf16x8 pb = pack8(P + 8 * c), sb = pack8(dS + 8 * c);
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    const int row = 32 * m + col;
+                    dvT[m] = mfma32(lds_t_operand(OT, row, c, lane), pb, dvT[m]);
+                    dkT[m] = mfma32(lds_t_operand(QT, row, c, lane), sb, dkT[m]);
+                }
+            }
+        }
+        dg_acc = wave_sum(dg_acc);
+        dt_acc = wave_sum(dt_acc);
+        if (lane == 0) {
+            gtp[2 * g] = dg_acc;
+            gtp[2 * g + 1] = dt_acc;
+        }
+    }
+    if (!wave_on) return;
+    ds_acc += __shfl_xor(ds_acc, 32, WAVE);
+    if (lane < 32 && key_ok && a.ds_part != nullptr) a.ds_part[(int64_t)kvh * a.Kt + lo + key] = ds_acc;
+    if (!key_ok) return;
+    bf16* dkp = a.dk + ((int64_t)(lo + key) * a.Hkv + kvh) * DH;
+    bf16* dvp = a.dv + ((int64_t)(lo + key) * a.Hkv + kvh) * DH;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * m + 8 * q4 + 4 * (lane / 32);
+            bf16x4 xk, xv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                xk[e] = (bf16)dkT[m][4 * q4 + e];
+                xv[e] = (bf16)dvT[m][4 * q4 + e];
+            }
+            st8(dkp + d0, __builtin_bit_cast(u32x2, xk));
+            st8(dvp + d0, __builtin_bit_cast(u32x2, xv));
+        }
+}
+
+// Q-major pass: dQ.
+template <int DH>
+__global__ __launch_bounds__(BT) void bwd_q_kernel(BwdArgs a) {
+    constexpr int KS = DH / 16;
+    constexpr int MT = DH / 32;
+    __shared__ __align__(16) bf16 KT[DH * TPAD];
+    __shared__ float sb2[TB];
+
+    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lo = a.cu[b], n = a.cu[b + 1] - lo;
+    if (qb * BW * TB >= n) return;
+    const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
+    const int col = lane % 32;
+    const int kvh = h / a.G;
+    const int i0 = qb * BW * TB + w * TB;
+    const bool wave_on = i0 < n;
+    const int qi = i0 + col;
+    const bool q_ok = qi < n;
+
+    u32x4 qr[KS], orr[KS];
+    load_rows<DH>(a.q + (int64_t)lo * a.Hq * DH + h * DH, (int64_t)a.Hq * DH, qi, n, lane, qr);
+    load_rows<DH>(a.dout + (int64_t)lo * a.Hq * DH + h * DH, (int64_t)a.Hq * DH, qi, n, lane, orr);
+    const float tau = a.temp[h];
+    const float gn = a.gain != nullptr ? a.gain[h] : 0.0f;
+    const float c1 = tau * a.inv_sqrt_dh * LOG2E;
+    const float lq = q_ok ? a.lse[(int64_t)h * a.Kt + lo + qi] * LOG2E : 0.0f;
+    const float Dv = q_ok ? a.D[(int64_t)h * a.Kt + lo + qi] : 0.0f;
+    const bf16* kh = a.k + (int64_t)lo * a.Hkv * DH + kvh * DH;
+    const bf16* vh = a.v + (int64_t)lo * a.Hkv * DH + kvh * DH;
+
+    f32x16 dqT[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dqT[m][r] = 0.0f;
+
+    const int jend = min(n, qb * BW * TB + BW * TB);
+    for (int j0 = 0; j0 < jend; j0 += TB) {
+        __syncthreads();
+        stage_transposed<DH>(KT, kh, (int64_t)a.Hkv * DH, j0, n, tid);
+        if (tid < TB) {
+            const bool ok = j0 + tid < n && a.s != nullptr;
+            sb2[tid] = ok ? gn * a.s[lo + j0 + tid] * LOG2E : 0.0f;
+        }
+        __syncthreads();
+        if (!wave_on || j0 > i0 + TB - 1) continue;
+
+        u32x4 ka[KS], va[KS];
+        load_rows<DH>(kh, (int64_t)a.Hkv * DH, j0 + col, n, lane, ka);
+        load_rows<DH>(vh, (int64_t)a.Hkv * DH, j0 + col, n, lane, va);
+        f32x16 S, dP;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            S = mfma32(as_bf16x8(ka[t]), as_bf16x8(qr[t]), S);
+            dP = mfma32(as_bf16x8(va[t]), as_bf16x8(orr[t]), dP);
+        }
+        float dS[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int kk = 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+            const int kj = j0 + kk;
+            const bool ok = q_ok && kj < n && qi >= kj;
+            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[r], c1, sb2[kk]) - lq) : 0.0f;
+            dS[r] = p * (dP[r] - Dv);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const bf16x8 sbv = pack8(dS + 8 * c);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                dqT[m] = mfma32(lds_t_operand(KT, 32 * m + col, c, lane), sbv, dqT[m]);
+        }
+    }
+    if (!q_ok) return;
+    const float qs = tau * a.inv_sqrt_dh;
+    bf16* dqp = a.dq + ((int64_t)(lo + qi) * a.Hq + h) * DH;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * m + 8 * q4 + 4 * (lane / 32);
+            bf16x4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (bf16)(dqT[m][4 * q4 + e] * qs);
+            st8(dqp + d0, __builtin_bit_cast(u32x2, x));
+        }
+}
+
+// ds[j] = sum over KV heads of the partial column sums; dgain, dtemp = sums of
+// the per-wave partials in a fixed order (block 0).
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a.ds != nullptr && j < a.Kt) {
+        float acc = 0.0f;
+        for (int kv = 0; kv < a.Hkv; ++kv) acc += a.ds_part[(int64_t)kv * a.Kt + j];
+        a.ds[j] = acc;
+    }
+    if (blockIdx.x == 0) {
+        const int64_t nblk = (int64_t)a.batch * a.nkb;
+        for (int hh = threadIdx.x; hh < 2 * a.Hq; hh += blockDim.x) {
+            const int h = hh / 2, kv = h / a.G, g = h % a.G;
+            float acc = 0.0f;
+            for (int64_t blk = 0; blk < nblk; ++blk)
+                for (int ww = 0; ww < BW; ++ww)
+                    acc += a.gt_part[((blk * a.Hkv + kv) * BW + ww) * a.G * 2 + 2 * g + hh % 2];
+            if (hh % 2 == 0) {
+                if (a.dgain != nullptr) a.dgain[h] = acc;
+            } else {
+                a.dtemp[h] = acc;
+            }
+        }
+    }
+}
+
+int key_blocks(const AttnShape& sh) {
+    int mx = 0;
+    for (int b = 0; b < sh.batch; ++b) mx = std::max(mx, sh.cu[b + 1] - sh.cu[b]);
+    return (mx + BW * TB - 1) / (BW * TB);
+}
+
+template <int DH>
+hipError_t launch_dh(BwdArgs& a, const AttnShape& sh, hipStream_t st) {
+    const int64_t rows = a.Kt * a.Hq;
+    hipLaunchKernelGGL(bwd_dot_kernel<DH>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_kv_kernel<DH>, dim3(a.nkb, a.Hkv, sh.batch), dim3(BT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_q_kernel<DH>, dim3(a.nkb, a.Hq, sh.batch), dim3(BT), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)std::max<int64_t>(1, (a.Kt + 255) / 256)),
+                       dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(const AttnShape& sh) {
+    const int64_t nkb = key_blocks(sh);
+    const auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    return (size_t)(up(sh.Kt * sh.Hq * 4) + up(sh.Kt * sh.Hkv * 4) +
+                    up((int64_t)sh.batch * nkb * BW * sh.Hq * 2 * 4));
+}
+
+hipError_t launch_attn_bwd(const AttnShape& sh, const void* q, const void* k, const void* v,
+                           const float* s, const float* gain, const float* temp, const void* out,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* ds, float* dgain, float* dtemp, void* ws, hipStream_t st) {
+    BwdArgs a;
+    a.q = (const bf16*)q;
+    a.k = (const bf16*)k;
+    a.v = (const bf16*)v;
+    a.s = s;
+    a.gain = gain;
+    a.temp = temp;
+    a.out = (const bf16*)out;
+    a.lse = lse;
+    a.dout = (const bf16*)dout;
+    a.dq = (bf16*)dq;
+    a.dk = (bf16*)dk;
+    a.dv = (bf16*)dv;
+    a.ds = ds;
+    a.dgain = dgain;
+    a.dtemp = dtemp;
+    a.Kt = sh.Kt;
+    a.Hq = sh.Hq;
+    a.Hkv = sh.Hkv;
+    a.G = sh.Hq / sh.Hkv;
+    a.nkb = key_blocks(sh);
+    a.batch = sh.batch;
+    a.inv_sqrt_dh = 1.0f / sqrtf((float)sh.d_head);
+    for (int i = 0; i <= sh.batch; ++i) a.cu[i] = sh.cu[i];
+    const auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    char* w = (char*)ws;
+    a.D = (float*)w;
+    w += up(sh.Kt * sh.Hq * 4);
+    a.ds_part = (float*)w;
+    w += up(sh.Kt * sh.Hkv * 4);
+    a.gt_part = (float*)w;
+    return sh.d_head == 128 ? launch_dh<128>(a, sh, st) : launch_dh<64>(a, sh, st);
+}
+
+}  // namespace tg

@@ -243,6 +243,83 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const
     return launched(tg::launch_attn_bf16(q, k, v, s_kept, gain, temp, sh, out, lse, stream));
 }
 
+namespace {
+tg_status attn_shape(const int32_t* cu_kept_host, int32_t batch, int32_t Hq, int32_t Hkv,
+                     int32_t d_head, tg::AttnShape* sh) {
+    if (cu_kept_host == nullptr) return TG_ERR_NULL_PTR;
+    if (batch < 1 || batch > TG_MAX_BATCH || Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+        return TG_ERR_BAD_SHAPE;
+    if (cu_kept_host[0] != 0) return TG_ERR_BAD_SHAPE;
+    sh->batch = batch;
+    sh->Hq = Hq;
+    sh->Hkv = Hkv;
+    sh->d_head = d_head;
+    for (int i = 0; i <= batch; ++i) {
+        if (i > 0 && cu_kept_host[i] < cu_kept_host[i - 1]) return TG_ERR_BAD_SHAPE;
+        sh->cu[i] = cu_kept_host[i];
+    }
+    sh->Kt = cu_kept_host[batch];
+    return TG_OK;
+}
+}  // namespace
+
+tg_status tg_attn_backward_plan(const int32_t* cu_kept_host, int32_t batch, int32_t Hq, int32_t Hkv,
+                                size_t* ws_bytes) {
+    if (ws_bytes == nullptr) return TG_ERR_NULL_PTR;
+    tg::AttnShape sh;
+    const tg_status st = attn_shape(cu_kept_host, batch, Hq, Hkv, 128, &sh);
+    if (st != TG_OK) return st;
+    *ws_bytes = tg::attn_bwd_workspace_bytes(sh);
+    return TG_OK;
+}
+
+tg_status tg_gated_attn_backward(tg_dtype dt, const void* q, const void* k, const void* v,
+                                 const float* s_kept, const float* gain, const float* temp,
+                                 const void* out, const float* lse, const void* dout,
+                                 const int32_t* cu_kept_host, int32_t batch, int32_t Hq,
+                                 int32_t Hkv, int32_t d_head, void* dq, void* dk, void* dv,
+                                 float* ds, float* dgain, float* dtemp, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (q == nullptr || k == nullptr || v == nullptr || temp == nullptr || out == nullptr ||
+        lse == nullptr || dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr ||
+        dtemp == nullptr)
+        return TG_ERR_NULL_PTR;
+    const bool bias = s_kept != nullptr;
+    if ((gain != nullptr) != bias || (ds != nullptr) != bias || (dgain != nullptr) != bias)
+        return TG_ERR_NULL_PTR;
+    tg::AttnShape sh;
+    const tg_status st = attn_shape(cu_kept_host, batch, Hq, Hkv, d_head, &sh);
+    if (st != TG_OK) return st;
+    if (dt != TG_BF16 || (d_head != 64 && d_head != 128)) return TG_ERR_UNSUPPORTED;
+    for (int i = 0; i < batch; ++i)
+        if ((int64_t)(cu_kept_host[i + 1] - cu_kept_host[i]) * Hq * d_head * 2 >= I32_LIMIT)
+            return TG_ERR_UNSUPPORTED;
+    const size_t need = tg::attn_bwd_workspace_bytes(sh);
+    if (ws == nullptr || ws_bytes < need) return TG_ERR_WORKSPACE;
+    const void* a16[] = {q, k, v, out, dout, dq, dk, dv, ws};
+    for (const void* p : a16)
+        if (!aligned16(p)) return TG_ERR_ALIGNMENT;
+    const void* a4[] = {s_kept, gain, temp, lse, ds, dgain, dtemp};
+    for (const void* p : a4)
+        if (p != nullptr && !aligned4(p)) return TG_ERR_ALIGNMENT;
+    const int64_t Kt = sh.Kt;
+    const int64_t qb = Kt * Hq * d_head * 2, kb = Kt * Hkv * d_head * 2;
+    const void* ins[] = {q, k, v, s_kept, gain, temp, out, lse, dout};
+    const int64_t inb[] = {qb, kb, kb, Kt * 4, Hq * 4, Hq * 4, qb, Kt * Hq * 4, qb};
+    void* outs[] = {dq, dk, dv, ds, dgain, dtemp, ws};
+    const int64_t outb[] = {qb, kb, kb, Kt * 4, Hq * 4, Hq * 4, (int64_t)need};
+    for (int o = 0; o < 7; ++o) {
+        for (int i = 0; i < 9; ++i)
+            if (overlap(outs[o], outb[o], ins[i], inb[i])) return TG_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < 7; ++o2)
+            if (overlap(outs[o], outb[o], outs[o2], outb[o2])) return TG_ERR_ALIAS;
+    }
+    if (Kt == 0) return TG_OK;
+    return launched(tg::launch_attn_bwd(sh, q, k, v, s_kept, gain, temp, out, lse, dout, dq, dk, dv,
+                                        ds, dgain, dtemp, ws, stream));
+}
+
 tg_status tg_decode_plan(int32_t batch, int32_t Hq, int32_t d_head, int32_t max_len,
                          size_t* ws_bytes) {
     if (ws_bytes == nullptr) return TG_ERR_NULL_PTR;

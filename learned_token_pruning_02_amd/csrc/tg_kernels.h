@@ -45,6 +45,12 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const f
                             const float* gain, const float* temp, const AttnShape& sh, void* out,
                             float* lse, hipStream_t st);
 
+size_t attn_bwd_workspace_bytes(const AttnShape& sh);
+hipError_t launch_attn_bwd(const AttnShape& sh, const void* q, const void* k, const void* v,
+                           const float* s, const float* gain, const float* temp, const void* out,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* ds, float* dgain, float* dtemp, void* ws, hipStream_t st);
+
 struct DecodeShape {
     int32_t batch;
     int32_t Hq, Hkv, d_head;

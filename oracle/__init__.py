@@ -440,13 +440,20 @@ def decoder_layer(x_kept: torch.Tensor, s_kept: torch.Tensor, pos: torch.Tensor,
 # --------------------------------------------------------------------------
 def gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                              s_kept: torch.Tensor, gain: torch.Tensor, temp: torch.Tensor,
-                             cu_kept: Sequence[int], dout: torch.Tensor) -> Dict[str, torch.Tensor]:
+                             cu_kept: Sequence[int], dout: torch.Tensor,
+                             out_stored: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """Gradients of sum(dout * gated_attention(...).out) w.r.t. q, k, v,
-    s_kept, gain and temp, float64."""
+    s_kept, gain and temp, float64.
+
+    out_stored: the forward output as a caller stored it (for instance in
+    bf16); D_i = dO_i . O_i is then evaluated on it, as an entry point that
+    takes the stored output does.  None uses the exact output."""
     Kt, Hq, dh = q.shape
     Hkv = k.shape[1]
     group = Hq // Hkv
     out, lse = gated_attention(q, k, v, s_kept, gain, temp, cu_kept)
+    if out_stored is not None:
+        out = out_stored.double()
     g = {"dq": torch.zeros(Kt, Hq, dh, dtype=torch.float64),
          "dk": torch.zeros(Kt, Hkv, dh, dtype=torch.float64),
          "dv": torch.zeros(Kt, Hkv, dh, dtype=torch.float64),

@@ -308,6 +308,42 @@ def test_layer_piece_validation():
     assert kp(A + 2, cs_p, ck_p, 2, B, None) == 6 and kp(A, cs_p, ck_p, 2, A + 8, None) == 9
 
 
+def test_attention_backward_validation():
+    L = tg.lib()
+    cu = tg._i32_array([0, 100])
+    P = ctypes.POINTER(ctypes.c_int32)
+    cu_p = ctypes.cast(cu, P)
+    ws = ctypes.c_size_t(0)
+    assert L.tg_attn_backward_plan(cu_p, 1, 16, 8, ctypes.byref(ws)) == 0 and ws.value > 0
+    assert L.tg_attn_backward_plan(cu_p, 1, 12, 8, ctypes.byref(ws)) == 2
+    assert L.tg_attn_backward_plan(None, 1, 16, 8, ctypes.byref(ws)) == 1
+    W = 64 << 20
+    X = [(9 + i) << 20 for i in range(8)]  # q k v out dout dq dk dv regions
+    small = [(20 << 20) + 4096 * i for i in range(8)]  # s gain temp lse ds dgain dtemp
+    ok = [1, X[0], X[1], X[2], small[0], small[1], small[2], X[3], small[3], X[4], cu_p, 1, 16, 8,
+          128, X[5], X[6], X[7], small[4], small[5], small[6], W, ws.value, None]
+    names = ["dt", "q", "k", "v", "s", "gain", "temp", "out", "lse", "dout", "cu", "batch", "Hq",
+             "Hkv", "dh", "dq", "dk", "dv", "ds", "dgain", "dtemp", "ws", "wsb", "st"]
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return L.tg_gated_attn_backward(*args)
+
+    assert call(dt=4) == 4
+    for nm in ("q", "k", "v", "temp", "out", "lse", "dout", "dq", "dk", "dv", "dtemp", "cu"):
+        assert call(**{nm: None}) == 1, nm
+    assert call(s=None) == 1 and call(ds=None) == 1 and call(dgain=None) == 1   # bias set all or none
+    assert call(batch=0) == 2 and call(Hq=12) == 2
+    assert call(dt=0) == 5 and call(dh=96) == 5                                  # fp32, d_head
+    assert call(ws=None) == 7 and call(wsb=ws.value - 1) == 7
+    assert call(q=X[0] + 8) == 6 and call(ws=W + 8) == 6 and call(lse=small[3] + 2) == 6
+    assert call(dq=X[0]) == 9 and call(dk=X[5]) == 9 and call(ws=X[2]) == 9 and call(ds=small[0]) == 9
+    zero = tg._i32_array([0, 0])
+    assert call(cu=ctypes.cast(zero, P)) == 0                                    # no rows: no-op
+
+
 def test_linear_validation():
     L = tg.lib()
     f = L.tg_linear

@@ -661,3 +661,17 @@ def test_attention_backward_special_cases():
     # dout = 0 gives zero gradients everywhere
     gz = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, torch.zeros_like(dout))
     assert all(float(t.abs().max()) == 0.0 for t in gz.values())
+
+
+def test_attention_backward_stored_output():
+    """Given the exact output as the stored one, nothing changes; given a
+    perturbed one, only the D_i term moves: dv is untouched."""
+    q, k, v, s, gain, temp, cu = _attn_case(75, lens=(7, 12))
+    dout = torch.randn(q.shape, generator=torch.Generator().manual_seed(175), dtype=torch.float64)
+    out, _ = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    a = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, dout)
+    b = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, dout, out_stored=out)
+    for n in a:
+        assert torch.equal(a[n], b[n]), n
+    c = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, dout, out_stored=out * 1.01)
+    assert torch.equal(c["dv"], a["dv"]) and not torch.equal(c["dq"], a["dq"])
