@@ -48,6 +48,8 @@ def parse():
                    help="only time the selector on T = 2^20 .. 2^26 random scores, K = T/16")
     p.add_argument("--layer", action="store_true",
                    help="only time one whole decoder layer on the 8192 kept rows of the 128k prompt")
+    p.add_argument("--backward", action="store_true",
+                   help="only time the token-gated attention backward on the 8192 kept rows of the 128k prompt")
     p.add_argument("--decode", action="store_true",
                    help="only time one decode step over kept-only KV caches (32 requests x 8193 rows)")
     return p.parse_args()
@@ -186,6 +188,81 @@ def cpu_baseline(w, gi, ai, s_gpu, kept, cu):
                    "each part scaled to the whole layer"),
         "seconds_scaled": {"gate": t_gate, "select": t_sel, "gather": t_gath, "attention": t_attn},
     }
+
+
+def backward_bench(args):
+    """The token-gated attention backward (all four kernels of one call) on
+    the 8192 kept rows of the 128k prompt, Qwen3-1.7B heads.  Algorithmic
+    work: the five matrix products of an attention backward (S, dP, dV, dK,
+    dQ), 2.5 times the forward's FLOPs; this implementation also recomputes
+    S and dP in its dQ pass, which the rate does not credit."""
+    import torch
+
+    import learned_token_pruning_02_amd as tg
+    import workloads
+
+    w = workloads.WORKLOADS["qwen3_1p7b_128k_niah"]
+    sh = w.shape
+    a = {k: v.cuda() for k, v in workloads.attn_inputs(w, seed=args.seed).items()}
+    Kt = w.total_kept
+    cu = [0, Kt]
+    s = workloads.random_scores(Kt, seed=args.seed + 2).cuda()
+    g = torch.Generator(device="cuda").manual_seed(args.seed + 3)
+    dout = torch.randn(Kt, sh.n_q_heads, sh.d_head, device="cuda", generator=g).to(sh.dtype)
+    out, lse = tg.tg_gated_attn_prefill(a["q"], a["k"], a["v"], s, a["gain"], a["temp"], cu, want_lse=True)
+    ws = torch.empty(tg.tg_attn_backward_plan(cu, sh.n_q_heads, sh.n_kv_heads), dtype=torch.uint8,
+                     device="cuda")
+    grads = {"dq": torch.empty_like(a["q"]), "dk": torch.empty_like(a["k"]), "dv": torch.empty_like(a["v"]),
+             "ds": torch.empty(Kt, device="cuda"), "dgain": torch.empty(sh.n_q_heads, device="cuda"),
+             "dtemp": torch.empty(sh.n_q_heads, device="cuda")}
+    st = torch.cuda.current_stream()
+
+    def call():
+        tg.tg_gated_attn_backward(a["q"], a["k"], a["v"], s, a["gain"], a["temp"], out, lse, dout, cu,
+                                  grads=grads, workspace=ws, stream=st)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(st)
+    for i in range(args.steps):
+        call()
+        ev[i + 1].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    mean = sum(ms) / len(ms)
+    flops = 2.5 * 4 * sh.d_head * sh.n_q_heads * Kt * (Kt + 1) // 2
+    tf = flops / (mean * 1e-3) / 1e12
+    rec = {
+        "metric": "gated attention backward tokens/s (context tokens per layer)",
+        "value": w.total_tokens / (mean * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded)",
+        "config": {"workload": "qwen3_1p7b_128k_backward", "tokens": w.total_tokens, "kept": Kt,
+                   "heads_q": sh.n_q_heads, "heads_kv": sh.n_kv_heads, "d_head": sh.d_head},
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "attention backward (dot, KV pass, Q pass, reduce; one call)",
+                     "algorithmic_flops_per_call": flops},
+        "ms_call": {"mean": mean, "median": sorted(ms)[len(ms) // 2], "min": min(ms)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        n_cpu = 2048
+        qc, kc, vc = (a[x][:n_cpu, :2].cpu().contiguous() if x == "q" else a[x][:n_cpu, :1].cpu().contiguous()
+                      for x in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        oracle.gated_attention_backward(qc, kc, vc, s[:n_cpu].cpu(), a["gain"][:2].cpu(), a["temp"][:2].cpu(),
+                                        [0, n_cpu], dout[:n_cpu, :2].cpu())
+        t = (time.perf_counter() - t0) * (sh.n_q_heads / 2) * (Kt / n_cpu) ** 2
+        rec["cpu_baseline"] = {"value": w.total_tokens / t, "unit": "tokens/s",
+                               "cores": torch.get_num_threads(), "kind": "oracle",
+                               "sample": (f"oracle backward for 2 of {sh.n_q_heads} heads on the first "
+                                          f"{n_cpu} of {Kt} kept rows, scaled by heads and (rows)^2")}
+    print(json.dumps(rec), flush=True)
 
 
 def decode_bench(args):
@@ -377,6 +454,12 @@ def main():
             print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
             sys.exit(2)
         layer_bench(args)
+        return
+    if args.backward:
+        if args.gpus != 1:
+            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
+            sys.exit(2)
+        backward_bench(args)
         return
     if args.decode:
         if args.gpus != 1:

@@ -32,6 +32,13 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source additions.  The attention backward keeps loop-carried MFMA
+# accumulators in plain VGPRs (its KV pass needs more than 256 registers, and
+# without this the compiler copies accumulators between the VGPR and AGPR files
+# on every iteration).
+EXTRA_FLAGS = {"attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -60,8 +67,8 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([hipcc, *HIPCC_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *lang, "-c",
-                     os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), f"-I{INCLUDE}", f"-I{CSRC}",
+                     *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"

@@ -96,23 +96,6 @@ __device__ __forceinline__ bf16x8 lds_t_operand(const bf16* T, int dh_row, int c
     return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// Stage rows [r0, r0+32) of a [rows][stride] bf16 matrix (DH columns from
-// `col0`) transposed into T[DH][TPAD]; rows past `rows` become zero.
-template <int DH>
-__device__ __forceinline__ void stage_transposed(bf16* T, const bf16* base, int64_t stride, int r0,
-                                                 int rows, int tid) {
-    constexpr int SEGS = DH / 8;            // 16-byte segments per row
-    for (int i = tid; i < TB * SEGS; i += BT) {
-        const int r = i % TB, seg = i / TB;
-        const int row = r0 + r;
-        u32x4 u = u32x4{0u, 0u, 0u, 0u};
-        if (row < rows) u = ld16(base + (int64_t)row * stride + seg * 8);
-        const bf16x8 h = as_bf16x8(u);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) T[(seg * 8 + e) * TPAD + r] = h[e];
-    }
-}
-
 // D[h][i] = dO_i . O_i over DH, one thread per (row, head).
 template <int DH>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
@@ -132,14 +115,61 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
     a.D[(int64_t)h * a.Kt + i] = acc;
 }
 
-// KV-major pass: dK, dV, score-gradient and gain/temperature partials.
+// Staging of two 32-row tiles (`mats` row-major [rows][stride] bf16
+// matrices, DH columns each) for one pipeline step: every thread fetches
+// PER 16-byte segments into registers, then writes them into an LDS buffer,
+// row-major (padded rows, for row-form operands) and, for the first
+// `ntrans` matrices, transposed (for operands that contract over the rows).
+template <int DH>
+struct TileStage {
+    static constexpr int SEGS = DH / 8;
+    static constexpr int RP = DH + 8;               // padded row-major row (bf16)
+    static constexpr int PER = 2 * TB * SEGS / BT;  // segments per thread
+    u32x4 r[PER];
+
+    __device__ __forceinline__ void fetch(const bf16* m0, const bf16* m1, int64_t stride, int row0,
+                                          int rows, int tid) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = tid + BT * u;
+            const int mat = idx / (TB * SEGS), rem = idx % (TB * SEGS);
+            const int rr = rem % TB, seg = rem / TB;
+            const int row = row0 + rr;
+            const bf16* base = mat == 0 ? m0 : m1;
+            r[u] = row < rows ? ld16(base + (int64_t)row * stride + seg * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    // rm: [2][TB*RP] row-major tiles; tr: [ntrans][DH*TPAD] transposed tiles
+    __device__ __forceinline__ void put(bf16* rm, bf16* tr, int ntrans, int tid) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int idx = tid + BT * u;
+            const int mat = idx / (TB * SEGS), rem = idx % (TB * SEGS);
+            const int rr = rem % TB, seg = rem / TB;
+            st16(rm + mat * TB * RP + rr * RP + seg * 8, r[u]);
+            if (mat < ntrans) {
+                const bf16x8 hv = as_bf16x8(r[u]);
+                bf16* t = tr + mat * DH * TPAD + seg * 8 * TPAD + rr;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) t[e * TPAD] = hv[e];
+            }
+        }
+    }
+};
+
+// KV-major pass: dK, dV, score-gradient and gain/temperature partials.  The
+// workgroup walks (query head of the group, 32-query block) pairs; the Q and
+// dO tiles of the next pair are fetched into registers while the current
+// pair is computed from the other LDS buffer (one barrier per step).
 template <int DH>
 __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
     constexpr int KS = DH / 16;   // k-steps over the head dimension
     constexpr int MT = DH / 32;   // 32-row output tiles over the head dimension
-    __shared__ __align__(16) bf16 QT[DH * TPAD];
-    __shared__ __align__(16) bf16 OT[DH * TPAD];
-    __shared__ float lse2[TB], Dq[TB];
+    using Stage = TileStage<DH>;
+    constexpr int RP = Stage::RP;
+    __shared__ __align__(16) bf16 Rm[2][2 * TB * RP];     // [buffer] Q | dO, row-major
+    __shared__ __align__(16) bf16 Tr[2][2 * DH * TPAD];   // [buffer] Q^T | dO^T
+    __shared__ float lse2[2][TB], Dq[2][TB];
 
     const int kb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int lo = a.cu[b], n = a.cu[b + 1] - lo;
@@ -148,11 +178,12 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
     // This wave's own slot of gain/temperature partials: the G heads of its
     // KV head, (dgain, dtemp) each.
     float* gtp = a.gt_part + ((((int64_t)b * a.nkb + kb) * a.Hkv + kvh) * BW + w) * a.G * 2;
-    if (kb * BW * TB >= n) {  // uniform: no key of this block exists
+    const int q0 = kb * BW * TB;
+    if (q0 >= n) {  // uniform: no key of this block exists
         for (int i = lane; i < a.G * 2; i += WAVE) gtp[i] = 0.0f;
         return;
     }
-    const int j0 = kb * BW * TB + w * TB;          // first key of this wave (request-local)
+    const int j0 = q0 + w * TB;                    // first key of this wave (request-local)
     const bool wave_on = j0 < n;
     const int key = j0 + col;
     const bool key_ok = key < n;
@@ -167,40 +198,52 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dkT[m][r] = dvT[m][r] = 0.0f;
-    float ds_acc = 0.0f;
+    float ds_acc = 0.0f, dg_acc = 0.0f, dt_acc = 0.0f;
 
-    for (int g = 0; g < a.G; ++g) {
+    const int nqb = (n - q0 + TB - 1) / TB;       // query blocks from the block's first key
+    const int iters = a.G * nqb;
+    const int64_t hs = (int64_t)a.Hq * DH;        // row stride of q and dout
+    Stage st;
+    float pl = 0.0f;
+    auto fetch = [&](int it) {
+        const int h = kvh * a.G + it / nqb, i0 = q0 + TB * (it % nqb);
+        st.fetch(a.q + (int64_t)lo * hs + h * DH, a.dout + (int64_t)lo * hs + h * DH, hs, i0, n, tid);
+        const int rr = tid % TB;
+        const bool ok = tid < 2 * TB && i0 + rr < n;
+        const int64_t at = (int64_t)h * a.Kt + lo + i0 + rr;
+        pl = !ok ? 0.0f : (tid < TB ? a.lse[at] * LOG2E : a.D[at]);
+    };
+    auto put = [&](int buf) {
+        st.put(Rm[buf], Tr[buf], 2, tid);
+        if (tid < TB) lse2[buf][tid] = pl;
+        else if (tid < 2 * TB) Dq[buf][tid - TB] = pl;
+    };
+    fetch(0);
+    put(0);
+    for (int it = 0; it < iters; ++it) {
+        const int buf = it & 1;
+        __syncthreads();  // buffer `buf` complete, buffer buf^1 no longer read
+        if (it + 1 < iters) fetch(it + 1);
+        const int g = it / nqb, i0 = q0 + TB * (it % nqb);
         const int h = kvh * a.G + g;
-        const float tau = a.temp[h];
-        const float gn = a.gain != nullptr ? a.gain[h] : 0.0f;
-        const float c1 = tau * a.inv_sqrt_dh * LOG2E;
-        const float bias2 = gn * s_key * LOG2E;
-        const float kscale = tau * a.inv_sqrt_dh;
-        float dg_acc = 0.0f, dt_acc = 0.0f;
-        const bf16* qh = a.q + (int64_t)lo * a.Hq * DH + h * DH;
-        const bf16* oh = a.dout + (int64_t)lo * a.Hq * DH + h * DH;
-        for (int i0 = kb * BW * TB; i0 < n; i0 += TB) {
-            __syncthreads();  // previous tiles fully consumed
-            stage_transposed<DH>(QT, qh, (int64_t)a.Hq * DH, i0, n, tid);
-            stage_transposed<DH>(OT, oh, (int64_t)a.Hq * DH, i0, n, tid);
-            if (tid < TB) {
-                const bool ok = i0 + tid < n;
-                lse2[tid] = ok ? a.lse[(int64_t)h * a.Kt + lo + i0 + tid] * LOG2E : 0.0f;
-                Dq[tid] = ok ? a.D[(int64_t)h * a.Kt + lo + i0 + tid] : 0.0f;
-            }
-            __syncthreads();
-            if (!wave_on || i0 + TB - 1 < j0) continue;  // no query of this block sees these keys
-
-            u32x4 qa[KS], oa[KS];
-            load_rows<DH>(qh, (int64_t)a.Hq * DH, i0 + col, n, lane, qa);
-            load_rows<DH>(oh, (int64_t)a.Hq * DH, i0 + col, n, lane, oa);
+        // Branch-free: a block no query of which sees these keys (or a wave
+        // past the request) is masked to P = dL = 0 below.  A branch here
+        // would make the compiler copy the loop-carried accumulators.
+        {
+            const float tau = a.temp[h];
+            const float gn = a.gain != nullptr ? a.gain[h] : 0.0f;
+            const float c1 = tau * a.inv_sqrt_dh * LOG2E;
+            const float bias2 = gn * s_key * LOG2E;
+            const float kscale = tau * a.inv_sqrt_dh;
+            const bf16* qrow = Rm[buf] + col * RP + 8 * (lane / 32);
+            const bf16* orow = qrow + TB * RP;
             f32x16 S, dP;
 #pragma unroll
             for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
 #pragma unroll
             for (int t = 0; t < KS; ++t) {
-                S = mfma32(as_bf16x8(qa[t]), as_bf16x8(kr[t]), S);
-                dP = mfma32(as_bf16x8(oa[t]), as_bf16x8(vr[t]), dP);
+                S = mfma32(as_bf16x8(ld16(qrow + 16 * t)), as_bf16x8(kr[t]), S);
+                dP = mfma32(as_bf16x8(ld16(orow + 16 * t)), as_bf16x8(vr[t]), dP);
             }
             float P[16], dS[16];
 #pragma unroll
@@ -208,31 +251,38 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
                 const int qq = 8 * (r / 4) + 4 * (lane / 32) + r % 4;
                 const int qi = i0 + qq;
                 const bool ok = key_ok && qi < n && qi >= key;
-                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[r], c1, bias2) - lse2[qq]) : 0.0f;
-                const float dl = p * (dP[r] - Dq[qq]);
+                // operands read unconditionally so the mask is a select, not a branch
+                const float e = __builtin_amdgcn_exp2f(fmaf(S[r], c1, bias2) - lse2[buf][qq]);
+                const float p = ok ? e : 0.0f;
+                const float dl = p * (dP[r] - Dq[buf][qq]);
                 P[r] = p;
                 dS[r] = dl * kscale;
                 ds_acc = fmaf(dl, gn, ds_acc);
                 dg_acc = fmaf(dl, s_key, dg_acc);
                 dt_acc = fmaf(dl, S[r] * a.inv_sqrt_dh, dt_acc);
             }
+            const bf16* qt = Tr[buf];
+            const bf16* ot = Tr[buf] + DH * TPAD;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const bf16x8 pb = pack8(P + 8 * c), sb = pack8(dS + 8 * c);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
                     const int row = 32 * m + col;
-                    dvT[m] = mfma32(lds_t_operand(OT, row, c, lane), pb, dvT[m]);
-                    dkT[m] = mfma32(lds_t_operand(QT, row, c, lane), sb, dkT[m]);
+                    dvT[m] = mfma32(lds_t_operand(ot, row, c, lane), pb, dvT[m]);
+                    dkT[m] = mfma32(lds_t_operand(qt, row, c, lane), sb, dkT[m]);
                 }
             }
         }
-        dg_acc = wave_sum(dg_acc);
-        dt_acc = wave_sum(dt_acc);
-        if (lane == 0) {
-            gtp[2 * g] = dg_acc;
-            gtp[2 * g + 1] = dt_acc;
+        if (it % nqb == nqb - 1) {  // last block of head g: leave its sums in the slot
+            const float dg = wave_sum(dg_acc), dt = wave_sum(dt_acc);
+            if (lane == 0) {
+                gtp[2 * g] = dg;
+                gtp[2 * g + 1] = dt;
+            }
+            dg_acc = dt_acc = 0.0f;
         }
+        if (it + 1 < iters) put(buf ^ 1);
     }
     if (!wave_on) return;
     ds_acc += __shfl_xor(ds_acc, 32, WAVE);
@@ -256,13 +306,17 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
         }
 }
 
-// Q-major pass: dQ.
+// Q-major pass: dQ.  The workgroup walks 32-key blocks; the K and V tiles of
+// the next block are fetched while the current one is computed.
 template <int DH>
-__global__ __launch_bounds__(BT) void bwd_q_kernel(BwdArgs a) {
+__global__ __launch_bounds__(BT, 2) void bwd_q_kernel(BwdArgs a) {
     constexpr int KS = DH / 16;
     constexpr int MT = DH / 32;
-    __shared__ __align__(16) bf16 KT[DH * TPAD];
-    __shared__ float sb2[TB];
+    using Stage = TileStage<DH>;
+    constexpr int RP = Stage::RP;
+    __shared__ __align__(16) bf16 Rm[2][2 * TB * RP];  // [buffer] K | V, row-major
+    __shared__ __align__(16) bf16 Tr[2][DH * TPAD];    // [buffer] K^T
+    __shared__ float sb2[2][TB];
 
     const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lo = a.cu[b], n = a.cu[b + 1] - lo;
@@ -283,8 +337,9 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BwdArgs a) {
     const float c1 = tau * a.inv_sqrt_dh * LOG2E;
     const float lq = q_ok ? a.lse[(int64_t)h * a.Kt + lo + qi] * LOG2E : 0.0f;
     const float Dv = q_ok ? a.D[(int64_t)h * a.Kt + lo + qi] : 0.0f;
-    const bf16* kh = a.k + (int64_t)lo * a.Hkv * DH + kvh * DH;
-    const bf16* vh = a.v + (int64_t)lo * a.Hkv * DH + kvh * DH;
+    const int64_t ks = (int64_t)a.Hkv * DH;
+    const bf16* kh = a.k + (int64_t)lo * ks + kvh * DH;
+    const bf16* vh = a.v + (int64_t)lo * ks + kvh * DH;
 
     f32x16 dqT[MT];
 #pragma unroll
@@ -293,43 +348,56 @@ __global__ __launch_bounds__(BT) void bwd_q_kernel(BwdArgs a) {
         for (int r = 0; r < 16; ++r) dqT[m][r] = 0.0f;
 
     const int jend = min(n, qb * BW * TB + BW * TB);
-    for (int j0 = 0; j0 < jend; j0 += TB) {
+    const int iters = (jend + TB - 1) / TB;
+    Stage st;
+    float pb = 0.0f;
+    auto fetch = [&](int it) {
+        const int j0 = TB * it;
+        st.fetch(kh, vh, ks, j0, n, tid);
+        const bool ok = tid < TB && j0 + tid < n && a.s != nullptr;
+        pb = ok ? gn * a.s[lo + j0 + tid] * LOG2E : 0.0f;
+    };
+    auto put = [&](int buf) {
+        st.put(Rm[buf], Tr[buf], 1, tid);
+        if (tid < TB) sb2[buf][tid] = pb;
+    };
+    fetch(0);
+    put(0);
+    for (int it = 0; it < iters; ++it) {
+        const int buf = it & 1;
         __syncthreads();
-        stage_transposed<DH>(KT, kh, (int64_t)a.Hkv * DH, j0, n, tid);
-        if (tid < TB) {
-            const bool ok = j0 + tid < n && a.s != nullptr;
-            sb2[tid] = ok ? gn * a.s[lo + j0 + tid] * LOG2E : 0.0f;
+        if (it + 1 < iters) fetch(it + 1);
+        const int j0 = TB * it;
+        {  // branch-free, as in the KV pass: the mask zeroes what no query sees
+            const bf16* krow = Rm[buf] + col * RP + 8 * (lane / 32);
+            const bf16* vrow = krow + TB * RP;
+            f32x16 S, dP;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+                S = mfma32(as_bf16x8(ld16(krow + 16 * t)), as_bf16x8(qr[t]), S);
+                dP = mfma32(as_bf16x8(ld16(vrow + 16 * t)), as_bf16x8(orr[t]), dP);
+            }
+            float dS[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = 8 * (r / 4) + 4 * (lane / 32) + r % 4;
+                const int kj = j0 + kk;
+                const bool ok = q_ok && kj < n && qi >= kj;
+                const float e = __builtin_amdgcn_exp2f(fmaf(S[r], c1, sb2[buf][kk]) - lq);
+                const float p = ok ? e : 0.0f;
+                dS[r] = p * (dP[r] - Dv);
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const bf16x8 sbv = pack8(dS + 8 * c);
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+                    dqT[m] = mfma32(lds_t_operand(Tr[buf], 32 * m + col, c, lane), sbv, dqT[m]);
+            }
         }
-        __syncthreads();
-        if (!wave_on || j0 > i0 + TB - 1) continue;
-
-        u32x4 ka[KS], va[KS];
-        load_rows<DH>(kh, (int64_t)a.Hkv * DH, j0 + col, n, lane, ka);
-        load_rows<DH>(vh, (int64_t)a.Hkv * DH, j0 + col, n, lane, va);
-        f32x16 S, dP;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.0f;
-#pragma unroll
-        for (int t = 0; t < KS; ++t) {
-            S = mfma32(as_bf16x8(ka[t]), as_bf16x8(qr[t]), S);
-            dP = mfma32(as_bf16x8(va[t]), as_bf16x8(orr[t]), dP);
-        }
-        float dS[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kk = 8 * (r / 4) + 4 * (lane / 32) + r % 4;
-            const int kj = j0 + kk;
-            const bool ok = q_ok && kj < n && qi >= kj;
-            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[r], c1, sb2[kk]) - lq) : 0.0f;
-            dS[r] = p * (dP[r] - Dv);
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const bf16x8 sbv = pack8(dS + 8 * c);
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                dqT[m] = mfma32(lds_t_operand(KT, 32 * m + col, c, lane), sbv, dqT[m]);
-        }
+        if (it + 1 < iters) put(buf ^ 1);
     }
     if (!q_ok) return;
     const float qs = tau * a.inv_sqrt_dh;

@@ -42,6 +42,10 @@ KERNELS = [
     ("qk_norm_rope_kernel", "layer", "learned_token_pruning_02_amd/csrc/layer.hip"),
     ("silu_mul_kernel", "layer", "learned_token_pruning_02_amd/csrc/layer.hip"),
     ("kept_positions_kernel", "layer", "learned_token_pruning_02_amd/csrc/layer.hip"),
+    ("bwd_dot_kernel", "backward", "learned_token_pruning_02_amd/csrc/attn_bwd.hip"),
+    ("bwd_kv_kernel", "backward", "learned_token_pruning_02_amd/csrc/attn_bwd.hip"),
+    ("bwd_q_kernel", "backward", "learned_token_pruning_02_amd/csrc/attn_bwd.hip"),
+    ("bwd_reduce_kernel", "backward", "learned_token_pruning_02_amd/csrc/attn_bwd.hip"),
     ("decode_chunk_kernel", "decode", "learned_token_pruning_02_amd/csrc/decode.hip"),
     ("decode_merge_kernel", "decode", "learned_token_pruning_02_amd/csrc/decode.hip"),
 ]
