@@ -67,6 +67,7 @@ __all__ = [
     "kept_positions",
     "decoder_layer",
     "gated_attention_backward",
+    "gate_backward",
 ]
 
 
@@ -485,3 +486,29 @@ def gated_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             g["dgain"][h] += (col * s64[lo:hi]).sum()
             g["dtemp"][h] += (dL * r).sum()
     return g
+
+
+# --------------------------------------------------------------------------
+# Backward of the gate MLP (spke.com page, "Comment TokenGate a-t-il appris
+# ...": the gate is trained through the score bias; the top-K choice carries
+# no gradient, so only kept tokens receive one).  For a kept token with
+# z = W1 x + b1 and s = w2 . GELU(z) + b2, an upstream gradient ds gives
+#   dz = ds * w2 * GELU'(z),  GELU'(z) = Phi(z) + z phi(z)
+#   dW1 = sum_t dz_t x_t^T,  db1 = sum_t dz_t,  dw2 = sum_t ds_t GELU(z_t),
+#   db2 = sum_t ds_t,  dx_t = W1^T dz_t
+# --------------------------------------------------------------------------
+def gate_backward(hidden_kept: torch.Tensor, w1: torch.Tensor, b1: Optional[torch.Tensor],
+                  w2: torch.Tensor, ds: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """Gradients of sum_t ds_t s_t over the given (kept) rows, float64:
+    dhidden[Kt][d], dw1[d_gate][d], db1[d_gate], dw2[d_gate], db2[1]."""
+    x = hidden_kept.double()
+    W1 = w1.double()
+    z = x @ W1.t()
+    if b1 is not None:
+        z = z + b1.double()
+    phi = torch.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+    Phi = 0.5 * (1.0 + torch.erf(z / math.sqrt(2.0)))
+    d64 = ds.double()
+    dz = d64[:, None] * w2.double()[None, :] * (Phi + z * phi)
+    return {"dhidden": dz @ W1, "dw1": dz.t() @ x, "db1": dz.sum(dim=0),
+            "dw2": gelu_erf(z).t() @ d64, "db2": d64.sum().reshape(1)}

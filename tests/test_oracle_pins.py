@@ -675,3 +675,62 @@ def test_attention_backward_stored_output():
         assert torch.equal(a[n], b[n]), n
     c = oracle.gated_attention_backward(q, k, v, s, gain, temp, cu, dout, out_stored=out * 1.01)
     assert torch.equal(c["dv"], a["dv"]) and not torch.equal(c["dq"], a["dq"])
+
+
+# -------------------------------------------------------------- gate backward ----
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_gate_backward_matches_autograd(with_bias):
+    """Autograd through gate_score's float64 definition (before its fp32
+    rounding) against the hand-derived backward."""
+    g = torch.Generator().manual_seed(90)
+    T, d, dg = 13, 24, 10
+    x = torch.randn(T, d, generator=g, dtype=torch.float64)
+    w1 = torch.randn(dg, d, generator=g, dtype=torch.float64) / math.sqrt(d)
+    b1 = torch.randn(dg, generator=g, dtype=torch.float64) if with_bias else None
+    w2 = torch.randn(dg, generator=g, dtype=torch.float64)
+    b2 = torch.randn(1, generator=g, dtype=torch.float64)
+    ds = torch.randn(T, generator=g, dtype=torch.float64)
+    leaves = [t.clone().requires_grad_(True) for t in (x, w1, w2, b2)] + \
+        ([b1.clone().requires_grad_(True)] if with_bias else [])
+    lx, lw1, lw2, lb2 = leaves[:4]
+    lb1 = leaves[4] if with_bias else None
+    z = lx @ lw1.t() + (lb1 if with_bias else 0.0)
+    s = oracle.gelu_erf(z) @ lw2 + lb2
+    (s * ds).sum().backward()
+    got = oracle.gate_backward(x, w1, b1, w2, ds)
+    torch.testing.assert_close(got["dhidden"], lx.grad, rtol=1e-12, atol=1e-12)
+    torch.testing.assert_close(got["dw1"], lw1.grad, rtol=1e-12, atol=1e-12)
+    torch.testing.assert_close(got["dw2"], lw2.grad, rtol=1e-12, atol=1e-12)
+    torch.testing.assert_close(got["db2"], lb2.grad, rtol=1e-12, atol=1e-12)
+    if with_bias:
+        torch.testing.assert_close(got["db1"], lb1.grad, rtol=1e-12, atol=1e-12)
+
+
+def test_gate_backward_finite_differences_and_cases():
+    g = torch.Generator().manual_seed(91)
+    T, d, dg = 6, 8, 5
+    x = torch.randn(T, d, generator=g, dtype=torch.float64)
+    w1 = torch.randn(dg, d, generator=g, dtype=torch.float64)
+    b1 = torch.randn(dg, generator=g, dtype=torch.float64)
+    w2 = torch.randn(dg, generator=g, dtype=torch.float64)
+    ds = torch.randn(T, generator=g, dtype=torch.float64)
+    got = oracle.gate_backward(x, w1, b1, w2, ds)
+
+    def loss(x=x, w1=w1, b1=b1, w2=w2):
+        z = x @ w1.t() + b1
+        return float((0.5 * z * (1 + torch.erf(z / math.sqrt(2))) @ w2 * ds).sum())
+
+    eps = 1e-6
+    for name, t, idx in (("dhidden", x, (2, 3)), ("dw1", w1, (4, 1)), ("db1", b1, (0,)), ("dw2", w2, (3,))):
+        plus, minus = t.clone(), t.clone()
+        plus[idx] += eps
+        minus[idx] -= eps
+        key = {"dhidden": "x", "dw1": "w1", "db1": "b1", "dw2": "w2"}[name]
+        fd = (loss(**{key: plus}) - loss(**{key: minus})) / (2 * eps)
+        assert abs(fd - float(got[name][idx])) < 1e-6 * max(1.0, abs(fd)), (name, fd)
+    assert float(got["db2"]) == float(ds.sum())
+    zero = oracle.gate_backward(x, w1, b1, w2, torch.zeros(T, dtype=torch.float64))
+    assert all(float(v.abs().max()) == 0.0 for v in zero.values())
+    # GELU'(0) = 1/2: with W1 = 0 and no bias, dz = ds * w2 / 2
+    z0 = oracle.gate_backward(x, torch.zeros(dg, d, dtype=torch.float64), None, w2, ds)
+    torch.testing.assert_close(z0["db1"], 0.5 * ds.sum() * w2, rtol=1e-14, atol=1e-14)
