@@ -273,6 +273,42 @@ tg_status tg_gated_attn_backward(tg_dtype dt, const void *q, const void *k, cons
                                  float *ds, float *dgain, float *dtemp, void *ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/*
+ * tg_gate_backward_plan -- workspace bytes of tg_gate_backward.  Errors:
+ * TG_ERR_NULL_PTR, TG_ERR_BAD_DTYPE, TG_ERR_BAD_SHAPE.
+ */
+tg_status tg_gate_backward_plan(tg_dtype dt, int64_t Kt, int32_t d_model, int32_t d_gate,
+                                size_t *ws_bytes);
+
+/*
+ * tg_gate_backward -- gradients of the gate MLP over the kept rows.  The gate
+ * is trained through the score bias of the attention above it (spke.com page,
+ * "Comment TokenGate a-t-il appris ..."); the top-K choice has no gradient, so
+ * only kept tokens receive one.  With z_t = W1 x_t + b1,
+ * s_t = w2 . GELU(z_t) + b2 and the score gradient ds (for instance ds of
+ * tg_gated_attn_backward), over the Kt given rows:
+ *     dz_t = ds_t * w2 * GELU'(z_t),   GELU'(z) = Phi(z) + z phi(z)
+ *     dhidden_t = W1^T dz_t,  dw1 = sum_t dz_t x_t^T,  db1 = sum_t dz_t,
+ *     dw2 = sum_t ds_t GELU(z_t),  db2 = sum_t ds_t
+ * hidden_kept : [Kt][d_model] in dt (the gathered kept rows; a pruned token's
+ * gradient is zero and its row need not be passed);  w1 [d_gate][d_model],
+ * b1 [d_gate] (nullable), w2 [d_gate] in dt;  ds_kept [Kt] fp32.
+ * dhidden_kept [Kt][d_model] and dw1 [d_gate][d_model] in dt; db1 (NULL iff
+ * b1 is NULL), dw2 [d_gate] and db2 [1] fp32.  All overwritten.
+ * ws: tg_gate_backward_plan bytes, caller-owned, 16-byte aligned.
+ * The products run on the tg_linear kernels (fp32 accumulation, one rounding
+ * of z, dz and the outputs to dt); the column sums are fixed-order reductions.
+ * Supported: TG_BF16 with d_model and d_gate multiples of 64, TG_F32 with
+ * multiples of 4.  Kt == 0 is a no-op.  Errors: TG_ERR_BAD_DTYPE,
+ * TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE, TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT,
+ * TG_ERR_WORKSPACE, TG_ERR_ALIAS, TG_ERR_LAUNCH.
+ */
+tg_status tg_gate_backward(tg_dtype dt, const void *hidden_kept, int64_t Kt, int32_t d_model,
+                           const void *w1, const void *b1, const void *w2, int32_t d_gate,
+                           const float *ds_kept, void *dhidden_kept, void *dw1, float *db1,
+                           float *dw2, float *db2, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
 /* Cached rows per split of tg_gated_attn_decode; its workspace is sized in
  * these. */
 #define TG_DECODE_CHUNK 128

@@ -33,6 +33,8 @@ __all__ = [
     "tg_gather_compact",
     "tg_gated_attn_prefill",
     "tg_attn_backward_plan",
+    "tg_gate_backward_plan",
+    "tg_gate_backward",
     "tg_gated_attn_backward",
     "tg_decode_plan",
     "tg_gated_attn_decode",
@@ -125,6 +127,11 @@ def lib() -> ctypes.CDLL:
     L.tg_gated_attn_backward.restype = ctypes.c_int
     L.tg_gated_attn_backward.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, p_i32, i32,
                                          i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.tg_gate_backward_plan.restype = ctypes.c_int
+    L.tg_gate_backward_plan.argtypes = [ctypes.c_int, i64, i32, i32, ctypes.POINTER(sz)]
+    L.tg_gate_backward.restype = ctypes.c_int
+    L.tg_gate_backward.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp, vp, i32, vp, vp, vp, vp, vp,
+                                   vp, vp, sz, vp]
     L.tg_decode_plan.restype = ctypes.c_int
     L.tg_decode_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(sz)]
     L.tg_gated_attn_decode.restype = ctypes.c_int
@@ -334,6 +341,39 @@ def tg_gated_attn_backward(q, k, v, s_kept, gain, temp, out, lse, dout, cu_kept:
         _dev(grads["dv"], "dv", q.dtype), _dev(grads["ds"], "ds", f32t),
         _dev(grads["dgain"], "dgain", f32t), _dev(grads["dtemp"], "dtemp", f32t),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return grads
+
+
+def tg_gate_backward_plan(dtype, Kt: int, d_model: int, d_gate: int) -> int:
+    """Workspace bytes of tg_gate_backward (dtype: a torch dtype)."""
+    ws = ctypes.c_size_t(0)
+    dt = TG_BF16 if dtype == _torch().bfloat16 else TG_F32
+    _check("tg_gate_backward_plan", lib().tg_gate_backward_plan(dt, Kt, d_model, d_gate, ctypes.byref(ws)))
+    return ws.value
+
+
+def tg_gate_backward(hidden_kept, w1, b1, w2, ds_kept, grads=None, workspace=None, stream=None):
+    """Gradients of the gate MLP over the kept rows; returns a dict with
+    dhidden, dw1 (in the input dtype) and db1 (None without b1), dw2, db2 (fp32)."""
+    torch = _torch()
+    Kt, d = hidden_kept.shape
+    dg = w1.shape[0]
+    f32 = dict(dtype=torch.float32, device=hidden_kept.device)
+    if grads is None:
+        grads = {"dhidden": torch.empty_like(hidden_kept), "dw1": torch.empty_like(w1),
+                 "db1": torch.empty(dg, **f32) if b1 is not None else None,
+                 "dw2": torch.empty(dg, **f32), "db2": torch.empty(1, **f32)}
+    if workspace is None:
+        workspace = torch.empty(max(1, tg_gate_backward_plan(hidden_kept.dtype, Kt, d, dg)),
+                                dtype=torch.uint8, device=hidden_kept.device)
+    x = hidden_kept
+    _check("tg_gate_backward", lib().tg_gate_backward(
+        _dt(x), _dev(x, "hidden_kept"), Kt, d, _dev(w1, "w1", x.dtype), _dev(b1, "b1", x.dtype),
+        _dev(w2, "w2", x.dtype), dg, _dev(ds_kept, "ds_kept", torch.float32),
+        _dev(grads["dhidden"], "dhidden", x.dtype), _dev(grads["dw1"], "dw1", x.dtype),
+        _dev(grads["db1"], "db1", torch.float32), _dev(grads["dw2"], "dw2", torch.float32),
+        _dev(grads["db2"], "db2", torch.float32), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
     return grads
 
 

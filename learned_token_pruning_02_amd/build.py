@@ -22,7 +22,7 @@ LIB_NAME = "libtokengate.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["tg_api.cpp", "gate.hip", "select.hip", "gather.hip", "attn.hip", "attn_bwd.hip", "decode.hip", "layer.hip", "linear.hip"]
+SOURCES = ["tg_api.cpp", "gate.hip", "gate_bwd.hip", "select.hip", "gather.hip", "attn.hip", "attn_bwd.hip", "decode.hip", "layer.hip", "linear.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

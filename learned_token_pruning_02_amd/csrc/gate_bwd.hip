@@ -1,0 +1,182 @@
+// Backward of the gate MLP over the kept rows.
+//
+// The gate learns through the score bias of the attention above it; the top-K
+// choice has no gradient, so only kept tokens receive a score gradient ds
+// (spke.com page, "Comment TokenGate a-t-il appris ...").  For a kept row x,
+// z = W1 x + b1, s = w2 . GELU(z) + b2:
+//   dz  = ds * w2 * GELU'(z),  GELU'(z) = Phi(z) + z phi(z)
+//   dW1 = sum_t dz_t x_t^T,  db1 = sum_t dz_t,  dw2 = sum_t ds_t GELU(z_t),
+//   db2 = sum_t ds_t,        dx_t = W1^T dz_t
+// The three products run on the matrix-core projection kernel (z = X W1^T,
+// dx = dZ W1, dW1 = dZ^T X through zero-padded transposes so that the
+// contraction over kept rows is a plain row-major product); the elementwise
+// part and the column sums are two small kernels here, the sums reduced in a
+// fixed order (no atomics).
+
+#include <algorithm>
+
+#include "tg_device.h"
+#include "tg_kernels.h"
+
+namespace tg {
+namespace {
+
+constexpr int DZ_ROWS = 64;     // kept rows per workgroup of the dz kernel
+constexpr int DZ_THREADS = 256;
+
+template <class T>
+__device__ __forceinline__ float ld1(const T* p) { return to_f32(*p); }
+
+// out[c][r] = in[r][c] for r < R, 0 for R <= r < Rpad; in is [R][C].
+template <class T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in, int64_t R, int C,
+                                                        T* __restrict__ out, int64_t Rpad) {
+    __shared__ T tile[32][33];
+    const int c0 = blockIdx.x * 32;
+    const int64_t r0 = (int64_t)blockIdx.y * 32;
+    const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 32 x 8
+#pragma unroll
+    for (int k = 0; k < 32; k += 8) {
+        const int64_t r = r0 + ty + k;
+        const int c = c0 + tx;
+        tile[ty + k][tx] = (r < R && c < C) ? in[r * C + c] : from_f32<T>(0.0f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 32; k += 8) {
+        const int c = c0 + ty + k;
+        const int64_t r = r0 + tx;
+        if (c < C && r < Rpad) out[(int64_t)c * Rpad + r] = tile[tx][ty + k];
+    }
+}
+
+// dz[t][u] from zlin[t][u] = (X W1^T)[t][u]; per-workgroup partial sums of
+// ds*GELU(z) (for dw2), dz (for db1) and ds (for db2).
+template <class T>
+__global__ __launch_bounds__(DZ_THREADS) void gate_dz_kernel(const T* __restrict__ zlin,
+                                                             const T* __restrict__ b1,
+                                                             const T* __restrict__ w2,
+                                                             const float* __restrict__ ds,
+                                                             int64_t Kt, int dg,
+                                                             T* __restrict__ dz,
+                                                             float* __restrict__ part) {
+    const int64_t t0 = (int64_t)blockIdx.x * DZ_ROWS;
+    const int64_t t1 = std::min<int64_t>(Kt, t0 + DZ_ROWS);
+    float* pb = part + (int64_t)blockIdx.x * (2 * dg + 1);
+    for (int u = threadIdx.x; u < dg; u += DZ_THREADS) {
+        const float bu = b1 != nullptr ? ld1(b1 + u) : 0.0f;
+        const float wu = ld1(w2 + u);
+        float sw = 0.0f, sz = 0.0f;
+        for (int64_t t = t0; t < t1; ++t) {
+            const float z = ld1(zlin + t * dg + u) + bu;
+            const float Phi = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
+            const float phi = 0.39894228040143268f * __expf(-0.5f * z * z);
+            const float d = ds[t];
+            const float g = d * wu * fmaf(z, phi, Phi);
+            dz[t * dg + u] = from_f32<T>(g);
+            sw = fmaf(d, z * Phi, sw);
+            sz += g;
+        }
+        pb[u] = sw;
+        pb[dg + u] = sz;
+    }
+    if (threadIdx.x == 0) {
+        float s = 0.0f;
+        for (int64_t t = t0; t < t1; ++t) s += ds[t];
+        pb[2 * dg] = s;
+    }
+}
+
+__global__ __launch_bounds__(256) void gate_bwd_reduce_kernel(const float* __restrict__ part,
+                                                              int nblk, int dg,
+                                                              float* __restrict__ dw2,
+                                                              float* __restrict__ db1,
+                                                              float* __restrict__ db2) {
+    for (int i = threadIdx.x; i < 2 * dg + 1; i += blockDim.x) {
+        float acc = 0.0f;
+        for (int b = 0; b < nblk; ++b) acc += part[(int64_t)b * (2 * dg + 1) + i];
+        if (i < dg) dw2[i] = acc;
+        else if (i < 2 * dg) { if (db1 != nullptr) db1[i - dg] = acc; }
+        else db2[0] = acc;
+    }
+}
+
+struct GateBwdLayout {
+    int64_t kt_pad, nblk;
+    size_t zlin, dz, dzT, xT, w1T, part, total;
+};
+
+GateBwdLayout layout(tg_dtype dt, int64_t Kt, int d, int dg) {
+    const int64_t eb = dt == TG_BF16 ? 2 : 4;
+    const auto up = [](int64_t x) { return (size_t)((x + 255) / 256 * 256); };
+    GateBwdLayout L;
+    L.kt_pad = (Kt + 63) / 64 * 64;
+    L.nblk = (Kt + DZ_ROWS - 1) / DZ_ROWS;
+    size_t o = 0;
+    L.zlin = o; o += up(Kt * dg * eb);
+    L.dz = o;   o += up(Kt * dg * eb);
+    L.dzT = o;  o += up((int64_t)dg * L.kt_pad * eb);
+    L.xT = o;   o += up((int64_t)d * L.kt_pad * eb);
+    L.w1T = o;  o += up((int64_t)d * dg * eb);
+    L.part = o; o += up(std::max<int64_t>(1, L.nblk) * (2 * dg + 1) * 4);
+    L.total = o;
+    return L;
+}
+
+template <class T>
+hipError_t transpose(const T* in, int64_t R, int C, T* out, int64_t Rpad, hipStream_t st) {
+    const dim3 grid((unsigned)((C + 31) / 32), (unsigned)((Rpad + 31) / 32));
+    hipLaunchKernelGGL(transpose_kernel<T>, grid, dim3(256), 0, st, in, R, C, out, Rpad);
+    return hipGetLastError();
+}
+
+template <class T>
+hipError_t run(tg_dtype dt, const T* x, int64_t Kt, int d, const T* w1, const T* b1, const T* w2,
+               int dg, const float* ds, T* dx, T* dw1, float* db1, float* dw2, float* db2, char* ws,
+               hipStream_t st) {
+    const GateBwdLayout L = layout(dt, Kt, d, dg);
+    T* zlin = (T*)(ws + L.zlin);
+    T* dz = (T*)(ws + L.dz);
+    T* dzT = (T*)(ws + L.dzT);
+    T* xT = (T*)(ws + L.xT);
+    T* w1T = (T*)(ws + L.w1T);
+    float* part = (float*)(ws + L.part);
+    const auto lin = [&](const T* a, const T* b, T* y, int64_t M, int N, int K) {
+        return dt == TG_BF16 ? launch_linear_bf16(a, b, y, M, N, K, 0, st)
+                             : launch_linear_f32((const float*)a, (const float*)b, (float*)y, M, N,
+                                                 K, 0, st);
+    };
+    hipError_t e;
+    if ((e = lin(x, w1, zlin, Kt, dg, d)) != hipSuccess) return e;              // z - b1
+    hipLaunchKernelGGL(gate_dz_kernel<T>, dim3((unsigned)L.nblk), dim3(DZ_THREADS), 0, st, zlin, b1,
+                       w2, ds, Kt, dg, dz, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(gate_bwd_reduce_kernel, dim3(1), dim3(256), 0, st, part, (int)L.nblk, dg, dw2,
+                       db1, db2);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = transpose(w1, dg, d, w1T, dg, st)) != hipSuccess) return e;        // W1^T [d][dg]
+    if ((e = lin(dz, w1T, dx, Kt, d, dg)) != hipSuccess) return e;              // dx = dZ W1
+    if ((e = transpose(dz, Kt, dg, dzT, L.kt_pad, st)) != hipSuccess) return e; // dZ^T [dg][Kt_pad]
+    if ((e = transpose(x, Kt, d, xT, L.kt_pad, st)) != hipSuccess) return e;    // X^T  [d][Kt_pad]
+    return lin(dzT, xT, dw1, dg, d, (int)L.kt_pad);                             // dW1 = dZ^T X
+}
+
+}  // namespace
+
+size_t gate_bwd_workspace_bytes(tg_dtype dt, int64_t Kt, int d, int dg) {
+    return layout(dt, Kt, d, dg).total;
+}
+
+hipError_t launch_gate_bwd(tg_dtype dt, const void* x, int64_t Kt, int d, const void* w1,
+                           const void* b1, const void* w2, int dg, const float* ds, void* dx,
+                           void* dw1, float* db1, float* dw2, float* db2, void* ws,
+                           hipStream_t st) {
+    if (dt == TG_BF16)
+        return run<bf16>(dt, (const bf16*)x, Kt, d, (const bf16*)w1, (const bf16*)b1,
+                         (const bf16*)w2, dg, ds, (bf16*)dx, (bf16*)dw1, db1, dw2, db2, (char*)ws, st);
+    return run<float>(dt, (const float*)x, Kt, d, (const float*)w1, (const float*)b1,
+                      (const float*)w2, dg, ds, (float*)dx, (float*)dw1, db1, dw2, db2, (char*)ws,
+                      st);
+}
+
+}  // namespace tg

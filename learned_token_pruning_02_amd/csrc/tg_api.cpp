@@ -320,6 +320,61 @@ tg_status tg_gated_attn_backward(tg_dtype dt, const void* q, const void* k, cons
                                         ds, dgain, dtemp, ws, stream));
 }
 
+namespace {
+tg_status gate_bwd_shape(tg_dtype dt, int64_t Kt, int32_t d, int32_t dg) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (Kt < 0 || Kt >= I32_LIMIT || d < 1 || dg < 1) return TG_ERR_BAD_SHAPE;
+    const int m = dt == TG_BF16 ? 64 : 4;
+    if (d % m != 0 || dg % m != 0) return TG_ERR_UNSUPPORTED;
+    return TG_OK;
+}
+}  // namespace
+
+tg_status tg_gate_backward_plan(tg_dtype dt, int64_t Kt, int32_t d_model, int32_t d_gate,
+                                size_t* ws_bytes) {
+    if (ws_bytes == nullptr) return TG_ERR_NULL_PTR;
+    const tg_status st = gate_bwd_shape(dt, Kt, d_model, d_gate);
+    if (st != TG_OK) return st;
+    *ws_bytes = tg::gate_bwd_workspace_bytes(dt, Kt, d_model, d_gate);
+    return TG_OK;
+}
+
+tg_status tg_gate_backward(tg_dtype dt, const void* hidden_kept, int64_t Kt, int32_t d_model,
+                           const void* w1, const void* b1, const void* w2, int32_t d_gate,
+                           const float* ds_kept, void* dhidden_kept, void* dw1, float* db1,
+                           float* dw2, float* db2, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (hidden_kept == nullptr || w1 == nullptr || w2 == nullptr || ds_kept == nullptr ||
+        dhidden_kept == nullptr || dw1 == nullptr || dw2 == nullptr || db2 == nullptr ||
+        (b1 == nullptr) != (db1 == nullptr))
+        return TG_ERR_NULL_PTR;
+    const tg_status st = gate_bwd_shape(dt, Kt, d_model, d_gate);
+    if (st != TG_OK) return st;
+    const size_t need = tg::gate_bwd_workspace_bytes(dt, Kt, d_model, d_gate);
+    if (ws == nullptr || ws_bytes < need) return TG_ERR_WORKSPACE;
+    const void* a16[] = {hidden_kept, w1, b1, w2, dhidden_kept, dw1, ws};
+    for (const void* p : a16)
+        if (p != nullptr && !aligned16(p)) return TG_ERR_ALIGNMENT;
+    const void* a4[] = {ds_kept, db1, dw2, db2};
+    for (const void* p : a4)
+        if (p != nullptr && !aligned4(p)) return TG_ERR_ALIGNMENT;
+    const int64_t eb = elt_bytes(dt);
+    const int64_t xb = Kt * d_model * eb, wb = (int64_t)d_gate * d_model * eb, vb = d_gate * eb;
+    const void* ins[] = {hidden_kept, w1, b1, w2, ds_kept};
+    const int64_t inb[] = {xb, wb, vb, vb, Kt * 4};
+    void* outs[] = {dhidden_kept, dw1, db1, dw2, db2, ws};
+    const int64_t outb[] = {xb, wb, (int64_t)d_gate * 4, (int64_t)d_gate * 4, 4, (int64_t)need};
+    for (int o = 0; o < 6; ++o) {
+        for (int i = 0; i < 5; ++i)
+            if (overlap(outs[o], outb[o], ins[i], inb[i])) return TG_ERR_ALIAS;
+        for (int o2 = o + 1; o2 < 6; ++o2)
+            if (overlap(outs[o], outb[o], outs[o2], outb[o2])) return TG_ERR_ALIAS;
+    }
+    if (Kt == 0) return TG_OK;
+    return launched(tg::launch_gate_bwd(dt, hidden_kept, Kt, d_model, w1, b1, w2, d_gate, ds_kept,
+                                        dhidden_kept, dw1, db1, dw2, db2, ws, stream));
+}
+
 tg_status tg_decode_plan(int32_t batch, int32_t Hq, int32_t d_head, int32_t max_len,
                          size_t* ws_bytes) {
     if (ws_bytes == nullptr) return TG_ERR_NULL_PTR;

@@ -51,6 +51,12 @@ hipError_t launch_attn_bwd(const AttnShape& sh, const void* q, const void* k, co
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* ds, float* dgain, float* dtemp, void* ws, hipStream_t st);
 
+size_t gate_bwd_workspace_bytes(tg_dtype dt, int64_t Kt, int d, int dg);
+hipError_t launch_gate_bwd(tg_dtype dt, const void* x, int64_t Kt, int d, const void* w1,
+                           const void* b1, const void* w2, int dg, const float* ds, void* dx,
+                           void* dw1, float* db1, float* dw2, float* db2, void* ws,
+                           hipStream_t st);
+
 struct DecodeShape {
     int32_t batch;
     int32_t Hq, Hkv, d_head;

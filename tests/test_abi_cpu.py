@@ -344,6 +344,37 @@ def test_attention_backward_validation():
     assert call(cu=ctypes.cast(zero, P)) == 0                                    # no rows: no-op
 
 
+def test_gate_backward_validation():
+    L = tg.lib()
+    ws = ctypes.c_size_t(0)
+    assert L.tg_gate_backward_plan(1, 777, 2048, 256, ctypes.byref(ws)) == 0 and ws.value > 0
+    assert L.tg_gate_backward_plan(1, 777, 2000, 256, ctypes.byref(ws)) == 5
+    assert L.tg_gate_backward_plan(1, -1, 2048, 256, ctypes.byref(ws)) == 2
+    assert L.tg_gate_backward_plan(3, 7, 2048, 256, ctypes.byref(ws)) == 4
+    assert L.tg_gate_backward_plan(1, 100, 2048, 256, ctypes.byref(ws)) == 0   # the shape called below
+    W = 96 << 20
+    f = L.tg_gate_backward
+    ok = [1, A, 100, 2048, B, C, D, 256, E, F, G, H, H + 1024, H + 2048, W, ws.value, None]
+    names = ["dt", "x", "Kt", "d", "w1", "b1", "w2", "dg", "ds", "dx", "dw1", "db1", "dw2", "db2",
+             "ws", "wsb", "st"]
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(dt=9) == 4
+    for nm in ("x", "w1", "w2", "ds", "dx", "dw1", "dw2", "db2"):
+        assert call(**{nm: None}) == 1, nm
+    assert call(b1=None) == 1 and call(db1=None) == 1                 # NULL together or not at all
+    assert call(Kt=-1) == 2 and call(d=0) == 2 and call(dg=100) == 5
+    assert call(ws=None) == 7 and call(wsb=ws.value - 1) == 7
+    assert call(x=A + 8) == 6 and call(db2=H + 2050) == 6
+    assert call(dx=A + 64) == 9 and call(dw1=B) == 9 and call(ws=F) == 9 and call(dw2=H) == 9
+    assert call(Kt=0) == 0
+
+
 def test_linear_validation():
     L = tg.lib()
     f = L.tg_linear
