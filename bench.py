@@ -236,6 +236,24 @@ def backward_bench(args):
     mean = sum(ms) / len(ms)
     flops = 2.5 * 4 * sh.d_head * sh.n_q_heads * Kt * (Kt + 1) // 2
     tf = flops / (mean * 1e-3) / 1e12
+
+    # The gate MLP backward on the same kept rows, fed the score gradient.
+    gi = workloads.gate_inputs(workloads.WORKLOADS["qwen3_1p7b_16k"], seed=args.seed)
+    gw = {k: (None if v is None else v.cuda()) for k, v in gi.items() if k != "hidden"}
+    gx = torch.randn(Kt, sh.d_model, device="cuda", generator=g).to(sh.dtype)
+    gws = torch.empty(tg.tg_gate_backward_plan(sh.dtype, Kt, sh.d_model, sh.d_gate), dtype=torch.uint8,
+                      device="cuda")
+    ggr = tg.tg_gate_backward(gx, gw["w1"], gw["b1"], gw["w2"], grads["ds"], workspace=gws, stream=st)
+    for _ in range(args.warmup):
+        tg.tg_gate_backward(gx, gw["w1"], gw["b1"], gw["w2"], grads["ds"], grads=ggr, workspace=gws, stream=st)
+    gev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    gev[0].record(st)
+    for i in range(args.steps):
+        tg.tg_gate_backward(gx, gw["w1"], gw["b1"], gw["w2"], grads["ds"], grads=ggr, workspace=gws, stream=st)
+        gev[i + 1].record(st)
+    torch.cuda.synchronize()
+    gms = sum(gev[i].elapsed_time(gev[i + 1]) for i in range(args.steps)) / args.steps
+    gflops = 3 * 2 * Kt * sh.d_model * sh.d_gate
     rec = {
         "metric": "gated attention backward tokens/s (context tokens per layer)",
         "value": w.total_tokens / (mean * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -248,6 +266,9 @@ def backward_bench(args):
                      "kernel": "attention backward (dot, KV pass, Q pass, reduce; one call)",
                      "algorithmic_flops_per_call": flops},
         "ms_call": {"mean": mean, "median": sorted(ms)[len(ms) // 2], "min": min(ms)},
+        "gate_backward": {"ms": gms, "TFLOP/s": gflops / (gms * 1e-3) / 1e12,
+                          "note": "gate MLP backward on the 8192 kept rows (three products on the "
+                                  "projection kernel, dz and column sums), fed this call's ds"},
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -414,8 +414,9 @@ __global__ __launch_bounds__(BT, 2) void bwd_q_kernel(BwdArgs a) {
         }
 }
 
-// ds[j] = sum over KV heads of the partial column sums; dgain, dtemp = sums of
-// the per-wave partials in a fixed order (block 0).
+// ds[j] = sum over KV heads of the partial column sums (one thread per key);
+// dgain, dtemp: one wave per (head, which) output, lanes summing strided
+// per-wave partials, then a fixed shuffle tree (deterministic).
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (a.ds != nullptr && j < a.Kt) {
@@ -423,20 +424,22 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
         for (int kv = 0; kv < a.Hkv; ++kv) acc += a.ds_part[(int64_t)kv * a.Kt + j];
         a.ds[j] = acc;
     }
-    if (blockIdx.x == 0) {
-        const int64_t nblk = (int64_t)a.batch * a.nkb;
-        for (int hh = threadIdx.x; hh < 2 * a.Hq; hh += blockDim.x) {
-            const int h = hh / 2, kv = h / a.G, g = h % a.G;
-            float acc = 0.0f;
-            for (int64_t blk = 0; blk < nblk; ++blk)
-                for (int ww = 0; ww < BW; ++ww)
-                    acc += a.gt_part[((blk * a.Hkv + kv) * BW + ww) * a.G * 2 + 2 * g + hh % 2];
-            if (hh % 2 == 0) {
-                if (a.dgain != nullptr) a.dgain[h] = acc;
-            } else {
-                a.dtemp[h] = acc;
-            }
-        }
+    const int hh = blockIdx.x * (256 / WAVE) + threadIdx.x / WAVE;  // 2 * head + which
+    if (hh >= 2 * a.Hq) return;
+    const int h = hh / 2, kv = h / a.G, g = h % a.G;
+    const int lane = lane_id();
+    const int64_t nslot = (int64_t)a.batch * a.nkb * BW;          // (block, wave) slots
+    float acc = 0.0f;
+    for (int64_t sl = lane; sl < nslot; sl += WAVE) {
+        const int64_t blk = sl / BW, ww = sl % BW;
+        acc += a.gt_part[((blk * a.Hkv + kv) * BW + ww) * a.G * 2 + 2 * g + hh % 2];
+    }
+    acc = wave_sum(acc);
+    if (lane != 0) return;
+    if (hh % 2 == 0) {
+        if (a.dgain != nullptr) a.dgain[h] = acc;
+    } else {
+        a.dtemp[h] = acc;
     }
 }
 
@@ -456,8 +459,9 @@ hipError_t launch_dh(BwdArgs& a, const AttnShape& sh, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_q_kernel<DH>, dim3(a.nkb, a.Hq, sh.batch), dim3(BT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)std::max<int64_t>(1, (a.Kt + 255) / 256)),
-                       dim3(256), 0, st, a);
+    const int64_t red_blocks = std::max<int64_t>((a.Kt + 255) / 256, (2 * a.Hq + 3) / 4);
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)std::max<int64_t>(1, red_blocks)), dim3(256), 0,
+                       st, a);
     return hipGetLastError();
 }
 

@@ -87,18 +87,23 @@ __global__ __launch_bounds__(DZ_THREADS) void gate_dz_kernel(const T* __restrict
     }
 }
 
+// One wave per output: lanes sum a strided share of the partials, then a
+// fixed shuffle tree combines the lanes (deterministic).
 __global__ __launch_bounds__(256) void gate_bwd_reduce_kernel(const float* __restrict__ part,
                                                               int nblk, int dg,
                                                               float* __restrict__ dw2,
                                                               float* __restrict__ db1,
                                                               float* __restrict__ db2) {
-    for (int i = threadIdx.x; i < 2 * dg + 1; i += blockDim.x) {
-        float acc = 0.0f;
-        for (int b = 0; b < nblk; ++b) acc += part[(int64_t)b * (2 * dg + 1) + i];
-        if (i < dg) dw2[i] = acc;
-        else if (i < 2 * dg) { if (db1 != nullptr) db1[i - dg] = acc; }
-        else db2[0] = acc;
-    }
+    const int i = blockIdx.x * (256 / WAVE) + threadIdx.x / WAVE;  // output index
+    if (i >= 2 * dg + 1) return;
+    const int lane = lane_id();
+    float acc = 0.0f;
+    for (int b = lane; b < nblk; b += WAVE) acc += part[(int64_t)b * (2 * dg + 1) + i];
+    acc = wave_sum(acc);
+    if (lane != 0) return;
+    if (i < dg) dw2[i] = acc;
+    else if (i < 2 * dg) { if (db1 != nullptr) db1[i - dg] = acc; }
+    else db2[0] = acc;
 }
 
 struct GateBwdLayout {
@@ -151,8 +156,8 @@ hipError_t run(tg_dtype dt, const T* x, int64_t Kt, int d, const T* w1, const T*
     hipLaunchKernelGGL(gate_dz_kernel<T>, dim3((unsigned)L.nblk), dim3(DZ_THREADS), 0, st, zlin, b1,
                        w2, ds, Kt, dg, dz, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(gate_bwd_reduce_kernel, dim3(1), dim3(256), 0, st, part, (int)L.nblk, dg, dw2,
-                       db1, db2);
+    hipLaunchKernelGGL(gate_bwd_reduce_kernel, dim3((unsigned)((2 * dg + 1 + 3) / 4)), dim3(256), 0, st,
+                       part, (int)L.nblk, dg, dw2, db1, db2);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = transpose(w1, dg, d, w1T, dg, st)) != hipSuccess) return e;        // W1^T [d][dg]
     if ((e = lin(dz, w1T, dx, Kt, d, dg)) != hipSuccess) return e;              // dx = dZ W1

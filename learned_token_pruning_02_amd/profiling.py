@@ -46,6 +46,9 @@ KERNELS = [
     ("bwd_kv_kernel", "backward", "learned_token_pruning_02_amd/csrc/attn_bwd.hip"),
     ("bwd_q_kernel", "backward", "learned_token_pruning_02_amd/csrc/attn_bwd.hip"),
     ("bwd_reduce_kernel", "backward", "learned_token_pruning_02_amd/csrc/attn_bwd.hip"),
+    ("gate_dz_kernel", "gate backward", "learned_token_pruning_02_amd/csrc/gate_bwd.hip"),
+    ("gate_bwd_reduce_kernel", "gate backward", "learned_token_pruning_02_amd/csrc/gate_bwd.hip"),
+    ("transpose_kernel", "gate backward", "learned_token_pruning_02_amd/csrc/gate_bwd.hip"),
     ("decode_chunk_kernel", "decode", "learned_token_pruning_02_amd/csrc/decode.hip"),
     ("decode_merge_kernel", "decode", "learned_token_pruning_02_amd/csrc/decode.hip"),
 ]
