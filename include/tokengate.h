@@ -137,6 +137,11 @@ tg_status tg_gate_score(tg_dtype dt, const void *hidden, int64_t T, int32_t d_mo
  *               16-byte aligned (may be NULL when that size is 0).  Its
  *               contents on entry do not matter; calls that share one
  *               workspace must not run concurrently.
+ * Two implementations give identical results: when every request's document
+ * has at most 32768 tokens, one 1024-thread workgroup per request selects in
+ * LDS in a single launch (the workspace is then unused); otherwise the
+ * document is cut into chunks over many workgroups.  Setting the environment
+ * variable TG_SELECT_PATH=multi forces the chunked path (for testing).
  * Errors: those of tg_plan, TG_ERR_NULL_PTR, TG_ERR_WORKSPACE, TG_ERR_LAUNCH.
  */
 tg_status tg_topk_select(const float *scores, const tg_batch *b, int32_t *kept_idx,

@@ -30,6 +30,7 @@
 //      table per workgroup), and the question tail after them.
 // Results do not depend on which workgroup finishes last.
 #include <algorithm>
+#include <cstdlib>
 
 #include "tg_device.h"
 #include "tg_kernels.h"
@@ -623,6 +624,149 @@ void chunk_plan(const BatchArgs& a, SelArgs* s, int* doc_chunks, int* all_chunks
     *all_chunks = ac;
 }
 
+// ------------------------------------------------ one-workgroup path ----
+// When every document of the batch is short enough, each request is selected
+// by one 1024-thread workgroup in a single launch: thread t holds the keys of
+// the document positions [t*IT, (t+1)*IT) in registers, three histogram
+// passes (11, 11, 10 key bits; one private 2048-bin LDS histogram per wave,
+// so atomics only contend within a wave -- gate scores crowd a few dozen
+// top-bit bins) find the exact K_doc-th best key T and how many keys equal
+// to T are kept, and one ordered compaction (block scans of the keys equal
+// to T in index order, then of the kept tokens) writes the kept ids.  No
+// workspace, no global atomics.
+constexpr int SM_THREADS = 1024;
+constexpr int SM_WAVES = SM_THREADS / WAVE;
+constexpr int SM_IT = 32;                       // keys per thread at most
+constexpr int SM_MAX = SM_THREADS * SM_IT;      // 32768 document tokens per request
+
+// Exclusive block scan over 1024 threads; *total gets the sum.
+__device__ __forceinline__ uint32_t scan1024_excl(uint32_t v, uint32_t* wtot, uint32_t* total) {
+    const int lane = lane_id(), w = threadIdx.x / WAVE;
+    uint32_t x = v;
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint32_t n = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += n;
+    }
+    if (lane == WAVE - 1) wtot[w] = x;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < SM_WAVES; ++i) {
+        if (i < w) before += wtot[i];
+        all += wtot[i];
+    }
+    __syncthreads();
+    *total = all;
+    return x - v + before;
+}
+
+__global__ __launch_bounds__(SM_THREADS) void sel_small_kernel(SelArgs a) {
+    __shared__ uint32_t whist[SM_WAVES][NBIN];   // 128 KiB: one histogram per wave
+    __shared__ uint32_t wtot[SM_WAVES];
+    __shared__ uint32_t sh_d, sh_rem;
+
+    const int b = blockIdx.x, tid = threadIdx.x, w = tid / WAVE, lane = lane_id();
+    if (b == 0 && a.cu_dev != nullptr)
+        for (int i = tid; i <= a.batch; i += SM_THREADS) a.cu_dev[i] = a.out[i];
+    const int off = a.off[b], N = a.off[b + 1] - off;
+    const int out = a.out[b], K = a.out[b + 1] - out;
+    int32_t* kept = a.kept + out;
+    if (K >= N) {  // the budget covers the request
+        for (int i = tid; i < N; i += SM_THREADS) kept[i] = off + i;
+        return;
+    }
+    const int q = a.q[b], p = a.p[b];
+    const int ndoc = N - q - p, kdoc = K - q - p;
+    for (int i = tid; i < p; i += SM_THREADS) kept[i] = off + i;
+    for (int i = tid; i < q; i += SM_THREADS) kept[p + kdoc + i] = off + N - q + i;
+
+    const int IT = (ndoc + SM_THREADS - 1) / SM_THREADS;
+    const int i0 = min(ndoc, tid * IT), i1 = min(ndoc, i0 + IT);
+    const int nmine = i1 - i0;
+    uint32_t kr[SM_IT];
+    const float* s = a.scores + off + p + i0;
+#pragma unroll
+    for (int j = 0; j < SM_IT; ++j) kr[j] = j < nmine ? order_key(s[j]) : 0u;
+
+    // Threshold key T (the kdoc-th best key) and `need`, the number of keys
+    // equal to T that are kept (the lowest-indexed ones).  kdoc == 0 keeps
+    // nothing: T above every key.
+    uint32_t thr = 0xffffffffu, need = 0;
+    if (kdoc > 0) {
+        uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kdoc;
+        uint32_t* hw = whist[w];
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+            const int width = pass == 2 ? 10 : 11;
+            const uint32_t dmask = (1u << width) - 1u;
+            for (int i = lane; i < NBIN; i += WAVE) hw[i] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < SM_IT; ++j)
+                if (j < nmine && (kr[j] & pmask) == prefix) atomicAdd(&hw[(kr[j] >> shift) & dmask], 1u);
+            __syncthreads();
+            // Thread t owns bins 2047-2t and 2046-2t (descending order in thread order).
+            const int hi = NBIN - 1 - 2 * tid;
+            uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+            for (int ww = 0; ww < SM_WAVES; ++ww) {
+                c0 += whist[ww][hi];
+                c1 += whist[ww][hi - 1];
+            }
+            uint32_t tot;
+            const uint32_t above = scan1024_excl(c0 + c1, wtot, &tot);  // keys in higher bins
+            if (above < rem && rem <= above + c0) {
+                sh_d = (uint32_t)hi;
+                sh_rem = rem - above;
+            } else if (above + c0 < rem && rem <= above + c0 + c1) {
+                sh_d = (uint32_t)(hi - 1);
+                sh_rem = rem - above - c0;
+            }
+            __syncthreads();
+            prefix |= sh_d << shift;
+            pmask |= dmask << shift;
+            rem = sh_rem;
+            __syncthreads();
+        }
+        thr = prefix;
+        need = rem;
+    }
+
+    // Ordered compaction over this thread's positions [i0, i1).
+    uint32_t eq = 0;
+#pragma unroll
+    for (int j = 0; j < SM_IT; ++j) eq += (j < nmine && kr[j] == thr) ? 1u : 0u;
+    uint32_t tot;
+    const uint32_t eq_before = scan1024_excl(eq, wtot, &tot);
+    uint32_t nk = 0, e = eq_before;
+#pragma unroll
+    for (int j = 0; j < SM_IT; ++j) {
+        const bool t_eq = j < nmine && kr[j] == thr;
+        nk += (j < nmine && kr[j] > thr) || (t_eq && e < need);
+        e += t_eq;
+    }
+    uint32_t pos = scan1024_excl(nk, wtot, &tot);
+    int32_t* dst = kept + p;
+    e = eq_before;
+#pragma unroll
+    for (int j = 0; j < SM_IT; ++j) {
+        const bool t_eq = j < nmine && kr[j] == thr;
+        if ((j < nmine && kr[j] > thr) || (t_eq && e < need)) dst[pos++] = off + p + i0 + j;
+        e += t_eq;
+    }
+}
+
+}  // namespace
+
+namespace {
+bool small_batch(const BatchArgs& a) {
+    const char* path = std::getenv("TG_SELECT_PATH");  // "multi": always the chunked path
+    if (path != nullptr && path[0] == 'm') return false;
+    for (int b = 0; b < a.batch; ++b)
+        if (a.cu_seq[b + 1] - a.cu_seq[b] - a.q_len[b] - a.p_len[b] > SM_MAX) return false;
+    return true;
+}
 }  // namespace
 
 size_t select_workspace_bytes(const BatchArgs& a) {
@@ -643,13 +787,17 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
         s.q[b] = a.q_len[b];
         s.p[b] = a.p_len[b];
     }
+    s.scores = scores;
+    s.kept = kept;
+    s.cu_dev = cu_dev;
+    if (small_batch(a)) {  // every document fits in one workgroup's LDS
+        hipLaunchKernelGGL(sel_small_kernel, dim3(a.batch), dim3(SM_THREADS), 0, st, s);
+        return hipGetLastError();
+    }
     int dc, ac;
     chunk_plan(a, &s, &dc, &ac);
     const WsLayout L = ws_layout(a.batch, dc, a.cu_seq[a.batch]);
     char* base = (char*)ws;
-    s.scores = scores;
-    s.kept = kept;
-    s.cu_dev = cu_dev;
     s.hist = (uint32_t*)(base + L.hist);
     s.meta = (uint32_t*)(base + L.meta);
     s.ctr = (uint32_t*)(base + L.ctr);

@@ -5,6 +5,7 @@ tolerance.  Selection, run on the oracle's fp32 scores: bit-exact kept ids.
 Gather: bitwise.
 """
 import math
+import os
 
 import pytest
 import torch
@@ -84,15 +85,28 @@ def test_gate_deterministic():
 
 # ---------------------------------------------------------------- select ----
 def _select_case(seq, q, bud, scores, prefix=None):
-    announce(f"select B={len(seq)} T={sum(seq)} seq={seq[:4]} q={q[:4]} budget={bud[:4]}"
-             + ("" if prefix is None else f" prefix={prefix[:4]}"))
+    """Both implementations (one workgroup per request when every document
+    fits in LDS, the chunked multi-workgroup path otherwise or when forced)
+    must give the oracle's kept ids bit for bit, and the device cu_kept."""
     ref, cu_ref = oracle.topk_select(scores, seq, q, bud, prefix)
-    got, cu = tg.tg_topk_select(scores.cuda(), seq, q, bud,
-                                cu_kept_dev=torch.empty(len(seq) + 1, dtype=torch.int32, device="cuda"),
-                                prefix_len=prefix)
-    torch.cuda.synchronize()
-    assert cu == cu_ref
-    assert torch.equal(got.cpu(), ref), "kept ids differ"
+    sg = scores.cuda()
+    for path in ("auto", "multi"):
+        announce(f"select[{path}] B={len(seq)} T={sum(seq)} seq={seq[:4]} q={q[:4]} budget={bud[:4]}"
+                 + ("" if prefix is None else f" prefix={prefix[:4]}"))
+        old = os.environ.pop("TG_SELECT_PATH", None)
+        if path == "multi":
+            os.environ["TG_SELECT_PATH"] = "multi"
+        try:
+            cu_dev = torch.full((len(seq) + 1,), -1, dtype=torch.int32, device="cuda")
+            got, cu = tg.tg_topk_select(sg, seq, q, bud, cu_kept_dev=cu_dev, prefix_len=prefix)
+            torch.cuda.synchronize()
+        finally:
+            os.environ.pop("TG_SELECT_PATH", None)
+            if old is not None:
+                os.environ["TG_SELECT_PATH"] = old
+        assert cu == cu_ref
+        assert cu_dev.cpu().tolist() == cu_ref, f"{path}: device cu_kept"
+        assert torch.equal(got.cpu(), ref), f"{path}: kept ids differ"
 
 
 @pytest.mark.parametrize("wname", list(workloads.WORKLOADS))
@@ -147,6 +161,21 @@ def test_select_max_batch_and_large_request():
     _select_case(seq, q, bud, torch.randn(sum(seq), generator=g))
     T = 1 << 20
     _select_case([T], [128], [T // 16], workloads.random_scores(T, seed=10))
+
+
+def test_select_one_workgroup_limits():
+    """Documents of exactly 32768 tokens (the largest the one-workgroup path
+    takes), 32769 (chunked path), ties across the threshold, NaN and +-0, a
+    budget of one, and a batch mixing keep-all requests."""
+    g = torch.Generator().manual_seed(30)
+    s = workloads.random_scores(32768 + 64, seed=31, ties=300)
+    s[torch.randint(0, 32768, (500,), generator=g)] = float("nan")
+    s[torch.randint(0, 32768, (500,), generator=g)] = -0.0
+    _select_case([32768 + 64], [64], [5000], s)
+    _select_case([32768 + 65], [64], [5000], workloads.random_scores(32768 + 65, seed=32, ties=300))
+    _select_case([40000], [1], [1], workloads.random_scores(40000, seed=33))
+    seq = [100, 20000, 7, 32768, 513, 20000]                 # the last keeps only its question token
+    _select_case(seq, [10, 100, 7, 0, 13, 1], [100, 3000, 9, 30000, 64, 1], torch.randn(sum(seq), generator=g))
 
 
 def test_select_sweep_scale():
