@@ -8,6 +8,8 @@
 // consecutive columns n per accumulator group: stores are 8-byte runs.
 // x and w k-chunks of 64 are double buffered in LDS; within a chunk lane half
 // h covers k in [32h, 32h+32) for both operands.
+#include <cstdlib>
+
 #include "tg_device.h"
 #include "tg_kernels.h"
 
@@ -32,93 +34,134 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict
 }
 
 // ---------------------------------------------------------------- bf16 ----
-constexpr int LB = 128;        // tile rows (m) and cols (n)
-constexpr int LK = 64;         // k chunk
-constexpr int LS = LK + 8;     // LDS row stride (bf16 elements)
-
-__global__ __launch_bounds__(256, 2) void linear_bf16_kernel(const bf16* __restrict__ x,
-                                                             const bf16* __restrict__ w,
-                                                             bf16* __restrict__ y, int64_t M,
-                                                             int N, int K, int accumulate) {
-    __shared__ __attribute__((aligned(16))) bf16 Xs[2][LB * LS];
-    __shared__ __attribute__((aligned(16))) bf16 Ws[2][LB * LS];
+// WM x WN tiles of 32x32 per wave, GM x GN waves per workgroup, k chunks of
+// KC.  The operands stream through L2, so the workgroup tile sets the
+// FLOPs per byte fetched: <2,2,64,2,2> 128x128 (64 FLOP/B, two workgroups
+// per CU), <4,2,32,2,2> 256x128 (85 FLOP/B), <4,2,32,2,4> 256x256 with eight
+// waves (128 FLOP/B, one workgroup per CU).  Every variant stays under 256
+// registers, so the accumulators live in ordinary VGPRs.
+template <int WM, int WN, int KC, int GM, int GN>
+__global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf16_kernel(
+        const bf16* __restrict__ x, const bf16* __restrict__ w, bf16* __restrict__ y, int64_t M,
+        int N, int K, int accumulate) {
+    constexpr int THREADS = 64 * GM * GN;
+    constexpr int LK = KC;                       // k chunk
+    constexpr int LS = LK + 8;                   // LDS row stride (bf16 elements)
+    constexpr int BM = 32 * WM * GM, BN = 32 * WN * GN;  // workgroup tile rows (m), cols (n)
+    constexpr int XU = BM * (LK / 8) / THREADS;  // 16-byte units per thread of x
+    constexpr int WU = BN * (LK / 8) / THREADS;  // and of w
+    static_assert(XU * THREADS == BM * (LK / 8) && WU * THREADS == BN * (LK / 8), "staging");
+    constexpr int KSTEPS = LK / 16;
+    __shared__ __attribute__((aligned(16))) bf16 Xs[2][BM * LS];
+    __shared__ __attribute__((aligned(16))) bf16 Ws[2][BN * LS];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
     const int wv = tid / WAVE;
-    const int wm = wv % 2, wn = wv / 2;
+    const int wm = wv % GM, wn = wv / GM;
     const int hh = lane / 32, l32 = lane % 32;
-    const int64_t m0 = (int64_t)blockIdx.x * LB;
-    const int n0 = blockIdx.y * LB;
+    const int64_t m0 = (int64_t)blockIdx.x * BM;
+    const int n0 = blockIdx.y * BN;
 
-    // 16-byte units of one 128x64 chunk: 1024, four per thread.
-    u32x4 xr[4], wr[4];
-    auto load = [&](int k0) {
+    // Chunks stream from HBM through a ring of two register sets, issued two
+    // chunks before their compute: chunk s+1 is stored into LDS at the end of
+    // step s, after which its registers take the loads of chunk s+3.
+    struct Regs {
+        u32x4 x[XU], w[WU];
+    };
+    auto load = [&](Regs& r, int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int uu = tid + i * 256;
+        for (int i = 0; i < XU; ++i) {
+            const int uu = tid + i * THREADS;
             const int row = uu / (LK / 8), c = uu % (LK / 8);
             int64_t mr = m0 + row;
             if (mr > M - 1) mr = M - 1;
+            r.x[i] = ld16(x + mr * K + k0 + 8 * c);
+        }
+#pragma unroll
+        for (int i = 0; i < WU; ++i) {
+            const int uu = tid + i * THREADS;
+            const int row = uu / (LK / 8), c = uu % (LK / 8);
             int nr = n0 + row;
             if (nr > N - 1) nr = N - 1;
-            xr[i] = ld16(x + mr * K + k0 + 8 * c);
-            wr[i] = ld16(w + (int64_t)nr * K + k0 + 8 * c);
+            r.w[i] = ld16(w + (int64_t)nr * K + k0 + 8 * c);
         }
     };
-    auto store = [&](int buf) {
+    auto store = [&](const Regs& r, int buf) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int uu = tid + i * 256;
-            const int row = uu / (LK / 8), c = uu % (LK / 8);
-            st16(&Xs[buf][row * LS + 8 * c], xr[i]);
-            st16(&Ws[buf][row * LS + 8 * c], wr[i]);
+        for (int i = 0; i < XU; ++i) {
+            const int uu = tid + i * THREADS;
+            st16(&Xs[buf][(uu / (LK / 8)) * LS + 8 * (uu % (LK / 8))], r.x[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < WU; ++i) {
+            const int uu = tid + i * THREADS;
+            st16(&Ws[buf][(uu / (LK / 8)) * LS + 8 * (uu % (LK / 8))], r.w[i]);
         }
     };
 
-    f32x16 acc[2][2];  // [nt][mt]: D[n][m]
+    f32x16 acc[WN][WM];  // [nt][mt]: D[n][m]
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < WN; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < WM; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
     const int nsteps = K / LK;
-    load(0);
-    store(0);
+    const int last = (nsteps - 1) * LK;
+    Regs ra, rb;
+    load(ra, 0);
+    store(ra, 0);
+    load(ra, min(LK, last));
+    load(rb, min(2 * LK, last));
     __syncthreads();
-    for (int s = 0; s < nsteps; ++s) {
-        const int buf = s & 1;
-        const bool more = s + 1 < nsteps;
-        if (more) load((s + 1) * LK);
+    // Branch-free so that every wait for a register set is a partial one:
+    // past the end the chunk index clamps to the last chunk, and the extra
+    // loads and stores go to a buffer nobody reads again.
+    auto mma = [&](int buf) {
+        // Within a chunk, lane half hh covers k in [hh*LK/2, (hh+1)*LK/2) for
+        // both operands (a permutation of k shared by A and B).
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            bf16x8 af[2], bfv[2];
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+            bf16x8 af[WN], bfv[WM];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                af[t] = as_bf16x8(ld16(&Ws[buf][(64 * wn + 32 * t + l32) * LS + 32 * hh + 8 * kk]));
-                bfv[t] = as_bf16x8(ld16(&Xs[buf][(64 * wm + 32 * t + l32) * LS + 32 * hh + 8 * kk]));
-            }
+            for (int t = 0; t < WN; ++t)
+                af[t] = as_bf16x8(ld16(&Ws[buf][(32 * WN * wn + 32 * t + l32) * LS + (LK / 2) * hh + 8 * kk]));
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int t = 0; t < WM; ++t)
+                bfv[t] = as_bf16x8(ld16(&Xs[buf][(32 * WM * wm + 32 * t + l32) * LS + (LK / 2) * hh + 8 * kk]));
 #pragma unroll
-                for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = mfma32(af[nt], bfv[mt], acc[nt][mt]);
+            for (int nt = 0; nt < WN; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < WM; ++mt) acc[nt][mt] = mfma32(af[nt], bfv[mt], acc[nt][mt]);
         }
-        if (more) store(buf ^ 1);
+    };
+    // step s: compute chunk s from LDS; nx holds chunk s+1 (stored now) and
+    // then takes the loads of chunk s+3.
+    auto step = [&](int s, Regs& nx) {
+        mma(s & 1);
+        store(nx, (s + 1) & 1);
+        load(nx, min((s + 3) * LK, last));
         __syncthreads();
+    };
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {  // two steps per trip: the register sets alternate
+        step(s, ra);
+        step(s + 1, rb);
     }
+    if (s < nsteps) mma(s & 1);  // odd count: the last chunk is already in LDS
 
-    // D[n][m]: lane owns m = 64wm + 32mt + l32, n = 64wn + 32nt + 8(r/4) + 4hh + r%4.
+    // D[n][m]: lane owns m = 32WM wm + 32mt + l32, n = 32WN wn + 32nt + 8(r/4) + 4hh + r%4.
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int64_t m = m0 + 64 * wm + 32 * mt + l32;
+    for (int mt = 0; mt < WM; ++mt) {
+        const int64_t m = m0 + 32 * WM * wm + 32 * mt + l32;
         if (m >= M) continue;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < WN; ++nt) {
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
-                const int nn = n0 + 64 * wn + 32 * nt + 8 * rq + 4 * hh;
+                const int nn = n0 + 32 * WN * wn + 32 * nt + 8 * rq + 4 * hh;
                 if (nn >= N) continue;
                 bf16x4* dst = reinterpret_cast<bf16x4*>(y + m * N + nn);
                 bf16x4 ov;
@@ -148,9 +191,27 @@ hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M
 
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
                               int accumulate, hipStream_t st) {
-    const dim3 grid((unsigned)((M + LB - 1) / LB), (unsigned)((N + LB - 1) / LB));
-    hipLaunchKernelGGL(linear_bf16_kernel, grid, dim3(256), 0, st, (const bf16*)x,
-                       (const bf16*)w, (bf16*)y, M, N, K, accumulate);
+    // The largest tile that still gives every CU at least one workgroup
+    // (two for the 256x128 tile, which runs two per CU).
+    // TG_LINEAR_TILE=small|mid|large forces one (for testing).
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
+    const char* force = std::getenv("TG_LINEAR_TILE");
+    const char f = force != nullptr ? force[0] : 0;
+    const int choice = f == 's' ? 0 : f == 'm' ? 1 : f == 'l' ? 2 : (t256 >= 256 ? 2 : t128 >= 512 ? 1 : 0);
+    if (choice == 2) {
+        const dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 255) / 256));
+        hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 4>), grid, dim3(512), 0, st,
+                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate);
+    } else if (choice == 1) {
+        const dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 127) / 128));
+        hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 2>), grid, dim3(256), 0, st,
+                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate);
+    } else {
+        const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
+        hipLaunchKernelGGL((linear_bf16_kernel<2, 2, 64, 2, 2>), grid, dim3(256), 0, st,
+                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate);
+    }
     return hipGetLastError();
 }
 

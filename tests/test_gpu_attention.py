@@ -219,11 +219,40 @@ def test_attention_eight_wave_sampled(name, lens, Hq, Hkv, dh):
 
 
 # ---------------------------------------------------------------- linear ----
+@pytest.mark.parametrize("tile", ["small", "mid", "large"])
+def test_linear_every_tiling(tile):
+    """Each workgroup tiling (128x128, 256x128, 256x256; the launcher picks
+    one by output size, TG_LINEAR_TILE forces it) on ragged m and n, with odd
+    (K = 192 in 64-wide chunks) and even numbers of k chunks, accumulating and
+    not."""
+    import os
+    rt, at = tol(torch.bfloat16)
+    for M, N, K, acc in ((777, 320, 2048, False), (1000, 192, 192, True), (300, 2112, 64, True)):
+        announce(f"linear tile={tile} M={M} N={N} K={K} acc={acc}")
+        g = torch.Generator().manual_seed(M * 7 + N)
+        x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+        w = (torch.randn(N, K, generator=g) / K ** 0.5).to(torch.bfloat16)
+        y0 = torch.randn(M, N, generator=g).to(torch.bfloat16)
+        y = y0.cuda().clone()
+        os.environ["TG_LINEAR_TILE"] = tile
+        try:
+            tg.tg_linear(x.cuda(), w.cuda(), y=y, accumulate=acc)
+            torch.cuda.synchronize()
+        finally:
+            os.environ.pop("TG_LINEAR_TILE", None)
+        ref = oracle.linear(x, w) + (y0.double() if acc else 0.0)
+        assert_within(y.cpu(), ref, rt, at, f"linear {tile}")
+
+
 @pytest.mark.parametrize("M,N,K,dtype,acc", [
     (300, 192, 256, torch.bfloat16, False),
     (300, 192, 256, torch.bfloat16, True),
     (1, 64, 64, torch.bfloat16, True),
     (4096, 1024, 2048, torch.bfloat16, False),
+    # 256x128-tile kernel (taken when the output has >= 512 such tiles): ragged m and n
+    (8192 + 77, 2048 + 64, 2048, torch.bfloat16, False),
+    (8192 + 77, 2048 + 64, 2048, torch.bfloat16, True),
+    (16384 + 5, 4096, 64, torch.bfloat16, True),
     (37, 50, 20, torch.float32, False),
     (37, 50, 20, torch.float32, True),
 ])
