@@ -264,8 +264,8 @@ tg_status tg_attn_backward_plan(const int32_t *cu_kept_host, int32_t batch, int3
  * NULL (no bias term) or all non-NULL.  Every gradient is overwritten.
  * ws: tg_attn_backward_plan bytes, caller-owned, 16-byte aligned, no
  * initialisation needed.  Deterministic: no floating-point atomics.
- * Supported: TG_BF16 only, d_head in {64, 128}, Hq % Hkv == 0, per-request
- * K/V spans below 2 GiB; else TG_ERR_UNSUPPORTED.
+ * Supported: TG_BF16 only, d_head in {64, 128}, Hq % Hkv == 0 with
+ * Hq / Hkv <= 64, per-request K/V spans below 2 GiB; else TG_ERR_UNSUPPORTED.
  * Errors: TG_ERR_BAD_DTYPE, TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE,
  * TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT, TG_ERR_WORKSPACE, TG_ERR_ALIAS,
  * TG_ERR_LAUNCH.

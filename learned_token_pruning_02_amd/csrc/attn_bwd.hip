@@ -39,6 +39,7 @@ constexpr int BW = 4;            // waves per workgroup
 constexpr int BT = BW * WAVE;
 constexpr int TB = 32;           // rows per wave (keys or queries) and per tile
 constexpr int TPAD = TB + 4;     // transposed tile row: 32 rows + pad, 8-byte aligned
+constexpr int BWD_MAX_GROUP = 64;  // query heads per KV head (Hq / Hkv) supported
 
 struct BwdArgs {
     const bf16* q;      // [Kt][Hq][DH]
@@ -127,6 +128,8 @@ struct TileStage {
     static constexpr int PER = 2 * TB * SEGS / BT;  // segments per thread
     u32x4 r[PER];
 
+    // Rows past `rows` clamp to the last row (no branch, so no wait at a
+    // join); the kernels mask everything those rows contribute.
     __device__ __forceinline__ void fetch(const bf16* m0, const bf16* m1, int64_t stride, int row0,
                                           int rows, int tid) {
 #pragma unroll
@@ -134,9 +137,9 @@ struct TileStage {
             const int idx = tid + BT * u;
             const int mat = idx / (TB * SEGS), rem = idx % (TB * SEGS);
             const int rr = rem % TB, seg = rem / TB;
-            const int row = row0 + rr;
+            const int row = min(row0 + rr, rows - 1);
             const bf16* base = mat == 0 ? m0 : m1;
-            r[u] = row < rows ? ld16(base + (int64_t)row * stride + seg * 8) : u32x4{0u, 0u, 0u, 0u};
+            r[u] = ld16(base + (int64_t)row * stride + seg * 8);
         }
     }
     // rm: [2][TB*RP] row-major tiles; tr: [ntrans][DH*TPAD] transposed tiles
@@ -170,6 +173,7 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
     __shared__ __align__(16) bf16 Rm[2][2 * TB * RP];     // [buffer] Q | dO, row-major
     __shared__ __align__(16) bf16 Tr[2][2 * DH * TPAD];   // [buffer] Q^T | dO^T
     __shared__ float lse2[2][TB], Dq[2][TB];
+    __shared__ float s_tau[BWD_MAX_GROUP], s_gain[BWD_MAX_GROUP];
 
     const int kb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int lo = a.cu[b], n = a.cu[b + 1] - lo;
@@ -200,23 +204,36 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
         for (int r = 0; r < 16; ++r) dkT[m][r] = dvT[m][r] = 0.0f;
     float ds_acc = 0.0f, dg_acc = 0.0f, dt_acc = 0.0f;
 
+    // Per-head constants staged once: loads issued inside the loop after the
+    // prefetch would make every wait for them a wait for the prefetch too
+    // (the vector-memory counter retires in order).
+    for (int g = tid; g < a.G; g += BT) {
+        s_tau[g] = a.temp[kvh * a.G + g];
+        s_gain[g] = a.gain != nullptr ? a.gain[kvh * a.G + g] : 0.0f;
+    }
+
     const int nqb = (n - q0 + TB - 1) / TB;       // query blocks from the block's first key
     const int iters = a.G * nqb;
     const int64_t hs = (int64_t)a.Hq * DH;        // row stride of q and dout
     Stage st;
     float pl = 0.0f;
+    bool pl_ok = false;
+    const float* const lse_p = a.lse;
+    const float* const d_p = a.D;
+    const float* const row_src = tid < TB ? lse_p : d_p;  // this thread's per-row value
     auto fetch = [&](int it) {
         const int h = kvh * a.G + it / nqb, i0 = q0 + TB * (it % nqb);
         st.fetch(a.q + (int64_t)lo * hs + h * DH, a.dout + (int64_t)lo * hs + h * DH, hs, i0, n, tid);
+        // branch-free: the row index clamps, the value is masked when stored
         const int rr = tid % TB;
-        const bool ok = tid < 2 * TB && i0 + rr < n;
-        const int64_t at = (int64_t)h * a.Kt + lo + i0 + rr;
-        pl = !ok ? 0.0f : (tid < TB ? a.lse[at] * LOG2E : a.D[at]);
+        pl_ok = i0 + rr < n;
+        const int64_t at = (int64_t)h * a.Kt + lo + min(i0 + rr, n - 1);
+        pl = row_src[at];
     };
     auto put = [&](int buf) {
         st.put(Rm[buf], Tr[buf], 2, tid);
-        if (tid < TB) lse2[buf][tid] = pl;
-        else if (tid < 2 * TB) Dq[buf][tid - TB] = pl;
+        if (tid < TB) lse2[buf][tid] = pl_ok ? pl * LOG2E : 0.0f;
+        else if (tid < 2 * TB) Dq[buf][tid - TB] = pl_ok ? pl : 0.0f;
     };
     fetch(0);
     put(0);
@@ -230,8 +247,8 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
         // past the request) is masked to P = dL = 0 below.  A branch here
         // would make the compiler copy the loop-carried accumulators.
         {
-            const float tau = a.temp[h];
-            const float gn = a.gain != nullptr ? a.gain[h] : 0.0f;
+            const float tau = s_tau[g];
+            const float gn = s_gain[g];
             const float c1 = tau * a.inv_sqrt_dh * LOG2E;
             const float bias2 = gn * s_key * LOG2E;
             const float kscale = tau * a.inv_sqrt_dh;
@@ -351,15 +368,18 @@ __global__ __launch_bounds__(BT, 2) void bwd_q_kernel(BwdArgs a) {
     const int iters = (jend + TB - 1) / TB;
     Stage st;
     float pb = 0.0f;
+    bool pb_ok = false;
+    const float* sp = a.s != nullptr ? a.s : a.temp;  // any readable array when there is no bias
     auto fetch = [&](int it) {
         const int j0 = TB * it;
         st.fetch(kh, vh, ks, j0, n, tid);
-        const bool ok = tid < TB && j0 + tid < n && a.s != nullptr;
-        pb = ok ? gn * a.s[lo + j0 + tid] * LOG2E : 0.0f;
+        // branch-free: the key index clamps, the value is masked when stored
+        pb_ok = a.s != nullptr && j0 + (tid % TB) < n;
+        pb = sp[a.s != nullptr ? lo + min(j0 + tid % TB, n - 1) : 0];
     };
     auto put = [&](int buf) {
         st.put(Rm[buf], Tr[buf], 1, tid);
-        if (tid < TB) sb2[buf][tid] = pb;
+        if (tid < TB) sb2[buf][tid] = pb_ok ? gn * pb * LOG2E : 0.0f;
     };
     fetch(0);
     put(0);

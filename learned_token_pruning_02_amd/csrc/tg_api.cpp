@@ -291,7 +291,7 @@ tg_status tg_gated_attn_backward(tg_dtype dt, const void* q, const void* k, cons
     tg::AttnShape sh;
     const tg_status st = attn_shape(cu_kept_host, batch, Hq, Hkv, d_head, &sh);
     if (st != TG_OK) return st;
-    if (dt != TG_BF16 || (d_head != 64 && d_head != 128)) return TG_ERR_UNSUPPORTED;
+    if (dt != TG_BF16 || (d_head != 64 && d_head != 128) || Hq / Hkv > 64) return TG_ERR_UNSUPPORTED;
     for (int i = 0; i < batch; ++i)
         if ((int64_t)(cu_kept_host[i + 1] - cu_kept_host[i]) * Hq * d_head * 2 >= I32_LIMIT)
             return TG_ERR_UNSUPPORTED;
