@@ -128,6 +128,21 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mt][nt][r] = 0.f;
 
+    // This lane's epilogue units (b1 and w2 of units 32nt + l32), loaded before
+    // the main loop and branch-free (w2 stands in for a missing b1 and the
+    // value is dropped), so that no wait for them follows the loop.
+    float bias[NT], wout[NT];
+    {
+        const bf16* bsrc = b1 != nullptr ? b1 : w2;
+        const float bkeep = b1 != nullptr ? 1.0f : 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int u = 32 * nt + l32;
+            bias[nt] = to_f32(bsrc[u]) * bkeep;
+            wout[nt] = to_f32(w2[u]);
+        }
+    }
+
     const int nsteps = d / GK;
     // Each workgroup walks the k chunks starting at its own offset, so that
     // concurrent workgroups read different column slices of their rows (and
@@ -289,13 +304,6 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
     // partial of token slot j = 16mt + r into row 2j + hh, and lane i then adds
     // up row i (token slot i/2, half i%2), a transpose instead of 32
     // five-level shuffle butterflies.
-    float bias[NT], wout[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int u = 32 * nt + l32;
-        bias[nt] = b1 != nullptr ? to_f32(b1[u]) : 0.f;
-        wout[nt] = to_f32(w2[u]);
-    }
     float* rt = (RED_IN_WL ? reinterpret_cast<float*>(&wl[0][0]) : red_own) + w * RED_FLOATS;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
