@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--workload", default="qwen3_1p7b_128k_niah")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--eager", action="store_true",
+                   help="time the step as separate launches instead of one HIP graph replay")
     p.add_argument("--detail", default="", help="also write per-kernel detail JSON to this path")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of 512 MiB (reference for HBM byte counters)")
@@ -561,7 +563,36 @@ def main():
     samples = {n: sorted(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
     per = {n: sum(v) / len(v) for n, v in samples.items()}  # ms per launch (mean)
     gpu_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step_eager = wall * 1e3 / args.steps
+    ms_per_step = ms_per_step_eager
+    launch = "eager (one launch per kernel)"
+    if not args.eager:
+        # The whole step (every shape is fixed by the host-side plan, nothing
+        # in it reads back to the host or clears memory with a memset) is
+        # captured once as a HIP graph; K replays are timed, so the kernels
+        # run back to back without per-launch gaps.  A replay must reproduce
+        # the eager step's outputs bit for bit.
+        ref_out, ref_kept = layer.out.clone(), layer.kept.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        layer.out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not (torch.equal(layer.out, ref_out) and torch.equal(layer.kept, ref_kept)):
+            raise RuntimeError("graph replay of the step does not reproduce the eager step")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        launch = "hip graph (one step captured, replayed)"
 
     kept_per_req = [layer.cu_kept[i + 1] - layer.cu_kept[i] for i in range(w.batch)]
     alg = algorithmic(w, kept_per_req)
@@ -671,6 +702,8 @@ def main():
         "kernels": kernels,
         "derived": derived,
         "gpu_ms_per_step": gpu_ms,
+        "launch": launch,
+        "ms_per_step_eager": ms_per_step_eager,
     }
     if cold is not None:
         line["cold_after_cache_flush"] = cold

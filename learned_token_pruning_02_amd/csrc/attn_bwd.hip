@@ -97,23 +97,24 @@ __device__ __forceinline__ bf16x8 lds_t_operand(const bf16* T, int dh_row, int c
     return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// D[h][i] = dO_i . O_i over DH, one thread per (row, head).
+// D[h][i] = dO_i . O_i over DH: DH/8 lanes per (row, head), 16 bytes each,
+// so that a wave reads 1 KB of each matrix contiguously per load; a lane
+// butterfly sums the partial dots.
 template <int DH>
 __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= a.Kt * a.Hq) return;
-    const int64_t i = idx / a.Hq;
-    const int h = (int)(idx % a.Hq);
-    const bf16* o = a.out + (i * a.Hq + h) * DH;
-    const bf16* d = a.dout + (i * a.Hq + h) * DH;
+    constexpr int LPR = DH / 8;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t idx = gid / LPR;  // (row, head) pair: row-major [Kt][Hq]
+    const int sub = (int)(gid % LPR);
+    const bool ok = idx < a.Kt * a.Hq;
+    const int64_t at = (ok ? idx : 0) * DH + sub * 8;
+    const bf16x8 x = as_bf16x8(ld16(a.out + at)), y = as_bf16x8(ld16(a.dout + at));
     float acc = 0.0f;
-#pragma unroll 4
-    for (int c = 0; c < DH; c += 8) {
-        const bf16x8 x = as_bf16x8(ld16(o + c)), y = as_bf16x8(ld16(d + c));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
-    }
-    a.D[(int64_t)h * a.Kt + i] = acc;
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) acc += __shfl_xor(acc, o, WAVE);
+    if (ok && sub == 0) a.D[(idx % a.Hq) * a.Kt + idx / a.Hq] = acc;
 }
 
 // Staging of two 32-row tiles (`mats` row-major [rows][stride] bf16
@@ -472,7 +473,7 @@ int key_blocks(const AttnShape& sh) {
 template <int DH>
 hipError_t launch_dh(BwdArgs& a, const AttnShape& sh, hipStream_t st) {
     const int64_t rows = a.Kt * a.Hq;
-    hipLaunchKernelGGL(bwd_dot_kernel<DH>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_dot_kernel<DH>, dim3((unsigned)((rows * (DH / 8) + 255) / 256)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(bwd_kv_kernel<DH>, dim3(a.nkb, a.Hkv, sh.batch), dim3(BT), 0, st, a);

@@ -123,6 +123,7 @@ CASES = [
     ("ragged_dh128", (1, 100, 257), 16, 8, 128, True),
     ("g1_nobias", (130, 64), 4, 4, 128, False),
     ("g4_dh64", (300,), 8, 2, 64, True),
+    ("g3_odd_steps", (77, 200), 6, 2, 128, True),
     ("qwen_2k", (2048,), 16, 8, 128, True),
 ]
 
