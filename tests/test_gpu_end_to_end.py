@@ -129,3 +129,40 @@ def test_stack_reduced_step_by_step():
         assert_within(a, ref_a, 2e-2, 1e-2, f"layer {li} attention")
         ref_x = x_in.double() + oracle.linear(a.view(Kt, Hq * dh), L["wo"])
         assert_within(x.cpu(), ref_x, 2e-2, 1e-2, f"layer {li} residual")
+
+
+def test_gated_layer_graph_replays():
+    """The gated layer captured once as a HIP graph (as the benchmark times
+    it): three replays, each on new inputs written into the captured buffers,
+    with eager work and host synchronisations in between, each equal bit for
+    bit to an eager layer run on the same inputs."""
+    w = workloads.WORKLOADS["qwen3_1p7b_16k"]
+    sh = w.shape
+    announce("gated layer graph replays 16k")
+    g = {k: v.cuda() for k, v in workloads.gate_inputs(w, seed=0).items()}
+    a = {k: v.cuda() for k, v in workloads.attn_inputs(w, seed=0).items()}
+    mk = lambda: GatedLayer(w.total_tokens, sh.d_model, sh.n_q_heads, sh.d_head, w.seq_len,
+                            w.q_len, w.budget, sh.dtype)
+    layer, eager = mk(), mk()
+    run = lambda L: L(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"], a["q"], a["k"], a["v"],
+                      a["gain"], a["temp"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(layer)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(layer)
+    for rep in range(3):
+        gen = torch.Generator(device="cuda").manual_seed(100 + rep)
+        g["hidden"].copy_(torch.randn(g["hidden"].shape, generator=gen, device="cuda"))
+        a["q"].copy_(torch.randn(a["q"].shape, generator=gen, device="cuda"))
+        layer.out.zero_()
+        layer.kept.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        run(eager)
+        torch.cuda.synchronize()
+        for name in ["scores", "kept", "s_kept", "hidden_kept", "out"]:
+            assert torch.equal(getattr(layer, name), getattr(eager, name)), (rep, name)
