@@ -21,7 +21,7 @@
 namespace tg {
 namespace {
 
-constexpr int DZ_ROWS = 64;     // kept rows per workgroup of the dz kernel
+constexpr int DZ_ROWS = 16;     // kept rows per workgroup of the dz kernel
 constexpr int DZ_THREADS = 256;
 
 template <class T>
@@ -50,10 +50,11 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ in
     }
 }
 
-// dz[t][u] from zlin[t][u] = (X W1^T)[t][u]; per-workgroup partial sums of
-// ds*GELU(z) (for dw2), dz (for db1) and ds (for db2).
+// dz[t][u] from zlin = X W1^T, given as S fp32 partials zlin[s][t][u] summed
+// here in slice order; per-workgroup partial sums of ds*GELU(z) (for dw2), dz
+// (for db1) and ds (for db2).
 template <class T>
-__global__ __launch_bounds__(DZ_THREADS) void gate_dz_kernel(const T* __restrict__ zlin,
+__global__ __launch_bounds__(DZ_THREADS) void gate_dz_kernel(const float* __restrict__ zlin, int S,
                                                              const T* __restrict__ b1,
                                                              const T* __restrict__ w2,
                                                              const float* __restrict__ ds,
@@ -68,7 +69,9 @@ __global__ __launch_bounds__(DZ_THREADS) void gate_dz_kernel(const T* __restrict
         const float wu = ld1(w2 + u);
         float sw = 0.0f, sz = 0.0f;
         for (int64_t t = t0; t < t1; ++t) {
-            const float z = ld1(zlin + t * dg + u) + bu;
+            float zs = zlin[t * dg + u];
+            for (int q = 1; q < S; ++q) zs += zlin[((int64_t)q * Kt + t) * dg + u];
+            const float z = zs + bu;
             const float Phi = 0.5f * (1.0f + erff(z * 0.70710678118654752f));
             const float phi = 0.39894228040143268f * __expf(-0.5f * z * z);
             const float d = ds[t];
@@ -106,24 +109,64 @@ __global__ __launch_bounds__(256) void gate_bwd_reduce_kernel(const float* __res
     else db2[0] = acc;
 }
 
+// dW1 = dZ^T X contracts over the kept rows into only d_gate x d outputs, too
+// few tiles to fill the chip: the contraction is split into S slices of at
+// least 512 rows (S <= 16), each writing an fp32 partial, summed in slice
+// order by split_sum_kernel (deterministic).
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part, int S, int64_t n,
+                                                        bf16* __restrict__ y) {
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (i >= n) return;
+    f32x4 acc = __builtin_bit_cast(f32x4, ld16(part + i));
+    for (int z = 1; z < S; ++z) {
+        const f32x4 v = __builtin_bit_cast(f32x4, ld16(part + z * n + i));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    }
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = to_bf16(acc[e]);
+    st8(y + i, __builtin_bit_cast(u32x2, o));
+}
+
+int dw1_slices(tg_dtype dt, int64_t Kt) {
+    if (dt != TG_BF16) return 1;
+    return (int)std::min<int64_t>(16, std::max<int64_t>(1, (Kt + 511) / 512));
+}
+
+// z = X W1^T has d_gate outputs per row: split its contraction over d in up
+// to four slices while the 128x128 tiles alone number fewer than 512.
+int z_slices(tg_dtype dt, int64_t Kt, int d, int dg) {
+    if (dt != TG_BF16) return 1;
+    const int64_t tiles = ((Kt + 127) / 128) * ((dg + 127) / 128);
+    int S = 1;
+    while (S < 4 && tiles * S < 512 && d % (64 * 2 * S) == 0) S *= 2;
+    return S;
+}
+
 struct GateBwdLayout {
     int64_t kt_pad, nblk;
-    size_t zlin, dz, dzT, xT, w1T, part, total;
+    int slices, zs;
+    size_t zlin, dz, dzT, xT, w1T, part, dw1p, total;
 };
 
 GateBwdLayout layout(tg_dtype dt, int64_t Kt, int d, int dg) {
     const int64_t eb = dt == TG_BF16 ? 2 : 4;
     const auto up = [](int64_t x) { return (size_t)((x + 255) / 256 * 256); };
     GateBwdLayout L;
-    L.kt_pad = (Kt + 63) / 64 * 64;
+    L.slices = dw1_slices(dt, Kt);
+    L.zs = z_slices(dt, Kt, d, dg);
+    const int64_t q = 64 * L.slices;  // every slice a whole number of 64-row chunks
+    L.kt_pad = (Kt + q - 1) / q * q;
     L.nblk = (Kt + DZ_ROWS - 1) / DZ_ROWS;
     size_t o = 0;
-    L.zlin = o; o += up(Kt * dg * eb);
+    L.zlin = o; o += up((int64_t)L.zs * Kt * dg * 4);  // fp32 partials of X W1^T
     L.dz = o;   o += up(Kt * dg * eb);
     L.dzT = o;  o += up((int64_t)dg * L.kt_pad * eb);
     L.xT = o;   o += up((int64_t)d * L.kt_pad * eb);
     L.w1T = o;  o += up((int64_t)d * dg * eb);
     L.part = o; o += up(std::max<int64_t>(1, L.nblk) * (2 * dg + 1) * 4);
+    L.dw1p = o; o += L.slices > 1 ? up((int64_t)L.slices * dg * d * 4) : 0;
     L.total = o;
     return L;
 }
@@ -140,7 +183,7 @@ hipError_t run(tg_dtype dt, const T* x, int64_t Kt, int d, const T* w1, const T*
                int dg, const float* ds, T* dx, T* dw1, float* db1, float* dw2, float* db2, char* ws,
                hipStream_t st) {
     const GateBwdLayout L = layout(dt, Kt, d, dg);
-    T* zlin = (T*)(ws + L.zlin);
+    float* zlin = (float*)(ws + L.zlin);
     T* dz = (T*)(ws + L.dz);
     T* dzT = (T*)(ws + L.dzT);
     T* xT = (T*)(ws + L.xT);
@@ -152,8 +195,12 @@ hipError_t run(tg_dtype dt, const T* x, int64_t Kt, int d, const T* w1, const T*
                                                  K, 0, st);
     };
     hipError_t e;
-    if ((e = lin(x, w1, zlin, Kt, dg, d)) != hipSuccess) return e;              // z - b1
-    hipLaunchKernelGGL(gate_dz_kernel<T>, dim3((unsigned)L.nblk), dim3(DZ_THREADS), 0, st, zlin, b1,
+    if (dt == TG_BF16)                                                           // z - b1
+        e = launch_linear_bf16_splitk(x, w1, zlin, Kt, dg, d, L.zs, st);
+    else
+        e = lin(x, w1, (T*)zlin, Kt, dg, d);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gate_dz_kernel<T>, dim3((unsigned)L.nblk), dim3(DZ_THREADS), 0, st, zlin, L.zs, b1,
                        w2, ds, Kt, dg, dz, part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(gate_bwd_reduce_kernel, dim3((unsigned)((2 * dg + 1 + 3) / 4)), dim3(256), 0, st,
@@ -163,7 +210,14 @@ hipError_t run(tg_dtype dt, const T* x, int64_t Kt, int d, const T* w1, const T*
     if ((e = lin(dz, w1T, dx, Kt, d, dg)) != hipSuccess) return e;              // dx = dZ W1
     if ((e = transpose(dz, Kt, dg, dzT, L.kt_pad, st)) != hipSuccess) return e; // dZ^T [dg][Kt_pad]
     if ((e = transpose(x, Kt, d, xT, L.kt_pad, st)) != hipSuccess) return e;    // X^T  [d][Kt_pad]
-    return lin(dzT, xT, dw1, dg, d, (int)L.kt_pad);                             // dW1 = dZ^T X
+    if (L.slices == 1) return lin(dzT, xT, dw1, dg, d, (int)L.kt_pad);         // dW1 = dZ^T X
+    float* dw1p = (float*)(ws + L.dw1p);
+    if ((e = launch_linear_bf16_splitk(dzT, xT, dw1p, dg, d, (int)L.kt_pad, L.slices, st)) != hipSuccess)
+        return e;
+    const int64_t nout = (int64_t)dg * d;
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((nout / 4 + 255) / 256)), dim3(256), 0, st, dw1p,
+                       L.slices, nout, (bf16*)dw1);
+    return hipGetLastError();
 }
 
 }  // namespace

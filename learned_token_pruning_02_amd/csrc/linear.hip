@@ -40,10 +40,13 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict
 // per CU), <4,2,32,2,2> 256x128 (85 FLOP/B), <4,2,32,2,4> 256x256 with eight
 // waves (128 FLOP/B, one workgroup per CU).  Every variant stays under 256
 // registers, so the accumulators live in ordinary VGPRs.
+// Split over k (blockIdx.z = slice): the workgroup contracts k in
+// [z K, (z + 1) K) of rows that are ldk long, and with `part` set writes its
+// fp32 partial to part[z][M][N] instead of y.
 template <int WM, int WN, int KC, int GM, int GN>
 __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf16_kernel(
         const bf16* __restrict__ x, const bf16* __restrict__ w, bf16* __restrict__ y, int64_t M,
-        int N, int K, int accumulate) {
+        int N, int K, int accumulate, int64_t ldk, float* __restrict__ part) {
     constexpr int THREADS = 64 * GM * GN;
     constexpr int LK = KC;                       // k chunk
     constexpr int LS = LK + 8;                   // LDS row stride (bf16 elements)
@@ -62,6 +65,8 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
     const int hh = lane / 32, l32 = lane % 32;
     const int64_t m0 = (int64_t)blockIdx.x * BM;
     const int n0 = blockIdx.y * BN;
+    x += (int64_t)blockIdx.z * K;
+    w += (int64_t)blockIdx.z * K;
 
     // Chunks stream from HBM through a ring of two register sets, issued two
     // chunks before their compute: chunk s+1 is stored into LDS at the end of
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
             const int row = uu / (LK / 8), c = uu % (LK / 8);
             int64_t mr = m0 + row;
             if (mr > M - 1) mr = M - 1;
-            r.x[i] = ld16(x + mr * K + k0 + 8 * c);
+            r.x[i] = ld16(x + mr * ldk + k0 + 8 * c);
         }
 #pragma unroll
         for (int i = 0; i < WU; ++i) {
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
             const int row = uu / (LK / 8), c = uu % (LK / 8);
             int nr = n0 + row;
             if (nr > N - 1) nr = N - 1;
-            r.w[i] = ld16(w + (int64_t)nr * K + k0 + 8 * c);
+            r.w[i] = ld16(w + (int64_t)nr * ldk + k0 + 8 * c);
         }
     };
     auto store = [&](const Regs& r, int buf) {
@@ -163,6 +168,12 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
             for (int rq = 0; rq < 4; ++rq) {
                 const int nn = n0 + 32 * WN * wn + 32 * nt + 8 * rq + 4 * hh;
                 if (nn >= N) continue;
+                if (part != nullptr) {
+                    const f32x4 pv = {acc[nt][mt][4 * rq], acc[nt][mt][4 * rq + 1], acc[nt][mt][4 * rq + 2],
+                                      acc[nt][mt][4 * rq + 3]};
+                    st16(part + ((int64_t)blockIdx.z * M + m) * N + nn, __builtin_bit_cast(u32x4, pv));
+                    continue;
+                }
                 bf16x4* dst = reinterpret_cast<bf16x4*>(y + m * N + nn);
                 bf16x4 ov;
                 if (accumulate) {
@@ -202,16 +213,25 @@ hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, 
     if (choice == 2) {
         const dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 255) / 256));
         hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 4>), grid, dim3(512), 0, st,
-                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate);
+                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate, (int64_t)K, nullptr);
     } else if (choice == 1) {
         const dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 127) / 128));
         hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 2>), grid, dim3(256), 0, st,
-                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate);
+                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate, (int64_t)K, nullptr);
     } else {
         const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
         hipLaunchKernelGGL((linear_bf16_kernel<2, 2, 64, 2, 2>), grid, dim3(256), 0, st,
-                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate);
+                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate, (int64_t)K, nullptr);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_bf16_splitk(const void* x, const void* w, float* part, int64_t M, int N,
+                                     int K, int slices, hipStream_t st) {
+    const int ks = K / slices;  // a multiple of 64 (checked by the caller)
+    const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128), (unsigned)slices);
+    hipLaunchKernelGGL((linear_bf16_kernel<2, 2, 64, 2, 2>), grid, dim3(256), 0, st, (const bf16*)x,
+                       (const bf16*)w, (bf16*)nullptr, M, N, ks, 0, (int64_t)K, part);
     return hipGetLastError();
 }
 

@@ -84,5 +84,8 @@ hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M
                              int accumulate, hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
                               int accumulate, hipStream_t st);
+// part[z][M][N] = x[:, zK/S : (z+1)K/S] . w[:, same]^T in fp32, z < S (K/S a multiple of 64).
+hipError_t launch_linear_bf16_splitk(const void* x, const void* w, float* part, int64_t M, int N,
+                                     int K, int slices, hipStream_t st);
 
 }  // namespace tg

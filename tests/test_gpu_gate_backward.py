@@ -65,6 +65,7 @@ def _run_check(x, w1, b1, w2, ds, what):
 CASES = [
     ("bf16_ragged", 777, 2048, 256, torch.bfloat16, True),
     ("bf16_nobias", 64, 512, 128, torch.bfloat16, False),
+    ("bf16_six_slices", 3001, 1024, 192, torch.bfloat16, True),
     ("bf16_one_row", 1, 128, 64, torch.bfloat16, True),
     ("f32_small", 300, 256, 64, torch.float32, True),
 ]
