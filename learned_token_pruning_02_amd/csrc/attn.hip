@@ -418,6 +418,15 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         sacc[mt_][r_] = y_;                                                                  \
         mx = fmaxf(mx, y_);                                                                  \
     } while (0)
+// The same without the row max (tiles after the first: the max is only
+// taken, in TG_SOFTMAX_TAIL, when a row's probabilities sum past 2^8).
+#define TG_MASK(MASKED, C)                                                                   \
+    do {                                                                                     \
+        const int mt_ = (C) / 16, r_ = (C) % 16;                                             \
+        float y_ = sacc[mt_][r_] * c1;                                                       \
+        if (MASKED && j0 + 32 * mt_ + 8 * (r_ / 4) + 4 * hh + (r_ % 4) > qi) y_ = -INFINITY; \
+        sacc[mt_][r_] = y_;                                                                  \
+    } while (0)
 #define TG_EXP_PAIR(X, SUB)                                                                  \
     do {                                                                                     \
         const int kk_ = (X) / 8, e_ = (X) % 8;                                               \
@@ -435,10 +444,17 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     // rescale owed by a change of base is recorded and the row sum updated.
 #define TG_SOFTMAX_TAIL()                                                                    \
     do {                                                                                     \
-        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                            \
+        /* Every probability is at most the row's sum, so a row whose sum  */                \
+        /* stays within 2^8 cannot have grown past the slack: the row max */                 \
+        /* is only needed when some row's sum exceeds it (or overflows).  */                 \
+        const float ps_ = psum[0] + psum[1];                                                 \
+        const float tot_ = ps_ + __shfl_xor(ps_, 32, WAVE);                                  \
         float pf_new = mcur;                                                                 \
-        const bool grow = mx > RESCALE_SLACK;                                                \
-        if (__any(grow)) {                                                                   \
+        if (__any(!(tot_ <= 0x1p8f))) {                                                      \
+            float mx = -INFINITY;                                                            \
+            _Pragma("unroll") for (int c = 0; c < 32; ++c) mx = fmaxf(mx, sacc[c / 16][c % 16]); \
+            mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));                                        \
+            const bool grow = mx > RESCALE_SLACK;                                            \
             const float m_old = mcur;                                                        \
             if (grow) set_base(m_old + mx);                                                  \
             const bool redo = mx > REBASE_LIMIT;                                             \
@@ -496,8 +512,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         __builtin_amdgcn_sched_barrier(0);                                                   \
         _Pragma("unroll") for (int i = 0; i < NPV; ++i)                                      \
             o[i % NMD] = mfma32(i < NMD ? v0[i] : TG_VFRAG(i), pold[i / NMD], o[i % NMD]);   \
-        float mx = -INFINITY;                                                                \
-        _Pragma("unroll") for (int c = 0; c < 32; ++c) TG_MASK_MAX(MASKED, c);               \
+        _Pragma("unroll") for (int c = 0; c < 32; ++c) TG_MASK(MASKED, c);                   \
         float psum[2] = {0.f, 0.f};                                                          \
         bf16x8 pnew[4];                                                                      \
         _Pragma("unroll") for (int x = 0; x < 32; x += 2) TG_EXP_PAIR(x, 0.f);               \
@@ -527,7 +542,6 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         const int j0 = jt * KVT;                                                             \
         bf16x8 vq[4];                                                                        \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) vq[i] = TG_VFRAG(i);                   \
-        float mx = -INFINITY;                                                                \
         float psum[2] = {0.f, 0.f};                                                          \
         bf16x8 pnew[4];                                                                      \
         __builtin_amdgcn_sched_barrier(0);                                                   \
@@ -536,8 +550,8 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
             if (i + 4 < NPV) vq[i % 4] = TG_VFRAG(i + 4);                                    \
             _Pragma("unroll") for (int x = i * CPM; x < (i + 1) * CPM; x += 2) {             \
                 const int kk = x / 8, e = x % 8;                                             \
-                TG_MASK_MAX(MASKED, 16 * (kk / 2) + 8 * (kk % 2) + e);                       \
-                TG_MASK_MAX(MASKED, 16 * (kk / 2) + 8 * (kk % 2) + e + 1);                   \
+                TG_MASK(MASKED, 16 * (kk / 2) + 8 * (kk % 2) + e);                           \
+                TG_MASK(MASKED, 16 * (kk / 2) + 8 * (kk % 2) + e + 1);                       \
                 TG_EXP_PAIR(x, 0.f);                                                         \
             }                                                                                \
             __builtin_amdgcn_sched_barrier(0);                                               \
@@ -606,6 +620,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 #undef TG_SOFTMAX_TAIL
 #undef TG_EXP_PAIR
 #undef TG_MASK_MAX
+#undef TG_MASK
 #undef TG_VFRAG
 #undef TG_QK
 #undef TG_KFRAG
