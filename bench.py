@@ -189,7 +189,20 @@ def cpu_baseline(w, gi, ai, s_gpu, kept, cu):
                    f"attention for {hs} of {sh.n_q_heads} query heads on all {len(kept)} kept rows; "
                    "each part scaled to the whole layer"),
         "seconds_scaled": {"gate": t_gate, "select": t_sel, "gather": t_gath, "attention": t_attn},
+        "cpu_model": cpu_model(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def backward_bench(args):
@@ -643,6 +656,17 @@ def main():
     t_bias = timed(lambda: layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"]), 10)
     t_nobias = timed(lambda: tg.tg_gated_attn_prefill(a["q"], a["k"], a["v"], None, None, a["temp"],
                                                      layer.cu_kept, out=nobias_out), 10)
+    # Context: the same kernel on every token of the prompt without pruning
+    # (no bias, temperature 1): what the layer's attention would cost on all N.
+    gfull = torch.Generator(device=dev).manual_seed(args.seed + 7)
+    Tn = w.total_tokens
+    qf = torch.randn(Tn, sh.n_q_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+    kf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+    vf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+    of = torch.empty_like(qf)
+    ones = torch.ones(sh.n_q_heads, device=dev)
+    t_full = timed(lambda: tg.tg_gated_attn_prefill(qf, kf, vf, None, None, ones, layer.cu_seq, out=of), 3)
+    del qf, kf, vf, of
     eb = 2 if bf16 else 4
     kv_row = 2 * sh.n_kv_heads * sh.d_head * eb
     derived = {
@@ -653,6 +677,8 @@ def main():
         "attn_ms_median_nobias": t_nobias[len(t_nobias) // 2],
         "kv_bytes_kept": layer.Kt * kv_row,
         "kv_bytes_full": w.total_tokens * kv_row,
+        "full_prefill_attn_ms_median": t_full[len(t_full) // 2],
+        "attention_saving": t_full[len(t_full) // 2] / t_bias[len(t_bias) // 2],
     }
 
     cold = None
