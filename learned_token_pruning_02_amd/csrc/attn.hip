@@ -578,8 +578,12 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 
     // Tiles strictly before this wave's rows need no mask; the tile holding
     // the wave's first row is the diagonal one; later tiles are skipped by
-    // this wave (the workgroup still stages them).
-    const int jt_diag = qmin / KVT;  // <= nkv - 1
+    // this wave (the workgroup still stages them).  A wave whose rows all lie
+    // past the end of the request (in a request's last tile) takes the last
+    // key tile as its diagonal: its rows are never stored, and it runs the
+    // same nkv + 1 steps (barriers) as the other waves instead of computing
+    // on a key tile that was never staged.
+    const int jt_diag = min(qmin / KVT, nkv - 1);
     // Waves 4-7 share each SIMD with one of waves 0-3, which the hardware
     // favours when both can issue; raising their priority evens out the
     // two waves' step times, so neither idles long at the barrier.

@@ -201,6 +201,9 @@ EIGHT_WAVE = [
     ("dh64_mha", [8192], 16, 16, 64),
     ("dh128_group4", [8192], 16, 4, 128),
     ("dh64_group2_varlen", [3000, 9000, 5000], 16, 8, 64),
+    # Paired workgroups (two query tiles each) whose first tile is the
+    # partial last tile of a request, with waves past the request's end.
+    ("dh128_group2_varlen_partial", [5000, 7000, 3333], 16, 8, 128),
 ]
 
 
