@@ -301,8 +301,12 @@ tg_status tg_gate_backward_plan(tg_dtype dt, int64_t Kt, int32_t d_model, int32_
  * dhidden_kept [Kt][d_model] and dw1 [d_gate][d_model] in dt; db1 (NULL iff
  * b1 is NULL), dw2 [d_gate] and db2 [1] fp32.  All overwritten.
  * ws: tg_gate_backward_plan bytes, caller-owned, 16-byte aligned.
- * The products run on the tg_linear kernels (fp32 accumulation, one rounding
- * of z, dz and the outputs to dt); the column sums are fixed-order reductions.
+ * The products run on the tg_linear kernels with fp32 accumulation.  For
+ * TG_BF16 the two products with few output tiles are split over their
+ * contraction into fp32 partials summed in a fixed order: z (over d_model;
+ * z is not rounded before GELU') and dw1 (over the kept rows); dz and the
+ * outputs are rounded once to dt.  For TG_F32, z, dz and the outputs are
+ * fp32.  The column sums are fixed-order reductions.
  * Supported: TG_BF16 with d_model and d_gate multiples of 64, TG_F32 with
  * multiples of 4.  Kt == 0 is a no-op.  Errors: TG_ERR_BAD_DTYPE,
  * TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE, TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT,
