@@ -41,6 +41,9 @@ def parse():
     p.add_argument("--workload", default="qwen3_1p7b_128k_niah")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-context", action="store_true",
+                   help="skip the context timings (attention without bias, attention on all N "
+                        "tokens), so that a profile holds the hot path's kernels only")
     p.add_argument("--graph", action="store_true",
                    help="report the HIP graph replay time of the step as the value")
     p.add_argument("--detail", default="", help="also write per-kernel detail JSON to this path")
@@ -654,19 +657,22 @@ def main():
 
     nobias_out = torch.empty_like(layer.out)
     t_bias = timed(lambda: layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"]), 10)
-    t_nobias = timed(lambda: tg.tg_gated_attn_prefill(a["q"], a["k"], a["v"], None, None, a["temp"],
-                                                     layer.cu_kept, out=nobias_out), 10)
+    t_nobias = t_bias if args.no_context else timed(
+        lambda: tg.tg_gated_attn_prefill(a["q"], a["k"], a["v"], None, None, a["temp"],
+                                         layer.cu_kept, out=nobias_out), 10)
     # Context: the same kernel on every token of the prompt without pruning
     # (no bias, temperature 1): what the layer's attention would cost on all N.
-    gfull = torch.Generator(device=dev).manual_seed(args.seed + 7)
-    Tn = w.total_tokens
-    qf = torch.randn(Tn, sh.n_q_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
-    kf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
-    vf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
-    of = torch.empty_like(qf)
-    ones = torch.ones(sh.n_q_heads, device=dev)
-    t_full = timed(lambda: tg.tg_gated_attn_prefill(qf, kf, vf, None, None, ones, layer.cu_seq, out=of), 3)
-    del qf, kf, vf, of
+    t_full = [float("nan")]
+    if not args.no_context:
+        gfull = torch.Generator(device=dev).manual_seed(args.seed + 7)
+        Tn = w.total_tokens
+        qf = torch.randn(Tn, sh.n_q_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+        kf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+        vf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+        of = torch.empty_like(qf)
+        ones = torch.ones(sh.n_q_heads, device=dev)
+        t_full = timed(lambda: tg.tg_gated_attn_prefill(qf, kf, vf, None, None, ones, layer.cu_seq, out=of), 3)
+        del qf, kf, vf, of
     eb = 2 if bf16 else 4
     kv_row = 2 * sh.n_kv_heads * sh.d_head * eb
     derived = {
