@@ -3,7 +3,10 @@
 //
 // hidden_kept[r] = hidden[kept[r]] bit for bit; scores_kept[r] = scores[kept[r]].
 // Pure data movement, bound by HBM: each wave copies one row with 16-byte
-// lane accesses, several loads in flight before the matching stores.
+// lane accesses, several loads in flight before the matching stores.  The row
+// index is wave-uniform (the kept id comes through a scalar load) and the
+// row's loads are issued before the score's, so a wave waits for two memory
+// round trips rather than three.
 #include "tg_device.h"
 #include "tg_kernels.h"
 
@@ -21,23 +24,24 @@ __global__ __launch_bounds__(GATHER_THREADS) void gather_rows_kernel(
     float* __restrict__ s_out) {
     const int lane = lane_id();
     const int64_t stride = (int64_t)gridDim.x * ROWS_PER_BLOCK;
-    for (int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + threadIdx.x / WAVE; row < Kt;
-         row += stride) {
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / WAVE);
+    for (int64_t row = (int64_t)blockIdx.x * ROWS_PER_BLOCK + wv; row < Kt; row += stride) {
         const int32_t src = kept[row];
         const bool ok = src >= 0 && (int64_t)src < T;
-        if (s_out != nullptr && lane == 0) s_out[row] = ok ? scores[src] : __builtin_nanf("");
-        if (!ok) continue;
-        const u32x4* s = hidden + (int64_t)src * row_vecs;
-        u32x4* d = out + row * row_vecs;
-        int c = lane;
-        for (; c + (UNROLL - 1) * WAVE < row_vecs; c += UNROLL * WAVE) {
-            u32x4 t[UNROLL];
+        if (ok) {
+            const u32x4* s = hidden + (int64_t)src * row_vecs;
+            u32x4* d = out + row * row_vecs;
+            int c = lane;
+            for (; c + (UNROLL - 1) * WAVE < row_vecs; c += UNROLL * WAVE) {
+                u32x4 t[UNROLL];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) t[u] = s[c + u * WAVE];
+                for (int u = 0; u < UNROLL; ++u) t[u] = s[c + u * WAVE];
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) d[c + u * WAVE] = t[u];
+                for (int u = 0; u < UNROLL; ++u) d[c + u * WAVE] = t[u];
+            }
+            for (; c < row_vecs; c += WAVE) d[c] = s[c];
         }
-        for (; c < row_vecs; c += WAVE) d[c] = s[c];
+        if (s_out != nullptr && lane == 0) s_out[row] = ok ? scores[src] : __builtin_nanf("");
     }
 }
 
