@@ -5,16 +5,20 @@ One step is one gated layer over one batch of synthetic, HBM-resident input:
     -> gather/compact -> causal GQA token-gated attention over the kept rows
 (plus the four QKV/attention/O layers above the gate for the stack workload).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--graph] [--no-context]
     python bench.py --select-sweep      # selector alone, T = 2^20 .. 2^26, K = T/16
+    python bench.py --layer | --backward | --decode   # the other paths, one line each
 
 Prints ONE JSON line: whole-step throughput in tokens of context per second
-(N / step time), the per-kernel split (mean, median, minimum), the roofline of
-the dominant kernel, derived rates (attention-only and kept-token rates, the
-bias overhead against the bias-free build of the same attention kernel, K/V
-bytes kept vs full) and the CPU oracle timed on a bounded sample of the same
-workload.  With --detail, each kernel is also timed cold, right after 512 MiB
-are written to evict the 256 MiB Infinity Cache.
+(N / step time, one launch per kernel; the same step replayed as one HIP graph
+is reported beside it, and is the value with --graph), the per-kernel split
+(mean, median, minimum), the roofline of the dominant kernel, derived rates
+(attention-only and kept-token rates, the bias overhead against the bias-free
+build of the same attention kernel, attention on all N tokens without pruning,
+K/V bytes kept vs full) and the CPU oracle timed on a bounded sample of the
+same workload.  --no-context skips the two context timings (for profiles that
+should hold the hot path only).  With --detail, each kernel is also timed cold,
+right after 512 MiB are written to evict the 256 MiB Infinity Cache.
 """
 from __future__ import annotations
 
