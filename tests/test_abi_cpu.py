@@ -387,3 +387,27 @@ def test_linear_validation():
     assert f(1, A, B, C + 2, 10, 128, 128, 0, None) == 6
     assert f(1, A, B, A + 16, 10, 128, 128, 1, None) == 9
     assert f(1, A, B, C, 0, 128, 128, 0, None) == 0
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library every entry point raises: there is no
+    fallback implementation of any step."""
+    import subprocess
+    import sys
+    code = (
+        "import torch, learned_token_pruning_02_amd as tg\n"
+        "tg._LIB_PATH = '/nonexistent/libtokengate.so'\n"
+        "try:\n"
+        "    tg.lib()\n"
+        "except RuntimeError as e:\n"
+        "    assert 'missing' in str(e)\n"
+        "else:\n"
+        "    raise SystemExit('lib() did not raise')\n"
+        "try:\n"
+        "    tg.tg_gate_score(torch.zeros(4, 64), torch.zeros(64, 64), None, torch.zeros(64), None)\n"
+        "except RuntimeError:\n"
+        "    print('raised')\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and "raised" in r.stdout, (r.returncode, r.stdout, r.stderr)
