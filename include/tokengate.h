@@ -139,9 +139,8 @@ tg_status tg_gate_score(tg_dtype dt, const void *hidden, int64_t T, int32_t d_mo
  *               workspace must not run concurrently.
  * Two implementations give identical results: when every request's document
  * has at most 32768 tokens, one 1024-thread workgroup per request selects in
- * LDS in a single launch (the workspace is then unused); otherwise the
- * document is cut into chunks over many workgroups.  Setting the environment
- * variable TG_SELECT_PATH=multi forces the chunked path (for testing).
+ * a single launch (the workspace is then unused); otherwise the document is
+ * cut into chunks over many workgroups (tg_topk_select_path forces either).
  * Errors: those of tg_plan, TG_ERR_NULL_PTR, TG_ERR_WORKSPACE, TG_ERR_LAUNCH.
  */
 tg_status tg_topk_select(const float *scores, const tg_batch *b, int32_t *kept_idx,
@@ -188,6 +187,18 @@ tg_status tg_plan_prefix(const tg_batch_prefix *b, int32_t *cu_seqlens, int32_t 
 tg_status tg_topk_select_prefix(const float *scores, const tg_batch_prefix *b, int32_t *kept_idx,
                                 int32_t *cu_kept_dev, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/*
+ * tg_topk_select_path -- tg_topk_select_prefix with the implementation chosen
+ * by the caller (for testing that both give the same kept ids; prefix_len may
+ * be NULL, which is tg_topk_select): path 0 chooses as tg_topk_select does,
+ * 1 forces the one-workgroup path (TG_ERR_UNSUPPORTED when a document has
+ * more than 32768 tokens), 2 forces the chunked path.  Any other path is
+ * TG_ERR_BAD_SHAPE.  Other arguments and errors as tg_topk_select_prefix.
+ */
+tg_status tg_topk_select_path(const float *scores, const tg_batch_prefix *b, int32_t *kept_idx,
+                              int32_t *cu_kept_dev, void *ws, size_t ws_bytes, int path,
+                              hipStream_t stream);
 
 /*
  * tg_gather_compact -- compaction (spke.com page, third bullet: layers above L
@@ -446,10 +457,24 @@ tg_status tg_silu_mul(tg_dtype dt, const void *gu, int64_t M, int32_t F, void *o
  *     y[M][N] = y[M][N] + x[M][K] . w[N][K]^T  (accumulate != 0; residual add)
  * fp32 accumulation, one rounding to dt at the store.
  * Supported: TG_BF16 with N % 64 == 0 and K % 64 == 0; TG_F32 any N, K with
- * K % 4 == 0.  M == 0 is a no-op.
+ * K % 4 == 0.  M == 0 is a no-op.  The bf16 output tile (128x128, 256x128 or
+ * 256x256 rows x columns per workgroup) is the largest that still gives every
+ * compute unit work.  Errors: TG_ERR_BAD_DTYPE, TG_ERR_BAD_SHAPE,
+ * TG_ERR_NULL_PTR, TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT, TG_ERR_ALIAS,
+ * TG_ERR_LAUNCH.
  */
 tg_status tg_linear(tg_dtype dt, const void *x, const void *w, void *y, int64_t M,
                     int32_t N, int32_t K, int accumulate, hipStream_t stream);
+
+/*
+ * tg_linear_tile -- tg_linear with the bf16 output tile chosen by the caller
+ * (for testing every tile on the same shapes): tile 0 chooses as tg_linear
+ * does, 1 forces 128x128, 2 forces 256x128, 3 forces 256x256; any other tile
+ * is TG_ERR_BAD_SHAPE.  The fp32 path ignores it.  Other arguments and errors
+ * as tg_linear.
+ */
+tg_status tg_linear_tile(tg_dtype dt, const void *x, const void *w, void *y, int64_t M,
+                         int32_t N, int32_t K, int accumulate, int tile, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -113,6 +113,8 @@ def lib() -> ctypes.CDLL:
     L.tg_gate_score.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp, vp, vp, i32, vp, vp]
     L.tg_topk_select.restype = ctypes.c_int
     L.tg_topk_select.argtypes = [vp, ctypes.POINTER(_Batch), vp, vp, vp, sz, vp]
+    L.tg_topk_select_path.restype = ctypes.c_int
+    L.tg_topk_select_path.argtypes = [vp, ctypes.POINTER(_BatchPrefix), vp, vp, vp, sz, ctypes.c_int, vp]
     L.tg_plan_prefix.restype = ctypes.c_int
     L.tg_plan_prefix.argtypes = [ctypes.POINTER(_BatchPrefix), p_i32, p_i32, ctypes.POINTER(sz)]
     L.tg_topk_select_prefix.restype = ctypes.c_int
@@ -148,6 +150,8 @@ def lib() -> ctypes.CDLL:
     L.tg_silu_mul.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp]
     L.tg_linear.restype = ctypes.c_int
     L.tg_linear.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
+    L.tg_linear_tile.restype = ctypes.c_int
+    L.tg_linear_tile.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp]
     _lib = L
     return L
 
@@ -192,6 +196,31 @@ def _dev(t, name: str, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, name: str, shape) -> None:
+    """Raise ValueError unless tensor t (skipped when None) has exactly `shape`.
+
+    The C ABI receives bare pointers and sizes, so a tensor smaller than the
+    sizes passed with it would be read or written out of bounds on the GPU;
+    every wrapper checks its tensors here before any pointer is taken."""
+    if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+
+
+def _numel(t, name: str, n: int) -> None:
+    """Raise ValueError unless tensor t (skipped when None) has n elements."""
+    if t is not None and t.numel() != int(n):
+        raise ValueError(f"{name} must have {int(n)} elements, got {t.numel()}")
+
+
+def _ndim(t, name: str, nd: int) -> None:
+    if t.dim() != nd:
+        raise ValueError(f"{name} must be {nd}-D, got shape {tuple(t.shape)}")
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _i32_array(vals: Sequence[int]):
     arr = (ctypes.c_int32 * max(1, len(vals)))(*[int(v) for v in vals])
     return arr
@@ -230,8 +259,15 @@ def tg_plan(seq_len: Sequence[int], q_len: Sequence[int], budget: Sequence[int],
 def tg_gate_score(hidden, w1, b1, w2, b2, scores=None, stream=None):
     """scores[T] (fp32) = w2 . GELU(W1 x_t + b1) + b2 for every row x_t of hidden."""
     torch = _torch()
+    _ndim(hidden, "hidden", 2)
+    _ndim(w1, "w1", 2)
     T, d = hidden.shape
     dg = w1.shape[0]
+    _shape(w1, "w1", (dg, d))
+    _numel(b1, "b1", dg)
+    _numel(w2, "w2", dg)
+    _numel(b2, "b2", 1)
+    _numel(scores, "scores", T)
     dt = _dt(hidden)
     if scores is None:
         scores = torch.empty(T, dtype=torch.float32, device=hidden.device)
@@ -243,25 +279,40 @@ def tg_gate_score(hidden, w1, b1, w2, b2, scores=None, stream=None):
 
 
 def tg_topk_select(scores, seq_len: Sequence[int], q_len: Sequence[int], budget: Sequence[int],
-                   kept_idx=None, cu_kept_dev=None, workspace=None, stream=None, prefix_len=None):
+                   kept_idx=None, cu_kept_dev=None, workspace=None, stream=None, prefix_len=None,
+                   path: int = 0):
     """Kept global token ids (int32, ascending per request) and the host cu_kept list.
     With prefix_len, each request also keeps that many leading template tokens
     and selects from the span between them and the question
     (tg_topk_select_prefix).  Random-K selection is this call on random keys
-    drawn by the caller in place of the scores."""
+    drawn by the caller in place of the scores.  path (testing only): 1
+    forces the one-workgroup implementation, 2 the chunked one
+    (tg_topk_select_path); 0 lets the library choose."""
     torch = _torch()
     cu_s, cu_k, ws_bytes = tg_plan(seq_len, q_len, budget, prefix_len)
+    _numel(scores, "scores", cu_s[-1])
+    _numel(kept_idx, "kept_idx", cu_k[-1])
+    _numel(cu_kept_dev, "cu_kept_dev", len(cu_k))
+    if workspace is not None and _nbytes(workspace) < ws_bytes:
+        raise ValueError(f"workspace must hold {ws_bytes} bytes, got {_nbytes(workspace)}")
     if kept_idx is None:
         kept_idx = torch.empty(cu_k[-1], dtype=torch.int32, device=scores.device)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=scores.device)
-    bt, keep = _batch(seq_len, q_len, budget, prefix_len)
-    fn = lib().tg_topk_select if prefix_len is None else lib().tg_topk_select_prefix
-    _check("tg_topk_select" if prefix_len is None else "tg_topk_select_prefix", fn(
-        _dev(scores, "scores", torch.float32), ctypes.byref(bt),
-        _dev(kept_idx, "kept_idx", torch.int32), _dev(cu_kept_dev, "cu_kept_dev", torch.int32),
-        _dev(workspace, "workspace"), ws_bytes if workspace is None else workspace.numel(),
-        _stream(stream)))
+    if path:
+        # tg_topk_select_path takes a tg_batch_prefix (prefix_len NULL: none).
+        bt, keep = _batch(seq_len, q_len, budget, prefix_len if prefix_len is not None else [0] * len(seq_len))
+    else:
+        bt, keep = _batch(seq_len, q_len, budget, prefix_len)
+    args = (_dev(scores, "scores", torch.float32), ctypes.byref(bt),
+            _dev(kept_idx, "kept_idx", torch.int32), _dev(cu_kept_dev, "cu_kept_dev", torch.int32),
+            _dev(workspace, "workspace"), ws_bytes if workspace is None else _nbytes(workspace))
+    if path:
+        _check("tg_topk_select_path", lib().tg_topk_select_path(*args, int(path), _stream(stream)))
+    elif prefix_len is not None:
+        _check("tg_topk_select_prefix", lib().tg_topk_select_prefix(*args, _stream(stream)))
+    else:
+        _check("tg_topk_select", lib().tg_topk_select(*args, _stream(stream)))
     return kept_idx, cu_k
 
 
@@ -269,8 +320,12 @@ def tg_gather_compact(hidden, kept_idx, scores=None, hidden_kept=None, scores_ke
                       stream=None):
     """hidden_kept[r] = hidden[kept_idx[r]]; scores_kept[r] = scores[kept_idx[r]]."""
     torch = _torch()
+    _ndim(hidden, "hidden", 2)
     T, d = hidden.shape
     Kt = kept_idx.numel()
+    _numel(scores, "scores", T)
+    _shape(hidden_kept, "hidden_kept", (Kt, d))
+    _numel(scores_kept, "scores_kept", Kt)
     if hidden_kept is None:
         hidden_kept = torch.empty(Kt, d, dtype=hidden.dtype, device=hidden.device)
     if scores is not None and scores_kept is None:
@@ -282,6 +337,21 @@ def tg_gather_compact(hidden, kept_idx, scores=None, hidden_kept=None, scores_ke
     return hidden_kept, scores_kept
 
 
+def _attn_shapes(q, k, v, s_kept, gain, temp, cu_kept) -> None:
+    """Shape checks shared by the attention forward and backward wrappers."""
+    Kt, Hq, dh = q.shape
+    Hkv = k.shape[1]
+    if len(cu_kept) < 2 or int(cu_kept[-1]) != Kt:
+        raise ValueError(f"cu_kept[-1] must equal the {Kt} rows of q, got {list(cu_kept)[-1:]}")
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"query heads ({Hq}) must be a multiple of KV heads ({Hkv})")
+    _shape(k, "k", (Kt, Hkv, dh))
+    _shape(v, "v", (Kt, Hkv, dh))
+    _numel(s_kept, "s_kept", Kt)
+    _numel(gain, "gain", Hq)
+    _numel(temp, "temp", Hq)
+
+
 def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], out=None,
                           lse=None, want_lse: bool = False, stream=None):
     """Causal GQA token-gated attention over packed kept rows; returns (out, lse or None).
@@ -289,8 +359,13 @@ def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], o
     s_kept=None and gain=None drop the bias term (plain causal attention with
     the per-head temperature)."""
     torch = _torch()
+    _ndim(q, "q", 3)
+    _ndim(k, "k", 3)
     Kt, Hq, dh = q.shape
     Hkv = k.shape[1]
+    _attn_shapes(q, k, v, s_kept, gain, temp, cu_kept)
+    _shape(out, "out", q.shape)
+    _shape(lse, "lse", (Hq, Kt))
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
@@ -319,8 +394,23 @@ def tg_gated_attn_backward(q, k, v, s_kept, gain, temp, out, lse, dout, cu_kept:
     """Gradients of the token-gated attention; returns a dict with dq, dk, dv
     (bf16) and ds, dgain (fp32; None without the bias) and dtemp (fp32)."""
     torch = _torch()
+    _ndim(q, "q", 3)
+    _ndim(k, "k", 3)
     Kt, Hq, dh = q.shape
     Hkv = k.shape[1]
+    _attn_shapes(q, k, v, s_kept, gain, temp, cu_kept)
+    _shape(out, "out", q.shape)
+    _shape(dout, "dout", q.shape)
+    _shape(lse, "lse", (Hq, Kt))
+    if grads is not None:
+        _shape(grads["dq"], "dq", q.shape)
+        _shape(grads["dk"], "dk", k.shape)
+        _shape(grads["dv"], "dv", k.shape)
+        _numel(grads.get("ds"), "ds", Kt)
+        _numel(grads.get("dgain"), "dgain", Hq)
+        _numel(grads["dtemp"], "dtemp", Hq)
+    if workspace is not None and _nbytes(workspace) < tg_attn_backward_plan(cu_kept, Hq, Hkv):
+        raise ValueError("workspace is smaller than tg_attn_backward_plan reports")
     if grads is None:
         f32 = dict(dtype=torch.float32, device=q.device)
         grads = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
@@ -356,8 +446,24 @@ def tg_gate_backward(hidden_kept, w1, b1, w2, ds_kept, grads=None, workspace=Non
     """Gradients of the gate MLP over the kept rows; returns a dict with
     dhidden, dw1 (in the input dtype) and db1 (None without b1), dw2, db2 (fp32)."""
     torch = _torch()
+    _ndim(hidden_kept, "hidden_kept", 2)
+    _ndim(w1, "w1", 2)
     Kt, d = hidden_kept.shape
     dg = w1.shape[0]
+    _shape(w1, "w1", (dg, d))
+    _numel(b1, "b1", dg)
+    _numel(w2, "w2", dg)
+    _numel(ds_kept, "ds_kept", Kt)
+    if grads is not None:
+        _shape(grads["dhidden"], "dhidden", (Kt, d))
+        _shape(grads["dw1"], "dw1", (dg, d))
+        _numel(grads.get("db1"), "db1", dg)
+        _numel(grads["dw2"], "dw2", dg)
+        _numel(grads["db2"], "db2", 1)
+        if (grads.get("db1") is None) != (b1 is None):
+            raise ValueError("db1 must be given exactly when b1 is")
+    if workspace is not None and _nbytes(workspace) < tg_gate_backward_plan(hidden_kept.dtype, Kt, d, dg):
+        raise ValueError("workspace is smaller than tg_gate_backward_plan reports")
     f32 = dict(dtype=torch.float32, device=hidden_kept.device)
     if grads is None:
         grads = {"dhidden": torch.empty_like(hidden_kept), "dw1": torch.empty_like(w1),
@@ -392,13 +498,28 @@ def tg_gated_attn_decode(q, k, v, s, row_off, cache_len, gain, temp, max_len: in
     and cache_len (int32) are device tensors of length B.  s=None and
     gain=None drop the bias term."""
     torch = _torch()
+    _ndim(q, "q", 3)
+    _ndim(k, "k", 3)
     B, Hq, dh = q.shape
     R, Hkv = k.shape[0], k.shape[1]
+    if Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"query heads ({Hq}) must be a multiple of KV heads ({Hkv})")
+    _shape(k, "k", (R, Hkv, dh))
+    _shape(v, "v", (R, Hkv, dh))
+    _numel(s, "s", R)
+    _numel(row_off, "row_off", B)
+    _numel(cache_len, "cache_len", B)
+    _numel(gain, "gain", Hq)
+    _numel(temp, "temp", Hq)
+    _shape(out, "out", q.shape)
+    _shape(lse, "lse", (B, Hq))
+    need = tg_decode_plan(B, Hq, dh, max_len)
+    if workspace is not None and _nbytes(workspace) < need:
+        raise ValueError(f"workspace must hold {need} bytes, got {_nbytes(workspace)}")
     if out is None:
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
-    need = tg_decode_plan(B, Hq, dh, max_len)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check("tg_gated_attn_decode", lib().tg_gated_attn_decode(
@@ -417,6 +538,8 @@ def tg_rmsnorm(x, w, eps: float, y=None, stream=None):
     torch = _torch()
     d = x.shape[-1]
     M = x.numel() // d if d else 0
+    _numel(w, "w", d)
+    _shape(y, "y", x.shape)
     if y is None:
         y = torch.empty_like(x)
     _check("tg_rmsnorm", lib().tg_rmsnorm(_dt(x), _dev(x, "x"), _dev(w, "w", x.dtype), eps, M, d,
@@ -428,6 +551,10 @@ def tg_kept_positions(kept_idx, cu_seqlens: Sequence[int], cu_kept: Sequence[int
                       stream=None):
     """Original in-request position of every kept row (int32 device tensor)."""
     torch = _torch()
+    if len(cu_seqlens) != len(cu_kept):
+        raise ValueError("cu_seqlens and cu_kept must have the same length")
+    _numel(kept_idx, "kept_idx", int(cu_kept[-1]))
+    _numel(pos, "pos", int(cu_kept[-1]))
     if pos is None:
         pos = torch.empty(int(cu_kept[-1]), dtype=torch.int32, device=kept_idx.device)
     cs, ck = _i32_array(cu_seqlens), _i32_array(cu_kept)
@@ -442,7 +569,13 @@ def tg_qk_norm_rope(q, k, q_norm_w, k_norm_w, pos, theta: float, eps: float, str
     """In place: per-head RMSNorm of q[M][Hq][dh] and k[M][Hkv][dh] (weights may
     be None), then the rotary embedding at positions pos[M]."""
     torch = _torch()
+    _ndim(q, "q", 3)
+    _ndim(k, "k", 3)
     M, Hq, dh = q.shape
+    _shape(k, "k", (M, k.shape[1], dh))
+    _numel(q_norm_w, "q_norm_w", dh)
+    _numel(k_norm_w, "k_norm_w", dh)
+    _numel(pos, "pos", M)
     _check("tg_qk_norm_rope", lib().tg_qk_norm_rope(
         _dt(q), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(q_norm_w, "q_norm_w", q.dtype),
         _dev(k_norm_w, "k_norm_w", q.dtype), _dev(pos, "pos", torch.int32), M, Hq, k.shape[1], dh,
@@ -453,7 +586,11 @@ def tg_qk_norm_rope(q, k, q_norm_w, k_norm_w, pos, theta: float, eps: float, str
 def tg_silu_mul(gu, out=None, stream=None):
     """out[M][F] = silu(gu[:, :F]) * gu[:, F:] for gu[M][2F]."""
     torch = _torch()
+    _ndim(gu, "gu", 2)
     M, F2 = gu.shape
+    if F2 % 2 != 0:
+        raise ValueError(f"gu must have an even number of columns, got {F2}")
+    _shape(out, "out", (M, F2 // 2))
     if out is None:
         out = torch.empty(M, F2 // 2, dtype=gu.dtype, device=gu.device)
     _check("tg_silu_mul", lib().tg_silu_mul(_dt(gu), _dev(gu, "gu"), M, F2 // 2,
@@ -461,16 +598,25 @@ def tg_silu_mul(gu, out=None, stream=None):
     return out
 
 
-def tg_linear(x, w, y=None, accumulate: bool = False, stream=None):
-    """y = x w^T, or y += x w^T with accumulate=True (w in Linear layout [N][K])."""
+def tg_linear(x, w, y=None, accumulate: bool = False, stream=None, tile: int = 0):
+    """y = x w^T, or y += x w^T with accumulate=True (w in Linear layout [N][K]).
+    tile (testing only): 1, 2, 3 force the 128x128, 256x128, 256x256 bf16
+    output tile (tg_linear_tile); 0 lets the library choose."""
     torch = _torch()
+    _ndim(x, "x", 2)
+    _ndim(w, "w", 2)
     M, K = x.shape
     N = w.shape[0]
+    _shape(w, "w", (N, K))
+    _shape(y, "y", (M, N))
     if y is None:
         if accumulate:
             raise ValueError("accumulate=True needs y")
         y = torch.empty(M, N, dtype=x.dtype, device=x.device)
-    _check("tg_linear", lib().tg_linear(
-        _dt(x), _dev(x, "x"), _dev(w, "w", x.dtype), _dev(y, "y", x.dtype), M, N, K,
-        1 if accumulate else 0, _stream(stream)))
+    args = (_dt(x), _dev(x, "x"), _dev(w, "w", x.dtype), _dev(y, "y", x.dtype), M, N, K,
+            1 if accumulate else 0)
+    if tile:
+        _check("tg_linear_tile", lib().tg_linear_tile(*args, int(tile), _stream(stream)))
+    else:
+        _check("tg_linear", lib().tg_linear(*args, _stream(stream)))
     return y

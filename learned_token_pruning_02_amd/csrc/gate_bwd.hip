@@ -190,7 +190,7 @@ hipError_t run(tg_dtype dt, const T* x, int64_t Kt, int d, const T* w1, const T*
     T* w1T = (T*)(ws + L.w1T);
     float* part = (float*)(ws + L.part);
     const auto lin = [&](const T* a, const T* b, T* y, int64_t M, int N, int K) {
-        return dt == TG_BF16 ? launch_linear_bf16(a, b, y, M, N, K, 0, st)
+        return dt == TG_BF16 ? launch_linear_bf16(a, b, y, M, N, K, 0, 0, st)
                              : launch_linear_f32((const float*)a, (const float*)b, (float*)y, M, N,
                                                  K, 0, st);
     };

@@ -8,7 +8,6 @@
 // consecutive columns n per accumulator group: stores are 8-byte runs.
 // x and w k-chunks of 64 are double buffered in LDS; within a chunk lane half
 // h covers k in [32h, 32h+32) for both operands.
-#include <cstdlib>
 
 #include "tg_device.h"
 #include "tg_kernels.h"
@@ -201,15 +200,13 @@ hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M
 }
 
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
-                              int accumulate, hipStream_t st) {
-    // The largest tile that still gives every CU at least one workgroup
-    // (two for the 256x128 tile, which runs two per CU).
-    // TG_LINEAR_TILE=small|mid|large forces one (for testing).
+                              int accumulate, int tile, hipStream_t st) {
+    // tile 0: the largest tile that still gives every CU at least one
+    // workgroup (two for the 256x128 tile, which runs two per CU);
+    // 1, 2, 3 force the 128x128, 256x128 or 256x256 tile.
     const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
     const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
-    const char* force = std::getenv("TG_LINEAR_TILE");
-    const char f = force != nullptr ? force[0] : 0;
-    const int choice = f == 's' ? 0 : f == 'm' ? 1 : f == 'l' ? 2 : (t256 >= 256 ? 2 : t128 >= 512 ? 1 : 0);
+    const int choice = tile > 0 ? tile - 1 : (t256 >= 256 ? 2 : t128 >= 512 ? 1 : 0);
     if (choice == 2) {
         const dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 255) / 256));
         hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 4>), grid, dim3(512), 0, st,

@@ -1,6 +1,7 @@
 // Top-K selection with the question tail always kept (spke.com page,
-// three-phase list, second bullet; "Seule la partie document ..." for the
-// question; "Comment déployer TokenGate ?" for the max_kept_prefill_tokens
+// "Comment TokenGate a-t-il appris ...": the second bullet of the three-phase
+// list for the top-K, the sentence after the list for the question, which is
+// never pruned; "Comment déployer TokenGate ?" for the max_kept_prefill_tokens
 // budget).
 //
 // Per request b:
@@ -30,7 +31,6 @@
 //      table per workgroup), and the question tail after them.
 // Results do not depend on which workgroup finishes last.
 #include <algorithm>
-#include <cstdlib>
 
 #include "tg_device.h"
 #include "tg_kernels.h"
@@ -638,6 +638,7 @@ constexpr int SM_THREADS = 1024;
 constexpr int SM_WAVES = SM_THREADS / WAVE;
 constexpr int SM_IT = 32;                       // keys per thread at most
 constexpr int SM_MAX = SM_THREADS * SM_IT;      // 32768 document tokens per request
+static_assert(SM_MAX == SELECT_ONE_WG_MAX, "one-workgroup capacity");
 
 // Exclusive block scan over 1024 threads; *total gets the sum.
 __device__ __forceinline__ uint32_t scan1024_excl(uint32_t v, uint32_t* wtot, uint32_t* total) {
@@ -759,15 +760,11 @@ __global__ __launch_bounds__(SM_THREADS) void sel_small_kernel(SelArgs a) {
 
 }  // namespace
 
-namespace {
-bool small_batch(const BatchArgs& a) {
-    const char* path = std::getenv("TG_SELECT_PATH");  // "multi": always the chunked path
-    if (path != nullptr && path[0] == 'm') return false;
+bool select_one_wg_fits(const BatchArgs& a) {
     for (int b = 0; b < a.batch; ++b)
         if (a.cu_seq[b + 1] - a.cu_seq[b] - a.q_len[b] - a.p_len[b] > SM_MAX) return false;
     return true;
 }
-}  // namespace
 
 size_t select_workspace_bytes(const BatchArgs& a) {
     int dc, ac;
@@ -776,7 +773,7 @@ size_t select_workspace_bytes(const BatchArgs& a) {
 }
 
 hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept, int32_t* cu_dev,
-                         void* ws, hipStream_t st) {
+                         void* ws, int path, hipStream_t st) {
     SelArgs s;
     s.batch = a.batch;
     for (int b = 0; b <= a.batch; ++b) {
@@ -790,7 +787,8 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
     s.scores = scores;
     s.kept = kept;
     s.cu_dev = cu_dev;
-    if (small_batch(a)) {  // every document fits in one workgroup's LDS
+    const bool one_wg = path == SELECT_ONE_WG || (path == SELECT_AUTO && select_one_wg_fits(a));
+    if (one_wg) {  // every document fits in one workgroup's registers
         hipLaunchKernelGGL(sel_small_kernel, dim3(a.batch), dim3(SM_THREADS), 0, st, s);
         return hipGetLastError();
     }

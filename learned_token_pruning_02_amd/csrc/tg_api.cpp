@@ -75,8 +75,11 @@ tg_status plan_out(const tg::BatchArgs& a, int32_t* cu_seqlens, int32_t* cu_kept
 }
 
 tg_status select_checked(const float* scores, const tg::BatchArgs& a, int32_t* kept_idx,
-                         int32_t* cu_kept_dev, void* ws, size_t ws_bytes, hipStream_t stream) {
+                         int32_t* cu_kept_dev, void* ws, size_t ws_bytes, int path,
+                         hipStream_t stream) {
     if (scores == nullptr || kept_idx == nullptr) return TG_ERR_NULL_PTR;
+    if (path < tg::SELECT_AUTO || path > tg::SELECT_CHUNKED) return TG_ERR_BAD_SHAPE;
+    if (path == tg::SELECT_ONE_WG && !tg::select_one_wg_fits(a)) return TG_ERR_UNSUPPORTED;
     const size_t need = tg::select_workspace_bytes(a);
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return TG_ERR_WORKSPACE;
     if (!aligned4(scores) || !aligned4(kept_idx) || !aligned16(ws)) return TG_ERR_ALIGNMENT;
@@ -88,7 +91,7 @@ tg_status select_checked(const float* scores, const tg::BatchArgs& a, int32_t* k
         overlap(ws, wb, scores, T * 4) || overlap(ws, wb, kept_idx, Kt * 4) ||
         overlap(ws, wb, cu_kept_dev, (a.batch + 1) * 4))
         return TG_ERR_ALIAS;
-    return launched(tg::launch_select(scores, a, kept_idx, cu_kept_dev, ws, stream));
+    return launched(tg::launch_select(scores, a, kept_idx, cu_kept_dev, ws, path, stream));
 }
 
 }  // namespace
@@ -161,7 +164,16 @@ tg_status tg_topk_select(const float* scores, const tg_batch* b, int32_t* kept_i
     tg::BatchArgs a;
     const tg_status st = plan_batch(b, &a);
     if (st != TG_OK) return st;
-    return select_checked(scores, a, kept_idx, cu_kept_dev, ws, ws_bytes, stream);
+    return select_checked(scores, a, kept_idx, cu_kept_dev, ws, ws_bytes, tg::SELECT_AUTO, stream);
+}
+
+tg_status tg_topk_select_path(const float* scores, const tg_batch_prefix* b, int32_t* kept_idx,
+                              int32_t* cu_kept_dev, void* ws, size_t ws_bytes, int path,
+                              hipStream_t stream) {
+    tg::BatchArgs a;
+    const tg_status st = plan_batch(b, &a);
+    if (st != TG_OK) return st;
+    return select_checked(scores, a, kept_idx, cu_kept_dev, ws, ws_bytes, path, stream);
 }
 
 tg_status tg_topk_select_prefix(const float* scores, const tg_batch_prefix* b, int32_t* kept_idx,
@@ -170,7 +182,7 @@ tg_status tg_topk_select_prefix(const float* scores, const tg_batch_prefix* b, i
     tg::BatchArgs a;
     const tg_status st = plan_batch(b, &a);
     if (st != TG_OK) return st;
-    return select_checked(scores, a, kept_idx, cu_kept_dev, ws, ws_bytes, stream);
+    return select_checked(scores, a, kept_idx, cu_kept_dev, ws, ws_bytes, tg::SELECT_AUTO, stream);
 }
 
 tg_status tg_gather_compact(tg_dtype dt, const void* hidden, int64_t T, int32_t d_model,
@@ -502,10 +514,11 @@ tg_status tg_silu_mul(tg_dtype dt, const void* gu, int64_t M, int32_t F, void* o
     return launched(tg::launch_silu_mul(dt, gu, M, F, out, stream));
 }
 
-tg_status tg_linear(tg_dtype dt, const void* x, const void* w, void* y, int64_t M, int32_t N,
-                    int32_t K, int accumulate, hipStream_t stream) {
+namespace {
+tg_status linear_checked(tg_dtype dt, const void* x, const void* w, void* y, int64_t M, int32_t N,
+                         int32_t K, int accumulate, int tile, hipStream_t stream) {
     if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
-    if (M < 0 || N < 1 || K < 1 || M >= I32_LIMIT) return TG_ERR_BAD_SHAPE;
+    if (M < 0 || N < 1 || K < 1 || M >= I32_LIMIT || tile < 0 || tile > 3) return TG_ERR_BAD_SHAPE;
     if (x == nullptr || w == nullptr || y == nullptr) return TG_ERR_NULL_PTR;
     if (dt == TG_BF16 && (N % 64 != 0 || K % 64 != 0)) return TG_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return TG_ERR_ALIGNMENT;
@@ -516,7 +529,18 @@ tg_status tg_linear(tg_dtype dt, const void* x, const void* w, void* y, int64_t 
     if (dt == TG_F32)
         return launched(tg::launch_linear_f32((const float*)x, (const float*)w, (float*)y, M, N, K,
                                               accumulate, stream));
-    return launched(tg::launch_linear_bf16(x, w, y, M, N, K, accumulate, stream));
+    return launched(tg::launch_linear_bf16(x, w, y, M, N, K, accumulate, tile, stream));
+}
+}  // namespace
+
+tg_status tg_linear(tg_dtype dt, const void* x, const void* w, void* y, int64_t M, int32_t N,
+                    int32_t K, int accumulate, hipStream_t stream) {
+    return linear_checked(dt, x, w, y, M, N, K, accumulate, 0, stream);
+}
+
+tg_status tg_linear_tile(tg_dtype dt, const void* x, const void* w, void* y, int64_t M, int32_t N,
+                         int32_t K, int accumulate, int tile, hipStream_t stream) {
+    return linear_checked(dt, x, w, y, M, N, K, accumulate, tile, stream);
 }
 
 }  // extern "C"

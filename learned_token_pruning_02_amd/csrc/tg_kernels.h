@@ -23,9 +23,14 @@ hipError_t launch_gate_f32(const float* hidden, int64_t T, int d, const float* w
 hipError_t launch_gate_bf16(const void* hidden, int64_t T, int d, const void* w1, const void* b1,
                             const void* w2, const void* b2, int dg, float* scores, hipStream_t st);
 
+// Selector implementation: SELECT_AUTO picks the one-workgroup path when
+// every document has at most SELECT_ONE_WG_MAX tokens, else the chunked path.
+enum SelectPath { SELECT_AUTO = 0, SELECT_ONE_WG = 1, SELECT_CHUNKED = 2 };
+constexpr int SELECT_ONE_WG_MAX = 32768;
+bool select_one_wg_fits(const BatchArgs& a);
 size_t select_workspace_bytes(const BatchArgs& a);
 hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept, int32_t* cu_dev,
-                         void* ws, hipStream_t st);
+                         void* ws, int path, hipStream_t st);
 
 hipError_t launch_gather(const void* hidden, int64_t T, int row_bytes, const float* scores,
                          const int32_t* kept, int64_t Kt, void* hidden_kept, float* scores_kept,
@@ -82,8 +87,9 @@ hipError_t launch_kept_positions(const int32_t* kept, int64_t Kt, const BatchArg
 
 hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M, int N, int K,
                              int accumulate, hipStream_t st);
+// tile: 0 chooses by output size; 1, 2, 3 force the 128x128, 256x128, 256x256 tile.
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
-                              int accumulate, hipStream_t st);
+                              int accumulate, int tile, hipStream_t st);
 // part[z][M][N] = x[:, zK/S : (z+1)K/S] . w[:, same]^T in fp32, z < S (K/S a multiple of 64).
 hipError_t launch_linear_bf16_splitk(const void* x, const void* w, float* part, int64_t M, int N,
                                      int K, int slices, hipStream_t st);

@@ -411,3 +411,141 @@ def test_missing_library_fails_loudly():
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240)
     assert r.returncode == 0 and "raised" in r.stdout, (r.returncode, r.stdout, r.stderr)
+
+
+def test_select_path_validation():
+    """tg_topk_select_path: an unknown path is rejected, and the one-workgroup
+    path refuses a document longer than it can hold."""
+    L = tg.lib()
+    ws = tg.tg_plan([100], [10], [20])[2]
+    bt, keep = _batch([100], [10], [20], [0])
+    f = L.tg_topk_select_path
+    assert f(A, ctypes.byref(bt), B, None, C, ws, 3, None) == 2
+    assert f(A, ctypes.byref(bt), B, None, C, ws, -1, None) == 2
+    assert f(None, ctypes.byref(bt), B, None, C, ws, 2, None) == 1
+    n = 32768 + 11
+    ws2 = tg.tg_plan([n], [10], [20])[2]
+    bt2, keep2 = _batch([n], [10], [20], [0])
+    assert f(A, ctypes.byref(bt2), B, None, C, ws2, 1, None) == 5
+    # a tg_batch_prefix whose prefix_len is NULL is a plain batch
+    bt3 = tg._BatchPrefix(1, keep2[0], keep2[1], keep2[2], None)
+    assert f(None, ctypes.byref(bt3), B, None, C, ws2, 2, None) == 1
+    assert f(A, ctypes.byref(bt3), B, None, C, ws2, 1, None) == 5
+
+
+def test_linear_tile_validation():
+    L = tg.lib()
+    f = L.tg_linear_tile
+    assert f(1, A, B, C, 10, 128, 128, 0, 4, None) == 2
+    assert f(1, A, B, C, 10, 128, 128, 0, -1, None) == 2
+    assert f(1, A, B, C, 10, 96, 128, 0, 1, None) == 5
+    assert f(1, A, B, C, 0, 128, 128, 0, 3, None) == 0
+
+
+# ------------------------------------------- binding size checks (no GPU) ----
+def _meta(*shape, dtype=None):
+    import torch
+    return torch.empty(*shape, dtype=dtype or torch.bfloat16, device="meta")
+
+
+def _raises_size(fn, *args, match=None, **kw):
+    """The wrapper must reject the sizes itself (ValueError naming the size
+    problem), before it looks at where the tensors live."""
+    with pytest.raises(ValueError) as e:
+        fn(*args, **kw)
+    msg = str(e.value)
+    assert "GPU tensor" not in msg, msg
+    if match is not None:
+        assert match in msg, msg
+
+
+def test_binding_checks_gate_sizes():
+    import torch
+    h, w1, w2 = _meta(100, 256), _meta(64, 256), _meta(64)
+    _raises_size(tg.tg_gate_score, h, _meta(64, 128), None, w2, None, match="w1")
+    _raises_size(tg.tg_gate_score, h, w1, _meta(32), w2, None, match="b1")
+    _raises_size(tg.tg_gate_score, h, w1, None, _meta(63), None, match="w2")
+    _raises_size(tg.tg_gate_score, h, w1, None, w2, _meta(2), match="b2")
+    _raises_size(tg.tg_gate_score, h, w1, None, w2, None, scores=_meta(99, dtype=torch.float32),
+                 match="scores")
+    _raises_size(tg.tg_gate_score, _meta(100, 256, 1), w1, None, w2, None, match="hidden")
+
+
+def test_binding_checks_select_sizes():
+    import torch
+    f32, i32 = torch.float32, torch.int32
+    seq, q, bud = [300, 200], [10, 20], [50, 60]
+    s = _meta(500, dtype=f32)
+    _raises_size(tg.tg_topk_select, _meta(499, dtype=f32), seq, q, bud, match="scores")
+    _raises_size(tg.tg_topk_select, s, seq, q, bud, kept_idx=_meta(109, dtype=i32), match="kept_idx")
+    _raises_size(tg.tg_topk_select, s, seq, q, bud, cu_kept_dev=_meta(2, dtype=i32), match="cu_kept_dev")
+    ws = tg.tg_plan(seq, q, bud)[2]
+    # the workspace is counted in bytes whatever its element type
+    _raises_size(tg.tg_topk_select, s, seq, q, bud, workspace=_meta(ws // 4 - 1, dtype=i32),
+                 match="workspace")
+
+
+def test_binding_checks_gather_sizes():
+    import torch
+    h, kept = _meta(100, 64), _meta(20, dtype=torch.int32)
+    _raises_size(tg.tg_gather_compact, h, kept, scores=_meta(99, dtype=torch.float32), match="scores")
+    _raises_size(tg.tg_gather_compact, h, kept, hidden_kept=_meta(21, 64), match="hidden_kept")
+    _raises_size(tg.tg_gather_compact, h, kept, scores=_meta(100, dtype=torch.float32),
+                 scores_kept=_meta(19, dtype=torch.float32), match="scores_kept")
+
+
+def test_binding_checks_attention_sizes():
+    import torch
+    f32 = torch.float32
+    Kt, Hq, Hkv, dh = 96, 4, 2, 64
+    q, k, v = _meta(Kt, Hq, dh), _meta(Kt, Hkv, dh), _meta(Kt, Hkv, dh)
+    s, g, t = _meta(Kt, dtype=f32), _meta(Hq, dtype=f32), _meta(Hq, dtype=f32)
+    cu = [0, 40, Kt]
+    f = tg.tg_gated_attn_prefill
+    _raises_size(f, q, k, v, s, g, t, [0, 40, Kt - 1], match="cu_kept")
+    _raises_size(f, q, k, v, s, g, t, [0, 40, Kt + 1], match="cu_kept")
+    _raises_size(f, q, _meta(Kt - 1, Hkv, dh), v, s, g, t, cu, match="k")
+    _raises_size(f, q, k, _meta(Kt, Hkv, dh - 8), s, g, t, cu, match="v")
+    _raises_size(f, q, _meta(Kt, 3, dh), _meta(Kt, 3, dh), s, g, t, cu, match="multiple")
+    _raises_size(f, q, k, v, _meta(Kt - 1, dtype=f32), g, t, cu, match="s_kept")
+    _raises_size(f, q, k, v, s, _meta(Hq - 1, dtype=f32), t, cu, match="gain")
+    _raises_size(f, q, k, v, s, g, _meta(Hq + 1, dtype=f32), cu, match="temp")
+    _raises_size(f, q, k, v, s, g, t, cu, out=_meta(Kt, Hq, dh - 1), match="out")
+    _raises_size(f, q, k, v, s, g, t, cu, lse=_meta(Kt, Hq, dtype=f32), match="lse")
+    # backward: the same checks plus the gradient buffers
+    fb = tg.tg_gated_attn_backward
+    o, lse = _meta(Kt, Hq, dh), _meta(Hq, Kt, dtype=f32)
+    _raises_size(fb, q, k, v, s, g, t, o, lse, _meta(Kt, Hq, dh + 1), cu, match="dout")
+    _raises_size(fb, q, k, v, s, g, t, o, _meta(Hq, Kt - 1, dtype=f32), o, cu, match="lse")
+    grads = {"dq": _meta(Kt, Hq, dh), "dk": _meta(Kt, Hkv, dh), "dv": _meta(Kt, Hkv, dh - 1),
+             "ds": _meta(Kt, dtype=f32), "dgain": _meta(Hq, dtype=f32), "dtemp": _meta(Hq, dtype=f32)}
+    _raises_size(fb, q, k, v, s, g, t, o, lse, o, cu, grads=grads, match="dv")
+
+
+def test_binding_checks_other_sizes():
+    import torch
+    f32, i32 = torch.float32, torch.int32
+    # gate backward
+    x, w1, w2 = _meta(50, 128), _meta(64, 128), _meta(64)
+    _raises_size(tg.tg_gate_backward, x, w1, None, w2, _meta(49, dtype=f32), match="ds_kept")
+    _raises_size(tg.tg_gate_backward, x, _meta(64, 127), None, w2, _meta(50, dtype=f32), match="w1")
+    # decode
+    B, Hq, Hkv, dh, R = 3, 4, 2, 64, 40
+    qd, kd = _meta(B, Hq, dh), _meta(R, Hkv, dh)
+    args = (qd, kd, kd, _meta(R, dtype=f32), _meta(B, dtype=torch.int64), _meta(B, dtype=i32),
+            _meta(Hq, dtype=f32), _meta(Hq, dtype=f32), 16)
+    _raises_size(tg.tg_gated_attn_decode, qd, kd, _meta(R - 1, Hkv, dh), *args[3:], match="v")
+    _raises_size(tg.tg_gated_attn_decode, *args[:4], _meta(B + 1, dtype=torch.int64), *args[5:],
+                 match="row_off")
+    _raises_size(tg.tg_gated_attn_decode, *args, out=_meta(B, Hq, dh + 1), match="out")
+    # layer pieces and the projection
+    _raises_size(tg.tg_rmsnorm, _meta(10, 64), _meta(63), 1e-6, match="w")
+    _raises_size(tg.tg_rmsnorm, _meta(10, 64), _meta(64), 1e-6, y=_meta(9, 64), match="y")
+    _raises_size(tg.tg_qk_norm_rope, _meta(10, 4, 64), _meta(9, 2, 64), None, None,
+                 _meta(10, dtype=i32), 1e6, 1e-6, match="k")
+    _raises_size(tg.tg_qk_norm_rope, _meta(10, 4, 64), _meta(10, 2, 64), None, None,
+                 _meta(11, dtype=i32), 1e6, 1e-6, match="pos")
+    _raises_size(tg.tg_silu_mul, _meta(10, 128), out=_meta(10, 65), match="out")
+    _raises_size(tg.tg_kept_positions, _meta(10, dtype=i32), [0, 100], [0, 11], match="kept_idx")
+    _raises_size(tg.tg_linear, _meta(10, 128), _meta(64, 127), match="w")
+    _raises_size(tg.tg_linear, _meta(10, 128), _meta(64, 128), y=_meta(10, 63), match="y")

@@ -222,13 +222,12 @@ def test_attention_eight_wave_sampled(name, lens, Hq, Hkv, dh):
 
 
 # ---------------------------------------------------------------- linear ----
-@pytest.mark.parametrize("tile", ["small", "mid", "large"])
+@pytest.mark.parametrize("tile", [1, 2, 3])
 def test_linear_every_tiling(tile):
     """Each workgroup tiling (128x128, 256x128, 256x256; the launcher picks
-    one by output size, TG_LINEAR_TILE forces it) on ragged m and n, with odd
+    one by output size, tg_linear_tile forces it) on ragged m and n, with odd
     (K = 192 in 64-wide chunks) and even numbers of k chunks, accumulating and
     not."""
-    import os
     rt, at = tol(torch.bfloat16)
     for M, N, K, acc in ((777, 320, 2048, False), (1000, 192, 192, True), (300, 2112, 64, True)):
         announce(f"linear tile={tile} M={M} N={N} K={K} acc={acc}")
@@ -237,12 +236,8 @@ def test_linear_every_tiling(tile):
         w = (torch.randn(N, K, generator=g) / K ** 0.5).to(torch.bfloat16)
         y0 = torch.randn(M, N, generator=g).to(torch.bfloat16)
         y = y0.cuda().clone()
-        os.environ["TG_LINEAR_TILE"] = tile
-        try:
-            tg.tg_linear(x.cuda(), w.cuda(), y=y, accumulate=acc)
-            torch.cuda.synchronize()
-        finally:
-            os.environ.pop("TG_LINEAR_TILE", None)
+        tg.tg_linear(x.cuda(), w.cuda(), y=y, accumulate=acc, tile=tile)
+        torch.cuda.synchronize()
         ref = oracle.linear(x, w) + (y0.double() if acc else 0.0)
         assert_within(y.cpu(), ref, rt, at, f"linear {tile}")
 

@@ -5,7 +5,6 @@ tolerance.  Selection, run on the oracle's fp32 scores: bit-exact kept ids.
 Gather: bitwise.
 """
 import math
-import os
 
 import pytest
 import torch
@@ -90,20 +89,13 @@ def _select_case(seq, q, bud, scores, prefix=None):
     must give the oracle's kept ids bit for bit, and the device cu_kept."""
     ref, cu_ref = oracle.topk_select(scores, seq, q, bud, prefix)
     sg = scores.cuda()
-    for path in ("auto", "multi"):
-        announce(f"select[{path}] B={len(seq)} T={sum(seq)} seq={seq[:4]} q={q[:4]} budget={bud[:4]}"
+    # path 0: the library's choice; 2: the chunked path forced.
+    for path in (0, 2):
+        announce(f"select[path {path}] B={len(seq)} T={sum(seq)} seq={seq[:4]} q={q[:4]} budget={bud[:4]}"
                  + ("" if prefix is None else f" prefix={prefix[:4]}"))
-        old = os.environ.pop("TG_SELECT_PATH", None)
-        if path == "multi":
-            os.environ["TG_SELECT_PATH"] = "multi"
-        try:
-            cu_dev = torch.full((len(seq) + 1,), -1, dtype=torch.int32, device="cuda")
-            got, cu = tg.tg_topk_select(sg, seq, q, bud, cu_kept_dev=cu_dev, prefix_len=prefix)
-            torch.cuda.synchronize()
-        finally:
-            os.environ.pop("TG_SELECT_PATH", None)
-            if old is not None:
-                os.environ["TG_SELECT_PATH"] = old
+        cu_dev = torch.full((len(seq) + 1,), -1, dtype=torch.int32, device="cuda")
+        got, cu = tg.tg_topk_select(sg, seq, q, bud, cu_kept_dev=cu_dev, prefix_len=prefix, path=path)
+        torch.cuda.synchronize()
         assert cu == cu_ref
         assert cu_dev.cpu().tolist() == cu_ref, f"{path}: device cu_kept"
         assert torch.equal(got.cpu(), ref), f"{path}: kept ids differ"
