@@ -188,6 +188,32 @@ tg_status tg_topk_select_prefix(const float *scores, const tg_batch_prefix *b, i
                                 int32_t *cu_kept_dev, void *ws, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* Size of the device scratch array behind tg_topk_select_noalloc. */
+#define TG_SELECT_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * tg_topk_select_noalloc -- tg_topk_select for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The selector's workspace is a file-scope device
+ * array of TG_SELECT_SCRATCH_BYTES (8 MiB) inside the library; every GPU the
+ * library runs on holds its own copy until the process ends.  The call
+ * allocates and frees nothing; the caller still owns scores, kept_idx and
+ * cu_kept_dev.  Arguments and results as tg_topk_select.
+ * Limit: a batch whose documents all fit the one-workgroup path (at most
+ * 32768 tokens each) uses no scratch; any other batch must need at most
+ * TG_SELECT_SCRATCH_BYTES of workspace (tg_plan's topk_ws_bytes; a single
+ * request of up to about 900k tokens), else TG_ERR_WORKSPACE and nothing is
+ * launched.
+ * Every call on one GPU shares that GPU's scratch, which keeps the previous
+ * call's contents (the call clears what must start at zero itself): calls
+ * that overlap in time on one GPU (two streams, two host threads) race, and
+ * the caller must serialise them.
+ * Errors: those of tg_topk_select (TG_ERR_WORKSPACE as above), and
+ * TG_ERR_LAUNCH when the scratch address cannot be obtained.
+ */
+tg_status tg_topk_select_noalloc(const float *scores, const tg_batch *b, int32_t *kept_idx,
+                                 int32_t *cu_kept_dev, hipStream_t stream);
+
 /*
  * tg_topk_select_path -- tg_topk_select_prefix with the implementation chosen
  * by the caller (for testing that both give the same kept ids; prefix_len may

@@ -30,6 +30,7 @@ __all__ = [
     "tg_plan",
     "tg_gate_score",
     "tg_topk_select",
+    "tg_topk_select_noalloc",
     "tg_gather_compact",
     "tg_gated_attn_prefill",
     "tg_attn_backward_plan",
@@ -113,6 +114,8 @@ def lib() -> ctypes.CDLL:
     L.tg_gate_score.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp, vp, vp, i32, vp, vp]
     L.tg_topk_select.restype = ctypes.c_int
     L.tg_topk_select.argtypes = [vp, ctypes.POINTER(_Batch), vp, vp, vp, sz, vp]
+    L.tg_topk_select_noalloc.restype = ctypes.c_int
+    L.tg_topk_select_noalloc.argtypes = [vp, ctypes.POINTER(_Batch), vp, vp, vp]
     L.tg_topk_select_path.restype = ctypes.c_int
     L.tg_topk_select_path.argtypes = [vp, ctypes.POINTER(_BatchPrefix), vp, vp, vp, sz, ctypes.c_int, vp]
     L.tg_plan_prefix.restype = ctypes.c_int
@@ -314,6 +317,24 @@ def tg_topk_select(scores, seq_len: Sequence[int], q_len: Sequence[int], budget:
     else:
         _check("tg_topk_select", lib().tg_topk_select(*args, _stream(stream)))
     return kept_idx, cu_k
+
+
+def tg_topk_select_noalloc(scores, seq_len: Sequence[int], q_len: Sequence[int],
+                           budget: Sequence[int], kept_idx, cu_kept_dev=None, stream=None):
+    """tg_topk_select with the workspace in the library's static device scratch:
+    the call allocates nothing (kept_idx must be given).  Returns the host
+    cu_kept list."""
+    torch = _torch()
+    cu_s, cu_k, _ = tg_plan(seq_len, q_len, budget)
+    _numel(scores, "scores", cu_s[-1])
+    _numel(kept_idx, "kept_idx", cu_k[-1])
+    _numel(cu_kept_dev, "cu_kept_dev", len(cu_k))
+    bt, keep = _batch(seq_len, q_len, budget)
+    _check("tg_topk_select_noalloc", lib().tg_topk_select_noalloc(
+        _dev(scores, "scores", torch.float32), ctypes.byref(bt),
+        _dev(kept_idx, "kept_idx", torch.int32), _dev(cu_kept_dev, "cu_kept_dev", torch.int32),
+        _stream(stream)))
+    return cu_k
 
 
 def tg_gather_compact(hidden, kept_idx, scores=None, hidden_kept=None, scores_kept=None,

@@ -31,6 +31,8 @@
 //      table per workgroup), and the question tail after them.
 // Results do not depend on which workgroup finishes last.
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "tg_device.h"
 #include "tg_kernels.h"
@@ -764,6 +766,52 @@ bool select_one_wg_fits(const BatchArgs& a) {
     for (int b = 0; b < a.batch; ++b)
         if (a.cu_seq[b + 1] - a.cu_seq[b] - a.q_len[b] - a.p_len[b] > SM_MAX) return false;
     return true;
+}
+
+}  // namespace tg
+
+// ----------------------------------------- allocation-free entry point ----
+// The workspace of tg_topk_select_noalloc: one copy per GPU, resident from the
+// library's load to the end of the process.  In host code this name is only a
+// host-side stand-in for the symbol, never a device address: select_scratch()
+// obtains each device's own address with hipGetSymbolAddress, and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[TG_SELECT_SCRATCH_BYTES];
+
+namespace tg {
+
+namespace {
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::atomic<void*> scratch_ptr[SCRATCH_MAX_DEVICES];
+std::mutex scratch_mu;
+}  // namespace
+
+hipError_t select_scratch(hipStream_t st, void** out) {
+    int dev = -1;
+    hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // First call on this device: look the address up with the device current.
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            int cur = -1;
+            if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (cur != dev) {
+                const hipError_t e2 = hipSetDevice(cur);
+                if (e == hipSuccess) e = e2;
+            }
+            if (e != hipSuccess) return e;
+            if (p == nullptr) return hipErrorInvalidSymbol;
+            scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
 }
 
 size_t select_workspace_bytes(const BatchArgs& a) {

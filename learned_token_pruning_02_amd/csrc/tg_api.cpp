@@ -167,6 +167,29 @@ tg_status tg_topk_select(const float* scores, const tg_batch* b, int32_t* kept_i
     return select_checked(scores, a, kept_idx, cu_kept_dev, ws, ws_bytes, tg::SELECT_AUTO, stream);
 }
 
+tg_status tg_topk_select_noalloc(const float* scores, const tg_batch* b, int32_t* kept_idx,
+                                 int32_t* cu_kept_dev, hipStream_t stream) {
+    tg::BatchArgs a;
+    const tg_status st = plan_batch(b, &a);
+    if (st != TG_OK) return st;
+    if (scores == nullptr || kept_idx == nullptr) return TG_ERR_NULL_PTR;
+    // The one-workgroup path needs no workspace; the chunked path's must fit
+    // the static scratch.  All of this is decided before any HIP call.
+    const bool chunked = !tg::select_one_wg_fits(a);
+    const size_t need = chunked ? tg::select_workspace_bytes(a) : 0;
+    if (need > TG_SELECT_SCRATCH_BYTES) return TG_ERR_WORKSPACE;
+    if (!aligned4(scores) || !aligned4(kept_idx) || !aligned4(cu_kept_dev)) return TG_ERR_ALIGNMENT;
+    const int64_t T = a.cu_seq[a.batch], Kt = a.cu_kept[a.batch];
+    if (overlap(kept_idx, Kt * 4, scores, T * 4) ||
+        overlap(cu_kept_dev, (a.batch + 1) * 4, scores, T * 4) ||
+        overlap(cu_kept_dev, (a.batch + 1) * 4, kept_idx, Kt * 4))
+        return TG_ERR_ALIAS;
+    void* ws = nullptr;
+    if (need > 0 && tg::select_scratch(stream, &ws) != hipSuccess) return TG_ERR_LAUNCH;
+    return launched(tg::launch_select(scores, a, kept_idx, cu_kept_dev, ws,
+                                      chunked ? tg::SELECT_CHUNKED : tg::SELECT_ONE_WG, stream));
+}
+
 tg_status tg_topk_select_path(const float* scores, const tg_batch_prefix* b, int32_t* kept_idx,
                               int32_t* cu_kept_dev, void* ws, size_t ws_bytes, int path,
                               hipStream_t stream) {

@@ -31,6 +31,9 @@ bool select_one_wg_fits(const BatchArgs& a);
 size_t select_workspace_bytes(const BatchArgs& a);
 hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept, int32_t* cu_dev,
                          void* ws, int path, hipStream_t st);
+// Device address of the library's select scratch array (TG_SELECT_SCRATCH_BYTES)
+// on the device of stream st, looked up once per device.
+hipError_t select_scratch(hipStream_t st, void** out);
 
 hipError_t launch_gather(const void* hidden, int64_t T, int row_bytes, const float* scores,
                          const int32_t* kept, int64_t Kt, void* hidden_kept, float* scores_kept,

@@ -549,3 +549,24 @@ def test_binding_checks_other_sizes():
     _raises_size(tg.tg_kept_positions, _meta(10, dtype=i32), [0, 100], [0, 11], match="kept_idx")
     _raises_size(tg.tg_linear, _meta(10, 128), _meta(64, 127), match="w")
     _raises_size(tg.tg_linear, _meta(10, 128), _meta(64, 128), y=_meta(10, 63), match="y")
+
+
+def test_select_noalloc_validation():
+    """tg_topk_select_noalloc decides on the host, before any HIP call, that a
+    batch needs more than the library's static scratch, and checks pointers
+    like tg_topk_select."""
+    L = tg.lib()
+    f = L.tg_topk_select_noalloc
+    bt, keep = _batch([100], [10], [20])
+    assert f(None, ctypes.byref(bt), B, None, None) == 1
+    assert f(A, ctypes.byref(bt), None, None, None) == 1
+    assert f(A, None, B, None, None) == 1
+    assert f(A + 2, ctypes.byref(bt), B, None, None) == 6
+    assert f(A, ctypes.byref(bt), A + 40, None, None) == 9        # kept ids inside the scores
+    bad, keep_b = _batch([10], [4], [3])
+    assert f(A, ctypes.byref(bad), B, None, None) == 3
+    # a chunked-path batch whose workspace exceeds the scratch
+    big = 1_200_000
+    assert tg.tg_plan([big], [128], [8192])[2] > 8 << 20
+    bt2, keep2 = _batch([big], [128], [8192])
+    assert f(A, ctypes.byref(bt2), B, None, None) == 7
