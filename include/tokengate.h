@@ -138,9 +138,10 @@ tg_status tg_gate_score(tg_dtype dt, const void *hidden, int64_t T, int32_t d_mo
  *               contents on entry do not matter; calls that share one
  *               workspace must not run concurrently.
  * Two implementations give identical results: when every request's document
- * has at most 32768 tokens, one 1024-thread workgroup per request selects in
- * a single launch (the workspace is then unused); otherwise the document is
- * cut into chunks over many workgroups (tg_topk_select_path forces either).
+ * has at most 65536 tokens, one 1024-thread workgroup per request selects in
+ * a single launch for the whole batch (the workspace is then unused);
+ * otherwise the documents are cut into chunks over many workgroups
+ * (tg_topk_select_path forces either).
  * Errors: those of tg_plan, TG_ERR_NULL_PTR, TG_ERR_WORKSPACE, TG_ERR_LAUNCH.
  */
 tg_status tg_topk_select(const float *scores, const tg_batch *b, int32_t *kept_idx,
@@ -200,7 +201,7 @@ tg_status tg_topk_select_prefix(const float *scores, const tg_batch_prefix *b, i
  * allocates and frees nothing; the caller still owns scores, kept_idx and
  * cu_kept_dev.  Arguments and results as tg_topk_select.
  * Limit: a batch whose documents all fit the one-workgroup path (at most
- * 32768 tokens each) uses no scratch; any other batch must need at most
+ * 65536 tokens each) uses no scratch; any other batch must need at most
  * TG_SELECT_SCRATCH_BYTES of workspace (tg_plan's topk_ws_bytes; a single
  * request of up to about 900k tokens), else TG_ERR_WORKSPACE and nothing is
  * launched.
@@ -219,7 +220,7 @@ tg_status tg_topk_select_noalloc(const float *scores, const tg_batch *b, int32_t
  * by the caller (for testing that both give the same kept ids; prefix_len may
  * be NULL, which is tg_topk_select): path 0 chooses as tg_topk_select does,
  * 1 forces the one-workgroup path (TG_ERR_UNSUPPORTED when a document has
- * more than 32768 tokens), 2 forces the chunked path.  Any other path is
+ * more than 65536 tokens), 2 forces the chunked path.  Any other path is
  * TG_ERR_BAD_SHAPE.  Other arguments and errors as tg_topk_select_prefix.
  */
 tg_status tg_topk_select_path(const float *scores, const tg_batch_prefix *b, int32_t *kept_idx,

@@ -111,8 +111,6 @@ struct AttnArgs {
 };
 
 constexpr int KVT = 64;          // keys per tile
-// Fourth word of a raw buffer resource (32-bit data format, no swizzle).
-constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
 constexpr int VT_STRIDE = KVT + 8;  // LDS row stride of V^T (bf16 elements)
 
 // Number of query tiles whose local index is >= t.

@@ -627,23 +627,49 @@ void chunk_plan(const BatchArgs& a, SelArgs* s, int* doc_chunks, int* all_chunks
 }
 
 // ------------------------------------------------ one-workgroup path ----
-// When every document of the batch is short enough, each request is selected
-// by one 1024-thread workgroup in a single launch: thread t holds the keys of
-// the document positions [t*IT, (t+1)*IT) in registers, three histogram
-// passes (11, 11, 10 key bits; one private 2048-bin LDS histogram per wave,
-// so atomics only contend within a wave -- gate scores crowd a few dozen
-// top-bit bins) find the exact K_doc-th best key T and how many keys equal
-// to T are kept, and one ordered compaction (block scans of the keys equal
-// to T in index order, then of the kept tokens) writes the kept ids.  No
-// workspace, no global atomics.
-constexpr int SM_THREADS = 1024;
-constexpr int SM_WAVES = SM_THREADS / WAVE;
-constexpr int SM_IT = 32;                       // keys per thread at most
-constexpr int SM_MAX = SM_THREADS * SM_IT;      // 32768 document tokens per request
-static_assert(SM_MAX == SELECT_ONE_WG_MAX, "one-workgroup capacity");
+// When every document of the batch has at most SELECT_ONE_WG_MAX tokens, each
+// request is selected by one 1024-thread workgroup, the whole batch in a
+// single launch.  The document is read in rows of 4096 keys, thread t taking
+// positions 4t .. 4t+3 of a row in one 16-byte load (a wave reads 1 KiB of
+// consecutive scores per load), four rows at a time; the first four rows
+// (16384 keys) stay in registers for every pass, later ones are re-read.
+//   1. the first rows give a value range: their mean +- 8 standard
+//      deviations within their min and max;
+//   2. every score goes to one of 2048 bins linear in that value range
+//      (scores outside it, NaN and infinities to the end bins).  The map is
+//      monotone, so every key of a higher bin beats every key of a lower one
+//      whatever the first rows missed, and a few outliers (planted needles,
+//      say) do not stretch the range over the bulk of the scores.  Linear in
+//      the value, it spreads gate scores evenly (the top bits of the float,
+//      or bins linear in the order key, crowd them into a few, and the
+//      histogram then stalls on same-address LDS atomics).  A descending scan
+//      over the bins finds the bin d holding the K_doc-th best key and how
+//      many of its keys are kept;
+//   3. one pass collects the keys of bin d with their positions (usually a
+//      few dozen) and counts, per (row, wave), the keys of higher bins; the
+//      candidates are ranked exactly under (key descending, position
+//      ascending) in LDS, the kept ones marked in a bitmap and added to their
+//      (row, wave) counts, which one block scan turns into output offsets;
+//   4. one pass writes the kept positions in order (wave ballots).
+// When bin d holds more than S1_CAND keys (heavy ties), its keys are ranked by
+// three radix passes over the 32-bit key instead (11, 11, 10 bits), which give
+// the threshold key T and how many keys equal to T are kept (the lowest
+// positions), and the counting pass also counts keys equal to T.
+constexpr int S1_THREADS = 1024;
+constexpr int S1_WAVES = S1_THREADS / WAVE;
+constexpr int S1_KPT = 4;                        // consecutive keys per thread per row
+constexpr int S1_ROW = S1_THREADS * S1_KPT;      // 4096 keys per row
+constexpr int S1_GR = 4;                         // rows per group (loads in flight per thread)
+constexpr int S1_GROUP = S1_ROW * S1_GR;         // 16384 keys per group
+constexpr int S1_MAX = SELECT_ONE_WG_MAX;        // document tokens per request
+constexpr int S1_ROWS = S1_MAX / S1_ROW;         // rows at most
+constexpr int S1_NB = 2048;                      // bins of the first histogram
+constexpr int S1_CAND = 1024;                    // candidates ranked in LDS
+constexpr int S1_BPT = S1_NB / S1_THREADS;       // bins per thread in the bin scans
+static_assert(S1_MAX % S1_GROUP == 0 && S1_ROWS * S1_WAVES <= S1_THREADS, "rows");
 
-// Exclusive block scan over 1024 threads; *total gets the sum.
-__device__ __forceinline__ uint32_t scan1024_excl(uint32_t v, uint32_t* wtot, uint32_t* total) {
+// Exclusive block scan over the S1_THREADS threads of v; *total gets the sum.
+__device__ __forceinline__ uint32_t s1_scan_excl(uint32_t v, uint32_t* wtot, uint32_t* total) {
     const int lane = lane_id(), w = threadIdx.x / WAVE;
     uint32_t x = v;
 #pragma unroll
@@ -655,7 +681,7 @@ __device__ __forceinline__ uint32_t scan1024_excl(uint32_t v, uint32_t* wtot, ui
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < SM_WAVES; ++i) {
+    for (int i = 0; i < S1_WAVES; ++i) {
         if (i < w) before += wtot[i];
         all += wtot[i];
     }
@@ -664,107 +690,365 @@ __device__ __forceinline__ uint32_t scan1024_excl(uint32_t v, uint32_t* wtot, ui
     return x - v + before;
 }
 
-__global__ __launch_bounds__(SM_THREADS) void sel_small_kernel(SelArgs a) {
-    __shared__ uint32_t whist[SM_WAVES][NBIN];   // 128 KiB: one histogram per wave
-    __shared__ uint32_t wtot[SM_WAVES];
-    __shared__ uint32_t sh_d, sh_rem;
+// Over the S1_NB bins of hist, the bin d holding the rem-th largest element
+// (count(bins > d) < rem <= count(bins >= d)): *d, the rank within it
+// (*rank_in) and its count (*cnt), set by the owning thread.  Thread t owns
+// the S1_BPT bins below S1_NB - S1_BPT t (descending order in thread order).
+__device__ __forceinline__ void s1_find_bin(const uint32_t* hist, uint32_t rem, uint32_t* wtot,
+                                            uint32_t* d, uint32_t* rank_in, uint32_t* cnt) {
+    const int top = S1_NB - 1 - S1_BPT * (int)threadIdx.x;
+    uint32_t c[S1_BPT], sum = 0;
+#pragma unroll
+    for (int k = 0; k < S1_BPT; ++k) {
+        c[k] = hist[top - k];
+        sum += c[k];
+    }
+    uint32_t tot;
+    uint32_t above = s1_scan_excl(sum, wtot, &tot);
+#pragma unroll
+    for (int k = 0; k < S1_BPT; ++k) {
+        if (above < rem && rem <= above + c[k]) {
+            *d = (uint32_t)(top - k);
+            *rank_in = rem - above;
+            *cnt = c[k];
+        }
+        above += c[k];
+    }
+}
+
+// In-place exclusive scan of n <= S1_THREADS counts in LDS (one per thread).
+__device__ __forceinline__ void s1_scan_counts(uint32_t* c, int n, uint32_t* wtot) {
+    const int t = threadIdx.x;
+    const uint32_t v = t < n ? c[t] : 0u;
+    uint32_t tot;
+    const uint32_t e = s1_scan_excl(v, wtot, &tot);
+    if (t < n) c[t] = e;
+    __syncthreads();
+}
+
+// Bin of score v for the value range [vmin, vmin + (S1_NB - 2) / scale]:
+// linear in the value, clamped to the end bins (NaN and -inf to bin 0, +inf
+// to the last), so monotone in the selection order (a higher key never lands
+// in a lower bin, and -0 and +0 share a bin).
+__device__ __forceinline__ uint32_t s1_bin(float v, float vmin, float scale) {
+    const float f = (v - vmin) * scale;
+    if (!(f >= 1.0f)) return 0u;  // below the range, NaN
+    return f < (float)(S1_NB - 1) ? (uint32_t)f : (uint32_t)(S1_NB - 1);
+}
+
+// The keys of this thread in one group of S1_GR rows: v[r][e] is position
+// S1_GROUP g + S1_ROW r + 4t + e (positions past the document read as 0 and
+// are excluded by the caller).  Whole vectors are reinterpreted: a bit cast
+// of one element of a u32x4 yielded element 0 for every index with this
+// toolchain.
+struct S1Group {
+    f32x4 v[S1_GR];
+};
+__device__ __forceinline__ S1Group s1_load(__amdgpu_buffer_rsrc_t r, int g) {
+    S1Group x;
+    const int base = (g * S1_GROUP + S1_KPT * (int)threadIdx.x) * 4;
+#pragma unroll
+    for (int k = 0; k < S1_GR; ++k)
+        x.v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, base + 4 * S1_ROW * k, 0, 0));
+    return x;
+}
+
+// Run body(row index, keys of that row as f32x4) over the rows of the
+// document: group 0 from registers (c0), later groups loaded per pass.
+template <class Body>
+__device__ __forceinline__ void s1_rows(__amdgpu_buffer_rsrc_t rs, int nrows, const S1Group& c0,
+                                        Body body) {
+#pragma unroll
+    for (int k = 0; k < S1_GR; ++k)
+        if (k < nrows) body(k, c0.v[k]);
+    const int ngroups = (nrows + S1_GR - 1) / S1_GR;
+    for (int g = 1; g < ngroups; ++g) {
+        const S1Group x = s1_load(rs, g);
+#pragma unroll
+        for (int k = 0; k < S1_GR; ++k)
+            if (g * S1_GR + k < nrows) body(g * S1_GR + k, x.v[k]);
+    }
+}
+
+__global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
+    __shared__ uint32_t hist[S1_NB];
+    __shared__ uint32_t cnt[S1_ROWS * S1_WAVES];    // per (row, wave): kept keys
+    __shared__ uint32_t eqc[S1_ROWS * S1_WAVES];    // per (row, wave): keys == T (ties path)
+    __shared__ uint32_t bits[S1_MAX / 32];          // kept candidates
+    __shared__ uint2 cand[S1_CAND];                 // (key, position) of the keys in bin d
+    __shared__ uint32_t wtot[S1_WAVES];
+    __shared__ float wmin[S1_WAVES], wmax[S1_WAVES], wsum[S1_WAVES], wsq[S1_WAVES], wcnt[S1_WAVES];
+    __shared__ uint32_t sh_d, sh_rem, sh_cnt, sh_ncand;
 
     const int b = blockIdx.x, tid = threadIdx.x, w = tid / WAVE, lane = lane_id();
     if (b == 0 && a.cu_dev != nullptr)
-        for (int i = tid; i <= a.batch; i += SM_THREADS) a.cu_dev[i] = a.out[i];
+        for (int i = tid; i <= a.batch; i += S1_THREADS) a.cu_dev[i] = a.out[i];
     const int off = a.off[b], N = a.off[b + 1] - off;
     const int out = a.out[b], K = a.out[b + 1] - out;
     int32_t* kept = a.kept + out;
     if (K >= N) {  // the budget covers the request
-        for (int i = tid; i < N; i += SM_THREADS) kept[i] = off + i;
+        for (int i = tid; i < N; i += S1_THREADS) kept[i] = off + i;
         return;
     }
     const int q = a.q[b], p = a.p[b];
     const int ndoc = N - q - p, kdoc = K - q - p;
-    for (int i = tid; i < p; i += SM_THREADS) kept[i] = off + i;
-    for (int i = tid; i < q; i += SM_THREADS) kept[p + kdoc + i] = off + N - q + i;
-
-    const int IT = (ndoc + SM_THREADS - 1) / SM_THREADS;
-    const int i0 = min(ndoc, tid * IT), i1 = min(ndoc, i0 + IT);
-    const int nmine = i1 - i0;
-    uint32_t kr[SM_IT];
-    const float* s = a.scores + off + p + i0;
-#pragma unroll
-    for (int j = 0; j < SM_IT; ++j) kr[j] = j < nmine ? order_key(s[j]) : 0u;
-
-    // Threshold key T (the kdoc-th best key) and `need`, the number of keys
-    // equal to T that are kept (the lowest-indexed ones).  kdoc == 0 keeps
-    // nothing: T above every key.
-    uint32_t thr = 0xffffffffu, need = 0;
-    if (kdoc > 0) {
-        uint32_t prefix = 0, pmask = 0, rem = (uint32_t)kdoc;
-        uint32_t* hw = whist[w];
-        for (int pass = 0; pass < 3; ++pass) {
-            const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-            const int width = pass == 2 ? 10 : 11;
-            const uint32_t dmask = (1u << width) - 1u;
-            for (int i = lane; i < NBIN; i += WAVE) hw[i] = 0;
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < SM_IT; ++j)
-                if (j < nmine && (kr[j] & pmask) == prefix) atomicAdd(&hw[(kr[j] >> shift) & dmask], 1u);
-            __syncthreads();
-            // Thread t owns bins 2047-2t and 2046-2t (descending order in thread order).
-            const int hi = NBIN - 1 - 2 * tid;
-            uint32_t c0 = 0, c1 = 0;
-#pragma unroll
-            for (int ww = 0; ww < SM_WAVES; ++ww) {
-                c0 += whist[ww][hi];
-                c1 += whist[ww][hi - 1];
-            }
-            uint32_t tot;
-            const uint32_t above = scan1024_excl(c0 + c1, wtot, &tot);  // keys in higher bins
-            if (above < rem && rem <= above + c0) {
-                sh_d = (uint32_t)hi;
-                sh_rem = rem - above;
-            } else if (above + c0 < rem && rem <= above + c0 + c1) {
-                sh_d = (uint32_t)(hi - 1);
-                sh_rem = rem - above - c0;
-            }
-            __syncthreads();
-            prefix |= sh_d << shift;
-            pmask |= dmask << shift;
-            rem = sh_rem;
-            __syncthreads();
-        }
-        thr = prefix;
-        need = rem;
-    }
-
-    // Ordered compaction over this thread's positions [i0, i1).
-    uint32_t eq = 0;
-#pragma unroll
-    for (int j = 0; j < SM_IT; ++j) eq += (j < nmine && kr[j] == thr) ? 1u : 0u;
-    uint32_t tot;
-    const uint32_t eq_before = scan1024_excl(eq, wtot, &tot);
-    uint32_t nk = 0, e = eq_before;
-#pragma unroll
-    for (int j = 0; j < SM_IT; ++j) {
-        const bool t_eq = j < nmine && kr[j] == thr;
-        nk += (j < nmine && kr[j] > thr) || (t_eq && e < need);
-        e += t_eq;
-    }
-    uint32_t pos = scan1024_excl(nk, wtot, &tot);
+    for (int i = tid; i < p; i += S1_THREADS) kept[i] = off + i;
+    for (int i = tid; i < q; i += S1_THREADS) kept[p + kdoc + i] = off + N - q + i;
+    if (kdoc <= 0) return;  // only the prefix and the question are kept
+    const float* s = a.scores + off + p;  // document keys, positions 0..ndoc-1
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)s, (short)0, ndoc * 4, BUFFER_RSRC_WORD3);
+    const int nrows = (ndoc + S1_ROW - 1) / S1_ROW;
+    const int nslot = nrows * S1_WAVES;
+    const int pos0 = S1_KPT * tid;  // this thread's first position in a row
     int32_t* dst = kept + p;
-    e = eq_before;
+    // The ranks of this lane's keys within its wave's slice of a row: keys
+    // of lower lanes first, then this lane's in position order.
+    auto lane_offset = [&](uint32_t m4) {  // m4: this lane's 4 flags
+        uint32_t o = 0;
 #pragma unroll
-    for (int j = 0; j < SM_IT; ++j) {
-        const bool t_eq = j < nmine && kr[j] == thr;
-        if ((j < nmine && kr[j] > thr) || (t_eq && e < need)) dst[pos++] = off + p + i0 + j;
-        e += t_eq;
+        for (int e = 0; e < S1_KPT; ++e) o += lanes_below(__ballot((m4 >> e) & 1u));
+        return o;
+    };
+    auto wave_count = [&](uint32_t m4) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < S1_KPT; ++e) c += (uint32_t)__popcll(__ballot((m4 >> e) & 1u));
+        return c;
+    };
+
+    // ---- 1. value range from the first group ----------------------------------
+    const S1Group c0 = s1_load(rs, 0);
+    float vmin = INFINITY, vmax = -INFINITY, sum = 0.f, sq = 0.f, cnt_f = 0.f;
+#pragma unroll
+    for (int k = 0; k < S1_GR; ++k) {
+#pragma unroll
+        for (int e = 0; e < S1_KPT; ++e) {
+            const float v = c0.v[k][e];
+            if (S1_ROW * k + pos0 + e < ndoc && fabsf(v) <= 3.402823466e38f) {  // finite
+                vmin = fminf(vmin, v);
+                vmax = fmaxf(vmax, v);
+                sum += v;
+                sq = fmaf(v, v, sq);
+                cnt_f += 1.f;
+            }
+        }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        vmin = fminf(vmin, __shfl_xor(vmin, o, WAVE));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, o, WAVE));
+        sum += __shfl_xor(sum, o, WAVE);
+        sq += __shfl_xor(sq, o, WAVE);
+        cnt_f += __shfl_xor(cnt_f, o, WAVE);
+    }
+    for (int i = tid; i < S1_NB; i += S1_THREADS) hist[i] = 0u;
+    if (lane == 0) {
+        wmin[w] = vmin;
+        wmax[w] = vmax;
+        wsum[w] = sum;
+        wsq[w] = sq;
+        wcnt[w] = cnt_f;
+    }
+    __syncthreads();
+    sum = sq = cnt_f = 0.f;
+#pragma unroll
+    for (int i = 0; i < S1_WAVES; ++i) {
+        vmin = fminf(vmin, wmin[i]);
+        vmax = fmaxf(vmax, wmax[i]);
+        sum += wsum[i];
+        sq += wsq[i];
+        cnt_f += wcnt[i];
+    }
+    float lo = vmin, hi = vmax;
+    if (cnt_f > 0.f) {
+        const float mu = sum / cnt_f;
+        const float sd = sqrtf(fmaxf(sq / cnt_f - mu * mu, 0.f));
+        if (sd <= 3.402823466e38f) {
+            lo = fmaxf(lo, mu - 8.f * sd);
+            hi = fminf(hi, mu + 8.f * sd);
+        }
+    }
+    // Bins of width (hi - lo) / (S1_NB - 2) between the end bins; a
+    // degenerate or non-finite range puts every score in bin 0.
+    const float span = hi - lo;
+    const float scale = span > 0.f && span <= 3.402823466e38f ? (float)(S1_NB - 2) / span : 0.f;
+    const float vlo = lo >= -3.402823466e38f ? lo : 0.f;
+
+    // ---- 2. histogram, threshold bin ------------------------------------------
+    s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
+        const int i0 = r * S1_ROW + pos0;
+#pragma unroll
+        for (int e = 0; e < S1_KPT; ++e)
+            if (i0 + e < ndoc) atomicAdd(&hist[s1_bin(x[e], vlo, scale)], 1u);
+    });
+    __syncthreads();
+    s1_find_bin(hist, (uint32_t)kdoc, wtot, &sh_d, &sh_rem, &sh_cnt);
+    if (tid == 0) sh_ncand = 0u;
+    for (int i = tid; i < (ndoc + 31) / 32; i += S1_THREADS) bits[i] = 0u;
+    __syncthreads();
+    const uint32_t d = sh_d, rem = sh_rem;
+
+    if (sh_cnt <= (uint32_t)S1_CAND) {
+        // ---- 3. candidates of bin d, counts of higher bins ---------------------
+        s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
+            const int i0 = r * S1_ROW + pos0;
+            uint32_t up = 0u;
+#pragma unroll
+            for (int e = 0; e < S1_KPT; ++e) {
+                if (i0 + e < ndoc) {
+                    const uint32_t bn = s1_bin(x[e], vlo, scale);
+                    if (bn > d) up |= 1u << e;
+                    if (bn == d) cand[atomicAdd(&sh_ncand, 1u)] = make_uint2(order_key(x[e]), (uint32_t)(i0 + e));
+                }
+            }
+            const uint32_t c = wave_count(up);
+            if (lane == 0) cnt[r * S1_WAVES + w] = c;
+        });
+        __syncthreads();
+        // Exact rank of each candidate under (key desc, position asc); the
+        // first rem are kept.
+        const uint32_t nc = sh_ncand;
+        for (uint32_t c = tid; c < nc; c += S1_THREADS) {
+            const uint2 me = cand[c];
+            uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+            uint32_t o = 0;
+            for (; o + 4 <= nc; o += 4) {
+                const uint2 e0 = cand[o], e1 = cand[o + 1], e2 = cand[o + 2], e3 = cand[o + 3];
+                r0 += (e0.x > me.x) || (e0.x == me.x && e0.y < me.y);
+                r1 += (e1.x > me.x) || (e1.x == me.x && e1.y < me.y);
+                r2 += (e2.x > me.x) || (e2.x == me.x && e2.y < me.y);
+                r3 += (e3.x > me.x) || (e3.x == me.x && e3.y < me.y);
+            }
+            for (; o < nc; ++o) {
+                const uint2 e0 = cand[o];
+                r0 += (e0.x > me.x) || (e0.x == me.x && e0.y < me.y);
+            }
+            if (r0 + r1 + r2 + r3 < rem) {
+                atomicOr(&bits[me.y / 32], 1u << (me.y % 32));
+                atomicAdd(&cnt[(me.y / S1_ROW) * S1_WAVES + (me.y % S1_ROW) / (S1_KPT * WAVE)], 1u);
+            }
+        }
+        __syncthreads();
+        s1_scan_counts(cnt, nslot, wtot);
+        // ---- 4. ordered write ------------------------------------------------
+        s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
+            const int i0 = r * S1_ROW + pos0;
+            uint32_t km = 0u;
+#pragma unroll
+            for (int e = 0; e < S1_KPT; ++e) {
+                const int i = i0 + e;
+                if (i < ndoc) {
+                    const uint32_t bn = s1_bin(x[e], vlo, scale);
+                    if (bn > d || (bn == d && ((bits[i / 32] >> (i % 32)) & 1u))) km |= 1u << e;
+                }
+            }
+            uint32_t pos = cnt[r * S1_WAVES + w] + lane_offset(km);
+#pragma unroll
+            for (int e = 0; e < S1_KPT; ++e) {
+                if ((km >> e) & 1u) {
+                    if (pos < (uint32_t)kdoc) dst[pos] = off + p + i0 + e;
+                    ++pos;
+                }
+            }
+        });
+        return;
+    }
+
+    // ---- 3'. heavy ties: radix passes over the keys of bin d --------------
+    uint32_t prefix = 0u, pmask = 0u, rr = rem;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int width = pass == 2 ? 10 : 11;
+        const uint32_t dmask = (1u << width) - 1u;
+        for (int i = tid; i < S1_NB; i += S1_THREADS) hist[i] = 0u;
+        __syncthreads();
+        s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
+            const int i0 = r * S1_ROW + pos0;
+#pragma unroll
+            for (int e = 0; e < S1_KPT; ++e) {
+                if (i0 + e < ndoc) {
+                    const uint32_t k = order_key(x[e]);
+                    if (s1_bin(x[e], vlo, scale) == d && (k & pmask) == prefix)
+                        atomicAdd(&hist[(k >> shift) & dmask], 1u);
+                }
+            }
+        });
+        __syncthreads();
+        s1_find_bin(hist, rr, wtot, &sh_d, &sh_rem, &sh_cnt);
+        __syncthreads();
+        prefix |= sh_d << shift;
+        pmask |= dmask << shift;
+        rr = sh_rem;
+        __syncthreads();
+    }
+    const uint32_t T = prefix, need = rr;  // keep keys > T and the first `need` keys == T
+    // Counts per (row, wave): keys above T in cnt, keys equal to T in eqc.
+    s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
+        const int i0 = r * S1_ROW + pos0;
+        uint32_t um = 0u, em = 0u;
+#pragma unroll
+        for (int e = 0; e < S1_KPT; ++e) {
+            if (i0 + e < ndoc) {
+                const uint32_t k = order_key(x[e]);
+                if (k > T) um |= 1u << e;
+                if (k == T) em |= 1u << e;
+            }
+        }
+        const uint32_t cu = wave_count(um), ce = wave_count(em);
+        if (lane == 0) {
+            cnt[r * S1_WAVES + w] = cu;
+            eqc[r * S1_WAVES + w] = ce;
+        }
+    });
+    __syncthreads();
+    {
+        // keys == T of each (row, wave) that are kept: those ranked below `need`
+        const uint32_t e_here = tid < nslot ? eqc[tid] : 0u;
+        uint32_t tot;
+        const uint32_t e_before = s1_scan_excl(e_here, wtot, &tot);
+        if (tid < nslot) {
+            cnt[tid] += e_before >= need ? 0u : min(need - e_before, e_here);
+            eqc[tid] = e_before;
+        }
+    }
+    __syncthreads();
+    s1_scan_counts(cnt, nslot, wtot);
+    s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
+        const int i0 = r * S1_ROW + pos0;
+        uint32_t em = 0u, km = 0u;
+#pragma unroll
+        for (int e = 0; e < S1_KPT; ++e) {
+            if (i0 + e < ndoc) {
+                const uint32_t k = order_key(x[e]);
+                if (k == T) em |= 1u << e;
+                if (k > T) km |= 1u << e;
+            }
+        }
+        uint32_t er = eqc[r * S1_WAVES + w] + lane_offset(em);  // rank of this lane's first key == T
+#pragma unroll
+        for (int e = 0; e < S1_KPT; ++e) {
+            if ((em >> e) & 1u) {
+                if (er < need) km |= 1u << e;
+                ++er;
+            }
+        }
+        uint32_t pos = cnt[r * S1_WAVES + w] + lane_offset(km);
+#pragma unroll
+        for (int e = 0; e < S1_KPT; ++e) {
+            if ((km >> e) & 1u) {
+                if (pos < (uint32_t)kdoc) dst[pos] = off + p + i0 + e;
+                ++pos;
+            }
+        }
+    });
 }
 
 }  // namespace
 
 bool select_one_wg_fits(const BatchArgs& a) {
     for (int b = 0; b < a.batch; ++b)
-        if (a.cu_seq[b + 1] - a.cu_seq[b] - a.q_len[b] - a.p_len[b] > SM_MAX) return false;
+        if (a.cu_seq[b + 1] - a.cu_seq[b] - a.q_len[b] - a.p_len[b] > S1_MAX) return false;
     return true;
 }
 
@@ -836,8 +1120,8 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
     s.kept = kept;
     s.cu_dev = cu_dev;
     const bool one_wg = path == SELECT_ONE_WG || (path == SELECT_AUTO && select_one_wg_fits(a));
-    if (one_wg) {  // every document fits in one workgroup's registers
-        hipLaunchKernelGGL(sel_small_kernel, dim3(a.batch), dim3(SM_THREADS), 0, st, s);
+    if (one_wg) {  // every document is short enough for one workgroup
+        hipLaunchKernelGGL(sel_one_kernel, dim3(a.batch), dim3(S1_THREADS), 0, st, s);
         return hipGetLastError();
     }
     int dc, ac;

@@ -30,6 +30,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int WAVE = 64;
 
+// Fourth word of a raw buffer resource (32-bit data format, no swizzle):
+// loads through such a resource past its size return zeros without touching
+// memory.
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -26,7 +26,7 @@ hipError_t launch_gate_bf16(const void* hidden, int64_t T, int d, const void* w1
 // Selector implementation: SELECT_AUTO picks the one-workgroup path when
 // every document has at most SELECT_ONE_WG_MAX tokens, else the chunked path.
 enum SelectPath { SELECT_AUTO = 0, SELECT_ONE_WG = 1, SELECT_CHUNKED = 2 };
-constexpr int SELECT_ONE_WG_MAX = 32768;
+constexpr int SELECT_ONE_WG_MAX = 65536;
 bool select_one_wg_fits(const BatchArgs& a);
 size_t select_workspace_bytes(const BatchArgs& a);
 hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept, int32_t* cu_dev,

@@ -423,7 +423,7 @@ def test_select_path_validation():
     assert f(A, ctypes.byref(bt), B, None, C, ws, 3, None) == 2
     assert f(A, ctypes.byref(bt), B, None, C, ws, -1, None) == 2
     assert f(None, ctypes.byref(bt), B, None, C, ws, 2, None) == 1
-    n = 32768 + 11
+    n = 65536 + 11
     ws2 = tg.tg_plan([n], [10], [20])[2]
     bt2, keep2 = _batch([n], [10], [20], [0])
     assert f(A, ctypes.byref(bt2), B, None, C, ws2, 1, None) == 5

@@ -156,18 +156,40 @@ def test_select_max_batch_and_large_request():
 
 
 def test_select_one_workgroup_limits():
-    """Documents of exactly 32768 tokens (the largest the one-workgroup path
-    takes), 32769 (chunked path), ties across the threshold, NaN and +-0, a
+    """Documents of exactly 65536 tokens (the largest the one-workgroup path
+    takes), 65537 (chunked path), ties across the threshold, NaN and +-0, a
     budget of one, and a batch mixing keep-all requests."""
     g = torch.Generator().manual_seed(30)
-    s = workloads.random_scores(32768 + 64, seed=31, ties=300)
-    s[torch.randint(0, 32768, (500,), generator=g)] = float("nan")
-    s[torch.randint(0, 32768, (500,), generator=g)] = -0.0
-    _select_case([32768 + 64], [64], [5000], s)
-    _select_case([32768 + 65], [64], [5000], workloads.random_scores(32768 + 65, seed=32, ties=300))
+    L = 65536
+    s = workloads.random_scores(L + 64, seed=31, ties=300)
+    s[torch.randint(0, L, (500,), generator=g)] = float("nan")
+    s[torch.randint(0, L, (500,), generator=g)] = -0.0
+    _select_case([L + 64], [64], [5000], s)
+    _select_case([L + 65], [64], [5000], workloads.random_scores(L + 65, seed=32, ties=300))
     _select_case([40000], [1], [1], workloads.random_scores(40000, seed=33))
     seq = [100, 20000, 7, 32768, 513, 20000]                 # the last keeps only its question token
     _select_case(seq, [10, 100, 7, 0, 13, 1], [100, 3000, 9, 30000, 64, 1], torch.randn(sum(seq), generator=g))
+
+
+def test_select_one_workgroup_bins():
+    """The one-workgroup path's key range comes from a sample and its bins
+    are linear in it: keys far outside the sampled range (a few huge and tiny
+    scores), a threshold inside the end bins, and a threshold bin with more
+    candidates than are ranked in LDS (then the radix passes rank it)."""
+    g = torch.Generator().manual_seed(34)
+    T = 60000
+    s = torch.randn(T, generator=g)
+    s[torch.randint(0, T, (7,), generator=g)] = 1e30       # outliers beyond the binned range
+    s[torch.randint(0, T, (7,), generator=g)] = -1e30
+    for bud in (3, 20, 30000, 59990):                       # thresholds at the ends of the range
+        _select_case([T], [0], [bud], s)
+    # 3000 copies of one value straddling the threshold: bin d is too big to rank in LDS
+    s2 = torch.randn(T, generator=g)
+    s2[torch.randint(0, T, (3000,), generator=g)] = 1.0
+    n_above = int((s2 > 1.0).sum())
+    _select_case([T], [10], [n_above + 1500], s2)
+    # a bf16-rounded normal: many small ties, a modest candidate set
+    _select_case([T], [128], [T // 8], torch.randn(T, generator=g).to(torch.bfloat16).float())
 
 
 def test_select_sweep_scale():
