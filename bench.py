@@ -16,9 +16,12 @@ is reported beside it, and is the value with --graph), the per-kernel split
 (attention-only and kept-token rates, the bias overhead against the bias-free
 build of the same attention kernel, attention on all N tokens without pruning,
 K/V bytes kept vs full) and the CPU oracle timed on a bounded sample of the
-same workload.  --no-context skips the two context timings (for profiles that
-should hold the hot path only).  With --detail, each kernel is also timed cold,
-right after 512 MiB are written to evict the 256 MiB Infinity Cache.
+same workload.  Each kernel is also timed cold, right after 512 MiB are
+written to evict the 256 MiB Infinity Cache (labelled *_cold).  Under
+"configs", every other workload (16k, 32k with the 4-layer stack, the varlen
+batch, the tiny fp32 layer) gets its own step time, throughput and per-kernel
+warm and cold figures; --no-configs skips them.  --no-context skips the two
+context timings (for profiles that should hold the hot path only).
 """
 from __future__ import annotations
 
@@ -50,7 +53,9 @@ def parse():
                         "tokens), so that a profile holds the hot path's kernels only")
     p.add_argument("--graph", action="store_true",
                    help="report the HIP graph replay time of the step as the value")
-    p.add_argument("--detail", default="", help="also write per-kernel detail JSON to this path")
+    p.add_argument("--detail", default="", help="also write the JSON line, indented, to this path")
+    p.add_argument("--no-configs", action="store_true",
+                   help="time the named workload only (not every other workload as well)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain device copy of 512 MiB (reference for HBM byte counters)")
     p.add_argument("--select-sweep", action="store_true",
@@ -487,53 +492,24 @@ def layer_bench(args):
     print(json.dumps(rec), flush=True)
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    if args.layer:
-        if args.gpus != 1:
-            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
-            sys.exit(2)
-        layer_bench(args)
-        return
-    if args.backward:
-        if args.gpus != 1:
-            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
-            sys.exit(2)
-        backward_bench(args)
-        return
-    if args.decode:
-        if args.gpus != 1:
-            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
-            sys.exit(2)
-        decode_bench(args)
-        return
-    if args.select_sweep:
-        select_sweep()
-        return
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the path is single-GPU; sharding is a design note, not built)", file=sys.stderr)
-        sys.exit(2)
-
+def measure_config(w, args, dev, primary: bool):
+    """One gated layer (plus the stack for the stack workload) of workload w:
+    per-kernel HIP-event times over args.steps eager steps, the same step
+    replayed as a HIP graph (checked bit for bit against the eager step),
+    and each kernel again right after 512 MiB are written (evicting the
+    256 MiB Infinity Cache).  With primary, also the context timings (the
+    attention without its bias, the attention on all N tokens).  Returns the
+    per-workload record and the objects the CPU baseline needs."""
     import torch
 
     import learned_token_pruning_02_amd as tg
     import workloads
     from learned_token_pruning_02_amd.path import AttentionStack, GatedLayer
 
-    tg.lib()  # fail loudly when the library is missing
-    if not torch.cuda.is_available():
-        raise RuntimeError("bench.py needs a GPU")
-    w = workloads.get(args.workload, args.seed)
     sh = w.shape
-    dev = torch.device("cuda:0")
-
     gi = workloads.gate_inputs(w, seed=args.seed)
     ai = workloads.attn_inputs(w, seed=args.seed)
-    g = {k: v.to(dev) for k, v in gi.items()}
+    g = {k: (None if v is None else v.to(dev)) for k, v in gi.items()}
     a = {k: v.to(dev) for k, v in ai.items()}
     layer = GatedLayer(w.total_tokens, sh.d_model, sh.n_q_heads, sh.d_head, w.seq_len, w.q_len,
                        w.budget, sh.dtype, device=dev)
@@ -570,7 +546,6 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
            for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -579,66 +554,224 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
     samples = {n: sorted(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
     per = {n: sum(v) / len(v) for n, v in samples.items()}  # ms per launch (mean)
     gpu_ms = evs[0][0].elapsed_time(evs[-1][-1]) / args.steps
     ms_per_step_eager = wall * 1e3 / args.steps
-    ms_per_step = ms_per_step_eager
-    launch = "eager (one launch per kernel)"
-    ms_per_step_graph = None
-    if True:
-        # The whole step (every shape is fixed by the host-side plan, nothing
-        # in it reads back to the host or clears memory with a memset) is
-        # also captured once as a HIP graph and K replays are timed, so the
-        # kernels run back to back without per-launch gaps.  Every replay
-        # must reproduce the eager step's outputs bit for bit.
-        ref_out, ref_kept = layer.out.clone(), layer.kept.clone()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        layer.out.zero_()
+
+    # The whole step (every shape is fixed by the host-side plan, nothing in
+    # it reads back to the host or clears memory with a memset) captured once
+    # as a HIP graph; K replays are timed, and every replay must reproduce
+    # the eager step's outputs bit for bit.
+    ref_out, ref_kept = layer.out.clone(), layer.kept.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    layer.out.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    if not (torch.equal(layer.out, ref_out) and torch.equal(layer.kept, ref_kept)):
+        raise RuntimeError(f"{w.name}: graph replay of the step does not reproduce the eager step")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
         graph.replay()
-        torch.cuda.synchronize()
-        if not (torch.equal(layer.out, ref_out) and torch.equal(layer.kept, ref_kept)):
-            raise RuntimeError("graph replay of the step does not reproduce the eager step")
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        ms_per_step_graph = (time.perf_counter() - t0) * 1e3 / args.steps
-        if not (torch.equal(layer.out, ref_out) and torch.equal(layer.kept, ref_kept)):
-            raise RuntimeError("the timed graph replays do not reproduce the eager step")
-        if args.graph:
-            ms_per_step = ms_per_step_graph
-            launch = "hip graph (one step captured, replayed)"
+    torch.cuda.synchronize()
+    ms_per_step_graph = (time.perf_counter() - t0) * 1e3 / args.steps
+    if not (torch.equal(layer.out, ref_out) and torch.equal(layer.kept, ref_kept)):
+        raise RuntimeError(f"{w.name}: the timed graph replays do not reproduce the eager step")
+    del graph
+
+    # Each kernel again right after 512 MiB are written (the 256 MiB Infinity
+    # Cache then holds none of its inputs), on the outputs of the last step.
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    calls = {"gate": lambda: layer.gate(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"]),
+             "select": layer.select,
+             "gather": lambda: layer.gather(g["hidden"]),
+             "attention": lambda: layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"])}
+    cold = {}
+    for n, fn in calls.items():
+        ms = []
+        for _ in range(5):
+            flush.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        ms.sort()
+        cold[n] = {"ms_median": ms[len(ms) // 2], "ms_min": ms[0]}
+    del flush
 
     kept_per_req = [layer.cu_kept[i + 1] - layer.cu_kept[i] for i in range(w.batch)]
     alg = algorithmic(w, kept_per_req)
+    bf16 = sh.dtype == torch.bfloat16
+    mfma_peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
     kernels = {}
     for n in ["gate", "select", "gather", "attention"]:
         t = per[n] * 1e-3
+        tc = cold[n]["ms_median"] * 1e-3
         kernels[n] = {"ms": per[n], "ms_median": samples[n][len(samples[n]) // 2],
                       "ms_min": samples[n][0], "GB/s": alg[n]["bytes"] / t / 1e9,
                       "hbm_frac": alg[n]["bytes"] / t / 1e9 / HBM_PEAK_GBS,
-                      "TFLOP/s": alg[n]["flops"] / t / 1e12}
-    bf16 = sh.dtype == torch.bfloat16
-    mfma_peak = BF16_PEAK_TFLOPS if bf16 else F32_PEAK_TFLOPS
-    kernels["attention"]["mfma_frac"] = kernels["attention"]["TFLOP/s"] / mfma_peak
-    kernels["gate"]["mfma_frac"] = kernels["gate"]["TFLOP/s"] / mfma_peak
+                      "TFLOP/s": alg[n]["flops"] / t / 1e12,
+                      "ms_cold": cold[n]["ms_median"],
+                      "hbm_frac_cold": alg[n]["bytes"] / tc / 1e9 / HBM_PEAK_GBS}
+        if n in ("gate", "attention"):
+            kernels[n]["mfma_frac"] = kernels[n]["TFLOP/s"] / mfma_peak
     if stack is not None:
         kernels["stack"] = {"ms": per["stack"]}
+
+    derived = None
+    if primary:
+        def timed(fn, reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+            for _ in range(2):
+                fn()
+            ev[0].record()
+            for i in range(reps):
+                fn()
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+
+        # The bias overhead: the same attention kernel built without the bias
+        # stage (s_kept = gain = NULL), same inputs, same stream.
+        nobias_out = torch.empty_like(layer.out)
+        t_bias = timed(lambda: layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"]), 10)
+        t_nobias = t_bias if args.no_context else timed(
+            lambda: tg.tg_gated_attn_prefill(a["q"], a["k"], a["v"], None, None, a["temp"],
+                                             layer.cu_kept, out=nobias_out), 10)
+        # Context: the same kernel on every token of the prompt without
+        # pruning (no bias, temperature 1).
+        t_full = [float("nan")]
+        if not args.no_context:
+            gfull = torch.Generator(device=dev).manual_seed(args.seed + 7)
+            Tn = w.total_tokens
+            qf = torch.randn(Tn, sh.n_q_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+            kf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+            vf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
+            of = torch.empty_like(qf)
+            ones = torch.ones(sh.n_q_heads, device=dev)
+            t_full = timed(lambda: tg.tg_gated_attn_prefill(qf, kf, vf, None, None, ones, layer.cu_seq,
+                                                            out=of), 3)
+            del qf, kf, vf, of
+        eb = 2 if bf16 else 4
+        kv_row = 2 * sh.n_kv_heads * sh.d_head * eb
+        derived = {
+            "attn_layer_tok_s": w.total_tokens / (per["attention"] * 1e-3),
+            "kept_tok_s": layer.Kt / (per["attention"] * 1e-3),
+            "bias_overhead": t_bias[len(t_bias) // 2] / t_nobias[len(t_nobias) // 2],
+            "attn_ms_median_bias": t_bias[len(t_bias) // 2],
+            "attn_ms_median_nobias": t_nobias[len(t_nobias) // 2],
+            "kv_bytes_kept": layer.Kt * kv_row,
+            "kv_bytes_full": w.total_tokens * kv_row,
+            "full_prefill_attn_ms_median": t_full[len(t_full) // 2],
+            "attention_saving": t_full[len(t_full) // 2] / t_bias[len(t_bias) // 2],
+        }
+
+    summary = {
+        "tokens": w.total_tokens, "kept": layer.Kt, "requests": w.batch,
+        "dtype": "bf16" if bf16 else "f32", "stack_layers": w.stack_layers,
+        "ms_per_step": ms_per_step_eager, "ms_per_step_graph": ms_per_step_graph,
+        "tokens_per_s": w.total_tokens / (ms_per_step_eager * 1e-3),
+        "tokens_per_s_graph": w.total_tokens / (ms_per_step_graph * 1e-3),
+        "kernels_us": {n: round(v["ms"] * 1e3, 2) for n, v in kernels.items()},
+        "kernels_us_cold": {n: round(cold[n]["ms_median"] * 1e3, 2) for n in cold},
+        "gate_hbm_frac": kernels["gate"]["hbm_frac"],
+        "gate_hbm_frac_cold": kernels["gate"]["hbm_frac_cold"],
+        "gather_hbm_frac": kernels["gather"]["hbm_frac"],
+        "gather_hbm_frac_cold": kernels["gather"]["hbm_frac_cold"],
+        "attn_mfma_frac": kernels["attention"]["mfma_frac"],
+        "select_us": kernels["select"]["ms"] * 1e3,
+    }
+    res = {"summary": summary, "kernels": kernels, "cold": cold, "derived": derived,
+           "per": per, "gpu_ms": gpu_ms, "ms_per_step_eager": ms_per_step_eager,
+           "ms_per_step_graph": ms_per_step_graph, "bf16": bf16, "mfma_peak": mfma_peak,
+           "Kt": layer.Kt, "cu_kept": list(layer.cu_kept)}
+    if primary and not args.no_cpu_baseline:
+        res["cpu_inputs"] = (gi, ai, layer.scores.cpu(), layer.kept.cpu())
+    del layer, stack, g, a
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.layer:
+        if args.gpus != 1:
+            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
+            sys.exit(2)
+        layer_bench(args)
+        return
+    if args.backward:
+        if args.gpus != 1:
+            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
+            sys.exit(2)
+        backward_bench(args)
+        return
+    if args.decode:
+        if args.gpus != 1:
+            print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported", flush=True)
+            sys.exit(2)
+        decode_bench(args)
+        return
+    if args.select_sweep:
+        select_sweep()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path is single-GPU; sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import learned_token_pruning_02_amd as tg
+    import workloads
+
+    tg.lib()  # fail loudly when the library is missing
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.workload, args.seed)
+    sh = w.shape
+
+    main_res = measure_config(w, args, dev, primary=True)
+    configs = {w.name: main_res["summary"]}
+    if not args.no_configs:
+        # Every other workload of the same layer shape (and the tiny fp32
+        # one): per-config step time, throughput, per-kernel warm and cold
+        # times and their roofline fractions.
+        for name in workloads.WORKLOADS:
+            if name == w.name:
+                continue
+            other = workloads.get(name, args.seed)
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            configs[name] = measure_config(other, args, dev, primary=False)["summary"]
+
+    per = main_res["per"]
+    kernels = main_res["kernels"]
+    bf16 = main_res["bf16"]
+    ms_per_step = main_res["ms_per_step_eager"]
+    launch = "eager (one launch per kernel)"
+    if args.graph:
+        ms_per_step = main_res["ms_per_step_graph"]
+        launch = "hip graph (one step captured, replayed)"
 
     dominant = max(["gate", "select", "gather", "attention"], key=lambda n: per[n])
     if dominant == "attention":
         roof = {"bound": "mfma" if bf16 else "alu", "achieved": kernels["attention"]["TFLOP/s"],
-                "peak": mfma_peak, "unit": "TFLOP/s"}
+                "peak": main_res["mfma_peak"], "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": kernels[dominant]["GB/s"], "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
@@ -646,80 +779,10 @@ def main():
     roof["traffic"] = recorded_traffic(w.name, dominant)
     roof["kernel"] = dominant
 
-    # Derived rates and the bias overhead: the same attention kernel built
-    # without the bias stage (s_kept = gain = NULL), same inputs, same stream.
-    def timed(fn, reps):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-        for _ in range(2):
-            fn()
-        ev[0].record()
-        for i in range(reps):
-            fn()
-            ev[i + 1].record()
-        torch.cuda.synchronize()
-        return sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
-
-    nobias_out = torch.empty_like(layer.out)
-    t_bias = timed(lambda: layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"]), 10)
-    t_nobias = t_bias if args.no_context else timed(
-        lambda: tg.tg_gated_attn_prefill(a["q"], a["k"], a["v"], None, None, a["temp"],
-                                         layer.cu_kept, out=nobias_out), 10)
-    # Context: the same kernel on every token of the prompt without pruning
-    # (no bias, temperature 1): what the layer's attention would cost on all N.
-    t_full = [float("nan")]
-    if not args.no_context:
-        gfull = torch.Generator(device=dev).manual_seed(args.seed + 7)
-        Tn = w.total_tokens
-        qf = torch.randn(Tn, sh.n_q_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
-        kf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
-        vf = torch.randn(Tn, sh.n_kv_heads, sh.d_head, device=dev, generator=gfull).to(sh.dtype)
-        of = torch.empty_like(qf)
-        ones = torch.ones(sh.n_q_heads, device=dev)
-        t_full = timed(lambda: tg.tg_gated_attn_prefill(qf, kf, vf, None, None, ones, layer.cu_seq, out=of), 3)
-        del qf, kf, vf, of
-    eb = 2 if bf16 else 4
-    kv_row = 2 * sh.n_kv_heads * sh.d_head * eb
-    derived = {
-        "attn_layer_tok_s": w.total_tokens / (per["attention"] * 1e-3),
-        "kept_tok_s": layer.Kt / (per["attention"] * 1e-3),
-        "bias_overhead": t_bias[len(t_bias) // 2] / t_nobias[len(t_nobias) // 2],
-        "attn_ms_median_bias": t_bias[len(t_bias) // 2],
-        "attn_ms_median_nobias": t_nobias[len(t_nobias) // 2],
-        "kv_bytes_kept": layer.Kt * kv_row,
-        "kv_bytes_full": w.total_tokens * kv_row,
-        "full_prefill_attn_ms_median": t_full[len(t_full) // 2],
-        "attention_saving": t_full[len(t_full) // 2] / t_bias[len(t_bias) // 2],
-    }
-
-    cold = None
-    if args.detail:
-        # Each kernel again, right after 512 MiB are written (evicting the
-        # 256 MiB Infinity Cache), on the outputs of the last timed step.
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        calls = {"gate": lambda: layer.gate(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"]),
-                 "select": layer.select,
-                 "gather": lambda: layer.gather(g["hidden"]),
-                 "attention": lambda: layer.attend(a["q"], a["k"], a["v"], a["gain"], a["temp"])}
-        cold = {}
-        for n, fn in calls.items():
-            ms = []
-            for _ in range(5):
-                flush.fill_(1)
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                torch.cuda.synchronize()
-                ms.append(e0.elapsed_time(e1))
-            ms.sort()
-            cold[n] = {"ms_median": ms[len(ms) // 2], "ms_min": ms[0]}
-        del flush
-
     cpu = None
-    if not args.no_cpu_baseline:
-        s_cpu = layer.scores.cpu()
-        kept_cpu = layer.kept.cpu()
-        cpu = cpu_baseline(w, gi, ai, s_cpu, kept_cpu, layer.cu_kept)
+    if "cpu_inputs" in main_res:
+        gi, ai, s_cpu, kept_cpu = main_res["cpu_inputs"]
+        cpu = cpu_baseline(w, gi, ai, s_cpu, kept_cpu, main_res["cu_kept"])
 
     line = {
         "metric": "gated-prefill tokens/s per layer",
@@ -734,21 +797,21 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded; random-init gate and projection weights)",
-        "config": {"workload": w.name, "tokens": w.total_tokens, "kept": layer.Kt,
+        "config": {"workload": w.name, "tokens": w.total_tokens, "kept": main_res["Kt"],
                    "requests": w.batch, "d_model": sh.d_model, "heads_q": sh.n_q_heads,
                    "heads_kv": sh.n_kv_heads, "d_head": sh.d_head, "d_gate": sh.d_gate,
                    "stack_layers": w.stack_layers},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "derived": derived,
-        "gpu_ms_per_step": gpu_ms,
+        "derived": main_res["derived"],
+        "gpu_ms_per_step": main_res["gpu_ms"],
         "launch": launch,
-        "ms_per_step_eager": ms_per_step_eager,
-        "ms_per_step_graph": ms_per_step_graph,
+        "ms_per_step_eager": main_res["ms_per_step_eager"],
+        "ms_per_step_graph": main_res["ms_per_step_graph"],
+        "cold_after_cache_flush": main_res["cold"],
+        "configs": configs,
     }
-    if cold is not None:
-        line["cold_after_cache_flush"] = cold
     if args.detail:
         with open(args.detail, "w") as f:
             json.dump(line, f, indent=1)
