@@ -63,14 +63,19 @@ constexpr int GK = 64;   // k chunk
 constexpr int RING = 3;  // residual fragment sets per wave (two chunks in flight)
 constexpr int RED_STRIDE = 36;  // floats per row of the unit-sum tile (16-byte aligned, skewed banks)
 
-template <int DG, int WAVES, int MT, int OCC>
+// US = 2 splits the gate units between two waves of the same tokens (each
+// owns DG/2 units; their partial scores are summed in LDS in a fixed order),
+// so that a short prompt still gives every SIMD a wave.
+template <int DG, int WAVES, int MT, int OCC, int US = 1>
 __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
     const bf16* __restrict__ hidden, int64_t T, int d, const bf16* __restrict__ w1,
     const bf16* __restrict__ b1, const bf16* __restrict__ w2, const bf16* __restrict__ b2,
     float* __restrict__ scores) {
-    constexpr int BM = 32 * MT * WAVES;   // tokens per workgroup (MT 32-token blocks per wave)
-    constexpr int NT = DG / 32;            // 32-unit tiles
-    constexpr int NFRAG = NT * 4;          // W1 fragments (1 KB each) per k chunk
+    constexpr int BM = 32 * MT * WAVES / US;  // tokens per workgroup (MT 32-token blocks per wave)
+    constexpr int NTA = DG / 32;           // 32-unit tiles staged per k chunk
+    constexpr int NT = NTA / US;           // 32-unit tiles of one wave
+    constexpr int NFRAG = NTA * 4;         // W1 fragments (1 KB each) per k chunk
+    static_assert(US == 1 || US == 2, "unit split");
 
     // W1 chunks in fragment layout: [buf][nt*4 + kk][lane] 16-byte units.
     __shared__ __attribute__((aligned(16))) u32x4 wl[2][NFRAG * WAVE];
@@ -84,6 +89,9 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
 
     const int lane = lane_id();
     const int w = threadIdx.x / WAVE;
+    const int tgw = w / US;        // token group of this wave
+    const int uh = w % US;         // unit half of this wave (US = 2)
+    const int nt0 = uh * NT;       // first 32-unit tile of this wave
     const int hh = lane / 32;
     const int l32 = lane % 32;
     const int64_t tok0 = (int64_t)blockIdx.x * BM;
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
     const bf16* arow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        int64_t r = tok0 + 32 * MT * w + 32 * mt + l32;
+        int64_t r = tok0 + 32 * MT * tgw + 32 * mt + l32;
         if (r > T - 1) r = T - 1;
         arow[mt] = hidden + r * d + 32 * hh;
     }
@@ -137,7 +145,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
         const float bkeep = b1 != nullptr ? 1.0f : 0.0f;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int u = 32 * nt + l32;
+            const int u = 32 * (nt0 + nt) + l32;
             bias[nt] = to_f32(bsrc[u]) * bkeep;
             wout[nt] = to_f32(w2[u]);
         }
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
 #define TG_READ_B(dst, buf, kk)                                                              \
     do {                                                                                     \
         _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                    \
-            dst[nt] = as_bf16x8(wl[buf][(nt * 4 + (kk)) * WAVE + rd_pos[kk]]);                \
+            dst[nt] = as_bf16x8(wl[buf][((nt0 + nt) * 4 + (kk)) * WAVE + rd_pos[kk]]);        \
     } while (0)
     // The 2*NT MFMAs of one k slice, with NL loads (LOAD1(li)) spread evenly
     // between them, so that the vector-memory pipe fills while MFMAs run
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
     // fragments: they are read PD MFMAs ahead, one at a time, with W1 loads
     // spread over slice 0 and residual loads over slice 1.
     constexpr int PD = 4;
-#define TG_BFRAG(buf, i) as_bf16x8(wl[buf][(((i) % NT) * 4 + (i) / NT) * WAVE + rd_pos[(i) / NT]])
+#define TG_BFRAG(buf, i) as_bf16x8(wl[buf][((nt0 + (i) % NT) * 4 + (i) / NT) * WAVE + rd_pos[(i) / NT]])
 #define TG_STEP_STREAM(s, cur, ahead)                                                        \
     do {                                                                                     \
         const int s_ = (s);                                                                  \
@@ -316,15 +324,26 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
         }
     }
     __builtin_amdgcn_wave_barrier();
+    float sum = 0.f;
     if (lane < 32 * MT) {
-        float sum = b2 != nullptr ? to_f32(b2[0]) : 0.f;
+        sum = (b2 != nullptr && uh == 0) ? to_f32(b2[0]) : 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             const f32x4 v = *reinterpret_cast<const f32x4*>(&rt[lane * RED_STRIDE + 4 * c]);
             sum += (v[0] + v[1]) + (v[2] + v[3]);
         }
+    }
+    if constexpr (US == 2) {
+        // The second half's partial score of each token, added to the first's.
+        __shared__ float half1[WAVES / 2][32 * MT];
+        if (uh == 1 && lane < 32 * MT) half1[tgw][lane] = sum;
+        __syncthreads();
+        if (uh == 1) return;
+        if (lane < 32 * MT) sum += half1[tgw][lane];
+    }
+    if (lane < 32 * MT) {
         const int j = lane / 2, half = lane % 2, mt = j / 16, r = j % 16;
-        const int64_t t = tok0 + 32 * MT * w + 32 * mt + 8 * (r / 4) + 4 * half + (r % 4);
+        const int64_t t = tok0 + 32 * MT * tgw + 32 * mt + 8 * (r / 4) + 4 * half + (r % 4);
         if (t < T) scores[t] = sum;
     }
 }
@@ -339,11 +358,19 @@ hipError_t launch_gate_bf16_dg(const bf16* hidden, int64_t T, int d, const bf16*
         hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 2, 1>), dim3((T + 255) / 256), dim3(256), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);
     } else if constexpr (DG == 256) {
-        // Below that, 128-token workgroups of 32-token waves, two per CU:
-        // more waves, and one workgroup's GELU epilogue overlaps the other's
-        // MFMAs and loads.
-        hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 1, 2>), dim3((T + 127) / 128), dim3(256), 0, st,
-                           hidden, T, d, w1, b1, w2, b2, scores);
+        if (T <= 128 * 256 / 2) {
+            // A short prompt (up to 16384 tokens): 64-token workgroups whose
+            // two pairs of waves split the gate units, so that every SIMD
+            // gets a wave (128-token workgroups leave half of them idle).
+            hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 1, 2, 2>), dim3((T + 63) / 64), dim3(256), 0,
+                               st, hidden, T, d, w1, b1, w2, b2, scores);
+        } else {
+            // Below 65536 tokens, 128-token workgroups of 32-token waves, two
+            // per CU: more waves, and one workgroup's GELU epilogue overlaps
+            // the other's MFMAs and loads.
+            hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 1, 2>), dim3((T + 127) / 128), dim3(256), 0, st,
+                               hidden, T, d, w1, b1, w2, b2, scores);
+        }
     } else if (T >= 128 * 512) {
         hipLaunchKernelGGL((gate_bf16_kernel<DG, 2, 2, 1>), dim3((T + 127) / 128), dim3(128), 0, st,
                            hidden, T, d, w1, b1, w2, b2, scores);

@@ -35,6 +35,8 @@ GATE_CASES = [
     ("bf16_T700_d128_dg64", (700, 128, 64, torch.bfloat16), False),
     ("bf16_T1000_d256_dg128", (1000, 256, 128, torch.bfloat16), True),
     ("bf16_T1_d64_dg64", (1, 64, 64, torch.bfloat16), True),
+    ("bf16_T16383_d2048_dg256", (16383, 2048, 256, torch.bfloat16), True),  # units split, ragged tail
+    ("bf16_T16385_d2048_dg256", (16385, 2048, 256, torch.bfloat16), False), # 128-token tiles
     ("bf16_T70001_d128_dg256", (70001, 128, 256, torch.bfloat16), True),     # 128-token tiles
     ("bf16_T131109_d128_dg256", (131109, 128, 256, torch.bfloat16), True),   # 256-token tiles
     ("qwen3_1p7b_16k", None, True),
