@@ -37,7 +37,16 @@ def _near_threshold_only(kept_a, kept_b, s_ref, w, rtol, atol):
         assert abs(float(s_ref[t]) - thr) <= atol + rtol * abs(thr), (t, float(s_ref[t]), thr)
 
 
-@pytest.mark.parametrize("wname", ["tiny_fp32", "qwen3_1p7b_16k", "qwen3_1p7b_varlen4"])
+def _oracle_scores(gi, rows_per_chunk=16384):
+    """The oracle's gate scores of every token, computed in row chunks to
+    bound the float64 working set."""
+    T = gi["hidden"].shape[0]
+    return torch.cat([oracle.gate_score(gi["hidden"][i:i + rows_per_chunk], gi["w1"], gi["b1"],
+                                        gi["w2"], gi["b2"]) for i in range(0, T, rows_per_chunk)])
+
+
+@pytest.mark.parametrize("wname", ["tiny_fp32", "qwen3_1p7b_16k", "qwen3_1p7b_varlen4",
+                                   "qwen3_1p7b_128k_niah"])
 def test_gated_layer_chain(wname):
     w = workloads.WORKLOADS[wname]
     sh = w.shape
@@ -54,8 +63,10 @@ def test_gated_layer_chain(wname):
     rtol, atol = tol(sh.dtype)
 
     s_gpu = layer.scores.cpu()
-    s_ref = oracle.gate_score(gi["hidden"], gi["w1"], gi["b1"], gi["w2"], gi["b2"])
+    s_ref = _oracle_scores(gi)
     assert_within(s_gpu, s_ref, rtol, atol, "scores")
+    if w.n_needles:
+        assert set(workloads.needle_positions(w, 0).tolist()) <= set(layer.kept.cpu().tolist())
 
     kept_gpu = layer.kept.cpu()
     kept_on_gpu_scores, cu = oracle.topk_select(s_gpu, w.seq_len, w.q_len, w.budget)
@@ -129,6 +140,43 @@ def test_stack_reduced_step_by_step():
         assert_within(a, ref_a, 2e-2, 1e-2, f"layer {li} attention")
         ref_x = x_in.double() + oracle.linear(a.view(Kt, Hq * dh), L["wo"])
         assert_within(x.cpu(), ref_x, 2e-2, 1e-2, f"layer {li} residual")
+
+
+def test_stack_full_size_sampled_rows():
+    """The 32k workload's four stack layers at their real size (the 4096 kept
+    rows the gated layer compacts, fed the gate's own kept scores), run as
+    the benchmark runs them; every sub-step of every layer is checked on
+    sampled rows against the oracle on the GPU's own inputs of that step
+    (projections from the GPU residual, attention from the GPU's q/k/v, the
+    residual update from the GPU's attention output)."""
+    w = workloads.WORKLOADS["qwen3_1p7b_32k_stack4"]
+    sh = w.shape
+    Hq, Hkv, dh = sh.n_q_heads, sh.n_kv_heads, sh.d_head
+    announce("stack 32k full size, sampled rows")
+    g = {k: v.cuda() for k, v in workloads.gate_inputs(w, seed=0).items()}
+    a = {k: v.cuda() for k, v in workloads.attn_inputs(w, seed=0).items()}
+    layer = GatedLayer(w.total_tokens, sh.d_model, Hq, dh, w.seq_len, w.q_len, w.budget, sh.dtype)
+    layer(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"], a["q"], a["k"], a["v"], a["gain"], a["temp"])
+    Kt = layer.Kt
+    assert Kt == 4096
+    cu = layer.cu_kept
+    s = layer.s_kept.cpu()
+    x = layer.hidden_kept.clone()
+    stack = AttentionStack(Kt, sh.d_model, Hq, Hkv, dh, sh.dtype)
+    rows = sorted(set(torch.randint(0, Kt, (96,), generator=torch.Generator().manual_seed(2)).tolist()
+                      + [0, 1, 63, 64, 127, 128, Kt - 1]))
+    for li, L in enumerate(workloads.stack_weights(w, 0)):
+        x_in = x.cpu()
+        stack(x, layer.s_kept, cu, [{k: v.cuda() for k, v in L.items()}])
+        torch.cuda.synchronize()
+        q, k, v, att = stack.q.cpu(), stack.k.cpu(), stack.v.cpu(), stack.attn.cpu()
+        for nm, got, wt in (("q", q, L["wq"]), ("k", k, L["wk"]), ("v", v, L["wv"])):
+            assert_within(got[rows], oracle.linear(x_in[rows], wt), 2e-2, 1e-2, f"layer {li} {nm}")
+        ref_a, _ = oracle.gated_attention_rows(q.view(Kt, Hq, dh), k.view(Kt, Hkv, dh), v.view(Kt, Hkv, dh),
+                                               s, L["gain"], L["temp"], cu, rows)
+        assert_within(att[rows], ref_a, 2e-2, 1e-2, f"layer {li} attention")
+        ref_x = x_in[rows].double() + oracle.linear(att.view(Kt, Hq * dh)[rows], L["wo"])
+        assert_within(x.cpu()[rows], ref_x, 2e-2, 1e-2, f"layer {li} residual")
 
 
 def test_gated_layer_graph_replays():
