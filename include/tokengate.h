@@ -138,7 +138,7 @@ tg_status tg_gate_score(tg_dtype dt, const void *hidden, int64_t T, int32_t d_mo
  *               contents on entry do not matter; calls that share one
  *               workspace must not run concurrently.
  * Two implementations give identical results: when every request's document
- * has at most 65536 tokens, one 1024-thread workgroup per request selects in
+ * has at most 32768 tokens, one 1024-thread workgroup per request selects in
  * a single launch for the whole batch (the workspace is then unused);
  * otherwise the documents are cut into chunks over many workgroups
  * (tg_topk_select_path forces either).
@@ -200,8 +200,8 @@ tg_status tg_topk_select_prefix(const float *scores, const tg_batch_prefix *b, i
  * library runs on holds its own copy until the process ends.  The call
  * allocates and frees nothing; the caller still owns scores, kept_idx and
  * cu_kept_dev.  Arguments and results as tg_topk_select.
- * Limit: a batch whose documents all fit the one-workgroup path (at most
- * 65536 tokens each) uses no scratch; any other batch must need at most
+ * Limit: a batch that tg_topk_select runs on the one-workgroup path (every
+ * document at most 32768 tokens) uses no scratch; any other batch must need at most
  * TG_SELECT_SCRATCH_BYTES of workspace (tg_plan's topk_ws_bytes; a single
  * request of up to about 900k tokens), else TG_ERR_WORKSPACE and nothing is
  * launched.

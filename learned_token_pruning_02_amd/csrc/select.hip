@@ -310,11 +310,49 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     }
 
     // ---- the last chunk: exact rank inside bucket d1 ----------------------
-    // The first digit comes from the histogram the chunks built; only the
-    // candidates sharing it (usually a handful) go on, staged in LDS when
-    // they fit (a degenerate bucket of heavy ties is read from global memory
-    // on every pass instead), through the remaining radix passes.
+    // The bucket's candidates (usually a few thousand) are staged in LDS once,
+    // eight device-coherent loads in flight per thread: loaded one per loop
+    // iteration, each pass over them waited a memory round trip per item.
+    // The first digit comes from the histogram the chunks built; the passes
+    // over the remaining digits and the per-chunk kept counts then read LDS.
+    // A degenerate bucket of heavy ties too big for LDS is read from global
+    // memory on every pass instead, in the same batches.
     const uint32_t cnt1 = m[2];
+    const bool in_lds = cnt1 <= CAND_LDS;
+    constexpr int CB = 8;  // candidate loads in flight per thread
+    auto for_cands = [&](auto f) {  // f(candidate) over all cnt1 candidates
+        if (in_lds) {
+            for (uint32_t j = tid; j < cnt1; j += SB) f(cl[j]);
+            return;
+        }
+        for (uint32_t j0 = 0; j0 < cnt1; j0 += CB * SB) {
+            uint2 e[CB];
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                const uint32_t j = j0 + u * SB + tid;
+                e[u] = j < cnt1 ? coherent_load2(&cand[j]) : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < CB; ++u)
+                if (j0 + u * SB + tid < cnt1) f(e[u]);
+        }
+    };
+    if (in_lds) {
+        for (uint32_t j0 = 0; j0 < cnt1; j0 += CB * SB) {
+            uint2 e[CB];
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                const uint32_t j = j0 + u * SB + tid;
+                e[u] = j < cnt1 ? coherent_load2(&cand[j]) : make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                const uint32_t j = j0 + u * SB + tid;
+                if (j < cnt1) cl[j] = e[u];
+            }
+        }
+    }
+    __syncthreads();
     uint32_t rem = m[1];
     uint64_t cprefix = 0, cmask = 0;
     {
@@ -326,18 +364,6 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         cmask = (uint64_t)(NBIN - 1) << pass_shift(0);
     }
     const uint32_t cnt0 = sh_cnt;  // candidates sharing the first digit
-    const bool in_lds = cnt0 <= CAND_LDS;
-    if (tid == 0) sh_total = 0u;
-    __syncthreads();
-    if (cnt0 != rem && in_lds) {
-        for (uint32_t j = tid; j < cnt1; j += SB) {
-            const uint2 e = coherent_load2(&cand[j]);
-            if ((composite(e.x, e.y) & cmask) == cprefix) cl[atomicAdd(&sh_total, 1u)] = e;
-        }
-    }
-    __syncthreads();
-    const uint32_t nlist = in_lds ? cnt0 : cnt1;
-    auto cand_at = [&](uint32_t j) { return in_lds ? cl[j] : coherent_load2(&cand[j]); };
 #pragma unroll 1
     for (int p = 1; p < NPASS && cnt0 != rem; ++p) {
         const int sh = pass_shift(p);
@@ -345,11 +371,10 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         const int nb = 1 << wd;
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
         __syncthreads();
-        for (uint32_t j = tid; j < nlist; j += SB) {
-            const uint2 e = cand_at(j);
+        for_cands([&](uint2 e) {
             const uint64_t cp = composite(e.x, e.y);
             if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
-        }
+        });
         __syncthreads();
         find_bin([&](int i) { return h[i]; }, nb, rem, wtot, &sh_d, &sh_gt, &sh_cnt);
         rem -= sh_gt;
@@ -368,20 +393,25 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     for (int c0 = 0; c0 < nck; c0 += NBIN) {
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
         __syncthreads();
-        for (uint32_t j = tid; j < cnt1; j += SB) {
-            const uint2 e = coherent_load2(&cand[j]);
+        for_cands([&](uint2 e) {
             const int ch = (int)(e.y / SCHUNK) - c0;
             if (ch >= 0 && ch < NBIN && (composite(e.x, e.y) & cmask) >= cprefix)
                 atomicAdd(&ccnt[ch], 1u);
-        }
+        });
         __syncthreads();
         // each thread owns NBIN/SB consecutive chunks
-        const int per = NBIN / SB;
-        uint32_t v[NBIN / SB];
+        constexpr int per = NBIN / SB;
+        uint32_t v[per];
         uint32_t sum = 0;
+#pragma unroll
         for (int j = 0; j < per; ++j) {
             const int ch = c0 + tid * per + j;
-            v[j] = ch < nck ? ccnt[tid * per + j] + coherent_load(&def[ch]) : 0u;
+            v[j] = ch < nck ? coherent_load(&def[ch]) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < per; ++j) {
+            const int ch = c0 + tid * per + j;
+            if (ch < nck) v[j] += ccnt[tid * per + j];
             sum += v[j];
         }
         const uint32_t incl2 = block_incl_scan(sum, wtot, &sh_total);
@@ -627,9 +657,12 @@ void chunk_plan(const BatchArgs& a, SelArgs* s, int* doc_chunks, int* all_chunks
 }
 
 // ------------------------------------------------ one-workgroup path ----
-// When every document of the batch has at most SELECT_ONE_WG_MAX tokens, each
-// request is selected by one 1024-thread workgroup, the whole batch in a
-// single launch.  The document is read in rows of 4096 keys, thread t taking
+// When every document of the batch has at most SELECT_ONE_WG_AUTO tokens
+// (SELECT_ONE_WG_MAX when forced), each request is selected by one
+// 1024-thread workgroup, the whole batch in a single launch.  Above 32768
+// tokens the chunked path is faster: one CU streams the document once per
+// pass, while the chunks spread it over the chip (measured at 65536 tokens:
+// 37 against 28 us per call).  The document is read in rows of 4096 keys, thread t taking
 // positions 4t .. 4t+3 of a row in one 16-byte load (a wave reads 1 KiB of
 // consecutive scores per load), four rows at a time; the first four rows
 // (16384 keys) stay in registers for every pass, later ones are re-read.
@@ -1046,9 +1079,10 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
 
 }  // namespace
 
-bool select_one_wg_fits(const BatchArgs& a) {
+bool select_one_wg_fits(const BatchArgs& a, int max_doc) {
     for (int b = 0; b < a.batch; ++b)
-        if (a.cu_seq[b + 1] - a.cu_seq[b] - a.q_len[b] - a.p_len[b] > S1_MAX) return false;
+        if (a.cu_seq[b + 1] - a.cu_seq[b] - a.q_len[b] - a.p_len[b] > std::min(max_doc, S1_MAX))
+            return false;
     return true;
 }
 
@@ -1119,7 +1153,7 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
     s.scores = scores;
     s.kept = kept;
     s.cu_dev = cu_dev;
-    const bool one_wg = path == SELECT_ONE_WG || (path == SELECT_AUTO && select_one_wg_fits(a));
+    const bool one_wg = path == SELECT_ONE_WG || (path == SELECT_AUTO && select_auto_one_wg(a));
     if (one_wg) {  // every document is short enough for one workgroup
         hipLaunchKernelGGL(sel_one_kernel, dim3(a.batch), dim3(S1_THREADS), 0, st, s);
         return hipGetLastError();

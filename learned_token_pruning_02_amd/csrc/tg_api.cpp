@@ -175,7 +175,7 @@ tg_status tg_topk_select_noalloc(const float* scores, const tg_batch* b, int32_t
     if (scores == nullptr || kept_idx == nullptr) return TG_ERR_NULL_PTR;
     // The one-workgroup path needs no workspace; the chunked path's must fit
     // the static scratch.  All of this is decided before any HIP call.
-    const bool chunked = !tg::select_one_wg_fits(a);
+    const bool chunked = !tg::select_auto_one_wg(a);
     const size_t need = chunked ? tg::select_workspace_bytes(a) : 0;
     if (need > TG_SELECT_SCRATCH_BYTES) return TG_ERR_WORKSPACE;
     if (!aligned4(scores) || !aligned4(kept_idx) || !aligned4(cu_kept_dev)) return TG_ERR_ALIGNMENT;

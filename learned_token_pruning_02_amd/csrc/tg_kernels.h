@@ -24,10 +24,13 @@ hipError_t launch_gate_bf16(const void* hidden, int64_t T, int d, const void* w1
                             const void* w2, const void* b2, int dg, float* scores, hipStream_t st);
 
 // Selector implementation: SELECT_AUTO picks the one-workgroup path when
-// every document has at most SELECT_ONE_WG_MAX tokens, else the chunked path.
+// every document has at most SELECT_ONE_WG_AUTO tokens, else the chunked path;
+// SELECT_ONE_WG can be forced up to SELECT_ONE_WG_MAX tokens per document.
 enum SelectPath { SELECT_AUTO = 0, SELECT_ONE_WG = 1, SELECT_CHUNKED = 2 };
 constexpr int SELECT_ONE_WG_MAX = 65536;
-bool select_one_wg_fits(const BatchArgs& a);
+constexpr int SELECT_ONE_WG_AUTO = 32768;
+bool select_one_wg_fits(const BatchArgs& a, int max_doc = SELECT_ONE_WG_MAX);
+inline bool select_auto_one_wg(const BatchArgs& a) { return select_one_wg_fits(a, SELECT_ONE_WG_AUTO); }
 size_t select_workspace_bytes(const BatchArgs& a);
 hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept, int32_t* cu_dev,
                          void* ws, int path, hipStream_t st);

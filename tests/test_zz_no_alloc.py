@@ -37,11 +37,11 @@ def _both(seq, q, bud, seed):
 
 def test_noalloc_matches_select_two_calls():
     # 1: one 128k request on the chunked path (the scratch in use);
-    # 2: a smaller varlen batch, also chunked (one document > 65536 tokens).
+    # 2: a smaller varlen batch, also chunked (one document > 32768 tokens).
     _both([131072], [128], [8192], seed=11)
     _both([70000, 3000, 500], [64, 100, 500], [9000, 700, 600], seed=12)
 
 
 def test_noalloc_small_batch_uses_no_scratch():
-    # Every document fits the one-workgroup path: no scratch at all.
-    _both([60000, 16384, 2048], [128, 128, 64], [6000, 2048, 256], seed=13)
+    # Every document takes the one-workgroup path: no scratch at all.
+    _both([30000, 16384, 2048], [128, 128, 64], [3000, 2048, 256], seed=13)
