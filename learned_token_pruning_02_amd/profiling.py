@@ -34,6 +34,9 @@ KERNELS = [
     ("sel_hist_kernel", "select", "learned_token_pruning_02_amd/csrc/select.hip"),
     ("sel_cand_kernel", "select", "learned_token_pruning_02_amd/csrc/select.hip"),
     ("sel_compact_kernel", "select", "learned_token_pruning_02_amd/csrc/select.hip"),
+    ("sel_one_kernel", "select", "learned_token_pruning_02_amd/csrc/select.hip"),
+    ("sel_rank_kernel", "select", "learned_token_pruning_02_amd/csrc/select.hip"),
+    ("sel_rankcount_kernel", "select", "learned_token_pruning_02_amd/csrc/select.hip"),
     ("gather_rows_kernel", "gather", "learned_token_pruning_02_amd/csrc/gather.hip"),
     ("attn_bf16_kernel", "attention", "learned_token_pruning_02_amd/csrc/attn.hip"),
     ("attn_f32_kernel", "attention", "learned_token_pruning_02_amd/csrc/attn.hip"),

@@ -37,8 +37,11 @@ GATE_CASES = [
     ("bf16_T1_d64_dg64", (1, 64, 64, torch.bfloat16), True),
     ("bf16_T16383_d2048_dg256", (16383, 2048, 256, torch.bfloat16), True),  # units split, ragged tail
     ("bf16_T16385_d2048_dg256", (16385, 2048, 256, torch.bfloat16), False), # 128-token tiles
-    ("bf16_T70001_d128_dg256", (70001, 128, 256, torch.bfloat16), True),     # 128-token tiles
-    ("bf16_T131109_d128_dg256", (131109, 128, 256, torch.bfloat16), True),   # 256-token tiles
+    ("bf16_T65535_d128_dg256", (65535, 128, 256, torch.bfloat16), True),     # 128-token tiles
+    ("bf16_T70001_d128_dg256", (70001, 128, 256, torch.bfloat16), True),     # 256-token tiles
+    ("bf16_T65536_d192_dg256_nobias", (65536, 192, 256, torch.bfloat16), False),  # same, three k chunks
+    ("bf16_T131109_d128_dg256", (131109, 128, 256, torch.bfloat16), True),   # same, ragged tail
+    ("bf16_T131109_d128_dg128", (131109, 128, 128, torch.bfloat16), True),   # same, d_gate 128
     ("qwen3_1p7b_16k", None, True),
 ]
 
