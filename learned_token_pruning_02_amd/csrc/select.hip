@@ -52,6 +52,9 @@ constexpr int NPASS = 5;                // radix passes over the 52-bit candidat
 constexpr int BIG_DOC = 1 << 20;        // documents above this rank their candidates with every workgroup
 constexpr int RANK_WG = 512;            // workgroups of the many-workgroup candidate passes
 constexpr uint32_t CAND_LDS = 8192;     // threshold-bucket candidates staged in LDS
+constexpr int MAX_GROUPS = 2048;        // workgroups of launches 2-4 at most (chunks grouped beyond)
+static_assert(SCHUNK <= (int)CAND_LDS, "one chunk's candidates fit the staging list");
+static_assert(SCHUNK < 65536, "per-chunk counts share one 32-bit scan");
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -108,6 +111,9 @@ struct SelArgs {
     int32_t p[TG_MAX_BATCH];              // template prefix (kept); the document is [p, N - q)
     int32_t doc_chunk0[TG_MAX_BATCH + 1]; // first document chunk (selecting requests only)
     int32_t all_chunk0[TG_MAX_BATCH + 1]; // first chunk over the whole request
+    int32_t group;                        // chunks per workgroup of launches 2-4
+    int32_t doc_group0[TG_MAX_BATCH + 1]; // first chunk group of each selecting request
+    int32_t all_group0[TG_MAX_BATCH + 1]; // first chunk group over whole requests
     const float* scores;
     int32_t* kept;
     int32_t* cu_dev;
@@ -195,26 +201,39 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
     __shared__ uint32_t wtot[SWAVES];
     __shared__ uint32_t sh_last, sh_d, sh_gt, sh_cnt;
     const int tid = threadIdx.x;
-    const int b = find_request(a.doc_chunk0, a.batch, blockIdx.x);
-    const int c = blockIdx.x - a.doc_chunk0[b];
+    const int b = find_request(a.doc_group0, a.batch, blockIdx.x);
+    const int grp = blockIdx.x - a.doc_group0[b];
+    const int ngrp = a.doc_group0[b + 1] - a.doc_group0[b];
     const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
     const int N = a.off[b + 1] - a.off[b];
     const int ndoc = N - a.q[b] - a.p[b];
     const int kdoc = a.out[b + 1] - a.out[b] - a.q[b] - a.p[b];
     const float* s = a.scores + a.off[b] + a.p[b];  // document tokens, indexed from 0
+    const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, nck);
 
     for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
     __syncthreads();
+    // The chunks of this group, the keys of the next one loaded before the
+    // histogram of the current one.
     uint32_t kv[SITEMS];
+    auto load = [&](int c) {
 #pragma unroll
-    for (int it = 0; it < SITEMS; ++it) {
-        const int i = c * SCHUNK + it * SB + tid;
-        kv[it] = i < ndoc ? order_key(s[i]) : 0u;
-    }
+        for (int it = 0; it < SITEMS; ++it) {
+            const int i = c * SCHUNK + it * SB + tid;
+            kv[it] = i < ndoc ? order_key(s[i]) : 0u;
+        }
+    };
+    load(c_lo);
+    for (int c = c_lo; c < c_hi; ++c) {
+        uint32_t cur[SITEMS];
 #pragma unroll
-    for (int it = 0; it < SITEMS; ++it) {
-        const int i = c * SCHUNK + it * SB + tid;
-        if (i < ndoc) atomicAdd(&h[kv[it] >> 21], 1u);
+        for (int it = 0; it < SITEMS; ++it) cur[it] = kv[it];
+        if (c + 1 < c_hi) load(c + 1);
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) {
+            const int i = c * SCHUNK + it * SB + tid;
+            if (i < ndoc) atomicAdd(&h[cur[it] >> 21], 1u);
+        }
     }
     __syncthreads();
     uint32_t* gh = a.hist + (size_t)b * NBIN;
@@ -222,7 +241,7 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
         if (h[i] != 0u) atomicAdd(&gh[i], h[i]);
     wait_own_writes();
     __syncthreads();
-    if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 0], 1u) == (uint32_t)(nck - 1);
+    if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 0], 1u) == (uint32_t)(ngrp - 1);
     __syncthreads();
     if (!sh_last) return;
     find_bin([&](int i) { return coherent_load(&gh[i]); }, NBIN, (uint32_t)kdoc, wtot, &sh_d,
@@ -242,8 +261,9 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     __shared__ uint32_t h[NBIN];
     __shared__ uint2 cl[CAND_LDS];
     const int tid = threadIdx.x;
-    const int b = find_request(a.doc_chunk0, a.batch, blockIdx.x);
-    const int c = blockIdx.x - a.doc_chunk0[b];
+    const int b = find_request(a.doc_group0, a.batch, blockIdx.x);
+    const int grp = blockIdx.x - a.doc_group0[b];
+    const int ngrp = a.doc_group0[b + 1] - a.doc_group0[b];
     const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
     const int N = a.off[b + 1] - a.off[b];
     const int ndoc = N - a.q[b] - a.p[b];
@@ -251,52 +271,79 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     uint32_t* m = a.meta + b * META;
     const uint32_t d1 = m[0];
     uint2* cand = a.cand + a.off[b];
+    const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, nck);
+    const bool hist1 = !a.big;  // the first ranking digit is histogrammed here
 
-    uint32_t kv[SITEMS];
-    uint32_t above = 0, ncand = 0;
-#pragma unroll
-    for (int it = 0; it < SITEMS; ++it) {
-        const int i = c * SCHUNK + it * SB + tid;
-        kv[it] = i < ndoc ? order_key(s[i]) : 0u;
-        if (i < ndoc) {
-            above += (kv[it] >> 21) > d1;
-            ncand += (kv[it] >> 21) == d1;
-        }
-    }
-    uint32_t tot_above;
-    block_incl_scan(above, wtot, &tot_above);
-    uint32_t tot_cand;
-    const uint32_t incl = block_incl_scan(ncand, wtot, &tot_cand);
-    if (tid == 0) {
-        coherent_store(&a.chunk_def[a.doc_chunk0[b] + c], tot_above);
-        sh_base = tot_cand ? atomicAdd(&a.ctr[b * CTR + 2], tot_cand) : 0u;
-    }
-    __syncthreads();
-    uint32_t pos = sh_base + incl - ncand;
-#pragma unroll
-    for (int it = 0; it < SITEMS; ++it) {
-        const int i = c * SCHUNK + it * SB + tid;
-        if (i < ndoc && (kv[it] >> 21) == d1) coherent_store2(&cand[pos++], make_uint2(kv[it], (uint32_t)i));
-    }
-    if (!a.big && tot_cand != 0u) {
-        // The first ranking digit of the candidates (key bits 10-20) is
-        // histogrammed here by every chunk, so that the last chunk starts
-        // from the request's histogram instead of a pass over all of them.
+    // Per chunk of the group: the count of keys above d1 (for its output
+    // offset), and the keys in d1 staged in LDS with their index; the group's
+    // candidates then go to the request's list with one atomic, and the
+    // first ranking digit (key bits 10-20) of each is histogrammed, so that
+    // the last workgroup starts from the request's histogram instead of a
+    // pass over all of them.
+    if (hist1)
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
+    __syncthreads();
+    uint32_t* gh0 = a.rank_hist + (size_t)b * NPASS * NBIN;
+    uint32_t run = 0;  // candidates staged in cl (the same in every thread)
+    // Move the staged candidates to the request's list (one atomic for all);
+    // `more`: the list is refilled afterwards.
+    auto flush = [&](bool more) {
+        if (tid == 0) sh_base = run ? atomicAdd(&a.ctr[b * CTR + 2], run) : 0u;
         __syncthreads();
+        for (uint32_t j = tid; j < run; j += SB) coherent_store2(&cand[sh_base + j], cl[j]);
+        if (more) __syncthreads();
+        run = 0;
+    };
+    uint32_t kv[SITEMS];
+    auto load = [&](int c) {
 #pragma unroll
         for (int it = 0; it < SITEMS; ++it) {
             const int i = c * SCHUNK + it * SB + tid;
-            if (i < ndoc && (kv[it] >> 21) == d1) atomicAdd(&h[(kv[it] >> 10) & (NBIN - 1)], 1u);
+            kv[it] = i < ndoc ? order_key(s[i]) : 0u;
         }
-        __syncthreads();
-        uint32_t* gh0 = a.rank_hist + (size_t)b * NPASS * NBIN;
+    };
+    load(c_lo);
+    for (int c = c_lo; c < c_hi; ++c) {
+        uint32_t cur[SITEMS];
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) cur[it] = kv[it];
+        if (c + 1 < c_hi) load(c + 1);
+        uint32_t above = 0, ncand = 0;
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) {
+            const int i = c * SCHUNK + it * SB + tid;
+            if (i < ndoc) {
+                above += (cur[it] >> 21) > d1;
+                ncand += (cur[it] >> 21) == d1;
+            }
+        }
+        // One scan for both counts (each at most SCHUNK per chunk, so the
+        // two 16-bit halves never carry into each other).
+        uint32_t tot2;
+        const uint32_t incl2 = block_incl_scan((above << 16) | ncand, wtot, &tot2);
+        const uint32_t tot_above = tot2 >> 16, tot_cand = tot2 & 0xffffu;
+        const uint32_t incl = incl2 & 0xffffu;
+        if (tid == 0) coherent_store(&a.chunk_def[a.doc_chunk0[b] + c], tot_above);
+        if (run + tot_cand > CAND_LDS) flush(true);
+        uint32_t pos = run + incl - ncand;
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) {
+            const int i = c * SCHUNK + it * SB + tid;
+            if (i < ndoc && (cur[it] >> 21) == d1) {
+                cl[pos++] = make_uint2(cur[it], (uint32_t)i);
+                if (hist1) atomicAdd(&h[(cur[it] >> 10) & (NBIN - 1)], 1u);
+            }
+        }
+        run += tot_cand;
+    }
+    flush(false);
+    if (hist1) {
         for (int i = tid; i < NBIN; i += SB)
             if (h[i] != 0u) atomicAdd(&gh0[i], h[i]);
     }
     wait_own_writes();
     __syncthreads();
-    if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 1], 1u) == (uint32_t)(nck - 1);
+    if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 1], 1u) == (uint32_t)(ngrp - 1);
     __syncthreads();
     if (!sh_last) return;
 
@@ -503,9 +550,28 @@ __global__ __launch_bounds__(SB) void sel_rankcount_kernel(SelArgs a) {
         const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
         const uint2* cand = a.cand + a.off[b];
         uint32_t* kc = a.chunk_kept + a.doc_chunk0[b];
-        for (uint32_t j = blockIdx.x * SB + tid; j < cnt1; j += RANK_WG * SB) {
-            const uint2 e = cand[j];
-            if ((composite(e.x, e.y) & cmask) >= cprefix) atomicAdd(&kc[e.y / SCHUNK], 1u);
+        // Candidates of one chunk sit next to each other in the list (each
+        // group appends its chunks' candidates in one block), so a wave's kept
+        // candidates usually span one or two chunks: one atomic per distinct
+        // chunk of the wave instead of one per candidate.
+        const uint32_t lane = lane_id();
+        for (uint32_t j0 = blockIdx.x * SB; j0 < cnt1; j0 += RANK_WG * SB) {
+            const uint32_t j = j0 + tid;
+            bool kept = false;
+            uint32_t ch = 0;
+            if (j < cnt1) {
+                const uint2 e = cand[j];
+                kept = (composite(e.x, e.y) & cmask) >= cprefix;
+                ch = e.y / SCHUNK;
+            }
+            uint64_t todo = __ballot(kept);
+            while (todo != 0ull) {
+                const uint32_t lead = (uint32_t)__builtin_ctzll(todo);
+                const uint32_t lc = (uint32_t)__shfl((int)ch, (int)lead, WAVE);
+                const uint64_t same = __ballot(kept && ch == lc);
+                if (lane == lead) atomicAdd(&kc[lc], (uint32_t)__popcll(same));
+                todo &= ~same;
+            }
         }
         wait_own_writes();
         __syncthreads();
@@ -542,8 +608,8 @@ __global__ __launch_bounds__(SB) void sel_rankcount_kernel(SelArgs a) {
 __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     __shared__ uint32_t tab[SITEMS * SWAVES];
     const int tid = threadIdx.x, lane = lane_id(), w = tid / WAVE;
-    const int b = find_request(a.all_chunk0, a.batch, blockIdx.x);
-    const int c = blockIdx.x - a.all_chunk0[b];
+    const int b = find_request(a.all_group0, a.batch, blockIdx.x);
+    const int grp = blockIdx.x - a.all_group0[b];
     if (blockIdx.x == 0 && a.cu_dev != nullptr)
         for (int i = tid; i <= a.batch; i += SB) a.cu_dev[i] = a.out[i];
     const int off = a.off[b];
@@ -552,64 +618,69 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     const int pf = a.p[b];
     const int out = a.out[b];
     const int keep = a.out[b + 1] - out;
-    const int lo = c * SCHUNK;
-    const int hi = min(lo + SCHUNK, N);
-    if (keep >= N) {
-        for (int i = lo + tid; i < hi; i += SB) a.kept[out + i] = off + i;
-        return;
-    }
     const int ndoc = N - q - pf;
     const int kdoc = keep - q - pf;
-    // The always-kept tokens, prefix then question, as one list of pf + q <= N
-    // entries shared out by chunk: prefix token f goes to output f, question
-    // token f - pf after the prefix and the kept document tokens.
-    for (int f = lo + tid; f < min(lo + SCHUNK, pf + q); f += SB) {
-        const int i = f < pf ? f : N - q + (f - pf);
-        a.kept[out + (f < pf ? f : pf + kdoc + (f - pf))] = off + i;
-    }
-    // Chunk c of the document: document tokens [lo, lo + SCHUNK), at request
-    // positions pf + i, written after the prefix.
-    if (kdoc <= 0 || lo >= ndoc) return;
-
-    const uint32_t* m = a.meta + b * META;
-    const uint32_t d1 = m[0];
-    const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
-    const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
-    const uint32_t base = a.chunk_off[a.doc_chunk0[b] + c];
     const float* s = a.scores + off + pf;
+    const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, (N + SCHUNK - 1) / SCHUNK);
+    for (int c = c_lo; c < c_hi; ++c) {  // the chunks of this group, in order
+        const int lo = c * SCHUNK;
+        const int hi = min(lo + SCHUNK, N);
+        if (keep >= N) {
+            for (int i = lo + tid; i < hi; i += SB) a.kept[out + i] = off + i;
+            continue;
+        }
+        // The always-kept tokens, prefix then question, as one list of
+        // pf + q <= N entries shared out by chunk: prefix token f goes to
+        // output f, question token f - pf after the prefix and the kept
+        // document tokens.
+        for (int f = lo + tid; f < min(lo + SCHUNK, pf + q); f += SB) {
+            const int i = f < pf ? f : N - q + (f - pf);
+            a.kept[out + (f < pf ? f : pf + kdoc + (f - pf))] = off + i;
+        }
+        // Chunk c of the document: document tokens [lo, lo + SCHUNK), at
+        // request positions pf + i, written after the prefix.
+        if (kdoc <= 0 || lo >= ndoc) continue;
 
-    uint64_t km[SITEMS];
+        const uint32_t* m = a.meta + b * META;
+        const uint32_t d1 = m[0];
+        const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
+        const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
+        const uint32_t base = a.chunk_off[a.doc_chunk0[b] + c];
+
+        uint64_t km[SITEMS];
 #pragma unroll
-    for (int it = 0; it < SITEMS; ++it) {
-        const int i = lo + it * SB + tid;
-        bool k = false;
-        if (i < ndoc) {
-            const uint32_t key = order_key(s[i]);
-            const uint32_t dg = key >> 21;
-            k = dg > d1 || (dg == d1 && (composite(key, (uint32_t)i) & cmask) >= cprefix);
-        }
-        km[it] = __ballot(k);
-        if (lane == 0) tab[it * SWAVES + w] = (uint32_t)__popcll(km[it]);
-    }
-    __syncthreads();
-    if (w == 0) {  // exclusive scan of the SITEMS*SWAVES = 32 counts
-        uint32_t v = lane < SITEMS * SWAVES ? tab[lane] : 0u;
-        uint32_t incl = v;
-#pragma unroll
-        for (int o = 1; o < WAVE; o <<= 1) {
-            const uint32_t n = __shfl_up(incl, o, WAVE);
-            if (lane >= o) incl += n;
-        }
-        if (lane < SITEMS * SWAVES) tab[lane] = incl - v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < SITEMS; ++it) {
-        if ((km[it] >> lane) & 1ull) {
+        for (int it = 0; it < SITEMS; ++it) {
             const int i = lo + it * SB + tid;
-            const uint32_t pos = base + tab[it * SWAVES + w] + lanes_below(km[it]);
-            if (pos < (uint32_t)kdoc) a.kept[out + pf + pos] = off + pf + i;
+            bool k = false;
+            if (i < ndoc) {
+                const uint32_t key = order_key(s[i]);
+                const uint32_t dg = key >> 21;
+                k = dg > d1 || (dg == d1 && (composite(key, (uint32_t)i) & cmask) >= cprefix);
+            }
+            km[it] = __ballot(k);
+            if (lane == 0) tab[it * SWAVES + w] = (uint32_t)__popcll(km[it]);
         }
+        __syncthreads();
+        if (w == 0) {  // exclusive scan of the SITEMS*SWAVES = 32 counts
+            uint32_t v = lane < SITEMS * SWAVES ? tab[lane] : 0u;
+            uint32_t incl = v;
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const uint32_t n = __shfl_up(incl, o, WAVE);
+                if (lane >= o) incl += n;
+            }
+            if (lane < SITEMS * SWAVES) tab[lane] = incl - v;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) {
+            if ((km[it] >> lane) & 1ull) {
+                const int i = lo + it * SB + tid;
+                const uint32_t pos = base + tab[it * SWAVES + w] + lanes_below(km[it]);
+                if (pos < (uint32_t)kdoc) a.kept[out + pf + pos] = off + pf + i;
+            }
+        }
+        if (c + 1 < c_hi) __syncthreads();  // tab is rewritten by the next chunk
     }
 }
 
@@ -651,6 +722,22 @@ void chunk_plan(const BatchArgs& a, SelArgs* s, int* doc_chunks, int* all_chunks
     if (s != nullptr) {
         s->doc_chunk0[a.batch] = dc;
         s->all_chunk0[a.batch] = ac;
+        // Chunks per workgroup: one, unless that would need more than
+        // MAX_GROUPS workgroups; then consecutive chunks of a request are
+        // grouped, so that tickets, histogram flushes and candidate appends
+        // (same-address atomics, which serialise) happen once per group.
+        const int most = std::max(dc, ac);
+        const int g = std::max(1, (most + MAX_GROUPS - 1) / MAX_GROUPS);
+        s->group = g;
+        int dg = 0, ag = 0;
+        for (int b = 0; b < a.batch; ++b) {
+            s->doc_group0[b] = dg;
+            s->all_group0[b] = ag;
+            dg += (s->doc_chunk0[b + 1] - s->doc_chunk0[b] + g - 1) / g;
+            ag += (s->all_chunk0[b + 1] - s->all_chunk0[b] + g - 1) / g;
+        }
+        s->doc_group0[a.batch] = dg;
+        s->all_group0[a.batch] = ag;
     }
     *doc_chunks = dc;
     *all_chunks = ac;
@@ -1181,15 +1268,17 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
         const int n_clear = std::max(std::max(n_hist, n_ctr), std::max(n_rank, n_kept));
         hipLaunchKernelGGL(sel_clear_kernel, dim3((n_clear + SB - 1) / SB), dim3(SB), 0, st, s.hist,
                            s.ctr, n_hist, n_ctr, s.rank_hist, n_rank, s.chunk_kept, n_kept);
-        hipLaunchKernelGGL(sel_hist_kernel, dim3(dc), dim3(SB), 0, st, s);
-        hipLaunchKernelGGL(sel_cand_kernel, dim3(dc), dim3(SB), 0, st, s);
+        const int dg = s.doc_group0[a.batch];
+        hipLaunchKernelGGL(sel_hist_kernel, dim3(dg), dim3(SB), 0, st, s);
+        hipLaunchKernelGGL(sel_cand_kernel, dim3(dg), dim3(SB), 0, st, s);
         if (s.big) {
             for (int p = 0; p < NPASS; ++p)
                 hipLaunchKernelGGL(sel_rank_kernel, dim3(RANK_WG), dim3(SB), 0, st, s, p);
             hipLaunchKernelGGL(sel_rankcount_kernel, dim3(RANK_WG), dim3(SB), 0, st, s);
         }
     }
-    hipLaunchKernelGGL(sel_compact_kernel, dim3(ac), dim3(SB), 0, st, s);
+    if (s.all_group0[a.batch] > 0)
+        hipLaunchKernelGGL(sel_compact_kernel, dim3(s.all_group0[a.batch]), dim3(SB), 0, st, s);
     return hipGetLastError();
 }
 

@@ -225,6 +225,22 @@ def test_select_large_document_in_a_batch():
     _select_case(seq, q, bud, s)
 
 
+def test_select_grouped_chunks():
+    """Beyond 2048 chunks of 2048 keys, each workgroup of the chunked path
+    takes a group of consecutive chunks (one ticket, one histogram flush and
+    one candidate append per group): a batch that crosses that line, and a
+    large document with heavy ties."""
+    seq = [(1 << 22) + 77, 3000, 100000, 5]
+    q = [0, 10, 64, 5]
+    bud = [(1 << 18) + 5, 2000, 9000, 5]
+    g = torch.Generator().manual_seed(14)
+    s = torch.randn(sum(seq), generator=g)
+    s[5000:9000] = 1.5  # a run of equal scores near the threshold of the large request
+    _select_case(seq, q, bud, s)
+    T = (1 << 23) + 11
+    _select_case([T], [3], [T // 16], workloads.random_scores(T, seed=15, ties=40))
+
+
 # ----------------------------------------------- select: template prefix ----
 def _prefixes(seq, q, bud, g, cap=600):
     return [int(torch.randint(0, max(1, min(cap, min(b, n) - qq) + 1), (1,), generator=g))
