@@ -255,11 +255,17 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
 }
 
 // ------------------------------------------------------------- launch 3 ----
+// BIG: the batch ranks its candidates with every workgroup afterwards
+// (sel_rank_kernel), so the last workgroup here only publishes the start of
+// the ranking, and LDS holds just the staging list (a chunk's candidates at
+// most) and no first-digit histogram: four times as many workgroups per CU.
+template <bool BIG>
 __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
+    constexpr uint32_t CL = BIG ? (uint32_t)SCHUNK : CAND_LDS;
     __shared__ uint32_t wtot[SWAVES];
     __shared__ uint32_t sh_base, sh_last, sh_d, sh_gt, sh_cnt, sh_total;
-    __shared__ uint32_t h[NBIN];
-    __shared__ uint2 cl[CAND_LDS];
+    __shared__ uint32_t h[BIG ? 1 : NBIN];
+    __shared__ uint2 cl[CL];
     const int tid = threadIdx.x;
     const int b = find_request(a.doc_group0, a.batch, blockIdx.x);
     const int grp = blockIdx.x - a.doc_group0[b];
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     const uint32_t d1 = m[0];
     uint2* cand = a.cand + a.off[b];
     const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, nck);
-    const bool hist1 = !a.big;  // the first ranking digit is histogrammed here
+    constexpr bool hist1 = !BIG;  // the first ranking digit is histogrammed here
 
     // Per chunk of the group: the count of keys above d1 (for its output
     // offset), and the keys in d1 staged in LDS with their index; the group's
@@ -324,7 +330,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         const uint32_t tot_above = tot2 >> 16, tot_cand = tot2 & 0xffffu;
         const uint32_t incl = incl2 & 0xffffu;
         if (tid == 0) coherent_store(&a.chunk_def[a.doc_chunk0[b] + c], tot_above);
-        if (run + tot_cand > CAND_LDS) flush(true);
+        if (run + tot_cand > CL) flush(true);
         uint32_t pos = run + incl - ncand;
 #pragma unroll
         for (int it = 0; it < SITEMS; ++it) {
@@ -347,14 +353,14 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     __syncthreads();
     if (!sh_last) return;
 
-    if (a.big) {
+    if constexpr (BIG) {
         // Ranking is left to the many-workgroup passes (sel_rank_kernel).
         if (tid == 0) {
             m[3] = m[4] = m[5] = m[6] = 0u;
             m[7] = 0u;
         }
         return;
-    }
+    } else {
 
     // ---- the last chunk: exact rank inside bucket d1 ----------------------
     // The bucket's candidates (usually a few thousand) are staged in LDS once,
@@ -477,6 +483,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         m[5] = (uint32_t)cmask;
         m[6] = (uint32_t)(cmask >> 32);
     }
+    }  // !BIG
 }
 
 // ------------------------------------ large documents: ranking by all ----
@@ -622,7 +629,23 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     const int kdoc = keep - q - pf;
     const float* s = a.scores + off + pf;
     const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, (N + SCHUNK - 1) / SCHUNK);
+    const bool doc = keep < N && kdoc > 0;  // the document is selected from
+    // Scores of the document part of a chunk, those of the next chunk loaded
+    // before the current one is written.
+    float sv[SITEMS];
+    auto load = [&](int c) {
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) {
+            const int i = c * SCHUNK + it * SB + tid;
+            sv[it] = i < ndoc ? s[i] : 0.f;
+        }
+    };
+    if (doc) load(c_lo);
     for (int c = c_lo; c < c_hi; ++c) {  // the chunks of this group, in order
+        float cur[SITEMS];
+#pragma unroll
+        for (int it = 0; it < SITEMS; ++it) cur[it] = sv[it];
+        if (doc && c + 1 < c_hi) load(c + 1);
         const int lo = c * SCHUNK;
         const int hi = min(lo + SCHUNK, N);
         if (keep >= N) {
@@ -653,7 +676,7 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
             const int i = lo + it * SB + tid;
             bool k = false;
             if (i < ndoc) {
-                const uint32_t key = order_key(s[i]);
+                const uint32_t key = order_key(cur[it]);
                 const uint32_t dg = key >> 21;
                 k = dg > d1 || (dg == d1 && (composite(key, (uint32_t)i) & cmask) >= cprefix);
             }
@@ -1270,7 +1293,10 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
                            s.ctr, n_hist, n_ctr, s.rank_hist, n_rank, s.chunk_kept, n_kept);
         const int dg = s.doc_group0[a.batch];
         hipLaunchKernelGGL(sel_hist_kernel, dim3(dg), dim3(SB), 0, st, s);
-        hipLaunchKernelGGL(sel_cand_kernel, dim3(dg), dim3(SB), 0, st, s);
+        if (s.big)
+            hipLaunchKernelGGL(sel_cand_kernel<true>, dim3(dg), dim3(SB), 0, st, s);
+        else
+            hipLaunchKernelGGL(sel_cand_kernel<false>, dim3(dg), dim3(SB), 0, st, s);
         if (s.big) {
             for (int p = 0; p < NPASS; ++p)
                 hipLaunchKernelGGL(sel_rank_kernel, dim3(RANK_WG), dim3(SB), 0, st, s, p);
