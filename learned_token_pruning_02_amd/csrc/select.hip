@@ -135,6 +135,27 @@ __device__ __forceinline__ int find_request(const int32_t* base, int batch, int 
     return b;
 }
 
+// Keys c*SCHUNK + 8*tid + e (e < 8) of a document's chunk c, as two 16-byte
+// loads per thread through a buffer resource bounded by the chunk's end, so
+// that positions past the document read as 0 (callers skip them).  The
+// histogram and the candidate pass do not depend on which thread holds which
+// key; the compaction, which writes in order, keeps its own layout.
+struct Chunk8 {
+    f32x4 v[2];
+};
+__device__ __forceinline__ Chunk8 load_chunk8(const float* doc, int ndoc, int c) {
+    const int lo = c * SCHUNK;
+    const int n = min(SCHUNK, ndoc - lo);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(doc + lo), (short)0, n > 0 ? n * 4 : 0, BUFFER_RSRC_WORD3);
+    Chunk8 x;
+    // Whole vectors are reinterpreted (a bit cast of one element of a
+    // u32x4 yielded element 0 for every index with this toolchain).
+    x.v[0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * (int)threadIdx.x, 0, 0));
+    x.v[1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, 32 * (int)threadIdx.x + 16, 0, 0));
+    return x;
+}
+
 // Inclusive block scan (256 threads) of v; *total gets the sum.
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wtot, uint32_t* total) {
     const int lane = lane_id(), w = threadIdx.x / WAVE;
@@ -215,24 +236,15 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
     __syncthreads();
     // The chunks of this group, the keys of the next one loaded before the
     // histogram of the current one.
-    uint32_t kv[SITEMS];
-    auto load = [&](int c) {
-#pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            const int i = c * SCHUNK + it * SB + tid;
-            kv[it] = i < ndoc ? order_key(s[i]) : 0u;
-        }
-    };
-    load(c_lo);
+    static_assert(SITEMS == 8, "two 16-byte loads per thread and chunk");
+    Chunk8 nxt = load_chunk8(s, ndoc, c_lo);
     for (int c = c_lo; c < c_hi; ++c) {
-        uint32_t cur[SITEMS];
+        const Chunk8 cur = nxt;
+        if (c + 1 < c_hi) nxt = load_chunk8(s, ndoc, c + 1);
 #pragma unroll
-        for (int it = 0; it < SITEMS; ++it) cur[it] = kv[it];
-        if (c + 1 < c_hi) load(c + 1);
-#pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            const int i = c * SCHUNK + it * SB + tid;
-            if (i < ndoc) atomicAdd(&h[cur[it] >> 21], 1u);
+        for (int e = 0; e < SITEMS; ++e) {
+            const int i = c * SCHUNK + SITEMS * tid + e;
+            if (i < ndoc) atomicAdd(&h[order_key(cur.v[e / 4][e % 4]) >> 21], 1u);
         }
     }
     __syncthreads();
@@ -300,27 +312,19 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         if (more) __syncthreads();
         run = 0;
     };
-    uint32_t kv[SITEMS];
-    auto load = [&](int c) {
-#pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            const int i = c * SCHUNK + it * SB + tid;
-            kv[it] = i < ndoc ? order_key(s[i]) : 0u;
-        }
-    };
-    load(c_lo);
+    Chunk8 nxt = load_chunk8(s, ndoc, c_lo);
     for (int c = c_lo; c < c_hi; ++c) {
         uint32_t cur[SITEMS];
 #pragma unroll
-        for (int it = 0; it < SITEMS; ++it) cur[it] = kv[it];
-        if (c + 1 < c_hi) load(c + 1);
+        for (int e = 0; e < SITEMS; ++e) cur[e] = order_key(nxt.v[e / 4][e % 4]);
+        if (c + 1 < c_hi) nxt = load_chunk8(s, ndoc, c + 1);
         uint32_t above = 0, ncand = 0;
 #pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            const int i = c * SCHUNK + it * SB + tid;
+        for (int e = 0; e < SITEMS; ++e) {
+            const int i = c * SCHUNK + SITEMS * tid + e;
             if (i < ndoc) {
-                above += (cur[it] >> 21) > d1;
-                ncand += (cur[it] >> 21) == d1;
+                above += (cur[e] >> 21) > d1;
+                ncand += (cur[e] >> 21) == d1;
             }
         }
         // One scan for both counts (each at most SCHUNK per chunk, so the
@@ -333,11 +337,11 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         if (run + tot_cand > CL) flush(true);
         uint32_t pos = run + incl - ncand;
 #pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            const int i = c * SCHUNK + it * SB + tid;
-            if (i < ndoc && (cur[it] >> 21) == d1) {
-                cl[pos++] = make_uint2(cur[it], (uint32_t)i);
-                if (hist1) atomicAdd(&h[(cur[it] >> 10) & (NBIN - 1)], 1u);
+        for (int e = 0; e < SITEMS; ++e) {
+            const int i = c * SCHUNK + SITEMS * tid + e;
+            if (i < ndoc && (cur[e] >> 21) == d1) {
+                cl[pos++] = make_uint2(cur[e], (uint32_t)i);
+                if (hist1) atomicAdd(&h[(cur[e] >> 10) & (NBIN - 1)], 1u);
             }
         }
         run += tot_cand;
@@ -588,26 +592,39 @@ __global__ __launch_bounds__(SB) void sel_rankcount_kernel(SelArgs a) {
         const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
         const uint32_t* def = a.chunk_def + a.doc_chunk0[b];
         uint32_t* coff = a.chunk_off + a.doc_chunk0[b];
-        uint32_t carry = 0;
-        constexpr int per = NBIN / SB;
-        for (int c0 = 0; c0 < nck; c0 += NBIN) {
-            uint32_t v[per];
-            uint32_t sum = 0;
-            for (int j = 0; j < per; ++j) {
-                const int ch = c0 + tid * per + j;
-                v[j] = ch < nck ? coherent_load(&kc[ch]) + coherent_load(&def[ch]) : 0u;
-                sum += v[j];
+        // Thread t owns the contiguous chunks [t per, (t+1) per): their kept
+        // counts are summed in batches of loads in flight, one block scan
+        // gives each thread its start, and a second pass writes the offsets
+        // (a document of 2^26 tokens has 32768 chunks: one scan, not 16).
+        const int per = (nck + SB - 1) / SB;
+        const int cb = min(tid * per, nck), ce = min(cb + per, nck);
+        constexpr int LB = 8;  // loads in flight per array
+        auto batch = [&](int c, uint32_t* v) {
+#pragma unroll
+            for (int u = 0; u < LB; ++u) {
+                const int ch = c + u;
+                v[u] = ch < ce ? coherent_load(&kc[ch]) + coherent_load(&def[ch]) : 0u;
             }
-            const uint32_t incl = block_incl_scan(sum, wtot, &sh_total);
-            uint32_t run = carry + incl - sum;
-            for (int j = 0; j < per; ++j) {
-                const int ch = c0 + tid * per + j;
-                if (ch < nck) coff[ch] = run;
-                run += v[j];
-            }
-            carry += sh_total;
-            __syncthreads();
+        };
+        uint32_t sum = 0;
+        for (int c = cb; c < ce; c += LB) {
+            uint32_t v[LB];
+            batch(c, v);
+#pragma unroll
+            for (int u = 0; u < LB; ++u) sum += v[u];
         }
+        const uint32_t incl = block_incl_scan(sum, wtot, &sh_total);
+        uint32_t run = incl - sum;
+        for (int c = cb; c < ce; c += LB) {
+            uint32_t v[LB];
+            batch(c, v);
+#pragma unroll
+            for (int u = 0; u < LB; ++u) {
+                if (c + u < ce) coff[c + u] = run;
+                run += v[u];
+            }
+        }
+        __syncthreads();
     }
 }
 
