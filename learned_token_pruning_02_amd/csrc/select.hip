@@ -630,8 +630,8 @@ __global__ __launch_bounds__(SB) void sel_rankcount_kernel(SelArgs a) {
 
 // ------------------------------------------------------------- launch 4 ----
 __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
-    __shared__ uint32_t tab[SITEMS * SWAVES];
-    const int tid = threadIdx.x, lane = lane_id(), w = tid / WAVE;
+    __shared__ uint32_t wtot[SWAVES];
+    const int tid = threadIdx.x;
     const int b = find_request(a.all_group0, a.batch, blockIdx.x);
     const int grp = blockIdx.x - a.all_group0[b];
     if (blockIdx.x == 0 && a.cu_dev != nullptr)
@@ -647,22 +647,14 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     const float* s = a.scores + off + pf;
     const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, (N + SCHUNK - 1) / SCHUNK);
     const bool doc = keep < N && kdoc > 0;  // the document is selected from
-    // Scores of the document part of a chunk, those of the next chunk loaded
-    // before the current one is written.
-    float sv[SITEMS];
-    auto load = [&](int c) {
-#pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            const int i = c * SCHUNK + it * SB + tid;
-            sv[it] = i < ndoc ? s[i] : 0.f;
-        }
-    };
-    if (doc) load(c_lo);
+    // Scores of chunk c of the document, thread t holding positions
+    // c*SCHUNK + 8t .. 8t+7; the next chunk's are loaded before the current
+    // one is written.
+    Chunk8 nxt = {};
+    if (doc) nxt = load_chunk8(s, ndoc, c_lo);
     for (int c = c_lo; c < c_hi; ++c) {  // the chunks of this group, in order
-        float cur[SITEMS];
-#pragma unroll
-        for (int it = 0; it < SITEMS; ++it) cur[it] = sv[it];
-        if (doc && c + 1 < c_hi) load(c + 1);
+        const Chunk8 cur = nxt;
+        if (doc && c + 1 < c_hi) nxt = load_chunk8(s, ndoc, c + 1);
         const int lo = c * SCHUNK;
         const int hi = min(lo + SCHUNK, N);
         if (keep >= N) {
@@ -678,7 +670,9 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
             a.kept[out + (f < pf ? f : pf + kdoc + (f - pf))] = off + i;
         }
         // Chunk c of the document: document tokens [lo, lo + SCHUNK), at
-        // request positions pf + i, written after the prefix.
+        // request positions pf + i, written after the prefix in order: each
+        // thread's kept keys (8 consecutive positions) after those of the
+        // threads before it (one block scan).
         if (kdoc <= 0 || lo >= ndoc) continue;
 
         const uint32_t* m = a.meta + b * META;
@@ -686,41 +680,28 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
         const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
         const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
         const uint32_t base = a.chunk_off[a.doc_chunk0[b] + c];
-
-        uint64_t km[SITEMS];
+        const int i0 = lo + SITEMS * tid;
+        uint32_t km = 0u;
 #pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            const int i = lo + it * SB + tid;
-            bool k = false;
+        for (int e = 0; e < SITEMS; ++e) {
+            const int i = i0 + e;
             if (i < ndoc) {
-                const uint32_t key = order_key(cur[it]);
+                const uint32_t key = order_key(cur.v[e / 4][e % 4]);
                 const uint32_t dg = key >> 21;
-                k = dg > d1 || (dg == d1 && (composite(key, (uint32_t)i) & cmask) >= cprefix);
+                if (dg > d1 || (dg == d1 && (composite(key, (uint32_t)i) & cmask) >= cprefix))
+                    km |= 1u << e;
             }
-            km[it] = __ballot(k);
-            if (lane == 0) tab[it * SWAVES + w] = (uint32_t)__popcll(km[it]);
         }
-        __syncthreads();
-        if (w == 0) {  // exclusive scan of the SITEMS*SWAVES = 32 counts
-            uint32_t v = lane < SITEMS * SWAVES ? tab[lane] : 0u;
-            uint32_t incl = v;
+        const uint32_t n = (uint32_t)__popc(km);
+        uint32_t tot;
+        uint32_t pos = base + block_incl_scan(n, wtot, &tot) - n;
 #pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const uint32_t n = __shfl_up(incl, o, WAVE);
-                if (lane >= o) incl += n;
-            }
-            if (lane < SITEMS * SWAVES) tab[lane] = incl - v;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int it = 0; it < SITEMS; ++it) {
-            if ((km[it] >> lane) & 1ull) {
-                const int i = lo + it * SB + tid;
-                const uint32_t pos = base + tab[it * SWAVES + w] + lanes_below(km[it]);
-                if (pos < (uint32_t)kdoc) a.kept[out + pf + pos] = off + pf + i;
+        for (int e = 0; e < SITEMS; ++e) {
+            if ((km >> e) & 1u) {
+                if (pos < (uint32_t)kdoc) a.kept[out + pf + pos] = off + pf + i0 + e;
+                ++pos;
             }
         }
-        if (c + 1 < c_hi) __syncthreads();  // tab is rewritten by the next chunk
     }
 }
 
