@@ -162,9 +162,14 @@ struct TileStage {
 };
 
 // KV-major pass: dK, dV, score-gradient and gain/temperature partials.  The
-// workgroup walks (query head of the group, 32-query block) pairs; the Q and
+// workgroup walks (32-query block, query head of the group) pairs; the Q and
 // dO tiles of the next pair are fetched into registers while the current
 // pair is computed from the other LDS buffer (one barrier per step).
+// Consecutive workgroup ids cycle over the KV heads, so that (with as many
+// KV heads as XCDs) the workgroups of one KV head share one XCD's L2, and
+// every workgroup walks the query blocks from the request's last one down,
+// heads inner: the workgroups running at the same time then read the same
+// Q and dO tiles at about the same time, from L2 after the first.
 template <int DH>
 __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
     constexpr int KS = DH / 16;   // k-steps over the head dimension
@@ -175,8 +180,11 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
     __shared__ __align__(16) bf16 Tr[2][2 * DH * TPAD];   // [buffer] Q^T | dO^T
     __shared__ float lse2[2][TB], Dq[2][TB];
     __shared__ float s_tau[BWD_MAX_GROUP], s_gain[BWD_MAX_GROUP];
+    __shared__ float s_gt[BW][BWD_MAX_GROUP][2];  // per wave and head: (dgain, dtemp) sums
 
-    const int kb = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int kvh = (int)(blockIdx.x % (unsigned)a.Hkv);
+    const int kb = (int)((blockIdx.x / (unsigned)a.Hkv) % (unsigned)a.nkb);
+    const int b = (int)(blockIdx.x / (unsigned)(a.Hkv * a.nkb));
     const int lo = a.cu[b], n = a.cu[b + 1] - lo;
     const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
     const int col = lane % 32;
@@ -212,9 +220,14 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
         s_tau[g] = a.temp[kvh * a.G + g];
         s_gain[g] = a.gain != nullptr ? a.gain[kvh * a.G + g] : 0.0f;
     }
+    for (int i = tid; i < BW * BWD_MAX_GROUP * 2; i += BT) (&s_gt[0][0][0])[i] = 0.0f;
 
     const int nqb = (n - q0 + TB - 1) / TB;       // query blocks from the block's first key
+    const int nbt = (n + TB - 1) / TB;            // query blocks of the request
     const int iters = a.G * nqb;
+    // Step it: head g = it % G of query block nbt - 1 - it / G.
+    auto step_head = [&](int it) { return it % a.G; };
+    auto step_row = [&](int it) { return TB * (nbt - 1 - it / a.G); };
     const int64_t hs = (int64_t)a.Hq * DH;        // row stride of q and dout
     Stage st;
     float pl = 0.0f;
@@ -223,7 +236,7 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
     const float* const d_p = a.D;
     const float* const row_src = tid < TB ? lse_p : d_p;  // this thread's per-row value
     auto fetch = [&](int it) {
-        const int h = kvh * a.G + it / nqb, i0 = q0 + TB * (it % nqb);
+        const int h = kvh * a.G + step_head(it), i0 = step_row(it);
         st.fetch(a.q + (int64_t)lo * hs + h * DH, a.dout + (int64_t)lo * hs + h * DH, hs, i0, n, tid);
         // branch-free: the row index clamps, the value is masked when stored
         const int rr = tid % TB;
@@ -242,8 +255,7 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
         const int buf = it & 1;
         __syncthreads();  // buffer `buf` complete, buffer buf^1 no longer read
         if (it + 1 < iters) fetch(it + 1);
-        const int g = it / nqb, i0 = q0 + TB * (it % nqb);
-        const int h = kvh * a.G + g;
+        const int g = step_head(it), i0 = step_row(it);
         // Branch-free: a block no query of which sees these keys (or a wave
         // past the request) is masked to P = dL = 0 below.  A branch here
         // would make the compiler copy the loop-carried accumulators.
@@ -292,16 +304,18 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
                 }
             }
         }
-        if (it % nqb == nqb - 1) {  // last block of head g: leave its sums in the slot
+        {  // this step's gain/temperature terms into the wave's sums of head g
             const float dg = wave_sum(dg_acc), dt = wave_sum(dt_acc);
             if (lane == 0) {
-                gtp[2 * g] = dg;
-                gtp[2 * g + 1] = dt;
+                s_gt[w][g][0] += dg;
+                s_gt[w][g][1] += dt;
             }
             dg_acc = dt_acc = 0.0f;
         }
         if (it + 1 < iters) put(buf ^ 1);
     }
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < a.G * 2; i += WAVE) gtp[i] = s_gt[w][i / 2][i % 2];
     if (!wave_on) return;
     ds_acc += __shfl_xor(ds_acc, 32, WAVE);
     if (lane < 32 && key_ok && a.ds_part != nullptr) a.ds_part[(int64_t)kvh * a.Kt + lo + key] = ds_acc;
@@ -336,7 +350,15 @@ __global__ __launch_bounds__(BT, 2) void bwd_q_kernel(BwdArgs a) {
     __shared__ __align__(16) bf16 Tr[2][DH * TPAD];    // [buffer] K^T
     __shared__ float sb2[2][TB];
 
-    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // Consecutive workgroup ids cycle over the KV heads (the workgroups of one
+    // KV head share an XCD's L2, and all walk its key blocks from the first
+    // in step), then over the heads of the group; query blocks with the most
+    // keys come first.
+    const int kvh_u = (int)(blockIdx.x % (unsigned)a.Hkv);
+    const int rest = (int)(blockIdx.x / (unsigned)a.Hkv);
+    const int h = kvh_u * a.G + rest % a.G;
+    const int qb = a.nkb - 1 - (rest / a.G) % a.nkb;
+    const int b = rest / (a.G * a.nkb);
     const int lo = a.cu[b], n = a.cu[b + 1] - lo;
     if (qb * BW * TB >= n) return;
     const int tid = threadIdx.x, w = tid / WAVE, lane = tid % WAVE;
@@ -476,9 +498,9 @@ hipError_t launch_dh(BwdArgs& a, const AttnShape& sh, hipStream_t st) {
     hipLaunchKernelGGL(bwd_dot_kernel<DH>, dim3((unsigned)((rows * (DH / 8) + 255) / 256)), dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_kv_kernel<DH>, dim3(a.nkb, a.Hkv, sh.batch), dim3(BT), 0, st, a);
+    hipLaunchKernelGGL(bwd_kv_kernel<DH>, dim3((unsigned)(a.nkb * a.Hkv * sh.batch)), dim3(BT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_q_kernel<DH>, dim3(a.nkb, a.Hq, sh.batch), dim3(BT), 0, st, a);
+    hipLaunchKernelGGL(bwd_q_kernel<DH>, dim3((unsigned)(a.nkb * a.Hq * sh.batch)), dim3(BT), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t red_blocks = std::max<int64_t>((a.Kt + 255) / 256, (2 * a.Hq + 3) / 4);
     hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)std::max<int64_t>(1, red_blocks)), dim3(256), 0,
