@@ -143,6 +143,29 @@ KERNEL_FRAG = {"gate": "gate_bf16_kernel", "select": "sel_cand_kernel",
                "decode": "decode_chunk_kernel"}
 
 
+def recorded_traffic_sum(workload: str, frags):
+    """HBM bytes per call summed over the kernels `frags` of a committed
+    counter record of this workload, or None when one is missing or its
+    source changed since."""
+    import glob
+    import hashlib
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.json"))):
+        rec = json.load(open(f))
+        if not rec.get("workload", "").startswith(workload):
+            continue
+        total = 0.0
+        for frag in frags:
+            k = rec.get("kernels", {}).get(frag)
+            if k is None:
+                return None
+            with open(os.path.join(ROOT, k["source"]), "rb") as src:
+                if hashlib.sha256(src.read()).hexdigest() != k["source_sha256"]:
+                    return None
+            total += k["read_bytes"] + k["written_bytes"]
+        return total
+    return None
+
+
 def recorded_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` from a committed counter record of this
     workload, or None when there is none or the kernel source changed since."""
@@ -289,7 +312,10 @@ def backward_bench(args):
         "config": {"workload": "qwen3_1p7b_128k_backward", "tokens": w.total_tokens, "kept": Kt,
                    "heads_q": sh.n_q_heads, "heads_kv": sh.n_kv_heads, "d_head": sh.d_head},
         "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / BF16_PEAK_TFLOPS, "traffic": None,
+                     "frac": tf / BF16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic_sum(
+                         "qwen3_1p7b_128k_backward",
+                         ["bwd_dot_kernel", "bwd_kv_kernel", "bwd_q_kernel", "bwd_reduce_kernel"]),
                      "kernel": "attention backward (dot, KV pass, Q pass, reduce; one call)",
                      "algorithmic_flops_per_call": flops},
         "ms_call": {"mean": mean, "median": sorted(ms)[len(ms) // 2], "min": min(ms)},

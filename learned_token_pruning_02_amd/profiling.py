@@ -64,10 +64,13 @@ def source_sha(rel: str) -> str:
 
 
 def short(name: str):
+    """The longest kernel-name fragment of KERNELS that `name` contains (so
+    that gate_bwd_reduce_kernel is not taken for bwd_reduce_kernel)."""
+    best = None
     for frag, s, src in KERNELS:
-        if frag in name:
-            return frag, s, src
-    return None
+        if frag in name and (best is None or len(frag) > len(best[0])):
+            best = (frag, s, src)
+    return best
 
 
 def _csv(d: str, suffix: str):
@@ -131,17 +134,21 @@ def main():
           "Command (from the repository root):", "", "```", a.command, "```", "",
           "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read MiB | written MiB |",
           "|---|---|---|---|---|"]
+    seen = collections.Counter()
     for name in sorted(set(fetch) | set(write)):
         s = short(name)
         if s is None:
             continue
         frag, _, src = s
+        # Several instantiations of one kernel template get their own keys.
+        seen[frag] += 1
+        key = frag if seen[frag] == 1 else f"{frag}#{seen[frag]}"
         f_kib, w_kib = fetch.get(name, 0.0), write.get(name, 0.0)
         rb, wb = f_kib * 1024 * ff, w_kib * 1024 * wf
-        rec["kernels"][frag] = {"source": src, "source_sha256": source_sha(src),
-                                "fetch_kib": f_kib, "write_kib": w_kib,
-                                "read_bytes": rb, "written_bytes": wb}
-        md.append(f"| `{frag}` | {f_kib:.1f} | {w_kib:.1f} | {rb / 2**20:.2f} | {wb / 2**20:.2f} |")
+        rec["kernels"][key] = {"source": src, "source_sha256": source_sha(src), "name": name[:120],
+                               "fetch_kib": f_kib, "write_kib": w_kib,
+                               "read_bytes": rb, "written_bytes": wb}
+        md.append(f"| `{key}` | {f_kib:.1f} | {w_kib:.1f} | {rb / 2**20:.2f} | {wb / 2**20:.2f} |")
     open(a.out + "_hbm_traffic.md", "w").write("\n".join(md) + "\n")
     with open(a.out + "_hbm_traffic.json", "w") as f:
         json.dump(rec, f, indent=1)
