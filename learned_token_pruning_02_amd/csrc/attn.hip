@@ -121,11 +121,19 @@ __device__ __forceinline__ int tiles_at_or_above(const AttnArgs& a, int t) {
 }
 
 // Request b and query tile t of the u-th workgroup (per head group): tiles
-// with more keys first, so that the heaviest work starts earliest.
+// with more keys first, so that the heaviest work starts earliest.  With
+// PAIR (one request, four-wave workgroups, two per CU, the whole grid
+// resident at once) the first half of the ids takes the heavy half of the
+// tiles from the heaviest down and the second half the light ones from the
+// lightest up, so that the two workgroups sharing a CU (ids u and u + half)
+// hold tiles t and nt - 1 - t: equal work on every CU.
+template <bool PAIR>
 __device__ __forceinline__ bool locate_tile(const AttnArgs& a, int u, int& b, int& t) {
     if (a.batch == 1) {
         b = 0;
-        t = a.ntiles[0] - 1 - u;
+        const int nt = a.ntiles[0];
+        const int half = (nt + 1) / 2;
+        t = !PAIR || u < half ? nt - 1 - u : u - half;
         return true;
     }
     int lo = 0, hi = a.max_tiles - 1;
@@ -177,7 +185,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     // ---- which (request, query tile, head group) this workgroup owns ------
     const int hg = blockIdx.x % a.n_hg;
     int b, t;
-    if (!locate_tile(a, (int)(blockIdx.x / a.n_hg), b, t)) return;
+    if (!locate_tile<NWAVE == 4>(a, (int)(blockIdx.x / a.n_hg), b, t)) return;
     const int64_t rbase = a.cu[b];
     const int n = a.cu[b + 1] - a.cu[b];
     const int q0 = t * BQ;
