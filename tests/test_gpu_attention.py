@@ -61,6 +61,28 @@ def test_attention_parity(name, lens, Hq, Hkv, dh, dtype):
     assert_within(lse, ref_lse, rtol, atol, f"{name} lse")
 
 
+@pytest.mark.parametrize("lens,Hq,Hkv,dh,dtype", [
+    ([0, 100, 0, 700, 0], 16, 8, 128, torch.bfloat16),   # empty requests around ragged ones
+    ([0, 0, 65], 4, 2, 64, torch.bfloat16),
+    ([0, 33, 0], 4, 2, 64, torch.float32),
+    ([1] * 64, 16, 8, 128, torch.bfloat16),               # the largest batch of one-row requests
+])
+def test_attention_empty_and_tiny_requests(lens, Hq, Hkv, dh, dtype):
+    """Requests with no kept rows inside a batch take no work and leave the
+    other requests' rows exact; one-row requests attend only to themselves."""
+    announce(f"attn empty/tiny lens={lens[:6]} Hq={Hq} Hkv={Hkv} dh={dh} {dtype}")
+    q, k, v, s, gain, temp, cu = _inputs(lens, Hq, Hkv, dh, dtype, seed=41)
+    out, lse = _run(q, k, v, s, gain, temp, cu)
+    ref, ref_lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+    rtol, atol = tol(dtype)
+    assert_within(out, ref, rtol, atol, "empty/tiny out")
+    assert_within(lse, ref_lse, rtol, atol, "empty/tiny lse")
+    if all(n == 1 for n in lens):
+        # a lone key: the output is its value row, the lse its logit
+        vv = v.float().repeat_interleave(Hq // Hkv, dim=1)
+        assert_within(out.float(), vv, rtol, atol, "one-row requests")
+
+
 def test_attention_gain0_temp1_is_plain_causal():
     q, k, v, s, _, _, cu = _inputs([333, 77], 16, 8, 128, torch.bfloat16, seed=21)
     Hq = q.shape[1]
