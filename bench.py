@@ -538,7 +538,7 @@ def measure_config(w, args, dev, primary: bool):
     g = {k: (None if v is None else v.to(dev)) for k, v in gi.items()}
     a = {k: v.to(dev) for k, v in ai.items()}
     layer = GatedLayer(w.total_tokens, sh.d_model, sh.n_q_heads, sh.d_head, w.seq_len, w.q_len,
-                       w.budget, sh.dtype, device=dev)
+                       w.budget, sh.dtype, device=dev, n_kv_heads=sh.n_kv_heads)
     stack = None
     if w.stack_layers:
         stack = AttentionStack(layer.Kt, sh.d_model, sh.n_q_heads, sh.n_kv_heads, sh.d_head,

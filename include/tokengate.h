@@ -275,6 +275,45 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void *q, const void *k, const
                                 hipStream_t stream);
 
 /*
+ * tg_attn_prefill_plan -- workspace bytes of tg_gated_attn_prefill_ws for this
+ * packed batch (arguments as for tg_gated_attn_prefill).  Nonzero only for
+ * TG_BF16, a single request, two or more query heads per KV head, a request
+ * too short to give every CU two workgroups with whole query tiles (fewer
+ * than 512 four-wave workgroups), and a longest query tile of more than 8
+ * key tiles of 64; *ws_bytes = 0 otherwise.  Errors: TG_ERR_NULL_PTR,
+ * TG_ERR_BAD_DTYPE, TG_ERR_BAD_SHAPE, TG_ERR_UNSUPPORTED (d_head).
+ */
+tg_status tg_attn_prefill_plan(tg_dtype dt, const int32_t *cu_kept_host, int32_t batch,
+                               int32_t Hq, int32_t Hkv, int32_t d_head, size_t *ws_bytes);
+
+/*
+ * tg_gated_attn_prefill_ws -- tg_gated_attn_prefill with a caller workspace
+ * (the same attention: spke.com page, "Qu'est-ce que l'attention gérée par
+ * des tokens ?").  When tg_attn_prefill_plan gives nonzero bytes, each query
+ * tile is cut into pieces of at most 8 key tiles of near-equal length, one
+ * workgroup each, so that the short causal tiles of one request spread over
+ * the whole chip.  Each piece leaves its unnormalised output, exponent base
+ * and row sum in fp32 in ws; the last piece of a tile to finish combines the
+ * pieces in piece order (the result does not depend on which finishes last)
+ * and writes out and lse.  The result equals tg_gated_attn_prefill's within
+ * the rounding of the bf16 probabilities and the fp32 sums (the bf16 outputs
+ * may differ in the last bits).
+ * ws : at least tg_attn_prefill_plan bytes, caller-owned, 16-byte aligned;
+ *      may be NULL when that size is 0.  Its first 2048 bytes are per-tile
+ *      counters that must be zero before the first call: zero-fill the
+ *      workspace once when it is allocated.  Every call that completes leaves
+ *      them zero again, so the workspace serves any later call (of any shape)
+ *      without clearing.  Calls that share one workspace must not run
+ *      concurrently.
+ * Errors: those of tg_gated_attn_prefill, and TG_ERR_WORKSPACE.
+ */
+tg_status tg_gated_attn_prefill_ws(tg_dtype dt, const void *q, const void *k, const void *v,
+                                   const float *s_kept, const float *gain, const float *temp,
+                                   const int32_t *cu_kept_host, int32_t batch, int32_t Hq,
+                                   int32_t Hkv, int32_t d_head, void *out, float *lse, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
+/*
  * tg_attn_backward_plan -- workspace bytes of tg_gated_attn_backward for this
  * packed batch (cu_kept_host as for tg_gated_attn_prefill).  Errors:
  * TG_ERR_NULL_PTR, TG_ERR_BAD_SHAPE (batch, heads, cu_kept_host).

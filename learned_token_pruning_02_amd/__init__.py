@@ -33,6 +33,7 @@ __all__ = [
     "tg_topk_select_noalloc",
     "tg_gather_compact",
     "tg_gated_attn_prefill",
+    "tg_attn_prefill_plan",
     "tg_attn_backward_plan",
     "tg_gate_backward_plan",
     "tg_gate_backward",
@@ -127,6 +128,11 @@ def lib() -> ctypes.CDLL:
     L.tg_gated_attn_prefill.restype = ctypes.c_int
     L.tg_gated_attn_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, p_i32, i32, i32,
                                         i32, i32, vp, vp, vp]
+    L.tg_attn_prefill_plan.restype = ctypes.c_int
+    L.tg_attn_prefill_plan.argtypes = [ctypes.c_int, p_i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.tg_gated_attn_prefill_ws.restype = ctypes.c_int
+    L.tg_gated_attn_prefill_ws.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, p_i32, i32, i32,
+                                           i32, i32, vp, vp, vp, sz, vp]
     L.tg_attn_backward_plan.restype = ctypes.c_int
     L.tg_attn_backward_plan.argtypes = [p_i32, i32, i32, i32, ctypes.POINTER(sz)]
     L.tg_gated_attn_backward.restype = ctypes.c_int
@@ -373,12 +379,29 @@ def _attn_shapes(q, k, v, s_kept, gain, temp, cu_kept) -> None:
     _numel(temp, "temp", Hq)
 
 
+def tg_attn_prefill_plan(cu_kept: Sequence[int], Hq: int, Hkv: int, d_head: int,
+                         dtype=None) -> int:
+    """Workspace bytes of tg_gated_attn_prefill with a workspace (bf16 unless
+    dtype is torch.float32); 0 when the shape does not split its tiles."""
+    torch = _torch()
+    ws = ctypes.c_size_t(0)
+    cu = _i32_array(cu_kept)
+    dt = TG_F32 if dtype == torch.float32 else TG_BF16
+    _check("tg_attn_prefill_plan", lib().tg_attn_prefill_plan(
+        dt, ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)), len(cu_kept) - 1, Hq, Hkv, d_head,
+        ctypes.byref(ws)))
+    return ws.value
+
+
 def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], out=None,
-                          lse=None, want_lse: bool = False, stream=None):
+                          lse=None, want_lse: bool = False, stream=None, workspace=None):
     """Causal GQA token-gated attention over packed kept rows; returns (out, lse or None).
 
     s_kept=None and gain=None drop the bias term (plain causal attention with
-    the per-head temperature)."""
+    the per-head temperature).  With a workspace (tg_attn_prefill_plan bytes,
+    zero-filled before its first use) the call is tg_gated_attn_prefill_ws,
+    which cuts the query tiles of a short single request into pieces of at
+    most 8 key tiles, one workgroup each."""
     torch = _torch()
     _ndim(q, "q", 3)
     _ndim(k, "k", 3)
@@ -392,12 +415,16 @@ def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], o
     if want_lse and lse is None:
         lse = torch.empty(Hq, Kt, dtype=torch.float32, device=q.device)
     cu = _i32_array(cu_kept)
-    _check("tg_gated_attn_prefill", lib().tg_gated_attn_prefill(
-        _dt(q), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
-        _dev(s_kept, "s_kept", torch.float32), _dev(gain, "gain", torch.float32),
-        _dev(temp, "temp", torch.float32), ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
-        len(cu_kept) - 1, Hq, Hkv, dh, _dev(out, "out", q.dtype),
-        _dev(lse, "lse", torch.float32), _stream(stream)))
+    args = (_dt(q), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
+            _dev(s_kept, "s_kept", torch.float32), _dev(gain, "gain", torch.float32),
+            _dev(temp, "temp", torch.float32), ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
+            len(cu_kept) - 1, Hq, Hkv, dh, _dev(out, "out", q.dtype),
+            _dev(lse, "lse", torch.float32))
+    if workspace is None:
+        _check("tg_gated_attn_prefill", lib().tg_gated_attn_prefill(*args, _stream(stream)))
+    else:
+        _check("tg_gated_attn_prefill_ws", lib().tg_gated_attn_prefill_ws(
+            *args, _dev(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
     return out, lse
 
 

@@ -34,6 +34,12 @@
 // consumed.  Heavy query tiles (many keys) are
 // dispatched first and consecutive workgroup ids cycle over the KV heads, so
 // the 8 XCDs each keep one head's K/V in their own L2.
+// A single request too short to fill the chip (four-wave workgroups, fewer
+// than two per CU) can, given a workspace, cut each query tile into pieces of
+// at most 24 key tiles, one workgroup each: every piece leaves its
+// unnormalised output, exponent base and row sum in fp32, takes a ticket, and
+// the last piece of the tile combines all of them in piece order, so the
+// result does not depend on which piece finished last.
 #include "tg_device.h"
 #include "tg_kernels.h"
 
@@ -108,10 +114,66 @@ struct AttnArgs {
     int32_t Hq, Hkv, n_hg, batch, max_tiles;
     int32_t cu[TG_MAX_BATCH + 1];
     int32_t ntiles[TG_MAX_BATCH];
+    // Key split (one request, four-wave workgroups): query tile t is cut into
+    // ceil(nkv / split_len) pieces of near-equal key ranges, one workgroup
+    // each; every piece leaves its partial result in part, and the last piece
+    // of a tile to finish (ticket in cnt) combines them.
+    int32_t split_len;
+    uint32_t* cnt;  // [n_hg][ntiles[0]] tickets (< SPLIT_MAX_TILES), zero between calls
+    float* part;    // [gridDim.x][SPLIT_SLOT_FLOATS<DH>()] partial results
 };
 
 constexpr int KVT = 64;          // keys per tile
 constexpr int VT_STRIDE = KVT + 8;  // LDS row stride of V^T (bf16 elements)
+
+// The key split serves grids of fewer than SPLIT_MAX_TILES (query tile, head
+// group) pairs; their tickets fill a counter region of fixed size at the start
+// of the workspace, so that the partial results of any shape start after it
+// and a workspace zeroed once keeps every ticket at zero between calls of any
+// shapes.
+constexpr int SPLIT_MAX_TILES = 512;
+constexpr size_t SPLIT_CNT_BYTES = SPLIT_MAX_TILES * 4;
+
+// Partial result of one piece of a split query tile, per four-wave workgroup:
+// the unnormalised output registers (two per 8-byte word, lane-minor, so each
+// wave's store of one register pair is 512 contiguous bytes), then each
+// lane's (exponent base, row-sum half).
+template <int DH>
+constexpr int split_slot_floats() { return 4 * 64 * (DH / 32 * 16 + 2); }
+
+// Key tiles of query tile t (BQ rows per head) of a request of n rows.
+__device__ __forceinline__ int tile_keys(int t, int bq, int n) {
+    return (min(bq * (t + 1), n) + KVT - 1) / KVT;
+}
+
+// Query tile t, piece p of np of the u-th workgroup (per head group) of a
+// key-split launch: tiles from the last (most keys) down, each taking
+// ceil(nkv / split_len) consecutive ids.
+__device__ __forceinline__ void split_locate(const AttnArgs& a, int u, int bq, int& t, int& p,
+                                             int& np) {
+    const int n = a.cu[1] - a.cu[0];
+    t = a.ntiles[0] - 1;
+    for (;;) {
+        np = (tile_keys(t, bq, n) + a.split_len - 1) / a.split_len;
+        if (u < np || t == 0) break;
+        u -= np;
+        --t;
+    }
+    p = u;
+}
+
+// Device-coherent 8-byte store and load: the partial results one workgroup
+// leaves for another inside a launch bypass the per-XCD caches, so no cache
+// needs writing back or invalidating.
+__device__ __forceinline__ void coherent_st64(uint64_t* p, float lo, float hi) {
+    const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+                       ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 coherent_ld64(const uint64_t* p) {
+    const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__builtin_bit_cast(float, (uint32_t)v), __builtin_bit_cast(float, (uint32_t)(v >> 32)));
+}
 
 // Number of query tiles whose local index is >= t.
 __device__ __forceinline__ int tiles_at_or_above(const AttnArgs& a, int t) {
@@ -153,7 +215,7 @@ __device__ __forceinline__ bool locate_tile(const AttnArgs& a, int u, int& b, in
     return b < a.batch;  // false only for an inconsistent tile count
 }
 
-template <int DH, int HPB, int NWAVE, bool BIAS>
+template <int DH, int HPB, int NWAVE, bool BIAS, bool SPLIT>
 __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnArgs a) {
     // NWAVE = 8: two waves per SIMD from one workgroup; 4: two workgroups per CU.
     constexpr int WPH = NWAVE / HPB;   // waves per head
@@ -170,6 +232,9 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     // the interleave to scheduling groups, which measures faster there.
     constexpr bool FUSED = NWAVE == 4;
     constexpr int NKB = 2;  // K buffers
+    // A split piece needs every wave's rows inside the tile's last key tile
+    // (at most 64 query rows per head), so that only the last piece masks.
+    static_assert(!SPLIT || (NWAVE == 4 && BQ <= KVT), "key split: four waves, <= 64 rows per head");
 
     __shared__ __attribute__((aligned(16))) bf16 Ks[NKB][KVT * KS];
     __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * VT_STRIDE];
@@ -184,13 +249,17 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 
     // ---- which (request, query tile, head group) this workgroup owns ------
     const int hg = blockIdx.x % a.n_hg;
-    int b, t;
-    if (!locate_tile<NWAVE == 4>(a, (int)(blockIdx.x / a.n_hg), b, t)) return;
+    int b = 0, t, piece = 0, npiece = 1;
+    if (SPLIT) split_locate(a, (int)(blockIdx.x / a.n_hg), BQ, t, piece, npiece);
+    else if (!locate_tile<NWAVE == 4>(a, (int)(blockIdx.x / a.n_hg), b, t)) return;
     const int64_t rbase = a.cu[b];
     const int n = a.cu[b + 1] - a.cu[b];
     const int q0 = t * BQ;
     const int kend = min(q0 + BQ, n);
     const int nkv = (kend + KVT - 1) / KVT;
+    // Key tiles [jbeg, jend) of this workgroup: all of them, or one piece.
+    const int jbeg = SPLIT ? piece * nkv / npiece : 0;
+    const int jend = SPLIT ? (piece + 1) * nkv / npiece : nkv;
     const int group = a.Hq / a.Hkv;
     const int kvh = (hg * HPB) / group;
     const int hp = w / WPH;  // head of this wave within the workgroup
@@ -568,11 +637,11 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 
     // One step of the workgroup: stage K(jt+1) and V(jt) around BODY.
     // Every wave takes nkv + 1 steps, each ending in one barrier.
-    int jt = 0;
+    int jt = jbeg;
 #define TG_STEP(BODY)                                     \
     do {                                                  \
-        const bool knext = jt + 1 < nkv;                  \
-        const bool vnow = jt < nkv;                       \
+        const bool knext = jt + 1 < jend;                 \
+        const bool vnow = jt < jend;                      \
         BODY;                                             \
         if (knext) store_k((jt + 1) % NKB);               \
         if (vnow) store_v(jt & 1);                        \
@@ -590,25 +659,31 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     // same nkv + 1 steps (barriers) as the other waves instead of computing
     // on a key tile that was never staged.
     const int jt_diag = min(qmin / KVT, nkv - 1);
+    // The last key tile this wave computes, and whether it is the diagonal
+    // one (always, unless this is a piece before the last of a split tile).
+    const int jlast = SPLIT ? jend - 1 : jt_diag;
+    const bool mlast = !SPLIT || jend == nkv;
     // Waves 4-7 share each SIMD with one of waves 0-3, which the hardware
     // favours when both can issue; raising their priority evens out the
     // two waves' step times, so neither idles long at the barrier.
     if (NWAVE == 8 && w >= 4) __builtin_amdgcn_s_setprio(2);
-    load_part(0, true, 0, false, 0);
-    load_part(1, true, 0, false, 0);
-    load_part(2, true, 0, false, 0);
-    load_part(3, true, 0, false, 0);
-    store_k(0);
+    load_part(0, true, jbeg, false, 0);
+    load_part(1, true, jbeg, false, 0);
+    load_part(2, true, jbeg, false, 0);
+    load_part(3, true, jbeg, false, 0);
+    store_k(jbeg % NKB);
     __syncthreads();
-    if (jt_diag == 0) {
-        TG_STEP({ TG_QK(jt, TG_LD); TG_SOFTMAX_FIRST(true); });
+    if (jlast == jbeg) {
+        if (mlast) TG_STEP({ TG_QK(jt, TG_LD); TG_SOFTMAX_FIRST(true); });
+        else TG_STEP({ TG_QK(jt, TG_LD); TG_SOFTMAX_FIRST(false); });
     } else {
         TG_STEP({ TG_QK(jt, TG_LD); TG_SOFTMAX_FIRST(false); });
         if (FUSED) {
-            while (jt < jt_diag) TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM_FUSED(false); });
-            TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM_FUSED(true); });
+            while (jt < jlast) TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM_FUSED(false); });
+            if (mlast) TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM_FUSED(true); });
+            else TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM_FUSED(false); });
         } else {
-            while (jt < jt_diag) TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM(false); });
+            while (jt < jlast) TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM(false); });
             TG_STEP({ TG_RESCALE(); TG_QK(jt, TG_LD); TG_PVSM(true); });
         }
     }
@@ -619,7 +694,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         const int vb = (jt - 1) & 1;
         _Pragma("unroll") for (int i = 0; i < NPV; ++i) o[i % NMD] = mfma32(TG_VFRAG(i), pold[i / NMD], o[i % NMD]);
     });
-    while (jt <= nkv) TG_STEP(TG_LD_ALL());
+    while (jt <= jend) TG_STEP(TG_LD_ALL());
 #undef TG_LD_ALL
 #undef TG_LD
 #undef TG_STEP
@@ -634,6 +709,75 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
 #undef TG_VFRAG
 #undef TG_QK
 #undef TG_KFRAG
+
+    // ---- pieces of a split tile: the last one to finish combines them -------
+    if (SPLIT && npiece > 1) {
+        constexpr int NPAIR = NMD * 8;  // 8-byte words of output registers per lane
+        constexpr int SLOT = split_slot_floats<DH>();
+        uint64_t* const mine = reinterpret_cast<uint64_t*>(a.part + (int64_t)blockIdx.x * SLOT);
+#pragma unroll
+        for (int i = 0; i < NPAIR; ++i)
+            coherent_st64(mine + (w * NPAIR + i) * WAVE + lane, o[i / 8][2 * (i % 8)], o[i / 8][2 * (i % 8) + 1]);
+        coherent_st64(mine + 4 * NPAIR * WAVE + w * WAVE + lane, pf, lpart);
+        __shared__ int s_last;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are performed
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t* const c = a.cnt + hg * a.ntiles[0] + t;
+            const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = old == (uint32_t)(npiece - 1);
+            // Every piece has taken its ticket: reset it for the next call.
+            if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        // Combine the pieces in piece order (whichever finished last), each
+        // rescaled from its own base to the largest: the result does not
+        // depend on the order in which the pieces ran.
+        const uint64_t* const first =
+            reinterpret_cast<const uint64_t*>(a.part + (int64_t)(blockIdx.x - piece * a.n_hg) * SLOT);
+        const int64_t stride = (int64_t)a.n_hg * SLOT / 2;  // 8-byte words between pieces
+        const int mlw = 4 * NPAIR * WAVE + w * WAVE + lane;  // this lane's (base, sum) word
+        // Largest base over the pieces, eight loads in flight at a time.
+        float mx = -INFINITY;
+        for (int i0 = 0; i0 < npiece; i0 += 8) {
+            float2 ml[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ml[i] = i0 + i < npiece ? coherent_ld64(first + (i0 + i) * stride + mlw) : make_float2(-INFINITY, 0.f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mx = fmaxf(mx, ml[i].x);
+        }
+        // Each piece's output registers are loaded while the previous
+        // piece's are accumulated.
+        auto load_piece = [&](int i, float2* v) {
+            const uint64_t* const src = first + (int64_t)i * stride;
+#pragma unroll
+            for (int j = 0; j < NPAIR; ++j) v[j] = coherent_ld64(src + (w * NPAIR + j) * WAVE + lane);
+            v[NPAIR] = coherent_ld64(src + mlw);
+        };
+        float2 cur[NPAIR + 1], nxt[NPAIR + 1] = {};
+        load_piece(0, cur);
+#pragma unroll
+        for (int md = 0; md < NMD; ++md)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[md][r] = 0.f;
+        lpart = 0.f;
+        for (int i = 0; i < npiece; ++i) {
+            if (i + 1 < npiece) load_piece(i + 1, nxt);
+            const float f = __builtin_amdgcn_exp2f(cur[NPAIR].x - mx);
+            lpart = fmaf(cur[NPAIR].y, f, lpart);
+#pragma unroll
+            for (int j = 0; j < NPAIR; ++j) {
+                o[j / 8][2 * (j % 8)] = fmaf(cur[j].x, f, o[j / 8][2 * (j % 8)]);
+                o[j / 8][2 * (j % 8) + 1] = fmaf(cur[j].y, f, o[j / 8][2 * (j % 8) + 1]);
+            }
+#pragma unroll
+            for (int j = 0; j <= NPAIR; ++j) cur[j] = nxt[j];
+        }
+        pf = mx;
+    }
 
     // ---- normalise and store ------------------------------------------------
     const float l = lpart + __shfl_xor(lpart, 32, WAVE);
@@ -654,20 +798,42 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     }
 }
 
-template <int DH, int HPB, int NWAVE>
-hipError_t launch_bf16(const AttnArgs& a, int total_tiles, hipStream_t st) {
-    const int blocks = total_tiles * a.n_hg;
+template <int DH, int HPB, int NWAVE, bool SPLIT>
+hipError_t launch_bf16(const AttnArgs& a, int blocks, hipStream_t st) {
     if (a.s != nullptr)
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB, NWAVE, true>), dim3(blocks), dim3(64 * NWAVE), 0, st, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB, NWAVE, true, SPLIT>), dim3(blocks), dim3(64 * NWAVE), 0, st, a);
     else
-        hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB, NWAVE, false>), dim3(blocks), dim3(64 * NWAVE), 0, st, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<DH, HPB, NWAVE, false, SPLIT>), dim3(blocks), dim3(64 * NWAVE), 0, st, a);
     return hipGetLastError();
 }
 
-template <int DH, int HPB>
-hipError_t launch_bf16_w(AttnArgs& a, const AttnShape& sh, hipStream_t st) {
-    // Eight-wave workgroups (K/V staged once for 256 query rows) unless that
-    // leaves fewer than two workgroups per CU; then four-wave workgroups.
+// Key tiles per piece of a split query tile.  The 16k layer's 2048 kept rows
+// (32 query tiles of 1..32 key tiles, 8 head groups) then run as 320
+// workgroups of at most 16 steps instead of 256 whose longest walks 32 key
+// tiles.  Shorter pieces balance better but each costs a partial result
+// written, a ticket and a share of a merge (a few microseconds of memory
+// round trips); measured at 1000, 2048 and 3000 rows, 24 was fastest.
+#ifndef TG_ATTN_SPLIT_LEN
+#define TG_ATTN_SPLIT_LEN 24
+#endif
+constexpr int SPLIT_LEN = TG_ATTN_SPLIT_LEN;
+
+// How a packed batch is launched: eight-wave workgroups (K/V staged once for
+// 256 query rows) unless that leaves fewer than two workgroups per CU; then
+// four-wave workgroups, two per CU.  A single request whose four-wave grid
+// still holds at most one workgroup per CU has its query tiles split over
+// several workgroups (the key split), when it has a workspace and at least
+// two query heads share a KV head.
+struct AttnPlan {
+    int nwave;         // 8 or 4
+    int blocks;        // workgroups without the key split
+    int tiles;         // query tiles over all requests
+    bool split;
+    int split_blocks;  // workgroups with it
+    size_t ws_bytes;   // workspace of the key split (0 without it)
+};
+
+AttnPlan plan_bf16(AttnArgs& a, const AttnShape& sh, int hpb) {
     auto tiles = [&](int bq) {
         int total = 0, mx = 0;
         for (int b = 0; b < sh.batch; ++b) {
@@ -679,11 +845,49 @@ hipError_t launch_bf16_w(AttnArgs& a, const AttnShape& sh, hipStream_t st) {
         a.max_tiles = mx;
         return total;
     };
-    const int t8 = tiles(256 / HPB);
-    if (t8 * a.n_hg >= 512) return launch_bf16<DH, HPB, 8>(a, t8, st);
-    const int t4 = tiles(128 / HPB);
-    if (t4 == 0) return hipSuccess;
-    return launch_bf16<DH, HPB, 4>(a, t4, st);
+    AttnPlan pl{};
+    const int t8 = tiles(256 / hpb);
+    if (t8 * a.n_hg >= 512) {
+        pl = {8, t8 * a.n_hg, t8, false, 0, 0};
+        return pl;
+    }
+    const int bq = 128 / hpb;
+    const int t4 = tiles(bq);
+    pl = {4, t4 * a.n_hg, t4, false, 0, 0};
+    if (sh.batch != 1 || hpb < 2 || t4 * a.n_hg >= SPLIT_MAX_TILES) return pl;
+    const int n = sh.cu[1] - sh.cu[0];
+    int pieces = 0;
+    for (int t = 0; t < t4; ++t) {
+        const int nkv = ((bq * (t + 1) < n ? bq * (t + 1) : n) + KVT - 1) / KVT;
+        pieces += (nkv + SPLIT_LEN - 1) / SPLIT_LEN;
+    }
+    if (pieces == t4) return pl;  // no tile is long enough to split
+    const size_t slot = (size_t)(sh.d_head == 64 ? split_slot_floats<64>() : split_slot_floats<128>()) * 4;
+    pl.split = true;
+    pl.split_blocks = pieces * a.n_hg;
+    pl.ws_bytes = SPLIT_CNT_BYTES + (size_t)pl.split_blocks * slot;
+    return pl;
+}
+
+template <int DH, int HPB>
+hipError_t launch_bf16_w(AttnArgs& a, const AttnShape& sh, void* ws, hipStream_t st) {
+    const AttnPlan pl = plan_bf16(a, sh, HPB);
+    if (pl.tiles == 0) return hipSuccess;
+    if (pl.nwave == 8) return launch_bf16<DH, HPB, 8, false>(a, pl.blocks, st);
+    if constexpr (HPB >= 2) {
+        if (pl.split && ws != nullptr) {
+            a.split_len = SPLIT_LEN;
+            a.cnt = (uint32_t*)ws;
+            a.part = (float*)((char*)ws + SPLIT_CNT_BYTES);
+            return launch_bf16<DH, HPB, 4, true>(a, pl.split_blocks, st);
+        }
+    }
+    return launch_bf16<DH, HPB, 4, false>(a, pl.blocks, st);
+}
+
+int heads_per_block(const AttnShape& sh) {
+    const int group = sh.Hq / sh.Hkv;
+    return group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
 }
 
 }  // namespace
@@ -702,12 +906,20 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const
     return hipGetLastError();
 }
 
+size_t attn_prefill_workspace_bytes(const AttnShape& sh) {
+    if (sh.Kt == 0) return 0;
+    AttnArgs a{};
+    const int hpb = heads_per_block(sh);
+    a.n_hg = sh.Hq / hpb;
+    return plan_bf16(a, sh, hpb).ws_bytes;
+}
+
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const float* s,
                             const float* gain, const float* temp, const AttnShape& sh, void* out,
-                            float* lse, hipStream_t st) {
-    const int group = sh.Hq / sh.Hkv;
-    const int hpb = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
-    AttnArgs a;
+                            float* lse, void* ws, size_t ws_bytes, hipStream_t st) {
+    (void)ws_bytes;  // checked against attn_prefill_workspace_bytes by the caller
+    const int hpb = heads_per_block(sh);
+    AttnArgs a{};
     a.q = (const bf16*)q;
     a.k = (const bf16*)k;
     a.v = (const bf16*)v;
@@ -724,13 +936,13 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const f
     for (int b = 0; b <= sh.batch; ++b) a.cu[b] = sh.cu[b];
     if (sh.Kt == 0) return hipSuccess;
     if (sh.d_head == 64) {
-        if (hpb == 4) return launch_bf16_w<64, 4>(a, sh, st);
-        if (hpb == 2) return launch_bf16_w<64, 2>(a, sh, st);
-        return launch_bf16_w<64, 1>(a, sh, st);
+        if (hpb == 4) return launch_bf16_w<64, 4>(a, sh, ws, st);
+        if (hpb == 2) return launch_bf16_w<64, 2>(a, sh, ws, st);
+        return launch_bf16_w<64, 1>(a, sh, ws, st);
     }
-    if (hpb == 4) return launch_bf16_w<128, 4>(a, sh, st);
-    if (hpb == 2) return launch_bf16_w<128, 2>(a, sh, st);
-    return launch_bf16_w<128, 1>(a, sh, st);
+    if (hpb == 4) return launch_bf16_w<128, 4>(a, sh, ws, st);
+    if (hpb == 2) return launch_bf16_w<128, 2>(a, sh, ws, st);
+    return launch_bf16_w<128, 1>(a, sh, ws, st);
 }
 
 }  // namespace tg

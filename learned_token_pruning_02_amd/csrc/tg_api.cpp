@@ -231,11 +231,12 @@ tg_status tg_gather_compact(tg_dtype dt, const void* hidden, int64_t T, int32_t 
                                       scores_kept, stream));
 }
 
-tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const void* v,
-                                const float* s_kept, const float* gain, const float* temp,
-                                const int32_t* cu_kept_host, int32_t batch, int32_t Hq,
-                                int32_t Hkv, int32_t d_head, void* out, float* lse,
-                                hipStream_t stream) {
+namespace {
+tg_status attn_prefill_checked(tg_dtype dt, const void* q, const void* k, const void* v,
+                               const float* s_kept, const float* gain, const float* temp,
+                               const int32_t* cu_kept_host, int32_t batch, int32_t Hq,
+                               int32_t Hkv, int32_t d_head, void* out, float* lse, void* ws,
+                               size_t ws_bytes, bool with_ws, hipStream_t stream) {
     if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
     if (q == nullptr || k == nullptr || v == nullptr || temp == nullptr || cu_kept_host == nullptr ||
         out == nullptr || (s_kept == nullptr) != (gain == nullptr))
@@ -260,22 +261,53 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const
             if ((int64_t)(cu_kept_host[i + 1] - cu_kept_host[i]) * Hkv * d_head * 2 >= I32_LIMIT)
                 return TG_ERR_UNSUPPORTED;
     }
+    const size_t need = with_ws && dt == TG_BF16 ? tg::attn_prefill_workspace_bytes(sh) : 0;
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return TG_ERR_WORKSPACE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         (s_kept != nullptr && (!aligned4(s_kept) || !aligned4(gain))) || !aligned4(temp) ||
-        (lse != nullptr && !aligned4(lse)))
+        (lse != nullptr && !aligned4(lse)) || (need > 0 && !aligned16(ws)))
         return TG_ERR_ALIGNMENT;
     const int64_t eb = elt_bytes(dt);
     const int64_t qb = sh.Kt * Hq * d_head * eb, kb = sh.Kt * Hkv * d_head * eb;
+    const int64_t lb = (int64_t)Hq * sh.Kt * 4, wb = (int64_t)need;
     if (overlap(out, qb, q, qb) || overlap(out, qb, k, kb) || overlap(out, qb, v, kb) ||
-        overlap(out, qb, s_kept, sh.Kt * 4) || overlap(lse, (int64_t)Hq * sh.Kt * 4, out, qb) ||
-        overlap(lse, (int64_t)Hq * sh.Kt * 4, q, qb) || overlap(lse, (int64_t)Hq * sh.Kt * 4, k, kb) ||
-        overlap(lse, (int64_t)Hq * sh.Kt * 4, v, kb))
+        overlap(out, qb, s_kept, sh.Kt * 4) || overlap(lse, lb, out, qb) ||
+        overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb))
         return TG_ERR_ALIAS;
+    if (need > 0) {
+        const void* ins[] = {q, k, v, out};
+        const int64_t sz[] = {qb, kb, kb, qb};
+        for (int i = 0; i < 4; ++i)
+            if (overlap(ws, wb, ins[i], sz[i])) return TG_ERR_ALIAS;
+        if (overlap(ws, wb, s_kept, sh.Kt * 4) || overlap(ws, wb, lse, lb) ||
+            overlap(ws, wb, gain, Hq * 4) || overlap(ws, wb, temp, Hq * 4))
+            return TG_ERR_ALIAS;
+    }
     if (sh.Kt == 0) return TG_OK;
     if (dt == TG_F32)
         return launched(tg::launch_attn_f32((const float*)q, (const float*)k, (const float*)v,
                                             s_kept, gain, temp, sh, (float*)out, lse, stream));
-    return launched(tg::launch_attn_bf16(q, k, v, s_kept, gain, temp, sh, out, lse, stream));
+    return launched(tg::launch_attn_bf16(q, k, v, s_kept, gain, temp, sh, out, lse,
+                                         need > 0 ? ws : nullptr, need, stream));
+}
+}  // namespace
+
+tg_status tg_gated_attn_prefill(tg_dtype dt, const void* q, const void* k, const void* v,
+                                const float* s_kept, const float* gain, const float* temp,
+                                const int32_t* cu_kept_host, int32_t batch, int32_t Hq,
+                                int32_t Hkv, int32_t d_head, void* out, float* lse,
+                                hipStream_t stream) {
+    return attn_prefill_checked(dt, q, k, v, s_kept, gain, temp, cu_kept_host, batch, Hq, Hkv,
+                                d_head, out, lse, nullptr, 0, false, stream);
+}
+
+tg_status tg_gated_attn_prefill_ws(tg_dtype dt, const void* q, const void* k, const void* v,
+                                   const float* s_kept, const float* gain, const float* temp,
+                                   const int32_t* cu_kept_host, int32_t batch, int32_t Hq,
+                                   int32_t Hkv, int32_t d_head, void* out, float* lse, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+    return attn_prefill_checked(dt, q, k, v, s_kept, gain, temp, cu_kept_host, batch, Hq, Hkv,
+                                d_head, out, lse, ws, ws_bytes, true, stream);
 }
 
 namespace {
@@ -297,6 +329,18 @@ tg_status attn_shape(const int32_t* cu_kept_host, int32_t batch, int32_t Hq, int
     return TG_OK;
 }
 }  // namespace
+
+tg_status tg_attn_prefill_plan(tg_dtype dt, const int32_t* cu_kept_host, int32_t batch,
+                               int32_t Hq, int32_t Hkv, int32_t d_head, size_t* ws_bytes) {
+    if (ws_bytes == nullptr) return TG_ERR_NULL_PTR;
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (d_head != 64 && d_head != 128) return TG_ERR_UNSUPPORTED;
+    tg::AttnShape sh;
+    const tg_status st = attn_shape(cu_kept_host, batch, Hq, Hkv, d_head, &sh);
+    if (st != TG_OK) return st;
+    *ws_bytes = dt == TG_BF16 ? tg::attn_prefill_workspace_bytes(sh) : 0;
+    return TG_OK;
+}
 
 tg_status tg_attn_backward_plan(const int32_t* cu_kept_host, int32_t batch, int32_t Hq, int32_t Hkv,
                                 size_t* ws_bytes) {

@@ -52,9 +52,13 @@ struct AttnShape {
 hipError_t launch_attn_f32(const float* q, const float* k, const float* v, const float* s,
                            const float* gain, const float* temp, const AttnShape& sh, float* out,
                            float* lse, hipStream_t st);
+// ws (attn_prefill_workspace_bytes, zeroed before its first use, or NULL)
+// lets a single request whose grid cannot fill the chip cut its query tiles
+// into pieces of at most 8 key tiles, one workgroup each.
+size_t attn_prefill_workspace_bytes(const AttnShape& sh);
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, const float* s,
                             const float* gain, const float* temp, const AttnShape& sh, void* out,
-                            float* lse, hipStream_t st);
+                            float* lse, void* ws, size_t ws_bytes, hipStream_t st);
 
 size_t attn_bwd_workspace_bytes(const AttnShape& sh);
 hipError_t launch_attn_bwd(const AttnShape& sh, const void* q, const void* k, const void* v,

@@ -13,8 +13,26 @@ from typing import Dict, List, Optional, Sequence
 
 import torch
 
-from . import (tg_gate_score, tg_gated_attn_prefill, tg_gather_compact, tg_kept_positions,
-               tg_linear, tg_plan, tg_qk_norm_rope, tg_rmsnorm, tg_silu_mul, tg_topk_select)
+from . import (tg_attn_prefill_plan, tg_gate_score, tg_gated_attn_prefill, tg_gather_compact,
+               tg_kept_positions, tg_linear, tg_plan, tg_qk_norm_rope, tg_rmsnorm, tg_silu_mul,
+               tg_topk_select)
+
+
+class _AttnWorkspace:
+    """The attention's optional workspace per kept-row layout, allocated (and
+    zero-filled, as its counters require) on the first call with that layout,
+    so that later calls, and HIP graphs captured after it, allocate nothing."""
+
+    def __init__(self, Hq: int, Hkv: int, d_head: int, dtype: torch.dtype, device):
+        self.Hq, self.Hkv, self.dh, self.dtype, self.device = Hq, Hkv, d_head, dtype, device
+        self.bufs: Dict[tuple, Optional[torch.Tensor]] = {}
+
+    def get(self, cu_kept: Sequence[int]) -> Optional[torch.Tensor]:
+        key = tuple(cu_kept)
+        if key not in self.bufs:
+            n = tg_attn_prefill_plan(list(cu_kept), self.Hq, self.Hkv, self.dh, self.dtype)
+            self.bufs[key] = torch.zeros(n, dtype=torch.uint8, device=self.device) if n else None
+        return self.bufs[key]
 
 
 class GatedLayer:
@@ -22,7 +40,7 @@ class GatedLayer:
 
     def __init__(self, T: int, d_model: int, n_q_heads: int, d_head: int, seq_len: Sequence[int],
                  q_len: Sequence[int], budget: Sequence[int], dtype: torch.dtype,
-                 device="cuda", want_lse: bool = False):
+                 device="cuda", want_lse: bool = False, n_kv_heads: Optional[int] = None):
         self.seq_len, self.q_len, self.budget = list(seq_len), list(q_len), list(budget)
         self.cu_seq, self.cu_kept, ws = tg_plan(self.seq_len, self.q_len, self.budget)
         if self.cu_seq[-1] != T:
@@ -37,6 +55,13 @@ class GatedLayer:
         self.s_kept = torch.empty(Kt, dtype=torch.float32, device=device)
         self.out = torch.empty(Kt, n_q_heads, d_head, dtype=dtype, device=device)
         self.lse = torch.empty(n_q_heads, Kt, dtype=torch.float32, device=device) if want_lse else None
+        # With the KV head count known, the attention gets its workspace,
+        # zero-filled once (a short single request then splits its query
+        # tiles over more workgroups).
+        self.attn_ws = None
+        if n_kv_heads is not None and Kt > 0:
+            n = tg_attn_prefill_plan(self.cu_kept, n_q_heads, n_kv_heads, d_head, dtype)
+            self.attn_ws = torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
     def gate(self, hidden, w1, b1, w2, b2):
         return tg_gate_score(hidden, w1, b1, w2, b2, scores=self.scores)
@@ -52,7 +77,7 @@ class GatedLayer:
 
     def attend(self, q, k, v, gain, temp):
         return tg_gated_attn_prefill(q, k, v, self.s_kept, gain, temp, self.cu_kept, out=self.out,
-                                     lse=self.lse)[0]
+                                     lse=self.lse, workspace=self.attn_ws)[0]
 
     def __call__(self, hidden, w1, b1, w2, b2, q, k, v, gain, temp):
         """gate -> select -> gather -> gated attention; returns the attention output."""
@@ -73,6 +98,7 @@ class AttentionStack:
         self.k = torch.empty(Kt, n_kv_heads * d_head, dtype=dtype, device=device)
         self.v = torch.empty(Kt, n_kv_heads * d_head, dtype=dtype, device=device)
         self.attn = torch.empty(Kt, n_q_heads, d_head, dtype=dtype, device=device)
+        self.attn_ws = _AttnWorkspace(n_q_heads, n_kv_heads, d_head, dtype, device)
 
     def __call__(self, x, s_kept, cu_kept: Sequence[int], layers: List[Dict[str, torch.Tensor]]):
         Kt = x.shape[0]
@@ -82,7 +108,7 @@ class AttentionStack:
             tg_linear(x, L["wv"], y=self.v)
             tg_gated_attn_prefill(self.q.view(Kt, self.Hq, self.dh), self.k.view(Kt, self.Hkv, self.dh),
                                   self.v.view(Kt, self.Hkv, self.dh), s_kept, L["gain"], L["temp"],
-                                  cu_kept, out=self.attn)
+                                  cu_kept, out=self.attn, workspace=self.attn_ws.get(cu_kept))
             tg_linear(self.attn.view(Kt, self.Hq * self.dh), L["wo"], y=x, accumulate=True)
         return x
 
@@ -116,6 +142,7 @@ class DecoderLayer:
         self.gu = torch.empty(Kt, 2 * d_ffn, **e)
         self.m = torch.empty(Kt, d_ffn, **e)
         self.pos = torch.empty(Kt, dtype=torch.int32, device=device)
+        self.attn_ws = _AttnWorkspace(n_q_heads, n_kv_heads, d_head, dtype, device)
 
     def positions(self, kept_idx, cu_seqlens: Sequence[int], cu_kept: Sequence[int]):
         return tg_kept_positions(kept_idx, cu_seqlens, cu_kept, pos=self.pos)
@@ -129,7 +156,7 @@ class DecoderLayer:
         tg_linear(self.xn, L["wv"], y=self.v.view(Kt, -1))
         tg_qk_norm_rope(self.q, self.k, L["q_norm"], L["k_norm"], self.pos, self.theta, self.eps)
         tg_gated_attn_prefill(self.q, self.k, self.v, s_kept, L["gain"], L["temp"], cu_kept,
-                              out=self.attn)
+                              out=self.attn, workspace=self.attn_ws.get(cu_kept))
         tg_linear(self.attn.view(Kt, -1), L["wo"], y=x, accumulate=True)
         tg_rmsnorm(x, L["post_norm"], self.eps, y=self.xn)
         tg_linear(self.xn, L["wgu"], y=self.gu)

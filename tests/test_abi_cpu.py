@@ -217,6 +217,66 @@ def test_attention_validation():
     assert call(cu=ctypes.cast(big, ctypes.POINTER(ctypes.c_int32))) == 5
 
 
+# Key split plan: a fixed 2 KiB region of per-tile counters (the split serves
+# fewer than 512 query tiles x head groups), then one slot per workgroup: 4
+# waves x 64 lanes x (d_head / 2 + 2) floats.  Query tiles are cut into
+# ceil(nkv / 24) pieces.  16k layer: 32 query tiles of 1..32 key tiles, sum of
+# ceil((t + 1) / 24) = 40 pieces per head group, 8 head groups.
+SLOT128 = 4 * 64 * (128 // 2 + 2) * 4
+SLOT64 = 4 * 64 * (64 // 2 + 2) * 4
+
+
+@pytest.mark.parametrize("cu,Hq,Hkv,dh,dt,expect", [
+    ([0, 2048], 16, 8, 128, 1, 2048 + 320 * SLOT128),     # 16k layer's kept rows: split
+    ([0, 4096], 16, 8, 128, 1, 0),                         # 32k: two whole tiles per CU already
+    ([0, 1600], 8, 2, 64, 1, 2048 + 104 * SLOT64),         # four heads per workgroup, 32-row tiles
+    ([0, 1537], 16, 8, 128, 1, 2048 + 208 * SLOT128),      # 25 key tiles: the shortest split
+    ([0, 1536], 16, 8, 128, 1, 0),                         # 24 key tiles: no split
+    ([0, 13000], 2, 1, 64, 1, 2048 + 972 * SLOT64),        # one head group, up to 9 pieces
+    ([0, 8192], 16, 8, 128, 1, 0),                         # eight-wave grid fills the chip
+    ([0, 1000, 2048], 16, 8, 128, 1, 0),                   # two requests
+    ([0, 2048], 16, 16, 128, 1, 0),                        # one head per workgroup
+    ([0, 2048], 16, 8, 128, 0, 0),                         # fp32 path
+])
+def test_attn_prefill_plan(cu, Hq, Hkv, dh, dt, expect):
+    """The key split is host logic: which shapes get a workspace, and its size."""
+    L = tg.lib()
+    ws = ctypes.c_size_t(123)
+    arr = tg._i32_array(cu)
+    assert L.tg_attn_prefill_plan(dt, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)), len(cu) - 1,
+                                  Hq, Hkv, dh, ctypes.byref(ws)) == 0
+    assert ws.value == expect
+
+
+def test_attn_prefill_ws_validation():
+    L = tg.lib()
+    f = L.tg_gated_attn_prefill_ws
+    cu = tg._i32_array([0, 2048])
+    cu_p = ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32))
+    need = 2048 + 320 * SLOT128
+    W = 1 << 30
+    ok = [1, A, B, C, D, E, F, cu_p, 1, 16, 8, 128, 1 << 28, None, W, need, None]
+    names = ["dt", "q", "k", "v", "s", "gain", "temp", "cu", "batch", "Hq", "Hkv", "dh",
+             "out", "lse", "ws", "ws_bytes", "stream"]
+
+    def call(**kw):
+        args = list(ok)
+        for k, v in kw.items():
+            args[names.index(k)] = v
+        return f(*args)
+
+    assert call(ws=None) == 7                       # the shape splits: a workspace is required
+    assert call(ws_bytes=need - 1) == 7
+    assert call(ws=W + 8) == 6                      # 16-byte alignment
+    assert call(ws=A) == 9                          # workspace overlaps q
+    assert call(ws=(1 << 28) - 4096) == 9           # workspace overlaps out
+    assert call(dt=5) == 4
+    assert L.tg_attn_prefill_plan(1, cu_p, 1, 16, 8, 128, None) == 1
+    short = tg._i32_array([0, 100])                 # no split: no workspace needed
+    assert call(cu=ctypes.cast(short, ctypes.POINTER(ctypes.c_int32)), ws=None, ws_bytes=0,
+                q=None) == 1                        # (then the usual checks apply)
+
+
 def test_decode_plan():
     L = tg.lib()
     ws = ctypes.c_size_t(0)

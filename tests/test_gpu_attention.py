@@ -201,6 +201,79 @@ def _sampled_rows(cu, per_req, seed):
     return sorted(set(rows))
 
 
+SPLIT_CASES = [
+    # (name, lens, Hq, Hkv, d_head, score kind): one request short enough that
+    # its query tiles are cut into pieces of at most 24 key tiles (the plan
+    # gives a workspace), checked against the oracle and against the unsplit
+    # call.
+    ("16k_kept", [2048], 16, 8, 128, "random"),
+    ("16k_kept_step_up", [2048], 16, 8, 128, "step_up"),
+    ("ragged_tail", [1800], 16, 8, 128, "random"),
+    ("group4_dh64", [1600], 8, 2, 64, "climb"),
+    ("shortest_split", [1537], 16, 8, 128, "low_first_tile"),
+    ("three_pieces", [4000], 16, 8, 128, "random"),
+    ("nine_pieces_one_group", [13000], 2, 1, 64, "descent"),
+]
+
+
+@pytest.mark.parametrize("name,lens,Hq,Hkv,dh,kind", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_attention_key_split(name, lens, Hq, Hkv, dh, kind):
+    announce(f"attn key split {name} lens={lens} Hq={Hq} Hkv={Hkv} dh={dh} scores={kind}")
+    q, k, v, s, gain, temp, cu = _inputs(lens, Hq, Hkv, dh, torch.bfloat16, seed=zlib.crc32(name.encode()) % 1000)
+    if kind != "random":
+        s = _score_pattern(kind, cu[-1], torch.Generator().manual_seed(5))
+    nbytes = tg.tg_attn_prefill_plan(cu, Hq, Hkv, dh)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    gq, gk, gv, gs, gg, gt = (x.cuda() for x in (q, k, v, s, gain, temp))
+    out, lse = tg.tg_gated_attn_prefill(gq, gk, gv, gs, gg, gt, cu, want_lse=True, workspace=ws)
+    out2, lse2 = tg.tg_gated_attn_prefill(gq, gk, gv, gs, gg, gt, cu, want_lse=True)
+    # The same workspace again: its counters were left at zero, and the
+    # pieces are combined in a fixed order, so the result repeats bit for bit.
+    out3, lse3 = tg.tg_gated_attn_prefill(gq, gk, gv, gs, gg, gt, cu, want_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out3, out) and torch.equal(lse3, lse)
+    assert int(ws[:2048].count_nonzero().item()) == 0
+    out, lse, out2, lse2 = out.cpu(), lse.cpu(), out2.cpu(), lse2.cpu()
+    if cu[-1] > 2048:
+        rows = _sampled_rows(cu, 32, seed=9) + list(range(cu[-1] - 70, cu[-1]))
+        rows = sorted(set(rows))
+        ref, ref_lse = oracle.gated_attention_rows(q, k, v, s, gain, temp, cu, rows)
+        got, got_lse = out[rows], lse[:, rows]
+    else:
+        ref, ref_lse = oracle.gated_attention(q, k, v, s, gain, temp, cu)
+        got, got_lse = out, lse
+    assert_within(got, ref, 2e-2, 1e-2, f"{name} out")
+    assert_within(got_lse, ref_lse, 2e-2, 1e-2, f"{name} lse")
+    # Against the unsplit call: each piece takes its bf16 probabilities
+    # against its own exponent base, so they round differently (2^-9 relative
+    # each); a row dominated by one key moves its sum, hence its lse, by up to
+    # that.
+    assert (out.float() - out2.float()).abs().max().item() <= 2 ** -6 * max(1.0, out2.float().abs().max().item())
+    assert (lse - lse2).abs().max().item() <= 2 ** -7
+
+
+def test_attention_key_split_workspace_reuse():
+    """One workspace serves calls of different shapes in turn (each call
+    leaves its counters at zero): every result equals that of the same call
+    on a fresh zeroed workspace, bit for bit."""
+    shapes = [[2048], [1800], [1537], [4000], [2048]]
+    announce(f"attn key split workspace reuse: rows {[s[0] for s in shapes]}")
+    big = max(tg.tg_attn_prefill_plan([0, n[0]], 16, 8, 128) for n in shapes)
+    shared = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    for i, lens in enumerate(shapes):
+        q, k, v, s, gain, temp, cu = _inputs(lens, 16, 8, 128, torch.bfloat16, seed=40 + i)
+        g = [x.cuda() for x in (q, k, v, s, gain, temp)]
+        need = tg.tg_attn_prefill_plan(cu, 16, 8, 128)
+        assert need > 0
+        fresh = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        o1, l1 = tg.tg_gated_attn_prefill(*g, cu, want_lse=True, workspace=shared)
+        o2, l2 = tg.tg_gated_attn_prefill(*g, cu, want_lse=True, workspace=fresh)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), lens
+    assert int(shared[:2048].count_nonzero().item()) == 0
+
+
 @pytest.mark.parametrize("wname", ["qwen3_1p7b_128k_niah", "qwen3_1p7b_varlen4", "qwen3_1p7b_32k_stack4"])
 def test_attention_full_size_sampled(wname):
     """Workload-size attention (kept rows only) in the benchmark's launch

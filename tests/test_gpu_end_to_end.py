@@ -56,7 +56,7 @@ def test_gated_layer_chain(wname):
     g = {k: v.cuda() for k, v in gi.items()}
     a = {k: v.cuda() for k, v in ai.items()}
     layer = GatedLayer(w.total_tokens, sh.d_model, sh.n_q_heads, sh.d_head, w.seq_len, w.q_len,
-                       w.budget, sh.dtype)
+                       w.budget, sh.dtype, n_kv_heads=sh.n_kv_heads)
     out = layer(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"], a["q"], a["k"], a["v"],
                 a["gain"], a["temp"])
     torch.cuda.synchronize()
@@ -190,7 +190,7 @@ def test_gated_layer_graph_replays():
     g = {k: v.cuda() for k, v in workloads.gate_inputs(w, seed=0).items()}
     a = {k: v.cuda() for k, v in workloads.attn_inputs(w, seed=0).items()}
     mk = lambda: GatedLayer(w.total_tokens, sh.d_model, sh.n_q_heads, sh.d_head, w.seq_len,
-                            w.q_len, w.budget, sh.dtype)
+                            w.q_len, w.budget, sh.dtype, n_kv_heads=sh.n_kv_heads)
     layer, eager = mk(), mk()
     run = lambda L: L(g["hidden"], g["w1"], g["b1"], g["w2"], g["b2"], a["q"], a["k"], a["v"],
                       a["gain"], a["temp"])
