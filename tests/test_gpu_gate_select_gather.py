@@ -299,14 +299,20 @@ def test_select_random_keys():
 
 
 # ---------------------------------------------------------------- gather ----
-@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 2048), (torch.float32, 256), (torch.bfloat16, 8)])
-def test_gather_bitwise(dtype, d):
-    announce(f"gather {dtype} d={d}")
+@pytest.mark.parametrize("dtype,d,T,Kt", [
+    (torch.bfloat16, 2048, 5000, 777),    # 4 KiB rows: one pass of four loads per lane
+    (torch.bfloat16, 2048, 20000, 9000),  # the 128k layer's row size, more rows
+    (torch.bfloat16, 4096, 5000, 777),    # 8 KiB rows: two passes
+    (torch.float32, 2048, 3000, 1500),    # fp32 8 KiB rows
+    (torch.float32, 256, 5000, 777),      # 1 KiB rows: the tail loop only
+    (torch.bfloat16, 8, 5000, 777),       # 16-byte rows: one lane per row
+])
+def test_gather_bitwise(dtype, d, T, Kt):
+    announce(f"gather {dtype} d={d} T={T} Kt={Kt}")
     g = torch.Generator().manual_seed(11)
-    T = 5000
     hidden = torch.randn(T, d, generator=g).to(dtype)
     s = torch.randn(T, generator=g)
-    kept = torch.sort(torch.randperm(T, generator=g)[:777]).values.to(torch.int32)
+    kept = torch.sort(torch.randperm(T, generator=g)[:Kt]).values.to(torch.int32)
     hk, sk = tg.tg_gather_compact(hidden.cuda(), kept.cuda(), s.cuda())
     rh, rs = oracle.gather_compact(hidden, s, kept)
     bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
@@ -314,8 +320,9 @@ def test_gather_bitwise(dtype, d):
     assert torch.equal(sk.cpu().view(torch.int32), rs.view(torch.int32))
 
 
-def test_gather_out_of_range_rows_untouched():
-    T, d = 100, 64
+@pytest.mark.parametrize("d", [64, 2048])
+def test_gather_out_of_range_rows_untouched(d):
+    T = 100
     hidden = torch.randn(T, d).to(torch.bfloat16).cuda()
     s = torch.randn(T).cuda()
     kept = torch.tensor([3, -1, 99, 100, 7], dtype=torch.int32).cuda()
