@@ -415,15 +415,16 @@ def tg_gated_attn_prefill(q, k, v, s_kept, gain, temp, cu_kept: Sequence[int], o
     if want_lse and lse is None:
         lse = torch.empty(Hq, Kt, dtype=torch.float32, device=q.device)
     cu = _i32_array(cu_kept)
+    L = lib()
     args = (_dt(q), _dev(q, "q"), _dev(k, "k", q.dtype), _dev(v, "v", q.dtype),
             _dev(s_kept, "s_kept", torch.float32), _dev(gain, "gain", torch.float32),
             _dev(temp, "temp", torch.float32), ctypes.cast(cu, ctypes.POINTER(ctypes.c_int32)),
             len(cu_kept) - 1, Hq, Hkv, dh, _dev(out, "out", q.dtype),
             _dev(lse, "lse", torch.float32))
     if workspace is None:
-        _check("tg_gated_attn_prefill", lib().tg_gated_attn_prefill(*args, _stream(stream)))
+        _check("tg_gated_attn_prefill", L.tg_gated_attn_prefill(*args, _stream(stream)))
     else:
-        _check("tg_gated_attn_prefill_ws", lib().tg_gated_attn_prefill_ws(
+        _check("tg_gated_attn_prefill_ws", L.tg_gated_attn_prefill_ws(
             *args, _dev(workspace, "workspace"), _nbytes(workspace), _stream(stream)))
     return out, lse
 

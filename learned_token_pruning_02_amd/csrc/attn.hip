@@ -162,18 +162,6 @@ __device__ __forceinline__ void split_locate(const AttnArgs& a, int u, int bq, i
     p = u;
 }
 
-// Device-coherent 8-byte store and load: the partial results one workgroup
-// leaves for another inside a launch bypass the per-XCD caches, so no cache
-// needs writing back or invalidating.
-__device__ __forceinline__ void coherent_st64(uint64_t* p, float lo, float hi) {
-    const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) |
-                       ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float2 coherent_ld64(const uint64_t* p) {
-    const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return make_float2(__builtin_bit_cast(float, (uint32_t)v), __builtin_bit_cast(float, (uint32_t)(v >> 32)));
-}
 
 // Number of query tiles whose local index is >= t.
 __device__ __forceinline__ int tiles_at_or_above(const AttnArgs& a, int t) {

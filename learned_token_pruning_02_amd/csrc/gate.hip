@@ -362,7 +362,9 @@ hipError_t launch_gate_bf16_dg(const bf16* hidden, int64_t T, int d, const bf16*
             // A short prompt (up to 16384 tokens): 64-token workgroups whose
             // two pairs of waves split the gate units, so that every SIMD
             // gets a wave (128-token workgroups leave half of them idle).
-            hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 1, 2, 2>), dim3((T + 63) / 64), dim3(256), 0,
+            // One workgroup per CU, so each wave holds whole slices of W1
+            // fragments.
+            hipLaunchKernelGGL((gate_bf16_kernel<DG, 4, 1, 1, 2>), dim3((T + 63) / 64), dim3(256), 0,
                                st, hidden, T, d, w1, b1, w2, b2, scores);
         } else {
             // Below 65536 tokens, 128-token workgroups of 32-token waves, two

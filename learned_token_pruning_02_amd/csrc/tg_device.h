@@ -46,6 +46,21 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
 
+// Device-coherent 8-byte store and load of two floats: partial results that
+// one workgroup leaves for another inside a launch bypass the per-XCD caches,
+// so no cache needs writing back or invalidating.  A workgroup waits for its
+// own stores (s_waitcnt vmcnt(0)) before it takes the ticket that hands them
+// over.
+__device__ __forceinline__ void coherent_st64(uint64_t* p, float lo, float hi) {
+    const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+                       ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 coherent_ld64(const uint64_t* p) {
+    const uint64_t v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__builtin_bit_cast(float, (uint32_t)v), __builtin_bit_cast(float, (uint32_t)(v >> 32)));
+}
+
 // Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }
 

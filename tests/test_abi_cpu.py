@@ -467,10 +467,17 @@ def test_missing_library_fails_loudly():
         "    tg.tg_gate_score(torch.zeros(4, 64), torch.zeros(64, 64), None, torch.zeros(64), None)\n"
         "except RuntimeError:\n"
         "    print('raised')\n"
+        "q, k = torch.zeros(8, 2, 64), torch.zeros(8, 1, 64)\n"
+        "for ws in (None, torch.zeros(64, dtype=torch.uint8)):\n"
+        "    try:\n"
+        "        tg.tg_gated_attn_prefill(q, k, k, None, None, torch.ones(2), [0, 8], workspace=ws)\n"
+        "    except RuntimeError:\n"
+        "        print('attention raised')\n"
     )
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=240)
     assert r.returncode == 0 and "raised" in r.stdout, (r.returncode, r.stdout, r.stderr)
+    assert r.stdout.count("attention raised") == 2, (r.stdout, r.stderr)
 
 
 def test_select_path_validation():
