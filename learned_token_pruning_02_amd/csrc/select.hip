@@ -958,11 +958,12 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
         return c;
     };
 
-    // ---- 1. value range from the first group ----------------------------------
+    // ---- 1. value range from the first row -----------------------------------
+    // (The other rows of the first group are still arriving meanwhile.)
     const S1Group c0 = s1_load(rs, 0);
     float vmin = INFINITY, vmax = -INFINITY, sum = 0.f, sq = 0.f, cnt_f = 0.f;
 #pragma unroll
-    for (int k = 0; k < S1_GR; ++k) {
+    for (int k = 0; k < 1; ++k) {
 #pragma unroll
         for (int e = 0; e < S1_KPT; ++e) {
             const float v = c0.v[k][e];
@@ -1032,16 +1033,26 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
 
     if (sh_cnt <= (uint32_t)S1_CAND) {
         // ---- 3. candidates of bin d, counts of higher bins ---------------------
+        // For the first group's rows (in registers) the masks of keys above
+        // bin d and in bin d are kept for the write pass.
+        uint32_t up0 = 0u, eq0 = 0u;
         s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
             const int i0 = r * S1_ROW + pos0;
-            uint32_t up = 0u;
+            uint32_t up = 0u, eq = 0u;
 #pragma unroll
             for (int e = 0; e < S1_KPT; ++e) {
                 if (i0 + e < ndoc) {
                     const uint32_t bn = s1_bin(x[e], vlo, scale);
                     if (bn > d) up |= 1u << e;
-                    if (bn == d) cand[atomicAdd(&sh_ncand, 1u)] = make_uint2(order_key(x[e]), (uint32_t)(i0 + e));
+                    if (bn == d) {
+                        eq |= 1u << e;
+                        cand[atomicAdd(&sh_ncand, 1u)] = make_uint2(order_key(x[e]), (uint32_t)(i0 + e));
+                    }
                 }
+            }
+            if (r < S1_GR) {
+                up0 |= up << (S1_KPT * r);
+                eq0 |= eq << (S1_KPT * r);
             }
             const uint32_t c = wave_count(up);
             if (lane == 0) cnt[r * S1_WAVES + w] = c;
@@ -1076,12 +1087,26 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
         s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
             const int i0 = r * S1_ROW + pos0;
             uint32_t km = 0u;
+            if (r < S1_GR) {
+                // Keys above bin d are kept; of those in bin d (a few per
+                // request) only the candidates marked in bits.
+                km = (up0 >> (S1_KPT * r)) & 0xFu;
+                const uint32_t eq = (eq0 >> (S1_KPT * r)) & 0xFu;
+                if (eq != 0u) {
 #pragma unroll
-            for (int e = 0; e < S1_KPT; ++e) {
-                const int i = i0 + e;
-                if (i < ndoc) {
-                    const uint32_t bn = s1_bin(x[e], vlo, scale);
-                    if (bn > d || (bn == d && ((bits[i / 32] >> (i % 32)) & 1u))) km |= 1u << e;
+                    for (int e = 0; e < S1_KPT; ++e) {
+                        const int i = i0 + e;
+                        if (((eq >> e) & 1u) && ((bits[i / 32] >> (i % 32)) & 1u)) km |= 1u << e;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < S1_KPT; ++e) {
+                    const int i = i0 + e;
+                    if (i < ndoc) {
+                        const uint32_t bn = s1_bin(x[e], vlo, scale);
+                        if (bn > d || (bn == d && ((bits[i / 32] >> (i % 32)) & 1u))) km |= 1u << e;
+                    }
                 }
             }
             uint32_t pos = cnt[r * S1_WAVES + w] + lane_offset(km);
