@@ -1018,11 +1018,17 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
     const float vlo = lo >= -3.402823466e38f ? lo : 0.f;
 
     // ---- 2. histogram, threshold bin ------------------------------------------
+    // The bins of the first group's keys (in registers) are kept, two 16-bit
+    // bins per word, for the candidate pass.
+    uint32_t bq[S1_GR][S1_KPT / 2] = {};
     s1_rows(rs, nrows, c0, [&](int r, f32x4 x) {
         const int i0 = r * S1_ROW + pos0;
 #pragma unroll
-        for (int e = 0; e < S1_KPT; ++e)
-            if (i0 + e < ndoc) atomicAdd(&hist[s1_bin(x[e], vlo, scale)], 1u);
+        for (int e = 0; e < S1_KPT; ++e) {
+            const uint32_t bn = s1_bin(x[e], vlo, scale);
+            if (r < S1_GR) bq[r][e / 2] |= bn << (16 * (e % 2));
+            if (i0 + e < ndoc) atomicAdd(&hist[bn], 1u);
+        }
     });
     __syncthreads();
     s1_find_bin(hist, (uint32_t)kdoc, wtot, &sh_d, &sh_rem, &sh_cnt);
@@ -1042,7 +1048,8 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
 #pragma unroll
             for (int e = 0; e < S1_KPT; ++e) {
                 if (i0 + e < ndoc) {
-                    const uint32_t bn = s1_bin(x[e], vlo, scale);
+                    const uint32_t bn = r < S1_GR ? (bq[r][e / 2] >> (16 * (e % 2))) & 0xFFFFu
+                                                  : s1_bin(x[e], vlo, scale);
                     if (bn > d) up |= 1u << e;
                     if (bn == d) {
                         eq |= 1u << e;
