@@ -253,6 +253,29 @@ def test_attention_key_split(name, lens, Hq, Hkv, dh, kind):
     assert (lse - lse2).abs().max().item() <= 2 ** -7
 
 
+@pytest.mark.parametrize("lens,Hq,Hkv,dh", [([2048], 16, 8, 128), ([1600], 8, 2, 64)])
+def test_attention_key_split_without_bias(lens, Hq, Hkv, dh):
+    """The key split of the bias-free build (s_kept = gain = NULL) equals the
+    definition with a zero bias, and the unsplit call within the rounding of
+    each piece's probabilities."""
+    announce(f"attn key split no-bias lens={lens} Hq={Hq} Hkv={Hkv} dh={dh}")
+    q, k, v, s, gain, temp, cu = _inputs(lens, Hq, Hkv, dh, torch.bfloat16, seed=33)
+    nbytes = tg.tg_attn_prefill_plan(cu, Hq, Hkv, dh)
+    assert nbytes > 0
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    gq, gk, gv, gt = (x.cuda() for x in (q, k, v, temp))
+    out, lse = tg.tg_gated_attn_prefill(gq, gk, gv, None, None, gt, cu, want_lse=True, workspace=ws)
+    out2, lse2 = tg.tg_gated_attn_prefill(gq, gk, gv, None, None, gt, cu, want_lse=True)
+    torch.cuda.synchronize()
+    assert int(ws[:2048].count_nonzero().item()) == 0
+    out, lse, out2, lse2 = out.cpu(), lse.cpu(), out2.cpu(), lse2.cpu()
+    ref, ref_lse = oracle.gated_attention(q, k, v, torch.zeros_like(s), gain, temp, cu)
+    assert_within(out, ref, 2e-2, 1e-2, "split no-bias out")
+    assert_within(lse, ref_lse, 2e-2, 1e-2, "split no-bias lse")
+    assert (out.float() - out2.float()).abs().max().item() <= 2 ** -6 * max(1.0, out2.float().abs().max().item())
+    assert (lse - lse2).abs().max().item() <= 2 ** -7
+
+
 def test_attention_key_split_workspace_reuse():
     """One workspace serves calls of different shapes in turn (each call
     leaves its counters at zero): every result equals that of the same call
