@@ -125,6 +125,11 @@ struct AttnArgs {
 
 constexpr int KVT = 64;          // keys per tile
 constexpr int VT_STRIDE = KVT + 8;  // LDS row stride of V^T (bf16 elements)
+// LDS row stride of V kept key-major (bf16 elements): 80 dwords, 16 modulo the
+// 64 banks, so the four key rows a half-wave's transposing read touches fall
+// on disjoint banks.
+template <int DH>
+constexpr int vs_stride() { return DH + 32; }
 
 // The key split serves grids of fewer than SPLIT_MAX_TILES (query tile, head
 // group) pairs; their tickets fill a counter region of fixed size at the start
@@ -225,7 +230,14 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     static_assert(!SPLIT || (NWAVE == 4 && BQ <= KVT), "key split: four waves, <= 64 rows per head");
 
     __shared__ __attribute__((aligned(16))) bf16 Ks[NKB][KVT * KS];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH * VT_STRIDE];
+    // V in LDS: the four-wave kernel keeps it key-major, as loaded, and reads
+    // the PV operands with gfx950's transposing LDS reads (no register
+    // transpose when staging); the eight-wave kernel, whose step is bound by
+    // LDS instruction issue, stores it transposed so that each operand is one
+    // 16-byte read.
+    constexpr bool VTR = NWAVE == 4;
+    constexpr int VS = vs_stride<DH>();
+    __shared__ __attribute__((aligned(16))) bf16 Vt[2][VTR ? KVT * VS : DH * VT_STRIDE];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -350,8 +362,12 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         const int row = uu / (DH / 8), c = uu % (DH / 8);
         return (int)(row * row_elems * 2) + 16 * c;
     };
+    // Thread st stages keys 4kg + {0..3}, dims 8dg + {0..7} of the V tile:
+    // for the key-major layout sixteen consecutive threads cover one key row
+    // (coalesced loads, whole-row LDS stores); for the transposed one they
+    // cover sixteen keys of the same dims.
     auto v_off = [&](int i) {
-        const int kg = st % (KVT / 4), dg = st / (KVT / 4);
+        const int kg = VTR ? st / (DH / 8) : st % (KVT / 4), dg = VTR ? st % (DH / 8) : st / (KVT / 4);
         return st < VU ? (int)((4 * kg + i) * row_elems * 2) + 16 * dg : OFF_NONE;
     };
     // With eight waves a thread stages either K or V (one shared register
@@ -406,7 +422,11 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         }
     };
     auto store_v = [&](int buf) {
-        if (vstager && st < VU) {
+        if (VTR && st < VU) {
+            const int kg = st / (DH / 8), dg = st % (DH / 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st16(&Vt[buf][(4 * kg + i) * VS + 8 * dg], vreg[i]);
+        } else if (!VTR && vstager && st < VU) {
             const int kg = st % (KVT / 4), dg = st / (KVT / 4);
             // Keys 16G + 4h + {0..3} and 16G + 8 + 4h + {0..3} (one PV operand
             // of lane half h) are stored next to each other at 16G + 8h.
@@ -423,6 +443,24 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
                 st8(&Vt[buf][(8 * dg + e) * VT_STRIDE + vpos], pk);
             }
         }
+    };
+
+    // PV operand of dh tile md, k step kk: keys 16kk + 4hh + {0..3} and
+    // 16kk + 8 + 4hh + {0..3} (the order of the probabilities in the score
+    // registers) of dim 32md + l32.  Key-major V: two transposing reads; in
+    // each 16-lane group, lane i points at four dims of one key row, and lane
+    // j receives dim j of the group's rows j/4, j/4 + 4, j/4 + 8 and j/4 + 12,
+    // so lane i of a group points at key 4hh + i/4 and dims 16 (group % 2) +
+    // 4 (i % 4).  Transposed V: one 16-byte read.
+    const int vtr = (4 * hh + (lane % 16) / 4) * VS + 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+    typedef short v4i16_t __attribute__((ext_vector_type(4)));
+    auto vfrag_tr = [&](int vb, int md, int kk) {
+        const bf16* p0 = &Vt[vb][(16 * kk) * VS + 32 * md + vtr];
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p0);
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(p0 + 8 * VS));
+        const u32x2 a = __builtin_bit_cast(u32x2, lo), c = __builtin_bit_cast(u32x2, hi);
+        return as_bf16x8(u32x4{a[0], a[1], c[0], c[1]});
     };
 
     f32x16 o[NMD];
@@ -598,7 +636,8 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     constexpr int CPM = 32 / NPV;           // logits per MFMA (even)
     constexpr int SG_VALU = (5 * 32 / 2 + NPV - 1) / NPV;  // VALU per MFMA in the scheduling groups
 #define TG_VFRAG(I)                                                                          \
-    as_bf16x8(ld16(&Vt[vb][(32 * ((I) % NMD) + l32) * VT_STRIDE + 16 * ((I) / NMD) + 8 * hh]))
+    (VTR ? vfrag_tr(vb, (I) % NMD, (I) / NMD)                                                \
+         : as_bf16x8(ld16(&Vt[vb][(32 * ((I) % NMD) + l32) * VT_STRIDE + 16 * ((I) / NMD) + 8 * hh])))
 #define TG_PVSM_FUSED(MASKED)                                                                \
     do {                                                                                     \
         const int vb = (jt - 1) & 1;                                                         \
