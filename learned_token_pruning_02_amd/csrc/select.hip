@@ -15,20 +15,26 @@
 // is cut into chunks of 2048 keys, one 256-thread workgroup per chunk, and
 // the whole batch goes through four launches:
 //   1. clear the per-request histograms and counters;
-//   2. histogram of the top 11 key bits per chunk (LDS), summed into the
+//   2. histogram of the keys over 2048 bins per chunk (LDS), summed into the
 //      request's histogram with global atomics; the chunk that finishes last
-//      (atomic ticket, no waiting) finds the bucket d1 holding the K_doc-th
-//      best key;
-//   3. per chunk, count the keys above d1, append the keys in d1 with their
-//      index and histogram their next 11 key bits; the last chunk picks the
-//      first digit from that histogram and ranks the candidates sharing it
-//      exactly by an LDS radix select over the 52-bit composite (low 21 key
-//      bits, then reversed index), which turns (key desc, index asc) into a
-//      single descending order, then counts the kept tokens of every chunk and
-//      scans them into output offsets;
-//   4. per chunk, re-derive each key's keep flag from (d1, composite prefix)
-//      and write the kept ids in index order (wave ballots + a small count
-//      table per workgroup), and the question tail after them.
+//      (atomic ticket, no waiting) finds the bin d1 holding the K_doc-th best
+//      key.  The bins are linear in the score over a range taken from the
+//      document's first chunk (mean +- 8 standard deviations within its min
+//      and max; every workgroup derives the same range from the same keys),
+//      and clamped to the end bins, so monotone in the key;
+//   3. per chunk, count the keys above d1 and append the keys in d1 with
+//      their index; the last chunk ranks the candidates exactly under the
+//      63-bit composite (key, then reversed index), which turns (key desc,
+//      index asc) into a single descending order, by counting for each one
+//      the candidates that beat it (a few hundred at most) or else by an LDS
+//      radix select over the composite, then counts the kept tokens of every
+//      chunk and scans them into output offsets;
+//   4. per chunk, re-derive each key's keep flag from (d1, composite
+//      threshold) and write the kept ids in index order (wave ballots + a
+//      small count table per workgroup), and the question tail after them.
+// A batch with a document above BIG_DOC tokens bins by the top 11 key bits
+// instead (candidates then share those bits and the composite keeps the low
+// 21), and ranks its candidates with every workgroup in separate launches.
 // Results do not depend on which workgroup finishes last.
 #include <algorithm>
 #include <atomic>
@@ -46,9 +52,11 @@ constexpr int SWAVES = SB / WAVE;
 constexpr int SITEMS = 8;               // keys per thread
 constexpr int SCHUNK = SB * SITEMS;     // 2048 keys per chunk
 constexpr int NBIN = 2048;
-constexpr int META = 8;                 // u32 words of per-request metadata
+constexpr int META = 10;                // u32 words of per-request metadata
 constexpr int CTR = 16;                 // u32 counters per request (tickets, candidate count)
 constexpr int NPASS = 5;                // radix passes over the 52-bit candidate composite
+constexpr int LPASS = 6;                // radix passes over the 63-bit composite of linear bins
+constexpr uint32_t RC_MAX = 384;        // candidates ranked by counting (linear bins)
 constexpr int BIG_DOC = 1 << 20;        // documents above this rank their candidates with every workgroup
 constexpr int RANK_WG = 512;            // workgroups of the many-workgroup candidate passes
 constexpr uint32_t CAND_LDS = 8192;     // threshold-bucket candidates staged in LDS
@@ -74,6 +82,96 @@ __device__ __forceinline__ int pass_shift(int p) {
     return p == 0 ? 41 : (p == 1 ? 31 : (p == 2 ? 20 : (p == 3 ? 9 : 0)));
 }
 __device__ __forceinline__ int pass_width(int p) { return p == 1 ? 10 : (p == 4 ? 9 : 11); }
+
+// With linear bins the candidates of a bin share no key bits: the composite
+// is the whole key, then 0x7fffffff - index (63 bits), and its radix digits
+// are 11 + 11 + 10 + 11 + 10 + 10 bits from the top.
+__device__ __forceinline__ uint64_t composite_full(uint32_t key, uint32_t idx) {
+    return ((uint64_t)key << 31) | (uint64_t)(0x7fffffffu - idx);
+}
+__device__ __forceinline__ int lpass_shift(int p) {
+    return p == 0 ? 52 : (p == 1 ? 41 : (p == 2 ? 31 : (p == 3 ? 20 : (p == 4 ? 10 : 0))));
+}
+__device__ __forceinline__ int lpass_width(int p) { return (p == 0 || p == 1 || p == 3) ? 11 : 10; }
+
+template <bool LIN>
+__device__ __forceinline__ uint64_t rank_key(uint32_t key, uint32_t idx) {
+    return LIN ? composite_full(key, idx) : composite(key, idx);
+}
+
+// Bin of score v among NBIN bins linear in the value over the range
+// [vmin, vmin + (NBIN - 2) / scale], clamped to the end bins (NaN and -inf
+// to bin 0, +inf to the last), so monotone in the selection order: a higher
+// key never lands in a lower bin, and -0 and +0 share a bin.  A zero scale
+// puts every score in bin 0.
+__device__ __forceinline__ uint32_t lin_bin(float v, float vmin, float scale) {
+    const float f = (v - vmin) * scale;
+    if (!(f >= 1.0f)) return 0u;  // below the range, NaN
+    return f < (float)(NBIN - 1) ? (uint32_t)f : (uint32_t)(NBIN - 1);
+}
+
+// The range of the linear bins from the finite scores among `vals` (n of
+// them over the workgroup, `valid` marking this thread's): their mean +- 8
+// standard deviations, within their min and max; *vlo and *scale as
+// lin_bin takes them.  Every thread gets the same bits, and so does every
+// workgroup that reduces the same values in the same thread layout.
+template <int NT, int NV, class Vals>
+__device__ __forceinline__ void value_range(Vals vals, float* red, float* out_lo, float* out_scale) {
+    constexpr int NW = NT / WAVE;
+    const int lane = lane_id(), w = threadIdx.x / WAVE;
+    float vmin = INFINITY, vmax = -INFINITY, sum = 0.f, sq = 0.f, cnt_f = 0.f;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+        bool ok;
+        const float v = vals(e, &ok);
+        if (ok && fabsf(v) <= 3.402823466e38f) {  // finite
+            vmin = fminf(vmin, v);
+            vmax = fmaxf(vmax, v);
+            sum += v;
+            sq = fmaf(v, v, sq);
+            cnt_f += 1.f;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        vmin = fminf(vmin, __shfl_xor(vmin, o, WAVE));
+        vmax = fmaxf(vmax, __shfl_xor(vmax, o, WAVE));
+        sum += __shfl_xor(sum, o, WAVE);
+        sq += __shfl_xor(sq, o, WAVE);
+        cnt_f += __shfl_xor(cnt_f, o, WAVE);
+    }
+    if (lane == 0) {
+        red[w] = vmin;
+        red[NW + w] = vmax;
+        red[2 * NW + w] = sum;
+        red[3 * NW + w] = sq;
+        red[4 * NW + w] = cnt_f;
+    }
+    __syncthreads();
+    sum = sq = cnt_f = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        vmin = fminf(vmin, red[i]);
+        vmax = fmaxf(vmax, red[NW + i]);
+        sum += red[2 * NW + i];
+        sq += red[3 * NW + i];
+        cnt_f += red[4 * NW + i];
+    }
+    float lo = vmin, hi = vmax;
+    if (cnt_f > 0.f) {
+        const float mu = sum / cnt_f;
+        const float sd = sqrtf(fmaxf(sq / cnt_f - mu * mu, 0.f));
+        if (sd <= 3.402823466e38f) {
+            lo = fmaxf(lo, mu - 8.f * sd);
+            hi = fminf(hi, mu + 8.f * sd);
+        }
+    }
+    // Bins of width (hi - lo) / (NBIN - 2) between the end bins; a
+    // degenerate or non-finite range puts every score in bin 0.
+    const float span = hi - lo;
+    *out_scale = span > 0.f && span <= 3.402823466e38f ? (float)(NBIN - 2) / span : 0.f;
+    *out_lo = lo >= -3.402823466e38f ? lo : 0.f;
+}
 
 __device__ __forceinline__ uint32_t coherent_load(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -118,10 +216,11 @@ struct SelArgs {
     int32_t* kept;
     int32_t* cu_dev;
     uint32_t* hist;       // [B][NBIN]
-    uint32_t* meta;       // [B][META]: d1, rem1, cnt1, cprefix lo/hi, cmask lo/hi, done
+    uint32_t* meta;       // [B][META]: d1, rem1, cnt1, cprefix lo/hi, cmask lo/hi, done,
+                          //            bin range low, bin scale (float bits)
     uint32_t* ctr;        // [B][CTR]: hist ticket, candidate ticket, candidate count,
                           //           rank-pass tickets [4, 4+NPASS), count ticket 4+NPASS
-    uint32_t* rank_hist;  // [B][NPASS][NBIN]: first-digit histogram ([b][0]), and every pass of the many-workgroup ranking
+    uint32_t* rank_hist;  // [B][NPASS][NBIN]: every pass of the many-workgroup ranking (top-bit bins)
     uint32_t* chunk_kept; // [doc chunks]: kept candidates per chunk (many-workgroup ranking only)
     int32_t big;          // rank candidates with every workgroup (some document > BIG_DOC)
     uint32_t* chunk_def;  // [doc chunks]: keys above d1
@@ -217,9 +316,14 @@ __global__ __launch_bounds__(SB) void sel_clear_kernel(uint32_t* hist, uint32_t*
 }
 
 // ------------------------------------------------------------- launch 2 ----
+// LIN: bins linear in the score over the range of the document's first chunk
+// (published in the request's metadata for launches 3 and 4); else the top
+// 11 key bits.
+template <bool LIN>
 __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
     __shared__ uint32_t h[NBIN];
     __shared__ uint32_t wtot[SWAVES];
+    __shared__ float red[LIN ? 5 * SWAVES : 1];
     __shared__ uint32_t sh_last, sh_d, sh_gt, sh_cnt;
     const int tid = threadIdx.x;
     const int b = find_request(a.doc_group0, a.batch, blockIdx.x);
@@ -233,18 +337,30 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
     const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, nck);
 
     for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
-    __syncthreads();
     // The chunks of this group, the keys of the next one loaded before the
     // histogram of the current one.
     static_assert(SITEMS == 8, "two 16-byte loads per thread and chunk");
     Chunk8 nxt = load_chunk8(s, ndoc, c_lo);
+    float vlo = 0.f, scale = 0.f;
+    if constexpr (LIN) {
+        const Chunk8 z = c_lo == 0 ? nxt : load_chunk8(s, ndoc, 0);
+        value_range<SB, SITEMS>(
+            [&](int e, bool* ok) {
+                *ok = SITEMS * tid + e < ndoc;
+                return z.v[e / 4][e % 4];
+            },
+            red, &vlo, &scale);
+    } else {
+        __syncthreads();
+    }
     for (int c = c_lo; c < c_hi; ++c) {
         const Chunk8 cur = nxt;
         if (c + 1 < c_hi) nxt = load_chunk8(s, ndoc, c + 1);
 #pragma unroll
         for (int e = 0; e < SITEMS; ++e) {
             const int i = c * SCHUNK + SITEMS * tid + e;
-            if (i < ndoc) atomicAdd(&h[order_key(cur.v[e / 4][e % 4]) >> 21], 1u);
+            const float v = cur.v[e / 4][e % 4];
+            if (i < ndoc) atomicAdd(&h[LIN ? lin_bin(v, vlo, scale) : order_key(v) >> 21], 1u);
         }
     }
     __syncthreads();
@@ -263,19 +379,24 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
         m[0] = sh_d;
         m[1] = (uint32_t)kdoc - sh_gt;
         m[2] = sh_cnt;
+        m[8] = __float_as_uint(vlo);
+        m[9] = __float_as_uint(scale);
     }
 }
 
 // ------------------------------------------------------------- launch 3 ----
-// BIG: the batch ranks its candidates with every workgroup afterwards
-// (sel_rank_kernel), so the last workgroup here only publishes the start of
-// the ranking, and LDS holds just the staging list (a chunk's candidates at
-// most) and no first-digit histogram: four times as many workgroups per CU.
+// BIG: the batch bins by the top key bits and ranks its candidates with every
+// workgroup afterwards (sel_rank_kernel), so the last workgroup here only
+// publishes the start of the ranking, and LDS holds just the staging list (a
+// chunk's candidates at most): four times as many workgroups per CU.  Else
+// the bins are linear in the score and the last workgroup ranks.
 template <bool BIG>
 __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
+    constexpr bool LIN = !BIG;
     constexpr uint32_t CL = BIG ? (uint32_t)SCHUNK : CAND_LDS;
     __shared__ uint32_t wtot[SWAVES];
     __shared__ uint32_t sh_base, sh_last, sh_d, sh_gt, sh_cnt, sh_total;
+    __shared__ uint64_t sh_t;
     __shared__ uint32_t h[BIG ? 1 : NBIN];
     __shared__ uint2 cl[CL];
     const int tid = threadIdx.x;
@@ -288,20 +409,14 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     const float* s = a.scores + a.off[b] + a.p[b];  // document tokens, indexed from 0
     uint32_t* m = a.meta + b * META;
     const uint32_t d1 = m[0];
+    const float vlo = __uint_as_float(m[8]), scale = __uint_as_float(m[9]);
     uint2* cand = a.cand + a.off[b];
     const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, nck);
-    constexpr bool hist1 = !BIG;  // the first ranking digit is histogrammed here
+    auto bin_of = [&](float v) { return LIN ? lin_bin(v, vlo, scale) : order_key(v) >> 21; };
 
     // Per chunk of the group: the count of keys above d1 (for its output
     // offset), and the keys in d1 staged in LDS with their index; the group's
-    // candidates then go to the request's list with one atomic, and the
-    // first ranking digit (key bits 10-20) of each is histogrammed, so that
-    // the last workgroup starts from the request's histogram instead of a
-    // pass over all of them.
-    if (hist1)
-        for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
-    __syncthreads();
-    uint32_t* gh0 = a.rank_hist + (size_t)b * NPASS * NBIN;
+    // candidates then go to the request's list with one atomic.
     uint32_t run = 0;  // candidates staged in cl (the same in every thread)
     // Move the staged candidates to the request's list (one atomic for all);
     // `more`: the list is refilled afterwards.
@@ -314,17 +429,21 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     };
     Chunk8 nxt = load_chunk8(s, ndoc, c_lo);
     for (int c = c_lo; c < c_hi; ++c) {
-        uint32_t cur[SITEMS];
+        float cur[SITEMS];
+        uint32_t bn[SITEMS];
 #pragma unroll
-        for (int e = 0; e < SITEMS; ++e) cur[e] = order_key(nxt.v[e / 4][e % 4]);
+        for (int e = 0; e < SITEMS; ++e) {
+            cur[e] = nxt.v[e / 4][e % 4];
+            bn[e] = bin_of(cur[e]);
+        }
         if (c + 1 < c_hi) nxt = load_chunk8(s, ndoc, c + 1);
         uint32_t above = 0, ncand = 0;
 #pragma unroll
         for (int e = 0; e < SITEMS; ++e) {
             const int i = c * SCHUNK + SITEMS * tid + e;
             if (i < ndoc) {
-                above += (cur[e] >> 21) > d1;
-                ncand += (cur[e] >> 21) == d1;
+                above += bn[e] > d1;
+                ncand += bn[e] == d1;
             }
         }
         // One scan for both counts (each at most SCHUNK per chunk, so the
@@ -339,18 +458,11 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
 #pragma unroll
         for (int e = 0; e < SITEMS; ++e) {
             const int i = c * SCHUNK + SITEMS * tid + e;
-            if (i < ndoc && (cur[e] >> 21) == d1) {
-                cl[pos++] = make_uint2(cur[e], (uint32_t)i);
-                if (hist1) atomicAdd(&h[(cur[e] >> 10) & (NBIN - 1)], 1u);
-            }
+            if (i < ndoc && bn[e] == d1) cl[pos++] = make_uint2(order_key(cur[e]), (uint32_t)i);
         }
         run += tot_cand;
     }
     flush(false);
-    if (hist1) {
-        for (int i = tid; i < NBIN; i += SB)
-            if (h[i] != 0u) atomicAdd(&gh0[i], h[i]);
-    }
     wait_own_writes();
     __syncthreads();
     if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 1], 1u) == (uint32_t)(ngrp - 1);
@@ -366,14 +478,15 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         return;
     } else {
 
-    // ---- the last chunk: exact rank inside bucket d1 ----------------------
-    // The bucket's candidates (usually a few thousand) are staged in LDS once,
-    // eight device-coherent loads in flight per thread: loaded one per loop
-    // iteration, each pass over them waited a memory round trip per item.
-    // The first digit comes from the histogram the chunks built; the passes
-    // over the remaining digits and the per-chunk kept counts then read LDS.
-    // A degenerate bucket of heavy ties too big for LDS is read from global
-    // memory on every pass instead, in the same batches.
+    // ---- the last chunk: exact rank inside bin d1 --------------------------
+    // The bin's candidates (usually a few dozen to a few hundred) are staged
+    // in LDS once, eight device-coherent loads in flight per thread.  Up to
+    // RC_MAX of them are ranked by counting, for each, the candidates that
+    // beat it under (key desc, index asc); the rem-th best gives the
+    // threshold composite.  A bigger bin (heavy ties, or scores the first
+    // chunk did not represent) is ranked by LDS radix passes over the
+    // composite instead, read from global memory on every pass when it does
+    // not fit in LDS.
     const uint32_t cnt1 = m[2];
     const bool in_lds = cnt1 <= CAND_LDS;
     constexpr int CB = 8;  // candidate loads in flight per thread
@@ -410,36 +523,51 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         }
     }
     __syncthreads();
-    uint32_t rem = m[1];
+    uint32_t rem = m[1];  // 1 <= rem <= cnt1
     uint64_t cprefix = 0, cmask = 0;
-    {
-        const uint32_t* gh0 = a.rank_hist + (size_t)b * NPASS * NBIN;
-        find_bin([&](int i) { return coherent_load(&gh0[i]); }, NBIN, rem, wtot, &sh_d, &sh_gt,
-                 &sh_cnt);
-        rem -= sh_gt;
-        cprefix = (uint64_t)sh_d << pass_shift(0);
-        cmask = (uint64_t)(NBIN - 1) << pass_shift(0);
-    }
-    const uint32_t cnt0 = sh_cnt;  // candidates sharing the first digit
+    if (cnt1 <= RC_MAX) {
+        for (uint32_t c = tid; c < cnt1; c += SB) {
+            const uint2 me = cl[c];
+            uint32_t r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+            uint32_t o = 0;
+            for (; o + 4 <= cnt1; o += 4) {
+                const uint2 e0 = cl[o], e1 = cl[o + 1], e2 = cl[o + 2], e3 = cl[o + 3];
+                r0 += (e0.x > me.x) || (e0.x == me.x && e0.y < me.y);
+                r1 += (e1.x > me.x) || (e1.x == me.x && e1.y < me.y);
+                r2 += (e2.x > me.x) || (e2.x == me.x && e2.y < me.y);
+                r3 += (e3.x > me.x) || (e3.x == me.x && e3.y < me.y);
+            }
+            for (; o < cnt1; ++o) {
+                const uint2 e0 = cl[o];
+                r0 += (e0.x > me.x) || (e0.x == me.x && e0.y < me.y);
+            }
+            if (r0 + r1 + r2 + r3 == rem - 1) sh_t = composite_full(me.x, me.y);
+        }
+        __syncthreads();
+        cprefix = sh_t;  // the kept candidates: composite >= the rem-th best
+        cmask = ~0ull;
+    } else {
+        uint32_t cnt = cnt1;  // candidates matching the prefix fixed so far
 #pragma unroll 1
-    for (int p = 1; p < NPASS && cnt0 != rem; ++p) {
-        const int sh = pass_shift(p);
-        const int wd = pass_width(p);
-        const int nb = 1 << wd;
-        for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
-        __syncthreads();
-        for_cands([&](uint2 e) {
-            const uint64_t cp = composite(e.x, e.y);
-            if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
-        });
-        __syncthreads();
-        find_bin([&](int i) { return h[i]; }, nb, rem, wtot, &sh_d, &sh_gt, &sh_cnt);
-        rem -= sh_gt;
-        cprefix |= (uint64_t)sh_d << sh;
-        cmask |= (uint64_t)(nb - 1) << sh;
-        const uint32_t cnt = sh_cnt;
-        __syncthreads();
-        if (cnt == rem) break;  // every composite with this prefix is kept
+        for (int p = 0; p < LPASS && cnt != rem; ++p) {
+            const int sh = lpass_shift(p);
+            const int nb = 1 << lpass_width(p);
+            for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
+            __syncthreads();
+            for_cands([&](uint2 e) {
+                const uint64_t cp = composite_full(e.x, e.y);
+                if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
+            });
+            __syncthreads();
+            find_bin([&](int i) { return h[i]; }, nb, rem, wtot, &sh_d, &sh_gt, &sh_cnt);
+            rem -= sh_gt;
+            cprefix |= (uint64_t)sh_d << sh;
+            cmask |= (uint64_t)(nb - 1) << sh;
+            cnt = sh_cnt;
+            __syncthreads();
+        }
+        // Every composite with this prefix is kept (cnt == rem), or the
+        // prefix covers all 63 bits.
     }
 
     // Kept candidates per chunk, then exclusive offsets of all chunks.
@@ -452,7 +580,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         __syncthreads();
         for_cands([&](uint2 e) {
             const int ch = (int)(e.y / SCHUNK) - c0;
-            if (ch >= 0 && ch < NBIN && (composite(e.x, e.y) & cmask) >= cprefix)
+            if (ch >= 0 && ch < NBIN && (composite_full(e.x, e.y) & cmask) >= cprefix)
                 atomicAdd(&ccnt[ch], 1u);
         });
         __syncthreads();
@@ -629,6 +757,7 @@ __global__ __launch_bounds__(SB) void sel_rankcount_kernel(SelArgs a) {
 }
 
 // ------------------------------------------------------------- launch 4 ----
+template <bool LIN>
 __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     __shared__ uint32_t wtot[SWAVES];
     const int tid = threadIdx.x;
@@ -679,6 +808,7 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
         const uint32_t d1 = m[0];
         const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
         const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
+        const float vlo = __uint_as_float(m[8]), scale = __uint_as_float(m[9]);
         const uint32_t base = a.chunk_off[a.doc_chunk0[b] + c];
         const int i0 = lo + SITEMS * tid;
         uint32_t km = 0u;
@@ -686,9 +816,10 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
         for (int e = 0; e < SITEMS; ++e) {
             const int i = i0 + e;
             if (i < ndoc) {
-                const uint32_t key = order_key(cur.v[e / 4][e % 4]);
-                const uint32_t dg = key >> 21;
-                if (dg > d1 || (dg == d1 && (composite(key, (uint32_t)i) & cmask) >= cprefix))
+                const float v = cur.v[e / 4][e % 4];
+                const uint32_t key = order_key(v);
+                const uint32_t dg = LIN ? lin_bin(v, vlo, scale) : key >> 21;
+                if (dg > d1 || (dg == d1 && (rank_key<LIN>(key, (uint32_t)i) & cmask) >= cprefix))
                     km |= 1u << e;
             }
         }
@@ -804,7 +935,7 @@ constexpr int S1_GR = 4;                         // rows per group (loads in fli
 constexpr int S1_GROUP = S1_ROW * S1_GR;         // 16384 keys per group
 constexpr int S1_MAX = SELECT_ONE_WG_MAX;        // document tokens per request
 constexpr int S1_ROWS = S1_MAX / S1_ROW;         // rows at most
-constexpr int S1_NB = 2048;                      // bins of the first histogram
+constexpr int S1_NB = NBIN;                      // bins of the first histogram
 constexpr int S1_CAND = 1024;                    // candidates ranked in LDS
 constexpr int S1_BPT = S1_NB / S1_THREADS;       // bins per thread in the bin scans
 static_assert(S1_MAX % S1_GROUP == 0 && S1_ROWS * S1_WAVES <= S1_THREADS, "rows");
@@ -867,16 +998,6 @@ __device__ __forceinline__ void s1_scan_counts(uint32_t* c, int n, uint32_t* wto
     __syncthreads();
 }
 
-// Bin of score v for the value range [vmin, vmin + (S1_NB - 2) / scale]:
-// linear in the value, clamped to the end bins (NaN and -inf to bin 0, +inf
-// to the last), so monotone in the selection order (a higher key never lands
-// in a lower bin, and -0 and +0 share a bin).
-__device__ __forceinline__ uint32_t s1_bin(float v, float vmin, float scale) {
-    const float f = (v - vmin) * scale;
-    if (!(f >= 1.0f)) return 0u;  // below the range, NaN
-    return f < (float)(S1_NB - 1) ? (uint32_t)f : (uint32_t)(S1_NB - 1);
-}
-
 // The keys of this thread in one group of S1_GR rows: v[r][e] is position
 // S1_GROUP g + S1_ROW r + 4t + e (positions past the document read as 0 and
 // are excluded by the caller).  Whole vectors are reinterpreted: a bit cast
@@ -918,7 +1039,7 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
     __shared__ uint32_t bits[S1_MAX / 32];          // kept candidates
     __shared__ uint2 cand[S1_CAND];                 // (key, position) of the keys in bin d
     __shared__ uint32_t wtot[S1_WAVES];
-    __shared__ float wmin[S1_WAVES], wmax[S1_WAVES], wsum[S1_WAVES], wsq[S1_WAVES], wcnt[S1_WAVES];
+    __shared__ float red[5 * S1_WAVES];
     __shared__ uint32_t sh_d, sh_rem, sh_cnt, sh_ncand;
 
     const int b = blockIdx.x, tid = threadIdx.x, w = tid / WAVE, lane = lane_id();
@@ -961,61 +1082,14 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
     // ---- 1. value range from the first row -----------------------------------
     // (The other rows of the first group are still arriving meanwhile.)
     const S1Group c0 = s1_load(rs, 0);
-    float vmin = INFINITY, vmax = -INFINITY, sum = 0.f, sq = 0.f, cnt_f = 0.f;
-#pragma unroll
-    for (int k = 0; k < 1; ++k) {
-#pragma unroll
-        for (int e = 0; e < S1_KPT; ++e) {
-            const float v = c0.v[k][e];
-            if (S1_ROW * k + pos0 + e < ndoc && fabsf(v) <= 3.402823466e38f) {  // finite
-                vmin = fminf(vmin, v);
-                vmax = fmaxf(vmax, v);
-                sum += v;
-                sq = fmaf(v, v, sq);
-                cnt_f += 1.f;
-            }
-        }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        vmin = fminf(vmin, __shfl_xor(vmin, o, WAVE));
-        vmax = fmaxf(vmax, __shfl_xor(vmax, o, WAVE));
-        sum += __shfl_xor(sum, o, WAVE);
-        sq += __shfl_xor(sq, o, WAVE);
-        cnt_f += __shfl_xor(cnt_f, o, WAVE);
-    }
     for (int i = tid; i < S1_NB; i += S1_THREADS) hist[i] = 0u;
-    if (lane == 0) {
-        wmin[w] = vmin;
-        wmax[w] = vmax;
-        wsum[w] = sum;
-        wsq[w] = sq;
-        wcnt[w] = cnt_f;
-    }
-    __syncthreads();
-    sum = sq = cnt_f = 0.f;
-#pragma unroll
-    for (int i = 0; i < S1_WAVES; ++i) {
-        vmin = fminf(vmin, wmin[i]);
-        vmax = fmaxf(vmax, wmax[i]);
-        sum += wsum[i];
-        sq += wsq[i];
-        cnt_f += wcnt[i];
-    }
-    float lo = vmin, hi = vmax;
-    if (cnt_f > 0.f) {
-        const float mu = sum / cnt_f;
-        const float sd = sqrtf(fmaxf(sq / cnt_f - mu * mu, 0.f));
-        if (sd <= 3.402823466e38f) {
-            lo = fmaxf(lo, mu - 8.f * sd);
-            hi = fminf(hi, mu + 8.f * sd);
-        }
-    }
-    // Bins of width (hi - lo) / (S1_NB - 2) between the end bins; a
-    // degenerate or non-finite range puts every score in bin 0.
-    const float span = hi - lo;
-    const float scale = span > 0.f && span <= 3.402823466e38f ? (float)(S1_NB - 2) / span : 0.f;
-    const float vlo = lo >= -3.402823466e38f ? lo : 0.f;
+    float vlo, scale;
+    value_range<S1_THREADS, S1_KPT>(
+        [&](int e, bool* ok) {
+            *ok = pos0 + e < ndoc;
+            return c0.v[0][e];
+        },
+        red, &vlo, &scale);
 
     // ---- 2. histogram, threshold bin ------------------------------------------
     // The bins of the first group's keys (in registers) are kept, two 16-bit
@@ -1025,7 +1099,7 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
         const int i0 = r * S1_ROW + pos0;
 #pragma unroll
         for (int e = 0; e < S1_KPT; ++e) {
-            const uint32_t bn = s1_bin(x[e], vlo, scale);
+            const uint32_t bn = lin_bin(x[e], vlo, scale);
             if (r < S1_GR) bq[r][e / 2] |= bn << (16 * (e % 2));
             if (i0 + e < ndoc) atomicAdd(&hist[bn], 1u);
         }
@@ -1049,7 +1123,7 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
             for (int e = 0; e < S1_KPT; ++e) {
                 if (i0 + e < ndoc) {
                     const uint32_t bn = r < S1_GR ? (bq[r][e / 2] >> (16 * (e % 2))) & 0xFFFFu
-                                                  : s1_bin(x[e], vlo, scale);
+                                                  : lin_bin(x[e], vlo, scale);
                     if (bn > d) up |= 1u << e;
                     if (bn == d) {
                         eq |= 1u << e;
@@ -1111,7 +1185,7 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
                 for (int e = 0; e < S1_KPT; ++e) {
                     const int i = i0 + e;
                     if (i < ndoc) {
-                        const uint32_t bn = s1_bin(x[e], vlo, scale);
+                        const uint32_t bn = lin_bin(x[e], vlo, scale);
                         if (bn > d || (bn == d && ((bits[i / 32] >> (i % 32)) & 1u))) km |= 1u << e;
                     }
                 }
@@ -1142,7 +1216,7 @@ __global__ __launch_bounds__(S1_THREADS) void sel_one_kernel(SelArgs a) {
             for (int e = 0; e < S1_KPT; ++e) {
                 if (i0 + e < ndoc) {
                     const uint32_t k = order_key(x[e]);
-                    if (s1_bin(x[e], vlo, scale) == d && (k & pmask) == prefix)
+                    if (lin_bin(x[e], vlo, scale) == d && (k & pmask) == prefix)
                         atomicAdd(&hist[(k >> shift) & dmask], 1u);
                 }
             }
@@ -1317,12 +1391,15 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
             s.big = 1;
     if (dc > 0) {
         const int n_hist = a.batch * NBIN, n_ctr = a.batch * CTR;
-        const int n_rank = a.batch * NPASS * NBIN, n_kept = s.big ? dc : 0;
+        const int n_rank = s.big ? a.batch * NPASS * NBIN : 0, n_kept = s.big ? dc : 0;
         const int n_clear = std::max(std::max(n_hist, n_ctr), std::max(n_rank, n_kept));
         hipLaunchKernelGGL(sel_clear_kernel, dim3((n_clear + SB - 1) / SB), dim3(SB), 0, st, s.hist,
                            s.ctr, n_hist, n_ctr, s.rank_hist, n_rank, s.chunk_kept, n_kept);
         const int dg = s.doc_group0[a.batch];
-        hipLaunchKernelGGL(sel_hist_kernel, dim3(dg), dim3(SB), 0, st, s);
+        if (s.big)
+            hipLaunchKernelGGL(sel_hist_kernel<false>, dim3(dg), dim3(SB), 0, st, s);
+        else
+            hipLaunchKernelGGL(sel_hist_kernel<true>, dim3(dg), dim3(SB), 0, st, s);
         if (s.big)
             hipLaunchKernelGGL(sel_cand_kernel<true>, dim3(dg), dim3(SB), 0, st, s);
         else
@@ -1333,8 +1410,12 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
             hipLaunchKernelGGL(sel_rankcount_kernel, dim3(RANK_WG), dim3(SB), 0, st, s);
         }
     }
-    if (s.all_group0[a.batch] > 0)
-        hipLaunchKernelGGL(sel_compact_kernel, dim3(s.all_group0[a.batch]), dim3(SB), 0, st, s);
+    if (s.all_group0[a.batch] > 0) {
+        if (s.big)
+            hipLaunchKernelGGL(sel_compact_kernel<false>, dim3(s.all_group0[a.batch]), dim3(SB), 0, st, s);
+        else
+            hipLaunchKernelGGL(sel_compact_kernel<true>, dim3(s.all_group0[a.batch]), dim3(SB), 0, st, s);
+    }
     return hipGetLastError();
 }
 

@@ -197,6 +197,31 @@ def test_select_one_workgroup_bins():
     _select_case([T], [128], [T // 8], torch.randn(T, generator=g).to(torch.bfloat16).float())
 
 
+@pytest.mark.parametrize("n", [1, 2, 383, 384, 385, 1000, 9000])
+def test_select_chunked_bins_candidates(n):
+    """The chunked path bins linearly over the range of the document's first
+    chunk.  Here that chunk holds the largest ordinary score (5.0), so the
+    top bin holds exactly the n planted scores above it: n straddles the
+    count the last workgroup ranks by counting (384), the LDS radix passes
+    and the passes that read the candidates from global memory.  Planted
+    scores equal (ranked by index alone) and distinct (by value)."""
+    g = torch.Generator().manual_seed(40 + n)
+    T = 100_000
+    s = torch.randn(T, generator=g).clamp(-4.9, 4.9)
+    s[0] = 5.0
+    pos = 2048 + torch.randperm(T - 2048 - 64, generator=g)[:n]
+    for distinct in (False, True):
+        x = s.clone()
+        x[pos] = 10.0 + (torch.randperm(n, generator=g).float() * 1e-3 if distinct else 0.0)
+        _select_case([T], [64], [64 + (n + 1) // 2], x)
+    if n in (1, 1000):
+        # a first chunk far narrower than the rest: most keys clamp to the
+        # end bins, and the threshold bin holds ~T/2 candidates
+        y = torch.randn(T, generator=g)
+        y[:2048] *= 1e-3
+        _select_case([T], [64], [64 + 3 * n], y)
+
+
 def test_select_sweep_scale():
     """The selector at the throughput sweep's scale (one request, no tail,
     K = T/16), bit-exact against the oracle."""
