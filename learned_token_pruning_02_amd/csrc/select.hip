@@ -32,9 +32,9 @@
 //   4. per chunk, re-derive each key's keep flag from (d1, composite
 //      threshold) and write the kept ids in index order (wave ballots + a
 //      small count table per workgroup), and the question tail after them.
-// A batch with a document above BIG_DOC tokens bins by the top 11 key bits
-// instead (candidates then share those bits and the composite keeps the low
-// 21), and ranks its candidates with every workgroup in separate launches.
+// A batch with a document above BIG_DOC tokens ranks its candidates with
+// every workgroup instead, in separate launches (radix passes over the
+// composite, then a counting launch).
 // Results do not depend on which workgroup finishes last.
 #include <algorithm>
 #include <atomic>
@@ -54,12 +54,12 @@ constexpr int SCHUNK = SB * SITEMS;     // 2048 keys per chunk
 constexpr int NBIN = 2048;
 constexpr int META = 10;                // u32 words of per-request metadata
 constexpr int CTR = 16;                 // u32 counters per request (tickets, candidate count)
-constexpr int NPASS = 5;                // radix passes over the 52-bit candidate composite
-constexpr int LPASS = 6;                // radix passes over the 63-bit composite of linear bins
+constexpr int NPASS = 6;                // radix passes over the 63-bit candidate composite
 constexpr uint32_t RC_MAX = 384;        // candidates ranked by counting (linear bins)
 constexpr int BIG_DOC = 1 << 20;        // documents above this rank their candidates with every workgroup
-constexpr int RANK_WG = 512;            // workgroups of the many-workgroup candidate passes
-constexpr uint32_t CAND_LDS = 8192;     // threshold-bucket candidates staged in LDS
+constexpr int RANK_WG = 512;            // workgroups of the many-workgroup candidate passes, at most
+constexpr uint32_t RANK_PER_WG = 4 * SB; // candidates per workgroup of those passes, at least
+constexpr uint32_t CAND_LDS = 8192;     // threshold-bin candidates staged in LDS
 constexpr int MAX_GROUPS = 2048;        // workgroups of launches 2-4 at most (chunks grouped beyond)
 static_assert(SCHUNK <= (int)CAND_LDS, "one chunk's candidates fit the staging list");
 static_assert(SCHUNK < 65536, "per-chunk counts share one 32-bit scan");
@@ -71,33 +71,17 @@ __device__ __forceinline__ uint32_t order_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Composite rank key of a candidate inside the threshold bucket: the low 21
-// key bits, then 0x7fffffff - index, so that larger = better and unique.
+// Rank key of a candidate inside the threshold bin (whose keys share no key
+// bits): the whole key, then 0x7fffffff - index, so that larger = better and
+// unique (63 bits).  Its radix digits are 11 + 11 + 10 + 11 + 10 + 10 bits
+// from the top.
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t idx) {
-    return ((uint64_t)(key & 0x1fffffu) << 31) | (uint64_t)(0x7fffffffu - idx);
-}
-
-// Digit p of the composite: bit offset and width (11 + 10 + 11 + 11 + 9 = 52).
-__device__ __forceinline__ int pass_shift(int p) {
-    return p == 0 ? 41 : (p == 1 ? 31 : (p == 2 ? 20 : (p == 3 ? 9 : 0)));
-}
-__device__ __forceinline__ int pass_width(int p) { return p == 1 ? 10 : (p == 4 ? 9 : 11); }
-
-// With linear bins the candidates of a bin share no key bits: the composite
-// is the whole key, then 0x7fffffff - index (63 bits), and its radix digits
-// are 11 + 11 + 10 + 11 + 10 + 10 bits from the top.
-__device__ __forceinline__ uint64_t composite_full(uint32_t key, uint32_t idx) {
     return ((uint64_t)key << 31) | (uint64_t)(0x7fffffffu - idx);
 }
-__device__ __forceinline__ int lpass_shift(int p) {
+__device__ __forceinline__ int pass_shift(int p) {
     return p == 0 ? 52 : (p == 1 ? 41 : (p == 2 ? 31 : (p == 3 ? 20 : (p == 4 ? 10 : 0))));
 }
-__device__ __forceinline__ int lpass_width(int p) { return (p == 0 || p == 1 || p == 3) ? 11 : 10; }
-
-template <bool LIN>
-__device__ __forceinline__ uint64_t rank_key(uint32_t key, uint32_t idx) {
-    return LIN ? composite_full(key, idx) : composite(key, idx);
-}
+__device__ __forceinline__ int pass_width(int p) { return (p == 0 || p == 1 || p == 3) ? 11 : 10; }
 
 // Bin of score v among NBIN bins linear in the value over the range
 // [vmin, vmin + (NBIN - 2) / scale], clamped to the end bins (NaN and -inf
@@ -220,11 +204,11 @@ struct SelArgs {
                           //            bin range low, bin scale (float bits)
     uint32_t* ctr;        // [B][CTR]: hist ticket, candidate ticket, candidate count,
                           //           rank-pass tickets [4, 4+NPASS), count ticket 4+NPASS
-    uint32_t* rank_hist;  // [B][NPASS][NBIN]: every pass of the many-workgroup ranking (top-bit bins)
-    uint32_t* chunk_kept; // [doc chunks]: kept candidates per chunk (many-workgroup ranking only)
+    uint32_t* rank_hist;  // [B][NPASS][NBIN]: every pass of the many-workgroup ranking
+    uint32_t* grp_kept;   // [doc groups]: kept candidates per chunk group (many-workgroup ranking only)
     int32_t big;          // rank candidates with every workgroup (some document > BIG_DOC)
-    uint32_t* chunk_def;  // [doc chunks]: keys above d1
-    uint32_t* chunk_off;  // [doc chunks]: output offset of the chunk's first kept token
+    uint32_t* grp_def;    // [doc groups]: keys above d1 per chunk group
+    uint32_t* grp_off;    // [doc groups]: output offset of the group's first kept document token
     uint2* cand;          // [T]: (key, local index), request b at off[b]
 };
 
@@ -307,23 +291,22 @@ __device__ __forceinline__ void find_bin(Get get, int nb, uint32_t rem, uint32_t
 // ------------------------------------------------------------- launch 1 ----
 __global__ __launch_bounds__(SB) void sel_clear_kernel(uint32_t* hist, uint32_t* ctr, int n_hist,
                                                        int n_ctr, uint32_t* rank_hist, int n_rank,
-                                                       uint32_t* chunk_kept, int n_kept) {
+                                                       uint32_t* grp_kept, int n_kept) {
     const int i = blockIdx.x * SB + threadIdx.x;
     if (i < n_hist) hist[i] = 0u;
     if (i < n_ctr) ctr[i] = 0u;
     if (i < n_rank) rank_hist[i] = 0u;
-    if (i < n_kept) chunk_kept[i] = 0u;
+    if (i < n_kept) grp_kept[i] = 0u;
 }
 
 // ------------------------------------------------------------- launch 2 ----
-// LIN: bins linear in the score over the range of the document's first chunk
-// (published in the request's metadata for launches 3 and 4); else the top
-// 11 key bits.
-template <bool LIN>
+// The bin range comes from the document's first chunk, which every workgroup
+// reduces the same way; the last one publishes it in the request's metadata
+// for launches 3 and 4.
 __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
     __shared__ uint32_t h[NBIN];
     __shared__ uint32_t wtot[SWAVES];
-    __shared__ float red[LIN ? 5 * SWAVES : 1];
+    __shared__ float red[5 * SWAVES];
     __shared__ uint32_t sh_last, sh_d, sh_gt, sh_cnt;
     const int tid = threadIdx.x;
     const int b = find_request(a.doc_group0, a.batch, blockIdx.x);
@@ -341,8 +324,8 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
     // histogram of the current one.
     static_assert(SITEMS == 8, "two 16-byte loads per thread and chunk");
     Chunk8 nxt = load_chunk8(s, ndoc, c_lo);
-    float vlo = 0.f, scale = 0.f;
-    if constexpr (LIN) {
+    float vlo, scale;
+    {
         const Chunk8 z = c_lo == 0 ? nxt : load_chunk8(s, ndoc, 0);
         value_range<SB, SITEMS>(
             [&](int e, bool* ok) {
@@ -350,8 +333,6 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
                 return z.v[e / 4][e % 4];
             },
             red, &vlo, &scale);
-    } else {
-        __syncthreads();
     }
     for (int c = c_lo; c < c_hi; ++c) {
         const Chunk8 cur = nxt;
@@ -360,7 +341,7 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
         for (int e = 0; e < SITEMS; ++e) {
             const int i = c * SCHUNK + SITEMS * tid + e;
             const float v = cur.v[e / 4][e % 4];
-            if (i < ndoc) atomicAdd(&h[LIN ? lin_bin(v, vlo, scale) : order_key(v) >> 21], 1u);
+            if (i < ndoc) atomicAdd(&h[lin_bin(v, vlo, scale)], 1u);
         }
     }
     __syncthreads();
@@ -385,14 +366,12 @@ __global__ __launch_bounds__(SB) void sel_hist_kernel(SelArgs a) {
 }
 
 // ------------------------------------------------------------- launch 3 ----
-// BIG: the batch bins by the top key bits and ranks its candidates with every
-// workgroup afterwards (sel_rank_kernel), so the last workgroup here only
-// publishes the start of the ranking, and LDS holds just the staging list (a
-// chunk's candidates at most): four times as many workgroups per CU.  Else
-// the bins are linear in the score and the last workgroup ranks.
+// BIG: the batch ranks its candidates with every workgroup afterwards
+// (sel_rank_kernel), so the last workgroup here only publishes the start of
+// the ranking, and LDS holds just the staging list (a chunk's candidates at
+// most): four times as many workgroups per CU.  Else the last workgroup ranks.
 template <bool BIG>
 __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
-    constexpr bool LIN = !BIG;
     constexpr uint32_t CL = BIG ? (uint32_t)SCHUNK : CAND_LDS;
     __shared__ uint32_t wtot[SWAVES];
     __shared__ uint32_t sh_base, sh_last, sh_d, sh_gt, sh_cnt, sh_total;
@@ -412,12 +391,13 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     const float vlo = __uint_as_float(m[8]), scale = __uint_as_float(m[9]);
     uint2* cand = a.cand + a.off[b];
     const int c_lo = grp * a.group, c_hi = min(c_lo + a.group, nck);
-    auto bin_of = [&](float v) { return LIN ? lin_bin(v, vlo, scale) : order_key(v) >> 21; };
 
-    // Per chunk of the group: the count of keys above d1 (for its output
-    // offset), and the keys in d1 staged in LDS with their index; the group's
-    // candidates then go to the request's list with one atomic.
-    uint32_t run = 0;  // candidates staged in cl (the same in every thread)
+    // Per chunk of the group: the count of keys above d1 (summed over the
+    // group for its output offset), and the keys in d1 staged in LDS with
+    // their index; the group's candidates then go to the request's list with
+    // one atomic.
+    uint32_t run = 0;        // candidates staged in cl (the same in every thread)
+    uint32_t grp_above = 0;  // keys above d1 in the group's chunks so far
     // Move the staged candidates to the request's list (one atomic for all);
     // `more`: the list is refilled afterwards.
     auto flush = [&](bool more) {
@@ -434,7 +414,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
 #pragma unroll
         for (int e = 0; e < SITEMS; ++e) {
             cur[e] = nxt.v[e / 4][e % 4];
-            bn[e] = bin_of(cur[e]);
+            bn[e] = lin_bin(cur[e], vlo, scale);
         }
         if (c + 1 < c_hi) nxt = load_chunk8(s, ndoc, c + 1);
         uint32_t above = 0, ncand = 0;
@@ -452,7 +432,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         const uint32_t incl2 = block_incl_scan((above << 16) | ncand, wtot, &tot2);
         const uint32_t tot_above = tot2 >> 16, tot_cand = tot2 & 0xffffu;
         const uint32_t incl = incl2 & 0xffffu;
-        if (tid == 0) coherent_store(&a.chunk_def[a.doc_chunk0[b] + c], tot_above);
+        grp_above += tot_above;
         if (run + tot_cand > CL) flush(true);
         uint32_t pos = run + incl - ncand;
 #pragma unroll
@@ -463,6 +443,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         run += tot_cand;
     }
     flush(false);
+    if (tid == 0) coherent_store(&a.grp_def[a.doc_group0[b] + grp], grp_above);
     wait_own_writes();
     __syncthreads();
     if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 1], 1u) == (uint32_t)(ngrp - 1);
@@ -541,7 +522,7 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
                 const uint2 e0 = cl[o];
                 r0 += (e0.x > me.x) || (e0.x == me.x && e0.y < me.y);
             }
-            if (r0 + r1 + r2 + r3 == rem - 1) sh_t = composite_full(me.x, me.y);
+            if (r0 + r1 + r2 + r3 == rem - 1) sh_t = composite(me.x, me.y);
         }
         __syncthreads();
         cprefix = sh_t;  // the kept candidates: composite >= the rem-th best
@@ -549,13 +530,13 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
     } else {
         uint32_t cnt = cnt1;  // candidates matching the prefix fixed so far
 #pragma unroll 1
-        for (int p = 0; p < LPASS && cnt != rem; ++p) {
-            const int sh = lpass_shift(p);
-            const int nb = 1 << lpass_width(p);
+        for (int p = 0; p < NPASS && cnt != rem; ++p) {
+            const int sh = pass_shift(p);
+            const int nb = 1 << pass_width(p);
             for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
             __syncthreads();
             for_cands([&](uint2 e) {
-                const uint64_t cp = composite_full(e.x, e.y);
+                const uint64_t cp = composite(e.x, e.y);
                 if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
             });
             __syncthreads();
@@ -570,40 +551,42 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
         // prefix covers all 63 bits.
     }
 
-    // Kept candidates per chunk, then exclusive offsets of all chunks.
-    uint32_t* ccnt = h;  // reuse: up to NBIN chunks handled per round
-    const uint32_t* def = a.chunk_def + a.doc_chunk0[b];
-    uint32_t* coff = a.chunk_off + a.doc_chunk0[b];
+    // Kept candidates per chunk group, then exclusive offsets of all groups
+    // (the compaction accumulates the chunks of its group itself).
+    uint32_t* gcnt = h;  // reuse: up to NBIN groups handled per round
+    const uint32_t* gdef = a.grp_def + a.doc_group0[b];
+    uint32_t* goff = a.grp_off + a.doc_group0[b];
+    const int G = a.group;
     uint32_t carry = 0;
-    for (int c0 = 0; c0 < nck; c0 += NBIN) {
+    for (int g0 = 0; g0 < ngrp; g0 += NBIN) {
         for (int i = tid; i < NBIN; i += SB) h[i] = 0u;
         __syncthreads();
         for_cands([&](uint2 e) {
-            const int ch = (int)(e.y / SCHUNK) - c0;
-            if (ch >= 0 && ch < NBIN && (composite_full(e.x, e.y) & cmask) >= cprefix)
-                atomicAdd(&ccnt[ch], 1u);
+            const int gi = (int)(e.y / SCHUNK) / G - g0;
+            if (gi >= 0 && gi < NBIN && (composite(e.x, e.y) & cmask) >= cprefix)
+                atomicAdd(&gcnt[gi], 1u);
         });
         __syncthreads();
-        // each thread owns NBIN/SB consecutive chunks
+        // each thread owns NBIN/SB consecutive groups
         constexpr int per = NBIN / SB;
         uint32_t v[per];
         uint32_t sum = 0;
 #pragma unroll
         for (int j = 0; j < per; ++j) {
-            const int ch = c0 + tid * per + j;
-            v[j] = ch < nck ? coherent_load(&def[ch]) : 0u;
+            const int gg = g0 + tid * per + j;
+            v[j] = gg < ngrp ? coherent_load(&gdef[gg]) : 0u;
         }
 #pragma unroll
         for (int j = 0; j < per; ++j) {
-            const int ch = c0 + tid * per + j;
-            if (ch < nck) v[j] += ccnt[tid * per + j];
+            const int gg = g0 + tid * per + j;
+            if (gg < ngrp) v[j] += gcnt[tid * per + j];
             sum += v[j];
         }
         const uint32_t incl2 = block_incl_scan(sum, wtot, &sh_total);
         uint32_t run = carry + incl2 - sum;
         for (int j = 0; j < per; ++j) {
-            const int ch = c0 + tid * per + j;
-            if (ch < nck) coff[ch] = run;
+            const int gg = g0 + tid * per + j;
+            if (gg < ngrp) goff[gg] = run;
             run += v[j];
         }
         carry += sh_total;
@@ -624,7 +607,14 @@ __global__ __launch_bounds__(SB) void sel_cand_kernel(SelArgs a) {
 // RANK_WG workgroups: each histograms its share of the candidates that match
 // the prefix fixed so far (LDS, then global atomics), and the workgroup that
 // finishes last picks the digit and updates the request's prefix.  Launched
-// once per pass; a request whose rank is already fixed is skipped.
+// once per pass; a request whose rank is already fixed is skipped.  A request
+// takes one workgroup per RANK_PER_WG candidates, at most RANK_WG (the others
+// skip it), so that a few thousand candidates do not pay for hundreds of
+// histogram flushes and tickets.
+__device__ __forceinline__ uint32_t rank_workgroups(uint32_t cnt) {
+    return min((uint32_t)RANK_WG, max(1u, (cnt + RANK_PER_WG - 1) / RANK_PER_WG));
+}
+
 __global__ __launch_bounds__(SB) void sel_rank_kernel(SelArgs a, int p) {
     __shared__ uint32_t h[NBIN];
     __shared__ uint32_t wtot[SWAVES];
@@ -636,12 +626,14 @@ __global__ __launch_bounds__(SB) void sel_rank_kernel(SelArgs a, int p) {
         uint32_t* m = a.meta + b * META;
         if (m[7] != 0u) continue;  // rank already fixed by an earlier pass
         const uint32_t cnt1 = m[2];
+        const uint32_t nwg = rank_workgroups(cnt1);
+        if (blockIdx.x >= nwg) continue;
         const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
         const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
         const uint2* cand = a.cand + a.off[b];
         for (int i = tid; i < nb; i += SB) h[i] = 0u;
         __syncthreads();
-        for (uint32_t j = blockIdx.x * SB + tid; j < cnt1; j += RANK_WG * SB) {
+        for (uint32_t j = blockIdx.x * SB + tid; j < cnt1; j += nwg * SB) {
             const uint2 e = cand[j];
             const uint64_t cp = composite(e.x, e.y);
             if ((cp & cmask) == cprefix) atomicAdd(&h[(cp >> sh) & (uint64_t)(nb - 1)], 1u);
@@ -652,7 +644,7 @@ __global__ __launch_bounds__(SB) void sel_rank_kernel(SelArgs a, int p) {
             if (h[i] != 0u) atomicAdd(&gh[i], h[i]);
         wait_own_writes();
         __syncthreads();
-        if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 4 + p], 1u) == (uint32_t)(RANK_WG - 1);
+        if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 4 + p], 1u) == nwg - 1;
         __syncthreads();
         if (sh_last) {
             const uint32_t rem = m[1];
@@ -674,90 +666,80 @@ __global__ __launch_bounds__(SB) void sel_rank_kernel(SelArgs a, int p) {
     }
 }
 
-// Kept candidates per chunk (global atomics over all workgroups), then the
-// workgroup finishing last scans every chunk's kept count into its output
-// offset, as the last chunk of sel_cand does for small documents.
+// Kept candidates per chunk group (global atomics over the workgroups), then
+// the workgroup finishing last scans the groups' kept counts into their
+// output offsets, as the last chunk of sel_cand does for small documents.
 __global__ __launch_bounds__(SB) void sel_rankcount_kernel(SelArgs a) {
     __shared__ uint32_t wtot[SWAVES];
     __shared__ uint32_t sh_last, sh_total;
     const int tid = threadIdx.x;
+    const int G = a.group;
     for (int b = 0; b < a.batch; ++b) {
         if (a.doc_chunk0[b + 1] == a.doc_chunk0[b]) continue;
         const uint32_t* m = a.meta + b * META;
         const uint32_t cnt1 = m[2];
+        const uint32_t nwg = rank_workgroups(cnt1);
+        if (blockIdx.x >= nwg) continue;
         const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
         const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
         const uint2* cand = a.cand + a.off[b];
-        uint32_t* kc = a.chunk_kept + a.doc_chunk0[b];
-        // Candidates of one chunk sit next to each other in the list (each
-        // group appends its chunks' candidates in one block), so a wave's kept
-        // candidates usually span one or two chunks: one atomic per distinct
-        // chunk of the wave instead of one per candidate.
+        uint32_t* kc = a.grp_kept + a.doc_group0[b];
+        // Candidates of one group sit next to each other in the list (each
+        // group appends its candidates in one block), so a wave's kept
+        // candidates usually span one or two groups: one atomic per distinct
+        // group of the wave instead of one per candidate.
         const uint32_t lane = lane_id();
-        for (uint32_t j0 = blockIdx.x * SB; j0 < cnt1; j0 += RANK_WG * SB) {
+        for (uint32_t j0 = blockIdx.x * SB; j0 < cnt1; j0 += nwg * SB) {
             const uint32_t j = j0 + tid;
             bool kept = false;
-            uint32_t ch = 0;
+            uint32_t gi = 0;
             if (j < cnt1) {
                 const uint2 e = cand[j];
                 kept = (composite(e.x, e.y) & cmask) >= cprefix;
-                ch = e.y / SCHUNK;
+                gi = e.y / SCHUNK / (uint32_t)G;
             }
             uint64_t todo = __ballot(kept);
             while (todo != 0ull) {
                 const uint32_t lead = (uint32_t)__builtin_ctzll(todo);
-                const uint32_t lc = (uint32_t)__shfl((int)ch, (int)lead, WAVE);
-                const uint64_t same = __ballot(kept && ch == lc);
-                if (lane == lead) atomicAdd(&kc[lc], (uint32_t)__popcll(same));
+                const uint32_t lg = (uint32_t)__shfl((int)gi, (int)lead, WAVE);
+                const uint64_t same = __ballot(kept && gi == lg);
+                if (lane == lead) atomicAdd(&kc[lg], (uint32_t)__popcll(same));
                 todo &= ~same;
             }
         }
         wait_own_writes();
         __syncthreads();
-        if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 4 + NPASS], 1u) == (uint32_t)(RANK_WG - 1);
+        if (tid == 0) sh_last = atomicAdd(&a.ctr[b * CTR + 4 + NPASS], 1u) == nwg - 1;
         __syncthreads();
         if (!sh_last) continue;
-        const int nck = a.doc_chunk0[b + 1] - a.doc_chunk0[b];
-        const uint32_t* def = a.chunk_def + a.doc_chunk0[b];
-        uint32_t* coff = a.chunk_off + a.doc_chunk0[b];
-        // Thread t owns the contiguous chunks [t per, (t+1) per): their kept
-        // counts are summed in batches of loads in flight, one block scan
-        // gives each thread its start, and a second pass writes the offsets
-        // (a document of 2^26 tokens has 32768 chunks: one scan, not 16).
-        const int per = (nck + SB - 1) / SB;
-        const int cb = min(tid * per, nck), ce = min(cb + per, nck);
-        constexpr int LB = 8;  // loads in flight per array
-        auto batch = [&](int c, uint32_t* v) {
-#pragma unroll
-            for (int u = 0; u < LB; ++u) {
-                const int ch = c + u;
-                v[u] = ch < ce ? coherent_load(&kc[ch]) + coherent_load(&def[ch]) : 0u;
-            }
-        };
+        const int ngrp = a.doc_group0[b + 1] - a.doc_group0[b];  // at most MAX_GROUPS
+        const uint32_t* gdef = a.grp_def + a.doc_group0[b];
+        uint32_t* goff = a.grp_off + a.doc_group0[b];
+        // Thread t owns the contiguous groups [t per, (t+1) per), per <= 8:
+        // one batch of loads, one block scan.
+        const int per = (ngrp + SB - 1) / SB;
+        const int cb = min(tid * per, ngrp), ce = min(cb + per, ngrp);
+        constexpr int LB = MAX_GROUPS / SB;
+        uint32_t v[LB];
         uint32_t sum = 0;
-        for (int c = cb; c < ce; c += LB) {
-            uint32_t v[LB];
-            batch(c, v);
 #pragma unroll
-            for (int u = 0; u < LB; ++u) sum += v[u];
+        for (int u = 0; u < LB; ++u) {
+            const int gg = cb + u;
+            v[u] = gg < ce ? coherent_load(&kc[gg]) + coherent_load(&gdef[gg]) : 0u;
+            sum += v[u];
         }
         const uint32_t incl = block_incl_scan(sum, wtot, &sh_total);
         uint32_t run = incl - sum;
-        for (int c = cb; c < ce; c += LB) {
-            uint32_t v[LB];
-            batch(c, v);
 #pragma unroll
-            for (int u = 0; u < LB; ++u) {
-                if (c + u < ce) coff[c + u] = run;
-                run += v[u];
-            }
+        for (int u = 0; u < LB; ++u) {
+            if (cb + u < ce) goff[cb + u] = run;
+            run += v[u];
         }
         __syncthreads();
     }
 }
 
 // ------------------------------------------------------------- launch 4 ----
-template <bool LIN>
 __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     __shared__ uint32_t wtot[SWAVES];
     const int tid = threadIdx.x;
@@ -781,6 +763,10 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
     // one is written.
     Chunk8 nxt = {};
     if (doc) nxt = load_chunk8(s, ndoc, c_lo);
+    // Output position of the next kept document token of this group: the
+    // group's offset, then the kept tokens of its chunks so far.
+    uint32_t run_off = 0;
+    bool have_off = false;
     for (int c = c_lo; c < c_hi; ++c) {  // the chunks of this group, in order
         const Chunk8 cur = nxt;
         if (doc && c + 1 < c_hi) nxt = load_chunk8(s, ndoc, c + 1);
@@ -809,7 +795,10 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
         const uint64_t cprefix = (uint64_t)m[3] | ((uint64_t)m[4] << 32);
         const uint64_t cmask = (uint64_t)m[5] | ((uint64_t)m[6] << 32);
         const float vlo = __uint_as_float(m[8]), scale = __uint_as_float(m[9]);
-        const uint32_t base = a.chunk_off[a.doc_chunk0[b] + c];
+        if (!have_off) {  // the first document chunk of this group
+            run_off = a.grp_off[a.doc_group0[b] + grp];
+            have_off = true;
+        }
         const int i0 = lo + SITEMS * tid;
         uint32_t km = 0u;
 #pragma unroll
@@ -818,14 +807,15 @@ __global__ __launch_bounds__(SB) void sel_compact_kernel(SelArgs a) {
             if (i < ndoc) {
                 const float v = cur.v[e / 4][e % 4];
                 const uint32_t key = order_key(v);
-                const uint32_t dg = LIN ? lin_bin(v, vlo, scale) : key >> 21;
-                if (dg > d1 || (dg == d1 && (rank_key<LIN>(key, (uint32_t)i) & cmask) >= cprefix))
+                const uint32_t dg = lin_bin(v, vlo, scale);
+                if (dg > d1 || (dg == d1 && (composite(key, (uint32_t)i) & cmask) >= cprefix))
                     km |= 1u << e;
             }
         }
         const uint32_t n = (uint32_t)__popc(km);
         uint32_t tot;
-        uint32_t pos = base + block_incl_scan(n, wtot, &tot) - n;
+        uint32_t pos = run_off + block_incl_scan(n, wtot, &tot) - n;
+        run_off += tot;
 #pragma unroll
         for (int e = 0; e < SITEMS; ++e) {
             if ((km >> e) & 1u) {
@@ -848,7 +838,7 @@ WsLayout ws_layout(int batch, int doc_chunks, int64_t T) {
     L.hist = p; p = align256(p + (size_t)batch * NBIN * 4);
     L.meta = p; p = align256(p + (size_t)batch * META * 4);
     L.ctr = p;  p = align256(p + (size_t)batch * CTR * 4);
-    L.def = p;  p = align256(p + (size_t)doc_chunks * 4);
+    L.def = p;  p = align256(p + (size_t)doc_chunks * 4);  // per group (groups <= chunks)
     L.off = p;  p = align256(p + (size_t)doc_chunks * 4);
     L.cand = p; p = align256(p + (size_t)T * 8);
     L.rank = p; p = align256(p + (size_t)batch * NPASS * NBIN * 4);
@@ -1379,11 +1369,11 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
     s.hist = (uint32_t*)(base + L.hist);
     s.meta = (uint32_t*)(base + L.meta);
     s.ctr = (uint32_t*)(base + L.ctr);
-    s.chunk_def = (uint32_t*)(base + L.def);
-    s.chunk_off = (uint32_t*)(base + L.off);
+    s.grp_def = (uint32_t*)(base + L.def);
+    s.grp_off = (uint32_t*)(base + L.off);
     s.cand = (uint2*)(base + L.cand);
     s.rank_hist = (uint32_t*)(base + L.rank);
-    s.chunk_kept = (uint32_t*)(base + L.kept);
+    s.grp_kept = (uint32_t*)(base + L.kept);
     s.big = 0;
     for (int b = 0; b < a.batch; ++b)
         if (s.doc_chunk0[b + 1] > s.doc_chunk0[b] &&
@@ -1391,15 +1381,13 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
             s.big = 1;
     if (dc > 0) {
         const int n_hist = a.batch * NBIN, n_ctr = a.batch * CTR;
-        const int n_rank = s.big ? a.batch * NPASS * NBIN : 0, n_kept = s.big ? dc : 0;
+        const int n_rank = s.big ? a.batch * NPASS * NBIN : 0;
+        const int n_kept = s.big ? s.doc_group0[a.batch] : 0;
         const int n_clear = std::max(std::max(n_hist, n_ctr), std::max(n_rank, n_kept));
         hipLaunchKernelGGL(sel_clear_kernel, dim3((n_clear + SB - 1) / SB), dim3(SB), 0, st, s.hist,
-                           s.ctr, n_hist, n_ctr, s.rank_hist, n_rank, s.chunk_kept, n_kept);
+                           s.ctr, n_hist, n_ctr, s.rank_hist, n_rank, s.grp_kept, n_kept);
         const int dg = s.doc_group0[a.batch];
-        if (s.big)
-            hipLaunchKernelGGL(sel_hist_kernel<false>, dim3(dg), dim3(SB), 0, st, s);
-        else
-            hipLaunchKernelGGL(sel_hist_kernel<true>, dim3(dg), dim3(SB), 0, st, s);
+        hipLaunchKernelGGL(sel_hist_kernel, dim3(dg), dim3(SB), 0, st, s);
         if (s.big)
             hipLaunchKernelGGL(sel_cand_kernel<true>, dim3(dg), dim3(SB), 0, st, s);
         else
@@ -1410,12 +1398,8 @@ hipError_t launch_select(const float* scores, const BatchArgs& a, int32_t* kept,
             hipLaunchKernelGGL(sel_rankcount_kernel, dim3(RANK_WG), dim3(SB), 0, st, s);
         }
     }
-    if (s.all_group0[a.batch] > 0) {
-        if (s.big)
-            hipLaunchKernelGGL(sel_compact_kernel<false>, dim3(s.all_group0[a.batch]), dim3(SB), 0, st, s);
-        else
-            hipLaunchKernelGGL(sel_compact_kernel<true>, dim3(s.all_group0[a.batch]), dim3(SB), 0, st, s);
-    }
+    if (s.all_group0[a.batch] > 0)
+        hipLaunchKernelGGL(sel_compact_kernel, dim3(s.all_group0[a.batch]), dim3(SB), 0, st, s);
     return hipGetLastError();
 }
 
