@@ -224,7 +224,17 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     // MFMAs by hand, slice by slice; eight waves (one workgroup per CU) leave
     // the interleave to scheduling groups, which measures faster there.
     constexpr bool FUSED = NWAVE == 4;
-    constexpr int NKB = 2;  // K buffers
+    // Staging distance and LDS buffers.  The four-wave kernels stage K one
+    // tile ahead (V of the current tile) into two buffers each and take a
+    // barrier after every step.  The eight-wave kernel (one workgroup per CU,
+    // room for more LDS) stages K two tiles ahead and V one ahead into four
+    // buffers each and takes a barrier after every second step: a tile
+    // written in step s is first read in step s + 2, always after the next
+    // barrier, and each buffer it overwrites was last read before the
+    // previous one.  Waves then meet half as often.
+    constexpr int AHEAD = NWAVE == 8 ? 2 : 1;
+    constexpr int NKB = 2 * AHEAD;  // K buffers
+    constexpr int NVB = 2 * AHEAD;  // V buffers
     // A split piece needs every wave's rows inside the tile's last key tile
     // (at most 64 query rows per head), so that only the last piece masks.
     static_assert(!SPLIT || (NWAVE == 4 && BQ <= KVT), "key split: four waves, <= 64 rows per head");
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     // 16-byte read.
     constexpr bool VTR = NWAVE == 4;
     constexpr int VS = vs_stride<DH>();
-    __shared__ __attribute__((aligned(16))) bf16 Vt[2][VTR ? KVT * VS : DH * VT_STRIDE];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[NVB][VTR ? KVT * VS : DH * VT_STRIDE];
 
     const int tid = threadIdx.x;
     const int lane = lane_id();
@@ -605,7 +615,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     } while (0)
 #define TG_PVSM(MASKED)                                                                      \
     do {                                                                                     \
-        const int vb = (jt - 1) & 1;                                                         \
+        const int vb = (jt - 1) & (NVB - 1);                                                 \
         const int j0 = jt * KVT;                                                             \
         bf16x8 v0[NMD];                                                                      \
         _Pragma("unroll") for (int md = 0; md < NMD; ++md) v0[md] = TG_VFRAG(md);            \
@@ -640,7 +650,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
          : as_bf16x8(ld16(&Vt[vb][(32 * ((I) % NMD) + l32) * VT_STRIDE + 16 * ((I) / NMD) + 8 * hh])))
 #define TG_PVSM_FUSED(MASKED)                                                                \
     do {                                                                                     \
-        const int vb = (jt - 1) & 1;                                                         \
+        const int vb = (jt - 1) & (NVB - 1);                                                 \
         const int j0 = jt * KVT;                                                             \
         bf16x8 vq[4];                                                                        \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) vq[i] = TG_VFRAG(i);                   \
@@ -662,20 +672,21 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
         TG_SOFTMAX_TAIL();                                                                   \
     } while (0)
 
-    // One step of the workgroup: stage K(jt+1) and V(jt) around BODY.
-    // Every wave takes nkv + 1 steps, each ending in one barrier.
+    // One step of the workgroup: stage K(jt+AHEAD) and V(jt+AHEAD-1) around
+    // BODY.  Every wave takes nkv + 1 steps; a barrier ends every step (four
+    // waves) or every second one (eight waves).
     int jt = jbeg;
-#define TG_STEP(BODY)                                     \
-    do {                                                  \
-        const bool knext = jt + 1 < jend;                 \
-        const bool vnow = jt < jend;                      \
-        BODY;                                             \
-        if (knext) store_k((jt + 1) % NKB);               \
-        if (vnow) store_v(jt & 1);                        \
-        __syncthreads();                                  \
-        ++jt;                                             \
+#define TG_STEP(BODY)                                               \
+    do {                                                            \
+        const bool knext = jt + AHEAD < jend;                       \
+        const bool vnow = jt + AHEAD - 1 < jend;                    \
+        BODY;                                                       \
+        if (knext) store_k((jt + AHEAD) % NKB);                     \
+        if (vnow) store_v((jt + AHEAD - 1) % NVB);                  \
+        if (AHEAD == 1 || ((jt - jbeg) & 1)) __syncthreads();       \
+        ++jt;                                                       \
     } while (0)
-#define TG_LD(i) load_part((i), knext, jt + 1, vnow, jt)
+#define TG_LD(i) load_part((i), knext, jt + AHEAD, vnow, jt + AHEAD - 1)
 #define TG_LD_ALL() do { TG_LD(0); TG_LD(1); TG_LD(2); TG_LD(3); } while (0)
 
     // Tiles strictly before this wave's rows need no mask; the tile holding
@@ -699,6 +710,15 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     load_part(2, true, jbeg, false, 0);
     load_part(3, true, jbeg, false, 0);
     store_k(jbeg % NKB);
+    if (AHEAD == 2) {  // the first epoch also reads K(jbeg+1) and V(jbeg)
+        const bool k1 = jbeg + 1 < jend;
+        load_part(0, k1, jbeg + 1, true, jbeg);
+        load_part(1, k1, jbeg + 1, true, jbeg);
+        load_part(2, k1, jbeg + 1, true, jbeg);
+        load_part(3, k1, jbeg + 1, true, jbeg);
+        if (k1) store_k((jbeg + 1) % NKB);
+        store_v(jbeg % NVB);
+    }
     __syncthreads();
     if (jlast == jbeg) {
         if (mlast) TG_STEP({ TG_QK(jt, TG_LD); TG_SOFTMAX_FIRST(true); });
@@ -718,7 +738,7 @@ __global__ __launch_bounds__(64 * NWAVE, 8 / NWAVE) void attn_bf16_kernel(AttnAr
     TG_STEP({
         TG_LD_ALL();
         TG_RESCALE();
-        const int vb = (jt - 1) & 1;
+        const int vb = (jt - 1) & (NVB - 1);
         _Pragma("unroll") for (int i = 0; i < NPV; ++i) o[i % NMD] = mfma32(TG_VFRAG(i), pold[i / NMD], o[i % NMD]);
     });
     while (jt <= jend) TG_STEP(TG_LD_ALL());
