@@ -38,7 +38,6 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr int BW = 4;            // waves per workgroup
 constexpr int BT = BW * WAVE;
 constexpr int TB = 32;           // rows per wave (keys or queries) and per tile
-constexpr int TPAD = TB + 4;     // transposed tile row: 32 rows + pad, 8-byte aligned
 constexpr int BWD_MAX_GROUP = 64;  // query heads per KV head (Hq / Hkv) supported
 
 struct BwdArgs {
@@ -87,14 +86,29 @@ __device__ __forceinline__ void load_rows(const bf16* base, int64_t row_stride, 
     for (int t = 0; t < DH / 16; ++t) r[t] = ok ? ld16(p + 16 * t) : u32x4{0u, 0u, 0u, 0u};
 }
 
-// A operand read from a transposed LDS tile T[dh][TPAD] for the contraction
-// over its 32 columns in the C-register order of k-block c: slots 0..3 are
-// columns 16c + 4*(lane/32) + 0..3, slots 4..7 are 16c + 8 + 4*(lane/32) + 0..3.
-__device__ __forceinline__ bf16x8 lds_t_operand(const bf16* T, int dh_row, int c, int lane) {
-    const bf16* p = T + dh_row * TPAD + 16 * c + 4 * (lane / 32);
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
-    return as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+// A operand for a contraction over the 32 rows (keys or queries) of a
+// row-major LDS tile T[TB][RT]: rows 32m + (lane % 32) of the head
+// dimension, rows 16c + 4(lane / 32) + {0..3} and 16c + 8 + 4(lane / 32) +
+// {0..3} of the tile (the order of the C registers that feed the B
+// operand).  gfx950's transposing LDS read returns, in each group of 16
+// lanes where lane i points at four values of one row, to lane j value j % 4
+// of the rows that lanes j/4, j/4 + 4, j/4 + 8 and j/4 + 12 point at; so
+// lane i of a group points at tile row 4(lane / 32) + i/4 and head dims
+// 16 (group % 2) + 4 (i % 4), and two reads, eight rows apart, give the
+// operand.  A row stride of DH + 32 (16 or 48 dwords modulo 64 banks) keeps
+// the four rows a half-wave reads on disjoint banks.
+template <int DH>
+constexpr int tr_stride() { return DH + 32; }
+template <int RT>
+__device__ __forceinline__ bf16x8 lds_tr_operand(const bf16* T, int m, int c, int lane) {
+    typedef short v4i16_t __attribute__((ext_vector_type(4)));
+    const int off = (4 * (lane / 32) + (lane % 16) / 4) * RT + 16 * ((lane / 16) % 2) + 4 * (lane % 4);
+    const bf16* p0 = T + (16 * c) * RT + 32 * m + off;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p0);
+    const v4i16_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p0 + 8 * RT));
+    const u32x2 x = __builtin_bit_cast(u32x2, lo), y = __builtin_bit_cast(u32x2, hi);
+    return as_bf16x8(u32x4{x[0], x[1], y[0], y[1]});
 }
 
 // D[h][i] = dO_i . O_i over DH: DH/8 lanes per (row, head), 16 bytes each,
@@ -120,12 +134,15 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
 // Staging of two 32-row tiles (`mats` row-major [rows][stride] bf16
 // matrices, DH columns each) for one pipeline step: every thread fetches
 // PER 16-byte segments into registers, then writes them into an LDS buffer,
-// row-major (padded rows, for row-form operands) and, for the first
-// `ntrans` matrices, transposed (for operands that contract over the rows).
+// row-major with rows of RP (row-form operands: conflict-free 16-byte
+// reads) and, for the first `ntrans` matrices, a second row-major copy with
+// rows of RT (operands that contract over the rows, read by transposing
+// reads).  All stores are 16 bytes.
 template <int DH>
 struct TileStage {
     static constexpr int SEGS = DH / 8;
     static constexpr int RP = DH + 8;               // padded row-major row (bf16)
+    static constexpr int RT = tr_stride<DH>();      // row of the copy read transposed
     static constexpr int PER = 2 * TB * SEGS / BT;  // segments per thread
     u32x4 r[PER];
 
@@ -143,7 +160,7 @@ struct TileStage {
             r[u] = ld16(base + (int64_t)row * stride + seg * 8);
         }
     }
-    // rm: [2][TB*RP] row-major tiles; tr: [ntrans][DH*TPAD] transposed tiles
+    // rm: [2][TB*RP] row-major tiles; tr: [ntrans][TB*RT] their second copies
     __device__ __forceinline__ void put(bf16* rm, bf16* tr, int ntrans, int tid) const {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
@@ -151,12 +168,7 @@ struct TileStage {
             const int mat = idx / (TB * SEGS), rem = idx % (TB * SEGS);
             const int rr = rem % TB, seg = rem / TB;
             st16(rm + mat * TB * RP + rr * RP + seg * 8, r[u]);
-            if (mat < ntrans) {
-                const bf16x8 hv = as_bf16x8(r[u]);
-                bf16* t = tr + mat * DH * TPAD + seg * 8 * TPAD + rr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) t[e * TPAD] = hv[e];
-            }
+            if (mat < ntrans) st16(tr + mat * TB * RT + rr * RT + seg * 8, r[u]);
         }
     }
 };
@@ -176,8 +188,9 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
     constexpr int MT = DH / 32;   // 32-row output tiles over the head dimension
     using Stage = TileStage<DH>;
     constexpr int RP = Stage::RP;
+    constexpr int RT = Stage::RT;
     __shared__ __align__(16) bf16 Rm[2][2 * TB * RP];     // [buffer] Q | dO, row-major
-    __shared__ __align__(16) bf16 Tr[2][2 * DH * TPAD];   // [buffer] Q^T | dO^T
+    __shared__ __align__(16) bf16 Tr[2][2 * TB * RT];     // [buffer] Q | dO, copies read transposed
     __shared__ float lse2[2][TB], Dq[2][TB];
     __shared__ float s_tau[BWD_MAX_GROUP], s_gain[BWD_MAX_GROUP];
     __shared__ float s_gt[BW][BWD_MAX_GROUP][2];  // per wave and head: (dgain, dtemp) sums
@@ -292,15 +305,14 @@ __global__ __launch_bounds__(BT) void bwd_kv_kernel(BwdArgs a) {
                 dt_acc = fmaf(dl, S[r] * a.inv_sqrt_dh, dt_acc);
             }
             const bf16* qt = Tr[buf];
-            const bf16* ot = Tr[buf] + DH * TPAD;
+            const bf16* ot = Tr[buf] + TB * RT;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const bf16x8 pb = pack8(P + 8 * c), sb = pack8(dS + 8 * c);
 #pragma unroll
                 for (int m = 0; m < MT; ++m) {
-                    const int row = 32 * m + col;
-                    dvT[m] = mfma32(lds_t_operand(ot, row, c, lane), pb, dvT[m]);
-                    dkT[m] = mfma32(lds_t_operand(qt, row, c, lane), sb, dkT[m]);
+                    dvT[m] = mfma32(lds_tr_operand<RT>(ot, m, c, lane), pb, dvT[m]);
+                    dkT[m] = mfma32(lds_tr_operand<RT>(qt, m, c, lane), sb, dkT[m]);
                 }
             }
         }
@@ -346,8 +358,9 @@ __global__ __launch_bounds__(BT, 2) void bwd_q_kernel(BwdArgs a) {
     constexpr int MT = DH / 32;
     using Stage = TileStage<DH>;
     constexpr int RP = Stage::RP;
+    constexpr int RT = Stage::RT;
     __shared__ __align__(16) bf16 Rm[2][2 * TB * RP];  // [buffer] K | V, row-major
-    __shared__ __align__(16) bf16 Tr[2][DH * TPAD];    // [buffer] K^T
+    __shared__ __align__(16) bf16 Tr[2][TB * RT];      // [buffer] K, the copy read transposed
     __shared__ float sb2[2][TB];
 
     // Consecutive workgroup ids cycle over the KV heads (the workgroups of one
@@ -437,7 +450,7 @@ __global__ __launch_bounds__(BT, 2) void bwd_q_kernel(BwdArgs a) {
                 const bf16x8 sbv = pack8(dS + 8 * c);
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
-                    dqT[m] = mfma32(lds_t_operand(Tr[buf], 32 * m + col, c, lane), sbv, dqT[m]);
+                    dqT[m] = mfma32(lds_tr_operand<RT>(Tr[buf], m, c, lane), sbv, dqT[m]);
             }
         }
         if (it + 1 < iters) put(buf ^ 1);
