@@ -108,13 +108,24 @@ def main():
     a = ap.parse_args()
 
     stats = _csv(a.trace, "kernel_stats.csv")
+    # Per-call durations from the trace, for the median (the average also
+    # holds the first calls, made while the chip's clocks still ramp up).
+    durs = collections.defaultdict(list)
+    try:
+        for r in _csv(a.trace, "kernel_trace.csv"):
+            durs[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    except (FileNotFoundError, KeyError, ValueError):
+        durs.clear()
     lines = [f"# Kernel time: {a.workload}", "",
-             "rocprofv3 kernel-trace statistics (`--kernel-trace --stats --output-format csv`).", "",
+             "rocprofv3 kernel-trace statistics (`--kernel-trace --stats --output-format csv`); "
+             "the median is over the per-call durations of the trace.", "",
              "Command (from the repository root):", "", "```", a.command, "```", "",
-             "| kernel | calls | average us | min us | max us | share |",
-             "|---|---|---|---|---|---|"]
+             "| kernel | calls | average us | median us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|"]
     for r in stats:
-        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+        d = sorted(durs.get(r["Name"], []))
+        med = f"{d[len(d) // 2] / 1e3:.1f}" if d else "-"
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {med} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f}% |")
     open(a.out + "_kernel_stats.md", "w").write("\n".join(lines) + "\n")
