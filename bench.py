@@ -322,7 +322,8 @@ def backward_bench(args):
                          ["bwd_dot_kernel", "bwd_kv_kernel", "bwd_q_kernel", "bwd_reduce_kernel"]),
                      "kernel": "attention backward (dot, KV pass, Q pass, reduce; one call)",
                      "algorithmic_flops_per_call": flops},
-        "ms_call": {"mean": mean, "median": sorted(ms)[len(ms) // 2], "min": min(ms)},
+        "ms_call": {"mean": mean, "median": sorted(ms)[len(ms) // 2], "min": min(ms),
+                    "all": [round(x, 4) for x in ms]},
         "gate_backward": {"ms": gms, "TFLOP/s": gflops / (gms * 1e-3) / 1e12,
                           "note": "gate MLP backward on the 8192 kept rows (three products on the "
                                   "projection kernel, dz and column sums), fed this call's ds"},

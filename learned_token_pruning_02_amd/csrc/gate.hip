@@ -103,18 +103,23 @@ __global__ __launch_bounds__(64 * WAVES, OCC) void gate_bf16_kernel(
         if (r > T - 1) r = T - 1;
         arow[mt] = hidden + r * d + 32 * hh;
     }
-    // W1 chunk staging: 16-byte unit u = tid + i*THREADS of a chunk is row
-    // u/8, column 8*(u%8) (coalesced rows).  It lands in the fragment-major LDS
-    // layout (fragment f = nt*4 + kk, 64 lanes of 16 bytes) at position
-    // lane ^ swz(kk, half) with swz = 2*kk + 8*half: a bijection on the low
-    // four position bits, so the fragment reads stay conflict-free, while the
-    // 16 lanes of every write group (two rows x four kk x two halves) land on
-    // 16 distinct bank quads.
+    // W1 chunk staging: each wave stores 8 rows x 8 sixteen-byte columns of a
+    // chunk per round (rows r0 + R*i, column 8*c0).  It lands in the
+    // fragment-major LDS layout (fragment f = nt*4 + kk, 64 lanes of 16 bytes)
+    // at position lane ^ swz(kk, half) with swz = 2*kk + 8*half: a bijection
+    // on the low four position bits, so the fragment reads stay
+    // conflict-free.  The LDS takes a 16-byte store eight lanes at a time
+    // over 32 four-byte banks, so each group of eight lanes holds two rows x
+    // four kk of one half (positions distinct modulo 8), and each group of
+    // sixteen lanes both halves (distinct modulo 16); one row per group of
+    // eight lanes, as a row-major assignment gives, hits each bank quad twice
+    // (measured: SQ_LDS_BANK_CONFLICT 4.3 M cycles per 128k call, now none).
     constexpr int THREADS = 64 * WAVES;
     constexpr int WUNITS = NFRAG * WAVE / THREADS;
     constexpr int R = THREADS / 8;
     static_assert(32 % R == 0 || R % 32 == 0, "rows per staging round");
-    const int r0 = threadIdx.x / 8, c0 = threadIdx.x % 8;
+    const int wv_ = threadIdx.x / WAVE, l_ = threadIdx.x % WAVE;
+    const int r0 = 8 * wv_ + 2 * (l_ / 16) + (l_ % 8) / 4, c0 = (l_ % 4) + 4 * ((l_ % 16) / 8);
     const bf16* wbase = w1 + (int64_t)r0 * d + 8 * c0;
     const int wkk = c0 % 4, whq = c0 / 4;
     auto wpos = [&](int i) {
