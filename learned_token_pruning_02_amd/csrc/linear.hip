@@ -73,11 +73,27 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
     struct Regs {
         u32x4 x[XU], w[WU];
     };
+    // Row and 16-byte column of staging unit uu.  The LDS takes a 16-byte
+    // store eight lanes at a time over 32 four-byte banks.  With 32-wide k
+    // chunks (four units per 80-byte row) eight consecutive lanes store two
+    // rows four apart, whose units fall on disjoint bank quads; two adjacent
+    // rows would share one quad.  With 64-wide chunks a row is eight units.
+    auto unit_rc = [&](int uu, int& row, int& c) {
+        if constexpr (LK / 8 == 4) {
+            const int q = uu / 32, l = uu % 32, g = l / 8, j = l % 8;
+            row = 8 * q + g + 4 * (j / 4);
+            c = j % 4;
+        } else {
+            row = uu / (LK / 8);
+            c = uu % (LK / 8);
+        }
+    };
     auto load = [&](Regs& r, int k0) {
 #pragma unroll
         for (int i = 0; i < XU; ++i) {
             const int uu = tid + i * THREADS;
-            const int row = uu / (LK / 8), c = uu % (LK / 8);
+            int row, c;
+            unit_rc(uu, row, c);
             int64_t mr = m0 + row;
             if (mr > M - 1) mr = M - 1;
             r.x[i] = ld16(x + mr * ldk + k0 + 8 * c);
@@ -85,7 +101,8 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
 #pragma unroll
         for (int i = 0; i < WU; ++i) {
             const int uu = tid + i * THREADS;
-            const int row = uu / (LK / 8), c = uu % (LK / 8);
+            int row, c;
+            unit_rc(uu, row, c);
             int nr = n0 + row;
             if (nr > N - 1) nr = N - 1;
             r.w[i] = ld16(w + (int64_t)nr * ldk + k0 + 8 * c);
@@ -94,13 +111,15 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
     auto store = [&](const Regs& r, int buf) {
 #pragma unroll
         for (int i = 0; i < XU; ++i) {
-            const int uu = tid + i * THREADS;
-            st16(&Xs[buf][(uu / (LK / 8)) * LS + 8 * (uu % (LK / 8))], r.x[i]);
+            int row, c;
+            unit_rc(tid + i * THREADS, row, c);
+            st16(&Xs[buf][row * LS + 8 * c], r.x[i]);
         }
 #pragma unroll
         for (int i = 0; i < WU; ++i) {
-            const int uu = tid + i * THREADS;
-            st16(&Ws[buf][(uu / (LK / 8)) * LS + 8 * (uu % (LK / 8))], r.w[i]);
+            int row, c;
+            unit_rc(tid + i * THREADS, row, c);
+            st16(&Ws[buf][row * LS + 8 * c], r.w[i]);
         }
     };
 
