@@ -137,7 +137,11 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(BwdArgs a) {
 // row-major with rows of RP (row-form operands: conflict-free 16-byte
 // reads) and, for the first `ntrans` matrices, a second row-major copy with
 // rows of RT (operands that contract over the rows, read by transposing
-// reads).  All stores are 16 bytes.
+// reads).  All stores are 16 bytes.  Consecutive threads take consecutive
+// segments of a row: the LDS takes a 16-byte store eight lanes at a time over
+// 32 four-byte banks, and eight segments of one row fall on eight distinct
+// bank quads in both copies (eight rows of one segment, at RT = DH + 32,
+// would share two quads).
 template <int DH>
 struct TileStage {
     static constexpr int SEGS = DH / 8;
@@ -154,7 +158,7 @@ struct TileStage {
         for (int u = 0; u < PER; ++u) {
             const int idx = tid + BT * u;
             const int mat = idx / (TB * SEGS), rem = idx % (TB * SEGS);
-            const int rr = rem % TB, seg = rem / TB;
+            const int rr = rem / SEGS, seg = rem % SEGS;
             const int row = min(row0 + rr, rows - 1);
             const bf16* base = mat == 0 ? m0 : m1;
             r[u] = ld16(base + (int64_t)row * stride + seg * 8);
@@ -166,7 +170,7 @@ struct TileStage {
         for (int u = 0; u < PER; ++u) {
             const int idx = tid + BT * u;
             const int mat = idx / (TB * SEGS), rem = idx % (TB * SEGS);
-            const int rr = rem % TB, seg = rem / TB;
+            const int rr = rem / SEGS, seg = rem % SEGS;
             st16(rm + mat * TB * RP + rr * RP + seg * 8, r[u]);
             if (mat < ntrans) st16(tr + mat * TB * RT + rr * RT + seg * 8, r[u]);
         }
