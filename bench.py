@@ -439,13 +439,13 @@ def layer_bench(args):
     layer.positions(kept.cuda(), cu_s, cu_k)
     st = torch.cuda.current_stream()
     theta, eps = layer.theta, layer.eps
-    names = ["in_norm", "q_proj", "k_proj", "v_proj", "qk_norm_rope", "attention", "o_proj",
+    names = ["in_norm", "qkv_proj", "qk_norm_rope", "attention", "o_proj",
              "post_norm", "gate_up", "silu_mul", "down"]
     calls = [
         lambda: tg.tg_rmsnorm(x, L["in_norm"], eps, y=layer.xn, stream=st),
-        lambda: tg.tg_linear(layer.xn, L["wq"], y=layer.q.view(Kt, -1), stream=st),
-        lambda: tg.tg_linear(layer.xn, L["wk"], y=layer.k.view(Kt, -1), stream=st),
-        lambda: tg.tg_linear(layer.xn, L["wv"], y=layer.v.view(Kt, -1), stream=st),
+        lambda: tg.tg_linear_multi(layer.xn, [L["wq"], L["wk"], L["wv"]],
+                                   ys=[layer.q.view(Kt, -1), layer.k.view(Kt, -1), layer.v.view(Kt, -1)],
+                                   stream=st),
         lambda: tg.tg_qk_norm_rope(layer.q, layer.k, L["q_norm"], L["k_norm"], layer.pos, theta, eps,
                                    stream=st),
         lambda: tg.tg_gated_attn_prefill(layer.q, layer.k, layer.v, s, L["gain"], L["temp"], cu_k,
@@ -472,7 +472,7 @@ def layer_bench(args):
     per = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
     step_ms = sum(e[0].elapsed_time(e[-1]) for e in evs) / args.steps
     d, hq, hkv, dh = sh.d_model, sh.n_q_heads, sh.n_kv_heads, sh.d_head
-    flops = {"q_proj": 2 * Kt * d * hq * dh, "k_proj": 2 * Kt * d * hkv * dh, "v_proj": 2 * Kt * d * hkv * dh,
+    flops = {"qkv_proj": 2 * Kt * d * (hq + 2 * hkv) * dh,
              "o_proj": 2 * Kt * hq * dh * d, "gate_up": 2 * Kt * d * 2 * F, "down": 2 * Kt * F * d,
              "attention": 4 * dh * hq * Kt * (Kt + 1) // 2}
     eb = 2

@@ -542,6 +542,32 @@ tg_status tg_linear(tg_dtype dt, const void *x, const void *w, void *y, int64_t 
 tg_status tg_linear_tile(tg_dtype dt, const void *x, const void *w, void *y, int64_t M,
                          int32_t N, int32_t K, int accumulate, int tile, hipStream_t stream);
 
+/* Most products of one tg_linear_multi call. */
+#define TG_LINEAR_MAX_SEG 3
+
+/*
+ * tg_linear_multi -- several projections of the same rows in one launch:
+ * the q, k and v projections of a layer above the gate, run on the kept
+ * rows only (spke.com page, three-phase list, third bullet).  For i < nseg:
+ *     y_i[M][n_i] (+)= x[M][K] . w_i[n_i][K]^T
+ * with accumulate as for tg_linear, fp32 accumulation and one rounding to dt
+ * at the store.  x : [M][K] device; w, y : HOST arrays of nseg device
+ * pointers (w_i [n_i][K], y_i [M][n_i], each contiguous); n : HOST array of
+ * the nseg sizes; 1 <= nseg <= TG_LINEAR_MAX_SEG.  The bf16 products share
+ * one grid whose output tile is chosen from M and the sum of the n_i as
+ * tg_linear chooses it (tile: 0, or 1-3 to force one as in tg_linear_tile);
+ * each y_i is bit-identical to tg_linear_tile of the same product with that
+ * tile.  TG_F32 runs the products one after another.
+ * Supported: TG_BF16 with K % 64 == 0 and every n_i a multiple of 256 (of
+ * 64 when nseg == 1); TG_F32 with K % 4 == 0.  M == 0 is a no-op.
+ * Errors: TG_ERR_BAD_DTYPE, TG_ERR_BAD_SHAPE (nseg, M, K, n_i, tile),
+ * TG_ERR_NULL_PTR, TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT, TG_ERR_ALIAS (an
+ * output overlapping x, a weight or another output), TG_ERR_LAUNCH.
+ */
+tg_status tg_linear_multi(tg_dtype dt, const void *x, int32_t nseg, const void *const *w,
+                          void *const *y, const int32_t *n, int64_t M, int32_t K, int accumulate,
+                          int tile, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,7 @@ __all__ = [
     "tg_decode_plan",
     "tg_gated_attn_decode",
     "tg_rmsnorm",
+    "tg_linear_multi",
     "tg_kept_positions",
     "tg_qk_norm_rope",
     "tg_silu_mul",
@@ -161,6 +162,9 @@ def lib() -> ctypes.CDLL:
     L.tg_linear.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
     L.tg_linear_tile.restype = ctypes.c_int
     L.tg_linear_tile.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp]
+    L.tg_linear_multi.restype = ctypes.c_int
+    L.tg_linear_multi.argtypes = [ctypes.c_int, vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), p_i32,
+                                  i64, i32, ctypes.c_int, ctypes.c_int, vp]
     _lib = L
     return L
 
@@ -669,3 +673,36 @@ def tg_linear(x, w, y=None, accumulate: bool = False, stream=None, tile: int = 0
     else:
         _check("tg_linear", lib().tg_linear(*args, _stream(stream)))
     return y
+
+
+def tg_linear_multi(x, ws, ys=None, accumulate: bool = False, stream=None, tile: int = 0):
+    """ys[i] = x ws[i]^T (or += with accumulate=True) for up to three weights
+    in Linear layout [N_i][K], in one launch (the q, k and v projections).
+    Returns the list of outputs.  tile as in tg_linear."""
+    torch = _torch()
+    _ndim(x, "x", 2)
+    M, K = x.shape
+    ws = list(ws)
+    if not 1 <= len(ws) <= 3:
+        raise ValueError(f"tg_linear_multi takes 1 to 3 weights, got {len(ws)}")
+    ns = []
+    for i, w in enumerate(ws):
+        _ndim(w, f"w[{i}]", 2)
+        _shape(w, f"w[{i}]", (w.shape[0], K))
+        ns.append(w.shape[0])
+    if ys is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs ys")
+        ys = [torch.empty(M, n, dtype=x.dtype, device=x.device) for n in ns]
+    ys = list(ys)
+    if len(ys) != len(ws):
+        raise ValueError(f"{len(ys)} outputs for {len(ws)} weights")
+    for i, (y, n) in enumerate(zip(ys, ns)):
+        _shape(y, f"y[{i}]", (M, n))
+    wp = (ctypes.c_void_p * len(ws))(*[_dev(w, f"w[{i}]", x.dtype) for i, w in enumerate(ws)])
+    yp = (ctypes.c_void_p * len(ys))(*[_dev(y, f"y[{i}]", x.dtype) for i, y in enumerate(ys)])
+    na = _i32_array(ns)
+    _check("tg_linear_multi", lib().tg_linear_multi(
+        _dt(x), _dev(x, "x"), len(ws), wp, yp, ctypes.cast(na, ctypes.POINTER(ctypes.c_int32)), M, K,
+        1 if accumulate else 0, int(tile), _stream(stream)))
+    return ys

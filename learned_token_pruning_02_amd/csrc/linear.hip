@@ -42,10 +42,21 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(const float* __restrict
 // Split over k (blockIdx.z = slice): the workgroup contracts k in
 // [z K, (z + 1) K) of rows that are ldk long, and with `part` set writes its
 // fp32 partial to part[z][M][N] instead of y.
+// Several products of the same x in one launch (the q, k and v projections):
+// the columns of segment i are [nend[i-1], nend[i]) of the grid, each
+// boundary a multiple of the workgroup tile, with their own weights and
+// output (rows of nend[i] - nend[i-1]).  One product is one segment.
+struct LinSegs {
+    const bf16* w[LINEAR_MAX_SEG];
+    bf16* y[LINEAR_MAX_SEG];
+    int nend[LINEAR_MAX_SEG];
+    int nseg;
+};
+
 template <int WM, int WN, int KC, int GM, int GN>
 __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf16_kernel(
-        const bf16* __restrict__ x, const bf16* __restrict__ w, bf16* __restrict__ y, int64_t M,
-        int N, int K, int accumulate, int64_t ldk, float* __restrict__ part) {
+        const bf16* __restrict__ x, LinSegs sg, int64_t M, int K, int accumulate, int64_t ldk,
+        float* __restrict__ part) {
     constexpr int THREADS = 64 * GM * GN;
     constexpr int LK = KC;                       // k chunk
     constexpr int LS = LK + 8;                   // LDS row stride (bf16 elements)
@@ -63,7 +74,16 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
     const int wm = wv % GM, wn = wv / GM;
     const int hh = lane / 32, l32 = lane % 32;
     const int64_t m0 = (int64_t)blockIdx.x * BM;
-    const int n0 = blockIdx.y * BN;
+    // This workgroup's segment, and its columns within it.
+    int n0 = blockIdx.y * BN, sgi = 0;
+#pragma unroll
+    for (int i = 0; i + 1 < LINEAR_MAX_SEG; ++i)
+        if (sgi + 1 < sg.nseg && n0 >= sg.nend[sgi]) ++sgi;
+    const int nbeg = sgi > 0 ? sg.nend[sgi - 1] : 0;
+    const bf16* __restrict__ w = sg.w[sgi];
+    bf16* __restrict__ y = sg.y[sgi];
+    const int N = sg.nend[sgi] - nbeg;
+    n0 -= nbeg;
     x += (int64_t)blockIdx.z * K;
     w += (int64_t)blockIdx.z * K;
 
@@ -218,8 +238,18 @@ hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M
     return hipGetLastError();
 }
 
-hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
-                              int accumulate, int tile, hipStream_t st) {
+hipError_t launch_linear_bf16_multi(const void* x, int nseg, const void* const* w, void* const* y,
+                                    const int* n, int64_t M, int K, int accumulate, int tile,
+                                    hipStream_t st) {
+    LinSegs sg{};
+    int N = 0;
+    for (int i = 0; i < nseg; ++i) {
+        sg.w[i] = (const bf16*)w[i];
+        sg.y[i] = (bf16*)y[i];
+        N += n[i];
+        sg.nend[i] = N;
+    }
+    sg.nseg = nseg;
     // tile 0: the largest tile that still gives every CU at least one
     // workgroup (two for the 256x128 tile, which runs two per CU);
     // 1, 2, 3 force the 128x128, 256x128 or 256x256 tile.
@@ -229,25 +259,35 @@ hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, 
     if (choice == 2) {
         const dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 255) / 256));
         hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 4>), grid, dim3(512), 0, st,
-                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate, (int64_t)K, nullptr);
+                           (const bf16*)x, sg, M, K, accumulate, (int64_t)K, nullptr);
     } else if (choice == 1) {
         const dim3 grid((unsigned)((M + 255) / 256), (unsigned)((N + 127) / 128));
         hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 2>), grid, dim3(256), 0, st,
-                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate, (int64_t)K, nullptr);
+                           (const bf16*)x, sg, M, K, accumulate, (int64_t)K, nullptr);
     } else {
         const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
         hipLaunchKernelGGL((linear_bf16_kernel<2, 2, 64, 2, 2>), grid, dim3(256), 0, st,
-                           (const bf16*)x, (const bf16*)w, (bf16*)y, M, N, K, accumulate, (int64_t)K, nullptr);
+                           (const bf16*)x, sg, M, K, accumulate, (int64_t)K, nullptr);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
+                              int accumulate, int tile, hipStream_t st) {
+    return launch_linear_bf16_multi(x, 1, &w, &y, &N, M, K, accumulate, tile, st);
 }
 
 hipError_t launch_linear_bf16_splitk(const void* x, const void* w, float* part, int64_t M, int N,
                                      int K, int slices, hipStream_t st) {
     const int ks = K / slices;  // a multiple of 64 (checked by the caller)
     const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128), (unsigned)slices);
+    LinSegs sg{};
+    sg.w[0] = (const bf16*)w;
+    sg.y[0] = nullptr;
+    sg.nend[0] = N;
+    sg.nseg = 1;
     hipLaunchKernelGGL((linear_bf16_kernel<2, 2, 64, 2, 2>), grid, dim3(256), 0, st, (const bf16*)x,
-                       (const bf16*)w, (bf16*)nullptr, M, N, ks, 0, (int64_t)K, part);
+                       sg, M, ks, 0, (int64_t)K, part);
     return hipGetLastError();
 }
 

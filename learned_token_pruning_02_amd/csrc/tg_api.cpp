@@ -610,4 +610,50 @@ tg_status tg_linear_tile(tg_dtype dt, const void* x, const void* w, void* y, int
     return linear_checked(dt, x, w, y, M, N, K, accumulate, tile, stream);
 }
 
+tg_status tg_linear_multi(tg_dtype dt, const void* x, int32_t nseg, const void* const* w,
+                          void* const* y, const int32_t* n, int64_t M, int32_t K, int accumulate,
+                          int tile, hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (nseg < 1 || nseg > TG_LINEAR_MAX_SEG || M < 0 || K < 1 || M >= I32_LIMIT || tile < 0 ||
+        tile > 3)
+        return TG_ERR_BAD_SHAPE;
+    if (x == nullptr || w == nullptr || y == nullptr || n == nullptr) return TG_ERR_NULL_PTR;
+    int64_t total = 0;
+    for (int i = 0; i < nseg; ++i) {
+        if (w[i] == nullptr || y[i] == nullptr) return TG_ERR_NULL_PTR;
+        if (n[i] < 1) return TG_ERR_BAD_SHAPE;
+        total += n[i];
+    }
+    if (total >= I32_LIMIT) return TG_ERR_BAD_SHAPE;
+    if (dt == TG_BF16) {
+        if (K % 64 != 0) return TG_ERR_UNSUPPORTED;
+        for (int i = 0; i < nseg; ++i)
+            if (n[i] % (nseg > 1 ? 256 : 64) != 0) return TG_ERR_UNSUPPORTED;
+    }
+    if (!aligned16(x)) return TG_ERR_ALIGNMENT;
+    for (int i = 0; i < nseg; ++i)
+        if (!aligned16(w[i]) || !aligned16(y[i])) return TG_ERR_ALIGNMENT;
+    const int64_t eb = elt_bytes(dt);
+    for (int i = 0; i < nseg; ++i) {
+        const int64_t yb = M * n[i] * eb;
+        if (overlap(y[i], yb, x, M * K * eb)) return TG_ERR_ALIAS;
+        for (int j = 0; j < nseg; ++j) {
+            if (overlap(y[i], yb, w[j], (int64_t)n[j] * K * eb)) return TG_ERR_ALIAS;
+            if (j != i && overlap(y[i], yb, y[j], M * n[j] * eb)) return TG_ERR_ALIAS;
+        }
+    }
+    if (M == 0) return TG_OK;
+    if (dt == TG_F32) {
+        for (int i = 0; i < nseg; ++i) {
+            const hipError_t e = tg::launch_linear_f32((const float*)x, (const float*)w[i],
+                                                       (float*)y[i], M, n[i], K, accumulate, stream);
+            if (e != hipSuccess) return launched(e);
+        }
+        return TG_OK;
+    }
+    int nn[TG_LINEAR_MAX_SEG];
+    for (int i = 0; i < nseg; ++i) nn[i] = n[i];
+    return launched(tg::launch_linear_bf16_multi(x, nseg, w, y, nn, M, K, accumulate, tile, stream));
+}
+
 }  // extern "C"

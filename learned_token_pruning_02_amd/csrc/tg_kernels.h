@@ -98,6 +98,12 @@ hipError_t launch_kept_positions(const int32_t* kept, int64_t Kt, const BatchArg
 hipError_t launch_linear_f32(const float* x, const float* w, float* y, int64_t M, int N, int K,
                              int accumulate, hipStream_t st);
 // tile: 0 chooses by output size; 1, 2, 3 force the 128x128, 256x128, 256x256 tile.
+// Products of one x with up to LINEAR_MAX_SEG weights in one launch; every
+// n[i] a multiple of 256 when nseg > 1.
+constexpr int LINEAR_MAX_SEG = 3;
+hipError_t launch_linear_bf16_multi(const void* x, int nseg, const void* const* w, void* const* y,
+                                    const int* n, int64_t M, int K, int accumulate, int tile,
+                                    hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
                               int accumulate, int tile, hipStream_t st);
 // part[z][M][N] = x[:, zK/S : (z+1)K/S] . w[:, same]^T in fp32, z < S (K/S a multiple of 64).

@@ -14,8 +14,20 @@ from typing import Dict, List, Optional, Sequence
 import torch
 
 from . import (tg_attn_prefill_plan, tg_gate_score, tg_gated_attn_prefill, tg_gather_compact,
-               tg_kept_positions, tg_linear, tg_plan, tg_qk_norm_rope, tg_rmsnorm, tg_silu_mul,
-               tg_topk_select)
+               tg_kept_positions, tg_linear, tg_linear_multi, tg_plan, tg_qk_norm_rope, tg_rmsnorm,
+               tg_silu_mul, tg_topk_select)
+
+
+def qkv_projections(x, wq, wk, wv, yq, yk, yv):
+    """yq, yk, yv = x wq^T, x wk^T, x wv^T: one launch when every output width
+    is a multiple of 256 (the three products then share one grid that fills
+    the chip), else three."""
+    if x.dtype == torch.bfloat16 and all(w.shape[0] % 256 == 0 for w in (wq, wk, wv)):
+        tg_linear_multi(x, [wq, wk, wv], ys=[yq, yk, yv])
+    else:
+        tg_linear(x, wq, y=yq)
+        tg_linear(x, wk, y=yk)
+        tg_linear(x, wv, y=yv)
 
 
 class _AttnWorkspace:
@@ -88,8 +100,9 @@ class GatedLayer:
 
 
 class AttentionStack:
-    """Layers above the gate on the kept rows only: per layer q|k|v = x W^T,
-    token-gated attention, x += attn W_o^T (the residual updated in place)."""
+    """Layers above the gate on the kept rows only: per layer q|k|v = x W^T
+    (one launch for the three products), token-gated attention,
+    x += attn W_o^T (the residual updated in place)."""
 
     def __init__(self, Kt: int, d_model: int, n_q_heads: int, n_kv_heads: int, d_head: int,
                  dtype: torch.dtype, device="cuda"):
@@ -103,9 +116,7 @@ class AttentionStack:
     def __call__(self, x, s_kept, cu_kept: Sequence[int], layers: List[Dict[str, torch.Tensor]]):
         Kt = x.shape[0]
         for L in layers:
-            tg_linear(x, L["wq"], y=self.q)
-            tg_linear(x, L["wk"], y=self.k)
-            tg_linear(x, L["wv"], y=self.v)
+            qkv_projections(x, L["wq"], L["wk"], L["wv"], self.q, self.k, self.v)
             tg_gated_attn_prefill(self.q.view(Kt, self.Hq, self.dh), self.k.view(Kt, self.Hkv, self.dh),
                                   self.v.view(Kt, self.Hkv, self.dh), s_kept, L["gain"], L["temp"],
                                   cu_kept, out=self.attn, workspace=self.attn_ws.get(cu_kept))
@@ -151,9 +162,8 @@ class DecoderLayer:
         """x[Kt][d] is updated in place; self.pos must hold the positions."""
         Kt = x.shape[0]
         tg_rmsnorm(x, L["in_norm"], self.eps, y=self.xn)
-        tg_linear(self.xn, L["wq"], y=self.q.view(Kt, -1))
-        tg_linear(self.xn, L["wk"], y=self.k.view(Kt, -1))
-        tg_linear(self.xn, L["wv"], y=self.v.view(Kt, -1))
+        qkv_projections(self.xn, L["wq"], L["wk"], L["wv"], self.q.view(Kt, -1), self.k.view(Kt, -1),
+                        self.v.view(Kt, -1))
         tg_qk_norm_rope(self.q, self.k, L["q_norm"], L["k_norm"], self.pos, self.theta, self.eps)
         tg_gated_attn_prefill(self.q, self.k, self.v, s_kept, L["gain"], L["temp"], cu_kept,
                               out=self.attn, workspace=self.attn_ws.get(cu_kept))

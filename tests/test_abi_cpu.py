@@ -509,6 +509,30 @@ def test_linear_tile_validation():
     assert f(1, A, B, C, 0, 128, 128, 0, 3, None) == 0
 
 
+def test_linear_multi_validation():
+    L = tg.lib()
+    f = L.tg_linear_multi
+    vp = ctypes.c_void_p
+    two = lambda a, b: (vp * 2)(a, b)
+    n = lambda *v: (ctypes.c_int32 * len(v))(*v)
+    W, Y = two(B, B + 4096), two(C, C + (1 << 20))
+    assert f(7, A, 2, W, Y, n(256, 256), 10, 128, 0, 0, None) == 4        # dtype
+    assert f(1, A, 0, W, Y, n(256, 256), 10, 128, 0, 0, None) == 2        # nseg 0
+    assert f(1, A, 4, W, Y, n(256, 256), 10, 128, 0, 0, None) == 2        # nseg > 3
+    assert f(1, A, 2, W, Y, n(256, 256), 10, 128, 0, 4, None) == 2        # tile
+    assert f(1, A, 2, W, Y, n(256, 0), 10, 128, 0, 0, None) == 2          # a zero width
+    assert f(1, None, 2, W, Y, n(256, 256), 10, 128, 0, 0, None) == 1
+    assert f(1, A, 2, None, Y, n(256, 256), 10, 128, 0, 0, None) == 1
+    assert f(1, A, 2, two(B, None), Y, n(256, 256), 10, 128, 0, 0, None) == 1
+    assert f(1, A, 2, W, Y, None, 10, 128, 0, 0, None) == 1
+    assert f(1, A, 2, W, Y, n(256, 192), 10, 128, 0, 0, None) == 5        # width not a multiple of 256
+    assert f(1, A, 2, W, Y, n(256, 256), 10, 96, 0, 0, None) == 5         # K % 64
+    assert f(1, A, 2, two(B, B + 8), Y, n(256, 256), 10, 128, 0, 0, None) == 6  # alignment
+    assert f(1, A, 2, W, two(C, C + 512), n(256, 256), 10, 128, 0, 0, None) == 9  # outputs overlap
+    assert f(1, A, 2, W, two(A, C), n(256, 256), 10, 128, 0, 0, None) == 9     # an output over x
+    assert f(1, A, 2, W, Y, n(256, 256), 0, 128, 0, 0, None) == 0             # M == 0: no-op
+
+
 # ------------------------------------------- binding size checks (no GPU) ----
 def _meta(*shape, dtype=None):
     import torch

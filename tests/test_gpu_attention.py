@@ -383,3 +383,33 @@ def test_linear_parity(M, N, K, dtype, acc):
     ref = oracle.linear(x, w) + (y0.double() if acc else 0.0)
     rtol, atol = tol(dtype)
     assert_within(y.cpu(), ref, rtol, atol, "linear")
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_linear_multi_matches_separate_products(tile):
+    """Three projections of the same rows in one launch (tg_linear_multi):
+    every output equal bit for bit to tg_linear_tile of the same product with
+    the tile the fused grid uses, and within the bf16 bound of the oracle;
+    ragged M, accumulating and not, the q/k/v widths of the 32k stack."""
+    rt, at = tol(torch.bfloat16)
+    for M, ns, K, acc in ((1000 + 13, (512, 256, 256), 256, False), (4096, (2048, 1024, 1024), 2048, False),
+                          (777, (256, 512), 192, True)):
+        announce(f"linear_multi tile={tile} M={M} N={ns} K={K} acc={acc}")
+        g = torch.Generator().manual_seed(M * 3 + sum(ns) + tile)
+        x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+        ws = [(torch.randn(n, K, generator=g) / K ** 0.5).to(torch.bfloat16) for n in ns]
+        y0 = [torch.randn(M, n, generator=g).to(torch.bfloat16) for n in ns]
+        ys = [t.cuda().clone() for t in y0]
+        xc, wc = x.cuda(), [w.cuda() for w in ws]
+        tg.tg_linear_multi(xc, wc, ys=ys, accumulate=acc, tile=tile)
+        # the tile the fused grid takes for the whole width (as tg_linear chooses)
+        N = sum(ns)
+        t256, t128 = ((M + 255) // 256) * ((N + 255) // 256), ((M + 255) // 256) * ((N + 127) // 128)
+        used = tile if tile else (3 if t256 >= 256 else 2 if t128 >= 512 else 1)
+        for i, (w, n) in enumerate(zip(wc, ns)):
+            sep = y0[i].cuda().clone()
+            tg.tg_linear(xc, w, y=sep, accumulate=acc, tile=used)
+            torch.cuda.synchronize()
+            assert torch.equal(ys[i].cpu(), sep.cpu()), f"segment {i} differs from tg_linear_tile {used}"
+            ref = oracle.linear(x, ws[i]) + (y0[i].double() if acc else 0.0)
+            assert_within(ys[i].cpu(), ref, rt, at, f"linear_multi segment {i}")

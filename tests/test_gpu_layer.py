@@ -15,7 +15,7 @@ import torch
 import learned_token_pruning_02_amd as tg
 import oracle
 import workloads
-from learned_token_pruning_02_amd.path import DecoderLayer
+from learned_token_pruning_02_amd.path import DecoderLayer, qkv_projections
 from parity_util import announce, assert_within, tol
 
 pytestmark = pytest.mark.gpu
@@ -121,8 +121,9 @@ def _steps_checked(shape, F, L, kept, cu_s, cu_k, x, s, rows=None):
     tg.tg_rmsnorm(xg, Lg["in_norm"], EPS, y=layer.xn)
     xn = cpu(layer.xn)
     assert_within(xn[sel], oracle.rms_norm(x[sel], L["in_norm"], EPS), *rt, "in_norm")
+    qkv_projections(layer.xn, Lg["wq"], Lg["wk"], Lg["wv"], layer.q.view(Kt, -1), layer.k.view(Kt, -1),
+                    layer.v.view(Kt, -1))
     for name, buf in (("wq", layer.q), ("wk", layer.k), ("wv", layer.v)):
-        tg.tg_linear(layer.xn, Lg[name], y=buf.view(Kt, -1))
         assert_within(cpu(buf).view(Kt, -1)[sel], oracle.linear(xn[sel], L[name]), *rt, name)
     q0, k0 = cpu(layer.q), cpu(layer.k)
     tg.tg_qk_norm_rope(layer.q, layer.k, Lg["q_norm"], Lg["k_norm"], pos, THETA, EPS)
