@@ -440,7 +440,7 @@ def layer_bench(args):
     st = torch.cuda.current_stream()
     theta, eps = layer.theta, layer.eps
     names = ["in_norm", "qkv_proj", "qk_norm_rope", "attention", "o_proj",
-             "post_norm", "gate_up", "silu_mul", "down"]
+             "post_norm", "gate_up_silu", "down"]
     calls = [
         lambda: tg.tg_rmsnorm(x, L["in_norm"], eps, y=layer.xn, stream=st),
         lambda: tg.tg_linear_multi(layer.xn, [L["wq"], L["wk"], L["wv"]],
@@ -452,8 +452,7 @@ def layer_bench(args):
                                          out=layer.attn, stream=st),
         lambda: tg.tg_linear(layer.attn.view(Kt, -1), L["wo"], y=x, accumulate=True, stream=st),
         lambda: tg.tg_rmsnorm(x, L["post_norm"], eps, y=layer.xn, stream=st),
-        lambda: tg.tg_linear(layer.xn, L["wgu"], y=layer.gu, stream=st),
-        lambda: tg.tg_silu_mul(layer.gu, out=layer.m, stream=st),
+        lambda: tg.tg_linear_swiglu(layer.xn, L["wgu"], out=layer.m, stream=st),
         lambda: tg.tg_linear(layer.m, L["wd"], y=x, accumulate=True, stream=st),
     ]
     for _ in range(args.warmup):
@@ -473,11 +472,11 @@ def layer_bench(args):
     step_ms = sum(e[0].elapsed_time(e[-1]) for e in evs) / args.steps
     d, hq, hkv, dh = sh.d_model, sh.n_q_heads, sh.n_kv_heads, sh.d_head
     flops = {"qkv_proj": 2 * Kt * d * (hq + 2 * hkv) * dh,
-             "o_proj": 2 * Kt * hq * dh * d, "gate_up": 2 * Kt * d * 2 * F, "down": 2 * Kt * F * d,
+             "o_proj": 2 * Kt * hq * dh * d, "gate_up_silu": 2 * Kt * d * 2 * F, "down": 2 * Kt * F * d,
              "attention": 4 * dh * hq * Kt * (Kt + 1) // 2}
     eb = 2
     hbm = {"in_norm": 2 * Kt * d * eb, "post_norm": 2 * Kt * d * eb,
-           "qk_norm_rope": 2 * Kt * (hq + hkv) * dh * eb + Kt * 4, "silu_mul": 3 * Kt * F * eb}
+           "qk_norm_rope": 2 * Kt * (hq + hkv) * dh * eb + Kt * 4}
     kern = {n: {"ms": per[n]} for n in names}
     for n, f in flops.items():
         kern[n]["TFLOP/s"] = f / (per[n] * 1e-3) / 1e12
@@ -485,7 +484,7 @@ def layer_bench(args):
     for n, b in hbm.items():
         kern[n]["GB/s"] = b / (per[n] * 1e-3) / 1e9
         kern[n]["hbm_frac"] = kern[n]["GB/s"] / HBM_PEAK_GBS
-    gu = kern["gate_up"]["TFLOP/s"]
+    gu = kern["gate_up_silu"]["TFLOP/s"]
     rec = {
         "metric": "pruned decoder layer tokens/s (context tokens per layer)",
         "value": w.total_tokens / (step_ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -495,7 +494,7 @@ def layer_bench(args):
         "config": {"workload": "qwen3_1p7b_128k_layer", "tokens": w.total_tokens, "kept": Kt,
                    "d_model": d, "heads_q": hq, "heads_kv": hkv, "d_head": dh, "d_ffn": F},
         "roofline": {"bound": "mfma", "achieved": gu, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gu / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "gate_up (tg_linear)"},
+                     "frac": gu / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "gate|up projection with the SwiGLU product (tg_linear_swiglu)"},
         "kept_rows_per_s": Kt / (step_ms * 1e-3), "gpu_ms_per_layer": step_ms,
         "layer_TFLOP/s": sum(flops.values()) / (step_ms * 1e-3) / 1e12,
         "kernels": kern,

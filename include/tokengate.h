@@ -542,6 +542,23 @@ tg_status tg_linear(tg_dtype dt, const void *x, const void *w, void *y, int64_t 
 tg_status tg_linear_tile(tg_dtype dt, const void *x, const void *w, void *y, int64_t M,
                          int32_t N, int32_t K, int accumulate, int tile, hipStream_t stream);
 
+/*
+ * tg_linear_swiglu -- the gate and up projections of the feed-forward block
+ * of a layer above the gate with the SwiGLU product in their epilogue, on
+ * the kept rows only (spke.com page, three-phase list, third bullet):
+ *     out[M][F] = silu(x . w_gu[0:F]^T) * (x . w_gu[F:2F]^T),
+ * silu(z) = z / (1 + e^-z), from the fp32 accumulators, one rounding to bf16
+ * at the store (tg_linear followed by tg_silu_mul rounds both products to
+ * bf16 first).  x : [M][K], w_gu : [2F][K] (gate rows, then up rows),
+ * out : [M][F], bf16, device.  tile as in tg_linear_tile (0 chooses from M
+ * and 2F).  Supported: TG_BF16 with F % 128 == 0 and K % 64 == 0, else
+ * TG_ERR_UNSUPPORTED.  M == 0 is a no-op.  Errors: TG_ERR_BAD_DTYPE,
+ * TG_ERR_BAD_SHAPE, TG_ERR_NULL_PTR, TG_ERR_UNSUPPORTED, TG_ERR_ALIGNMENT,
+ * TG_ERR_ALIAS, TG_ERR_LAUNCH.
+ */
+tg_status tg_linear_swiglu(tg_dtype dt, const void *x, const void *w_gu, void *out, int64_t M,
+                           int32_t F, int32_t K, int tile, hipStream_t stream);
+
 /* Most products of one tg_linear_multi call. */
 #define TG_LINEAR_MAX_SEG 3
 

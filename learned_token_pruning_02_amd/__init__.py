@@ -42,6 +42,7 @@ __all__ = [
     "tg_gated_attn_decode",
     "tg_rmsnorm",
     "tg_linear_multi",
+    "tg_linear_swiglu",
     "tg_kept_positions",
     "tg_qk_norm_rope",
     "tg_silu_mul",
@@ -162,6 +163,8 @@ def lib() -> ctypes.CDLL:
     L.tg_linear.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
     L.tg_linear_tile.restype = ctypes.c_int
     L.tg_linear_tile.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, ctypes.c_int, vp]
+    L.tg_linear_swiglu.restype = ctypes.c_int
+    L.tg_linear_swiglu.argtypes = [ctypes.c_int, vp, vp, vp, i64, i32, i32, ctypes.c_int, vp]
     L.tg_linear_multi.restype = ctypes.c_int
     L.tg_linear_multi.argtypes = [ctypes.c_int, vp, i32, ctypes.POINTER(vp), ctypes.POINTER(vp), p_i32,
                                   i64, i32, ctypes.c_int, ctypes.c_int, vp]
@@ -706,3 +709,23 @@ def tg_linear_multi(x, ws, ys=None, accumulate: bool = False, stream=None, tile:
         _dt(x), _dev(x, "x"), len(ws), wp, yp, ctypes.cast(na, ctypes.POINTER(ctypes.c_int32)), M, K,
         1 if accumulate else 0, int(tile), _stream(stream)))
     return ys
+
+
+def tg_linear_swiglu(x, w_gu, out=None, stream=None, tile: int = 0):
+    """out = silu(x w_gu[:F]^T) * (x w_gu[F:]^T) in one launch; w_gu is [2F][K]
+    (gate rows then up rows), out [M][F].  tile as in tg_linear."""
+    torch = _torch()
+    _ndim(x, "x", 2)
+    _ndim(w_gu, "w_gu", 2)
+    M, K = x.shape
+    if w_gu.shape[0] % 2 != 0:
+        raise ValueError(f"w_gu has {w_gu.shape[0]} rows; it stacks F gate rows and F up rows")
+    F = w_gu.shape[0] // 2
+    _shape(w_gu, "w_gu", (2 * F, K))
+    _shape(out, "out", (M, F))
+    if out is None:
+        out = torch.empty(M, F, dtype=x.dtype, device=x.device)
+    _check("tg_linear_swiglu", lib().tg_linear_swiglu(
+        _dt(x), _dev(x, "x"), _dev(w_gu, "w_gu", x.dtype), _dev(out, "out", x.dtype), M, F, K,
+        int(tile), _stream(stream)))
+    return out

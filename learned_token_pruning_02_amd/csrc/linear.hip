@@ -53,7 +53,11 @@ struct LinSegs {
     int nseg;
 };
 
-template <int WM, int WN, int KC, int GM, int GN>
+// GLU: the grid's columns are the 2F rows of a stacked [gate; up] weight,
+// arranged so that each wave's two 32-column tiles are the gate and the up
+// rows of the same 32 units; the epilogue stores silu(gate) * up to an
+// [M][F] output instead of both products.
+template <int WM, int WN, int KC, int GM, int GN, bool GLU = false>
 __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf16_kernel(
         const bf16* __restrict__ x, LinSegs sg, int64_t M, int K, int accumulate, int64_t ldk,
         float* __restrict__ part) {
@@ -84,6 +88,8 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
     bf16* __restrict__ y = sg.y[sgi];
     const int N = sg.nend[sgi] - nbeg;
     n0 -= nbeg;
+    static_assert(!GLU || WN == 2, "GLU: a wave's two column tiles are gate and up");
+    const int F = N / 2, fbase = n0 / 2;  // GLU: units of this workgroup start at fbase
     x += (int64_t)blockIdx.z * K;
     w += (int64_t)blockIdx.z * K;
 
@@ -124,6 +130,9 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
             int row, c;
             unit_rc(uu, row, c);
             int nr = n0 + row;
+            if constexpr (GLU) {  // row 64 wn + 32 t + j: gate (t = 0) or up row of unit 32 wn + j
+                nr = (row % 64) / 32 * F + fbase + 32 * (row / 64) + row % 32;
+            }
             if (nr > N - 1) nr = N - 1;
             r.w[i] = ld16(w + (int64_t)nr * ldk + k0 + 8 * c);
         }
@@ -195,6 +204,26 @@ __global__ __launch_bounds__(64 * GM * GN, GM * GN == 4 ? 2 : 1) void linear_bf1
     }
     if (s < nsteps) mma(s & 1);  // odd count: the last chunk is already in LDS
 
+    if constexpr (GLU) {
+        // acc[0] holds gate and acc[1] up of units fbase + 32 wn + 8(r/4) + 4hh + r%4.
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt) {
+            const int64_t m = m0 + 32 * WM * wm + 32 * mt + l32;
+            if (m >= M) continue;
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {
+                const int f = fbase + 32 * wn + 8 * rq + 4 * hh;
+                bf16x4 ov;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float g = acc[0][mt][4 * rq + e], u = acc[1][mt][4 * rq + e];
+                    ov[e] = to_bf16(g / (1.0f + __expf(-g)) * u);
+                }
+                *reinterpret_cast<bf16x4*>(y + m * F + f) = ov;
+            }
+        }
+        return;
+    }
     // D[n][m]: lane owns m = 32WM wm + 32mt + l32, n = 32WN wn + 32nt + 8(r/4) + 4hh + r%4.
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt) {
@@ -268,6 +297,33 @@ hipError_t launch_linear_bf16_multi(const void* x, int nseg, const void* const* 
         const dim3 grid((unsigned)((M + 127) / 128), (unsigned)((N + 127) / 128));
         hipLaunchKernelGGL((linear_bf16_kernel<2, 2, 64, 2, 2>), grid, dim3(256), 0, st,
                            (const bf16*)x, sg, M, K, accumulate, (int64_t)K, nullptr);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_bf16_swiglu(const void* x, const void* wgu, void* out, int64_t M, int F,
+                                     int K, int tile, hipStream_t st) {
+    LinSegs sg{};
+    const int N = 2 * F;
+    sg.w[0] = (const bf16*)wgu;
+    sg.y[0] = (bf16*)out;
+    sg.nend[0] = N;
+    sg.nseg = 1;
+    const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
+    const int64_t t128 = ((M + 255) / 256) * ((N + 127) / 128);
+    const int choice = tile > 0 ? tile - 1 : (t256 >= 256 ? 2 : t128 >= 512 ? 1 : 0);
+    if (choice == 2) {
+        const dim3 grid((unsigned)((M + 255) / 256), (unsigned)(N / 256));
+        hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 4, true>), grid, dim3(512), 0, st,
+                           (const bf16*)x, sg, M, K, 0, (int64_t)K, nullptr);
+    } else if (choice == 1) {
+        const dim3 grid((unsigned)((M + 255) / 256), (unsigned)(N / 128));
+        hipLaunchKernelGGL((linear_bf16_kernel<4, 2, 32, 2, 2, true>), grid, dim3(256), 0, st,
+                           (const bf16*)x, sg, M, K, 0, (int64_t)K, nullptr);
+    } else {
+        const dim3 grid((unsigned)((M + 127) / 128), (unsigned)(N / 128));
+        hipLaunchKernelGGL((linear_bf16_kernel<2, 2, 64, 2, 2, true>), grid, dim3(256), 0, st,
+                           (const bf16*)x, sg, M, K, 0, (int64_t)K, nullptr);
     }
     return hipGetLastError();
 }

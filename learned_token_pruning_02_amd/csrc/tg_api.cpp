@@ -610,6 +610,21 @@ tg_status tg_linear_tile(tg_dtype dt, const void* x, const void* w, void* y, int
     return linear_checked(dt, x, w, y, M, N, K, accumulate, tile, stream);
 }
 
+tg_status tg_linear_swiglu(tg_dtype dt, const void* x, const void* w_gu, void* out, int64_t M,
+                           int32_t F, int32_t K, int tile, hipStream_t stream) {
+    if (!valid_dtype(dt)) return TG_ERR_BAD_DTYPE;
+    if (M < 0 || F < 1 || K < 1 || M >= I32_LIMIT || F >= I32_LIMIT / 2 || tile < 0 || tile > 3)
+        return TG_ERR_BAD_SHAPE;
+    if (x == nullptr || w_gu == nullptr || out == nullptr) return TG_ERR_NULL_PTR;
+    if (dt != TG_BF16 || F % 128 != 0 || K % 64 != 0) return TG_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w_gu) || !aligned16(out)) return TG_ERR_ALIGNMENT;
+    const int64_t ob = M * F * 2;
+    if (overlap(out, ob, x, M * K * 2) || overlap(out, ob, w_gu, 2 * (int64_t)F * K * 2))
+        return TG_ERR_ALIAS;
+    if (M == 0) return TG_OK;
+    return launched(tg::launch_linear_bf16_swiglu(x, w_gu, out, M, F, K, tile, stream));
+}
+
 tg_status tg_linear_multi(tg_dtype dt, const void* x, int32_t nseg, const void* const* w,
                           void* const* y, const int32_t* n, int64_t M, int32_t K, int accumulate,
                           int tile, hipStream_t stream) {

@@ -104,6 +104,9 @@ constexpr int LINEAR_MAX_SEG = 3;
 hipError_t launch_linear_bf16_multi(const void* x, int nseg, const void* const* w, void* const* y,
                                     const int* n, int64_t M, int K, int accumulate, int tile,
                                     hipStream_t st);
+// out[M][F] = silu(x wgu[0:F]^T) * (x wgu[F:2F]^T); F a multiple of 128.
+hipError_t launch_linear_bf16_swiglu(const void* x, const void* wgu, void* out, int64_t M, int F,
+                                     int K, int tile, hipStream_t st);
 hipError_t launch_linear_bf16(const void* x, const void* w, void* y, int64_t M, int N, int K,
                               int accumulate, int tile, hipStream_t st);
 // part[z][M][N] = x[:, zK/S : (z+1)K/S] . w[:, same]^T in fp32, z < S (K/S a multiple of 64).

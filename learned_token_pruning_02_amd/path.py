@@ -14,8 +14,19 @@ from typing import Dict, List, Optional, Sequence
 import torch
 
 from . import (tg_attn_prefill_plan, tg_gate_score, tg_gated_attn_prefill, tg_gather_compact,
-               tg_kept_positions, tg_linear, tg_linear_multi, tg_plan, tg_qk_norm_rope, tg_rmsnorm,
-               tg_silu_mul, tg_topk_select)
+               tg_kept_positions, tg_linear, tg_linear_multi, tg_linear_swiglu, tg_plan,
+               tg_qk_norm_rope, tg_rmsnorm, tg_silu_mul, tg_topk_select)
+
+
+def swiglu_projection(xn, wgu, gu, m):
+    """m = silu(xn wg^T) * (xn wu^T) with wgu = [wg; wu]: one launch with the
+    product in the projection's epilogue when F is a multiple of 128 (bf16),
+    else the gate|up projection into gu and the product as a second launch."""
+    if xn.dtype == torch.bfloat16 and (wgu.shape[0] // 2) % 128 == 0:
+        tg_linear_swiglu(xn, wgu, out=m)
+    else:
+        tg_linear(xn, wgu, y=gu)
+        tg_silu_mul(gu, out=m)
 
 
 def qkv_projections(x, wq, wk, wv, yq, yk, yv):
@@ -131,7 +142,7 @@ class DecoderLayer:
         xn = rmsnorm(x);  q, k, v = xn Wq^T, xn Wk^T, xn Wv^T
         q, k <- rotary(rmsnorm_head(q)), rotary(rmsnorm_head(k))  at original positions
         x += gated_attention(q, k, v; s_kept) Wo^T
-        xn = rmsnorm(x);  x += (silu(xn Wg^T) * (xn Wu^T)) Wd^T
+        xn = rmsnorm(x);  x += (silu(xn Wg^T) * (xn Wu^T)) Wd^T   (q|k|v and gate|up*silu one launch each)
 
     Weights: in_norm[d], wq[Hq*dh][d], wk, wv[Hkv*dh][d], q_norm, k_norm[dh],
     wo[d][Hq*dh], gain, temp[Hq], post_norm[d], wgu[2F][d] (gate rows then up
@@ -169,7 +180,6 @@ class DecoderLayer:
                               out=self.attn, workspace=self.attn_ws.get(cu_kept))
         tg_linear(self.attn.view(Kt, -1), L["wo"], y=x, accumulate=True)
         tg_rmsnorm(x, L["post_norm"], self.eps, y=self.xn)
-        tg_linear(self.xn, L["wgu"], y=self.gu)
-        tg_silu_mul(self.gu, out=self.m)
+        swiglu_projection(self.xn, L["wgu"], self.gu, self.m)
         tg_linear(self.m, L["wd"], y=x, accumulate=True)
         return x

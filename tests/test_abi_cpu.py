@@ -533,6 +533,25 @@ def test_linear_multi_validation():
     assert f(1, A, 2, W, Y, n(256, 256), 0, 128, 0, 0, None) == 0             # M == 0: no-op
 
 
+def test_linear_swiglu_validation():
+    L = tg.lib()
+    f = L.tg_linear_swiglu
+    assert f(7, A, B, C, 10, 128, 128, 0, None) == 4          # dtype
+    assert f(1, A, B, C, -1, 128, 128, 0, None) == 2          # M
+    assert f(1, A, B, C, 10, 0, 128, 0, None) == 2            # F
+    assert f(1, A, B, C, 10, 128, 128, 4, None) == 2          # tile
+    assert f(1, None, B, C, 10, 128, 128, 0, None) == 1
+    assert f(1, A, None, C, 10, 128, 128, 0, None) == 1
+    assert f(1, A, B, None, 10, 128, 128, 0, None) == 1
+    assert f(0, A, B, C, 10, 128, 128, 0, None) == 5          # fp32 not built
+    assert f(1, A, B, C, 10, 192, 128, 0, None) == 5          # F % 128
+    assert f(1, A, B, C, 10, 128, 96, 0, None) == 5           # K % 64
+    assert f(1, A + 8, B, C, 10, 128, 128, 0, None) == 6
+    assert f(1, A, B, A, 10, 128, 128, 0, None) == 9          # out over x
+    assert f(1, A, B, B, 10, 128, 128, 0, None) == 9          # out over the weights
+    assert f(1, A, B, C, 0, 128, 128, 0, None) == 0           # M == 0: no-op
+
+
 # ------------------------------------------- binding size checks (no GPU) ----
 def _meta(*shape, dtype=None):
     import torch

@@ -413,3 +413,20 @@ def test_linear_multi_matches_separate_products(tile):
             assert torch.equal(ys[i].cpu(), sep.cpu()), f"segment {i} differs from tg_linear_tile {used}"
             ref = oracle.linear(x, ws[i]) + (y0[i].double() if acc else 0.0)
             assert_within(ys[i].cpu(), ref, rt, at, f"linear_multi segment {i}")
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_linear_swiglu(tile):
+    """Gate and up projections with the SwiGLU product in the epilogue
+    (tg_linear_swiglu) against the oracle's silu(x Wg^T) * (x Wu^T), on
+    ragged M, one or several k chunks and several unit blocks."""
+    rt, at = tol(torch.bfloat16)
+    for M, F, K in ((777, 384, 192), (300, 128, 64), (4096 + 31, 1536, 2048)):
+        announce(f"linear_swiglu tile={tile} M={M} F={F} K={K}")
+        g = torch.Generator().manual_seed(M + F + K + tile)
+        x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+        w = (torch.randn(2 * F, K, generator=g) / K ** 0.5).to(torch.bfloat16)
+        out = tg.tg_linear_swiglu(x.cuda(), w.cuda(), tile=tile)
+        torch.cuda.synchronize()
+        gu = oracle.linear(x, w)
+        assert_within(out.cpu(), oracle.silu(gu[:, :F]) * gu[:, F:], rt, at, f"swiglu {tile}")

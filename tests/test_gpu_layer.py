@@ -15,7 +15,7 @@ import torch
 import learned_token_pruning_02_amd as tg
 import oracle
 import workloads
-from learned_token_pruning_02_amd.path import DecoderLayer, qkv_projections
+from learned_token_pruning_02_amd.path import DecoderLayer, qkv_projections, swiglu_projection
 from parity_util import announce, assert_within, tol
 
 pytestmark = pytest.mark.gpu
@@ -147,12 +147,10 @@ def _steps_checked(shape, F, L, kept, cu_s, cu_k, x, s, rows=None):
     tg.tg_rmsnorm(xg, Lg["post_norm"], EPS, y=layer.xn)
     xn2 = cpu(layer.xn)
     assert_within(xn2[sel], oracle.rms_norm(h[sel], L["post_norm"], EPS), *rt, "post_norm")
-    tg.tg_linear(layer.xn, Lg["wgu"], y=layer.gu)
-    gu = cpu(layer.gu)
-    assert_within(gu[sel], oracle.linear(xn2[sel], L["wgu"]), *rt, "gate|up")
-    tg.tg_silu_mul(layer.gu, out=layer.m)
+    swiglu_projection(layer.xn, Lg["wgu"], layer.gu, layer.m)
     m = cpu(layer.m)
-    assert_within(m[sel], oracle.silu(gu[sel, :F]) * gu[sel, F:].double(), *rt, "silu*up")
+    gu_ref = oracle.linear(xn2[sel], L["wgu"])
+    assert_within(m[sel], oracle.silu(gu_ref[:, :F]) * gu_ref[:, F:], *rt, "gate|up, silu*up")
     tg.tg_linear(layer.m, Lg["wd"], y=xg, accumulate=True)
     out = cpu(xg)
     assert_within(out[sel], h[sel].double() + oracle.linear(m[sel], L["wd"]), *rt, "down + residual")
@@ -163,7 +161,9 @@ def test_decoder_layer_small():
     """Every step on all rows against the oracle (each fed the GPU's previous
     output); DecoderLayer (one library call per step) bit-identical to that
     step sequence; and the whole layer against the oracle rounding to bf16
-    wherever the GPU stores, normwise.  Elementwise, a whole layer can differ
+    at its stores, normwise (the oracle also rounds the gate|up product,
+    which the fused GPU step keeps in fp32; one bf16 rounding of it is far
+    inside the bound).  Elementwise, a whole layer can differ
     by one bf16 ulp of the residual (|h| up to ~6, ulp 0.03) wherever the FFN
     cancels h to near zero, so the end-to-end bound is on the norm: 1e-2
     relative, three times the gap that rounding to bf16 at the stores alone
