@@ -279,7 +279,7 @@ tg_status tg_gated_attn_prefill(tg_dtype dt, const void *q, const void *k, const
  * packed batch (arguments as for tg_gated_attn_prefill).  Nonzero only for
  * TG_BF16, a single request, two or more query heads per KV head, a request
  * too short to give every CU two workgroups with whole query tiles (fewer
- * than 512 four-wave workgroups), and a longest query tile of more than 8
+ * than 512 four-wave workgroups), and a longest query tile of more than 18
  * key tiles of 64; *ws_bytes = 0 otherwise.  Errors: TG_ERR_NULL_PTR,
  * TG_ERR_BAD_DTYPE, TG_ERR_BAD_SHAPE, TG_ERR_UNSUPPORTED (d_head).
  */
@@ -290,7 +290,8 @@ tg_status tg_attn_prefill_plan(tg_dtype dt, const int32_t *cu_kept_host, int32_t
  * tg_gated_attn_prefill_ws -- tg_gated_attn_prefill with a caller workspace
  * (the same attention: spke.com page, "Qu'est-ce que l'attention gérée par
  * des tokens ?").  When tg_attn_prefill_plan gives nonzero bytes, each query
- * tile is cut into pieces of at most 8 key tiles of near-equal length, one
+ * tile is cut into pieces of near-equal length, at most 24 key tiles of 64
+ * (at most 16 when the request's longest tile has 19 to 24), one
  * workgroup each, so that the short causal tiles of one request spread over
  * the whole chip.  Each piece leaves its unnormalised output, exponent base
  * and row sum in fp32 in ws; the last piece of a tile to finish combines the

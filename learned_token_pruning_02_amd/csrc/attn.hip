@@ -864,6 +864,12 @@ hipError_t launch_bf16(const AttnArgs& a, int blocks, hipStream_t st) {
 #define TG_ATTN_SPLIT_LEN 24
 #endif
 constexpr int SPLIT_LEN = TG_ATTN_SPLIT_LEN;
+// A request whose longest query tile has 19..SPLIT_LEN key tiles (1153 to
+// 1536 kept rows) would not be split at that length; pieces of at most
+// SPLIT_SHORT key tiles still spread it (measured: 1536 rows 35.2 -> 28.9
+// us, 1200 rows 27.9 -> 26.7 us; at 1025 rows the split lost, 24.5 -> 25.9).
+constexpr int SPLIT_SHORT = 16;
+constexpr int SPLIT_SHORT_MIN = 19;  // key tiles of the longest tile, at least
 
 // How a packed batch is launched: eight-wave workgroups (K/V staged once for
 // 256 query rows) unless that leaves fewer than two workgroups per CU; then
@@ -876,6 +882,7 @@ struct AttnPlan {
     int blocks;        // workgroups without the key split
     int tiles;         // query tiles over all requests
     bool split;
+    int split_len;     // key tiles per piece, at most
     int split_blocks;  // workgroups with it
     size_t ws_bytes;   // workspace of the key split (0 without it)
 };
@@ -895,22 +902,25 @@ AttnPlan plan_bf16(AttnArgs& a, const AttnShape& sh, int hpb) {
     AttnPlan pl{};
     const int t8 = tiles(256 / hpb);
     if (t8 * a.n_hg >= 512) {
-        pl = {8, t8 * a.n_hg, t8, false, 0, 0};
+        pl = {8, t8 * a.n_hg, t8, false, 0, 0, 0};
         return pl;
     }
     const int bq = 128 / hpb;
     const int t4 = tiles(bq);
-    pl = {4, t4 * a.n_hg, t4, false, 0, 0};
+    pl = {4, t4 * a.n_hg, t4, false, 0, 0, 0};
     if (sh.batch != 1 || hpb < 2 || t4 * a.n_hg >= SPLIT_MAX_TILES) return pl;
     const int n = sh.cu[1] - sh.cu[0];
+    const int nkv_max = (n + KVT - 1) / KVT;  // key tiles of the last query tile
+    const int len = nkv_max > SPLIT_LEN || nkv_max < SPLIT_SHORT_MIN ? SPLIT_LEN : SPLIT_SHORT;
     int pieces = 0;
     for (int t = 0; t < t4; ++t) {
         const int nkv = ((bq * (t + 1) < n ? bq * (t + 1) : n) + KVT - 1) / KVT;
-        pieces += (nkv + SPLIT_LEN - 1) / SPLIT_LEN;
+        pieces += (nkv + len - 1) / len;
     }
     if (pieces == t4) return pl;  // no tile is long enough to split
     const size_t slot = (size_t)(sh.d_head == 64 ? split_slot_floats<64>() : split_slot_floats<128>()) * 4;
     pl.split = true;
+    pl.split_len = len;
     pl.split_blocks = pieces * a.n_hg;
     pl.ws_bytes = SPLIT_CNT_BYTES + (size_t)pl.split_blocks * slot;
     return pl;
@@ -923,7 +933,7 @@ hipError_t launch_bf16_w(AttnArgs& a, const AttnShape& sh, void* ws, hipStream_t
     if (pl.nwave == 8) return launch_bf16<DH, HPB, 8, false>(a, pl.blocks, st);
     if constexpr (HPB >= 2) {
         if (pl.split && ws != nullptr) {
-            a.split_len = SPLIT_LEN;
+            a.split_len = pl.split_len;
             a.cnt = (uint32_t*)ws;
             a.part = (float*)((char*)ws + SPLIT_CNT_BYTES);
             return launch_bf16<DH, HPB, 4, true>(a, pl.split_blocks, st);

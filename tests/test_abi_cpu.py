@@ -220,7 +220,8 @@ def test_attention_validation():
 # Key split plan: a fixed 2 KiB region of per-tile counters (the split serves
 # fewer than 512 query tiles x head groups), then one slot per workgroup: 4
 # waves x 64 lanes x (d_head / 2 + 2) floats.  Query tiles are cut into
-# ceil(nkv / 24) pieces.  16k layer: 32 query tiles of 1..32 key tiles, sum of
+# ceil(nkv / 24) pieces, or ceil(nkv / 16) when the longest tile has 19 to
+# 24 key tiles.  16k layer: 32 query tiles of 1..32 key tiles, sum of
 # ceil((t + 1) / 24) = 40 pieces per head group, 8 head groups.
 SLOT128 = 4 * 64 * (128 // 2 + 2) * 4
 SLOT64 = 4 * 64 * (64 // 2 + 2) * 4
@@ -231,7 +232,9 @@ SLOT64 = 4 * 64 * (64 // 2 + 2) * 4
     ([0, 4096], 16, 8, 128, 1, 0),                         # 32k: two whole tiles per CU already
     ([0, 1600], 8, 2, 64, 1, 2048 + 104 * SLOT64),         # four heads per workgroup, 32-row tiles
     ([0, 1537], 16, 8, 128, 1, 2048 + 208 * SLOT128),      # 25 key tiles: the shortest split
-    ([0, 1536], 16, 8, 128, 1, 0),                         # 24 key tiles: no split
+    ([0, 1536], 16, 8, 128, 1, 2048 + 256 * SLOT128),      # 24 key tiles: pieces of 16 (16 + 2 x 8 per group)
+    ([0, 1153], 16, 8, 128, 1, 2048 + 176 * SLOT128),      # 19 key tiles: the shortest split into pieces of 16
+    ([0, 1152], 16, 8, 128, 1, 0),                         # 18 key tiles: no split
     ([0, 13000], 2, 1, 64, 1, 2048 + 972 * SLOT64),        # one head group, up to 9 pieces
     ([0, 8192], 16, 8, 128, 1, 0),                         # eight-wave grid fills the chip
     ([0, 1000, 2048], 16, 8, 128, 1, 0),                   # two requests

@@ -211,6 +211,8 @@ SPLIT_CASES = [
     ("ragged_tail", [1800], 16, 8, 128, "random"),
     ("group4_dh64", [1600], 8, 2, 64, "climb"),
     ("shortest_split", [1537], 16, 8, 128, "low_first_tile"),
+    ("short_pieces", [1500], 16, 8, 128, "random"),
+    ("shortest_short_pieces", [1153], 16, 8, 128, "climb"),
     ("three_pieces", [4000], 16, 8, 128, "random"),
     ("nine_pieces_one_group", [13000], 2, 1, 64, "descent"),
 ]
@@ -280,7 +282,7 @@ def test_attention_key_split_workspace_reuse():
     """One workspace serves calls of different shapes in turn (each call
     leaves its counters at zero): every result equals that of the same call
     on a fresh zeroed workspace, bit for bit."""
-    shapes = [[2048], [1800], [1537], [4000], [2048]]
+    shapes = [[2048], [1500], [1800], [1537], [4000], [1153], [2048]]
     announce(f"attn key split workspace reuse: rows {[s[0] for s in shapes]}")
     big = max(tg.tg_attn_prefill_plan([0, n[0]], 16, 8, 128) for n in shapes)
     shared = torch.zeros(big, dtype=torch.uint8, device="cuda")
